@@ -1,0 +1,603 @@
+// CSA2 Hierarchical Sparse Indexer for decode (P1 section "Compressed Sparse
+// Attention 2 (CSA2)"; P2 section 03; P4 section 二 and its mode table; P5
+// figure caption "Hierarchical Sparse Indexer").
+//
+// Full layer:  scan every visible indexer entry -> block maxima over 8
+//              positions (+ a 4096-bin histogram of their keys)
+//              -> pool of the top P blocks (threshold bin, exact resolution
+//              of the boundary bin) -> re-score the pool positions -> Top-K.
+// Reindex:     re-score the given pool with the layer's own query -> Top-K.
+//
+// Score s_j = sum_h w_h * max(0, q_h . k_j).  The dot products run on MFMA
+// (v_mfma_f32_16x16x32_f16): rows = indexer heads, columns = 16 positions,
+// k = channels.  FP4 keys decode exactly to f16 (e2m1 * e4m3 has <= 6
+// significant bits); each head's bf16 query is scaled by a power of two so
+// its largest element lies in [2^14, 2^15) and converts exactly to f16, and
+// the inverse power of two is folded into w_h.  Products are therefore exact
+// and only the fp32 accumulation rounds.
+#include "csa2_internal.hpp"
+
+namespace csa2 {
+
+constexpr int kScanTiles = 128;                  // 16-position tiles per scan workgroup
+constexpr int kScanChunk = kScanTiles * 16;      // 2048 positions
+constexpr int kScanBlocks = kScanChunk / kBlock; // 256 block maxima
+constexpr int kFilterBlocks = 1024;              // blocks per pool-filter workgroup
+constexpr int kRescoreEntries = 64;              // pool blocks per re-score workgroup
+
+// ---------------------------------------------------------------------------
+// per-wave query operands
+// ---------------------------------------------------------------------------
+
+template <int DI>
+struct IdxQuery {
+  half8_t a[DI / 32];  // A operand of MFMA t: lane (row m = l%16, quarter qq = l/16)
+                       // holds channels qq*DI/4 + 8t .. +7 of head m
+  float w[4];          // scaled weights of heads 4*qq + j (0 for missing heads)
+};
+
+CSA2_DEV float max_rows4(float v) {
+  uint32_t u = __float_as_uint(v);
+  auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  float a = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  uint32_t ua = __float_as_uint(a);
+  auto s16 = __builtin_amdgcn_permlane16_swap(ua, ua, false, false);
+  return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+}
+
+// q: [H][DI] bf16 of this query, w: [H] fp32.
+template <int DI>
+CSA2_DEV void load_idx_query(const uint16_t *__restrict__ q, const float *__restrict__ w, int H,
+                             IdxQuery<DI> &Q) {
+  const int l = lane_id();
+  const int m = l & 15, qq = l >> 4;
+  constexpr int PER = DI / 4;
+  float v[PER];
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    v[i] = (m < H) ? bf16_to_f32(q[m * DI + qq * PER + i]) : 0.0f;
+    mx = fmaxf(mx, fabsf(v[i]));
+  }
+  mx = max_rows4(mx);
+  int e = 0;
+  (void)frexpf(mx, &e);
+  const int kf = (mx > 0.0f) ? 15 - e : 0;  // head max scaled into [2^14, 2^15)
+#pragma unroll
+  for (int t = 0; t < DI / 32; ++t)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Q.a[t][i] = (_Float16)ldexpf(v[8 * t + i], kf);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = 4 * qq + j;
+    const int kh = __shfl(kf, h, 64);
+    Q.w[j] = (h < H) ? ldexpf(w[h], -kh) : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// one 16-position tile
+// ---------------------------------------------------------------------------
+
+// The codes this lane feeds into the tile: DI/8 bytes of one row.
+template <int DI>
+struct LaneCodes {
+  uint32_t w[DI / 32];
+  uint32_t s;  // DI/64 scale bytes (little-endian)
+};
+
+template <int DI>
+CSA2_DEV void load_lane_codes(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, int64_t row,
+                              int qq, LaneCodes<DI> &c) {
+  const uint8_t *cp = codes + row * (DI / 2) + qq * (DI / 8);
+  const uint8_t *sp = scales + row * (DI / 16) + qq * (DI / 64);
+  if constexpr (DI == 64) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(cp);
+    c.w[0] = x.x;
+    c.w[1] = x.y;
+    c.s = *sp;
+  } else if constexpr (DI == 128) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(cp);
+    c.w[0] = x.x;
+    c.w[1] = x.y;
+    c.w[2] = x.z;
+    c.w[3] = x.w;
+    c.s = *reinterpret_cast<const uint16_t *>(sp);
+  } else {
+    static_assert(DI == 256, "indexer dim");
+    const uint4 x = reinterpret_cast<const uint4 *>(cp)[0];
+    const uint4 y = reinterpret_cast<const uint4 *>(cp)[1];
+    c.w[0] = x.x; c.w[1] = x.y; c.w[2] = x.z; c.w[3] = x.w;
+    c.w[4] = y.x; c.w[5] = y.y; c.w[6] = y.z; c.w[7] = y.w;
+    c.s = *reinterpret_cast<const uint32_t *>(sp);
+  }
+}
+
+// Score of position (lane % 16) of the tile, returned in all four quarters.
+template <int DI>
+CSA2_DEV float tile_score(const IdxQuery<DI> &Q, const LaneCodes<DI> &c) {
+  _Float16 sc[(DI / 64 > 0) ? DI / 64 : 1];
+  if constexpr (DI == 64) {
+    sc[0] = e4m3x2_to_f16(c.s)[0];
+  } else if constexpr (DI == 128) {
+    const half2_t s2 = e4m3x2_to_f16(c.s);
+    sc[0] = s2[0];
+    sc[1] = s2[1];
+  } else {
+    const half2_t s2 = e4m3x2_to_f16(c.s);
+    const half2_t s3 = e4m3x2_to_f16(c.s >> 16);
+    sc[0] = s2[0]; sc[1] = s2[1]; sc[2] = s3[0]; sc[3] = s3[1];
+  }
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int t = 0; t < DI / 32; ++t) {
+    const half8_t b = fp4x8_dequant_f16(c.w[t], sc[t / 2]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Q.a[t], b, acc, 0, 0, 0);
+  }
+  float part = Q.w[0] * fmaxf(acc[0], 0.0f);
+  part = fmaf(Q.w[1], fmaxf(acc[1], 0.0f), part);
+  part = fmaf(Q.w[2], fmaxf(acc[2], 0.0f), part);
+  part = fmaf(Q.w[3], fmaxf(acc[3], 0.0f), part);
+  return sum_rows4(part);
+}
+
+CSA2_DEV int64_t visible_entries(const int32_t *seq_len, const int32_t *q_seq, const int32_t *q_pos, int ratio,
+                                 int m, int *s_out) {
+  const int s = q_seq[m];
+  *s_out = s;
+  const int64_t lim = ((int64_t)q_pos[m] + 1) / ratio;
+  const int64_t v = min<int64_t>((int64_t)seq_len[s], lim);
+  return v > 0 ? v : 0;
+}
+
+// ---------------------------------------------------------------------------
+// kernels
+// ---------------------------------------------------------------------------
+
+__global__ void k_zero_u32(uint32_t *__restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// First scan: grid (chunks, queries), 4 waves, 2048 positions per workgroup.
+template <int DI>
+__global__ __launch_bounds__(256) void k_scan(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                              const int64_t *__restrict__ seq_start,
+                                              const int32_t *__restrict__ seq_len, int ratio,
+                                              const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
+                                              const uint16_t *__restrict__ q_idx, const float *__restrict__ w_idx,
+                                              int H, float *__restrict__ bmax, int64_t nb_stride,
+                                              uint32_t *__restrict__ hist) {
+  __shared__ float s_bmax[kScanBlocks];
+  __shared__ uint32_t s_hist[kHistBins];
+  const int m = blockIdx.y;
+  int s;
+  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
+  const int64_t p_begin = (int64_t)blockIdx.x * kScanChunk;
+  if (p_begin >= vis) return;
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) s_hist[i] = 0u;
+
+  IdxQuery<DI> Q;
+  load_idx_query<DI>(q_idx + (int64_t)m * H * DI, w_idx + (int64_t)m * H, H, Q);
+
+  const int64_t row0 = seq_start[s];
+  const int l = lane_id(), n = l & 15, qq = l >> 4, wv = threadIdx.x >> 6;
+  constexpr int U = 4;
+  for (int it = 0; it < kScanTiles / (4 * U); ++it) {
+    LaneCodes<DI> c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tile = (it * U + u) * 4 + wv;
+      const int64_t p = p_begin + tile * 16 + n;
+      load_lane_codes<DI>(codes, scales, row0 + min(p, vis - 1), qq, c[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tile = (it * U + u) * 4 + wv;
+      const int64_t p = p_begin + tile * 16 + n;
+      float sc = tile_score<DI>(Q, c[u]);
+      if (p >= vis) sc = -INFINITY;
+      const float bm = max8_lanes(sc);
+      if (l == 0 || l == 8) s_bmax[tile * 2 + (l >> 3)] = bm;
+    }
+  }
+  __syncthreads();
+  const int nb_here = (int)min<int64_t>(kScanBlocks, (vis - p_begin + kBlock - 1) / kBlock);
+  float *dst = bmax + (int64_t)m * nb_stride + (int64_t)blockIdx.x * kScanBlocks;
+  for (int i = threadIdx.x; i < nb_here; i += blockDim.x) {
+    const float v = s_bmax[i];
+    dst[i] = v;
+    atomicAdd(&s_hist[f2key(v) >> (32 - kHistBits)], 1u);
+  }
+  __syncthreads();
+  uint32_t *gh = hist + (int64_t)m * kHistBins;
+  for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) {
+    const uint32_t cnt = s_hist[b];
+    if (cnt) atomicAdd(&gh[b], cnt);
+  }
+}
+
+// Wave-aggregated append of `pred` lanes to list[*counter ...].
+CSA2_DEV void wave_append(bool pred, int32_t value, uint32_t *counter, int32_t *list) {
+  const uint64_t mask = __ballot(pred);
+  if (!mask) return;
+  const int l = lane_id();
+  const int leader = __ffsll((unsigned long long)mask) - 1;
+  uint32_t base = 0;
+  if (l == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
+  base = __shfl(base, leader, 64);
+  if (pred) list[base + __popcll(mask & ((1ull << l) - 1ull))] = value;
+}
+
+// Pool filter: threshold bin from the histogram; blocks above it are in the
+// pool for sure, blocks in it go to the tie list.
+__global__ __launch_bounds__(256) void k_pool_filter(const float *__restrict__ bmax, int64_t nb_stride,
+                                                     const uint32_t *__restrict__ hist,
+                                                     const int32_t *__restrict__ seq_len, const int32_t *__restrict__ q_seq,
+                                                     const int32_t *__restrict__ q_pos, int ratio, int P,
+                                                     uint32_t *__restrict__ counters, int32_t *__restrict__ sure,
+                                                     int32_t *__restrict__ tie) {
+  __shared__ int s_scan[8];
+  __shared__ int s_T;
+  const int m = blockIdx.y;
+  int s;
+  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
+  const int64_t nb = (vis + kBlock - 1) / kBlock;
+  const int64_t b0 = (int64_t)blockIdx.x * kFilterBlocks;
+  if (b0 >= nb) return;
+  const int64_t need = min<int64_t>(P, nb);
+  int T = -1;
+  if (nb > P) {
+    const uint32_t *h = hist + (int64_t)m * kHistBins;
+    // thread t owns bins [4096-16(t+1), 4096-16t) (thread 0 = highest bins)
+    const int hi = kHistBins - 16 * threadIdx.x;
+    int c = 0;
+    for (int b = hi - 16; b < hi; ++b) c += (int)h[b];
+    int tot;
+    const int before = block_exclusive_scan<256>(c, s_scan, &tot);
+    if (before < need && before + c >= need) {
+      int cum = before;
+      for (int b = hi - 1; b >= hi - 16; --b) {
+        cum += (int)h[b];
+        if (cum >= need) { s_T = b; break; }
+      }
+    }
+    __syncthreads();
+    T = s_T;
+  }
+  const float *bm = bmax + (int64_t)m * nb_stride;
+  for (int j = 0; j < kFilterBlocks / 256; ++j) {
+    const int64_t b = b0 + j * 256 + threadIdx.x;
+    const bool ok = b < nb;
+    const int bin = ok ? (int)(f2key(bm[ok ? b : 0]) >> (32 - kHistBits)) : -2;
+    wave_append(ok && bin > T, (int32_t)b, counters + m * 4 + 0, sure + (int64_t)m * P);
+    wave_append(ok && bin == T, (int32_t)b, counters + m * 4 + 1, tie + (int64_t)m * nb_stride);
+  }
+}
+
+// Pool finalisation, one workgroup per query: resolve the boundary bin
+// exactly on (key desc, block asc), then sort the pool ascending.
+constexpr int kMaxPool = 4096;
+
+__global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict__ bmax, int64_t nb_stride,
+                                                        const uint32_t *__restrict__ counters,
+                                                        const int32_t *__restrict__ sure,
+                                                        const int32_t *__restrict__ tie,
+                                                        const int32_t *__restrict__ seq_len,
+                                                        const int32_t *__restrict__ q_seq,
+                                                        const int32_t *__restrict__ q_pos, int ratio, int P,
+                                                        int32_t *__restrict__ pool_out,
+                                                        int32_t *__restrict__ pool_count) {
+  __shared__ int32_t s_pool[kMaxPool];
+  __shared__ uint32_t s_h[256];
+  __shared__ int s_digit, s_rem, s_cnt;
+  const int m = blockIdx.x;
+  int s;
+  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
+  const int64_t nb = (vis + kBlock - 1) / kBlock;
+  const int need = (int)min<int64_t>(P, nb);
+  const int n_sure = (int)counters[m * 4 + 0];
+  const int n_tie = (int)counters[m * 4 + 1];
+  const int need_t = need - n_sure;
+  const int32_t *su = sure + (int64_t)m * P;
+  const int32_t *ti = tie + (int64_t)m * nb_stride;
+  const float *bm = bmax + (int64_t)m * nb_stride;
+  for (int i = threadIdx.x; i < n_sure; i += blockDim.x) s_pool[i] = su[i];
+  if (threadIdx.x == 0) s_cnt = 0;
+  __syncthreads();
+  if (need_t > 0) {
+    if (need_t >= n_tie) {
+      for (int i = threadIdx.x; i < n_tie; i += blockDim.x) s_pool[n_sure + i] = ti[i];
+    } else {
+      // composite key: larger score first, then smaller block id
+      uint64_t prefix = 0, mask = 0;
+      int rem = need_t;
+      for (int d = 7; d >= 0; --d) {
+        const int shift = 8 * d;
+        for (int i = threadIdx.x; i < 256; i += blockDim.x) s_h[i] = 0u;
+        __syncthreads();
+        for (int i = threadIdx.x; i < n_tie; i += blockDim.x) {
+          const int32_t b = ti[i];
+          const uint64_t c = ((uint64_t)f2key(bm[b]) << 32) | (uint64_t)(~(uint32_t)b);
+          if ((c & mask) == prefix) atomicAdd(&s_h[(c >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          int cum = 0;
+          for (int v = 255; v >= 0; --v) {
+            const int hv = (int)s_h[v];
+            if (cum + hv >= rem) { s_digit = v; s_rem = rem - cum; break; }
+            cum += hv;
+          }
+        }
+        __syncthreads();
+        prefix |= (uint64_t)s_digit << shift;
+        mask |= (uint64_t)255 << shift;
+        rem = s_rem;
+        __syncthreads();
+      }
+      for (int i = threadIdx.x; i < n_tie; i += blockDim.x) {
+        const int32_t b = ti[i];
+        const uint64_t c = ((uint64_t)f2key(bm[b]) << 32) | (uint64_t)(~(uint32_t)b);
+        if (c >= prefix) s_pool[n_sure + atomicAdd(&s_cnt, 1)] = b;
+      }
+    }
+  }
+  __syncthreads();
+  int n2 = 64;
+  while (n2 < need) n2 <<= 1;
+  for (int i = need + threadIdx.x; i < n2; i += blockDim.x) s_pool[i] = 0x7FFFFFFF;
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += blockDim.x) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const int32_t a = s_pool[i], b = s_pool[ixj];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) { s_pool[i] = b; s_pool[ixj] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int32_t *out = pool_out + (int64_t)m * P;
+  for (int i = threadIdx.x; i < P; i += blockDim.x) out[i] = (i < need) ? s_pool[i] : -1;
+  if (threadIdx.x == 0) pool_count[m] = need;
+}
+
+// Re-score the positions of 64 pool blocks per workgroup.  Slot 8*e + r of a
+// query holds the score of position 8*pool[e] + r (-inf when not visible).
+template <int DI>
+__global__ __launch_bounds__(256) void k_rescore(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                                 const int64_t *__restrict__ seq_start,
+                                                 const int32_t *__restrict__ seq_len, int ratio,
+                                                 const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
+                                                 const uint16_t *__restrict__ q_idx, const float *__restrict__ w_idx,
+                                                 int H, const int32_t *__restrict__ pool,
+                                                 const int32_t *__restrict__ pool_count, int P,
+                                                 float *__restrict__ pscore) {
+  const int m = blockIdx.y;
+  int s;
+  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
+  const int cnt = min(pool_count[m], P);
+  const int e0 = blockIdx.x * kRescoreEntries;
+  if (e0 >= cnt) return;
+  float *ps = pscore + (int64_t)m * 8 * P;
+  const int l = lane_id(), n = l & 15, qq = l >> 4, wv = threadIdx.x >> 6;
+  if (vis == 0) {
+    for (int i = threadIdx.x; i < 8 * kRescoreEntries; i += blockDim.x)
+      if (e0 * 8 + i < 8 * cnt) ps[e0 * 8 + i] = -INFINITY;
+    return;
+  }
+  IdxQuery<DI> Q;
+  load_idx_query<DI>(q_idx + (int64_t)m * H * DI, w_idx + (int64_t)m * H, H, Q);
+  const int64_t row0 = seq_start[s];
+  const int32_t *pl = pool + (int64_t)m * P;
+  constexpr int TILES = kRescoreEntries / 2;
+  for (int t = wv; t < TILES; t += 4) {
+    const int e = e0 + 2 * t + (n >> 3);
+    const int32_t blk = (e < cnt) ? pl[e] : -1;
+    const int64_t pos = (int64_t)blk * kBlock + (n & 7);
+    const bool valid = blk >= 0 && pos < vis;
+    LaneCodes<DI> c;
+    load_lane_codes<DI>(codes, scales, row0 + (valid ? pos : 0), qq, c);
+    float sc = tile_score<DI>(Q, c);
+    if (!valid) sc = -INFINITY;
+    if (qq == 0 && e < cnt) ps[8 * e + (n & 7)] = sc;
+  }
+}
+
+// Top-K over the re-scored pool, one workgroup (1024 threads) per query.
+// Thread t owns slots [t*PER, (t+1)*PER); slot order equals position order
+// because the pool is ascending, so ties on the score resolve to the lower
+// slot and the compaction below emits positions in ascending order.
+template <int PER>
+__global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ pscore,
+                                                      const int32_t *__restrict__ pool,
+                                                      const int32_t *__restrict__ pool_count, int P, int K,
+                                                      int32_t *__restrict__ topk_out, float *__restrict__ topk_score) {
+  __shared__ uint32_t s_h[256];
+  __shared__ int s_scan[17];
+  __shared__ int s_digit, s_rem;
+  const int m = blockIdx.x;
+  const int cnt = min(pool_count[m], P);
+  const int nslots = 8 * cnt;
+  const float *ps = pscore + (int64_t)m * 8 * P;
+  uint32_t key[PER];
+  int nvalid = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int slot = threadIdx.x * PER + i;
+    const float v = (slot < nslots) ? ps[slot] : -INFINITY;
+    key[i] = (v > -INFINITY) ? f2key(v) : 0u;
+    nvalid += key[i] != 0u;
+  }
+  int total;
+  (void)block_exclusive_scan<1024>(nvalid, s_scan, &total);
+  const int Kp = min(K, total);
+  int32_t *out = topk_out + (int64_t)m * K;
+  float *osc = topk_score ? topk_score + (int64_t)m * K : nullptr;
+  uint32_t kstar = 0xFFFFFFFFu;
+  int rem = 0;
+  if (Kp > 0) {
+    uint32_t prefix = 0, mask = 0;
+    rem = Kp;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = threadIdx.x; i < 256; i += blockDim.x) s_h[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (key[i] != 0u && (key[i] & mask) == prefix) atomicAdd(&s_h[(key[i] >> shift) & 255u], 1u);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int cum = 0;
+        for (int v = 255; v >= 0; --v) {
+          const int hv = (int)s_h[v];
+          if (cum + hv >= rem) { s_digit = v; s_rem = rem - cum; break; }
+          cum += hv;
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_digit << shift;
+      mask |= 255u << shift;
+      rem = s_rem;
+      __syncthreads();
+    }
+    kstar = prefix;
+  }
+  // equal-key ranks (lowest slots first), then compaction
+  int neq = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) neq += (Kp > 0 && key[i] == kstar);
+  int tmp;
+  int eq_before = block_exclusive_scan<1024>(neq, s_scan, &tmp);
+  bool sel[PER];
+  int nsel = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    bool take = false;
+    if (Kp > 0 && key[i] != 0u) {
+      if (key[i] > kstar) take = true;
+      else if (key[i] == kstar) { take = eq_before < rem; ++eq_before; }
+    }
+    sel[i] = take;
+    nsel += take;
+  }
+  int rank = block_exclusive_scan<1024>(nsel, s_scan, &tmp);
+  const int32_t *pl = pool + (int64_t)m * P;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (sel[i]) {
+      const int slot = threadIdx.x * PER + i;
+      out[rank] = pl[slot >> 3] * kBlock + (slot & 7);
+      if (osc) osc[rank] = ps[slot];
+      ++rank;
+    }
+  }
+  for (int i = Kp + threadIdx.x; i < K; i += blockDim.x) {
+    out[i] = -1;
+    if (osc) osc[i] = __builtin_nanf("");
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+IndexWs index_ws_layout(int64_t max_len, int m, int pool_blocks, int top_k) {
+  (void)top_k;
+  IndexWs w{};
+  const int64_t chunks = (max_len + kScanChunk - 1) / kScanChunk;
+  w.nb_max = (chunks > 0 ? chunks : 1) * kScanBlocks;
+  w.slots = 8 * pool_blocks;
+  size_t off = 0;
+  w.bmax = off;     off = align256(off + sizeof(float) * (size_t)m * w.nb_max);
+  w.hist = off;     off = align256(off + sizeof(uint32_t) * (size_t)m * kHistBins);
+  w.counters = off; off = align256(off + sizeof(uint32_t) * (size_t)m * 4);
+  w.sure = off;     off = align256(off + sizeof(int32_t) * (size_t)m * pool_blocks);
+  w.tie = off;      off = align256(off + sizeof(int32_t) * (size_t)m * w.nb_max);
+  w.pscore = off;   off = align256(off + sizeof(float) * (size_t)m * w.slots);
+  w.total = off;
+  return w;
+}
+
+template <int DI>
+static int rescore_and_select(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
+                              const float *w_idx, int heads, const int32_t *pool, const int32_t *pool_count,
+                              int P, int K, int32_t *topk_out, float *topk_score, float *pscore,
+                              hipStream_t stream) {
+  const dim3 g5((P + kRescoreEntries - 1) / kRescoreEntries, qs.m);
+  hipLaunchKernelGGL(k_rescore<DI>, g5, dim3(256), 0, stream, idx.codes, idx.scales, idx.seq_start, idx.seq_len,
+                     idx.ratio, qs.seq, qs.pos, q_idx, w_idx, heads, pool, pool_count, P, pscore);
+  if (8 * P <= 1024 * 16)
+    hipLaunchKernelGGL(k_topk_select<16>, dim3(qs.m), dim3(1024), 0, stream, pscore, pool, pool_count, P, K,
+                       topk_out, topk_score);
+  else
+    hipLaunchKernelGGL(k_topk_select<32>, dim3(qs.m), dim3(1024), 0, stream, pscore, pool, pool_count, P, K,
+                       topk_out, topk_score);
+  return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+}
+
+template <int DI>
+static int index_full_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
+                           const float *w_idx, int heads, int P, int K, int32_t *pool_out, int32_t *pool_count,
+                           int32_t *topk_out, float *topk_score, void *ws, hipStream_t stream) {
+  const IndexWs L = index_ws_layout(idx.max_len, qs.m, P, K);
+  char *base = static_cast<char *>(ws);
+  float *bmax = reinterpret_cast<float *>(base + L.bmax);
+  uint32_t *hist = reinterpret_cast<uint32_t *>(base + L.hist);
+  uint32_t *counters = reinterpret_cast<uint32_t *>(base + L.counters);
+  int32_t *sure = reinterpret_cast<int32_t *>(base + L.sure);
+  int32_t *tie = reinterpret_cast<int32_t *>(base + L.tie);
+  float *pscore = reinterpret_cast<float *>(base + L.pscore);
+
+  // hist and counters are adjacent: clear both with one fill kernel
+  const int64_t nz = (int64_t)((L.sure - L.hist) / sizeof(uint32_t));
+  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
+  const int64_t chunks = (idx.max_len + kScanChunk - 1) / kScanChunk;
+  if (chunks > 0)
+    hipLaunchKernelGGL(k_scan<DI>, dim3((unsigned)chunks, qs.m), dim3(256), 0, stream, idx.codes, idx.scales,
+                       idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, q_idx, w_idx, heads, bmax, L.nb_max,
+                       hist);
+  const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);
+  hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, hist, idx.seq_len, qs.seq, qs.pos,
+                     idx.ratio, P, counters, sure, tie);
+  hipLaunchKernelGGL(k_pool_finalize, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, counters, sure, tie,
+                     idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
+  if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
+  return rescore_and_select<DI>(idx, qs, q_idx, w_idx, heads, pool_out, pool_count, P, K, topk_out, topk_score,
+                                pscore, stream);
+}
+
+int launch_index_full(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
+                      const float *w_idx, int heads, int P, int K, int32_t *pool_out, int32_t *pool_count,
+                      int32_t *topk_out, float *topk_score, void *ws, hipStream_t stream) {
+  switch (idx.dim) {
+    case 64: return index_full_impl<64>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, topk_out,
+                                        topk_score, ws, stream);
+    case 128: return index_full_impl<128>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, topk_out,
+                                          topk_score, ws, stream);
+    case 256: return index_full_impl<256>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, topk_out,
+                                          topk_score, ws, stream);
+    default: return CSA2_ERR_UNSUPPORTED;
+  }
+}
+
+int launch_reindex(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx, const float *w_idx,
+                   int heads, const int32_t *pool_in, const int32_t *pool_count, int P, int K, int32_t *topk_out,
+                   float *topk_score, void *ws, hipStream_t stream) {
+  const IndexWs L = index_ws_layout(idx.max_len, qs.m, P, K);
+  float *pscore = reinterpret_cast<float *>(static_cast<char *>(ws) + L.pscore);
+  switch (idx.dim) {
+    case 64: return rescore_and_select<64>(idx, qs, q_idx, w_idx, heads, pool_in, pool_count, P, K, topk_out,
+                                           topk_score, pscore, stream);
+    case 128: return rescore_and_select<128>(idx, qs, q_idx, w_idx, heads, pool_in, pool_count, P, K, topk_out,
+                                             topk_score, pscore, stream);
+    case 256: return rescore_and_select<256>(idx, qs, q_idx, w_idx, heads, pool_in, pool_count, P, K, topk_out,
+                                             topk_score, pscore, stream);
+    default: return CSA2_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace csa2

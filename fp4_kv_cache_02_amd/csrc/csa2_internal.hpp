@@ -1,0 +1,48 @@
+// Internal declarations shared by the CSA2 translation units.
+#pragma once
+
+#include "../../include/csa2.h"
+#include "csa2_device.hpp"
+
+namespace csa2 {
+
+// ---- write path (csa2_codec.hip) ----
+int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const int64_t *dst_row,
+                        uint8_t *codes, uint8_t *scales, const float *w_ik, int idx_dim, uint8_t *ik_codes,
+                        uint8_t *ik_scales, hipStream_t stream);
+int launch_quantize_fp8_rows(const void *x, int x_dtype, int64_t rows, int dim, const int64_t *dst_row,
+                             uint8_t *codes, float *scale, hipStream_t stream);
+int launch_dequant_fp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int dim, float *out,
+                       hipStream_t stream);
+
+// ---- indexer (csa2_index.hip) ----
+// Workspace layout of the indexer calls, all offsets 256-byte aligned.
+struct IndexWs {
+  size_t bmax, hist, counters, sure, tie, pscore, total;
+  int64_t nb_max;       // block slots per query
+  int32_t slots;        // 8 * pool_blocks
+};
+IndexWs index_ws_layout(int64_t max_len, int m, int pool_blocks, int top_k);
+
+int launch_index_full(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
+                      const float *w_idx, int heads, int pool_blocks, int top_k, int32_t *pool_out,
+                      int32_t *pool_count, int32_t *topk_out, float *topk_score, void *ws, hipStream_t stream);
+int launch_reindex(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx, const float *w_idx,
+                   int heads, const int32_t *pool_in, const int32_t *pool_count, int pool_blocks, int top_k,
+                   int32_t *topk_out, float *topk_score, void *ws, hipStream_t stream);
+
+// ---- flat (prefill) indexer (csa2_prefill.hip) ----
+size_t flat_ws_bytes(int64_t max_len, int m, int top_k);
+int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
+                      const float *w_idx, int heads, int top_k, int32_t *topk_out, float *topk_score, void *ws,
+                      hipStream_t stream);
+
+// ---- attention (csa2_attn.hip) ----
+size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int window);
+int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int q_dtype, int heads,
+                const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,
+                hipStream_t stream);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace csa2

@@ -34,6 +34,8 @@ TAG_W_IDX = 4     # indexer head weights
 TAG_Q = 5         # main attention queries
 TAG_SWA = 6       # pre-quantisation sliding-window rows
 TAG_LEN = 7       # ragged sequence lengths
+TAG_IDX_KEY = 8   # pre-quantisation indexer-key rows when the indexer is exercised on its own
+TAG_IDX_LIST = 9  # synthetic Top-K lists when attention is exercised on its own
 
 
 def rng(cfg: int, tag: int, layer: int = 0, seq: int = 0, chunk: int = 0) -> np.random.Generator:

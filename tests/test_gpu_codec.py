@@ -1,0 +1,125 @@
+"""GPU parity of the FP4 / FP8 codec and the indexer-key derivation (bit-exact)."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_kv_cache_02_amd as csa2
+import synth
+from oracle import codec
+from tests._gpu_util import announce, dev, empty_u8, gpu_quantize, h, t
+
+pytestmark = pytest.mark.gpu
+
+
+def test_dequant_exhaustive_codes_and_scales():
+    announce("dequant exhaustive")
+    scale_bytes = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], dtype=np.uint8)
+    rows = len(scale_bytes)
+    codes = np.tile(np.arange(256, dtype=np.uint8), (rows, 1))          # dim 512: every code byte
+    scales = np.repeat(scale_bytes[:, None], 32, axis=1)
+    out = torch.empty((rows, 512), dtype=torch.float32, device=dev())
+    csa2.csa2_dequant_fp4(t(codes), t(scales), out)
+    got = h(out).astype(np.float64)
+    ref = codec.fp4_decode(codes, scales)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
+def _adversarial_rows(dim=128):
+    rng = np.random.default_rng(31)
+    rows = []
+    mids = (codec.E2M1_POS[:-1] + codec.E2M1_POS[1:]) / 2
+    for sc in list(range(1, 127, 3)) + [1, 2, 7, 8, 9, 56, 125, 126]:
+        s = codec.E4M3_POS[sc]
+        g = []
+        for _ in range(dim // 16):
+            grp = np.zeros(16, np.float32)
+            grp[0] = np.float32(6 * s)
+            vals = np.float32(mids * s)
+            pick = rng.permutation(np.concatenate([vals, np.nextafter(vals, np.float32(np.inf)),
+                                                   np.nextafter(vals, np.float32(0))]))[:15]
+            grp[1:] = pick * rng.choice([-1, 1], 15)
+            g.append(grp)
+        rows.append(np.concatenate(g))
+    # scale ties: amax/6 exactly on an E4M3 midpoint, and just around it
+    emids = (codec.E4M3_POS[:-1] + codec.E4M3_POS[1:]) / 2
+    for i in range(0, 126, 5):
+        a = np.float32(6 * emids[i])
+        for v in (a, np.nextafter(a, np.float32(np.inf)), np.nextafter(a, np.float32(0))):
+            r = (rng.standard_normal(dim) * float(v) / 8).astype(np.float32)
+            r[::16] = v
+            rows.append(r)
+    special = np.zeros((6, dim), np.float32)
+    special[1, 3] = -0.0
+    special[2] = -0.0
+    special[3] = np.float32(6 * 2.0 ** -10)              # scale rounds to 0
+    special[4] = (rng.standard_normal(dim) * 1e5).astype(np.float32)   # scale saturates
+    special[5] = (rng.standard_normal(dim) * 1e-8).astype(np.float32)
+    return np.concatenate([np.stack(rows), special]).astype(np.float32)
+
+
+@pytest.mark.parametrize("dim", [128, 512])
+def test_quantize_bit_exact_random_and_adversarial(dim):
+    announce("quantize fp4", dim)
+    rng = np.random.default_rng(32)
+    x = np.concatenate([rng.standard_normal((3000, dim)).astype(np.float32), _adversarial_rows(dim)])
+    codes, scales = gpu_quantize(x)
+    rc, rs = codec.fp4_encode(x)
+    assert np.array_equal(h(scales), rs)
+    assert np.array_equal(h(codes), rc)
+
+
+def test_quantize_bf16_input_and_scattered_rows():
+    announce("quantize fp4 bf16 + dst_row")
+    rng = np.random.default_rng(33)
+    bits = synth.f32_to_bf16_bits(rng.standard_normal((257, 128)).astype(np.float32))
+    xf = synth.bf16_bits_to_f32(bits)
+    dst = rng.permutation(400)[:257].astype(np.int64)
+    codes, scales = empty_u8(400, 64), empty_u8(400, 8)
+    codes.zero_()
+    scales.zero_()
+    csa2.csa2_quantize_fp4(t(bits).view(torch.bfloat16), codes, scales, dst_row=t(dst))
+    rc, rs = codec.fp4_encode(xf)
+    gc, gs = h(codes), h(scales)
+    assert np.array_equal(gc[dst], rc) and np.array_equal(gs[dst], rs)
+    untouched = np.setdiff1d(np.arange(400), dst)
+    assert np.all(gc[untouched] == 0) and np.all(gs[untouched] == 0)
+
+
+@pytest.mark.parametrize("dim,di", [(128, 64), (512, 128), (256, 256)])
+def test_derive_indexer_key_bit_exact(dim, di):
+    announce("derive indexer key", dim, di)
+    x = synth.main_kv_rows(0, 0, 0, 2000, dim)
+    w = synth.w_ik(0, dim, di)
+    codes, scales, ikc, iks = gpu_quantize(x, w)
+    rc, rs = codec.fp4_encode(x)
+    assert np.array_equal(h(codes), rc) and np.array_equal(h(scales), rs)
+    kc, ks = codec.indexer_key(rc, rs, w)
+    assert np.array_equal(h(iks), ks)
+    assert np.array_equal(h(ikc), kc)
+
+
+def test_fp8_rows_bit_exact():
+    announce("fp8 rows")
+    rng = np.random.default_rng(34)
+    x = np.concatenate([rng.standard_normal((300, 512)),
+                        rng.standard_normal((5, 512)) * 1e-7,
+                        rng.standard_normal((5, 512)) * 1e7,
+                        np.zeros((2, 512))]).astype(np.float32)
+    x[-1, 7] = -0.0
+    codes = empty_u8(len(x), 512)
+    scale = torch.empty(len(x), dtype=torch.float32, device=dev())
+    csa2.csa2_quantize_fp8_rows(t(x), codes, scale)
+    rc, rs = codec.fp8_rows_encode(x)
+    assert np.array_equal(h(scale), rs)
+    assert np.array_equal(h(codes), rc)
+
+
+def test_quantize_full_cache_shape_sample():
+    # 65,536 rows of the 512-channel latent (one 64K decoder cache), every row checked
+    announce("quantize 64K x 512")
+    x = synth.main_kv_rows(1, 0, 0, 65536, 512)
+    codes, scales = gpu_quantize(x)
+    rc, rs = codec.fp4_encode(x)
+    assert np.array_equal(h(scales), rs)
+    assert np.array_equal(h(codes), rc)

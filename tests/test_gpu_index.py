@@ -1,0 +1,223 @@
+"""GPU parity of the hierarchical sparse indexer (Full, Reindex) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_kv_cache_02_amd as csa2
+import synth
+from oracle import codec, indexer
+from tests._gpu_util import (announce, assert_sets_equal_modulo_band, dev, gpu_quantize, h, t, workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+def _cache_from_raw(cfg, lens, di):
+    """Ragged indexer-key cache: GPU and oracle each quantise the same raw rows."""
+    xs = [synth.gaussian_rows(cfg, synth.TAG_IDX_KEY, 0, s, 0, n, di) for s, n in enumerate(lens)]
+    x = np.concatenate(xs) if xs else np.zeros((0, di), np.float32)
+    codes, scales = gpu_quantize(x)
+    rc, rs = codec.fp4_encode(x)
+    assert np.array_equal(h(codes), rc) and np.array_equal(h(scales), rs)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    return codes, scales, rc, rs, starts
+
+
+def _run_full(codes, scales, starts, lens, di, q_seq, q_pos, qi, wi, P, K, ratio=1):
+    M = len(q_seq)
+    cache = csa2.fp4_cache(codes, scales, t(starts), t(np.asarray(lens, np.int32)), di, max(lens), ratio)
+    qs = csa2.queries(t(np.asarray(q_seq, np.int32)), t(np.asarray(q_pos, np.int32)))
+    ws = workspace(csa2.csa2_index_workspace_size(cache, M, P, K))
+    pool = torch.full((M, P), -7, dtype=torch.int32, device=dev())
+    cnt = torch.full((M,), -7, dtype=torch.int32, device=dev())
+    topk = torch.full((M, K), -7, dtype=torch.int32, device=dev())
+    sc = torch.full((M, K), -7.0, dtype=torch.float32, device=dev())
+    csa2.csa2_index_full(cache, qs, t(qi).view(torch.bfloat16), t(wi), P, K, pool, cnt, topk, sc, ws)
+    return h(pool), h(cnt), h(topk), h(sc), (cache, qs, ws)
+
+
+def _check_query(rc, rs, start, vis, qf, w, P, K, gpool, gcnt, gtopk, gscore):
+    keys = codec.fp4_decode(rc[start:start + vis], rs[start:start + vis])
+    opool, ocnt, otopk, s = indexer.index_full(qf, w, keys, P, K)
+    assert gcnt == ocnt
+    assert np.all(gpool[gcnt:] == -1) and np.all(np.diff(gpool[:gcnt]) > 0)
+    bm = indexer.block_max(s) if vis else np.zeros(0)
+    nband_pool = assert_sets_equal_modulo_band(gpool[:gcnt], opool[:ocnt], lambda b: bm[b], P, what="pool")
+    sel = gtopk[gtopk >= 0]
+    nsel = int((otopk >= 0).sum())
+    assert len(sel) == nsel and np.all(gtopk[nsel:] == -1) and np.all(np.diff(sel) > 0)
+    if nband_pool == 0:
+        assert_sets_equal_modulo_band(sel, otopk[otopk >= 0], lambda j: s[j], K, what="topk")
+    else:
+        # pools differ inside the near-tie band: the GPU list must be a valid
+        # Top-K of the GPU pool under the exact scores
+        cand = indexer.pool_positions(gpool[:gcnt], vis)
+        assert set(sel.tolist()) <= set(cand.tolist())
+        theta = np.sort(s[cand])[::-1][nsel - 1]
+        tol = 1e-4 * abs(theta)
+        rest = np.setdiff1d(cand, sel)
+        assert np.all(s[sel] >= theta - tol) and (len(rest) == 0 or np.all(s[rest] <= theta + tol))
+    if len(sel):
+        ref = s[sel]
+        tol = 1e-5 * max(1.0, np.abs(s).max())
+        assert np.all(np.abs(gscore[:len(sel)] - ref) <= tol), np.abs(gscore[:len(sel)] - ref).max()
+        assert np.all(np.isnan(gscore[len(sel):]))
+    return opool, s
+
+
+@pytest.mark.parametrize("case", ["c0", "ragged", "ratio2", "c1"])
+def test_index_full_matches_oracle(case):
+    if case == "c0":
+        lens, di, H, P, K = [4096], 64, 4, 64, 64
+        q_seq, q_pos, ratio = [0], [4095], 1
+    elif case == "ragged":
+        lens, di, H, P, K = [1, 7, 64, 513, 5000, 9, 8], 128, 8, 16, 32
+        q_seq = [0, 1, 2, 3, 4, 5, 6, 4, 3]
+        q_pos = [0, 6, 63, 512, 4999, 8, 7, 1234, 100]
+        ratio = 1
+    elif case == "ratio2":
+        lens, di, H, P, K = [3000, 777], 128, 8, 32, 100
+        q_seq, q_pos, ratio = [0, 0, 1, 1], [5999, 2500, 1553, 0], 2
+    else:
+        lens, di, H, P, K = [65536], 128, 8, 2048, 512
+        q_seq, q_pos, ratio = [0], [65535], 1
+    announce("index_full", case)
+    cfg = {"c0": 100, "ragged": 101, "ratio2": 102, "c1": 103}[case]
+    codes, scales, rc, rs, starts = _cache_from_raw(cfg, lens, di)
+    M = len(q_seq)
+    qi = synth.q_idx(cfg, 0, M, H, di)
+    wi = synth.w_idx(cfg, 0, M, H)
+    gpool, gcnt, gtopk, gsc, _ = _run_full(codes, scales, starts, lens, di, q_seq, q_pos, qi, wi, P, K, ratio)
+    qf = synth.bf16_bits_to_f32(qi)
+    for i in range(M):
+        s_ = q_seq[i]
+        vis = indexer.visible_count(lens[s_], q_pos[i], ratio)
+        _check_query(rc, rs, starts[s_], vis, qf[i], wi[i], P, K, gpool[i], gcnt[i], gtopk[i], gsc[i])
+
+
+def test_index_all_equal_scores_take_lowest_ids():
+    announce("index_full ties")
+    lens, di, H, P, K = [3001], 64, 4, 10, 50
+    codes, scales, rc, rs, starts = _cache_from_raw(104, lens, di)
+    qi = synth.q_idx(104, 0, 1, H, di)
+    wi = np.zeros((1, H), np.float32)            # every score is exactly 0
+    gpool, gcnt, gtopk, gsc, _ = _run_full(codes, scales, starts, lens, di, [0], [3000], qi, wi, P, K)
+    assert gpool[0].tolist() == list(range(P)) and gcnt[0] == P
+    assert gtopk[0].tolist() == list(range(K))
+    assert np.all(gsc[0] == 0)
+
+
+def test_index_repeatable():
+    announce("index_full determinism")
+    lens, di, H, P, K = [20000], 128, 8, 256, 128
+    codes, scales, rc, rs, starts = _cache_from_raw(105, lens, di)
+    qi = synth.q_idx(105, 0, 1, H, di)
+    wi = synth.w_idx(105, 0, 1, H)
+    a = _run_full(codes, scales, starts, lens, di, [0], [19999], qi, wi, P, K)
+    b = _run_full(codes, scales, starts, lens, di, [0], [19999], qi, wi, P, K)
+    for x, y in zip(a[:4], b[:4]):
+        assert np.array_equal(x, y, equal_nan=True)
+
+
+def test_reindex_matches_oracle():
+    announce("reindex")
+    lens, di, H, P, K = [30000, 5000], 128, 8, 512, 256
+    codes, scales, rc, rs, starts = _cache_from_raw(106, lens, di)
+    M = 2
+    q_pos = [29999, 4999]
+    qi0, wi0 = synth.q_idx(106, 0, M, H, di), synth.w_idx(106, 0, M, H)
+    qi1, wi1 = synth.q_idx(106, 1, M, H, di), synth.w_idx(106, 1, M, H)
+    # the pool is an input: the oracle's pool of the Full layer
+    pools = np.full((M, P), -1, np.int32)
+    cnts = np.zeros(M, np.int32)
+    for i in range(M):
+        keys = codec.fp4_decode(rc[starts[i]:starts[i] + lens[i]], rs[starts[i]:starts[i] + lens[i]])
+        p, c, _, _ = indexer.index_full(synth.bf16_bits_to_f32(qi0[i]), wi0[i], keys, P, K)
+        pools[i], cnts[i] = p, c
+    cache = csa2.fp4_cache(codes, scales, t(starts), t(np.asarray(lens, np.int32)), di, max(lens), 1)
+    qs = csa2.queries(t(np.arange(M, dtype=np.int32)), t(np.asarray(q_pos, np.int32)))
+    ws = workspace(csa2.csa2_index_workspace_size(cache, M, P, K))
+    topk = torch.full((M, K), -7, dtype=torch.int32, device=dev())
+    sc = torch.zeros((M, K), dtype=torch.float32, device=dev())
+    csa2.csa2_reindex(cache, qs, t(qi1).view(torch.bfloat16), t(wi1), t(pools), t(cnts), K, topk, sc, ws)
+    gt, gs = h(topk), h(sc)
+    qf1 = synth.bf16_bits_to_f32(qi1)
+    for i in range(M):
+        keys = codec.fp4_decode(rc[starts[i]:starts[i] + lens[i]], rs[starts[i]:starts[i] + lens[i]])
+        otopk, _ = indexer.reindex(qf1[i], wi1[i], keys, pools[i], K)
+        s = indexer.scores(qf1[i], wi1[i], keys)
+        sel = gt[i][gt[i] >= 0]
+        assert len(sel) == int((otopk >= 0).sum())
+        assert_sets_equal_modulo_band(sel, otopk[otopk >= 0], lambda j: s[j], K, what="reindex")
+        assert np.all(np.abs(gs[i][:len(sel)] - s[sel]) <= 1e-5 * max(1.0, np.abs(s).max()))
+
+
+@pytest.mark.parametrize("shape", ["c4_one_seq", "c3_ragged"])
+def test_index_full_size_sampled_properties(shape):
+    """1M-entry (and ragged 32K-256K) caches: properties checked on sampled rows.
+
+    The oracle quantises only the rows it needs (rows are drawn per chunk, so
+    any sub-range regenerates identically): every row of the GPU pool blocks
+    plus a random sample of other blocks.
+    """
+    rng = np.random.default_rng(7)
+    if shape == "c4_one_seq":
+        lens = [1 << 20]
+        cfg = 107
+    else:
+        lens = synth.ragged_lengths(3, 32, 32768, 262144).tolist()[:6]
+        cfg = 108
+    di, H, P, K = 128, 8, 2048, 512
+    announce("index full-size", shape, sum(lens))
+    x = np.concatenate([synth.gaussian_rows(cfg, synth.TAG_IDX_KEY, 0, s, 0, n, di) for s, n in enumerate(lens)])
+    codes, scales = gpu_quantize(x)
+    del x
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    M = len(lens)
+    q_pos = [n - 1 for n in lens]
+    qi, wi = synth.q_idx(cfg, 0, M, H, di), synth.w_idx(cfg, 0, M, H)
+    gpool, gcnt, gtopk, gsc, _ = _run_full(codes, scales, starts, lens, di, list(range(M)), q_pos, qi, wi, P, K)
+    gc_all, gs_all = h(codes), h(scales)
+    qf = synth.bf16_bits_to_f32(qi)
+    for i in range(M):
+        n = lens[i]
+        nb = (n + 7) // 8
+        assert gcnt[i] == min(P, nb)
+        pool = gpool[i][:gcnt[i]]
+        sample_blocks = np.setdiff1d(rng.choice(nb, min(nb, 4000), replace=False), pool)
+        blocks = np.concatenate([pool, sample_blocks])
+        rows = (blocks[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+        rows = rows[rows < n]
+        # regenerate the needed rows chunk by chunk
+        raw = np.empty((len(rows), di), np.float32)
+        order = np.argsort(rows)
+        srows = rows[order]
+        for c in np.unique(srows // synth.CHUNK_ROWS):
+            sel = (srows // synth.CHUNK_ROWS) == c
+            lo = int(c) * synth.CHUNK_ROWS
+            hi = min(n, lo + synth.CHUNK_ROWS)
+            chunk = synth.gaussian_rows(cfg, synth.TAG_IDX_KEY, 0, i, lo, hi - lo, di)
+            raw[order[sel]] = chunk[srows[sel] - lo]
+        rc, rs = codec.fp4_encode(raw)
+        g0 = starts[i]
+        assert np.array_equal(gc_all[g0 + rows], rc) and np.array_equal(gs_all[g0 + rows], rs)
+        s = indexer.scores(qf[i], wi[i], codec.fp4_decode(rc, rs))
+        score_of = dict(zip(rows.tolist(), s.tolist()))
+        bmax = {}
+        for r, v in zip(rows.tolist(), s.tolist()):
+            b = r // 8
+            bmax[b] = max(bmax.get(b, -np.inf), v)
+        theta_p = min(bmax[b] for b in pool.tolist())
+        scale = max(1.0, max(abs(v) for v in bmax.values()))
+        outside = [bmax[b] for b in sample_blocks.tolist()]
+        assert max(outside) <= theta_p + 1e-4 * abs(theta_p) + 1e-6 * scale
+        sel = gtopk[i][gtopk[i] >= 0]
+        assert len(sel) == min(K, len(indexer.pool_positions(pool, n)))
+        cand = indexer.pool_positions(pool, n)
+        cs = np.array([score_of[int(j)] for j in cand])
+        ss = np.array([score_of[int(j)] for j in sel])
+        theta = np.sort(cs)[::-1][len(sel) - 1]
+        tol = 1e-4 * abs(theta) + 1e-6 * scale
+        rest = np.setdiff1d(cand, sel)
+        rs_ = np.array([score_of[int(j)] for j in rest])
+        assert np.all(ss >= theta - tol) and np.all(rs_ <= theta + tol)
+        assert np.all(np.abs(gsc[i][:len(sel)] - ss) <= 1e-5 * scale)
