@@ -133,18 +133,27 @@ def _dtype_code(t) -> int:
 # descriptors
 # ---------------------------------------------------------------------------
 
+# The descriptors below hold raw device addresses; each keeps a reference to
+# the tensors it points at (attribute `_keep`) so they outlive the descriptor.
+
 def fp4_cache(codes, scales, seq_start, seq_len, dim: int, max_len: int, ratio: int = 1) -> Fp4Cache:
     """Describe an FP4 cache (codes [rows, dim/2] u8, scales [rows, dim/16] u8, seq_start int64, seq_len int32)."""
-    return Fp4Cache(_ptr(codes), _ptr(scales), _ptr(seq_start), _ptr(seq_len), int(seq_len.numel()), int(dim),
-                    int(max_len), int(ratio))
+    c = Fp4Cache(_ptr(codes), _ptr(scales), _ptr(seq_start), _ptr(seq_len), int(seq_len.numel()), int(dim),
+                 int(max_len), int(ratio))
+    c._keep = (codes, scales, seq_start, seq_len)
+    return c
 
 
 def queries(seq, pos) -> Queries:
-    return Queries(_ptr(seq), _ptr(pos), int(seq.numel()))
+    q = Queries(_ptr(seq), _ptr(pos), int(seq.numel()))
+    q._keep = (seq, pos)
+    return q
 
 
 def swa(codes, scale, start, count, dim: int, window: int) -> Swa:
-    return Swa(_ptr(codes), _ptr(scale), _ptr(start), _ptr(count), int(dim), int(window))
+    w = Swa(_ptr(codes), _ptr(scale), _ptr(start), _ptr(count), int(dim), int(window))
+    w._keep = (codes, scale, start, count)
+    return w
 
 
 # ---------------------------------------------------------------------------
@@ -225,6 +234,9 @@ class Group:
                  pool, pool_count, topk, topk_score, q_list, q_dtype, heads, swa_list, out_list, lse_list,
                  softmax_scale, new_kv=None, new_dst_row=None, w_ik=None):
         n = len(q_list)
+        # keep every tensor and descriptor the raw addresses below refer to
+        self._keep = (kv, idx, qs, q_idx, w_idx, pool, pool_count, topk, topk_score, list(q_list), list(swa_list),
+                      list(out_list), list(lse_list) if lse_list is not None else None, new_kv, new_dst_row, w_ik)
         self._q = (c_void_p * n)(*[_ptr(t) for t in q_list])
         self._swa = (Swa * n)(*swa_list)
         self._out = (c_void_p * n)(*[_ptr(t) for t in out_list])

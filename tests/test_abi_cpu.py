@@ -165,3 +165,25 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(csa2, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not built"):
         csa2.lib()
+
+
+def test_descriptors_keep_their_tensors_alive():
+    # a descriptor stores raw addresses: the tensors behind them must outlive it
+    import weakref
+    import torch
+    refs = []
+
+    def tmp(dtype):
+        x = torch.zeros(3, dtype=dtype)
+        refs.append(weakref.ref(x))
+        return x
+    c = csa2.fp4_cache(tmp(torch.uint8), tmp(torch.uint8), tmp(torch.int64), tmp(torch.int32), 128, 10, 1)
+    q = csa2.queries(tmp(torch.int32), tmp(torch.int32))
+    w = csa2.swa(tmp(torch.uint8), tmp(torch.float32), tmp(torch.int32), tmp(torch.int32), 128, 16)
+    assert all(r() is not None for r in refs)
+    g = csa2.Group(csa2.CSA2_MODE_FULL, c, c, q, tmp(torch.int16).view(1, 3), tmp(torch.float32), 4, 8,
+                   tmp(torch.int32), tmp(torch.int32), tmp(torch.int32), None, [tmp(torch.float32)], 0, 8, [w],
+                   [tmp(torch.float32)], None, 0.1)
+    del c, q, w
+    assert all(r() is not None for r in refs)
+    del g
