@@ -22,6 +22,7 @@ EXPORTS = [
     "csa2_abi_version", "csa2_status_string", "csa2_quantize_fp4", "csa2_quantize_fp8_rows",
     "csa2_dequant_fp4", "csa2_index_workspace_size", "csa2_index_full", "csa2_reindex",
     "csa2_attn_workspace_size", "csa2_sparse_swa_attn", "csa2_group_workspace_size", "csa2_group_step",
+    "csa2_profile_scan", "csa2_profile_scan_read",
 ]
 
 
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
                                            POINTER(Swa), c_float, vp, vp, vp, sz, vp]),
             "csa2_group_workspace_size": (i32, [POINTER(GroupDesc), POINTER(c_size_t)]),
             "csa2_group_step": (i32, [POINTER(GroupDesc), vp, sz, vp]),
+            "csa2_profile_scan": (i32, [i32]),
+            "csa2_profile_scan_read": (i32, [POINTER(ctypes.c_double), POINTER(c_int64)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -276,3 +279,14 @@ def csa2_group_step(group: Group, workspace, stream=None):
     _check(lib().csa2_group_step(ctypes.byref(group.desc), _ptr(workspace),
                                  int(workspace.numel()) if workspace is not None else 0, _stream(stream)),
            "csa2_group_step")
+
+
+def csa2_profile_scan(enable: bool) -> None:
+    _check(lib().csa2_profile_scan(1 if enable else 0), "csa2_profile_scan")
+
+
+def csa2_profile_scan_read() -> tuple[float, int]:
+    """(summed first-scan kernel milliseconds, launches) since profiling was enabled."""
+    ms, n = ctypes.c_double(0.0), c_int64(0)
+    _check(lib().csa2_profile_scan_read(ctypes.byref(ms), ctypes.byref(n)), "csa2_profile_scan_read")
+    return float(ms.value), int(n.value)

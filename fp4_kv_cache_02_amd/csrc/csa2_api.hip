@@ -2,7 +2,35 @@
 // dispatch.  Every check runs before anything is enqueued.
 #include "csa2_internal.hpp"
 
+#include <vector>
+
 using namespace csa2;
+
+// ---------------------------------------------------------------------------
+// scan timing records
+// ---------------------------------------------------------------------------
+namespace csa2 {
+namespace {
+bool g_prof = false;
+std::vector<hipEvent_t> g_events;   // begin/end pairs in launch order
+}  // namespace
+
+bool scan_profiling() { return g_prof; }
+
+static void record(hipStream_t stream) {
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return;
+  if (hipEventRecord(e, stream) != hipSuccess) { (void)hipEventDestroy(e); return; }
+  g_events.push_back(e);
+}
+void scan_profile_begin(hipStream_t stream) { record(stream); }
+void scan_profile_end(hipStream_t stream) { record(stream); }
+
+static void clear_events() {
+  for (hipEvent_t e : g_events) (void)hipEventDestroy(e);
+  g_events.clear();
+}
+}  // namespace csa2
 
 namespace {
 
@@ -255,6 +283,29 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
                      g->out[i], g->lse ? g->lse[i] : nullptr, workspace, s);
     if (st) return st;
   }
+  return CSA2_OK;
+}
+
+int32_t csa2_profile_scan(int32_t enable) {
+  clear_events();
+  g_prof = enable != 0;
+  return CSA2_OK;
+}
+
+int32_t csa2_profile_scan_read(double *total_ms, int64_t *launches) {
+  if (!total_ms || !launches) return CSA2_ERR_NULL_ARG;
+  double tot = 0.0;
+  int64_t n = 0;
+  for (size_t i = 0; i + 1 < g_events.size(); i += 2) {
+    if (hipEventSynchronize(g_events[i + 1]) != hipSuccess) return CSA2_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, g_events[i], g_events[i + 1]) != hipSuccess) return CSA2_ERR_HIP;
+    tot += ms;
+    ++n;
+  }
+  clear_events();
+  *total_ms = tot;
+  *launches = n;
   return CSA2_OK;
 }
 

@@ -143,6 +143,79 @@ __global__ __launch_bounds__(256) void k_quantize_fp4_derive(const T *__restrict
   }
 }
 
+// Quantise one row per workgroup and derive its indexer key, for small
+// batches (the decode write path).  1024 threads: thread -> (output column,
+// slice of the channels); every W_ik value a thread needs is loaded before
+// the fp64 dot products start, and the slices are added in slice order.
+constexpr int kRowThreads = 1024;
+
+template <typename T, int PER>
+__global__ __launch_bounds__(kRowThreads) void k_quantize_fp4_derive_row(const T *__restrict__ x, int dim,
+                                                                          const int64_t *__restrict__ dst_row,
+                                                                          uint8_t *__restrict__ codes,
+                                                                          uint8_t *__restrict__ scales,
+                                                                          const float *__restrict__ w_ik,
+                                                                          int idx_dim, uint8_t *__restrict__ ik_codes,
+                                                                          uint8_t *__restrict__ ik_scales) {
+  __shared__ float dq[kDeriveLdsFloats];
+  __shared__ double part[kRowThreads];
+  __shared__ float yk[256];
+  const int64_t r = blockIdx.x;
+  const int64_t d = dst_row ? dst_row[r] : r;
+  const int gpr = dim / kGroup;
+  const int col = threadIdx.x % idx_dim;
+  const int nparts = kRowThreads / idx_dim;
+  const int pidx = threadIdx.x / idx_dim;
+  const int c0 = pidx * PER;              // dim == PER * nparts (checked by the launcher)
+  float wv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) wv[i] = w_ik[(int64_t)(c0 + i) * idx_dim + col];
+  for (int g = threadIdx.x; g < gpr; g += blockDim.x) {
+    float v[16];
+    const T *src = x + r * dim + g * kGroup;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = load_as_f32<T>(src + i);
+    uint2 packed;
+    uint8_t sb;
+    encode_group(v, &packed, &sb);
+    *reinterpret_cast<uint2 *>(codes + d * (dim / 2) + g * 8) = packed;
+    scales[d * gpr + g] = sb;
+    const float s = e4m3_pos_value(sb);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t c = (i < 8) ? (packed.x >> (4 * i)) & 15u : (packed.y >> (4 * (i - 8))) & 15u;
+      const uint32_t m = c & 7u;
+      const float mag = (m < 4) ? 0.5f * (float)m : (float)(1u << ((m - 2) >> 1)) * ((m & 1u) ? 1.5f : 1.0f);
+      const float val = mag * s;
+      dq[g * kGroup + i] = (c & 8u) ? -val : val;
+    }
+  }
+  __syncthreads();
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc = fma((double)dq[c0 + i], (double)wv[i], acc);
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x < idx_dim) {
+    double t = 0.0;
+    for (int k = 0; k < nparts; ++k) t += part[k * idx_dim + threadIdx.x];
+    yk[threadIdx.x] = (float)t;
+  }
+  __syncthreads();
+  const int igpr = idx_dim / kGroup;
+  if (threadIdx.x < igpr) {
+    const int g = threadIdx.x;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = yk[g * kGroup + i];
+    uint2 packed;
+    uint8_t sb;
+    encode_group(v, &packed, &sb);
+    *reinterpret_cast<uint2 *>(ik_codes + d * (idx_dim / 2) + g * 8) = packed;
+    ik_scales[d * igpr + g] = sb;
+  }
+}
+
 // FP8 window rows: one workgroup per row.
 template <typename T>
 __global__ __launch_bounds__(256) void k_quantize_fp8_rows(const T *__restrict__ x, int dim,
@@ -206,6 +279,22 @@ int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const
     else
       hipLaunchKernelGGL(k_quantize_fp4<uint16_t>, grid, dim3(256), 0, stream, (const uint16_t *)x, rows, dim,
                          dst_row, codes, scales);
+  } else if (rows <= 1024 && dim % (kRowThreads / idx_dim) == 0 &&
+             (dim / (kRowThreads / idx_dim) == 8 || dim / (kRowThreads / idx_dim) == 16 ||
+              dim / (kRowThreads / idx_dim) == 32 || dim / (kRowThreads / idx_dim) == 64)) {
+    const dim3 grid((unsigned)rows);
+    const int per = dim / (kRowThreads / idx_dim);
+#define CSA2_ROW_LAUNCH(T, PERV)                                                                                  \
+    hipLaunchKernelGGL((k_quantize_fp4_derive_row<T, PERV>), grid, dim3(kRowThreads), 0, stream, (const T *)x, dim, \
+                       dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales)
+    if (x_dtype == CSA2_F32) {
+      if (per == 8) CSA2_ROW_LAUNCH(float, 8); else if (per == 16) CSA2_ROW_LAUNCH(float, 16);
+      else if (per == 32) CSA2_ROW_LAUNCH(float, 32); else CSA2_ROW_LAUNCH(float, 64);
+    } else {
+      if (per == 8) CSA2_ROW_LAUNCH(uint16_t, 8); else if (per == 16) CSA2_ROW_LAUNCH(uint16_t, 16);
+      else if (per == 32) CSA2_ROW_LAUNCH(uint16_t, 32); else CSA2_ROW_LAUNCH(uint16_t, 64);
+    }
+#undef CSA2_ROW_LAUNCH
   } else {
     const int rb = kDeriveLdsFloats / dim;
     const dim3 grid((unsigned)((rows + rb - 1) / rb));

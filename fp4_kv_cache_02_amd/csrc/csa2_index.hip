@@ -19,8 +19,8 @@
 
 namespace csa2 {
 
-constexpr int kScanTiles = 128;                  // 16-position tiles per scan workgroup
-constexpr int kScanChunk = kScanTiles * 16;      // 2048 positions
+constexpr int kScanTiles = 256;                  // 16-position tiles per scan workgroup
+constexpr int kScanChunk = kScanTiles * 16;      // 4096 positions
 constexpr int kScanBlocks = kScanChunk / kBlock; // 256 block maxima
 constexpr int kFilterBlocks = 1024;              // blocks per pool-filter workgroup
 constexpr int kRescoreEntries = 64;              // pool blocks per re-score workgroup
@@ -45,7 +45,8 @@ CSA2_DEV float max_rows4(float v) {
   return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
 }
 
-// q: [H][DI] bf16 of this query, w: [H] fp32.
+// q: [H][DI] bf16 of this query, w: [H] fp32.  Lane (m, qq) loads the DI/4
+// contiguous channels it feeds to MFMA with 16-byte loads.
 template <int DI>
 CSA2_DEV void load_idx_query(const uint16_t *__restrict__ q, const float *__restrict__ w, int H,
                              IdxQuery<DI> &Q) {
@@ -54,11 +55,19 @@ CSA2_DEV void load_idx_query(const uint16_t *__restrict__ q, const float *__rest
   constexpr int PER = DI / 4;
   float v[PER];
   float mx = 0.0f;
+  const uint4 *src = reinterpret_cast<const uint4 *>(q + m * DI + qq * PER);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    v[i] = (m < H) ? bf16_to_f32(q[m * DI + qq * PER + i]) : 0.0f;
-    mx = fmaxf(mx, fabsf(v[i]));
+  for (int k = 0; k < PER / 8; ++k) {
+    const uint4 x = (m < H) ? src[k] : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t wds[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[8 * k + 2 * i] = __uint_as_float(wds[i] << 16);
+      v[8 * k + 2 * i + 1] = __uint_as_float(wds[i] & 0xFFFF0000u);
+    }
   }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) mx = fmaxf(mx, fabsf(v[i]));
   mx = max_rows4(mx);
   int e = 0;
   (void)frexpf(mx, &e);
@@ -159,7 +168,46 @@ __global__ void k_zero_u32(uint32_t *__restrict__ p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
-// First scan: grid (chunks, queries), 4 waves, 2048 positions per workgroup.
+// Radix digit search shared by the selection kernels: s_hist[256] holds the
+// counts of one 8-bit digit; find the digit v (scanning from 255 down) whose
+// bin holds the rem-th largest element.  Run by wave 0; writes the digit, the
+// rank left inside its bin, and the bin count.
+CSA2_DEV void find_digit(const uint32_t *s_hist, int rem, int *s_digit, int *s_rem, int *s_cnt) {
+  if (threadIdx.x >= 64) return;
+  const int l = threadIdx.x;
+  int h[4];
+  int local = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = (int)s_hist[255 - 4 * l - e];
+    local += h[e];
+  }
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (l >= off) incl += y;
+  }
+  int excl = incl - local;
+  if (excl < rem && incl >= rem) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (excl + h[e] >= rem) {
+        *s_digit = 255 - 4 * l - e;
+        *s_rem = rem - excl;
+        *s_cnt = h[e];
+        break;
+      }
+      excl += h[e];
+    }
+  }
+}
+
+// First scan: grid (chunks, queries), 4 waves, 4096 positions per workgroup.
+// Each wave streams 64 tiles in batches of U with the next batch's loads in
+// flight while the current batch is scored.
+constexpr int kScanU = 8;
+
 template <int DI>
 __global__ __launch_bounds__(256) void k_scan(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                               const int64_t *__restrict__ seq_start,
@@ -169,37 +217,55 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t *__restrict__ codes,
                                               int H, float *__restrict__ bmax, int64_t nb_stride,
                                               uint32_t *__restrict__ hist) {
   __shared__ float s_bmax[kScanBlocks];
-  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
   const int m = blockIdx.y;
   int s;
   const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
   const int64_t p_begin = (int64_t)blockIdx.x * kScanChunk;
   if (p_begin >= vis) return;
-  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) s_hist[i] = 0u;
+  for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x)
+    reinterpret_cast<uint4 *>(s_hist)[i] = make_uint4(0u, 0u, 0u, 0u);
 
   IdxQuery<DI> Q;
   load_idx_query<DI>(q_idx + (int64_t)m * H * DI, w_idx + (int64_t)m * H, H, Q);
 
   const int64_t row0 = seq_start[s];
   const int l = lane_id(), n = l & 15, qq = l >> 4, wv = threadIdx.x >> 6;
-  constexpr int U = 4;
-  for (int it = 0; it < kScanTiles / (4 * U); ++it) {
-    LaneCodes<DI> c[U];
+  constexpr int U = kScanU;
+  constexpr int NB = kScanTiles / 4 / U;  // batches per wave
+  const int64_t last = vis - 1;
+  // tile of batch b, slot u: (b*U + u)*4 + wv; a batch is live if its first tile starts before vis
+  auto live = [&](int b) { return p_begin + (int64_t)((b * U) * 4 + wv) * 16 < vis; };
+  auto load = [&](int b, LaneCodes<DI> *c) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int tile = (it * U + u) * 4 + wv;
-      const int64_t p = p_begin + tile * 16 + n;
-      load_lane_codes<DI>(codes, scales, row0 + min(p, vis - 1), qq, c[u]);
+      const int64_t p = p_begin + (int64_t)((b * U + u) * 4 + wv) * 16 + n;
+      load_lane_codes<DI>(codes, scales, row0 + min(p, last), qq, c[u]);
     }
+  };
+  auto score = [&](int b, const LaneCodes<DI> *c) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int tile = (it * U + u) * 4 + wv;
-      const int64_t p = p_begin + tile * 16 + n;
+      const int tile = (b * U + u) * 4 + wv;
+      const int64_t p = p_begin + (int64_t)tile * 16 + n;
       float sc = tile_score<DI>(Q, c[u]);
       if (p >= vis) sc = -INFINITY;
       const float bm = max8_lanes(sc);
       if (l == 0 || l == 8) s_bmax[tile * 2 + (l >> 3)] = bm;
     }
+  };
+  LaneCodes<DI> A[U], B[U];
+  if (live(0)) load(0, A);
+  for (int b = 0; b < NB; b += 2) {
+    if (!live(b)) break;
+    const bool l1 = (b + 1 < NB) && live(b + 1);
+    if (l1) load(b + 1, B);
+    score(b, A);
+    if (!l1) break;
+    const bool l2 = (b + 2 < NB) && live(b + 2);
+    if (l2) load(b + 2, A);
+    score(b + 1, B);
+    if (!l2) break;
   }
   __syncthreads();
   const int nb_here = (int)min<int64_t>(kScanBlocks, (vis - p_begin + kBlock - 1) / kBlock);
@@ -210,27 +276,30 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t *__restrict__ codes,
     atomicAdd(&s_hist[f2key(v) >> (32 - kHistBits)], 1u);
   }
   __syncthreads();
+  // flush: the first block of each bin to arrive moves the bin's count out
   uint32_t *gh = hist + (int64_t)m * kHistBins;
-  for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) {
-    const uint32_t cnt = s_hist[b];
-    if (cnt) atomicAdd(&gh[b], cnt);
+  for (int i = threadIdx.x; i < nb_here; i += blockDim.x) {
+    const uint32_t bin = f2key(s_bmax[i]) >> (32 - kHistBits);
+    const uint32_t cnt = atomicExch(&s_hist[bin], 0u);
+    if (cnt) atomicAdd(&gh[bin], cnt);
   }
 }
 
-// Wave-aggregated append of `pred` lanes to list[*counter ...].
-CSA2_DEV void wave_append(bool pred, int32_t value, uint32_t *counter, int32_t *list) {
+// Wave-aggregated append of the `pred` lanes to list[*counter ...].
+CSA2_DEV void wave_append(bool pred, int32_t value, int *counter, int32_t *list) {
   const uint64_t mask = __ballot(pred);
   if (!mask) return;
   const int l = lane_id();
   const int leader = __ffsll((unsigned long long)mask) - 1;
-  uint32_t base = 0;
-  if (l == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
+  int base = 0;
+  if (l == leader) base = atomicAdd(counter, (int)__popcll(mask));
   base = __shfl(base, leader, 64);
   if (pred) list[base + __popcll(mask & ((1ull << l) - 1ull))] = value;
 }
 
 // Pool filter: threshold bin from the histogram; blocks above it are in the
-// pool for sure, blocks in it go to the tie list.
+// pool for sure, blocks in it go to the tie list.  Appends are gathered in
+// LDS and reserved in the global lists with one atomic per list per workgroup.
 __global__ __launch_bounds__(256) void k_pool_filter(const float *__restrict__ bmax, int64_t nb_stride,
                                                      const uint32_t *__restrict__ hist,
                                                      const int32_t *__restrict__ seq_len, const int32_t *__restrict__ q_seq,
@@ -238,7 +307,8 @@ __global__ __launch_bounds__(256) void k_pool_filter(const float *__restrict__ b
                                                      uint32_t *__restrict__ counters, int32_t *__restrict__ sure,
                                                      int32_t *__restrict__ tie) {
   __shared__ int s_scan[8];
-  __shared__ int s_T;
+  __shared__ int s_T, s_ns, s_nt, s_bs, s_bt;
+  __shared__ int32_t s_sure[kFilterBlocks], s_tie[kFilterBlocks];
   const int m = blockIdx.y;
   int s;
   const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
@@ -246,38 +316,59 @@ __global__ __launch_bounds__(256) void k_pool_filter(const float *__restrict__ b
   const int64_t b0 = (int64_t)blockIdx.x * kFilterBlocks;
   if (b0 >= nb) return;
   const int64_t need = min<int64_t>(P, nb);
+  if (threadIdx.x == 0) { s_T = -1; s_ns = 0; s_nt = 0; }
   int T = -1;
   if (nb > P) {
     const uint32_t *h = hist + (int64_t)m * kHistBins;
     // thread t owns bins [4096-16(t+1), 4096-16t) (thread 0 = highest bins)
     const int hi = kHistBins - 16 * threadIdx.x;
+    const uint4 *h4 = reinterpret_cast<const uint4 *>(h + hi - 16);
+    int hv[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 x = h4[k];
+      hv[4 * k] = (int)x.x; hv[4 * k + 1] = (int)x.y; hv[4 * k + 2] = (int)x.z; hv[4 * k + 3] = (int)x.w;
+    }
     int c = 0;
-    for (int b = hi - 16; b < hi; ++b) c += (int)h[b];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) c += hv[k];
     int tot;
     const int before = block_exclusive_scan<256>(c, s_scan, &tot);
     if (before < need && before + c >= need) {
       int cum = before;
-      for (int b = hi - 1; b >= hi - 16; --b) {
-        cum += (int)h[b];
-        if (cum >= need) { s_T = b; break; }
+      for (int k = 15; k >= 0; --k) {
+        cum += hv[k];
+        if (cum >= need) { s_T = hi - 16 + k; break; }
       }
     }
-    __syncthreads();
-    T = s_T;
   }
+  __syncthreads();
+  T = s_T;
   const float *bm = bmax + (int64_t)m * nb_stride;
   for (int j = 0; j < kFilterBlocks / 256; ++j) {
     const int64_t b = b0 + j * 256 + threadIdx.x;
     const bool ok = b < nb;
-    const int bin = ok ? (int)(f2key(bm[ok ? b : 0]) >> (32 - kHistBits)) : -2;
-    wave_append(ok && bin > T, (int32_t)b, counters + m * 4 + 0, sure + (int64_t)m * P);
-    wave_append(ok && bin == T, (int32_t)b, counters + m * 4 + 1, tie + (int64_t)m * nb_stride);
+    const int bin = ok ? (int)(f2key(bm[b]) >> (32 - kHistBits)) : -2;
+    wave_append(ok && bin > T, (int32_t)b, &s_ns, s_sure);
+    wave_append(ok && bin == T, (int32_t)b, &s_nt, s_tie);
   }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    s_bs = s_ns ? (int)atomicAdd(&counters[m * 4 + 0], (uint32_t)s_ns) : 0;
+    s_bt = s_nt ? (int)atomicAdd(&counters[m * 4 + 1], (uint32_t)s_nt) : 0;
+  }
+  __syncthreads();
+  int32_t *su = sure + (int64_t)m * P + s_bs;
+  int32_t *ti = tie + (int64_t)m * nb_stride + s_bt;
+  for (int i = threadIdx.x; i < s_ns; i += blockDim.x) su[i] = s_sure[i];
+  for (int i = threadIdx.x; i < s_nt; i += blockDim.x) ti[i] = s_tie[i];
 }
 
 // Pool finalisation, one workgroup per query: resolve the boundary bin
-// exactly on (key desc, block asc), then sort the pool ascending.
+// exactly on (key desc, block asc), then emit the pool in ascending block
+// order by compacting a bitmap of the chosen blocks.
 constexpr int kMaxPool = 4096;
+constexpr int kBitmapWords = 16384;  // blocks up to 2^19 go through the bitmap
 
 __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict__ bmax, int64_t nb_stride,
                                                         const uint32_t *__restrict__ counters,
@@ -288,26 +379,36 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
                                                         const int32_t *__restrict__ q_pos, int ratio, int P,
                                                         int32_t *__restrict__ pool_out,
                                                         int32_t *__restrict__ pool_count) {
+  __shared__ uint32_t s_bits[kBitmapWords];
   __shared__ int32_t s_pool[kMaxPool];
   __shared__ uint32_t s_h[256];
-  __shared__ int s_digit, s_rem, s_cnt;
+  __shared__ int s_scan[17];
+  __shared__ int s_digit, s_rem, s_cnt, s_n;
   const int m = blockIdx.x;
   int s;
   const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
   const int64_t nb = (vis + kBlock - 1) / kBlock;
-  const int need = (int)min<int64_t>(P, nb);
   const int n_sure = (int)counters[m * 4 + 0];
   const int n_tie = (int)counters[m * 4 + 1];
+  const int need = (int)min<int64_t>(min<int64_t>(P, nb), (int64_t)n_sure + n_tie);
   const int need_t = need - n_sure;
   const int32_t *su = sure + (int64_t)m * P;
   const int32_t *ti = tie + (int64_t)m * nb_stride;
   const float *bm = bmax + (int64_t)m * nb_stride;
-  for (int i = threadIdx.x; i < n_sure; i += blockDim.x) s_pool[i] = su[i];
-  if (threadIdx.x == 0) s_cnt = 0;
+  const bool use_bits = nb <= 32 * (int64_t)kBitmapWords;
+  const int words = (int)((nb + 31) / 32);
+  if (use_bits)
+    for (int i = threadIdx.x; i < words; i += blockDim.x) s_bits[i] = 0u;
+  if (threadIdx.x == 0) s_n = 0;
   __syncthreads();
+  auto take = [&](int32_t b) {
+    if (use_bits) atomicOr(&s_bits[b >> 5], 1u << (b & 31));
+    else s_pool[atomicAdd(&s_n, 1)] = b;
+  };
+  for (int i = threadIdx.x; i < n_sure; i += blockDim.x) take(su[i]);
   if (need_t > 0) {
     if (need_t >= n_tie) {
-      for (int i = threadIdx.x; i < n_tie; i += blockDim.x) s_pool[n_sure + i] = ti[i];
+      for (int i = threadIdx.x; i < n_tie; i += blockDim.x) take(ti[i]);
     } else {
       // composite key: larger score first, then smaller block id
       uint64_t prefix = 0, mask = 0;
@@ -322,52 +423,68 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
           if ((c & mask) == prefix) atomicAdd(&s_h[(c >> shift) & 255u], 1u);
         }
         __syncthreads();
-        if (threadIdx.x == 0) {
-          int cum = 0;
-          for (int v = 255; v >= 0; --v) {
-            const int hv = (int)s_h[v];
-            if (cum + hv >= rem) { s_digit = v; s_rem = rem - cum; break; }
-            cum += hv;
-          }
-        }
+        find_digit(s_h, rem, &s_digit, &s_rem, &s_cnt);
         __syncthreads();
         prefix |= (uint64_t)s_digit << shift;
         mask |= (uint64_t)255 << shift;
         rem = s_rem;
-        __syncthreads();
       }
       for (int i = threadIdx.x; i < n_tie; i += blockDim.x) {
         const int32_t b = ti[i];
         const uint64_t c = ((uint64_t)f2key(bm[b]) << 32) | (uint64_t)(~(uint32_t)b);
-        if (c >= prefix) s_pool[n_sure + atomicAdd(&s_cnt, 1)] = b;
+        if (c >= prefix) take(b);
       }
     }
   }
   __syncthreads();
-  int n2 = 64;
-  while (n2 < need) n2 <<= 1;
-  for (int i = need + threadIdx.x; i < n2; i += blockDim.x) s_pool[i] = 0x7FFFFFFF;
-  __syncthreads();
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n2; i += blockDim.x) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int32_t a = s_pool[i], b = s_pool[ixj];
-          const bool up = (i & k) == 0;
-          if ((a > b) == up) { s_pool[i] = b; s_pool[ixj] = a; }
-        }
-      }
-      __syncthreads();
-    }
-  }
   int32_t *out = pool_out + (int64_t)m * P;
-  for (int i = threadIdx.x; i < P; i += blockDim.x) out[i] = (i < need) ? s_pool[i] : -1;
+  if (use_bits) {
+    // thread t compacts words [t*wpt, (t+1)*wpt)
+    const int wpt = (words + 1023) / 1024;
+    int cnt = 0;
+    for (int k = 0; k < wpt; ++k) {
+      const int w = threadIdx.x * wpt + k;
+      if (w < words) cnt += __popc(s_bits[w]);
+    }
+    int tot;
+    int pos = block_exclusive_scan<1024>(cnt, s_scan, &tot);
+    for (int k = 0; k < wpt; ++k) {
+      const int w = threadIdx.x * wpt + k;
+      if (w >= words) break;
+      uint32_t bits = s_bits[w];
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1;
+        out[pos++] = w * 32 + bit;
+      }
+    }
+  } else {
+    int n2 = 64;
+    while (n2 < need) n2 <<= 1;
+    for (int i = need + threadIdx.x; i < n2; i += blockDim.x) s_pool[i] = 0x7FFFFFFF;
+    __syncthreads();
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = threadIdx.x; i < n2; i += blockDim.x) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const int32_t a = s_pool[i], b = s_pool[ixj];
+            const bool up = (i & k) == 0;
+            if ((a > b) == up) { s_pool[i] = b; s_pool[ixj] = a; }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = threadIdx.x; i < need; i += blockDim.x) out[i] = s_pool[i];
+  }
+  for (int i = need + threadIdx.x; i < P; i += blockDim.x) out[i] = -1;
   if (threadIdx.x == 0) pool_count[m] = need;
 }
 
 // Re-score the positions of 64 pool blocks per workgroup.  Slot 8*e + r of a
 // query holds the score of position 8*pool[e] + r (-inf when not visible).
+// Each wave first loads its pool entries, then all its rows, then scores.
 template <int DI>
 __global__ __launch_bounds__(256) void k_rescore(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                                  const int64_t *__restrict__ seq_start,
@@ -390,20 +507,28 @@ __global__ __launch_bounds__(256) void k_rescore(const uint8_t *__restrict__ cod
       if (e0 * 8 + i < 8 * cnt) ps[e0 * 8 + i] = -INFINITY;
     return;
   }
-  IdxQuery<DI> Q;
-  load_idx_query<DI>(q_idx + (int64_t)m * H * DI, w_idx + (int64_t)m * H, H, Q);
   const int64_t row0 = seq_start[s];
   const int32_t *pl = pool + (int64_t)m * P;
-  constexpr int TILES = kRescoreEntries / 2;
-  for (int t = wv; t < TILES; t += 4) {
-    const int e = e0 + 2 * t + (n >> 3);
+  constexpr int TPW = kRescoreEntries / 2 / 4;  // tiles per wave
+  int64_t pos[TPW];
+  bool valid[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int e = e0 + 2 * (wv + 4 * k) + (n >> 3);
     const int32_t blk = (e < cnt) ? pl[e] : -1;
-    const int64_t pos = (int64_t)blk * kBlock + (n & 7);
-    const bool valid = blk >= 0 && pos < vis;
-    LaneCodes<DI> c;
-    load_lane_codes<DI>(codes, scales, row0 + (valid ? pos : 0), qq, c);
-    float sc = tile_score<DI>(Q, c);
-    if (!valid) sc = -INFINITY;
+    pos[k] = (int64_t)blk * kBlock + (n & 7);
+    valid[k] = blk >= 0 && pos[k] < vis;
+  }
+  LaneCodes<DI> c[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) load_lane_codes<DI>(codes, scales, row0 + (valid[k] ? pos[k] : 0), qq, c[k]);
+  IdxQuery<DI> Q;
+  load_idx_query<DI>(q_idx + (int64_t)m * H * DI, w_idx + (int64_t)m * H, H, Q);
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int e = e0 + 2 * (wv + 4 * k) + (n >> 3);
+    float sc = tile_score<DI>(Q, c[k]);
+    if (!valid[k]) sc = -INFINITY;
     if (qq == 0 && e < cnt) ps[8 * e + (n & 7)] = sc;
   }
 }
@@ -411,28 +536,43 @@ __global__ __launch_bounds__(256) void k_rescore(const uint8_t *__restrict__ cod
 // Top-K over the re-scored pool, one workgroup (1024 threads) per query.
 // Thread t owns slots [t*PER, (t+1)*PER); slot order equals position order
 // because the pool is ascending, so ties on the score resolve to the lower
-// slot and the compaction below emits positions in ascending order.
+// slot and the compaction below emits positions in ascending order.  Radix
+// passes count into one 256-bin histogram per wave, then merge.
 template <int PER>
 __global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ pscore,
                                                       const int32_t *__restrict__ pool,
                                                       const int32_t *__restrict__ pool_count, int P, int K,
                                                       int32_t *__restrict__ topk_out, float *__restrict__ topk_score) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_wh[16 * 256];
   __shared__ uint32_t s_h[256];
   __shared__ int s_scan[17];
-  __shared__ int s_digit, s_rem;
+  __shared__ int s_digit, s_rem, s_cnt;
   const int m = blockIdx.x;
+  const int wv = threadIdx.x >> 6;
   const int cnt = min(pool_count[m], P);
   const int nslots = 8 * cnt;
   const float *ps = pscore + (int64_t)m * 8 * P;
   uint32_t key[PER];
   int nvalid = 0;
+  if ((threadIdx.x + 1) * PER <= nslots) {
+    const float4 *src = reinterpret_cast<const float4 *>(ps + threadIdx.x * PER);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int slot = threadIdx.x * PER + i;
-    const float v = (slot < nslots) ? ps[slot] : -INFINITY;
-    key[i] = (v > -INFINITY) ? f2key(v) : 0u;
-    nvalid += key[i] != 0u;
+    for (int k = 0; k < PER / 4; ++k) {
+      const float4 v = src[k];
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) key[4 * k + i] = (vv[i] > -INFINITY) ? f2key(vv[i]) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int slot = threadIdx.x * PER + i;
+      const float v = (slot < nslots) ? ps[slot] : -INFINITY;
+      key[i] = (v > -INFINITY) ? f2key(v) : 0u;
+    }
   }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) nvalid += key[i] != 0u;
   int total;
   (void)block_exclusive_scan<1024>(nvalid, s_scan, &total);
   const int Kp = min(K, total);
@@ -444,25 +584,26 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ 
     uint32_t prefix = 0, mask = 0;
     rem = Kp;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = threadIdx.x; i < 256; i += blockDim.x) s_h[i] = 0u;
+      for (int i = threadIdx.x; i < 16 * 256 / 4; i += blockDim.x)
+        reinterpret_cast<uint4 *>(s_wh)[i] = make_uint4(0u, 0u, 0u, 0u);
       __syncthreads();
+      uint32_t *wh = s_wh + wv * 256;
 #pragma unroll
       for (int i = 0; i < PER; ++i)
-        if (key[i] != 0u && (key[i] & mask) == prefix) atomicAdd(&s_h[(key[i] >> shift) & 255u], 1u);
+        if (key[i] != 0u && (key[i] & mask) == prefix) atomicAdd(&wh[(key[i] >> shift) & 255u], 1u);
       __syncthreads();
-      if (threadIdx.x == 0) {
-        int cum = 0;
-        for (int v = 255; v >= 0; --v) {
-          const int hv = (int)s_h[v];
-          if (cum + hv >= rem) { s_digit = v; s_rem = rem - cum; break; }
-          cum += hv;
-        }
+      if (threadIdx.x < 256) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) t += s_wh[w * 256 + threadIdx.x];
+        s_h[threadIdx.x] = t;
       }
+      __syncthreads();
+      find_digit(s_h, rem, &s_digit, &s_rem, &s_cnt);
       __syncthreads();
       prefix |= (uint32_t)s_digit << shift;
       mask |= 255u << shift;
       rem = s_rem;
-      __syncthreads();
     }
     kstar = prefix;
   }
@@ -476,13 +617,13 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ 
   int nsel = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    bool take = false;
+    bool takeit = false;
     if (Kp > 0 && key[i] != 0u) {
-      if (key[i] > kstar) take = true;
-      else if (key[i] == kstar) { take = eq_before < rem; ++eq_before; }
+      if (key[i] > kstar) takeit = true;
+      else if (key[i] == kstar) { takeit = eq_before < rem; ++eq_before; }
     }
-    sel[i] = take;
-    nsel += take;
+    sel[i] = takeit;
+    nsel += takeit;
   }
   int rank = block_exclusive_scan<1024>(nsel, s_scan, &tmp);
   const int32_t *pl = pool + (int64_t)m * P;
@@ -556,10 +697,14 @@ static int index_full_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
   const int64_t nz = (int64_t)((L.sure - L.hist) / sizeof(uint32_t));
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
   const int64_t chunks = (idx.max_len + kScanChunk - 1) / kScanChunk;
-  if (chunks > 0)
+  if (chunks > 0) {
+    const bool prof = scan_profiling();
+    if (prof) scan_profile_begin(stream);
     hipLaunchKernelGGL(k_scan<DI>, dim3((unsigned)chunks, qs.m), dim3(256), 0, stream, idx.codes, idx.scales,
                        idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, q_idx, w_idx, heads, bmax, L.nb_max,
                        hist);
+    if (prof) scan_profile_end(stream);
+  }
   const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);
   hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, hist, idx.seq_len, qs.seq, qs.pos,
                      idx.ratio, P, counters, sure, tie);

@@ -45,4 +45,9 @@ int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q,
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// ---- scan timing (csa2_api.hip) ----
+bool scan_profiling();
+void scan_profile_begin(hipStream_t stream);
+void scan_profile_end(hipStream_t stream);
+
 }  // namespace csa2

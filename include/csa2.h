@@ -282,6 +282,21 @@ typedef struct csa2_group_desc {
 int32_t csa2_group_workspace_size(const csa2_group_desc *g, size_t *bytes);
 int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------
+ * csa2_profile_scan / csa2_profile_scan_read - timing of the Full layer's
+ * first scan (the step whose cost grows with the context, P4 section 二).
+ * While enabled, every first-scan kernel launched by csa2_index_full /
+ * csa2_group_step is bracketed by two HIP events recorded on its launch
+ * stream.  enable != 0 clears earlier records and starts recording; 0 stops.
+ * _read waits for the recorded events and returns the summed kernel time in
+ * milliseconds and the number of launches, then clears the records.  For
+ * measurement only; recording is host-side bookkeeping, not thread-safe
+ * with concurrent recording calls on other threads.
+ * Errors: NULL_ARG (read with a NULL output), HIP.
+ * ------------------------------------------------------------------- */
+int32_t csa2_profile_scan(int32_t enable);
+int32_t csa2_profile_scan_read(double *total_ms, int64_t *launches);
+
 #ifdef __cplusplus
 }
 #endif

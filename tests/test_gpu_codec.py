@@ -86,10 +86,12 @@ def test_quantize_bf16_input_and_scattered_rows():
     assert np.all(gc[untouched] == 0) and np.all(gs[untouched] == 0)
 
 
-@pytest.mark.parametrize("dim,di", [(128, 64), (512, 128), (256, 256)])
-def test_derive_indexer_key_bit_exact(dim, di):
-    announce("derive indexer key", dim, di)
-    x = synth.main_kv_rows(0, 0, 0, 2000, dim)
+@pytest.mark.parametrize("dim,di,rows", [(128, 64, 2000), (512, 128, 2000), (256, 256, 2000), (512, 128, 5),
+                                         (512, 128, 1024), (128, 64, 3)])
+def test_derive_indexer_key_bit_exact(dim, di, rows):
+    # up to 1024 rows take the one-row-per-workgroup path, more the multi-row path
+    announce("derive indexer key", dim, di, rows)
+    x = synth.main_kv_rows(0, 0, 0, rows, dim)
     w = synth.w_ik(0, dim, di)
     codes, scales, ikc, iks = gpu_quantize(x, w)
     rc, rs = codec.fp4_encode(x)
