@@ -19,9 +19,10 @@
 
 namespace csa2 {
 
-constexpr int kScanTiles = 256;                  // 16-position tiles per scan workgroup
-constexpr int kScanChunk = kScanTiles * 16;      // 4096 positions
-constexpr int kScanBlocks = kScanChunk / kBlock; // 256 block maxima
+constexpr int kScanWaves = 8;                    // waves per scan workgroup
+constexpr int kScanTiles = 1024;                 // 16-position tiles per scan workgroup (largest chunk)
+constexpr int kScanChunk = kScanTiles * 16;      // 16384 positions
+constexpr int kScanBlocks = kScanChunk / kBlock; // 2048 block maxima
 constexpr int kFilterBlocks = 1024;              // blocks per pool-filter workgroup
 constexpr int kRescoreEntries = 64;              // pool blocks per re-score workgroup
 
@@ -122,9 +123,25 @@ CSA2_DEV void load_lane_codes(const uint8_t *__restrict__ codes, const uint8_t *
   }
 }
 
-// Score of position (lane % 16) of the tile, returned in all four quarters.
+// max(x, 0) and max(a, b) as one v_med3_f32 each.  Scores are finite or
+// -inf (never NaN), and for such values the median with FLT_MAX is exactly
+// the maximum; fmaxf would add NaN canonicalisations (and a +inf bound is
+// folded back into fmaxf by the compiler).
+CSA2_DEV float relu_f(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.40282347e38f); }
+CSA2_DEV float max_f(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, 3.40282347e38f); }
+
+// max over the 8 lanes of each half-row (finite or -inf values)
+CSA2_DEV float max8_scores(float v) {
+  v = max_f(v, dpp_f<kDppXor1>(v));
+  v = max_f(v, dpp_f<kDppXor2>(v));
+  return max_f(v, dpp_f<kDppHalfMirror>(v));
+}
+
+// This lane's share of the score of position (lane % 16) of the tile: the
+// weighted ReLU of its four heads 4*(lane/16) + j.  The score is the sum of
+// the four quarters' shares, added as (q0 + q2) + (q1 + q3).
 template <int DI>
-CSA2_DEV float tile_score(const IdxQuery<DI> &Q, const LaneCodes<DI> &c) {
+CSA2_DEV float tile_partial(const IdxQuery<DI> &Q, const LaneCodes<DI> &c) {
   _Float16 sc[(DI / 64 > 0) ? DI / 64 : 1];
   if constexpr (DI == 64) {
     sc[0] = e4m3x2_to_f16(c.s)[0];
@@ -143,11 +160,63 @@ CSA2_DEV float tile_score(const IdxQuery<DI> &Q, const LaneCodes<DI> &c) {
     const half8_t b = fp4x8_dequant_f16(c.w[t], sc[t / 2]);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Q.a[t], b, acc, 0, 0, 0);
   }
-  float part = Q.w[0] * fmaxf(acc[0], 0.0f);
-  part = fmaf(Q.w[1], fmaxf(acc[1], 0.0f), part);
-  part = fmaf(Q.w[2], fmaxf(acc[2], 0.0f), part);
-  part = fmaf(Q.w[3], fmaxf(acc[3], 0.0f), part);
-  return sum_rows4(part);
+  float part = Q.w[0] * relu_f(acc[0]);
+  part = fmaf(Q.w[1], relu_f(acc[1]), part);
+  part = fmaf(Q.w[2], relu_f(acc[2]), part);
+  part = fmaf(Q.w[3], relu_f(acc[3]), part);
+  return part;
+}
+
+// Score of position (lane % 16) of the tile, returned in all four quarters.
+template <int DI>
+CSA2_DEV float tile_score(const IdxQuery<DI> &Q, const LaneCodes<DI> &c) {
+  return sum_rows4(tile_partial<DI>(Q, c));
+}
+
+// Scores of four tiles from their lane shares p0..p3 with three lane swaps:
+// row r (lanes 16r .. 16r+15) returns the 16 scores of tile kRowTile[r].
+// Same addition order as sum_rows4, so scores match tile_score bit for bit.
+CSA2_DEV int row_tile(int row) { return ((row & 1) << 1) | (row >> 1); }  // rows hold tiles 0, 2, 1, 3
+CSA2_DEV float tile_scores_x4(float p0, float p1, float p2, float p3) {
+  // permlane32_swap(x, y): x keeps its low half and takes y's low half; y takes x's high half
+  const auto a2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+  const float a = __uint_as_float(a2[0]) + __uint_as_float(a2[1]);   // [t0 q0+q2, t0 q1+q3, t1 .., t1 ..]
+  const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p2), __float_as_uint(p3), false, false);
+  const float b = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);   // same for tiles 2, 3
+  // permlane16_swap(x, y): odd rows of x trade places with even rows of y
+  const auto c2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(c2[0]) + __uint_as_float(c2[1]);
+}
+
+// Loads of one lane relative to a chunk: `row` counts from the chunk's first
+// entry, so the offsets stay 32-bit and the bases stay scalar.  The scan
+// reads every byte exactly once, so the loads are non-temporal (streamed
+// past the caches), which lifts the achievable HBM read rate.
+template <int DI>
+CSA2_DEV void load_lane_codes_rel(const uint8_t *__restrict__ cbase, const uint8_t *__restrict__ sbase,
+                                  uint32_t row, uint32_t qq, LaneCodes<DI> &c) {
+  const uint32_t co = row * (DI / 2) + qq * (DI / 8);
+  const uint32_t so = row * (DI / 16) + qq * (DI / 64);
+  if constexpr (DI == 64) {
+    const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(cbase + co));
+    c.w[0] = x[0];
+    c.w[1] = x[1];
+    c.s = __builtin_nontemporal_load(sbase + so);
+  } else if constexpr (DI == 128) {
+    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cbase + co));
+    c.w[0] = x[0];
+    c.w[1] = x[1];
+    c.w[2] = x[2];
+    c.w[3] = x[3];
+    c.s = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(sbase + so));
+  } else {
+    static_assert(DI == 256, "indexer dim");
+    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cbase + co));
+    const u32x4_t y = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cbase + co + 16));
+    c.w[0] = x[0]; c.w[1] = x[1]; c.w[2] = x[2]; c.w[3] = x[3];
+    c.w[4] = y[0]; c.w[5] = y[1]; c.w[6] = y[2]; c.w[7] = y[3];
+    c.s = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sbase + so));
+  }
 }
 
 CSA2_DEV int64_t visible_entries(const int32_t *seq_len, const int32_t *q_seq, const int32_t *q_pos, int ratio,
@@ -203,25 +272,40 @@ CSA2_DEV void find_digit(const uint32_t *s_hist, int rem, int *s_digit, int *s_r
   }
 }
 
-// First scan: grid (chunks, queries), 4 waves, 4096 positions per workgroup.
-// Each wave streams 64 tiles in batches of U with the next batch's loads in
-// flight while the current batch is scored.
+// First scan: grid (chunks, queries), WAVES waves, TILES * 16 positions per
+// workgroup.  Wave w scores tiles w, w + WAVES, ... in batches of U tiles:
+// all loads of a batch are issued before any of it is scored, and the other
+// waves of the CU cover the latency.  Large chunks amortise the per-workgroup
+// set-up (query load, histogram clear and flush); the host picks the chunk so
+// that the grid still fills the chip.  Four tiles at a time
+// share the cross-lane reduction (tile_scores_x4).  Block maxima are staged
+// in LDS, written out once, and counted into an LDS histogram whose non-zero
+// bins are added to the query's global histogram.
 constexpr int kScanU = 8;
+constexpr bool kScanDbuf = false;
+constexpr int kScanMinGrid = 240;  // workgroups that count as filling the 256 CUs
 
-template <int DI>
-__global__ __launch_bounds__(256) void k_scan(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-                                              const int64_t *__restrict__ seq_start,
-                                              const int32_t *__restrict__ seq_len, int ratio,
-                                              const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
-                                              const uint16_t *__restrict__ q_idx, const float *__restrict__ w_idx,
-                                              int H, float *__restrict__ bmax, int64_t nb_stride,
-                                              uint32_t *__restrict__ hist) {
-  __shared__ float s_bmax[kScanBlocks];
+template <int DI, int WAVES = kScanWaves, int TILES = kScanTiles, int U = kScanU, bool DBUF = kScanDbuf>
+__global__ __launch_bounds__(64 * WAVES) void k_scan(const uint8_t *__restrict__ codes,
+                                                     const uint8_t *__restrict__ scales,
+                                                     const int64_t *__restrict__ seq_start,
+                                                     const int32_t *__restrict__ seq_len, int ratio,
+                                                     const int32_t *__restrict__ q_seq,
+                                                     const int32_t *__restrict__ q_pos,
+                                                     const uint16_t *__restrict__ q_idx,
+                                                     const float *__restrict__ w_idx, int H,
+                                                     float *__restrict__ bmax, int64_t nb_stride,
+                                                     uint32_t *__restrict__ hist) {
+  constexpr int CHUNK = TILES * 16;
+  constexpr int BLOCKS = CHUNK / kBlock;
+  constexpr int NB = TILES / WAVES / U;  // batches per wave
+  static_assert(TILES % (WAVES * U) == 0 && U % 4 == 0, "scan tiling");
+  __shared__ float s_bmax[BLOCKS];
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
   const int m = blockIdx.y;
   int s;
   const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
-  const int64_t p_begin = (int64_t)blockIdx.x * kScanChunk;
+  const int64_t p_begin = (int64_t)blockIdx.x * CHUNK;
   if (p_begin >= vis) return;
   for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x)
     reinterpret_cast<uint4 *>(s_hist)[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -229,47 +313,60 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t *__restrict__ codes,
   IdxQuery<DI> Q;
   load_idx_query<DI>(q_idx + (int64_t)m * H * DI, w_idx + (int64_t)m * H, H, Q);
 
-  const int64_t row0 = seq_start[s];
   const int l = lane_id(), n = l & 15, qq = l >> 4, wv = threadIdx.x >> 6;
-  constexpr int U = kScanU;
-  constexpr int NB = kScanTiles / 4 / U;  // batches per wave
-  const int64_t last = vis - 1;
-  // tile of batch b, slot u: (b*U + u)*4 + wv; a batch is live if its first tile starts before vis
-  auto live = [&](int b) { return p_begin + (int64_t)((b * U) * 4 + wv) * 16 < vis; };
-  auto load = [&](int b, LaneCodes<DI> *c) {
+  // positions of this chunk, relative to p_begin; the tail is clamped to the last visible entry
+  const int n_here = (int)min<int64_t>(CHUNK, vis - p_begin);
+  const uint8_t *cbase = codes + (seq_start[s] + p_begin) * (DI / 2);
+  const uint8_t *sbase = scales + (seq_start[s] + p_begin) * (DI / 16);
+  const int rt = row_tile(l >> 4);
+  // batch b of this wave: tiles t0 + u*WAVES, t0 = b*U*WAVES + wv
+  auto live = [&](int b) { return b < NB && (b * U * WAVES + wv) * 16 < n_here; };
+  auto load_batch = [&](int b, LaneCodes<DI> *c) {
+    const int t0 = b * U * WAVES + wv;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t p = p_begin + (int64_t)((b * U + u) * 4 + wv) * 16 + n;
-      load_lane_codes<DI>(codes, scales, row0 + min(p, last), qq, c[u]);
+      const int p = min((t0 + u * WAVES) * 16 + n, n_here - 1);
+      load_lane_codes_rel<DI>(cbase, sbase, (uint32_t)p, (uint32_t)qq, c[u]);
     }
   };
-  auto score = [&](int b, const LaneCodes<DI> *c) {
+  auto score_batch = [&](int b, const LaneCodes<DI> *c) {
+    const int t0 = b * U * WAVES + wv;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tile = (b * U + u) * 4 + wv;
-      const int64_t p = p_begin + (int64_t)tile * 16 + n;
-      float sc = tile_score<DI>(Q, c[u]);
-      if (p >= vis) sc = -INFINITY;
-      const float bm = max8_lanes(sc);
-      if (l == 0 || l == 8) s_bmax[tile * 2 + (l >> 3)] = bm;
+    for (int g = 0; g < U / 4; ++g) {
+      float v = tile_scores_x4(tile_partial<DI>(Q, c[4 * g]), tile_partial<DI>(Q, c[4 * g + 1]),
+                               tile_partial<DI>(Q, c[4 * g + 2]), tile_partial<DI>(Q, c[4 * g + 3]));
+      const int tile = t0 + (4 * g + rt) * WAVES;
+      if (tile * 16 + n >= n_here) v = -INFINITY;
+      v = max8_scores(v);
+      if ((n & 7) == 0) s_bmax[tile * 2 + (n >> 3)] = v;
     }
   };
-  LaneCodes<DI> A[U], B[U];
-  if (live(0)) load(0, A);
-  for (int b = 0; b < NB; b += 2) {
-    if (!live(b)) break;
-    const bool l1 = (b + 1 < NB) && live(b + 1);
-    if (l1) load(b + 1, B);
-    score(b, A);
-    if (!l1) break;
-    const bool l2 = (b + 2 < NB) && live(b + 2);
-    if (l2) load(b + 2, A);
-    score(b + 1, B);
-    if (!l2) break;
+  // the scheduling barriers keep each batch's loads issued together, ahead of the scoring
+  if constexpr (!DBUF) {
+    for (int b = 0; live(b); ++b) {
+      LaneCodes<DI> c[U];
+      load_batch(b, c);
+      __builtin_amdgcn_sched_barrier(0);
+      score_batch(b, c);
+    }
+  } else {
+    // the next batch's loads are in flight while the current one is scored
+    LaneCodes<DI> A[U], B[U];
+    if (live(0)) load_batch(0, A);
+    for (int b = 0; live(b); b += 2) {
+      const bool l1 = live(b + 1);
+      if (l1) load_batch(b + 1, B);
+      __builtin_amdgcn_sched_barrier(0);
+      score_batch(b, A);
+      if (!l1) break;
+      if (live(b + 2)) load_batch(b + 2, A);
+      __builtin_amdgcn_sched_barrier(0);
+      score_batch(b + 1, B);
+    }
   }
   __syncthreads();
-  const int nb_here = (int)min<int64_t>(kScanBlocks, (vis - p_begin + kBlock - 1) / kBlock);
-  float *dst = bmax + (int64_t)m * nb_stride + (int64_t)blockIdx.x * kScanBlocks;
+  const int nb_here = (n_here + kBlock - 1) / kBlock;
+  float *dst = bmax + (int64_t)m * nb_stride + (int64_t)blockIdx.x * BLOCKS;
   for (int i = threadIdx.x; i < nb_here; i += blockDim.x) {
     const float v = s_bmax[i];
     dst[i] = v;
@@ -649,6 +746,7 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ 
 IndexWs index_ws_layout(int64_t max_len, int m, int pool_blocks, int top_k) {
   (void)top_k;
   IndexWs w{};
+  // room for the largest scan chunk's rounding (smaller chunks need less)
   const int64_t chunks = (max_len + kScanChunk - 1) / kScanChunk;
   w.nb_max = (chunks > 0 ? chunks : 1) * kScanBlocks;
   w.slots = 8 * pool_blocks;
@@ -696,13 +794,20 @@ static int index_full_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
   // hist and counters are adjacent: clear both with one fill kernel
   const int64_t nz = (int64_t)((L.sure - L.hist) / sizeof(uint32_t));
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
-  const int64_t chunks = (idx.max_len + kScanChunk - 1) / kScanChunk;
-  if (chunks > 0) {
+  if (idx.max_len > 0) {
     const bool prof = scan_profiling();
     if (prof) scan_profile_begin(stream);
-    hipLaunchKernelGGL(k_scan<DI>, dim3((unsigned)chunks, qs.m), dim3(256), 0, stream, idx.codes, idx.scales,
-                       idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, q_idx, w_idx, heads, bmax, L.nb_max,
-                       hist);
+    // largest chunk whose grid still gives about one workgroup per CU
+    auto chunks_of = [&](int chunk) { return (idx.max_len + chunk - 1) / chunk; };
+    const int64_t m = qs.m;
+#define CSA2_SCAN(T)                                                                                        \
+  hipLaunchKernelGGL((k_scan<DI, kScanWaves, T>), dim3((unsigned)chunks_of(T * 16), qs.m), dim3(64 * kScanWaves), \
+                     0, stream, idx.codes, idx.scales, idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, q_idx, \
+                     w_idx, heads, bmax, L.nb_max, hist)
+    if (chunks_of(kScanChunk) * m >= kScanMinGrid) CSA2_SCAN(kScanTiles);
+    else if (chunks_of(kScanChunk / 4) * m >= kScanMinGrid) CSA2_SCAN(kScanTiles / 4);
+    else CSA2_SCAN(kScanTiles / 16);
+#undef CSA2_SCAN
     if (prof) scan_profile_end(stream);
   }
   const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);

@@ -151,35 +151,42 @@ def test_reindex_matches_oracle():
         assert np.all(np.abs(gs[i][:len(sel)] - s[sel]) <= 1e-5 * max(1.0, np.abs(s).max()))
 
 
-@pytest.mark.parametrize("shape", ["c4_one_seq", "c3_ragged"])
+@pytest.mark.parametrize("shape", ["c4_one_seq", "c4_four_queries", "c3_ragged"])
 def test_index_full_size_sampled_properties(shape):
     """1M-entry (and ragged 32K-256K) caches: properties checked on sampled rows.
 
     The oracle quantises only the rows it needs (rows are drawn per chunk, so
     any sub-range regenerates identically): every row of the GPU pool blocks
-    plus a random sample of other blocks.
+    plus a random sample of other blocks.  The shapes cover the three scan
+    chunk sizes: one query over 1M entries and the ragged batch take the
+    4096-position chunks, four queries over 1M entries the 16384-position
+    chunks (the smaller cases above take the 1024-position chunks).
     """
     rng = np.random.default_rng(7)
     if shape == "c4_one_seq":
-        lens = [1 << 20]
-        cfg = 107
+        lens, cfg = [1 << 20], 107
+        q_seq, q_pos = [0], [(1 << 20) - 1]
+    elif shape == "c4_four_queries":
+        lens, cfg = [1 << 20], 109
+        q_seq, q_pos = [0, 0, 0, 0], [(1 << 20) - 1, 777776, 524290, 262149]
     else:
         lens = synth.ragged_lengths(3, 32, 32768, 262144).tolist()[:6]
         cfg = 108
+        q_seq, q_pos = list(range(len(lens))), [n - 1 for n in lens]
     di, H, P, K = 128, 8, 2048, 512
     announce("index full-size", shape, sum(lens))
     x = np.concatenate([synth.gaussian_rows(cfg, synth.TAG_IDX_KEY, 0, s, 0, n, di) for s, n in enumerate(lens)])
     codes, scales = gpu_quantize(x)
     del x
     starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
-    M = len(lens)
-    q_pos = [n - 1 for n in lens]
+    M = len(q_seq)
     qi, wi = synth.q_idx(cfg, 0, M, H, di), synth.w_idx(cfg, 0, M, H)
-    gpool, gcnt, gtopk, gsc, _ = _run_full(codes, scales, starts, lens, di, list(range(M)), q_pos, qi, wi, P, K)
+    gpool, gcnt, gtopk, gsc, _ = _run_full(codes, scales, starts, lens, di, q_seq, q_pos, qi, wi, P, K)
     gc_all, gs_all = h(codes), h(scales)
     qf = synth.bf16_bits_to_f32(qi)
     for i in range(M):
-        n = lens[i]
+        sq = q_seq[i]
+        n = indexer.visible_count(lens[sq], q_pos[i], 1)
         nb = (n + 7) // 8
         assert gcnt[i] == min(P, nb)
         pool = gpool[i][:gcnt[i]]
@@ -194,11 +201,11 @@ def test_index_full_size_sampled_properties(shape):
         for c in np.unique(srows // synth.CHUNK_ROWS):
             sel = (srows // synth.CHUNK_ROWS) == c
             lo = int(c) * synth.CHUNK_ROWS
-            hi = min(n, lo + synth.CHUNK_ROWS)
-            chunk = synth.gaussian_rows(cfg, synth.TAG_IDX_KEY, 0, i, lo, hi - lo, di)
+            hi = min(lens[sq], lo + synth.CHUNK_ROWS)
+            chunk = synth.gaussian_rows(cfg, synth.TAG_IDX_KEY, 0, sq, lo, hi - lo, di)
             raw[order[sel]] = chunk[srows[sel] - lo]
         rc, rs = codec.fp4_encode(raw)
-        g0 = starts[i]
+        g0 = starts[sq]
         assert np.array_equal(gc_all[g0 + rows], rc) and np.array_equal(gs_all[g0 + rows], rs)
         s = indexer.scores(qf[i], wi[i], codec.fp4_decode(rc, rs))
         score_of = dict(zip(rows.tolist(), s.tolist()))
