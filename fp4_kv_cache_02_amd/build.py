@@ -30,6 +30,8 @@ def build(verbose: bool = False) -> str:
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
                # no packed-fp32 instructions (CDNA packed fp32 ops are avoided on purpose)
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               # keep private arrays in registers: never move them into spare LDS
+               "-mllvm", "-disable-promote-alloca-to-lds",
                "-Wno-unused-result", os.path.join(CSRC, src), "-o", obj]
         jobs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
         objs.append(obj)

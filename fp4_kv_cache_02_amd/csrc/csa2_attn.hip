@@ -2,14 +2,24 @@
 // concatenated with the layer's own FP8 window rows, one joint softmax (P5
 // figure caption of the attention diagram: Selection / Top-K /
 // Concatenation; P1 CSA2 section: each layer keeps its own query and window
-// KV).  Keys double as values (MQA over the shared latent).
+// KV).  Keys double as values (MQA over the shared latent).  Key slots
+// 0..K-1 are the Top-K list, K..K+W-1 the window rows.
 //
-// Workgroup = (key range, query, block of 64 heads), 4 waves; wave w owns
-// heads 16w..16w+15, so the softmax of a head never leaves its wave.  Key
-// slots 0..K-1 are the Top-K list, K..K+W-1 the window rows.  Each 64-key
-// sub-chunk is decoded once into LDS as a row-major f16 tile [key][dim]:
-// S = Q K^T reads it as the MFMA B operand, and O = P V reads it through the
-// gfx950 transposing LDS load (ds_read_b64_tr_b16), which hands each lane four
+// Two schedules compute the same thing:
+//
+// * Few queries (decode): k_attn_decode, one workgroup per (64 output dims,
+//   query, 16 heads).  Its waves decode FP4 key rows straight into MFMA
+//   operand registers, keep the logits in registers, and meet only for the
+//   softmax statistics; the 64-dim V slice and P pass through LDS.  The
+//   logits are recomputed by each output slice, which costs spare MFMA time
+//   but makes one short kernel per layer: the grid covers the chip even for
+//   four queries, with no workspace and no partial outputs to merge.
+// * Many queries (prefill): k_attn, one workgroup per (query, 64 heads),
+//   streams 64-key sub-chunks with an online softmax (flash style).
+//
+// A decoded key tile (flash) or V slice (decode) sits in LDS as row-major f16
+// [key][dim]: S = Q K^T reads the tile as the MFMA B operand, and O = P V reads it through the gfx950
+// transposing LDS load (ds_read_b64_tr_b16), which hands each lane four
 // consecutive keys of one dimension - the B operand of the P V product -
 // without a transposed copy.  Both products run on v_mfma_f32_16x16x32_f16.
 //
@@ -17,18 +27,17 @@
 // convert to f16 exactly inside the f16 normal range (|q| in [2^-14, 65504];
 // smaller values round to f16 subnormals, larger ones are outside the
 // supported input range) and fp32 queries are split into hi + lo f16 parts.
-// Window rows carry an fp32 row scale r: it multiplies the
-// logits (z = tau * r * q.c) and the probabilities entering P V, where the
-// sub-chunk's P is lifted by a power of two 2^S (undone on the accumulator)
-// to keep small p * r values out of the f16 subnormal range.  P is rounded
-// to f16 (relative error <= 2^-11); everything else accumulates in fp32.
-// Several key ranges per query are combined by a log-sum-exp merge kernel.
+// Window rows carry an fp32 row scale r: it multiplies the logits
+// (z = tau * r * q.c) and the probabilities entering P V, where P is lifted
+// by a power of two 2^e (undone on the accumulator) to keep small p * r
+// values out of the f16 subnormal range.  P is rounded to f16 (relative
+// error <= 2^-11); everything else accumulates in fp32.
 #include "csa2_internal.hpp"
 
 namespace csa2 {
 
-constexpr int kKC = 64;    // keys per sub-chunk
-constexpr int kHB = 64;    // heads per workgroup (4 waves x 16)
+constexpr int kKC = 64;    // keys per decoded tile (flash kernel)
+constexpr int kHB = 64;    // heads per flash workgroup (4 waves x 16)
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
@@ -41,61 +50,324 @@ CSA2_DEV short4_t lds_read_tr16(const _Float16 *p) {
       (lds_short4_t *)((__attribute__((address_space(3))) char *)(p)));
 }
 
+// B operand of O += P V for one 32-key step: keys k0 + 8*quad .. +7 at dim
+// d0 + (lane % 16) of a row-major f16 tile with row stride `stride`.
+CSA2_DEV half8_t v_operand_tr(const _Float16 *tile, int stride, int k0, int d0, int row, int quad) {
+  const _Float16 *base = tile + (k0 + 8 * quad + (row >> 2)) * stride + d0 + 4 * (row & 3);
+  const short4_t lo = lds_read_tr16(base);
+  const short4_t hi = lds_read_tr16(base + 4 * stride);
+  return __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Eight E4M3 codes (two little-endian words) as f16.
+CSA2_DEV half8_t e4m3x8_to_f16(uint32_t a, uint32_t b) {
+  const half2_t a0 = e4m3x2_to_f16(a), a1 = e4m3x2_to_f16(a >> 16);
+  const half2_t a2 = e4m3x2_to_f16(b), a3 = e4m3x2_to_f16(b >> 16);
+  return (half8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+// Where key slot `slot` of query m comes from: the Top-K entry (main) or the
+// window row, its scale (1 for main rows, the window row scale r, 0 when
+// the slot is empty or the entry is not visible) and its row index.
+struct KeySrc {
+  float ks;
+  int64_t row;
+};
+CSA2_DEV KeySrc key_source(int slot, int m, int K, int nk, const int32_t *topk, int64_t vis, int64_t row0,
+                           int wcount, int64_t wstart, const float *swa_scale) {
+  KeySrc r{0.0f, 0};
+  if (slot < K) {
+    const int32_t j = topk[(int64_t)m * K + slot];
+    if (j >= 0 && j < vis) { r.ks = 1.0f; r.row = row0 + j; }
+  } else if (slot < nk && slot - K < wcount) {
+    r.row = wstart + (slot - K);
+    r.ks = swa_scale[r.row];
+  }
+  return r;
+}
+
+// This wave's queries (16 heads from h0) as MFMA A operands: lane (head row,
+// quad) holds dims 32*kk + 8*quad .. +7 for kk = 0 .. D/32-1.  bf16 converts
+// to f16 directly; fp32 splits into hi + lo f16 parts.
 template <int D, bool QF32>
-struct AttnLds {
-  static constexpr int KT = D + 8;     // [key][dim] row stride (f16)
-  static constexpr int PT = kKC + 8;   // [head][key] row stride of a wave's P tile
-  _Float16 kt[kKC * KT];
-  _Float16 p[4][16 * PT];
-  float kscale[kKC];     // per key: r (window row scale) or 1; 0 = masked
-  int64_t koff[kKC];     // per key: byte offset of its FP4 codes (main) or FP8 row (window)
-  float rmax;
+CSA2_DEV void load_q_operands(const void *__restrict__ q_any, int m, int H, int h0, int row, int quad,
+                              half8_t *qa, half8_t *qb) {
+  constexpr int NK = D / 32;
+  const int h = h0 + row;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const int64_t off = ((int64_t)m * H + h) * D + 32 * kk + 8 * quad;
+    if constexpr (QF32) {
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      if (h < H) {
+        a = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q_any) + off)[0];
+        b = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q_any) + off)[1];
+      }
+      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const _Float16 hi = (_Float16)v[i];
+        qa[kk][i] = hi;
+        qb[kk][i] = (_Float16)(v[i] - (float)hi);
+      }
+    } else {
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (h < H) x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(q_any) + off);
+      const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qa[kk][2 * i] = (_Float16)__uint_as_float(wd[i] << 16);
+        qa[kk][2 * i + 1] = (_Float16)__uint_as_float(wd[i] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+// Decode kKC keys (slots sub .. sub+63; kscale / koff already in LDS) into
+// the row-major f16 tile kt[key][dim] (row stride KT).  Item = 32 channels of
+// one key; all loads of a thread are issued before any is decoded.  Empty
+// slots decode to zeros.
+template <int D>
+CSA2_DEV void decode_tile_to_lds(_Float16 *kt, int KT, const float *kscale, const int64_t *koff, int sub, int K,
+                                 const uint8_t *__restrict__ kv_codes, const uint8_t *__restrict__ kv_scales,
+                                 const uint8_t *__restrict__ swa_codes) {
+  constexpr int G32 = D / 32;
+  constexpr int TOTAL = kKC * G32;
+  constexpr int NIT = (TOTAL + 255) / 256;
+  uint4 ca[NIT], cb[NIT];
+  uint32_t sc[NIT];
+#pragma unroll
+  for (int u = 0; u < NIT; ++u) {
+    const int item = threadIdx.x + 256 * u;
+    ca[u] = make_uint4(0u, 0u, 0u, 0u);
+    cb[u] = ca[u];
+    sc[u] = 0u;
+    if (item < TOTAL) {
+      const int key = item / G32, g = item % G32;
+      const int64_t r = koff[key];
+      if (kscale[key] != 0.0f) {
+        if (sub + key < K) {
+          ca[u] = *reinterpret_cast<const uint4 *>(kv_codes + r * (D / 2) + g * 16);
+          sc[u] = *reinterpret_cast<const uint16_t *>(kv_scales + r * (D / 16) + g * 2);
+        } else {
+          ca[u] = reinterpret_cast<const uint4 *>(swa_codes + r * D + g * 32)[0];
+          cb[u] = reinterpret_cast<const uint4 *>(swa_codes + r * D + g * 32)[1];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NIT; ++u) {
+    const int item = threadIdx.x + 256 * u;
+    if (item < TOTAL) {
+      const int key = item / G32, g = item % G32;
+      half8_t v[4];
+      if (sub + key < K) {
+        const half2_t s2 = e4m3x2_to_f16(sc[u]);
+        v[0] = fp4x8_dequant_f16(ca[u].x, s2[0]);
+        v[1] = fp4x8_dequant_f16(ca[u].y, s2[0]);
+        v[2] = fp4x8_dequant_f16(ca[u].z, s2[1]);
+        v[3] = fp4x8_dequant_f16(ca[u].w, s2[1]);
+      } else {
+        v[0] = e4m3x8_to_f16(ca[u].x, ca[u].y);
+        v[1] = e4m3x8_to_f16(ca[u].z, ca[u].w);
+        v[2] = e4m3x8_to_f16(cb[u].x, cb[u].y);
+        v[3] = e4m3x8_to_f16(cb[u].z, cb[u].w);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<half8_t *>(&kt[key * KT + g * 32 + 8 * i]) = v[i];
+    }
+  }
+}
+
+// S = Q K^T for this wave's 16 heads x 64 keys (4 key tiles).  Lane result
+// sacc[t][j]: key 16*t + (lane % 16), head 4*quad + j.
+template <int D, bool QF32>
+CSA2_DEV void qk_tile(const _Float16 *kt, int KT, const half8_t *qa, const half8_t *qb, int row, int quad,
+                      float4_t sacc[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) sacc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const half8_t b = *reinterpret_cast<const half8_t *>(&kt[(16 * t + row) * KT + 32 * kk + 8 * quad]);
+      sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sacc[t], 0, 0, 0);
+      if constexpr (QF32) sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sacc[t], 0, 0, 0);
+    }
+  }
+}
+
+// ===========================================================================
+// decode schedule: one fused kernel per layer
+// ===========================================================================
+
+constexpr int kDW = 8;                 // waves per decode workgroup
+constexpr int kDH = 16;                // heads per decode workgroup
+constexpr int kDD = 64;                // output dims per decode workgroup
+constexpr int kDC = 640;               // key slots per chunk (40 tiles of 16)
+
+struct DecLds {
+  static constexpr int VT = kDD + 8;   // [key][dim] row stride of the V slice (f16)
+  static constexpr int PT = kDC + 8;   // [head][key] row stride of P (f16)
+  _Float16 vt[kDC * VT];
+  _Float16 p[kDH * PT];
+  float wmax[kDW][kDH];
+  float wsum[kDW][kDH];
+  float wr[kDW];
+  float4_t ored[4][64];
 };
 
+// One lane's share of a key tile: the quarter quad*(D/4) .. +D/4 of key
+// (lane % 16).  Main rows: D/8 FP4 code bytes + D/64 E4M3 scale bytes;
+// window rows: D/4 FP8 code bytes.  Empty slots keep zeros.
+template <int D>
+struct KeyQuarter {
+  uint32_t w[D / 16];
+  uint32_t s[(D / 64 + 3) / 4];
+  float ks;      // 1 (main), r (window) or 0 (empty)
+  int main;      // 1: FP4 main row, 0: FP8 window row
+};
+
+template <int D>
+CSA2_DEV void load_key_quarter(KeyQuarter<D> &k, int slot, int quad, int m, int K, int nk,
+                               const int32_t *__restrict__ topk, int64_t vis, int64_t row0, int wcount,
+                               int64_t wstart, const uint8_t *__restrict__ kv_codes,
+                               const uint8_t *__restrict__ kv_scales, const uint8_t *__restrict__ swa_codes,
+                               const float *__restrict__ swa_scale) {
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) k.w[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < (D / 64 + 3) / 4; ++i) k.s[i] = 0u;
+  k.ks = 0.0f;
+  k.main = slot < K ? 1 : 0;
+  if (slot < K) {
+    const int32_t j = topk[(int64_t)m * K + slot];
+    if (j >= 0 && j < vis) {
+      const int64_t r = row0 + j;
+      k.ks = 1.0f;
+      const uint8_t *c = kv_codes + r * (D / 2) + quad * (D / 8);
+      if constexpr (D >= 128) {
+#pragma unroll
+        for (int i = 0; i < D / 128; ++i) {
+          const uint4 x = reinterpret_cast<const uint4 *>(c)[i];
+          k.w[4 * i] = x.x; k.w[4 * i + 1] = x.y; k.w[4 * i + 2] = x.z; k.w[4 * i + 3] = x.w;
+        }
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2 *>(c);
+        k.w[0] = x.x; k.w[1] = x.y;
+      }
+      const uint8_t *sp = kv_scales + r * (D / 16) + quad * (D / 64);
+      if constexpr (D == 512) {
+        const uint2 x = *reinterpret_cast<const uint2 *>(sp);
+        k.s[0] = x.x; k.s[1] = x.y;
+      } else if constexpr (D == 256) {
+        k.s[0] = *reinterpret_cast<const uint32_t *>(sp);
+      } else if constexpr (D == 128) {
+        k.s[0] = *reinterpret_cast<const uint16_t *>(sp);
+      } else {
+        k.s[0] = *sp;
+      }
+    }
+  } else if (slot < nk && slot - K < wcount) {
+    const int64_t r = wstart + (slot - K);
+    k.ks = swa_scale[r];
+    const uint8_t *c = swa_codes + r * D + quad * (D / 4);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      const uint4 x = reinterpret_cast<const uint4 *>(c)[i];
+      k.w[4 * i] = x.x; k.w[4 * i + 1] = x.y; k.w[4 * i + 2] = x.z; k.w[4 * i + 3] = x.w;
+    }
+  }
+}
+
+// S += Q K^T for one key tile (B operand of step kk: dims quad*(D/4) + 8*kk
+// .. +7 of the lane's key), storing the dims that fall in [d0, d0 + DD) into
+// the V slice row `vrow`.  An MFMA reads the operands of every lane whatever
+// the exec mask, so it must never sit under a lane-divergent branch: the
+// FP4 / FP8 choice branches only when the whole tile agrees (a tile across
+// the Top-K / window boundary decodes both and selects per lane).
+template <int D, bool QF32, int DD, int MODE>  // MODE 0: FP4, 1: FP8, 2: per lane
+CSA2_DEV void score_key_tile_mode(const KeyQuarter<D> &k, const half8_t *qa, const half8_t *qb, float4_t &sa,
+                                  _Float16 *vrow, int quad, int d0) {
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    half8_t b;
+    if constexpr (MODE != 1) {
+      const uint32_t sb = (k.s[kk / 8] >> (8 * ((kk / 2) % 4))) & 0xFFu;
+      b = fp4x8_dequant_f16(k.w[kk], e4m3x2_to_f16(sb)[0]);
+    }
+    if constexpr (MODE == 1) b = e4m3x8_to_f16(k.w[2 * kk], k.w[2 * kk + 1]);
+    if constexpr (MODE == 2) {
+      const half8_t bw = e4m3x8_to_f16(k.w[2 * kk], k.w[2 * kk + 1]);
+      b = k.main ? b : bw;
+    }
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sa, 0, 0, 0);
+    if constexpr (QF32) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sa, 0, 0, 0);
+    const int dim = quad * (D / 4) + 8 * kk - d0;
+    if (dim >= 0 && dim < DD) *reinterpret_cast<half8_t *>(vrow + dim) = b;
+  }
+}
+
+template <int D, bool QF32, int DD>
+CSA2_DEV void score_key_tile(const KeyQuarter<D> &k, const half8_t *qa, const half8_t *qb, float4_t &sa,
+                             _Float16 *vrow, int quad, int d0) {
+  const uint64_t mains = __ballot(k.main != 0);
+  if (mains == ~0ull) score_key_tile_mode<D, QF32, DD, 0>(k, qa, qb, sa, vrow, quad, d0);
+  else if (mains == 0ull) score_key_tile_mode<D, QF32, DD, 1>(k, qa, qb, sa, vrow, quad, d0);
+  else score_key_tile_mode<D, QF32, DD, 2>(k, qa, qb, sa, vrow, quad, d0);
+}
+
+// grid (D / 64 output slices, queries, head blocks of 16), 8 waves.
+// Channels are assigned to MFMA k-steps by quarter: lane quad q feeds dims
+// q*(D/4) + 8*kk .. +7 at step kk, for both the query (A) and the key (B), so
+// a lane streams D/8 contiguous FP4 bytes of its key straight into registers.
+// Key slots go in chunks of 640 (one chunk for Top-512 + 128 window rows):
+// wave w scores tiles w, w+8, ... of the chunk for the workgroup's 16 heads,
+// keeping the logits in registers, and stores its tiles' 64-dim V slice into
+// LDS; the chunk's softmax statistics meet in LDS; P (f16) goes to LDS; then
+// wave w multiplies P by V for dims 16*(w%4) .. +15 over every second 32-key
+// step, the two halves being added at the end.  Chunks combine online.
 template <int D, bool QF32>
-__global__ __launch_bounds__(256) void k_attn(const void *__restrict__ q_any, int H,
-                                              const uint8_t *__restrict__ kv_codes,
-                                              const uint8_t *__restrict__ kv_scales,
-                                              const int64_t *__restrict__ seq_start,
-                                              const int32_t *__restrict__ seq_len, int ratio,
-                                              const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
-                                              const int32_t *__restrict__ topk, int K,
-                                              const uint8_t *__restrict__ swa_codes,
-                                              const float *__restrict__ swa_scale,
-                                              const int32_t *__restrict__ swa_start,
-                                              const int32_t *__restrict__ swa_count, int W, float softmax_scale,
-                                              int span, float *__restrict__ out, float *__restrict__ lse) {
-  __shared__ AttnLds<D, QF32> L;
-  const int c = blockIdx.x, m = blockIdx.y, hb = blockIdx.z;
-  const int NC = gridDim.x;
+__global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict__ q_any, int H,
+                                                          const uint8_t *__restrict__ kv_codes,
+                                                          const uint8_t *__restrict__ kv_scales,
+                                                          const int64_t *__restrict__ seq_start,
+                                                          const int32_t *__restrict__ seq_len, int ratio,
+                                                          const int32_t *__restrict__ q_seq,
+                                                          const int32_t *__restrict__ q_pos,
+                                                          const int32_t *__restrict__ topk, int K,
+                                                          const uint8_t *__restrict__ swa_codes,
+                                                          const float *__restrict__ swa_scale,
+                                                          const int32_t *__restrict__ swa_start,
+                                                          const int32_t *__restrict__ swa_count, int W, float tau2,
+                                                          float *__restrict__ out, float *__restrict__ lse) {
+  __shared__ DecLds L;
+  constexpr int NK = D / 32;             // MFMA k-steps per key
+  constexpr int DD = D < kDD ? D : kDD;  // dims of this workgroup's output slice
+  constexpr int MAXT = kDC / 16 / kDW;   // tiles per wave per chunk
+  const int m = blockIdx.y, hb = blockIdx.z;
+  const int d0 = blockIdx.x * kDD;
   const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
   const int row = l & 15, quad = l >> 4;
   const int nk = K + W;
-  const int slot_lo = c * span, slot_hi = min(nk, (c + 1) * span);
-  const int h0 = hb * kHB + 16 * wv;        // first head of this wave
-  const bool wave_active = h0 < H;
+  const int nkp = (nk + 31) / 32 * 32;
 
   const int s = q_seq[m];
   const int64_t lim = ((int64_t)q_pos[m] + 1) / ratio;
   const int64_t vis = max<int64_t>(0, min<int64_t>(seq_len[s], lim));
   const int64_t row0 = seq_start[s];
-  const int wcount = min(swa_count[m], W);
-  const int64_t wstart = swa_start[m];
+  // with no window the window arrays may be null
+  const int wcount = (W > 0) ? min(swa_count[m], W) : 0;
+  const int64_t wstart = (W > 0) ? swa_start[m] : 0;
 
-  // ---- this wave's queries as MFMA A operands (registers) ----
-  // lane (head row, quad) holds dims 32*kk + 8*quad .. +7 for kk = 0 .. D/32-1.
-  // bf16 queries convert to f16 directly (exact inside the f16 normal range);
-  // fp32 queries are split into hi + lo f16 parts.
-  constexpr int NK = D / 32;
+  // ---- queries: lane (head row, quad) holds dims quad*(D/4) + 8*kk .. +7 ----
   half8_t qa[NK];
   half8_t qb[QF32 ? NK : 1];
-  // log2-domain softmax: z2 = log2(e) * tau * q.k, p = 2^(z2 - max)
-  const float tau2 = softmax_scale * 1.4426950408889634f;
   {
-    const int h = h0 + row;
+    const int h = hb * kDH + row;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const int64_t off = ((int64_t)m * H + h) * D + 32 * kk + 8 * quad;
+      const int64_t off = ((int64_t)m * H + h) * D + quad * (D / 4) + 8 * kk;
       if constexpr (QF32) {
         float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
         if (h < H) {
@@ -122,6 +394,182 @@ __global__ __launch_bounds__(256) void k_attn(const void *__restrict__ q_any, in
     }
   }
 
+  float m_run[4], l_part[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { m_run[j] = -INFINITY; l_part[j] = 0.0f; }
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  int e_cur = 0;                          // accumulator exponent: true O = acc * 2^-e_cur
+  const int dt = wv & 3, khalf = wv >> 2;  // P V: dims 16*dt .., k-steps khalf, khalf+2, ...
+
+  for (int c0 = 0; c0 < nkp; c0 += kDC) {
+    const int nc = min(kDC, nkp - c0);    // a multiple of 32
+    const int ntiles = nc / 16;
+    if (c0 > 0) __syncthreads();          // previous chunk's LDS reads are done
+    // ---- S for this wave's tiles, V slice into LDS ----
+    float4_t sacc[MAXT];
+    float kss[MAXT];
+    KeyQuarter<D> cur;
+    int t = wv;
+    if (t < ntiles)
+      load_key_quarter<D>(cur, c0 + 16 * t + row, quad, m, K, nk, topk, vis, row0, wcount, wstart, kv_codes,
+                          kv_scales, swa_codes, swa_scale);
+#pragma unroll
+    for (int i = 0; i < MAXT; ++i) {
+      t = wv + kDW * i;
+      sacc[i] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+      kss[i] = 0.0f;
+      if (t < ntiles) {
+        // the next tile's loads are in flight while this one is scored
+        KeyQuarter<D> nxt;
+        const bool more = i + 1 < MAXT && t + kDW < ntiles;
+        if (more)
+          load_key_quarter<D>(nxt, c0 + 16 * (t + kDW) + row, quad, m, K, nk, topk, vis, row0, wcount, wstart,
+                              kv_codes, kv_scales, swa_codes, swa_scale);
+        kss[i] = cur.ks;
+        score_key_tile<D, QF32, DD>(cur, qa, qb, sacc[i], &L.vt[(16 * t + row) * DecLds::VT], quad, d0);
+        if (more) cur = nxt;
+      }
+    }
+    // ---- chunk statistics: lane holds key (16t + row) of heads 4*quad + j ----
+    float zz[MAXT][4];
+    float rm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXT; ++i) {
+      rm = fmaxf(rm, kss[i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) zz[i][j] = (kss[i] != 0.0f) ? sacc[i][j] * tau2 * kss[i] : -INFINITY;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) rm = fmaxf(rm, __shfl_xor(rm, o, 64));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < MAXT; ++i) mx = fmaxf(mx, zz[i][j]);
+      mx = max16_lanes(mx);
+      if (row == 0) L.wmax[wv][4 * quad + j] = mx;
+    }
+    if (l == 0) L.wr[wv] = rm;
+    __syncthreads();
+    float mnew[4], alpha[4];
+    rm = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDW; ++w) rm = fmaxf(rm, L.wr[w]);
+    int e_new = 0;
+    (void)frexpf(rm, &e_new);
+    e_new = (rm > 0.0f) ? 1 - e_new : 0;  // chunk's largest r * 2^e_new in [1, 2)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float cm = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kDW; ++w) cm = fmaxf(cm, L.wmax[w][4 * quad + j]);
+      mnew[j] = fmaxf(m_run[j], cm);
+      alpha[j] = (m_run[j] == -INFINITY) ? 0.0f : exp2f(m_run[j] - mnew[j]);
+      m_run[j] = mnew[j];
+    }
+    // ---- P' = 2^(z - max) * r * 2^e_new as f16 into LDS [head][key] ----
+    // the denominator sums 2^(z - max); the window scale r enters only P'
+#pragma unroll
+    for (int j = 0; j < 4; ++j) l_part[j] *= alpha[j];
+#pragma unroll
+    for (int i = 0; i < MAXT; ++i) {
+      t = wv + kDW * i;
+      if (t >= ntiles) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pr = (zz[i][j] == -INFINITY) ? 0.0f : exp2f(zz[i][j] - mnew[j]);
+        l_part[j] += pr;
+        L.p[(4 * quad + j) * DecLds::PT + 16 * t + row] = (_Float16)ldexpf(pr * kss[i], e_new);
+      }
+    }
+    if (c0 > 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] *= ldexpf(alpha[j], e_new - e_cur);
+    }
+    e_cur = e_new;
+    __syncthreads();
+    // ---- acc += P V for dims 16*dt .. over k-steps khalf, khalf + 2, ... ----
+    if (16 * dt < DD) {
+      for (int k0 = 32 * khalf; k0 < nc; k0 += 64) {
+        const half8_t a = *reinterpret_cast<const half8_t *>(&L.p[row * DecLds::PT + k0 + 8 * quad]);
+        const half8_t b = v_operand_tr(L.vt, DecLds::VT, k0, 16 * dt, row, quad);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- softmax denominators: lane partials -> rows -> waves ----
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float v = sum16_lanes(l_part[j]);
+    if (row == 0) L.wsum[wv][4 * quad + j] = v;
+  }
+  if (khalf == 1) L.ored[dt][l] = acc;
+  __syncthreads();
+  if (khalf == 1 || 16 * dt >= DD) return;
+  acc += L.ored[dt][l];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int hh = 4 * quad + j, h = hb * kDH + hh;
+    float lt = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDW; ++w) lt += L.wsum[w][hh];
+    if (h >= H) continue;
+    out[((int64_t)m * H + h) * D + d0 + 16 * dt + row] = (lt > 0.0f) ? ldexpf(acc[j] / lt, -e_cur) : 0.0f;
+    if (blockIdx.x == 0 && dt == 0 && row == 0 && lse)
+      lse[(int64_t)m * H + h] = (lt > 0.0f) ? (m_run[j] + log2f(lt)) * 0.6931471805599453f : -INFINITY;
+  }
+}
+
+// ===========================================================================
+// prefill schedule: one workgroup per (query, 64 heads), online softmax
+// ===========================================================================
+
+template <int D, bool QF32>
+struct AttnLds {
+  static constexpr int KT = D + 8;     // [key][dim] row stride (f16)
+  static constexpr int PT = kKC + 8;   // [head][key] row stride of a wave's P tile
+  _Float16 kt[kKC * KT];
+  _Float16 p[4][16 * PT];
+  float kscale[kKC];     // per key: r (window row scale) or 1; 0 = masked
+  int64_t koff[kKC];     // per key: row of its FP4 codes (main) or FP8 row (window)
+  float rmax;
+};
+
+template <int D, bool QF32>
+__global__ __launch_bounds__(256) void k_attn(const void *__restrict__ q_any, int H,
+                                              const uint8_t *__restrict__ kv_codes,
+                                              const uint8_t *__restrict__ kv_scales,
+                                              const int64_t *__restrict__ seq_start,
+                                              const int32_t *__restrict__ seq_len, int ratio,
+                                              const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
+                                              const int32_t *__restrict__ topk, int K,
+                                              const uint8_t *__restrict__ swa_codes,
+                                              const float *__restrict__ swa_scale,
+                                              const int32_t *__restrict__ swa_start,
+                                              const int32_t *__restrict__ swa_count, int W, float tau2,
+                                              float *__restrict__ out, float *__restrict__ lse) {
+  __shared__ AttnLds<D, QF32> L;
+  const int m = blockIdx.x, hb = blockIdx.y;
+  const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
+  const int row = l & 15, quad = l >> 4;
+  const int nk = K + W;
+  const int h0 = hb * kHB + 16 * wv;        // first head of this wave
+  const bool wave_active = h0 < H;
+
+  const int s = q_seq[m];
+  const int64_t lim = ((int64_t)q_pos[m] + 1) / ratio;
+  const int64_t vis = max<int64_t>(0, min<int64_t>(seq_len[s], lim));
+  const int64_t row0 = seq_start[s];
+  // with no window the window arrays may be null
+  const int wcount = (W > 0) ? min(swa_count[m], W) : 0;
+  const int64_t wstart = (W > 0) ? swa_start[m] : 0;
+
+  constexpr int NK = D / 32;
+  half8_t qa[NK];
+  half8_t qb[QF32 ? NK : 1];
+  load_q_operands<D, QF32>(q_any, m, H, h0, row, quad, qa, qb);
+
   float m_run[4], l_run[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) { m_run[j] = -INFINITY; l_run[j] = 0.0f; }
@@ -132,81 +580,24 @@ __global__ __launch_bounds__(256) void k_attn(const void *__restrict__ q_any, in
   int e_cur = 0;  // accumulator exponent: true O = o_acc * 2^-e_cur
   _Float16 *pw = L.p[wv];
 
-  for (int sub = slot_lo; sub < slot_hi; sub += kKC) {
+  for (int sub = 0; sub < nk; sub += kKC) {
     __syncthreads();  // previous sub-chunk's LDS reads are done
-    // ---- per-key validity, scale and source offset (wave 0) ----
+    // ---- per-key validity, scale and source row (wave 0) ----
     if (tid < kKC) {
-      const int slot = sub + tid;
-      float ks = 0.0f;
-      int64_t off = 0;
-      if (slot < slot_hi) {
-        if (slot < K) {
-          const int32_t j = topk[(int64_t)m * K + slot];
-          if (j >= 0 && j < vis) { ks = 1.0f; off = row0 + j; }
-        } else if (slot - K < wcount) {
-          off = wstart + (slot - K);
-          ks = swa_scale[off];
-        }
-      }
-      L.kscale[tid] = ks;
-      L.koff[tid] = off;
-      float rm = ks;
+      const KeySrc src = key_source(sub + tid, m, K, nk, topk, vis, row0, wcount, wstart, swa_scale);
+      L.kscale[tid] = src.ks;
+      L.koff[tid] = src.row;
+      float rm = src.ks;
       for (int o = 32; o > 0; o >>= 1) rm = fmaxf(rm, __shfl_xor(rm, o, 64));
       if (tid == 0) L.rmax = rm;
     }
     __syncthreads();
-    // ---- decode 64 keys into kt[key][dim]; a wave covers contiguous groups of one row ----
-    constexpr int G8 = D / 8;
-    constexpr int ITEMS = kKC * G8 / 256;
-    constexpr int BATCH = ITEMS < 8 ? ITEMS : 8;   // loads in flight per thread
-#pragma unroll
-    for (int i0 = 0; i0 < ITEMS; i0 += BATCH) {
-      half8_t vals[BATCH];
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int item = tid + 256 * (i0 + u);
-        const int key = item / G8, g = item % G8;
-        const int slot = sub + key;
-        const float ks = L.kscale[key];
-        const int64_t r = L.koff[key];
-        half8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (ks != 0.0f) {
-          if (slot < K) {
-            const uint32_t w = *reinterpret_cast<const uint32_t *>(kv_codes + r * (D / 2) + g * 4);
-            const uint32_t sb = kv_scales[r * (D / 16) + (g >> 1)];
-            v = fp4x8_dequant_f16(w, e4m3x2_to_f16(sb)[0]);
-          } else {
-            const uint2 w = *reinterpret_cast<const uint2 *>(swa_codes + r * D + g * 8);
-            const half2_t a0 = e4m3x2_to_f16(w.x), a1 = e4m3x2_to_f16(w.x >> 16);
-            const half2_t a2 = e4m3x2_to_f16(w.y), a3 = e4m3x2_to_f16(w.y >> 16);
-            v = (half8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-          }
-        }
-        vals[u] = v;
-      }
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int item = tid + 256 * (i0 + u);
-        const int key = item / G8, g = item % G8;
-        *reinterpret_cast<half8_t *>(&L.kt[key * L.KT + g * 8]) = vals[u];
-      }
-    }
+    decode_tile_to_lds<D>(L.kt, L.KT, L.kscale, L.koff, sub, K, kv_codes, kv_scales, swa_codes);
     __syncthreads();
     if (!wave_active) continue;
 
-    // ---- S = Q K^T for 16 heads x 64 keys (4 key tiles) ----
     float4_t sacc[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) sacc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const half8_t b = *reinterpret_cast<const half8_t *>(&L.kt[(16 * t + row) * L.KT + 32 * kk + 8 * quad]);
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sacc[t], 0, 0, 0);
-        if constexpr (QF32) sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sacc[t], 0, 0, 0);
-      }
-    }
+    qk_tile<D, QF32>(L.kt, L.KT, qa, qb, row, quad, sacc);
     // lane: key 16*t + row of each tile, heads 4*quad + j
     float z[4][4], ksc[4];
 #pragma unroll
@@ -255,136 +646,82 @@ __global__ __launch_bounds__(256) void k_attn(const void *__restrict__ q_any, in
     // ---- O = alpha O + P V for 16 heads x D dims ----
     const half8_t pa0 = *reinterpret_cast<const half8_t *>(&pw[row * L.PT + 8 * quad]);
     const half8_t pa1 = *reinterpret_cast<const half8_t *>(&pw[row * L.PT + 32 + 8 * quad]);
-    // transposing-read addresses: lane i of the quad group supplies key 8*quad + 4*h + i/4, dims 4*(i%4)..
-    const int tr_key = 8 * quad + (row >> 2);
-    const int tr_dim = 4 * (row & 3);
-    const bool first = sub == slot_lo;   // accumulator still zero: no rescale
+    const bool first = sub == 0;   // accumulator still zero: no rescale
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       if (!first) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) o_acc[ct][j] *= alpha[j];
       }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const _Float16 *base = &L.kt[(32 * kk + tr_key) * L.KT + 16 * ct + tr_dim];
-        const short4_t lo = lds_read_tr16(base);
-        const short4_t hi = lds_read_tr16(base + 4 * L.KT);
-        const short8_t s8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        const half8_t b = __builtin_bit_cast(half8_t, s8);
-        o_acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kk ? pa1 : pa0, b, o_acc[ct], 0, 0, 0);
-      }
+      o_acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa0, v_operand_tr(L.kt, L.KT, 0, 16 * ct, row, quad),
+                                                         o_acc[ct], 0, 0, 0);
+      o_acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa1, v_operand_tr(L.kt, L.KT, 32, 16 * ct, row, quad),
+                                                         o_acc[ct], 0, 0, 0);
     }
   }
 
   if (!wave_active) return;
-  // ---- write o (normalised) and lse for this key range ----
-  const int64_t obase = (NC == 1) ? (int64_t)m * H : ((int64_t)m * NC + c) * H;
+  // ---- write o (normalised) and lse ----
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int h = h0 + 4 * quad + j;
     if (h >= H) continue;
     const float inv = (l_run[j] > 0.0f) ? ldexpf(1.0f / l_run[j], -e_cur) : 0.0f;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) out[(obase + h) * D + 16 * ct + row] = o_acc[ct][j] * inv;
+    for (int ct = 0; ct < NCT; ++ct) out[((int64_t)m * H + h) * D + 16 * ct + row] = o_acc[ct][j] * inv;
     if (row == 0 && lse)
-      lse[obase + h] = (l_run[j] > 0.0f) ? (m_run[j] + log2f(l_run[j])) * 0.6931471805599453f : -INFINITY;
+      lse[(int64_t)m * H + h] = (l_run[j] > 0.0f) ? (m_run[j] + log2f(l_run[j])) * 0.6931471805599453f : -INFINITY;
   }
-}
-
-// Log-sum-exp merge of NC partial results: grid (m, heads), D threads.  All
-// partial values are loaded before they are combined.
-constexpr int kMaxSplits = 32;
-
-template <int D>
-__global__ __launch_bounds__(D) void k_attn_merge(const float *__restrict__ po, const float *__restrict__ plse,
-                                                  int NC, int H, float *__restrict__ out, float *__restrict__ lse) {
-  const int m = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-  float lc[kMaxSplits], oc[kMaxSplits];
-#pragma unroll
-  for (int c = 0; c < kMaxSplits; ++c) {
-    if (c < NC) {
-      lc[c] = plse[((int64_t)m * NC + c) * H + h];
-      oc[c] = po[(((int64_t)m * NC + c) * H + h) * D + d];
-    }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int c = 0; c < kMaxSplits; ++c)
-    if (c < NC) mx = fmaxf(mx, lc[c]);
-  float acc = 0.0f, wsum = 0.0f;
-  if (mx > -INFINITY) {
-#pragma unroll
-    for (int c = 0; c < kMaxSplits; ++c) {
-      if (c < NC) {
-        const float wc = (lc[c] == -INFINITY) ? 0.0f : expf(lc[c] - mx);
-        wsum += wc;
-        acc = fmaf(wc, oc[c], acc);
-      }
-    }
-  }
-  out[((int64_t)m * H + h) * D + d] = (wsum > 0.0f) ? acc / wsum : 0.0f;
-  if (d == 0 && lse) lse[(int64_t)m * H + h] = (wsum > 0.0f) ? mx + logf(wsum) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
-static int attn_splits(int m, int heads, int top_k, int window) {
-  const int nsub = (top_k + window + kKC - 1) / kKC;
-  const int base = m * ((heads + kHB - 1) / kHB);
-  int nc = (512 + base - 1) / base;
-  if (nc > nsub) nc = nsub;
-  if (nc > kMaxSplits) nc = kMaxSplits;
-  if (nc < 1) nc = 1;
-  return nc;
-}
+// The fused decode kernel fills the chip when there are few queries; with
+// many queries (prefill) the flash kernel's one-workgroup-per-query grid is
+// already large and computes each logit once.
+static bool use_decode_kernel(int m, int heads) { return (int64_t)m * ((heads + kHB - 1) / kHB) < 256; }
 
 size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int window) {
-  const int nc = attn_splits(m, heads, top_k, window);
-  if (nc == 1) return 256;
-  return align256(sizeof(float) * (size_t)m * nc * heads * dim) + align256(sizeof(float) * (size_t)m * nc * heads);
+  (void)m; (void)heads; (void)dim; (void)top_k; (void)window;
+  return 256;  // no workspace
 }
 
 template <int D, bool QF32>
 static int attn_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int heads,
-                     const int32_t *topk, int K, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,
+                     const int32_t *topk, int K, const csa2_swa &swa, float scale, float *out, float *lse,
                      hipStream_t stream) {
   const int W = swa.window;
-  const int nc = attn_splits(qs.m, heads, K, W);
-  const int nsub = (K + W + kKC - 1) / kKC;
-  const int span = ((nsub + nc - 1) / nc) * kKC;
-  const int ncu = (K + W + span - 1) / span;  // ranges actually used
-  const dim3 grid(ncu, qs.m, (heads + kHB - 1) / kHB);
-  float *po = out, *pl = lse;
-  if (ncu > 1) {
-    po = static_cast<float *>(ws);
-    pl = reinterpret_cast<float *>(static_cast<char *>(ws) + align256(sizeof(float) * (size_t)qs.m * ncu * heads * D));
+  const float tau2 = scale * 1.4426950408889634f;  // log2-domain softmax: p = 2^(z - max)
+  if (use_decode_kernel(qs.m, heads)) {
+    const dim3 grid((D + kDD - 1) / kDD, qs.m, (heads + kDH - 1) / kDH);
+    hipLaunchKernelGGL((k_attn_decode<D, QF32>), grid, dim3(64 * kDW), 0, stream, q, heads, kv.codes, kv.scales,
+                       kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, swa.codes, swa.scale, swa.start,
+                       swa.count, W, tau2, out, lse);
+  } else {
+    const dim3 grid(qs.m, (heads + kHB - 1) / kHB);
+    hipLaunchKernelGGL((k_attn<D, QF32>), grid, dim3(256), 0, stream, q, heads, kv.codes, kv.scales, kv.seq_start,
+                       kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, swa.codes, swa.scale, swa.start, swa.count, W,
+                       tau2, out, lse);
   }
-  hipLaunchKernelGGL((k_attn<D, QF32>), grid, dim3(256), 0, stream, q, heads, kv.codes, kv.scales, kv.seq_start,
-                     kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, swa.codes, swa.scale, swa.start, swa.count, W,
-                     scale, span, po, pl);
-  if (ncu > 1)
-    hipLaunchKernelGGL(k_attn_merge<D>, dim3(qs.m, heads), dim3(D), 0, stream, po, pl, ncu, heads, out, lse);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 
 int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int q_dtype, int heads,
                 const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,
                 hipStream_t stream) {
+  (void)ws;
   const bool f32 = q_dtype == CSA2_F32;
+#define CSA2_ATTN(D, F) attn_impl<D, F>(kv, qs, q, heads, topk, top_k, swa, scale, out, lse, stream)
   switch (kv.dim) {
-    case 64: return f32 ? attn_impl<64, true>(kv, qs, q, heads, topk, top_k, swa, scale, out, lse, ws, stream)
-                        : attn_impl<64, false>(kv, qs, q, heads, topk, top_k, swa, scale, out, lse, ws, stream);
-    case 128: return f32 ? attn_impl<128, true>(kv, qs, q, heads, topk, top_k, swa, scale, out, lse, ws, stream)
-                         : attn_impl<128, false>(kv, qs, q, heads, topk, top_k, swa, scale, out, lse, ws, stream);
-    case 256: return f32 ? attn_impl<256, true>(kv, qs, q, heads, topk, top_k, swa, scale, out, lse, ws, stream)
-                         : attn_impl<256, false>(kv, qs, q, heads, topk, top_k, swa, scale, out, lse, ws, stream);
-    case 512: return f32 ? CSA2_ERR_UNSUPPORTED
-                         : attn_impl<512, false>(kv, qs, q, heads, topk, top_k, swa, scale, out, lse, ws, stream);
+    case 64: return f32 ? CSA2_ATTN(64, true) : CSA2_ATTN(64, false);
+    case 128: return f32 ? CSA2_ATTN(128, true) : CSA2_ATTN(128, false);
+    case 256: return f32 ? CSA2_ATTN(256, true) : CSA2_ATTN(256, false);
+    case 512: return f32 ? CSA2_ERR_UNSUPPORTED : CSA2_ATTN(512, false);
     default: return CSA2_ERR_UNSUPPORTED;
   }
+#undef CSA2_ATTN
 }
 
 }  // namespace csa2

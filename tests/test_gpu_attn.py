@@ -112,3 +112,9 @@ def test_attn_fp32_d256_partial_head_group_mixed_chunk():
 
 def test_attn_window_only_and_small_dim():
     _run(205, 100, 64, 3, "bf16", 0, 128, 2, [99, 99], [0, 0], [0, 0], [0, 0], [128, 3])
+
+
+def test_attn_no_window_padded_slots():
+    # K = 100 is not a multiple of the 64-slot chunk and there is no window:
+    # the padding slots past K must contribute nothing
+    _run(206, 3000, 128, 16, "bf16", 100, 0, 2, [2999, 1500], [100, 50], [0, 30], [0, 5], [0, 0])
