@@ -125,7 +125,7 @@ class DecodeWorkload:
             self.groups.append(g)
             layer += n
         ws_bytes = max(csa2.csa2_group_workspace_size(g) for g in self.groups)
-        self.ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)  # zero before first use
         torch.cuda.synchronize()
 
     def step(self):

@@ -215,19 +215,25 @@ int32_t csa2_sparse_swa_attn(const csa2_fp4_cache *kv, const csa2_queries *qs, c
                      (hipStream_t)stream);
 }
 
+// Group workspace: the indexer's region, then the attention region (whose
+// arrival counters must keep their zeros between calls, so the indexer never
+// writes there).
+static size_t group_attn_offset(const csa2_group_desc *g) {
+  return align256(index_bytes(&g->idx, g->qs.m, g->pool_blocks, g->top_k));
+}
+
 int32_t csa2_group_workspace_size(const csa2_group_desc *g, size_t *bytes) {
   if (!g || !bytes) return CSA2_ERR_NULL_ARG;
   if (g->qs.m < 0 || g->n_layers < 1 || g->heads < 1 || g->top_k < 1 || g->pool_blocks < 0)
     return CSA2_ERR_BAD_SHAPE;
   if (g->pool_blocks > 4096 || g->top_k > 2048) return CSA2_ERR_UNSUPPORTED;
-  size_t a = index_bytes(&g->idx, g->qs.m, g->pool_blocks, g->top_k);
   size_t b = 256;
   for (int i = 0; i < g->n_layers; ++i) {
     const int w = g->swa ? g->swa[i].window : 0;
     const size_t x = attn_ws_bytes(g->qs.m > 0 ? g->qs.m : 1, g->heads, g->kv.dim, g->top_k, w);
     if (x > b) b = x;
   }
-  *bytes = a > b ? a : b;
+  *bytes = group_attn_offset(g) + b;
   return CSA2_OK;
 }
 
@@ -280,7 +286,8 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
   if (st) return st;
   for (int i = 0; i < g->n_layers; ++i) {
     st = launch_attn(g->kv, g->qs, g->q[i], g->q_dtype, g->heads, g->topk, g->top_k, g->swa[i], g->softmax_scale,
-                     g->out[i], g->lse ? g->lse[i] : nullptr, workspace, s);
+                     g->out[i], g->lse ? g->lse[i] : nullptr,
+                     static_cast<char *>(workspace) + group_attn_offset(g), s);
     if (st) return st;
   }
   return CSA2_OK;

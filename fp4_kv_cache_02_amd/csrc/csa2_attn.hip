@@ -204,129 +204,151 @@ CSA2_DEV void qk_tile(const _Float16 *kt, int KT, const half8_t *qa, const half8
 constexpr int kDW = 8;                 // waves per decode workgroup
 constexpr int kDH = 16;                // heads per decode workgroup
 constexpr int kDD = 64;                // output dims per decode workgroup
-constexpr int kDC = 640;               // key slots per chunk (40 tiles of 16)
+constexpr int kDC = 320;               // key slots per chunk (20 tiles of 16)
+constexpr int kDMaxSplit = 4;          // key splits per (query, head block, output slice)
 
+template <int D, bool QF32>
 struct DecLds {
   static constexpr int VT = kDD + 8;   // [key][dim] row stride of the V slice (f16)
   static constexpr int PT = kDC + 8;   // [head][key] row stride of P (f16)
+  static constexpr int QT = D + 8;     // [head][dim] row stride of the staged queries (f16)
   _Float16 vt[kDC * VT];
   _Float16 p[kDH * PT];
+  _Float16 q[(QF32 ? 2 : 1) * kDH * QT];  // hi parts, then lo parts (fp32 queries)
   float wmax[kDW][kDH];
   float wsum[kDW][kDH];
   float wr[kDW];
   float4_t ored[4][64];
 };
 
-// One lane's share of a key tile: the quarter quad*(D/4) .. +D/4 of key
-// (lane % 16).  Main rows: D/8 FP4 code bytes + D/64 E4M3 scale bytes;
-// window rows: D/4 FP8 code bytes.  Empty slots keep zeros.
+// One pipeline unit of a lane's key data: D/8 bytes = D/32 words, i.e. the
+// lane's whole FP4 quarter of a main row (dims quad*(D/4) .. +D/4, plus its
+// D/64 E4M3 scale bytes) or half of its FP8 quarter of a window row.
 template <int D>
-struct KeyQuarter {
-  uint32_t w[D / 16];
+struct KeyUnit {
+  uint32_t w[D / 32];
   uint32_t s[(D / 64 + 3) / 4];
-  float ks;      // 1 (main), r (window) or 0 (empty)
-  int main;      // 1: FP4 main row, 0: FP8 window row
 };
 
+// Raw buffer descriptor over `bytes` bytes (gfx9 data format word).  Loads
+// at offsets past the end return zeros without touching memory, which is
+// how the decode kernel reads empty, padded or invisible keys and heads
+// beyond H: every load is unconditional.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+CSA2_DEV rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// An offset past every descriptor used here, with room for the per-load
+// additions (< 4 KB) without wrapping: descriptors stay below kMaxRsrcBytes.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int64_t kMaxRsrcBytes = 0x7FFF0000;
+
+template <int BYTES>
+CSA2_DEV void buffer_load_words(uint32_t *dst, rsrc_t r, uint32_t off) {
+  if constexpr (BYTES >= 16) {
+#pragma unroll
+    for (int i = 0; i < BYTES / 16; ++i) {
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0);
+      dst[4 * i] = x[0]; dst[4 * i + 1] = x[1]; dst[4 * i + 2] = x[2]; dst[4 * i + 3] = x[3];
+    }
+  } else if constexpr (BYTES == 8) {
+    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    dst[0] = x[0]; dst[1] = x[1];
+  } else if constexpr (BYTES == 4) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (BYTES == 2) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  } else {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+  }
+}
+
+// Unit `half` of the lane's key quarter: main tiles read the FP4 codes at
+// `code_off` of `codes` and the scales at `scale_off` of `scales`; window
+// tiles read FP8 codes at `code_off` of `win` (scale_off is out of range).
 template <int D>
-CSA2_DEV void load_key_quarter(KeyQuarter<D> &k, int slot, int quad, int m, int K, int nk,
-                               const int32_t *__restrict__ topk, int64_t vis, int64_t row0, int wcount,
-                               int64_t wstart, const uint8_t *__restrict__ kv_codes,
-                               const uint8_t *__restrict__ kv_scales, const uint8_t *__restrict__ swa_codes,
-                               const float *__restrict__ swa_scale) {
+CSA2_DEV void load_key_unit(KeyUnit<D> &u, bool main, rsrc_t codes, rsrc_t win, rsrc_t scales, uint32_t code_off,
+                            uint32_t scale_off) {
+  buffer_load_words<D / 8>(u.w, main ? codes : win, code_off);
+  buffer_load_words<D / 64>(u.s, scales, scale_off);
+}
+
+// S += Q K^T for one unit.  Main unit: steps kk = 0 .. D/32-1; window unit
+// `half`: steps half*D/64 .. +D/64.  The B operand of step kk is dims
+// quad*(D/4) + 8*kk .. +7 of the lane's key.  Called only under
+// wave-uniform conditions: an MFMA reads the operands of every lane whatever
+// the exec mask.
+template <int D, bool QF32>
+CSA2_DEV void score_unit(const KeyUnit<D> &u, bool main, int half, const half8_t *qa, const half8_t *qb,
+                         float4_t &sa) {
+  if (main) {
+    // the unit's D/64 group scales, two per conversion
+    half2_t sc[(D / 64 + 1) / 2];
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) k.w[i] = 0u;
+    for (int g = 0; g < (D / 64 + 1) / 2; ++g) sc[g] = e4m3x2_to_f16(u.s[g / 2] >> (16 * (g % 2)));
 #pragma unroll
-  for (int i = 0; i < (D / 64 + 3) / 4; ++i) k.s[i] = 0u;
-  k.ks = 0.0f;
-  k.main = slot < K ? 1 : 0;
-  if (slot < K) {
-    const int32_t j = topk[(int64_t)m * K + slot];
-    if (j >= 0 && j < vis) {
-      const int64_t r = row0 + j;
-      k.ks = 1.0f;
-      const uint8_t *c = kv_codes + r * (D / 2) + quad * (D / 8);
-      if constexpr (D >= 128) {
-#pragma unroll
-        for (int i = 0; i < D / 128; ++i) {
-          const uint4 x = reinterpret_cast<const uint4 *>(c)[i];
-          k.w[4 * i] = x.x; k.w[4 * i + 1] = x.y; k.w[4 * i + 2] = x.z; k.w[4 * i + 3] = x.w;
-        }
-      } else {
-        const uint2 x = *reinterpret_cast<const uint2 *>(c);
-        k.w[0] = x.x; k.w[1] = x.y;
-      }
-      const uint8_t *sp = kv_scales + r * (D / 16) + quad * (D / 64);
-      if constexpr (D == 512) {
-        const uint2 x = *reinterpret_cast<const uint2 *>(sp);
-        k.s[0] = x.x; k.s[1] = x.y;
-      } else if constexpr (D == 256) {
-        k.s[0] = *reinterpret_cast<const uint32_t *>(sp);
-      } else if constexpr (D == 128) {
-        k.s[0] = *reinterpret_cast<const uint16_t *>(sp);
-      } else {
-        k.s[0] = *sp;
-      }
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const half8_t b = fp4x8_dequant_f16(u.w[kk], sc[kk / 4][(kk / 2) % 2]);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sa, 0, 0, 0);
+      if constexpr (QF32) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sa, 0, 0, 0);
     }
-  } else if (slot < nk && slot - K < wcount) {
-    const int64_t r = wstart + (slot - K);
-    k.ks = swa_scale[r];
-    const uint8_t *c = swa_codes + r * D + quad * (D / 4);
+  } else {
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) {
-      const uint4 x = reinterpret_cast<const uint4 *>(c)[i];
-      k.w[4 * i] = x.x; k.w[4 * i + 1] = x.y; k.w[4 * i + 2] = x.z; k.w[4 * i + 3] = x.w;
+    for (int k2 = 0; k2 < D / 64; ++k2) {
+      const int kk = half * (D / 64) + k2;
+      const half8_t b = e4m3x8_to_f16(u.w[2 * k2], u.w[2 * k2 + 1]);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sa, 0, 0, 0);
+      if constexpr (QF32) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sa, 0, 0, 0);
     }
   }
 }
 
-// S += Q K^T for one key tile (B operand of step kk: dims quad*(D/4) + 8*kk
-// .. +7 of the lane's key), storing the dims that fall in [d0, d0 + DD) into
-// the V slice row `vrow`.  An MFMA reads the operands of every lane whatever
-// the exec mask, so it must never sit under a lane-divergent branch: the
-// FP4 / FP8 choice branches only when the whole tile agrees (a tile across
-// the Top-K / window boundary decodes both and selects per lane).
-template <int D, bool QF32, int DD, int MODE>  // MODE 0: FP4, 1: FP8, 2: per lane
-CSA2_DEV void score_key_tile_mode(const KeyQuarter<D> &k, const half8_t *qa, const half8_t *qb, float4_t &sa,
-                                  _Float16 *vrow, int quad, int d0) {
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-    half8_t b;
-    if constexpr (MODE != 1) {
-      const uint32_t sb = (k.s[kk / 8] >> (8 * ((kk / 2) % 4))) & 0xFFu;
-      b = fp4x8_dequant_f16(k.w[kk], e4m3x2_to_f16(sb)[0]);
-    }
-    if constexpr (MODE == 1) b = e4m3x8_to_f16(k.w[2 * kk], k.w[2 * kk + 1]);
-    if constexpr (MODE == 2) {
-      const half8_t bw = e4m3x8_to_f16(k.w[2 * kk], k.w[2 * kk + 1]);
-      b = k.main ? b : bw;
-    }
-    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sa, 0, 0, 0);
-    if constexpr (QF32) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sa, 0, 0, 0);
-    const int dim = quad * (D / 4) + 8 * kk - d0;
-    if (dim >= 0 && dim < DD) *reinterpret_cast<half8_t *>(vrow + dim) = b;
+// The V slice of one key tile: lane (key n, part p) holds dims d0 + 16p ..
+// +15 of key n (D >= 64: four parts cover the 64-dim slice), loaded apart
+// from the scoring units (a cached re-read of 8 code bytes + 1 scale byte, or
+// 16 FP8 bytes) and stored as f16 into row n of the tile's LDS rows.
+struct VPiece {
+  uint32_t w[4];
+};
+template <int D>
+CSA2_DEV void load_vpiece(VPiece &v, bool main, rsrc_t codes, rsrc_t win, rsrc_t scales, uint32_t code_off,
+                          uint32_t scale_off) {
+  if (main) {
+    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(codes, code_off, 0, 0);
+    v.w[0] = x[0];
+    v.w[1] = x[1];
+    v.w[2] = __builtin_amdgcn_raw_buffer_load_b8(scales, scale_off, 0, 0);
+    v.w[3] = 0u;
+  } else {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(win, code_off, 0, 0);
+    v.w[0] = x[0]; v.w[1] = x[1]; v.w[2] = x[2]; v.w[3] = x[3];
   }
 }
-
-template <int D, bool QF32, int DD>
-CSA2_DEV void score_key_tile(const KeyQuarter<D> &k, const half8_t *qa, const half8_t *qb, float4_t &sa,
-                             _Float16 *vrow, int quad, int d0) {
-  const uint64_t mains = __ballot(k.main != 0);
-  if (mains == ~0ull) score_key_tile_mode<D, QF32, DD, 0>(k, qa, qb, sa, vrow, quad, d0);
-  else if (mains == 0ull) score_key_tile_mode<D, QF32, DD, 1>(k, qa, qb, sa, vrow, quad, d0);
-  else score_key_tile_mode<D, QF32, DD, 2>(k, qa, qb, sa, vrow, quad, d0);
+CSA2_DEV void store_vpiece(const VPiece &v, bool main, _Float16 *dst) {
+  half8_t a, b;
+  if (main) {
+    const _Float16 sc = e4m3x2_to_f16(v.w[2])[0];
+    a = fp4x8_dequant_f16(v.w[0], sc);
+    b = fp4x8_dequant_f16(v.w[1], sc);
+  } else {
+    a = e4m3x8_to_f16(v.w[0], v.w[1]);
+    b = e4m3x8_to_f16(v.w[2], v.w[3]);
+  }
+  *reinterpret_cast<half8_t *>(dst) = a;
+  *reinterpret_cast<half8_t *>(dst + 8) = b;
 }
 
 // grid (D / 64 output slices, queries, head blocks of 16), 8 waves.
 // Channels are assigned to MFMA k-steps by quarter: lane quad q feeds dims
 // q*(D/4) + 8*kk .. +7 at step kk, for both the query (A) and the key (B), so
-// a lane streams D/8 contiguous FP4 bytes of its key straight into registers.
-// Key slots go in chunks of 640 (one chunk for Top-512 + 128 window rows):
-// wave w scores tiles w, w+8, ... of the chunk for the workgroup's 16 heads,
-// keeping the logits in registers, and stores its tiles' 64-dim V slice into
-// LDS; the chunk's softmax statistics meet in LDS; P (f16) goes to LDS; then
-// wave w multiplies P by V for dims 16*(w%4) .. +15 over every second 32-key
-// step, the two halves being added at the end.  Chunks combine online.
+// a lane streams contiguous bytes of its key straight into registers.  Key
+// tiles go in chunks of 40 (one chunk for Top-512 + 128 window rows): wave w
+// scores tiles w, w+8, ... of the chunk for the workgroup's 16 heads, loading
+// one unit ahead, keeping the logits in registers and storing its tiles'
+// 64-dim V slice into LDS; the chunk's softmax statistics meet in LDS; P (f16)
+// goes to LDS; then wave w multiplies P by V for dims 16*(w%4) .. +15 over
+// every second 32-key step, the two halves being added at the end.  Chunks
+// combine online.
 template <int D, bool QF32>
 __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict__ q_any, int H,
                                                           const uint8_t *__restrict__ kv_codes,
@@ -340,58 +362,83 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
                                                           const float *__restrict__ swa_scale,
                                                           const int32_t *__restrict__ swa_start,
                                                           const int32_t *__restrict__ swa_count, int W, float tau2,
-                                                          float *__restrict__ out, float *__restrict__ lse) {
-  __shared__ DecLds L;
+                                                          float *__restrict__ out, float *__restrict__ lse,
+                                                          int nsplit, float *__restrict__ part_o,
+                                                          float *__restrict__ part_lse,
+                                                          uint32_t *__restrict__ counters) {
+  using Lds = DecLds<D, QF32>;
+  __shared__ Lds L;
   constexpr int NK = D / 32;             // MFMA k-steps per key
   constexpr int DD = D < kDD ? D : kDD;  // dims of this workgroup's output slice
-  constexpr int MAXT = kDC / 16 / kDW;   // tiles per wave per chunk
+  constexpr int CT = kDC / 16;                 // tiles per chunk
+  constexpr int MAXT = (CT + kDW - 1) / kDW;   // tiles per wave per chunk
   const int m = blockIdx.y, hb = blockIdx.z;
-  const int d0 = blockIdx.x * kDD;
-  const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
+  const int ds = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;  // output slice, key split
+  const int d0 = ds * kDD;
+  // the wave index as a scalar: per-tile conditions (and the descriptor choice)
+  // are then wave-uniform branches, not exec-masked ones
+  const int tid = threadIdx.x, l = lane_id(), wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = l & 15, quad = l >> 4;
-  const int nk = K + W;
-  const int nkp = (nk + 31) / 32 * 32;
+  const int TM = (K + 15) / 16;                     // Top-K tiles
+  const int TT = (TM + (W + 15) / 16 + 1) / 2 * 2;  // all tiles, even
+  // this workgroup's tiles [tb, te): an even share of the key split
+  const int tps = (TT / 2 + nsplit - 1) / nsplit * 2;
+  const int tb = min(TT, sp * tps), te = min(TT, tb + tps);
 
   const int s = q_seq[m];
   const int64_t lim = ((int64_t)q_pos[m] + 1) / ratio;
   const int64_t vis = max<int64_t>(0, min<int64_t>(seq_len[s], lim));
   const int64_t row0 = seq_start[s];
-  // with no window the window arrays may be null
-  const int wcount = (W > 0) ? min(swa_count[m], W) : 0;
+  // with no window the window arrays may be null (their descriptors are empty)
+  const int wcount = (W > 0) ? max(0, min(swa_count[m], W)) : 0;
   const int64_t wstart = (W > 0) ? swa_start[m] : 0;
+  // descriptors: this query's visible rows, window rows, Top-K list and queries
+  const rsrc_t r_codes = make_rsrc(kv_codes + row0 * (D / 2), (uint32_t)(vis * (D / 2)));
+  const rsrc_t r_scales = make_rsrc(kv_scales + row0 * (D / 16), (uint32_t)(vis * (D / 16)));
+  const rsrc_t r_win = make_rsrc(wcount ? swa_codes + wstart * D : nullptr, (uint32_t)(wcount * D));
+  const rsrc_t r_wsc = make_rsrc(wcount ? swa_scale + wstart : nullptr, (uint32_t)(wcount * 4));
+  const rsrc_t r_topk = make_rsrc(K ? topk + (int64_t)m * K : nullptr, (uint32_t)(K * 4));
+  constexpr int QE = QF32 ? 4 : 2;  // query element bytes
+  const rsrc_t r_q = make_rsrc(static_cast<const char *>(q_any) + (int64_t)m * H * D * QE, (uint32_t)(H * D * QE));
 
-  // ---- queries: lane (head row, quad) holds dims quad*(D/4) + 8*kk .. +7 ----
-  half8_t qa[NK];
-  half8_t qb[QF32 ? NK : 1];
+  // ---- queries: staged once per workgroup as f16 [head][dim] in LDS (fp32:
+  // hi and lo parts), then each wave keeps its MFMA A operands in registers:
+  // lane (head row, quad) holds dims quad*(D/4) + 8*kk .. +7 ----
   {
-    const int h = hb * kDH + row;
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const int64_t off = ((int64_t)m * H + h) * D + quad * (D / 4) + 8 * kk;
+    constexpr int PIECES = kDH * D / 8;  // 8 dims per piece
+    for (int pc = tid; pc < PIECES; pc += 64 * kDW) {
+      const int h = pc / (D / 8), d = 8 * (pc % (D / 8));
+      const uint32_t off = (uint32_t)(((hb * kDH + h) * D + d) * QE);
+      half8_t hi, lo;
       if constexpr (QF32) {
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-        if (h < H) {
-          a = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q_any) + off)[0];
-          b = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q_any) + off)[1];
-        }
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t x[8];
+        buffer_load_words<32>(x, r_q, off);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const _Float16 hi = (_Float16)v[i];
-          qa[kk][i] = hi;
-          qb[kk][i] = (_Float16)(v[i] - (float)hi);
+          const float v = __uint_as_float(x[i]);
+          hi[i] = (_Float16)v;
+          lo[i] = (_Float16)(v - (float)hi[i]);
         }
+        *reinterpret_cast<half8_t *>(&L.q[kDH * Lds::QT + h * Lds::QT + d]) = lo;
       } else {
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (h < H) x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(q_any) + off);
-        const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+        uint32_t x[4];
+        buffer_load_words<16>(x, r_q, off);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          qa[kk][2 * i] = (_Float16)__uint_as_float(wd[i] << 16);
-          qa[kk][2 * i + 1] = (_Float16)__uint_as_float(wd[i] & 0xFFFF0000u);
+          hi[2 * i] = (_Float16)__uint_as_float(x[i] << 16);
+          hi[2 * i + 1] = (_Float16)__uint_as_float(x[i] & 0xFFFF0000u);
         }
       }
+      *reinterpret_cast<half8_t *>(&L.q[h * Lds::QT + d]) = hi;
     }
+  }
+  __syncthreads();
+  half8_t qa[NK];
+  half8_t qb[QF32 ? NK : 1];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    qa[kk] = *reinterpret_cast<const half8_t *>(&L.q[row * Lds::QT + quad * (D / 4) + 8 * kk]);
+    if constexpr (QF32) qb[kk] = *reinterpret_cast<const half8_t *>(&L.q[(kDH + row) * Lds::QT + quad * (D / 4) + 8 * kk]);
   }
 
   float m_run[4], l_part[4];
@@ -399,45 +446,86 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
   for (int j = 0; j < 4; ++j) { m_run[j] = -INFINITY; l_part[j] = 0.0f; }
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   int e_cur = 0;                          // accumulator exponent: true O = acc * 2^-e_cur
-  const int dt = wv & 3, khalf = wv >> 2;  // P V: dims 16*dt .., k-steps khalf, khalf+2, ...
+  const int dt = wv & 3, khalf = wv >> 2;  // P V: dims 16*dt .., k-steps khalf, khalf + 2, ...
 
-  for (int c0 = 0; c0 < nkp; c0 += kDC) {
-    const int nc = min(kDC, nkp - c0);    // a multiple of 32
-    const int ntiles = nc / 16;
-    if (c0 > 0) __syncthreads();          // previous chunk's LDS reads are done
-    // ---- S for this wave's tiles, V slice into LDS ----
-    float4_t sacc[MAXT];
-    float kss[MAXT];
-    KeyQuarter<D> cur;
-    int t = wv;
-    if (t < ntiles)
-      load_key_quarter<D>(cur, c0 + 16 * t + row, quad, m, K, nk, topk, vis, row0, wcount, wstart, kv_codes,
-                          kv_scales, swa_codes, swa_scale);
+  for (int ct0 = tb; ct0 < te; ct0 += CT) {
+    const int ntiles = min(CT, te - ct0);  // even
+    const int nc = 16 * ntiles;
+    if (ct0 > tb) __syncthreads();         // previous chunk's LDS reads are done
+    // ---- sources of this wave's tiles: all index loads of the chunk in one batch ----
+    int32_t jv[MAXT];
+    float rv[MAXT];
 #pragma unroll
     for (int i = 0; i < MAXT; ++i) {
-      t = wv + kDW * i;
-      sacc[i] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-      kss[i] = 0.0f;
-      if (t < ntiles) {
-        // the next tile's loads are in flight while this one is scored
-        KeyQuarter<D> nxt;
-        const bool more = i + 1 < MAXT && t + kDW < ntiles;
-        if (more)
-          load_key_quarter<D>(nxt, c0 + 16 * (t + kDW) + row, quad, m, K, nk, topk, vis, row0, wcount, wstart,
-                              kv_codes, kv_scales, swa_codes, swa_scale);
-        kss[i] = cur.ks;
-        score_key_tile<D, QF32, DD>(cur, qa, qb, sacc[i], &L.vt[(16 * t + row) * DecLds::VT], quad, d0);
-        if (more) cur = nxt;
-      }
+      const int t = ct0 + wv + kDW * i;
+      jv[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_topk, (uint32_t)(16 * t + row) * 4u, 0, 0);
+      rv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_wsc, (uint32_t)(16 * (t - TM) + row) * 4u, 0, 0));
     }
-    // ---- chunk statistics: lane holds key (16t + row) of heads 4*quad + j ----
+    // (selects, not branches: a branch would pull each load down to its use)
+    uint32_t coff[MAXT], soff[MAXT], vcoff[MAXT], vsoff[MAXT];
+    float sks[MAXT];
+#pragma unroll
+    for (int i = 0; i < MAXT; ++i) {
+      const int t = ct0 + wv + kDW * i;
+      const int slot = 16 * t + row;             // Top-K slot (main tiles)
+      const int wi = 16 * (t - TM) + row;        // window row (window tiles)
+      const int32_t j = jv[i];
+      const bool is_main = t < TM;
+      const bool okm = slot < K && j >= 0 && j < vis;
+      const uint32_t cm = okm ? (uint32_t)j * (D / 2) + quad * (D / 8) : kOutOfRange;
+      const uint32_t cw = (uint32_t)wi * D + quad * (D / 4);  // past the window rows: out of range
+      coff[i] = is_main ? cm : cw;
+      soff[i] = (is_main && okm) ? (uint32_t)j * (D / 16) + quad * (D / 64) : kOutOfRange;
+      // V slice piece of lane (key row, part quad): dims d0 + 16*quad .. +15
+      const int vd = d0 + 16 * quad;
+      vcoff[i] = is_main ? (okm ? (uint32_t)j * (D / 2) + vd / 2 : kOutOfRange) : (uint32_t)wi * D + vd;
+      vsoff[i] = (is_main && okm) ? (uint32_t)j * (D / 16) + vd / 16 : kOutOfRange;
+      sks[i] = is_main ? (okm ? 1.0f : 0.0f) : ((wi < wcount) ? rv[i] : 0.0f);
+    }
+    // ---- S for this wave's tiles, one unit ahead in flight; V slice into LDS ----
+    float4_t sacc[MAXT];
+#pragma unroll
+    for (int i = 0; i < MAXT; ++i) sacc[i] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+    KeyUnit<D> cur;
+    VPiece vp;
+    if (wv < ntiles) {
+      load_key_unit<D>(cur, ct0 + wv < TM, r_codes, r_win, r_scales, coff[0], soff[0]);
+      load_vpiece<D>(vp, ct0 + wv < TM, r_codes, r_win, r_scales, vcoff[0], vsoff[0]);
+    }
+#pragma unroll
+    for (int k = 0; k < 2 * MAXT; ++k) {
+      const int i = k >> 1, h = k & 1;
+      const int tl = wv + kDW * i;             // tile within the chunk
+      if (tl >= ntiles) break;
+      const bool main = ct0 + tl < TM;
+      if (main && h == 1) continue;            // a main tile is a single unit
+      const int ni = (!main && h == 0) ? i : i + 1;
+      const int nh = (!main && h == 0) ? 1 : 0;
+      const int ntl = wv + kDW * ni;
+      const bool more = ni < MAXT && ntl < ntiles;
+      const bool more_v = more && nh == 0;     // the next unit starts a new tile
+      KeyUnit<D> nxt;
+      VPiece nvp;
+      if (more) {
+        const int nn = ni < MAXT ? ni : 0;
+        load_key_unit<D>(nxt, ct0 + ntl < TM, r_codes, r_win, r_scales, coff[nn] + nh * (D / 8), soff[nn]);
+        if (more_v) load_vpiece<D>(nvp, ct0 + ntl < TM, r_codes, r_win, r_scales, vcoff[nn], vsoff[nn]);
+      }
+      score_unit<D, QF32>(cur, main, h, qa, qb, sacc[i]);
+      if (main || h == 1) store_vpiece(vp, main, &L.vt[(16 * tl + row) * Lds::VT + 16 * quad]);
+      if (more) cur = nxt;
+      if (more_v) vp = nvp;
+    }
+    // ---- chunk statistics: lane holds key (16*tile + row) of heads 4*quad + j ----
     float zz[MAXT][4];
     float rm = 0.0f;
 #pragma unroll
     for (int i = 0; i < MAXT; ++i) {
-      rm = fmaxf(rm, kss[i]);
+      const bool live = wv + kDW * i < ntiles;
+      const float ks = live ? sks[i] : 0.0f;
+      rm = fmaxf(rm, ks);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) zz[i][j] = (kss[i] != 0.0f) ? sacc[i][j] * tau2 * kss[i] : -INFINITY;
+      for (int j = 0; j < 4; ++j) zz[i][j] = (ks != 0.0f) ? sacc[i][j] * tau2 * ks : -INFINITY;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) rm = fmaxf(rm, __shfl_xor(rm, o, 64));
@@ -473,16 +561,16 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
     for (int j = 0; j < 4; ++j) l_part[j] *= alpha[j];
 #pragma unroll
     for (int i = 0; i < MAXT; ++i) {
-      t = wv + kDW * i;
-      if (t >= ntiles) continue;
+      const int tl = wv + kDW * i;
+      if (tl >= ntiles) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float pr = (zz[i][j] == -INFINITY) ? 0.0f : exp2f(zz[i][j] - mnew[j]);
+        const float pr = (zz[i][j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(zz[i][j] - mnew[j]);
         l_part[j] += pr;
-        L.p[(4 * quad + j) * DecLds::PT + 16 * t + row] = (_Float16)ldexpf(pr * kss[i], e_new);
+        L.p[(4 * quad + j) * Lds::PT + 16 * tl + row] = (_Float16)ldexpf(pr * sks[i], e_new);
       }
     }
-    if (c0 > 0) {
+    if (ct0 > tb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[j] *= ldexpf(alpha[j], e_new - e_cur);
     }
@@ -491,8 +579,8 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
     // ---- acc += P V for dims 16*dt .. over k-steps khalf, khalf + 2, ... ----
     if (16 * dt < DD) {
       for (int k0 = 32 * khalf; k0 < nc; k0 += 64) {
-        const half8_t a = *reinterpret_cast<const half8_t *>(&L.p[row * DecLds::PT + k0 + 8 * quad]);
-        const half8_t b = v_operand_tr(L.vt, DecLds::VT, k0, 16 * dt, row, quad);
+        const half8_t a = *reinterpret_cast<const half8_t *>(&L.p[row * Lds::PT + k0 + 8 * quad]);
+        const half8_t b = v_operand_tr(L.vt, Lds::VT, k0, 16 * dt, row, quad);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
       }
     }
@@ -506,18 +594,82 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
   }
   if (khalf == 1) L.ored[dt][l] = acc;
   __syncthreads();
-  if (khalf == 1 || 16 * dt >= DD) return;
-  acc += L.ored[dt][l];
+  if (nsplit == 1) {
+    if (khalf == 1 || 16 * dt >= DD) return;
+    acc += L.ored[dt][l];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int hh = 4 * quad + j, h = hb * kDH + hh;
-    float lt = 0.0f;
+    for (int j = 0; j < 4; ++j) {
+      const int hh = 4 * quad + j, h = hb * kDH + hh;
+      float lt = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kDW; ++w) lt += L.wsum[w][hh];
+      for (int w = 0; w < kDW; ++w) lt += L.wsum[w][hh];
+      if (h >= H) continue;
+      out[((int64_t)m * H + h) * D + d0 + 16 * dt + row] = (lt > 0.0f) ? ldexpf(acc[j] / lt, -e_cur) : 0.0f;
+      if (ds == 0 && dt == 0 && row == 0 && lse)
+        lse[(int64_t)m * H + h] = (lt > 0.0f) ? (m_run[j] + log2f(lt)) * 0.6931471805599453f : -INFINITY;
+    }
+    return;
+  }
+  // ---- key split: write this split's normalised partial and its log2-domain
+  // lse; the last split of the (query, head block, slice) to arrive merges.
+  // The partials go through device-coherent stores and loads (they bypass the
+  // per-XCD L2s), so no cache-wide fence is needed: the stores are complete
+  // (s_waitcnt) before the arrival is counted, and the merging workgroup loads
+  // them only after it has seen the count. ----
+  const int64_t grp = ((int64_t)m * gridDim.z + hb) * (gridDim.x / nsplit) + ds;
+  float *po = part_o + (grp * nsplit + sp) * (kDH * kDD);
+  float *pl = part_lse + (grp * nsplit + sp) * kDH;
+  if (khalf == 0 && 16 * dt < DD) {
+    acc += L.ored[dt][l];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hh = 4 * quad + j;
+      float lt = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kDW; ++w) lt += L.wsum[w][hh];
+      const float o = (lt > 0.0f) ? ldexpf(acc[j] / lt, -e_cur) : 0.0f;
+      __hip_atomic_store(&po[hh * kDD + 16 * dt + row], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (dt == 0 && row == 0)
+        __hip_atomic_store(&pl[hh], (lt > 0.0f) ? m_run[j] + log2f(lt) : -INFINITY, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // every store of this workgroup has completed
+  __syncthreads();
+  __shared__ uint32_t s_prev;
+  if (tid == 0) s_prev = atomicInc(&counters[grp], (uint32_t)nsplit - 1u);  // wraps back to 0
+  __syncthreads();
+  if (s_prev != (uint32_t)nsplit - 1u) return;
+  const float *pg = part_o + grp * nsplit * (kDH * kDD);
+  const float *lg = part_lse + grp * nsplit * kDH;
+  for (int idx = tid; idx < kDH * DD; idx += 64 * kDW) {
+    const int hh = idx / DD, dd = idx % DD, h = hb * kDH + hh;
     if (h >= H) continue;
-    out[((int64_t)m * H + h) * D + d0 + 16 * dt + row] = (lt > 0.0f) ? ldexpf(acc[j] / lt, -e_cur) : 0.0f;
-    if (blockIdx.x == 0 && dt == 0 && row == 0 && lse)
-      lse[(int64_t)m * H + h] = (lt > 0.0f) ? (m_run[j] + log2f(lt)) * 0.6931471805599453f : -INFINITY;
+    float ls[kDMaxSplit], os[kDMaxSplit];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int s2 = 0; s2 < kDMaxSplit; ++s2) {
+      ls[s2] = -INFINITY;
+      os[s2] = 0.0f;
+      if (s2 < nsplit) {
+        ls[s2] = __hip_atomic_load(&lg[s2 * kDH + hh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        os[s2] = __hip_atomic_load(&pg[(s2 * kDH + hh) * kDD + dd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < kDMaxSplit; ++s2) mx = fmaxf(mx, ls[s2]);
+    float wsum = 0.0f, o = 0.0f;
+    if (mx > -INFINITY) {
+#pragma unroll
+      for (int s2 = 0; s2 < kDMaxSplit; ++s2) {
+        const float wgt = (ls[s2] == -INFINITY) ? 0.0f : exp2f(ls[s2] - mx);
+        wsum += wgt;
+        o = fmaf(wgt, os[s2], o);
+      }
+    }
+    out[((int64_t)m * H + h) * D + d0 + dd] = (wsum > 0.0f) ? o / wsum : 0.0f;
+    if (ds == 0 && dd == 0 && lse)
+      lse[(int64_t)m * H + h] = (wsum > 0.0f) ? (mx + log2f(wsum)) * 0.6931471805599453f : -INFINITY;
   }
 }
 
@@ -681,24 +833,70 @@ __global__ __launch_bounds__(256) void k_attn(const void *__restrict__ q_any, in
 // The fused decode kernel fills the chip when there are few queries; with
 // many queries (prefill) the flash kernel's one-workgroup-per-query grid is
 // already large and computes each logit once.
-static bool use_decode_kernel(int m, int heads) { return (int64_t)m * ((heads + kHB - 1) / kHB) < 256; }
+static bool use_decode_kernel(int m, int heads, int dim, int64_t max_len) {
+  // its buffer descriptors span one sequence's rows: byte offsets must fit
+  if (max_len * (dim / 2) >= kMaxRsrcBytes) return false;
+  return (int64_t)m * ((heads + kHB - 1) / kHB) < 256;
+}
 
+// Key splits of the decode kernel: about one workgroup per CU (one 8-wave
+// workgroup fits a CU at this register use; a second round of workgroups
+// costs more than it saves), at least two tiles per split.
+static int decode_splits(int m, int heads, int dim, int top_k, int window) {
+  const int64_t base = (int64_t)m * ((heads + kDH - 1) / kDH) * ((dim + kDD - 1) / kDD);
+  const int tiles = ((top_k + 15) / 16 + (window + 15) / 16 + 1) / 2 * 2;
+  int64_t ns = 256 / (base > 0 ? base : 1);
+  if (ns > kDMaxSplit) ns = kDMaxSplit;
+  if (ns < 1) ns = 1;
+  while (ns > 1 && tiles / ns < 2) --ns;
+  return (int)ns;
+}
+
+// Decode-schedule workspace with key splits: arrival counters (zero before
+// the first call, left zero by every call), partial outputs, partial lse.
+struct AttnWs {
+  size_t counters, part_o, part_lse, total;
+};
+static AttnWs attn_ws_layout(int m, int heads, int dim, int nsplit) {
+  const size_t groups = (size_t)m * ((heads + kDH - 1) / kDH) * ((dim + kDD - 1) / kDD);
+  AttnWs w{};
+  size_t off = 0;
+  w.counters = off; off = align256(off + sizeof(uint32_t) * groups);
+  w.part_o = off;   off = align256(off + sizeof(float) * groups * nsplit * kDH * kDD);
+  w.part_lse = off; off = align256(off + sizeof(float) * groups * nsplit * kDH);
+  w.total = off;
+  return w;
+}
+
+// Sized for the decode kernel whenever the query count may select it (a
+// cache too long for it falls back to the flash kernel, which needs none).
 size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int window) {
-  (void)m; (void)heads; (void)dim; (void)top_k; (void)window;
-  return 256;  // no workspace
+  if (!use_decode_kernel(m, heads, dim, 0)) return 256;
+  const int ns = decode_splits(m, heads, dim, top_k, window);
+  return ns > 1 ? attn_ws_layout(m, heads, dim, ns).total : 256;
 }
 
 template <int D, bool QF32>
 static int attn_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int heads,
-                     const int32_t *topk, int K, const csa2_swa &swa, float scale, float *out, float *lse,
+                     const int32_t *topk, int K, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,
                      hipStream_t stream) {
   const int W = swa.window;
   const float tau2 = scale * 1.4426950408889634f;  // log2-domain softmax: p = 2^(z - max)
-  if (use_decode_kernel(qs.m, heads)) {
-    const dim3 grid((D + kDD - 1) / kDD, qs.m, (heads + kDH - 1) / kDH);
+  if (use_decode_kernel(qs.m, heads, D, kv.max_len)) {
+    const int ns = decode_splits(qs.m, heads, D, K, W);
+    float *po = nullptr, *pl = nullptr;
+    uint32_t *ctr = nullptr;
+    if (ns > 1) {
+      const AttnWs L = attn_ws_layout(qs.m, heads, D, ns);
+      char *base = static_cast<char *>(ws);
+      ctr = reinterpret_cast<uint32_t *>(base + L.counters);
+      po = reinterpret_cast<float *>(base + L.part_o);
+      pl = reinterpret_cast<float *>(base + L.part_lse);
+    }
+    const dim3 grid(((D + kDD - 1) / kDD) * ns, qs.m, (heads + kDH - 1) / kDH);
     hipLaunchKernelGGL((k_attn_decode<D, QF32>), grid, dim3(64 * kDW), 0, stream, q, heads, kv.codes, kv.scales,
                        kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, swa.codes, swa.scale, swa.start,
-                       swa.count, W, tau2, out, lse);
+                       swa.count, W, tau2, out, lse, ns, po, pl, ctr);
   } else {
     const dim3 grid(qs.m, (heads + kHB - 1) / kHB);
     hipLaunchKernelGGL((k_attn<D, QF32>), grid, dim3(256), 0, stream, q, heads, kv.codes, kv.scales, kv.seq_start,
@@ -711,9 +909,8 @@ static int attn_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, const voi
 int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int q_dtype, int heads,
                 const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,
                 hipStream_t stream) {
-  (void)ws;
   const bool f32 = q_dtype == CSA2_F32;
-#define CSA2_ATTN(D, F) attn_impl<D, F>(kv, qs, q, heads, topk, top_k, swa, scale, out, lse, stream)
+#define CSA2_ATTN(D, F) attn_impl<D, F>(kv, qs, q, heads, topk, top_k, swa, scale, out, lse, ws, stream)
   switch (kv.dim) {
     case 64: return f32 ? CSA2_ATTN(64, true) : CSA2_ATTN(64, false);
     case 128: return f32 ? CSA2_ATTN(128, true) : CSA2_ATTN(128, false);

@@ -38,6 +38,8 @@ int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const u
                       hipStream_t stream);
 
 // ---- attention (csa2_attn.hip) ----
+// workspace of an attention call; its first bytes hold arrival counters that must be
+// zero before the first call with that workspace (every call leaves them zero)
 size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int window);
 int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int q_dtype, int heads,
                 const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,

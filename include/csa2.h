@@ -220,6 +220,11 @@ int32_t csa2_reindex(const csa2_fp4_cache *idx, const csa2_queries *qs, const ui
  * out  device [m][heads][dim] fp32.  lse device [m][heads] fp32 or NULL.
  * Limits: dim in {64, 128, 256, 512}; 1 <= heads <= 256; top_k <= 2048;
  *         window <= 1024.
+ * Workspace: csa2_attn_workspace_size bytes (256-byte aligned), owned by
+ *   the caller.  It must be zero-filled before its first use; every call
+ *   leaves its counter words zero again, so a workspace reused by calls on
+ *   one stream needs no further clearing.  Calls that run at the same time
+ *   must not share a workspace.
  * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED, WORKSPACE, HIP.
  * ------------------------------------------------------------------- */
 int32_t csa2_attn_workspace_size(int32_t m, int32_t heads, int32_t dim, int32_t top_k,
@@ -279,6 +284,10 @@ typedef struct csa2_group_desc {
   float softmax_scale;
 } csa2_group_desc;
 
+/* Workspace of csa2_group_step: csa2_group_workspace_size bytes, 256-byte
+ * aligned, zero-filled before its first use (the attention part of it keeps
+ * counter words that every call leaves zero); not shared by calls that run
+ * at the same time. */
 int32_t csa2_group_workspace_size(const csa2_group_desc *g, size_t *bytes);
 int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_bytes, void *stream);
 

@@ -38,7 +38,8 @@ def empty_u8(*shape) -> torch.Tensor:
 
 
 def workspace(nbytes: int) -> torch.Tensor:
-    return torch.empty(max(256, nbytes), dtype=torch.uint8, device=dev())
+    # zero-filled before first use, as the attention and group calls require
+    return torch.zeros(max(256, nbytes), dtype=torch.uint8, device=dev())
 
 
 def gpu_quantize(x: np.ndarray, w_ik: np.ndarray | None = None):

@@ -83,7 +83,7 @@ def test_group_step_matches_oracle(shape):
                        D ** -0.5, new_kv=t(x[n - 1:n]) if full else None,
                        new_dst_row=t(np.array([n - 1], np.int64)) if full else None,
                        w_ik=t(w_ik) if full else None)
-        ws = torch.empty((csa2.csa2_group_workspace_size(g),), dtype=torch.uint8, device=dev())
+        ws = torch.zeros((csa2.csa2_group_workspace_size(g),), dtype=torch.uint8, device=dev())
         csa2.csa2_group_step(g, ws)
         if full:
             assert np.array_equal(h(kv_c), rc) and np.array_equal(h(kv_s), rs)
