@@ -154,32 +154,40 @@ CSA2_DEV float sum_rows4(float v) {
 
 CSA2_DEV int lane_id() { return __lane_id(); }
 
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active):
+// Hillis-Steele steps inside each 16-lane row (row_shr 1, 2, 4, 8), then the
+// row totals carried across rows with row_bcast 15 and row_bcast 31.  DPP
+// moves take a few cycles where a shuffle is an LDS round trip.
+CSA2_DEV int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Exclusive prefix sum of `v` over the threads of a block of NT threads
 // (NT a multiple of 64, <= 1024); `scratch` holds NT/64 + 1 ints of LDS.
-// Returns the prefix and writes the block total to *total.
+// Returns the prefix and writes the block total to *total.  Wave scans, then
+// wave 0 scans the wave totals; the scratch is free again on return.
 template <int NT>
 CSA2_DEV int block_exclusive_scan(int v, int *scratch, int *total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) scratch[wave] = x;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) scratch[wave] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int w = 0; w < NT / 64; ++w) {
-      int t = scratch[w];
-      scratch[w] = acc;
-      acc += t;
-    }
-    scratch[NT / 64] = acc;
+  if (wave == 0) {
+    const int t = (lane < NW) ? scratch[lane] : 0;
+    const int ti = wave_incl_scan(t);
+    if (lane < NW) scratch[lane] = ti - t;
+    if (lane == NW - 1) scratch[NW] = ti;
   }
   __syncthreads();
-  const int res = scratch[wave] + x - v;
-  *total = scratch[NT / 64];
+  const int res = scratch[wave] + incl - v;
+  *total = scratch[NW];
   __syncthreads();
   return res;
 }

@@ -251,12 +251,7 @@ CSA2_DEV void find_digit(const uint32_t *s_hist, int rem, int *s_digit, int *s_r
     h[e] = (int)s_hist[255 - 4 * l - e];
     local += h[e];
   }
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (l >= off) incl += y;
-  }
+  const int incl = wave_incl_scan(local);
   int excl = incl - local;
   if (excl < rem && incl >= rem) {
 #pragma unroll
@@ -441,6 +436,8 @@ __global__ __launch_bounds__(256) void k_pool_filter(const float *__restrict__ b
   }
   __syncthreads();
   T = s_T;
+  // the threshold bin, for the finalisation (every workgroup finds the same one)
+  if (blockIdx.x == 0 && threadIdx.x == 0) counters[m * 4 + 2] = (uint32_t)T;
   const float *bm = bmax + (int64_t)m * nb_stride;
   for (int j = 0; j < kFilterBlocks / 256; ++j) {
     const int64_t b = b0 + j * 256 + threadIdx.x;
@@ -487,6 +484,7 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
   const int64_t nb = (vis + kBlock - 1) / kBlock;
   const int n_sure = (int)counters[m * 4 + 0];
   const int n_tie = (int)counters[m * 4 + 1];
+  const uint32_t s_T = counters[m * 4 + 2];  // threshold bin (meaningful when there are ties)
   const int need = (int)min<int64_t>(min<int64_t>(P, nb), (int64_t)n_sure + n_tie);
   const int need_t = need - n_sure;
   const int32_t *su = sure + (int64_t)m * P;
@@ -507,29 +505,37 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
     if (need_t >= n_tie) {
       for (int i = threadIdx.x; i < n_tie; i += blockDim.x) take(ti[i]);
     } else {
-      // composite key: larger score first, then smaller block id
-      uint64_t prefix = 0, mask = 0;
+      // composite key: larger score first, then smaller block id.  Every tie
+      // entry shares the threshold bin (the top kHistBits of the score key),
+      // so the digits start below it; the passes stop as soon as the cut's bin
+      // holds exactly the entries still needed.
+      constexpr int kKnown = kHistBits;
+      uint64_t prefix = (uint64_t)s_T << (64 - kKnown);
+      uint64_t mask = ((1ull << kKnown) - 1ull) << (64 - kKnown);
       int rem = need_t;
-      for (int d = 7; d >= 0; --d) {
-        const int shift = 8 * d;
+      for (int hi = 64 - kKnown; hi > 0; hi -= 8) {
+        const int width = hi < 8 ? hi : 8;
+        const int shift = hi - width;
+        const uint64_t dmask = (1ull << width) - 1ull;
         for (int i = threadIdx.x; i < 256; i += blockDim.x) s_h[i] = 0u;
         __syncthreads();
         for (int i = threadIdx.x; i < n_tie; i += blockDim.x) {
           const int32_t b = ti[i];
           const uint64_t c = ((uint64_t)f2key(bm[b]) << 32) | (uint64_t)(~(uint32_t)b);
-          if ((c & mask) == prefix) atomicAdd(&s_h[(c >> shift) & 255u], 1u);
+          if ((c & mask) == prefix) atomicAdd(&s_h[(c >> shift) & dmask], 1u);
         }
         __syncthreads();
         find_digit(s_h, rem, &s_digit, &s_rem, &s_cnt);
         __syncthreads();
         prefix |= (uint64_t)s_digit << shift;
-        mask |= (uint64_t)255 << shift;
+        mask |= dmask << shift;
         rem = s_rem;
+        if (s_cnt == rem) break;
       }
       for (int i = threadIdx.x; i < n_tie; i += blockDim.x) {
         const int32_t b = ti[i];
         const uint64_t c = ((uint64_t)f2key(bm[b]) << 32) | (uint64_t)(~(uint32_t)b);
-        if (c >= prefix) take(b);
+        if ((c & mask) >= prefix) take(b);
       }
     }
   }
@@ -650,24 +656,28 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ 
   const int nslots = 8 * cnt;
   const float *ps = pscore + (int64_t)m * 8 * P;
   uint32_t key[PER];
+  float sv[PER];                 // the scores themselves, for the score output
+  int32_t blk[PER / kBlock];     // pool blocks of this thread's slots, loaded up front
+  const int32_t *pl = pool + (int64_t)m * P;
+#pragma unroll
+  for (int b = 0; b < PER / kBlock; ++b) blk[b] = pl[min((int)threadIdx.x * (PER / kBlock) + b, max(cnt, 1) - 1)];
   int nvalid = 0;
   if ((threadIdx.x + 1) * PER <= nslots) {
     const float4 *src = reinterpret_cast<const float4 *>(ps + threadIdx.x * PER);
 #pragma unroll
     for (int k = 0; k < PER / 4; ++k) {
       const float4 v = src[k];
-      const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) key[4 * k + i] = (vv[i] > -INFINITY) ? f2key(vv[i]) : 0u;
+      sv[4 * k] = v.x; sv[4 * k + 1] = v.y; sv[4 * k + 2] = v.z; sv[4 * k + 3] = v.w;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int slot = threadIdx.x * PER + i;
-      const float v = (slot < nslots) ? ps[slot] : -INFINITY;
-      key[i] = (v > -INFINITY) ? f2key(v) : 0u;
+      sv[i] = (slot < nslots) ? ps[slot] : -INFINITY;
     }
   }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) key[i] = (sv[i] > -INFINITY) ? f2key(sv[i]) : 0u;
 #pragma unroll
   for (int i = 0; i < PER; ++i) nvalid += key[i] != 0u;
   int total;
@@ -675,7 +685,7 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ 
   const int Kp = min(K, total);
   int32_t *out = topk_out + (int64_t)m * K;
   float *osc = topk_score ? topk_score + (int64_t)m * K : nullptr;
-  uint32_t kstar = 0xFFFFFFFFu;
+  uint32_t kstar = 0xFFFFFFFFu, kmask = 0xFFFFFFFFu;
   int rem = 0;
   if (Kp > 0) {
     uint32_t prefix = 0, mask = 0;
@@ -685,9 +695,20 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ 
         reinterpret_cast<uint4 *>(s_wh)[i] = make_uint4(0u, 0u, 0u, 0u);
       __syncthreads();
       uint32_t *wh = s_wh + wv * 256;
+      // Scores cluster in a few digit values (the high digits especially), so
+      // the lanes of a wave would hit one LDS counter together: each thread
+      // first folds its keys into at most two (digit, count) pairs.
+      uint32_t d0 = 0u, c0 = 0u, d1 = 0u, c1 = 0u;
 #pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (key[i] != 0u && (key[i] & mask) == prefix) atomicAdd(&wh[(key[i] >> shift) & 255u], 1u);
+      for (int i = 0; i < PER; ++i) {
+        if (key[i] == 0u || (key[i] & mask) != prefix) continue;
+        const uint32_t d = (key[i] >> shift) & 255u;
+        if (c0 == 0u || d == d0) { d0 = d; ++c0; }
+        else if (c1 == 0u || d == d1) { d1 = d; ++c1; }
+        else atomicAdd(&wh[d], 1u);
+      }
+      if (c0) atomicAdd(&wh[d0], c0);
+      if (c1) atomicAdd(&wh[d1], c1);
       __syncthreads();
       if (threadIdx.x < 256) {
         uint32_t t = 0;
@@ -701,13 +722,17 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ 
       prefix |= (uint32_t)s_digit << shift;
       mask |= 255u << shift;
       rem = s_rem;
+      // every key left in the cut's bin is taken: the lower digits cannot matter
+      if (s_cnt == rem) break;
     }
     kstar = prefix;
+    kmask = mask;
   }
-  // equal-key ranks (lowest slots first), then compaction
+  // keys above the cut (on the decided digits) are taken; keys equal to it
+  // are ranked by slot (lowest first), then compaction
   int neq = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) neq += (Kp > 0 && key[i] == kstar);
+  for (int i = 0; i < PER; ++i) neq += (Kp > 0 && (key[i] & kmask) == kstar);
   int tmp;
   int eq_before = block_exclusive_scan<1024>(neq, s_scan, &tmp);
   bool sel[PER];
@@ -716,20 +741,19 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ 
   for (int i = 0; i < PER; ++i) {
     bool takeit = false;
     if (Kp > 0 && key[i] != 0u) {
-      if (key[i] > kstar) takeit = true;
-      else if (key[i] == kstar) { takeit = eq_before < rem; ++eq_before; }
+      const uint32_t km = key[i] & kmask;
+      if (km > kstar) takeit = true;
+      else if (km == kstar) { takeit = eq_before < rem; ++eq_before; }
     }
     sel[i] = takeit;
     nsel += takeit;
   }
   int rank = block_exclusive_scan<1024>(nsel, s_scan, &tmp);
-  const int32_t *pl = pool + (int64_t)m * P;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (sel[i]) {
-      const int slot = threadIdx.x * PER + i;
-      out[rank] = pl[slot >> 3] * kBlock + (slot & 7);
-      if (osc) osc[rank] = ps[slot];
+      out[rank] = blk[i / kBlock] * kBlock + (i % kBlock);
+      if (osc) osc[rank] = sv[i];
       ++rank;
     }
   }

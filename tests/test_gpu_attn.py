@@ -31,7 +31,7 @@ def _lists(cfg, M, K, n_valid, vis, n_pad, n_invalid):
     return out
 
 
-def _run(cfg, n_rows, D, H, qdt, K, W, M, q_pos, n_valid, n_pad, n_invalid, counts, q_mult=1.0):
+def _run(cfg, n_rows, D, H, qdt, K, W, M, q_pos, n_valid, n_pad, n_invalid, counts, q_mult=1.0, sample=None):
     announce("attention", cfg, n_rows, D, H, qdt, K, W, M)
     x = synth.main_kv_rows(cfg, 0, 0, n_rows, D)
     codes, scales = gpu_quantize(x)
@@ -66,7 +66,7 @@ def _run(cfg, n_rows, D, H, qdt, K, W, M, q_pos, n_valid, n_pad, n_invalid, coun
     csa2.csa2_sparse_swa_attn(kv, qs, qd, t(idx) if K > 0 else None, K, sw, tau, out, lse, ws)
     go, gl = h(out), h(lse)
     worst = 0.0
-    for m in range(M):
+    for m in (range(M) if sample is None else sample):
         lo = m * W
         ro, rl = attention.sparse_swa_attention(qf[m], rc, rs, idx[m], vis[m], rc8[lo:lo + counts[m]],
                                                 rs8[lo:lo + counts[m]], tau)
@@ -118,3 +118,12 @@ def test_attn_no_window_padded_slots():
     # K = 100 is not a multiple of the 64-slot chunk and there is no window:
     # the padding slots past K must contribute nothing
     _run(206, 3000, 128, 16, "bf16", 100, 0, 2, [2999, 1500], [100, 50], [0, 30], [0, 5], [0, 0])
+
+
+def test_attn_prefill_schedule_sampled():
+    # 320 queries x 64 heads: the one-workgroup-per-query (flash) schedule;
+    # every query runs on the GPU, 12 sampled queries are checked
+    M = 320
+    rng = np.random.default_rng(207)
+    _run(207, 6000, 512, 64, "bf16", 512, 128, M, [5999] * M, [512] * M, [0] * M, [0] * M,
+         rng.integers(1, 129, M).tolist(), sample=sorted(rng.choice(M, 12, replace=False).tolist()))
