@@ -401,6 +401,50 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
   constexpr int QE = QF32 ? 4 : 2;  // query element bytes
   const rsrc_t r_q = make_rsrc(static_cast<const char *>(q_any) + (int64_t)m * H * D * QE, (uint32_t)(H * D * QE));
 
+  // ---- per chunk: sources of this wave's tiles (all index loads in one
+  // batch) and the first unit's loads; the first chunk's go out before the
+  // query staging so their latency overlaps it ----
+  uint32_t coff[MAXT], soff[MAXT], vcoff[MAXT], vsoff[MAXT];
+  float sks[MAXT];
+  KeyUnit<D> cur;
+  VPiece vp;
+  auto prepare_chunk = [&](int ct0) {
+    const int ntiles = min(CT, te - ct0);
+    // ---- sources of this wave's tiles: all index loads of the chunk in one batch ----
+    int32_t jv[MAXT];
+    float rv[MAXT];
+#pragma unroll
+    for (int i = 0; i < MAXT; ++i) {
+      const int t = ct0 + wv + kDW * i;
+      jv[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_topk, (uint32_t)(16 * t + row) * 4u, 0, 0);
+      rv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_wsc, (uint32_t)(16 * (t - TM) + row) * 4u, 0, 0));
+    }
+    // (selects, not branches: a branch would pull each load down to its use)
+#pragma unroll
+    for (int i = 0; i < MAXT; ++i) {
+      const int t = ct0 + wv + kDW * i;
+      const int slot = 16 * t + row;             // Top-K slot (main tiles)
+      const int wi = 16 * (t - TM) + row;        // window row (window tiles)
+      const int32_t j = jv[i];
+      const bool is_main = t < TM;
+      const bool okm = slot < K && j >= 0 && j < vis;
+      const uint32_t cm = okm ? (uint32_t)j * (D / 2) + quad * (D / 8) : kOutOfRange;
+      const uint32_t cw = (uint32_t)wi * D + quad * (D / 4);  // past the window rows: out of range
+      coff[i] = is_main ? cm : cw;
+      soff[i] = (is_main && okm) ? (uint32_t)j * (D / 16) + quad * (D / 64) : kOutOfRange;
+      // V slice piece of lane (key row, part quad): dims d0 + 16*quad .. +15
+      const int vd = d0 + 16 * quad;
+      vcoff[i] = is_main ? (okm ? (uint32_t)j * (D / 2) + vd / 2 : kOutOfRange) : (uint32_t)wi * D + vd;
+      vsoff[i] = (is_main && okm) ? (uint32_t)j * (D / 16) + vd / 16 : kOutOfRange;
+      sks[i] = is_main ? (okm ? 1.0f : 0.0f) : ((wi < wcount) ? rv[i] : 0.0f);
+    }
+    if (wv < ntiles) {
+      load_key_unit<D>(cur, ct0 + wv < TM, r_codes, r_win, r_scales, coff[0], soff[0]);
+      load_vpiece<D>(vp, ct0 + wv < TM, r_codes, r_win, r_scales, vcoff[0], vsoff[0]);
+    }
+  };
+  if (tb < te) prepare_chunk(tb);
+
   // ---- queries: staged once per workgroup as f16 [head][dim] in LDS (fp32:
   // hi and lo parts), then each wave keeps its MFMA A operands in registers:
   // lane (head row, quad) holds dims quad*(D/4) + 8*kk .. +7 ----
@@ -451,47 +495,14 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
   for (int ct0 = tb; ct0 < te; ct0 += CT) {
     const int ntiles = min(CT, te - ct0);  // even
     const int nc = 16 * ntiles;
-    if (ct0 > tb) __syncthreads();         // previous chunk's LDS reads are done
-    // ---- sources of this wave's tiles: all index loads of the chunk in one batch ----
-    int32_t jv[MAXT];
-    float rv[MAXT];
-#pragma unroll
-    for (int i = 0; i < MAXT; ++i) {
-      const int t = ct0 + wv + kDW * i;
-      jv[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_topk, (uint32_t)(16 * t + row) * 4u, 0, 0);
-      rv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_wsc, (uint32_t)(16 * (t - TM) + row) * 4u, 0, 0));
-    }
-    // (selects, not branches: a branch would pull each load down to its use)
-    uint32_t coff[MAXT], soff[MAXT], vcoff[MAXT], vsoff[MAXT];
-    float sks[MAXT];
-#pragma unroll
-    for (int i = 0; i < MAXT; ++i) {
-      const int t = ct0 + wv + kDW * i;
-      const int slot = 16 * t + row;             // Top-K slot (main tiles)
-      const int wi = 16 * (t - TM) + row;        // window row (window tiles)
-      const int32_t j = jv[i];
-      const bool is_main = t < TM;
-      const bool okm = slot < K && j >= 0 && j < vis;
-      const uint32_t cm = okm ? (uint32_t)j * (D / 2) + quad * (D / 8) : kOutOfRange;
-      const uint32_t cw = (uint32_t)wi * D + quad * (D / 4);  // past the window rows: out of range
-      coff[i] = is_main ? cm : cw;
-      soff[i] = (is_main && okm) ? (uint32_t)j * (D / 16) + quad * (D / 64) : kOutOfRange;
-      // V slice piece of lane (key row, part quad): dims d0 + 16*quad .. +15
-      const int vd = d0 + 16 * quad;
-      vcoff[i] = is_main ? (okm ? (uint32_t)j * (D / 2) + vd / 2 : kOutOfRange) : (uint32_t)wi * D + vd;
-      vsoff[i] = (is_main && okm) ? (uint32_t)j * (D / 16) + vd / 16 : kOutOfRange;
-      sks[i] = is_main ? (okm ? 1.0f : 0.0f) : ((wi < wcount) ? rv[i] : 0.0f);
+    if (ct0 > tb) {
+      __syncthreads();                     // previous chunk's LDS reads are done
+      prepare_chunk(ct0);
     }
     // ---- S for this wave's tiles, one unit ahead in flight; V slice into LDS ----
     float4_t sacc[MAXT];
 #pragma unroll
     for (int i = 0; i < MAXT; ++i) sacc[i] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-    KeyUnit<D> cur;
-    VPiece vp;
-    if (wv < ntiles) {
-      load_key_unit<D>(cur, ct0 + wv < TM, r_codes, r_win, r_scales, coff[0], soff[0]);
-      load_vpiece<D>(vp, ct0 + wv < TM, r_codes, r_win, r_scales, vcoff[0], vsoff[0]);
-    }
 #pragma unroll
     for (int k = 0; k < 2 * MAXT; ++k) {
       const int i = k >> 1, h = k & 1;
