@@ -16,6 +16,7 @@
 // the inverse power of two is folded into w_h.  Products are therefore exact
 // and only the fp32 accumulation rounds.
 #include "csa2_internal.hpp"
+#include "csa2_indexer.hpp"
 
 namespace csa2 {
 
@@ -26,207 +27,6 @@ constexpr int kScanBlocks = kScanChunk / kBlock; // 2048 block maxima
 constexpr int kFilterBlocks = 1024;              // blocks per pool-filter workgroup
 constexpr int kRescoreEntries = 64;              // pool blocks per re-score workgroup
 
-// ---------------------------------------------------------------------------
-// per-wave query operands
-// ---------------------------------------------------------------------------
-
-template <int DI>
-struct IdxQuery {
-  half8_t a[DI / 32];  // A operand of MFMA t: lane (row m = l%16, quarter qq = l/16)
-                       // holds channels qq*DI/4 + 8t .. +7 of head m
-  float w[4];          // scaled weights of heads 4*qq + j (0 for missing heads)
-};
-
-CSA2_DEV float max_rows4(float v) {
-  uint32_t u = __float_as_uint(v);
-  auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  float a = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-  uint32_t ua = __float_as_uint(a);
-  auto s16 = __builtin_amdgcn_permlane16_swap(ua, ua, false, false);
-  return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-}
-
-// q: [H][DI] bf16 of this query, w: [H] fp32.  Lane (m, qq) loads the DI/4
-// contiguous channels it feeds to MFMA with 16-byte loads.
-template <int DI>
-CSA2_DEV void load_idx_query(const uint16_t *__restrict__ q, const float *__restrict__ w, int H,
-                             IdxQuery<DI> &Q) {
-  const int l = lane_id();
-  const int m = l & 15, qq = l >> 4;
-  constexpr int PER = DI / 4;
-  float v[PER];
-  float mx = 0.0f;
-  const uint4 *src = reinterpret_cast<const uint4 *>(q + m * DI + qq * PER);
-#pragma unroll
-  for (int k = 0; k < PER / 8; ++k) {
-    const uint4 x = (m < H) ? src[k] : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t wds[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[8 * k + 2 * i] = __uint_as_float(wds[i] << 16);
-      v[8 * k + 2 * i + 1] = __uint_as_float(wds[i] & 0xFFFF0000u);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) mx = fmaxf(mx, fabsf(v[i]));
-  mx = max_rows4(mx);
-  int e = 0;
-  (void)frexpf(mx, &e);
-  const int kf = (mx > 0.0f) ? 15 - e : 0;  // head max scaled into [2^14, 2^15)
-#pragma unroll
-  for (int t = 0; t < DI / 32; ++t)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) Q.a[t][i] = (_Float16)ldexpf(v[8 * t + i], kf);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int h = 4 * qq + j;
-    const int kh = __shfl(kf, h, 64);
-    Q.w[j] = (h < H) ? ldexpf(w[h], -kh) : 0.0f;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// one 16-position tile
-// ---------------------------------------------------------------------------
-
-// The codes this lane feeds into the tile: DI/8 bytes of one row.
-template <int DI>
-struct LaneCodes {
-  uint32_t w[DI / 32];
-  uint32_t s;  // DI/64 scale bytes (little-endian)
-};
-
-template <int DI>
-CSA2_DEV void load_lane_codes(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, int64_t row,
-                              int qq, LaneCodes<DI> &c) {
-  const uint8_t *cp = codes + row * (DI / 2) + qq * (DI / 8);
-  const uint8_t *sp = scales + row * (DI / 16) + qq * (DI / 64);
-  if constexpr (DI == 64) {
-    const uint2 x = *reinterpret_cast<const uint2 *>(cp);
-    c.w[0] = x.x;
-    c.w[1] = x.y;
-    c.s = *sp;
-  } else if constexpr (DI == 128) {
-    const uint4 x = *reinterpret_cast<const uint4 *>(cp);
-    c.w[0] = x.x;
-    c.w[1] = x.y;
-    c.w[2] = x.z;
-    c.w[3] = x.w;
-    c.s = *reinterpret_cast<const uint16_t *>(sp);
-  } else {
-    static_assert(DI == 256, "indexer dim");
-    const uint4 x = reinterpret_cast<const uint4 *>(cp)[0];
-    const uint4 y = reinterpret_cast<const uint4 *>(cp)[1];
-    c.w[0] = x.x; c.w[1] = x.y; c.w[2] = x.z; c.w[3] = x.w;
-    c.w[4] = y.x; c.w[5] = y.y; c.w[6] = y.z; c.w[7] = y.w;
-    c.s = *reinterpret_cast<const uint32_t *>(sp);
-  }
-}
-
-// max(x, 0) and max(a, b) as one v_med3_f32 each.  Scores are finite or
-// -inf (never NaN), and for such values the median with FLT_MAX is exactly
-// the maximum; fmaxf would add NaN canonicalisations (and a +inf bound is
-// folded back into fmaxf by the compiler).
-CSA2_DEV float relu_f(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.40282347e38f); }
-CSA2_DEV float max_f(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, 3.40282347e38f); }
-
-// max over the 8 lanes of each half-row (finite or -inf values)
-CSA2_DEV float max8_scores(float v) {
-  v = max_f(v, dpp_f<kDppXor1>(v));
-  v = max_f(v, dpp_f<kDppXor2>(v));
-  return max_f(v, dpp_f<kDppHalfMirror>(v));
-}
-
-// This lane's share of the score of position (lane % 16) of the tile: the
-// weighted ReLU of its four heads 4*(lane/16) + j.  The score is the sum of
-// the four quarters' shares, added as (q0 + q2) + (q1 + q3).
-template <int DI>
-CSA2_DEV float tile_partial(const IdxQuery<DI> &Q, const LaneCodes<DI> &c) {
-  _Float16 sc[(DI / 64 > 0) ? DI / 64 : 1];
-  if constexpr (DI == 64) {
-    sc[0] = e4m3x2_to_f16(c.s)[0];
-  } else if constexpr (DI == 128) {
-    const half2_t s2 = e4m3x2_to_f16(c.s);
-    sc[0] = s2[0];
-    sc[1] = s2[1];
-  } else {
-    const half2_t s2 = e4m3x2_to_f16(c.s);
-    const half2_t s3 = e4m3x2_to_f16(c.s >> 16);
-    sc[0] = s2[0]; sc[1] = s2[1]; sc[2] = s3[0]; sc[3] = s3[1];
-  }
-  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int t = 0; t < DI / 32; ++t) {
-    const half8_t b = fp4x8_dequant_f16(c.w[t], sc[t / 2]);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Q.a[t], b, acc, 0, 0, 0);
-  }
-  float part = Q.w[0] * relu_f(acc[0]);
-  part = fmaf(Q.w[1], relu_f(acc[1]), part);
-  part = fmaf(Q.w[2], relu_f(acc[2]), part);
-  part = fmaf(Q.w[3], relu_f(acc[3]), part);
-  return part;
-}
-
-// Score of position (lane % 16) of the tile, returned in all four quarters.
-template <int DI>
-CSA2_DEV float tile_score(const IdxQuery<DI> &Q, const LaneCodes<DI> &c) {
-  return sum_rows4(tile_partial<DI>(Q, c));
-}
-
-// Scores of four tiles from their lane shares p0..p3 with three lane swaps:
-// row r (lanes 16r .. 16r+15) returns the 16 scores of tile kRowTile[r].
-// Same addition order as sum_rows4, so scores match tile_score bit for bit.
-CSA2_DEV int row_tile(int row) { return ((row & 1) << 1) | (row >> 1); }  // rows hold tiles 0, 2, 1, 3
-CSA2_DEV float tile_scores_x4(float p0, float p1, float p2, float p3) {
-  // permlane32_swap(x, y): x keeps its low half and takes y's low half; y takes x's high half
-  const auto a2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
-  const float a = __uint_as_float(a2[0]) + __uint_as_float(a2[1]);   // [t0 q0+q2, t0 q1+q3, t1 .., t1 ..]
-  const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p2), __float_as_uint(p3), false, false);
-  const float b = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);   // same for tiles 2, 3
-  // permlane16_swap(x, y): odd rows of x trade places with even rows of y
-  const auto c2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return __uint_as_float(c2[0]) + __uint_as_float(c2[1]);
-}
-
-// Loads of one lane relative to a chunk: `row` counts from the chunk's first
-// entry, so the offsets stay 32-bit and the bases stay scalar.  The scan
-// reads every byte exactly once, so the loads are non-temporal (streamed
-// past the caches), which lifts the achievable HBM read rate.
-template <int DI>
-CSA2_DEV void load_lane_codes_rel(const uint8_t *__restrict__ cbase, const uint8_t *__restrict__ sbase,
-                                  uint32_t row, uint32_t qq, LaneCodes<DI> &c) {
-  const uint32_t co = row * (DI / 2) + qq * (DI / 8);
-  const uint32_t so = row * (DI / 16) + qq * (DI / 64);
-  if constexpr (DI == 64) {
-    const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(cbase + co));
-    c.w[0] = x[0];
-    c.w[1] = x[1];
-    c.s = __builtin_nontemporal_load(sbase + so);
-  } else if constexpr (DI == 128) {
-    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cbase + co));
-    c.w[0] = x[0];
-    c.w[1] = x[1];
-    c.w[2] = x[2];
-    c.w[3] = x[3];
-    c.s = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(sbase + so));
-  } else {
-    static_assert(DI == 256, "indexer dim");
-    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cbase + co));
-    const u32x4_t y = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cbase + co + 16));
-    c.w[0] = x[0]; c.w[1] = x[1]; c.w[2] = x[2]; c.w[3] = x[3];
-    c.w[4] = y[0]; c.w[5] = y[1]; c.w[6] = y[2]; c.w[7] = y[3];
-    c.s = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sbase + so));
-  }
-}
-
-CSA2_DEV int64_t visible_entries(const int32_t *seq_len, const int32_t *q_seq, const int32_t *q_pos, int ratio,
-                                 int m, int *s_out) {
-  const int s = q_seq[m];
-  *s_out = s;
-  const int64_t lim = ((int64_t)q_pos[m] + 1) / ratio;
-  const int64_t v = min<int64_t>((int64_t)seq_len[s], lim);
-  return v > 0 ? v : 0;
-}
 
 // ---------------------------------------------------------------------------
 // kernels
@@ -636,65 +436,44 @@ __global__ __launch_bounds__(256) void k_rescore(const uint8_t *__restrict__ cod
   }
 }
 
-// Top-K over the re-scored pool, one workgroup (1024 threads) per query.
-// Thread t owns slots [t*PER, (t+1)*PER); slot order equals position order
-// because the pool is ascending, so ties on the score resolve to the lower
-// slot and the compaction below emits positions in ascending order.  Radix
-// passes count into one 256-bin histogram per wave, then merge.
-template <int PER>
-__global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ pscore,
-                                                      const int32_t *__restrict__ pool,
-                                                      const int32_t *__restrict__ pool_count, int P, int K,
-                                                      int32_t *__restrict__ topk_out, float *__restrict__ topk_score) {
-  __shared__ __attribute__((aligned(16))) uint32_t s_wh[16 * 256];
-  __shared__ uint32_t s_h[256];
-  __shared__ int s_scan[17];
-  __shared__ int s_digit, s_rem, s_cnt;
-  const int m = blockIdx.x;
+// Top-K by radix select over the scores of one query's slots, run by a
+// workgroup of NT threads: thread t owns slots [t*PER, (t+1)*PER), sv[] their
+// scores (-inf: no candidate).  The ranking is (score desc, slot asc); the
+// selected slots are handed to emit(rank, i, score) in ascending slot order
+// (i the thread-local slot index, rank the output position).  Radix passes
+// count into one 256-bin histogram per wave, then merge.  Returns the number
+// selected, min(K, #candidates).
+template <int NT>
+struct SelectLds {
+  uint32_t wh[NT / 64 * 256];
+  uint32_t h[256];
+  int scan[NT / 64 + 1];
+  int digit, rem, cnt;
+};
+
+template <int NT, int PER, typename Emit>
+CSA2_DEV int select_topk(const float (&sv)[PER], int K, SelectLds<NT> &sm, Emit emit) {
+  constexpr int NW = NT / 64;
   const int wv = threadIdx.x >> 6;
-  const int cnt = min(pool_count[m], P);
-  const int nslots = 8 * cnt;
-  const float *ps = pscore + (int64_t)m * 8 * P;
   uint32_t key[PER];
-  float sv[PER];                 // the scores themselves, for the score output
-  int32_t blk[PER / kBlock];     // pool blocks of this thread's slots, loaded up front
-  const int32_t *pl = pool + (int64_t)m * P;
-#pragma unroll
-  for (int b = 0; b < PER / kBlock; ++b) blk[b] = pl[min((int)threadIdx.x * (PER / kBlock) + b, max(cnt, 1) - 1)];
-  int nvalid = 0;
-  if ((threadIdx.x + 1) * PER <= nslots) {
-    const float4 *src = reinterpret_cast<const float4 *>(ps + threadIdx.x * PER);
-#pragma unroll
-    for (int k = 0; k < PER / 4; ++k) {
-      const float4 v = src[k];
-      sv[4 * k] = v.x; sv[4 * k + 1] = v.y; sv[4 * k + 2] = v.z; sv[4 * k + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int slot = threadIdx.x * PER + i;
-      sv[i] = (slot < nslots) ? ps[slot] : -INFINITY;
-    }
-  }
 #pragma unroll
   for (int i = 0; i < PER; ++i) key[i] = (sv[i] > -INFINITY) ? f2key(sv[i]) : 0u;
+  int nvalid = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) nvalid += key[i] != 0u;
   int total;
-  (void)block_exclusive_scan<1024>(nvalid, s_scan, &total);
+  (void)block_exclusive_scan<NT>(nvalid, sm.scan, &total);
   const int Kp = min(K, total);
-  int32_t *out = topk_out + (int64_t)m * K;
-  float *osc = topk_score ? topk_score + (int64_t)m * K : nullptr;
   uint32_t kstar = 0xFFFFFFFFu, kmask = 0xFFFFFFFFu;
   int rem = 0;
   if (Kp > 0) {
     uint32_t prefix = 0, mask = 0;
     rem = Kp;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = threadIdx.x; i < 16 * 256 / 4; i += blockDim.x)
-        reinterpret_cast<uint4 *>(s_wh)[i] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = threadIdx.x; i < NW * 256 / 4; i += NT)
+        reinterpret_cast<uint4 *>(sm.wh)[i] = make_uint4(0u, 0u, 0u, 0u);
       __syncthreads();
-      uint32_t *wh = s_wh + wv * 256;
+      uint32_t *wh = sm.wh + wv * 256;
       // Scores cluster in a few digit values (the high digits especially), so
       // the lanes of a wave would hit one LDS counter together: each thread
       // first folds its keys into at most two (digit, count) pairs.
@@ -710,20 +489,20 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ 
       if (c0) atomicAdd(&wh[d0], c0);
       if (c1) atomicAdd(&wh[d1], c1);
       __syncthreads();
-      if (threadIdx.x < 256) {
+      for (int i = threadIdx.x; i < 256; i += NT) {
         uint32_t t = 0;
 #pragma unroll
-        for (int w = 0; w < 16; ++w) t += s_wh[w * 256 + threadIdx.x];
-        s_h[threadIdx.x] = t;
+        for (int w = 0; w < NW; ++w) t += sm.wh[w * 256 + i];
+        sm.h[i] = t;
       }
       __syncthreads();
-      find_digit(s_h, rem, &s_digit, &s_rem, &s_cnt);
+      find_digit(sm.h, rem, &sm.digit, &sm.rem, &sm.cnt);
       __syncthreads();
-      prefix |= (uint32_t)s_digit << shift;
+      prefix |= (uint32_t)sm.digit << shift;
       mask |= 255u << shift;
-      rem = s_rem;
+      rem = sm.rem;
       // every key left in the cut's bin is taken: the lower digits cannot matter
-      if (s_cnt == rem) break;
+      if (sm.cnt == rem) break;
     }
     kstar = prefix;
     kmask = mask;
@@ -734,7 +513,7 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ 
 #pragma unroll
   for (int i = 0; i < PER; ++i) neq += (Kp > 0 && (key[i] & kmask) == kstar);
   int tmp;
-  int eq_before = block_exclusive_scan<1024>(neq, s_scan, &tmp);
+  int eq_before = block_exclusive_scan<NT>(neq, sm.scan, &tmp);
   bool sel[PER];
   int nsel = 0;
 #pragma unroll
@@ -748,19 +527,90 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float *__restrict__ 
     sel[i] = takeit;
     nsel += takeit;
   }
-  int rank = block_exclusive_scan<1024>(nsel, s_scan, &tmp);
+  int rank = block_exclusive_scan<NT>(nsel, sm.scan, &tmp);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (sel[i]) {
-      out[rank] = blk[i / kBlock] * kBlock + (i % kBlock);
-      if (osc) osc[rank] = sv[i];
+      emit(rank, i, sv[i]);
       ++rank;
     }
   }
-  for (int i = Kp + threadIdx.x; i < K; i += blockDim.x) {
+  return Kp;
+}
+
+// The PER scores of thread t's slots [t*PER, (t+1)*PER) of ps[0 .. n).
+// ps must be 16-byte aligned.
+template <int PER>
+CSA2_DEV void load_slot_scores(const float *__restrict__ ps, int n, float (&sv)[PER]) {
+  if ((int)(threadIdx.x + 1) * PER <= n) {
+    const float4 *src = reinterpret_cast<const float4 *>(ps + threadIdx.x * PER);
+#pragma unroll
+    for (int k = 0; k < PER / 4; ++k) {
+      const float4 v = src[k];
+      sv[4 * k] = v.x; sv[4 * k + 1] = v.y; sv[4 * k + 2] = v.z; sv[4 * k + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int slot = threadIdx.x * PER + i;
+      sv[i] = (slot < n) ? ps[slot] : -INFINITY;
+    }
+  }
+}
+
+// Top-K over the re-scored pool, one workgroup per query.  Slot 8e + r is
+// position 8*pool[e] + r; slot order equals position order because the pool
+// is ascending, so ties on the score resolve to the lower position and the
+// output comes out in ascending position order.
+template <int NT, int PER>
+__global__ __launch_bounds__(NT) void k_topk_select(const float *__restrict__ pscore,
+                                                    const int32_t *__restrict__ pool,
+                                                    const int32_t *__restrict__ pool_count, int P, int K,
+                                                    int32_t *__restrict__ topk_out, float *__restrict__ topk_score) {
+  __shared__ __attribute__((aligned(16))) SelectLds<NT> sm;
+  const int m = blockIdx.x;
+  const int cnt = min(pool_count[m], P);
+  int32_t blk[PER / kBlock];     // pool blocks of this thread's slots, loaded up front
+  const int32_t *pl = pool + (int64_t)m * P;
+#pragma unroll
+  for (int b = 0; b < PER / kBlock; ++b) blk[b] = pl[min((int)threadIdx.x * (PER / kBlock) + b, max(cnt, 1) - 1)];
+  float sv[PER];
+  load_slot_scores<PER>(pscore + (int64_t)m * 8 * P, 8 * cnt, sv);
+  int32_t *out = topk_out + (int64_t)m * K;
+  float *osc = topk_score ? topk_score + (int64_t)m * K : nullptr;
+  const int Kp = select_topk<NT, PER>(sv, K, sm, [&](int rank, int i, float v) {
+    out[rank] = blk[i / kBlock] * kBlock + (i % kBlock);
+    if (osc) osc[rank] = v;
+  });
+  for (int i = Kp + threadIdx.x; i < K; i += NT) {
     out[i] = -1;
     if (osc) osc[i] = __builtin_nanf("");
   }
+}
+
+// Pool of the top P blocks by (block max desc, block id asc) straight from
+// the block maxima, one workgroup per query: the blocks that hold a visible
+// position are the slots.  Used when every block of a query fits the
+// workgroup's registers.
+template <int NT, int PER>
+__global__ __launch_bounds__(NT) void k_block_select(const float *__restrict__ bmax, int64_t nb_stride,
+                                                     const int32_t *__restrict__ seq_len,
+                                                     const int32_t *__restrict__ q_seq,
+                                                     const int32_t *__restrict__ q_pos, int ratio, int P,
+                                                     int32_t *__restrict__ pool_out, int32_t *__restrict__ pool_count) {
+  __shared__ __attribute__((aligned(16))) SelectLds<NT> sm;
+  const int m = blockIdx.x;
+  int s;
+  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
+  const int nb = (int)((vis + kBlock - 1) / kBlock);
+  float sv[PER];
+  load_slot_scores<PER>(bmax + (int64_t)m * nb_stride, nb, sv);
+  int32_t *out = pool_out + (int64_t)m * P;
+  const int Kp = select_topk<NT, PER>(sv, P, sm, [&](int rank, int i, float) {
+    out[rank] = (int32_t)(threadIdx.x * PER + i);
+  });
+  for (int i = Kp + threadIdx.x; i < P; i += NT) out[i] = -1;
+  if (threadIdx.x == 0) pool_count[m] = Kp;
 }
 
 // ---------------------------------------------------------------------------
@@ -793,12 +643,16 @@ static int rescore_and_select(const csa2_fp4_cache &idx, const csa2_queries &qs,
   const dim3 g5((P + kRescoreEntries - 1) / kRescoreEntries, qs.m);
   hipLaunchKernelGGL(k_rescore<DI>, g5, dim3(256), 0, stream, idx.codes, idx.scales, idx.seq_start, idx.seq_len,
                      idx.ratio, qs.seq, qs.pos, q_idx, w_idx, heads, pool, pool_count, P, pscore);
-  if (8 * P <= 1024 * 16)
-    hipLaunchKernelGGL(k_topk_select<16>, dim3(qs.m), dim3(1024), 0, stream, pscore, pool, pool_count, P, K,
+  // 8P <= 32768 slots (P <= 4096)
+  if (8 * P <= 256 * 16)
+    hipLaunchKernelGGL((k_topk_select<256, 16>), dim3(qs.m), dim3(256), 0, stream, pscore, pool, pool_count, P, K,
                        topk_out, topk_score);
+  else if (8 * P <= 1024 * 16)
+    hipLaunchKernelGGL((k_topk_select<1024, 16>), dim3(qs.m), dim3(1024), 0, stream, pscore, pool, pool_count, P,
+                       K, topk_out, topk_score);
   else
-    hipLaunchKernelGGL(k_topk_select<32>, dim3(qs.m), dim3(1024), 0, stream, pscore, pool, pool_count, P, K,
-                       topk_out, topk_score);
+    hipLaunchKernelGGL((k_topk_select<1024, 32>), dim3(qs.m), dim3(1024), 0, stream, pscore, pool, pool_count, P,
+                       K, topk_out, topk_score);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 
@@ -858,20 +712,43 @@ int launch_index_full(const csa2_fp4_cache &idx, const csa2_queries &qs, const u
   }
 }
 
+int launch_rescore_select(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
+                          const float *w_idx, int heads, const int32_t *pool, const int32_t *pool_count, int P, int K,
+                          int32_t *topk_out, float *topk_score, float *pscore, hipStream_t stream) {
+  switch (idx.dim) {
+    case 64: return rescore_and_select<64>(idx, qs, q_idx, w_idx, heads, pool, pool_count, P, K, topk_out,
+                                           topk_score, pscore, stream);
+    case 128: return rescore_and_select<128>(idx, qs, q_idx, w_idx, heads, pool, pool_count, P, K, topk_out,
+                                             topk_score, pscore, stream);
+    case 256: return rescore_and_select<256>(idx, qs, q_idx, w_idx, heads, pool, pool_count, P, K, topk_out,
+                                             topk_score, pscore, stream);
+    default: return CSA2_ERR_UNSUPPORTED;
+  }
+}
+
+int launch_block_select(const float *bmax, int64_t nb_stride, int64_t nb_max, const csa2_fp4_cache &idx,
+                        const csa2_queries &qs, int P, int32_t *pool_out, int32_t *pool_count, hipStream_t stream) {
+  if (qs.m == 0) return CSA2_OK;
+#define CSA2_BSEL(NT, PER)                                                                                      \
+  hipLaunchKernelGGL((k_block_select<NT, PER>), dim3(qs.m), dim3(NT), 0, stream, bmax, nb_stride, idx.seq_len, \
+                     qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count)
+  if (nb_max <= 256 * 16) CSA2_BSEL(256, 16);
+  else if (nb_max <= 256 * 32) CSA2_BSEL(256, 32);
+  else if (nb_max <= 256 * 64) CSA2_BSEL(256, 64);
+  else if (nb_max <= 1024 * 32) CSA2_BSEL(1024, 32);
+  else if (nb_max <= kBlockSelectMax) CSA2_BSEL(1024, 64);
+  else return CSA2_ERR_UNSUPPORTED;
+#undef CSA2_BSEL
+  return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+}
+
 int launch_reindex(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx, const float *w_idx,
                    int heads, const int32_t *pool_in, const int32_t *pool_count, int P, int K, int32_t *topk_out,
                    float *topk_score, void *ws, hipStream_t stream) {
   const IndexWs L = index_ws_layout(idx.max_len, qs.m, P, K);
   float *pscore = reinterpret_cast<float *>(static_cast<char *>(ws) + L.pscore);
-  switch (idx.dim) {
-    case 64: return rescore_and_select<64>(idx, qs, q_idx, w_idx, heads, pool_in, pool_count, P, K, topk_out,
-                                           topk_score, pscore, stream);
-    case 128: return rescore_and_select<128>(idx, qs, q_idx, w_idx, heads, pool_in, pool_count, P, K, topk_out,
-                                             topk_score, pscore, stream);
-    case 256: return rescore_and_select<256>(idx, qs, q_idx, w_idx, heads, pool_in, pool_count, P, K, topk_out,
-                                             topk_score, pscore, stream);
-    default: return CSA2_ERR_UNSUPPORTED;
-  }
+  return launch_rescore_select(idx, qs, q_idx, w_idx, heads, pool_in, pool_count, P, K, topk_out, topk_score,
+                               pscore, stream);
 }
 
 }  // namespace csa2

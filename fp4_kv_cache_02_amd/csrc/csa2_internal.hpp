@@ -31,6 +31,18 @@ int launch_reindex(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint
                    int heads, const int32_t *pool_in, const int32_t *pool_count, int pool_blocks, int top_k,
                    int32_t *topk_out, float *topk_score, void *ws, hipStream_t stream);
 
+// Stages shared with the flat indexer.  Block select: the pool of the top P
+// blocks per query straight from the block maxima bmax[m * nb_stride + b]
+// (nb_max >= every query's block count, at most kBlockSelectMax).  Re-score
+// and select: the Top-K positions of the given pools, pscore holding 8P
+// floats per query.
+constexpr int64_t kBlockSelectMax = 1024 * 64;
+int launch_block_select(const float *bmax, int64_t nb_stride, int64_t nb_max, const csa2_fp4_cache &idx,
+                        const csa2_queries &qs, int P, int32_t *pool_out, int32_t *pool_count, hipStream_t stream);
+int launch_rescore_select(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
+                          const float *w_idx, int heads, const int32_t *pool, const int32_t *pool_count, int P, int K,
+                          int32_t *topk_out, float *topk_score, float *pscore, hipStream_t stream);
+
 // ---- flat (prefill) indexer (csa2_prefill.hip) ----
 size_t flat_ws_bytes(int64_t max_len, int m, int top_k);
 int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,

@@ -1,20 +1,260 @@
 // CSA2 flat Top-K indexer for encoder prefill chunks (P4 section 二: encoder
-// groups select without a candidate pool).
+// groups select without a candidate pool; P1 section "Compressed Sparse
+// Attention 2 (CSA2)" for the score and for which compressed entries a token
+// may see).
+//
+// Scoring.  The queries of a prefill chunk share their sequence's indexer
+// cache, so scoring is a dense contraction [queries x heads] x [channels] x
+// [entries] and runs on MFMA.  A workgroup takes 16 queries of up to 8 heads
+// (128 rows = 8 row tiles; 8 queries for up to 16 heads) and keeps them as A
+// operands in the registers of each of its 4 waves (one per SIMD, so the
+// queries can sit in the accumulation registers); wave w streams the
+// 16-entry column tiles w, w + 4, ... of the cache.  Each column tile is
+// decoded once (FP4 -> exact f16) and meets every row tile: 32 MFMAs per
+// tile for 128 channels.  The epilogue takes the weighted ReLU over each
+// query's heads, masks entries the query may not see, reduces 8-entry blocks
+// to their maximum and writes it to bmax.  The entries that all workgroups
+// stream stay in L2, so the loads are plain (not streamed past the caches).
+//
+// Selection.  The flat Top-K lies inside the top K blocks by (block max desc,
+// block id asc): every block ranked above a block that holds a Top-K
+// position holds its own maximum position, ranked above that Top-K position,
+// and there are fewer than K of those.  So the block select keeps P = K
+// blocks per query, their 8K positions are re-scored and the Top-K is taken
+// from them, with the same stages as the decoder's Full layer.
 #include "csa2_internal.hpp"
+#include "csa2_indexer.hpp"
 
 namespace csa2 {
 
-size_t flat_ws_bytes(int64_t max_len, int m, int top_k) {
-  (void)max_len; (void)m; (void)top_k;
-  return 256;
+constexpr int kMqWaves = 4;  // waves per scoring workgroup: one per SIMD, so each has the full register file
+constexpr int kMqDepth = 3;  // column tiles of loads in flight ahead of the one being scored
+
+template <int DI, int RPQ>
+struct MqShape {
+  static constexpr int RT = (DI == 256) ? 4 : 8;  // row tiles held by every wave
+  static constexpr int QB = RT * 16 / RPQ;        // queries per workgroup
+  static constexpr int NG = QB / 4;               // groups of four queries
+  static constexpr int TPG = RPQ / 4;             // row tiles per group
+  static constexpr int KT = DI / 32;              // MFMAs per (row tile, column tile)
+  static_assert(NG >= 1 && (TPG == 2 || TPG == 4), "multi-query tiling");
+};
+
+// Grid: ceil(M / QB) workgroups of 64 * kMqWaves threads.  Rows of the
+// workgroup's A block: row = RPQ * qi + h (query m0 + qi, head h).  The
+// queries of one workgroup may belong to several sequences: each sequence is
+// one pass over its entries with the other queries left out.
+template <int DI, int RPQ>
+__global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__restrict__ codes,
+                                                           const uint8_t *__restrict__ scales,
+                                                           const int64_t *__restrict__ seq_start,
+                                                           const int32_t *__restrict__ seq_len, int ratio,
+                                                           const int32_t *__restrict__ q_seq,
+                                                           const int32_t *__restrict__ q_pos, int M,
+                                                           const uint16_t *__restrict__ q_idx,
+                                                           const float *__restrict__ w_idx, int H,
+                                                           float *__restrict__ bmax, int64_t nb_stride) {
+  using S = MqShape<DI, RPQ>;
+  constexpr int kNone = 0x7FFFFFFF;
+  __shared__ int s_seq[S::QB], s_vis[S::QB];
+  const int m0 = blockIdx.x * S::QB;
+  if (threadIdx.x < S::QB) {
+    const int m = m0 + threadIdx.x;
+    int s = kNone, v = 0;
+    if (m < M) {
+      int ss;
+      v = (int)visible_entries(seq_len, q_seq, q_pos, ratio, m, &ss);
+      s = ss;
+    }
+    s_seq[threadIdx.x] = s;
+    s_vis[threadIdx.x] = v;
+  }
+  const int l = lane_id(), n = l & 15, g = l >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  half8_t A[S::RT][S::KT];
+  float W[S::RT][4];
+#pragma unroll
+  for (int r = 0; r < S::RT; ++r) {
+    const int row = r * 16 + n;
+    const int qi = row / RPQ, h = row % RPQ;
+    const bool valid = (m0 + qi < M) && (h < H);
+    const int64_t mh = valid ? (int64_t)(m0 + qi) * H + h : 0;
+    load_query_rows<DI>(q_idx + mh * DI, valid, valid ? w_idx[mh] : 0.0f, A[r], W[r]);
+  }
+  __syncthreads();
+
+  // finished queries of the workgroup (bit q), uniform across the workgroup
+  uint32_t done = 0;
+#pragma unroll
+  for (int q = 0; q < S::QB; ++q)
+    if (s_seq[q] == kNone || s_vis[q] == 0) done |= 1u << q;
+  done = __builtin_amdgcn_readfirstlane(done);
+  constexpr uint32_t kAll = (S::QB == 32) ? 0xFFFFFFFFu : ((1u << S::QB) - 1u);
+
+  // bmax row of this lane's query in each group (group p, lane row g -> query 4p + row_tile(g))
+  int64_t brow[S::NG];
+#pragma unroll
+  for (int p = 0; p < S::NG; ++p) brow[p] = (int64_t)(m0 + 4 * p + row_tile(g)) * nb_stride;
+
+  while (done != kAll) {
+    // next sequence: the smallest one among the unfinished queries
+    int sc = kNone;
+#pragma unroll
+    for (int q = 0; q < S::QB; ++q)
+      if (!((done >> q) & 1u)) sc = min(sc, s_seq[q]);
+    sc = __builtin_amdgcn_readfirstlane(sc);
+    uint32_t act = 0;
+    int maxvis = 0, minvis = kNone;
+#pragma unroll
+    for (int q = 0; q < S::QB; ++q) {
+      if (!((done >> q) & 1u) && s_seq[q] == sc) {
+        act |= 1u << q;
+        maxvis = max(maxvis, s_vis[q]);
+        minvis = min(minvis, s_vis[q]);
+      }
+    }
+    act = __builtin_amdgcn_readfirstlane(act);
+    maxvis = __builtin_amdgcn_readfirstlane(maxvis);
+    minvis = __builtin_amdgcn_readfirstlane(minvis);
+    done |= act;
+    // visible entries of this lane's query in each group; -1: not in this pass
+    int vis_l[S::NG];
+#pragma unroll
+    for (int p = 0; p < S::NG; ++p) {
+      const int q = 4 * p + row_tile(g);
+      vis_l[p] = ((act >> q) & 1u) ? s_vis[q] : -1;
+    }
+    const int ntile = (maxvis + 15) / 16;
+    const int full_tiles = minvis / 16;  // tiles every query of the pass sees whole
+    const int64_t row0 = seq_start[sc];
+    const uint8_t *cbase = codes + row0 * (DI / 2);
+    const uint8_t *sbase = scales + row0 * (DI / 16);
+
+    // rows past the pass's visible range are clamped to its last entry (in bounds, never stored)
+    auto load = [&](int c, LaneCodes<DI> &buf) {
+      const int e = min(c * 16 + n, maxvis - 1);
+      load_lane_codes_rel<DI, false>(cbase, sbase, (uint32_t)e, (uint32_t)g, buf);
+    };
+    auto tile = [&](int c, const LaneCodes<DI> &cur) {
+      half8_t B[S::KT];
+      decode_keys<DI>(cur, B);
+      const bool masked = c >= full_tiles;
+#pragma unroll
+      for (int p = 0; p < S::NG; ++p) {
+        float part[S::TPG];
+#pragma unroll
+        for (int u = 0; u < S::TPG; ++u) {
+          const int r = p * S::TPG + u;
+          float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int t = 0; t < S::KT; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][t], B[t], acc, 0, 0, 0);
+          part[u] = weighted_relu4(W[r], acc);
+        }
+        float v;
+        if constexpr (S::TPG == 2) v = tile_scores_x2(part[0], part[1]);
+        else v = tile_scores_x4(part[0], part[1], part[2], part[3]);
+        if (masked && c * 16 + n >= vis_l[p]) v = -INFINITY;
+        v = max8_scores(v);
+        if ((n & 7) == 0 && vis_l[p] >= 0) bmax[brow[p] + 2 * c + (n >> 3)] = v;
+      }
+    };
+    // ring of kMqDepth + 1 column tiles: the loads of the next kMqDepth are in flight
+    constexpr int NBUF = kMqDepth + 1;
+    int c = wv;
+    if (c < ntile) {
+      LaneCodes<DI> buf[NBUF];
+#pragma unroll
+      for (int i = 0; i < kMqDepth; ++i) load(c + i * kMqWaves, buf[i]);
+      for (bool more = true; more;) {
+#pragma unroll
+        for (int k = 0; k < NBUF; ++k) {
+          if (more) {
+            load(c + kMqDepth * kMqWaves, buf[(k + kMqDepth) % NBUF]);
+            __builtin_amdgcn_sched_barrier(0);
+            tile(c, buf[k]);
+            c += kMqWaves;
+            more = c < ntile;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+// Workspace of the flat indexer, all offsets 256-byte aligned.
+struct FlatWs {
+  size_t bmax, pool, pool_count, pscore, total;
+  int64_t nb_stride;  // block slots per query (covers every column tile's pair of blocks)
+};
+
+static FlatWs flat_ws_layout(int64_t max_len, int m, int top_k) {
+  FlatWs w{};
+  const int64_t pairs = (max_len + 15) / 16;
+  w.nb_stride = ((2 * pairs + 63) / 64) * 64;
+  if (w.nb_stride == 0) w.nb_stride = 64;
+  size_t off = 0;
+  w.bmax = off;       off = align256(off + sizeof(float) * (size_t)m * (size_t)w.nb_stride);
+  w.pool = off;       off = align256(off + sizeof(int32_t) * (size_t)m * (size_t)top_k);
+  w.pool_count = off; off = align256(off + sizeof(int32_t) * (size_t)m);
+  w.pscore = off;     off = align256(off + sizeof(float) * (size_t)m * 8 * (size_t)top_k);
+  w.total = off;
+  return w;
+}
+
+size_t flat_ws_bytes(int64_t max_len, int m, int top_k) { return flat_ws_layout(max_len, m, top_k).total; }
+
+template <int DI, int RPQ>
+static void launch_score_mq(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
+                            const float *w_idx, int heads, float *bmax, int64_t nb_stride, hipStream_t stream) {
+  using S = MqShape<DI, RPQ>;
+  const dim3 grid((unsigned)((qs.m + S::QB - 1) / S::QB));
+  hipLaunchKernelGGL((k_score_mq<DI, RPQ>), grid, dim3(64 * kMqWaves), 0, stream, idx.codes, idx.scales,
+                     idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, qs.m, q_idx, w_idx, heads, bmax,
+                     nb_stride);
 }
 
 int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
                       const float *w_idx, int heads, int top_k, int32_t *topk_out, float *topk_score, void *ws,
                       hipStream_t stream) {
-  (void)idx; (void)qs; (void)q_idx; (void)w_idx; (void)heads; (void)top_k; (void)topk_out; (void)topk_score;
-  (void)ws; (void)stream;
-  return CSA2_ERR_UNSUPPORTED;
+  if (qs.m == 0) return CSA2_OK;
+  if (heads < 1 || heads > 16) return CSA2_ERR_UNSUPPORTED;
+  const int64_t nb_max = (idx.max_len + kBlock - 1) / kBlock;
+  if (nb_max > kBlockSelectMax) return CSA2_ERR_UNSUPPORTED;
+  if (idx.dim != 64 && idx.dim != 128 && idx.dim != 256) return CSA2_ERR_UNSUPPORTED;
+  const FlatWs L = flat_ws_layout(idx.max_len, qs.m, top_k);
+  char *base = static_cast<char *>(ws);
+  float *bmax = reinterpret_cast<float *>(base + L.bmax);
+  int32_t *pool = reinterpret_cast<int32_t *>(base + L.pool);
+  int32_t *pool_count = reinterpret_cast<int32_t *>(base + L.pool_count);
+  float *pscore = reinterpret_cast<float *>(base + L.pscore);
+  if (idx.max_len > 0) {
+    const bool wide = heads > 8;
+    switch (idx.dim) {
+      case 64:
+        if (wide) launch_score_mq<64, 16>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
+        else launch_score_mq<64, 8>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
+        break;
+      case 128:
+        if (wide) launch_score_mq<128, 16>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
+        else launch_score_mq<128, 8>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
+        break;
+      default:
+        if (wide) launch_score_mq<256, 16>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
+        else launch_score_mq<256, 8>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
+        break;
+    }
+    if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
+  }
+  int st = launch_block_select(bmax, L.nb_stride, nb_max > 0 ? nb_max : 1, idx, qs, top_k, pool, pool_count,
+                               stream);
+  if (st != CSA2_OK) return st;
+  return launch_rescore_select(idx, qs, q_idx, w_idx, heads, pool, pool_count, top_k, top_k, topk_out, topk_score,
+                               pscore, stream);
 }
 
 }  // namespace csa2

@@ -36,6 +36,7 @@ TAG_SWA = 6       # pre-quantisation sliding-window rows
 TAG_LEN = 7       # ragged sequence lengths
 TAG_IDX_KEY = 8   # pre-quantisation indexer-key rows when the indexer is exercised on its own
 TAG_IDX_LIST = 9  # synthetic Top-K lists when attention is exercised on its own
+TAG_FP4_BYTES = 10  # raw FP4 cache bytes (codes and scale bytes drawn directly)
 
 
 def rng(cfg: int, tag: int, layer: int = 0, seq: int = 0, chunk: int = 0) -> np.random.Generator:
@@ -135,6 +136,18 @@ def q_main(cfg: int, layer: int, m: int, heads: int, dim: int, dtype: str) -> np
 def swa_rows(cfg: int, layer: int, seq: int, nrows: int, dim: int, row0: int = 0) -> np.ndarray:
     """Pre-quantisation sliding-window rows of one layer and sequence."""
     return gaussian_rows(cfg, TAG_SWA, layer, seq, row0, nrows, dim)
+
+
+def fp4_bytes(cfg: int, layer: int, nrows: int, dim: int):
+    """Raw bytes of an FP4 cache [nrows, dim]: code bytes uniform over 0..255
+    (two 4-bit codes each) and scale bytes uniform over 0x20..0x3F (positive
+    E4M3 codes of the values 1/8 .. 15/8), drawn directly so that large caches
+    need no quantisation pass.  Returns (codes uint8 [nrows, dim/2], scales
+    uint8 [nrows, dim/16])."""
+    g = rng(cfg, TAG_FP4_BYTES, layer)
+    codes = g.integers(0, 256, size=(nrows, dim // 2), dtype=np.uint8)
+    scales = g.integers(0x20, 0x40, size=(nrows, dim // 16), dtype=np.uint8)
+    return codes, scales
 
 
 def ragged_lengths(cfg: int, n: int, lo: int, hi: int) -> np.ndarray:
