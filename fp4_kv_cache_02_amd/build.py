@@ -12,6 +12,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
 SOURCES = ["csa2_api.hip", "csa2_codec.hip", "csa2_index.hip", "csa2_attn.hip", "csa2_prefill.hip"]
+# per-source code generation options
+EXTRA = {
+    # MFMA results in vector registers: the epilogue reads them with vector
+    # instructions, which cannot take accumulation registers as operands
+    "csa2_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 ARCH = os.environ.get("CSA2_OFFLOAD_ARCH", "gfx950")
 
 
@@ -32,7 +38,7 @@ def build(verbose: bool = False) -> str:
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                # keep private arrays in registers: never move them into spare LDS
                "-mllvm", "-disable-promote-alloca-to-lds",
-               "-Wno-unused-result", os.path.join(CSRC, src), "-o", obj]
+               "-Wno-unused-result", *EXTRA.get(src, []), os.path.join(CSRC, src), "-o", obj]
         jobs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
         objs.append(obj)
     failed = False

@@ -230,18 +230,9 @@ struct KeyUnit {
   uint32_t s[(D / 64 + 3) / 4];
 };
 
-// Raw buffer descriptor over `bytes` bytes (gfx9 data format word).  Loads
-// at offsets past the end return zeros without touching memory, which is
-// how the decode kernel reads empty, padded or invisible keys and heads
-// beyond H: every load is unconditional.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-CSA2_DEV rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-// An offset past every descriptor used here, with room for the per-load
-// additions (< 4 KB) without wrapping: descriptors stay below kMaxRsrcBytes.
-constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr int64_t kMaxRsrcBytes = 0x7FFF0000;
+// Buffer loads (make_rsrc, kOutOfRange) make every load unconditional: the
+// decode kernel reads empty, padded or invisible keys and heads beyond H at
+// out-of-range offsets, which return zeros.
 
 template <int BYTES>
 CSA2_DEV void buffer_load_words(uint32_t *dst, rsrc_t r, uint32_t off) {

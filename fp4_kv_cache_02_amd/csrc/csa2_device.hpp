@@ -110,6 +110,23 @@ CSA2_DEV uint32_t f2key(float f) {
 }
 
 // ---------------------------------------------------------------------------
+// raw buffer descriptors
+// ---------------------------------------------------------------------------
+
+// Raw buffer descriptor over `bytes` bytes (gfx9 data format word).  Loads
+// at offsets past the end return zeros and stores there are dropped, without
+// touching memory, so predicated accesses need no branch.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+CSA2_DEV rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// An offset past every descriptor used here, with room for per-access
+// additions (< 2 GB - kMaxRsrcBytes) without wrapping: descriptors stay
+// below kMaxRsrcBytes.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int64_t kMaxRsrcBytes = 0x7FFF0000;
+
+// ---------------------------------------------------------------------------
 // cross-lane helpers
 // ---------------------------------------------------------------------------
 

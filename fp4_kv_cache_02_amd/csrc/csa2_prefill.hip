@@ -25,10 +25,12 @@
 #include "csa2_internal.hpp"
 #include "csa2_indexer.hpp"
 
+#include <type_traits>
+
 namespace csa2 {
 
 constexpr int kMqWaves = 4;  // waves per scoring workgroup: one per SIMD, so each has the full register file
-constexpr int kMqDepth = 3;  // column tiles of loads in flight ahead of the one being scored
+constexpr int kMqValuPerMfma = 4;  // vector instructions scheduled between consecutive MFMAs
 
 template <int DI, int RPQ>
 struct MqShape {
@@ -39,6 +41,38 @@ struct MqShape {
   static constexpr int KT = DI / 32;              // MFMAs per (row tile, column tile)
   static_assert(NG >= 1 && (TPG == 2 || TPG == 4), "multi-query tiling");
 };
+
+// Block maxima of one column tile for NG groups of four queries at once.
+// v[p] holds, in lane (row g, column n), the score of entry n for query
+// 4p + row_tile(g); each half-row (8 lanes) is one block.  The groups are
+// spread over the lanes while they are reduced: the first exchange (lane i
+// with 7 - i) halves the groups each lane keeps, the second (i with i ^ 1)
+// halves them again, the third (i with i ^ 2) only takes the maximum.  Lane i
+// (= n % 8) ends with the block maximum of group lane_group<NG>(i); two lanes
+// hold each group and lane_stores<NG>(i) picks one.
+template <int NG>
+CSA2_DEV float block_max_groups(const float (&v)[NG], int i) {
+  if constexpr (NG == 4) {
+    const bool q1 = i >= 4, odd = (i & 1) != 0;
+    const float sa = q1 ? v[0] : v[2], sb = q1 ? v[1] : v[3];
+    const float ka = q1 ? v[2] : v[0], kb = q1 ? v[3] : v[1];
+    const float wa = max_f(ka, dpp_f<kDppHalfMirror>(sa));
+    const float wb = max_f(kb, dpp_f<kDppHalfMirror>(sb));
+    const float x = max_f(odd ? wb : wa, dpp_f<kDppXor1>(odd ? wa : wb));
+    return max_f(x, dpp_f<kDppXor2>(x));
+  } else if constexpr (NG == 2) {
+    const bool q1 = i >= 4;
+    float x = max_f(q1 ? v[1] : v[0], dpp_f<kDppHalfMirror>(q1 ? v[0] : v[1]));
+    x = max_f(x, dpp_f<kDppXor1>(x));
+    return max_f(x, dpp_f<kDppXor2>(x));
+  } else {
+    return max8_scores(v[0]);
+  }
+}
+template <int NG>
+CSA2_DEV int lane_group(int i) { return NG == 4 ? 2 * (i >> 2) + (i & 1) : NG == 2 ? (i >> 2) : 0; }
+template <int NG>
+CSA2_DEV bool lane_stores(int i) { return NG == 4 ? (i & 2) == 0 : NG == 2 ? (i & 3) == 0 : i == 0; }
 
 // Grid: ceil(M / QB) workgroups of 64 * kMqWaves threads.  Rows of the
 // workgroup's A block: row = RPQ * qi + h (query m0 + qi, head h).  The
@@ -82,6 +116,13 @@ __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__res
     const int64_t mh = valid ? (int64_t)(m0 + qi) * H + h : 0;
     load_query_rows<DI>(q_idx + mh * DI, valid, valid ? w_idx[mh] : 0.0f, A[r], W[r]);
   }
+  // the query operands are only read by MFMA: keep them in the accumulation
+  // registers, which leaves the vector registers to the accumulators and the
+  // epilogue (the vector ALUs cannot read accumulation registers)
+#pragma unroll
+  for (int r = 0; r < S::RT; ++r)
+#pragma unroll
+    for (int t = 0; t < S::KT; ++t) asm volatile("" : "+a"(A[r][t]));
   __syncthreads();
 
   // finished queries of the workgroup (bit q), uniform across the workgroup
@@ -92,10 +133,10 @@ __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__res
   done = __builtin_amdgcn_readfirstlane(done);
   constexpr uint32_t kAll = (S::QB == 32) ? 0xFFFFFFFFu : ((1u << S::QB) - 1u);
 
-  // bmax row of this lane's query in each group (group p, lane row g -> query 4p + row_tile(g))
-  int64_t brow[S::NG];
-#pragma unroll
-  for (int p = 0; p < S::NG; ++p) brow[p] = (int64_t)(m0 + 4 * p + row_tile(g)) * nb_stride;
+  const int i8 = n & 7;
+  const int q_store = 4 * lane_group<S::NG>(i8) + row_tile(g);  // query whose block maximum this lane stores
+  // the workgroup's rows of bmax; stores of lanes with nothing to store go past its end
+  const rsrc_t rb = make_rsrc(bmax + (int64_t)m0 * nb_stride, (uint32_t)(min(S::QB, M - m0) * nb_stride * 4));
 
   while (done != kAll) {
     // next sequence: the smallest one among the unfinished queries
@@ -118,15 +159,14 @@ __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__res
     maxvis = __builtin_amdgcn_readfirstlane(maxvis);
     minvis = __builtin_amdgcn_readfirstlane(minvis);
     done |= act;
-    // visible entries of this lane's query in each group; -1: not in this pass
+    // visible entries of this lane's query in each group (tail tiles only)
     int vis_l[S::NG];
 #pragma unroll
-    for (int p = 0; p < S::NG; ++p) {
-      const int q = 4 * p + row_tile(g);
-      vis_l[p] = ((act >> q) & 1u) ? s_vis[q] : -1;
-    }
+    for (int p = 0; p < S::NG; ++p) vis_l[p] = s_vis[4 * p + row_tile(g)];
+    const uint32_t soff = (lane_stores<S::NG>(i8) && ((act >> q_store) & 1u))
+                              ? (uint32_t)((q_store * nb_stride + (n >> 3)) * 4) : kOutOfRange;
     const int ntile = (maxvis + 15) / 16;
-    const int full_tiles = minvis / 16;  // tiles every query of the pass sees whole
+    const int full = minvis / 16;  // tiles every query of the pass sees whole
     const int64_t row0 = seq_start[sc];
     const uint8_t *cbase = codes + row0 * (DI / 2);
     const uint8_t *sbase = scales + row0 * (DI / 16);
@@ -136,48 +176,87 @@ __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__res
       const int e = min(c * 16 + n, maxvis - 1);
       load_lane_codes_rel<DI, false>(cbase, sbase, (uint32_t)e, (uint32_t)g, buf);
     };
-    auto tile = [&](int c, const LaneCodes<DI> &cur) {
-      half8_t B[S::KT];
-      decode_keys<DI>(cur, B);
-      const bool masked = c >= full_tiles;
+    // all row tiles against one column tile: RT independent accumulation chains
+    auto mfmas = [&](const half8_t (&B)[S::KT], float4_t (&acc)[S::RT]) {
+#pragma unroll
+      for (int t = 0; t < S::KT; ++t)
+#pragma unroll
+        for (int r = 0; r < S::RT; ++r) {
+          const float4_t c0 = {0.0f, 0.0f, 0.0f, 0.0f};
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][t], B[t], t == 0 ? c0 : acc[r], 0, 0, 0);
+        }
+    };
+    // weighted ReLU and head sums per query, block maxima, one store per lane
+    auto epilogue = [&](const float4_t (&acc)[S::RT], int c, auto mask_tag) {
+      float v[S::NG];
 #pragma unroll
       for (int p = 0; p < S::NG; ++p) {
         float part[S::TPG];
 #pragma unroll
-        for (int u = 0; u < S::TPG; ++u) {
-          const int r = p * S::TPG + u;
-          float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int t = 0; t < S::KT; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][t], B[t], acc, 0, 0, 0);
-          part[u] = weighted_relu4(W[r], acc);
-        }
-        float v;
-        if constexpr (S::TPG == 2) v = tile_scores_x2(part[0], part[1]);
-        else v = tile_scores_x4(part[0], part[1], part[2], part[3]);
-        if (masked && c * 16 + n >= vis_l[p]) v = -INFINITY;
-        v = max8_scores(v);
-        if ((n & 7) == 0 && vis_l[p] >= 0) bmax[brow[p] + 2 * c + (n >> 3)] = v;
+        for (int u = 0; u < S::TPG; ++u) part[u] = weighted_relu4(W[p * S::TPG + u], acc[p * S::TPG + u]);
+        if constexpr (S::TPG == 2) v[p] = tile_scores_x2(part[0], part[1]);
+        else v[p] = tile_scores_x4(part[0], part[1], part[2], part[3]);
+        if constexpr (decltype(mask_tag)::value)
+          if (c * 16 + n >= vis_l[p]) v[p] = -INFINITY;
       }
+      const float x = block_max_groups<S::NG>(v, i8);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rb, soff + 8u * (uint32_t)c, 0, 0);
     };
-    // ring of kMqDepth + 1 column tiles: the loads of the next kMqDepth are in flight
-    constexpr int NBUF = kMqDepth + 1;
-    int c = wv;
-    if (c < ntile) {
-      LaneCodes<DI> buf[NBUF];
+
+    // Tiles every query of the pass sees whole, software-pipelined: step i
+    // issues the loads of tile i + 3, the MFMAs of tile i, the epilogue of
+    // tile i - 1 and the decode of tile i + 1, so the matrix cores and the
+    // vector ALUs work on independent data.
+    const int T = (full > wv) ? (full - wv + kMqWaves - 1) / kMqWaves : 0;  // this wave's whole tiles
+    if (T > 0) {
+      LaneCodes<DI> buf[4];
+      half8_t B[2][S::KT];
+      float4_t acc[2][S::RT];
+      auto tile_of = [&](int i) { return wv + kMqWaves * i; };
+      load(tile_of(0), buf[0]);
+      load(tile_of(1), buf[1]);
+      load(tile_of(2), buf[2]);
+      decode_keys<DI>(buf[0], B[0]);
+      load(tile_of(3), buf[3]);
+      mfmas(B[0], acc[0]);
+      decode_keys<DI>(buf[1], B[1]);
+      auto step = [&](auto kc, int i) {
+        constexpr int K = decltype(kc)::value;  // i % 4
+        load(tile_of(i + 3), buf[(K + 3) % 4]);
+        mfmas(B[K % 2], acc[K % 2]);
+        epilogue(acc[(K + 1) % 2], tile_of(i - 1), std::false_type{});
+        decode_keys<DI>(buf[(K + 1) % 4], B[(K + 1) % 2]);
+        // interleave: each MFMA followed by a few independent vector instructions
 #pragma unroll
-      for (int i = 0; i < kMqDepth; ++i) load(c + i * kMqWaves, buf[i]);
-      for (bool more = true; more;) {
-#pragma unroll
-        for (int k = 0; k < NBUF; ++k) {
-          if (more) {
-            load(c + kMqDepth * kMqWaves, buf[(k + kMqDepth) % NBUF]);
-            __builtin_amdgcn_sched_barrier(0);
-            tile(c, buf[k]);
-            c += kMqWaves;
-            more = c < ntile;
-          }
+        for (int k = 0; k < S::RT * S::KT; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, kMqValuPerMfma, 0);
+        }
+      };
+      if (T == 1) {
+        epilogue(acc[0], tile_of(0), std::false_type{});
+      } else {
+        for (int i = 1;;) {
+          step(std::integral_constant<int, 1>{}, i);
+          if (++i == T) { epilogue(acc[1], tile_of(i - 1), std::false_type{}); break; }
+          step(std::integral_constant<int, 2>{}, i);
+          if (++i == T) { epilogue(acc[0], tile_of(i - 1), std::false_type{}); break; }
+          step(std::integral_constant<int, 3>{}, i);
+          if (++i == T) { epilogue(acc[1], tile_of(i - 1), std::false_type{}); break; }
+          step(std::integral_constant<int, 0>{}, i);
+          if (++i == T) { epilogue(acc[0], tile_of(i - 1), std::false_type{}); break; }
         }
       }
+    }
+    // the last tiles, which some query sees only in part: masked, one at a time
+    for (int c = wv + kMqWaves * T; c < ntile; c += kMqWaves) {
+      LaneCodes<DI> cur;
+      half8_t B[S::KT];
+      float4_t acc[S::RT];
+      load(c, cur);
+      decode_keys<DI>(cur, B);
+      mfmas(B, acc);
+      epilogue(acc, c, std::true_type{});
     }
   }
 }
