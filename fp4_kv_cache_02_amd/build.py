@@ -11,12 +11,14 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
-SOURCES = ["csa2_api.hip", "csa2_codec.hip", "csa2_index.hip", "csa2_attn.hip", "csa2_prefill.hip"]
+SOURCES = ["csa2_api.hip", "csa2_codec.hip", "csa2_index.hip", "csa2_attn.hip", "csa2_prefill.hip",
+           "csa2_attn_prefill.hip"]
 # per-source code generation options
 EXTRA = {
     # MFMA results in vector registers: the epilogue reads them with vector
     # instructions, which cannot take accumulation registers as operands
     "csa2_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "csa2_attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 ARCH = os.environ.get("CSA2_OFFLOAD_ARCH", "gfx950")
 

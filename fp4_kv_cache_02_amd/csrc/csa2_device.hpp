@@ -61,6 +61,39 @@ CSA2_DEV half8_t fp4x8_dequant_f16(uint32_t w, _Float16 s) {
 CSA2_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 // ---------------------------------------------------------------------------
+// LDS operand loads
+// ---------------------------------------------------------------------------
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+// ds_read_b64_tr_b16: in each 16-lane group, lane i receives element (i%4)
+// of the 8-byte chunks addressed by lanes i/4, i/4+4, i/4+8, i/4+12.
+CSA2_DEV short4_t lds_read_tr16(const _Float16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4_t *)((__attribute__((address_space(3))) char *)(p)));
+}
+
+// MFMA operand (16x16x32, A or B) of a product over 32 keys: the lane of
+// row/column lane % 16 and k-quarter quad holds keys k0 + 8*quad .. +7 at
+// dim d0 + (lane % 16) of a row-major [key][dim] f16 tile with row stride
+// `stride` (the tile read down its columns, without a transposed copy).
+CSA2_DEV half8_t v_operand_tr(const _Float16 *tile, int stride, int k0, int d0, int row, int quad) {
+  const _Float16 *base = tile + (k0 + 8 * quad + (row >> 2)) * stride + d0 + 4 * (row & 3);
+  const short4_t lo = lds_read_tr16(base);
+  const short4_t hi = lds_read_tr16(base + 4 * stride);
+  return __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Eight E4M3 codes (two little-endian words) as f16.
+CSA2_DEV half8_t e4m3x8_to_f16(uint32_t a, uint32_t b) {
+  const half2_t a0 = e4m3x2_to_f16(a), a1 = e4m3x2_to_f16(a >> 16);
+  const half2_t a2 = e4m3x2_to_f16(b), a3 = e4m3x2_to_f16(b >> 16);
+  return (half8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
+// ---------------------------------------------------------------------------
 // exact encoders (write path)
 // ---------------------------------------------------------------------------
 

@@ -57,6 +57,13 @@ int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q,
                 const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,
                 hipStream_t stream);
 
+// Prefill schedule for the 512-channel latent with bf16 queries
+// (csa2_attn_prefill.hip); needs top_k % 16 == 0 and no workspace.
+bool attn_prefill_supported(const csa2_fp4_cache &kv, int q_dtype, int top_k);
+int launch_attn_prefill(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int heads,
+                        const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out, float *lse,
+                        hipStream_t stream);
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---- scan timing (csa2_api.hip) ----
