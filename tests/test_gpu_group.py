@@ -108,3 +108,80 @@ def test_group_step_matches_oracle(shape):
             assert np.array_equal(gtopk, ref["idx"])
             _check_attn(ref["out"], out_list, lse_list)
         layer0 += nl
+
+
+def test_encoder_group_step_matches_oracle():
+    """One encoder group (Full + 5 Reuse, flat Top-512, ratio 2) over a
+    256-token prefill chunk: tokens 3840 .. 4095 of a 4,096-token prompt, so
+    the chunk writes the last 128 of the 2,048 compressed entries and every
+    query sees 1,920 .. 2,048 of them.  The write path is checked byte for
+    byte, every query's list against the oracle's flat Top-K (modulo the
+    near-tie band), and the six layers' outputs of eight sampled queries whose
+    lists match the oracle's exactly."""
+    cfg, E, D, H, DI, HI, K, W, ratio, n_layers = 330, 2048, 512, 64, 128, 8, 512, 128, 2, 6
+    T, M = ratio * E, 256
+    R = M // ratio
+    announce("encoder group step", E, M)
+    x = synth.main_kv_rows(cfg, 0, 0, E, D)
+    w_ik = synth.w_ik(cfg, D, DI)
+    kv_c, kv_s = empty_u8(E, D // 2), empty_u8(E, D // 16)
+    ik_c, ik_s = empty_u8(E, DI // 2), empty_u8(E, DI // 16)
+    for z in (kv_c, kv_s, ik_c, ik_s):
+        z.zero_()
+    csa2.csa2_quantize_fp4(t(x[:E - R]), kv_c, kv_s, w_ik=t(w_ik), ik_codes=ik_c, ik_scales=ik_s)
+    rc, rs = codec.fp4_encode(x)
+    ikc, iks = codec.indexer_key(rc, rs, w_ik)
+    seq_start, seq_len = t(np.zeros(1, np.int64)), t(np.array([E], np.int32))
+    kv = csa2.fp4_cache(kv_c, kv_s, seq_start, seq_len, D, E, ratio)
+    idx = csa2.fp4_cache(ik_c, ik_s, seq_start, seq_len, DI, E, ratio)
+    q_pos = np.arange(T - M, T, dtype=np.int32)
+    qs = csa2.queries(t(np.zeros(M, np.int32)), t(q_pos))
+    qi, wi = synth.q_idx(cfg, 0, M, HI, DI), synth.w_idx(cfg, 0, M, HI)
+    q_list, swa_list, out_list, lse_list, swx_list, qh_list = [], [], [], [], [], []
+    nsw = M + W - 1
+    for layer in range(n_layers):
+        qh_list.append(synth.q_main(cfg, layer, M, H, D, "bf16"))
+        q_list.append(t(qh_list[-1]).view(torch.bfloat16))
+        swx = synth.swa_rows(cfg, layer, 0, nsw, D)
+        sc, ss = empty_u8(nsw, D), torch.empty((nsw,), dtype=torch.float32, device=dev())
+        csa2.csa2_quantize_fp8_rows(t(swx), sc, ss)
+        swa_list.append(csa2.swa(sc, ss, t(np.arange(M, dtype=np.int32)), t(np.full(M, W, np.int32)), D, W))
+        swx_list.append((swx, sc, ss))
+        out_list.append(torch.empty((M, H, D), dtype=torch.float32, device=dev()))
+        lse_list.append(torch.empty((M, H), dtype=torch.float32, device=dev()))
+    topk = torch.full((M, K), -7, dtype=torch.int32, device=dev())
+    g = csa2.Group(csa2.CSA2_MODE_FULL, kv, idx, qs, t(qi).view(torch.bfloat16), t(wi), 0, K, None, None, topk, None,
+                   q_list, csa2.CSA2_BF16, H, swa_list, out_list, lse_list, D ** -0.5,
+                   new_kv=t(x[E - R:]), new_dst_row=t(np.arange(E - R, E, dtype=np.int64)), w_ik=t(w_ik))
+    ws = torch.zeros((csa2.csa2_group_workspace_size(g),), dtype=torch.uint8, device=dev())
+    csa2.csa2_group_step(g, ws)
+    assert np.array_equal(h(kv_c), rc) and np.array_equal(h(kv_s), rs)
+    assert np.array_equal(h(ik_c), ikc) and np.array_equal(h(ik_s), iks)
+    gtopk = h(topk)
+    qf = synth.bf16_bits_to_f32(qi)
+    keys = codec.fp4_decode(ikc, iks)
+    exact = []
+    for i in range(M):
+        vis = indexer.visible_count(E, int(q_pos[i]), ratio)
+        otopk, s = indexer.index_flat(qf[i], wi[i], keys[:vis], K)
+        sel = gtopk[i][gtopk[i] >= 0]
+        assert len(sel) == K and np.all(np.diff(sel) > 0)
+        if assert_sets_equal_modulo_band(sel, otopk, lambda j: s[j], K, what="encoder topk") == 0:
+            exact.append(i)
+    rng = np.random.default_rng(331)
+    sample = sorted(rng.choice(exact, min(8, len(exact)), replace=False).tolist())
+    assert len(sample) == 8
+    outs = [(h(o), h(l)) for o, l in zip(out_list, lse_list)]
+    for i in sample:
+        vis = indexer.visible_count(E, int(q_pos[i]), ratio)
+        layers = []
+        for layer, (swx, sc, ss) in enumerate(swx_list):
+            c8, s8 = codec.fp8_rows_encode(swx[i:i + W])
+            assert np.array_equal(h(sc)[i:i + W], c8) and np.array_equal(h(ss)[i:i + W], s8)
+            qm = synth.bf16_bits_to_f32(qh_list[layer][i]).astype(np.float64)
+            layers.append((qm, c8, s8))
+        ref = ogroup.encoder_group_query(rc, rs, ikc, iks, int(q_pos[i]), ratio, qf[i], wi[i], K, layers,
+                                         D ** -0.5)
+        assert np.array_equal(gtopk[i], ref["idx"])
+        _check_attn(ref["out"], [torch.from_numpy(o[i:i + 1]) for o, _ in outs],
+                    [torch.from_numpy(l[i:i + 1]) for _, l in outs])
