@@ -22,7 +22,7 @@ EXPORTS = [
     "csa2_abi_version", "csa2_status_string", "csa2_quantize_fp4", "csa2_quantize_fp8_rows",
     "csa2_dequant_fp4", "csa2_index_workspace_size", "csa2_index_full", "csa2_reindex",
     "csa2_attn_workspace_size", "csa2_sparse_swa_attn", "csa2_group_workspace_size", "csa2_group_step",
-    "csa2_profile_scan", "csa2_profile_scan_read",
+    "csa2_profile_scan", "csa2_profile_scan_read", "csa2_profile_attn", "csa2_profile_attn_read",
 ]
 
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
             "csa2_group_step": (i32, [POINTER(GroupDesc), vp, sz, vp]),
             "csa2_profile_scan": (i32, [i32]),
             "csa2_profile_scan_read": (i32, [POINTER(ctypes.c_double), POINTER(c_int64)]),
+            "csa2_profile_attn": (i32, [i32]),
+            "csa2_profile_attn_read": (i32, [POINTER(ctypes.c_double), POINTER(c_int64)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -289,4 +291,15 @@ def csa2_profile_scan_read() -> tuple[float, int]:
     """(summed first-scan kernel milliseconds, launches) since profiling was enabled."""
     ms, n = ctypes.c_double(0.0), c_int64(0)
     _check(lib().csa2_profile_scan_read(ctypes.byref(ms), ctypes.byref(n)), "csa2_profile_scan_read")
+    return float(ms.value), int(n.value)
+
+
+def csa2_profile_attn(enable: bool) -> None:
+    _check(lib().csa2_profile_attn(1 if enable else 0), "csa2_profile_attn")
+
+
+def csa2_profile_attn_read() -> tuple[float, int]:
+    """(summed attention kernel milliseconds, launches) since attention timing was enabled."""
+    ms, n = ctypes.c_double(0.0), c_int64(0)
+    _check(lib().csa2_profile_attn_read(ctypes.byref(ms), ctypes.byref(n)), "csa2_profile_attn_read")
     return float(ms.value), int(n.value)

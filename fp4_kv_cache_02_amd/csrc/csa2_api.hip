@@ -7,29 +7,50 @@
 using namespace csa2;
 
 // ---------------------------------------------------------------------------
-// scan timing records
+// kernel timing records: first scans and attention launches
 // ---------------------------------------------------------------------------
 namespace csa2 {
 namespace {
-bool g_prof = false;
-std::vector<hipEvent_t> g_events;   // begin/end pairs in launch order
-}  // namespace
+struct Timing {
+  bool on = false;
+  std::vector<hipEvent_t> events;   // begin/end pairs in launch order
+};
+Timing g_timing[2];                 // 0: first scan, 1: attention
 
-bool scan_profiling() { return g_prof; }
-
-static void record(hipStream_t stream) {
+void record(Timing &t, hipStream_t stream) {
+  if (!t.on) return;
   hipEvent_t e;
   if (hipEventCreate(&e) != hipSuccess) return;
   if (hipEventRecord(e, stream) != hipSuccess) { (void)hipEventDestroy(e); return; }
-  g_events.push_back(e);
+  t.events.push_back(e);
 }
-void scan_profile_begin(hipStream_t stream) { record(stream); }
-void scan_profile_end(hipStream_t stream) { record(stream); }
+void clear_events(Timing &t) {
+  for (hipEvent_t e : t.events) (void)hipEventDestroy(e);
+  t.events.clear();
+}
+int read_events(Timing &t, double *total_ms, int64_t *launches) {
+  if (!total_ms || !launches) return CSA2_ERR_NULL_ARG;
+  double tot = 0.0;
+  int64_t n = 0;
+  for (size_t i = 0; i + 1 < t.events.size(); i += 2) {
+    if (hipEventSynchronize(t.events[i + 1]) != hipSuccess) return CSA2_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, t.events[i], t.events[i + 1]) != hipSuccess) return CSA2_ERR_HIP;
+    tot += ms;
+    ++n;
+  }
+  clear_events(t);
+  *total_ms = tot;
+  *launches = n;
+  return CSA2_OK;
+}
+}  // namespace
 
-static void clear_events() {
-  for (hipEvent_t e : g_events) (void)hipEventDestroy(e);
-  g_events.clear();
-}
+bool scan_profiling() { return g_timing[0].on; }
+void scan_profile_begin(hipStream_t stream) { record(g_timing[0], stream); }
+void scan_profile_end(hipStream_t stream) { record(g_timing[0], stream); }
+void attn_profile_begin(hipStream_t stream) { record(g_timing[1], stream); }
+void attn_profile_end(hipStream_t stream) { record(g_timing[1], stream); }
 }  // namespace csa2
 
 namespace {
@@ -294,26 +315,23 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
 }
 
 int32_t csa2_profile_scan(int32_t enable) {
-  clear_events();
-  g_prof = enable != 0;
+  clear_events(g_timing[0]);
+  g_timing[0].on = enable != 0;
   return CSA2_OK;
 }
 
 int32_t csa2_profile_scan_read(double *total_ms, int64_t *launches) {
-  if (!total_ms || !launches) return CSA2_ERR_NULL_ARG;
-  double tot = 0.0;
-  int64_t n = 0;
-  for (size_t i = 0; i + 1 < g_events.size(); i += 2) {
-    if (hipEventSynchronize(g_events[i + 1]) != hipSuccess) return CSA2_ERR_HIP;
-    float ms = 0.0f;
-    if (hipEventElapsedTime(&ms, g_events[i], g_events[i + 1]) != hipSuccess) return CSA2_ERR_HIP;
-    tot += ms;
-    ++n;
-  }
-  clear_events();
-  *total_ms = tot;
-  *launches = n;
+  return read_events(g_timing[0], total_ms, launches);
+}
+
+int32_t csa2_profile_attn(int32_t enable) {
+  clear_events(g_timing[1]);
+  g_timing[1].on = enable != 0;
   return CSA2_OK;
+}
+
+int32_t csa2_profile_attn_read(double *total_ms, int64_t *launches) {
+  return read_events(g_timing[1], total_ms, launches);
 }
 
 }  // extern "C"

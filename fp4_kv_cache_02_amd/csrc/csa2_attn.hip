@@ -884,9 +884,9 @@ static int attn_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, const voi
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 
-int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int q_dtype, int heads,
-                const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,
-                hipStream_t stream) {
+static int launch_attn_kernel(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int q_dtype,
+                              int heads, const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out,
+                              float *lse, void *ws, hipStream_t stream) {
   const bool f32 = q_dtype == CSA2_F32;
 #define CSA2_ATTN(D, F) attn_impl<D, F>(kv, qs, q, heads, topk, top_k, swa, scale, out, lse, ws, stream)
   switch (kv.dim) {
@@ -897,6 +897,15 @@ int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q,
     default: return CSA2_ERR_UNSUPPORTED;
   }
 #undef CSA2_ATTN
+}
+
+int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int q_dtype, int heads,
+                const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,
+                hipStream_t stream) {
+  attn_profile_begin(stream);
+  const int st = launch_attn_kernel(kv, qs, q, q_dtype, heads, topk, top_k, swa, scale, out, lse, ws, stream);
+  attn_profile_end(stream);
+  return st;
 }
 
 }  // namespace csa2

@@ -66,9 +66,11 @@ int launch_attn_prefill(const csa2_fp4_cache &kv, const csa2_queries &qs, const 
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// ---- scan timing (csa2_api.hip) ----
+// ---- kernel timing (csa2_api.hip) ----
 bool scan_profiling();
 void scan_profile_begin(hipStream_t stream);
 void scan_profile_end(hipStream_t stream);
+void attn_profile_begin(hipStream_t stream);  // no-ops unless attention timing is on
+void attn_profile_end(hipStream_t stream);
 
 }  // namespace csa2

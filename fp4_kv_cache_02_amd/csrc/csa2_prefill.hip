@@ -312,6 +312,8 @@ int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const u
   int32_t *pool_count = reinterpret_cast<int32_t *>(base + L.pool_count);
   float *pscore = reinterpret_cast<float *>(base + L.pscore);
   if (idx.max_len > 0) {
+    const bool prof = scan_profiling();
+    if (prof) scan_profile_begin(stream);
     const bool wide = heads > 8;
     switch (idx.dim) {
       case 64:
@@ -327,6 +329,7 @@ int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const u
         else launch_score_mq<256, 8>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
         break;
     }
+    if (prof) scan_profile_end(stream);
     if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
   }
   int st = launch_block_select(bmax, L.nb_stride, nb_max > 0 ? nb_max : 1, idx, qs, top_k, pool, pool_count,

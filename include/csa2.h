@@ -293,7 +293,9 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
 
 /* ---------------------------------------------------------------------
  * csa2_profile_scan / csa2_profile_scan_read - timing of the Full layer's
- * first scan (the step whose cost grows with the context, P4 section 二).
+ * first scan (the step whose cost grows with the context, P4 section 二):
+ * the decoder's scan over every visible entry, or the multi-query scoring
+ * kernel of the flat (prefill) indexer.
  * While enabled, every first-scan kernel launched by csa2_index_full /
  * csa2_group_step is bracketed by two HIP events recorded on its launch
  * stream.  enable != 0 clears earlier records and starts recording; 0 stops.
@@ -305,6 +307,12 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
  * ------------------------------------------------------------------- */
 int32_t csa2_profile_scan(int32_t enable);
 int32_t csa2_profile_scan_read(double *total_ms, int64_t *launches);
+
+/* csa2_profile_attn / csa2_profile_attn_read - the same timing for every
+ * attention kernel launched by csa2_sparse_swa_attn / csa2_group_step (one
+ * launch per layer).  Same contract and errors as csa2_profile_scan. */
+int32_t csa2_profile_attn(int32_t enable);
+int32_t csa2_profile_attn_read(double *total_ms, int64_t *launches);
 
 #ifdef __cplusplus
 }
