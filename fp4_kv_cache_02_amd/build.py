@@ -59,6 +59,13 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
+    # every symbol must resolve: a kernel whose host stub the compiler left
+    # out links fine and only fails when the library is loaded
+    r = subprocess.run(["nm", "-u", "-C", tmp], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    missing = [ln.strip() for ln in r.stdout.splitlines() if "csa2::" in ln]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("libcsa2 has unresolved symbols:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

@@ -31,6 +31,45 @@ namespace csa2 {
 
 constexpr int kMqWaves = 4;  // waves per scoring workgroup: one per SIMD, so each has the full register file
 constexpr int kMqValuPerMfma = 4;  // vector instructions scheduled between consecutive MFMAs
+constexpr int kMqRing = 8;   // LDS slots per wave for column tiles loaded ahead
+
+// One column tile as it lands in LDS, in lane order: lane (entry n, quarter
+// g) = 16g + n owns its DI/8 code bytes and the word holding its scale bytes,
+// so every lane reads its own words back without bank conflicts.
+template <int DI>
+struct MqTile {
+  static constexpr int NW = DI / 32;                 // code words per lane
+  static constexpr int V = (NW % 4 == 0) ? 4 : 1;    // words per load into LDS
+  static constexpr int NL = NW / V + 1;              // loads into LDS per tile
+  uint32_t w[NW / V][kWave][V];
+  uint32_t s[kWave];
+};
+
+// Buffer descriptor words (as scalar operands of the loads below): base,
+// no stride, `bytes` valid bytes (offsets past them read zeros).
+CSA2_DEV u32x4_t rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return (u32x4_t){(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+// Loads into LDS: lane i of the wave puts its 16 (4) bytes at LDS byte
+// address lds + 16i (4i).  Written out so that the compiler, which cannot
+// tell the ring's slots apart, does not drain every load into LDS before
+// each LDS read; the ring's own waits (wait_vm) order them instead.  They
+// return nothing to registers.
+CSA2_DEV void lds_load16(const u32x4_t &rs, uint32_t lds, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds) : "memory");
+}
+CSA2_DEV void lds_load4(const u32x4_t &rs, uint32_t lds, uint32_t voff) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds) : "memory");
+}
+CSA2_DEV uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p; }
+
+// s_waitcnt with only the vector memory count bounded (n < 64)
+template <int N>
+CSA2_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 template <int DI, int RPQ>
 struct MqShape {
@@ -91,6 +130,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__res
   using S = MqShape<DI, RPQ>;
   constexpr int kNone = 0x7FFFFFFF;
   __shared__ int s_seq[S::QB], s_vis[S::QB];
+  __shared__ MqTile<DI> ring[kMqWaves][kMqRing];
   const int m0 = blockIdx.x * S::QB;
   if (threadIdx.x < S::QB) {
     const int m = m0 + threadIdx.x;
@@ -204,49 +244,94 @@ __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__res
     };
 
     // Tiles every query of the pass sees whole, software-pipelined: step i
-    // issues the loads of tile i + 3, the MFMAs of tile i, the epilogue of
-    // tile i - 1 and the decode of tile i + 1, so the matrix cores and the
-    // vector ALUs work on independent data.
+    // loads tile i + kMqRing - 1 straight into this wave's LDS ring (entries
+    // past the pass's visible range lie past the descriptors and arrive as
+    // zeros), issues the MFMAs of tile i, the epilogue of tile i - 1 and the
+    // decode of tile i + 1, read from the ring, so the matrix cores and the
+    // vector ALUs work on independent data and no registers hold tiles in
+    // flight.
     const int T = (full > wv) ? (full - wv + kMqWaves - 1) / kMqWaves : 0;  // this wave's whole tiles
     if (T > 0) {
-      LaneCodes<DI> buf[4];
+      using Tl = MqTile<DI>;
+      const u32x4_t rc = rsrc_words(cbase, (uint32_t)maxvis * (DI / 2));
+      const u32x4_t rs = rsrc_words(sbase, (uint32_t)maxvis * (DI / 16));
+      const uint32_t sshift = 8u * ((uint32_t)(g * (DI / 64)) & 3u);
+      auto tile_of = [&](int i) { return wv + kMqWaves * i; };
+      auto issue = [&](int i) {
+        Tl &t = ring[wv][i % kMqRing];
+        const uint32_t e = (uint32_t)(tile_of(i) * 16 + n);
+#pragma unroll
+        for (int r = 0; r < Tl::NW / Tl::V; ++r) {
+          const uint32_t off = e * (DI / 2) + (uint32_t)g * (DI / 8) + 4u * Tl::V * r;
+          if constexpr (Tl::V == 4) lds_load16(rc, lds_addr(&t.w[r][0][0]), off);
+          else lds_load4(rc, lds_addr(&t.w[r][0][0]), off);
+        }
+        lds_load4(rs, lds_addr(&t.s[0]), e * (DI / 16) + (((uint32_t)g * (DI / 64)) & ~3u));
+      };
+      auto read = [&](int i, LaneCodes<DI> &c) {
+        const Tl &t = ring[wv][i % kMqRing];
+#pragma unroll
+        for (int r = 0; r < Tl::NW / Tl::V; ++r) {
+          if constexpr (Tl::V == 4) {
+            const u32x4_t x = *reinterpret_cast<const u32x4_t *>(&t.w[r][l][0]);
+            c.w[4 * r] = x[0]; c.w[4 * r + 1] = x[1]; c.w[4 * r + 2] = x[2]; c.w[4 * r + 3] = x[3];
+          } else {
+            c.w[r] = t.w[r][l][0];
+          }
+        }
+        c.s = t.s[l] >> sshift;
+      };
       half8_t B[2][S::KT];
       float4_t acc[2][S::RT];
-      auto tile_of = [&](int i) { return wv + kMqWaves * i; };
-      load(tile_of(0), buf[0]);
-      load(tile_of(1), buf[1]);
-      load(tile_of(2), buf[2]);
-      decode_keys<DI>(buf[0], B[0]);
-      load(tile_of(3), buf[3]);
-      mfmas(B[0], acc[0]);
-      decode_keys<DI>(buf[1], B[1]);
-      auto step = [&](auto kc, int i) {
-        constexpr int K = decltype(kc)::value;  // i % 4
-        load(tile_of(i + 3), buf[(K + 3) % 4]);
-        mfmas(B[K % 2], acc[K % 2]);
-        epilogue(acc[(K + 1) % 2], tile_of(i - 1), std::false_type{});
-        decode_keys<DI>(buf[(K + 1) % 4], B[(K + 1) % 2]);
+      LaneCodes<DI> cn[2];  // codes of tiles i + 1 and i + 2, read from the ring two steps ahead
+#pragma unroll
+      for (int i = 0; i < kMqRing - 1; ++i) issue(i);
+      wait_vm<0>();
+      {
+        LaneCodes<DI> c0;
+        read(0, c0);
+        decode_keys<DI>(c0, B[0]);
+      }
+      read(1, cn[1]);
+      read(2, cn[0]);
+      // the ring slot of tile i + 3 has landed once at most (kMqRing - 5)
+      // tiles' loads and as many epilogue stores are younger than its loads
+      constexpr int kVm = (kMqRing - 5) * (MqTile<DI>::NL + 1);
+      // step i: the MFMAs of tile i, the epilogue of tile i - 1 and the
+      // decode of tile i + 1 as one interleaved stretch; then tile i + 3 from
+      // the ring and the load of tile i + kMqRing - 1 into the slot tile i - 1
+      // left
+      auto step = [&](auto kc, auto epi, int i) {
+        constexpr int K = decltype(kc)::value;  // i % 2
+        mfmas(B[K], acc[K]);
+        if constexpr (decltype(epi)::value) epilogue(acc[K ^ 1], tile_of(i - 1), std::false_type{});
+        decode_keys<DI>(cn[K ^ 1], B[K ^ 1]);
         // interleave: each MFMA followed by a few independent vector instructions
 #pragma unroll
         for (int k = 0; k < S::RT * S::KT; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, kMqValuPerMfma, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, K);
+          __builtin_amdgcn_sched_group_barrier(0x002, kMqValuPerMfma, K);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<kVm>();
+        read(i + 3, cn[K ^ 1]);
+        issue(i + kMqRing - 1);
+        __builtin_amdgcn_sched_barrier(0);
       };
+      using K0 = std::integral_constant<int, 0>;
+      using K1 = std::integral_constant<int, 1>;
+      step(K0{}, std::false_type{}, 0);
       if (T == 1) {
         epilogue(acc[0], tile_of(0), std::false_type{});
       } else {
         for (int i = 1;;) {
-          step(std::integral_constant<int, 1>{}, i);
+          step(K1{}, std::true_type{}, i);
           if (++i == T) { epilogue(acc[1], tile_of(i - 1), std::false_type{}); break; }
-          step(std::integral_constant<int, 2>{}, i);
-          if (++i == T) { epilogue(acc[0], tile_of(i - 1), std::false_type{}); break; }
-          step(std::integral_constant<int, 3>{}, i);
-          if (++i == T) { epilogue(acc[1], tile_of(i - 1), std::false_type{}); break; }
-          step(std::integral_constant<int, 0>{}, i);
+          step(K0{}, std::true_type{}, i);
           if (++i == T) { epilogue(acc[0], tile_of(i - 1), std::false_type{}); break; }
         }
       }
+      wait_vm<0>();  // the ring is idle before the next pass or the end
     }
     // the last tiles, which some query sees only in part: masked, one at a time
     for (int c = wv + kMqWaves * T; c < ntile; c += kMqWaves) {
