@@ -321,15 +321,18 @@ __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__res
       using K0 = std::integral_constant<int, 0>;
       using K1 = std::integral_constant<int, 1>;
       step(K0{}, std::false_type{}, 0);
-      if (T == 1) {
-        epilogue(acc[0], tile_of(0), std::false_type{});
+      // pairs of steps with one exit test, so that both steps of a pair are
+      // one block (the compiler moves no work from one step into the next)
+      int i = 1;
+      for (; i + 1 < T; i += 2) {
+        step(K1{}, std::true_type{}, i);
+        step(K0{}, std::true_type{}, i + 1);
+      }
+      if (i < T) {
+        step(K1{}, std::true_type{}, i);
+        epilogue(acc[1], tile_of(i), std::false_type{});
       } else {
-        for (int i = 1;;) {
-          step(K1{}, std::true_type{}, i);
-          if (++i == T) { epilogue(acc[1], tile_of(i - 1), std::false_type{}); break; }
-          step(K0{}, std::true_type{}, i);
-          if (++i == T) { epilogue(acc[0], tile_of(i - 1), std::false_type{}); break; }
-        }
+        epilogue(acc[0], tile_of(i - 1), std::false_type{});
       }
       wait_vm<0>();  // the ring is idle before the next pass or the end
     }
