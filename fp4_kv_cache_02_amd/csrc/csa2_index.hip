@@ -252,10 +252,15 @@ __global__ __launch_bounds__(256) void k_pool_filter(const float *__restrict__ b
     s_bt = s_nt ? (int)atomicAdd(&counters[m * 4 + 1], (uint32_t)s_nt) : 0;
   }
   __syncthreads();
+  // the lists hold P sure blocks and nb_stride tie blocks per query; a
+  // histogram that disagreed with the block maxima could ask for more, and
+  // those appends are dropped rather than written past the lists
   int32_t *su = sure + (int64_t)m * P + s_bs;
   int32_t *ti = tie + (int64_t)m * nb_stride + s_bt;
-  for (int i = threadIdx.x; i < s_ns; i += blockDim.x) su[i] = s_sure[i];
-  for (int i = threadIdx.x; i < s_nt; i += blockDim.x) ti[i] = s_tie[i];
+  const int ns = max(0, min(s_ns, P - s_bs));
+  const int nt = (int)max<int64_t>(0, min<int64_t>(s_nt, nb_stride - s_bt));
+  for (int i = threadIdx.x; i < ns; i += blockDim.x) su[i] = s_sure[i];
+  for (int i = threadIdx.x; i < nt; i += blockDim.x) ti[i] = s_tie[i];
 }
 
 // Pool finalisation, one workgroup per query: resolve the boundary bin
@@ -282,8 +287,10 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
   int s;
   const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
   const int64_t nb = (vis + kBlock - 1) / kBlock;
-  const int n_sure = (int)counters[m * 4 + 0];
-  const int n_tie = (int)counters[m * 4 + 1];
+  // counts as far as the lists reach (they never exceed them when the
+  // histogram agrees with the block maxima)
+  const int n_sure = (int)min<uint32_t>(counters[m * 4 + 0], (uint32_t)P);
+  const int n_tie = (int)min<int64_t>((int64_t)counters[m * 4 + 1], nb_stride);
   const uint32_t s_T = counters[m * 4 + 2];  // threshold bin (meaningful when there are ties)
   const int need = (int)min<int64_t>(min<int64_t>(P, nb), (int64_t)n_sure + n_tie);
   const int need_t = need - n_sure;
@@ -298,12 +305,17 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
   __syncthreads();
   auto take = [&](int32_t b) {
     if (use_bits) atomicOr(&s_bits[b >> 5], 1u << (b & 31));
-    else s_pool[atomicAdd(&s_n, 1)] = b;
+    else {
+      const int slot = atomicAdd(&s_n, 1);
+      if (slot < kMaxPool) s_pool[slot] = b;
+    }
   };
-  for (int i = threadIdx.x; i < n_sure; i += blockDim.x) take(su[i]);
+  for (int i = threadIdx.x; i < n_sure; i += blockDim.x)
+    if ((uint64_t)su[i] < (uint64_t)nb) take(su[i]);
   if (need_t > 0) {
     if (need_t >= n_tie) {
-      for (int i = threadIdx.x; i < n_tie; i += blockDim.x) take(ti[i]);
+      for (int i = threadIdx.x; i < n_tie; i += blockDim.x)
+        if ((uint64_t)ti[i] < (uint64_t)nb) take(ti[i]);
     } else {
       // composite key: larger score first, then smaller block id.  Every tie
       // entry shares the threshold bin (the top kHistBits of the score key),
@@ -321,6 +333,7 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
         __syncthreads();
         for (int i = threadIdx.x; i < n_tie; i += blockDim.x) {
           const int32_t b = ti[i];
+          if ((uint64_t)b >= (uint64_t)nb) continue;
           const uint64_t c = ((uint64_t)f2key(bm[b]) << 32) | (uint64_t)(~(uint32_t)b);
           if ((c & mask) == prefix) atomicAdd(&s_h[(c >> shift) & dmask], 1u);
         }
@@ -334,6 +347,7 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
       }
       for (int i = threadIdx.x; i < n_tie; i += blockDim.x) {
         const int32_t b = ti[i];
+        if ((uint64_t)b >= (uint64_t)nb) continue;
         const uint64_t c = ((uint64_t)f2key(bm[b]) << 32) | (uint64_t)(~(uint32_t)b);
         if ((c & mask) >= prefix) take(b);
       }
@@ -358,13 +372,16 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
       while (bits) {
         const int bit = __ffs(bits) - 1;
         bits &= bits - 1;
-        out[pos++] = w * 32 + bit;
+        if (pos < P) out[pos] = w * 32 + bit;
+        ++pos;
       }
     }
+    for (int i = min(tot, need) + threadIdx.x; i < need; i += blockDim.x) out[i] = -1;
   } else {
     int n2 = 64;
     while (n2 < need) n2 <<= 1;
-    for (int i = need + threadIdx.x; i < n2; i += blockDim.x) s_pool[i] = 0x7FFFFFFF;
+    // slots past what was taken sort last (rescoring treats them as not visible)
+    for (int i = min(s_n, need) + threadIdx.x; i < n2; i += blockDim.x) s_pool[i] = 0x7FFFFFFF;
     __syncthreads();
     for (int k = 2; k <= n2; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
