@@ -393,7 +393,7 @@ def run_prefill(args, wl, torch, csa2, synth):
     ms_total = t_start.elapsed_time(t_end)
     if not same(ref, W.snapshot()):
         raise RuntimeError("timed steps differ from the warm-up step")
-    # kernel durations: HIP events around each scoring / attention launch, same steps again
+    # kernel durations: HIP events stamped by each scoring / attention dispatch, same steps again
     csa2.csa2_profile_scan(True)
     csa2.csa2_profile_attn(True)
     for _ in range(args.steps):
@@ -428,7 +428,7 @@ def run_prefill(args, wl, torch, csa2, synth):
         "roofline": {"bound": "mfma", "kernel": "prefill attention (k_attn_prefill)", "achieved": round(at_tf, 1),
                      "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(at_tf / F16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": None, "avg_launch_ms": round(at_avg, 4),
-                     "timing": "HIP events around each attention launch (same steps run again)",
+                     "timing": "HIP events stamped by each attention dispatch (same steps run again)",
                      "algorithmic_flops_per_launch": W.attn_flops_per_launch()},
         "indexer_scoring": {"bound": "mfma", "kernel": "k_score_mq", "achieved": round(sc_tf, 1),
                             "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -515,7 +515,7 @@ def main():
         raise RuntimeError("timed steps differ from the eager reference")
     if graph is not None:
         # events cannot be timed inside a graph replay: the first scan's launch
-        # duration comes from HIP events around it in the same steps run eagerly
+        # duration comes from HIP events stamped by its dispatch in the same steps run eagerly
         csa2.csa2_profile_scan(True)
         for _ in range(args.steps):
             W.step()
@@ -566,7 +566,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "first scan (k_scan)", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "avg_launch_ms": round(scan_avg_ms, 5),
-                     "timing": "HIP events around each first-scan launch" + (
+                     "timing": "HIP events stamped by each first-scan dispatch" + (
                          " (same steps run eagerly after the timed graph replay)" if graph is not None else ""),
                      "algorithmic_bytes_per_launch": scan_bytes},
         "step_algorithmic_bytes": step_bytes,

@@ -17,13 +17,6 @@ struct Timing {
 };
 Timing g_timing[2];                 // 0: first scan, 1: attention
 
-void record(Timing &t, hipStream_t stream) {
-  if (!t.on) return;
-  hipEvent_t e;
-  if (hipEventCreate(&e) != hipSuccess) return;
-  if (hipEventRecord(e, stream) != hipSuccess) { (void)hipEventDestroy(e); return; }
-  t.events.push_back(e);
-}
 void clear_events(Timing &t) {
   for (hipEvent_t e : t.events) (void)hipEventDestroy(e);
   t.events.clear();
@@ -46,11 +39,18 @@ int read_events(Timing &t, double *total_ms, int64_t *launches) {
 }
 }  // namespace
 
-bool scan_profiling() { return g_timing[0].on; }
-void scan_profile_begin(hipStream_t stream) { record(g_timing[0], stream); }
-void scan_profile_end(hipStream_t stream) { record(g_timing[0], stream); }
-void attn_profile_begin(hipStream_t stream) { record(g_timing[1], stream); }
-void attn_profile_end(hipStream_t stream) { record(g_timing[1], stream); }
+void timing_events(int which, hipEvent_t *start, hipEvent_t *stop) {
+  *start = *stop = nullptr;
+  Timing &t = g_timing[which];
+  if (!t.on) return;
+  hipEvent_t a, b;
+  if (hipEventCreate(&a) != hipSuccess) return;
+  if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+  t.events.push_back(a);
+  t.events.push_back(b);
+  *start = a;
+  *stop = b;
+}
 }  // namespace csa2
 
 namespace {

@@ -870,16 +870,16 @@ static int attn_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, const voi
       pl = reinterpret_cast<float *>(base + L.part_lse);
     }
     const dim3 grid(((D + kDD - 1) / kDD) * ns, qs.m, (heads + kDH - 1) / kDH);
-    hipLaunchKernelGGL((k_attn_decode<D, QF32>), grid, dim3(64 * kDW), 0, stream, q, heads, kv.codes, kv.scales,
-                       kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, swa.codes, swa.scale, swa.start,
-                       swa.count, W, tau2, out, lse, ns, po, pl, ctr);
+    CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_decode<D, QF32>), grid, dim3(64 * kDW), stream, q, heads, kv.codes,
+                      kv.scales, kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, swa.codes, swa.scale,
+                      swa.start, swa.count, W, tau2, out, lse, ns, po, pl, ctr);
   } else if (attn_prefill_supported(kv, QF32 ? CSA2_F32 : CSA2_BF16, K)) {
     return launch_attn_prefill(kv, qs, q, heads, topk, K, swa, scale, out, lse, stream);
   } else {
     const dim3 grid(qs.m, (heads + kHB - 1) / kHB);
-    hipLaunchKernelGGL((k_attn<D, QF32>), grid, dim3(256), 0, stream, q, heads, kv.codes, kv.scales, kv.seq_start,
-                       kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, swa.codes, swa.scale, swa.start, swa.count, W,
-                       tau2, out, lse);
+    CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn<D, QF32>), grid, dim3(256), stream, q, heads, kv.codes, kv.scales,
+                      kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, swa.codes, swa.scale, swa.start,
+                      swa.count, W, tau2, out, lse);
   }
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
@@ -902,10 +902,7 @@ static int launch_attn_kernel(const csa2_fp4_cache &kv, const csa2_queries &qs, 
 int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int q_dtype, int heads,
                 const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,
                 hipStream_t stream) {
-  attn_profile_begin(stream);
-  const int st = launch_attn_kernel(kv, qs, q, q_dtype, heads, topk, top_k, swa, scale, out, lse, ws, stream);
-  attn_profile_end(stream);
-  return st;
+  return launch_attn_kernel(kv, qs, q, q_dtype, heads, topk, top_k, swa, scale, out, lse, ws, stream);
 }
 
 }  // namespace csa2

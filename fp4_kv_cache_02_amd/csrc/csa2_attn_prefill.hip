@@ -453,9 +453,9 @@ int launch_attn_prefill(const csa2_fp4_cache &kv, const csa2_queries &qs, const 
   const int hb = (heads + kPH - 1) / kPH;
   const int g = std::max(1, std::min(qs.m, 256 / hb));
   const dim3 grid(g, hb);
-  hipLaunchKernelGGL(k_attn_prefill, grid, dim3(256), 0, stream, static_cast<const uint16_t *>(q), qs.m, heads,
-                     kv.codes, kv.scales, kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, top_k, swa.codes,
-                     swa.scale, swa.start, swa.count, swa.window, tau2, out, lse);
+  CSA2_TIMED_LAUNCH(kTimedAttn, k_attn_prefill, grid, dim3(256), stream, static_cast<const uint16_t *>(q), qs.m,
+                    heads, kv.codes, kv.scales, kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, top_k,
+                    swa.codes, swa.scale, swa.start, swa.count, swa.window, tau2, out, lse);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 

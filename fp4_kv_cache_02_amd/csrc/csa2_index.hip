@@ -77,10 +77,9 @@ CSA2_DEV void find_digit(const uint32_t *s_hist, int rem, int *s_digit, int *s_r
 // in LDS, written out once, and counted into an LDS histogram whose non-zero
 // bins are added to the query's global histogram.
 constexpr int kScanU = 8;
-constexpr bool kScanDbuf = false;
 constexpr int kScanMinGrid = 240;  // workgroups that count as filling the 256 CUs
 
-template <int DI, int WAVES = kScanWaves, int TILES = kScanTiles, int U = kScanU, bool DBUF = kScanDbuf>
+template <int DI, int WAVES = kScanWaves, int TILES = kScanTiles, int U = kScanU>
 __global__ __launch_bounds__(64 * WAVES) void k_scan(const uint8_t *__restrict__ codes,
                                                      const uint8_t *__restrict__ scales,
                                                      const int64_t *__restrict__ seq_start,
@@ -137,27 +136,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_scan(const uint8_t *__restrict__
     }
   };
   // the scheduling barriers keep each batch's loads issued together, ahead of the scoring
-  if constexpr (!DBUF) {
-    for (int b = 0; live(b); ++b) {
-      LaneCodes<DI> c[U];
-      load_batch(b, c);
-      __builtin_amdgcn_sched_barrier(0);
-      score_batch(b, c);
-    }
-  } else {
-    // the next batch's loads are in flight while the current one is scored
-    LaneCodes<DI> A[U], B[U];
-    if (live(0)) load_batch(0, A);
-    for (int b = 0; live(b); b += 2) {
-      const bool l1 = live(b + 1);
-      if (l1) load_batch(b + 1, B);
-      __builtin_amdgcn_sched_barrier(0);
-      score_batch(b, A);
-      if (!l1) break;
-      if (live(b + 2)) load_batch(b + 2, A);
-      __builtin_amdgcn_sched_barrier(0);
-      score_batch(b + 1, B);
-    }
+  for (int b = 0; live(b); ++b) {
+    LaneCodes<DI> c[U];
+    load_batch(b, c);
+    __builtin_amdgcn_sched_barrier(0);
+    score_batch(b, c);
   }
   __syncthreads();
   const int nb_here = (n_here + kBlock - 1) / kBlock;
@@ -690,20 +673,17 @@ static int index_full_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
   const int64_t nz = (int64_t)((L.sure - L.hist) / sizeof(uint32_t));
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
   if (idx.max_len > 0) {
-    const bool prof = scan_profiling();
-    if (prof) scan_profile_begin(stream);
     // largest chunk whose grid still gives about one workgroup per CU
     auto chunks_of = [&](int chunk) { return (idx.max_len + chunk - 1) / chunk; };
     const int64_t m = qs.m;
 #define CSA2_SCAN(T)                                                                                        \
-  hipLaunchKernelGGL((k_scan<DI, kScanWaves, T>), dim3((unsigned)chunks_of(T * 16), qs.m), dim3(64 * kScanWaves), \
-                     0, stream, idx.codes, idx.scales, idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, q_idx, \
-                     w_idx, heads, bmax, L.nb_max, hist)
+  CSA2_TIMED_LAUNCH(kTimedScan, (k_scan<DI, kScanWaves, T>), dim3((unsigned)chunks_of(T * 16), qs.m),    \
+                    dim3(64 * kScanWaves), stream, idx.codes, idx.scales, idx.seq_start, idx.seq_len, idx.ratio, \
+                    qs.seq, qs.pos, q_idx, w_idx, heads, bmax, L.nb_max, hist)
     if (chunks_of(kScanChunk) * m >= kScanMinGrid) CSA2_SCAN(kScanTiles);
     else if (chunks_of(kScanChunk / 4) * m >= kScanMinGrid) CSA2_SCAN(kScanTiles / 4);
     else CSA2_SCAN(kScanTiles / 16);
 #undef CSA2_SCAN
-    if (prof) scan_profile_end(stream);
   }
   const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);
   hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, hist, idx.seq_len, qs.seq, qs.pos,

@@ -4,6 +4,8 @@
 #include "../../include/csa2.h"
 #include "csa2_device.hpp"
 
+#include <hip/hip_ext.h>
+
 namespace csa2 {
 
 // ---- write path (csa2_codec.hip) ----
@@ -67,10 +69,22 @@ int launch_attn_prefill(const csa2_fp4_cache &kv, const csa2_queries &qs, const 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---- kernel timing (csa2_api.hip) ----
-bool scan_profiling();
-void scan_profile_begin(hipStream_t stream);
-void scan_profile_end(hipStream_t stream);
-void attn_profile_begin(hipStream_t stream);  // no-ops unless attention timing is on
-void attn_profile_end(hipStream_t stream);
+// Timed kernels: the first scan of an index call (decode scan or prefill
+// scoring) and each attention launch.  timing_events hands out a fresh
+// start/stop pair when that timing is on (both null otherwise); launched with
+// hipExtLaunchKernelGGL, the pair takes the dispatch's own start and end
+// times, so no marker packets sit between the events and the kernel.
+enum TimedKernel { kTimedScan = 0, kTimedAttn = 1 };
+void timing_events(int which, hipEvent_t *start, hipEvent_t *stop);
+
+#define CSA2_TIMED_LAUNCH(which, kernel, grid, block, stream, ...)                                  \
+  do {                                                                                              \
+    hipEvent_t csa2_t0_, csa2_t1_;                                                                  \
+    ::csa2::timing_events(which, &csa2_t0_, &csa2_t1_);                                             \
+    if (csa2_t0_)                                                                                   \
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, csa2_t0_, csa2_t1_, 0, __VA_ARGS__);    \
+    else                                                                                            \
+      hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);                              \
+  } while (0)
 
 }  // namespace csa2

@@ -380,9 +380,9 @@ static void launch_score_mq(const csa2_fp4_cache &idx, const csa2_queries &qs, c
                             const float *w_idx, int heads, float *bmax, int64_t nb_stride, hipStream_t stream) {
   using S = MqShape<DI, RPQ>;
   const dim3 grid((unsigned)((qs.m + S::QB - 1) / S::QB));
-  hipLaunchKernelGGL((k_score_mq<DI, RPQ>), grid, dim3(64 * kMqWaves), 0, stream, idx.codes, idx.scales,
-                     idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, qs.m, q_idx, w_idx, heads, bmax,
-                     nb_stride);
+  CSA2_TIMED_LAUNCH(kTimedScan, (k_score_mq<DI, RPQ>), grid, dim3(64 * kMqWaves), stream, idx.codes, idx.scales,
+                    idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, qs.m, q_idx, w_idx, heads, bmax,
+                    nb_stride);
 }
 
 int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
@@ -400,8 +400,6 @@ int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const u
   int32_t *pool_count = reinterpret_cast<int32_t *>(base + L.pool_count);
   float *pscore = reinterpret_cast<float *>(base + L.pscore);
   if (idx.max_len > 0) {
-    const bool prof = scan_profiling();
-    if (prof) scan_profile_begin(stream);
     const bool wide = heads > 8;
     switch (idx.dim) {
       case 64:
@@ -417,7 +415,6 @@ int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const u
         else launch_score_mq<256, 8>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
         break;
     }
-    if (prof) scan_profile_end(stream);
     if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
   }
   int st = launch_block_select(bmax, L.nb_stride, nb_max > 0 ? nb_max : 1, idx, qs, top_k, pool, pool_count,

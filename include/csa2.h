@@ -297,8 +297,11 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
  * the decoder's scan over every visible entry, or the multi-query scoring
  * kernel of the flat (prefill) indexer.
  * While enabled, every first-scan kernel launched by csa2_index_full /
- * csa2_group_step is bracketed by two HIP events recorded on its launch
- * stream.  enable != 0 clears earlier records and starts recording; 0 stops.
+ * csa2_group_step gets two HIP events that its own dispatch stamps with its
+ * start and end times (an extended launch on its stream), so the elapsed time
+ * is the kernel's alone.  Launches made while disabled are plain launches
+ * (safe under stream capture).  enable != 0 clears earlier records and
+ * starts recording; 0 stops.
  * _read waits for the recorded events and returns the summed kernel time in
  * milliseconds and the number of launches, then clears the records.  For
  * measurement only; recording is host-side bookkeeping, not thread-safe

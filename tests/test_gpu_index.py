@@ -118,6 +118,30 @@ def test_index_repeatable():
         assert np.array_equal(x, y, equal_nan=True)
 
 
+def test_scan_timing_records_one_pair_per_launch_and_changes_nothing():
+    """While scan timing is on, each Full call's first scan is launched with
+    dispatch-stamped events: one positive duration per call, identical results;
+    with timing off nothing is recorded."""
+    announce("index_full scan timing")
+    lens, di, H, P, K = [20000], 128, 8, 256, 128
+    codes, scales, rc, rs, starts = _cache_from_raw(105, lens, di)
+    qi = synth.q_idx(105, 0, 1, H, di)
+    wi = synth.w_idx(105, 0, 1, H)
+    base = _run_full(codes, scales, starts, lens, di, [0], [19999], qi, wi, P, K)
+    csa2.csa2_profile_scan(True)
+    try:
+        runs = [_run_full(codes, scales, starts, lens, di, [0], [19999], qi, wi, P, K) for _ in range(3)]
+        ms, n = csa2.csa2_profile_scan_read()
+    finally:
+        csa2.csa2_profile_scan(False)
+    assert n == 3 and 0.0 < ms < 1000.0
+    for r in runs:
+        for x, y in zip(base[:4], r[:4]):
+            assert np.array_equal(x, y, equal_nan=True)
+    _run_full(codes, scales, starts, lens, di, [0], [19999], qi, wi, P, K)
+    assert csa2.csa2_profile_scan_read() == (0.0, 0)
+
+
 def test_reindex_matches_oracle():
     announce("reindex")
     lens, di, H, P, K = [30000, 5000], 128, 8, 512, 256
