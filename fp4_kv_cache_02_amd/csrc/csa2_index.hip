@@ -68,16 +68,22 @@ CSA2_DEV void find_digit(const uint32_t *s_hist, int rem, int *s_digit, int *s_r
 }
 
 // First scan: grid (chunks, queries), WAVES waves, TILES * 16 positions per
-// workgroup.  Wave w scores tiles w, w + WAVES, ... in batches of U tiles:
-// all loads of a batch are issued before any of it is scored, and the other
-// waves of the CU cover the latency.  Large chunks amortise the per-workgroup
+// workgroup, scored in batches of U consecutive tiles: all loads of a batch
+// are issued before any of it is scored, and the other waves of the CU cover
+// the latency.  Wave w starts with batch w and then claims the next unclaimed
+// batch from an LDS counter, so the waves of a workgroup finish together
+// even when the memory system serves them unevenly (a fixed round-robin left
+// them several microseconds apart).  Large chunks amortise the per-workgroup
 // set-up (query load, histogram clear and flush); the host picks the chunk so
-// that the grid still fills the chip.  Four tiles at a time
-// share the cross-lane reduction (tile_scores_x4).  Block maxima are staged
-// in LDS, written out once, and counted into an LDS histogram whose non-zero
-// bins are added to the query's global histogram.
+// that the grid still fills the chip.  Four tiles at a time share the
+// cross-lane reduction (tile_scores_x4).  Block maxima are staged in LDS,
+// written out once, and counted into an LDS histogram whose non-zero bins are
+// added to one of the query's hist_rep global histogram replicas (chunk %
+// hist_rep): every workgroup of a query hits the same few bins, and device
+// atomics on one address serialise.
 constexpr int kScanU = 8;
 constexpr int kScanMinGrid = 240;  // workgroups that count as filling the 256 CUs
+constexpr int kHistMaxReplicas = 8;
 
 template <int DI, int WAVES = kScanWaves, int TILES = kScanTiles, int U = kScanU>
 __global__ __launch_bounds__(64 * WAVES) void k_scan(const uint8_t *__restrict__ codes,
@@ -89,13 +95,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_scan(const uint8_t *__restrict__
                                                      const uint16_t *__restrict__ q_idx,
                                                      const float *__restrict__ w_idx, int H,
                                                      float *__restrict__ bmax, int64_t nb_stride,
-                                                     uint32_t *__restrict__ hist) {
+                                                     uint32_t *__restrict__ hist, int hist_rep) {
   constexpr int CHUNK = TILES * 16;
   constexpr int BLOCKS = CHUNK / kBlock;
-  constexpr int NB = TILES / WAVES / U;  // batches per wave
   static_assert(TILES % (WAVES * U) == 0 && U % 4 == 0, "scan tiling");
   __shared__ float s_bmax[BLOCKS];
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
+  __shared__ int s_next;  // next unclaimed batch
   const int m = blockIdx.y;
   int s;
   const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
@@ -103,6 +109,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_scan(const uint8_t *__restrict__
   if (p_begin >= vis) return;
   for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x)
     reinterpret_cast<uint4 *>(s_hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x == 0) s_next = WAVES;
 
   IdxQuery<DI> Q;
   load_idx_query<DI>(q_idx + (int64_t)m * H * DI, w_idx + (int64_t)m * H, H, Q);
@@ -113,34 +120,43 @@ __global__ __launch_bounds__(64 * WAVES) void k_scan(const uint8_t *__restrict__
   const uint8_t *cbase = codes + (seq_start[s] + p_begin) * (DI / 2);
   const uint8_t *sbase = scales + (seq_start[s] + p_begin) * (DI / 16);
   const int rt = row_tile(l >> 4);
-  // batch b of this wave: tiles t0 + u*WAVES, t0 = b*U*WAVES + wv
-  auto live = [&](int b) { return b < NB && (b * U * WAVES + wv) * 16 < n_here; };
+  // batch b: tiles b*U .. b*U + U-1 (positions past the chunk's end are
+  // clamped to its last entry and score -inf into slots nobody reads)
+  const int n_batches = (n_here + U * 16 - 1) / (U * 16);
   auto load_batch = [&](int b, LaneCodes<DI> *c) {
-    const int t0 = b * U * WAVES + wv;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int p = min((t0 + u * WAVES) * 16 + n, n_here - 1);
+      const int p = min((b * U + u) * 16 + n, n_here - 1);
       load_lane_codes_rel<DI>(cbase, sbase, (uint32_t)p, (uint32_t)qq, c[u]);
     }
   };
   auto score_batch = [&](int b, const LaneCodes<DI> *c) {
-    const int t0 = b * U * WAVES + wv;
 #pragma unroll
     for (int g = 0; g < U / 4; ++g) {
       float v = tile_scores_x4(tile_partial<DI>(Q, c[4 * g]), tile_partial<DI>(Q, c[4 * g + 1]),
                                tile_partial<DI>(Q, c[4 * g + 2]), tile_partial<DI>(Q, c[4 * g + 3]));
-      const int tile = t0 + (4 * g + rt) * WAVES;
+      const int tile = b * U + 4 * g + rt;
       if (tile * 16 + n >= n_here) v = -INFINITY;
       v = max8_scores(v);
       if ((n & 7) == 0) s_bmax[tile * 2 + (n >> 3)] = v;
     }
   };
-  // the scheduling barriers keep each batch's loads issued together, ahead of the scoring
-  for (int b = 0; live(b); ++b) {
+  auto claim = [&]() {
+    int v = 0;
+    if (l == 0) v = atomicAdd(&s_next, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  __syncthreads();  // s_next is set
+  // the scheduling barriers keep each batch's loads issued together, ahead of
+  // the scoring; the next claim is in flight while the batch is scored
+  int b = __builtin_amdgcn_readfirstlane(wv);
+  while (b < n_batches) {
     LaneCodes<DI> c[U];
     load_batch(b, c);
+    const int next = claim();
     __builtin_amdgcn_sched_barrier(0);
     score_batch(b, c);
+    b = next;
   }
   __syncthreads();
   const int nb_here = (n_here + kBlock - 1) / kBlock;
@@ -152,7 +168,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_scan(const uint8_t *__restrict__
   }
   __syncthreads();
   // flush: the first block of each bin to arrive moves the bin's count out
-  uint32_t *gh = hist + (int64_t)m * kHistBins;
+  uint32_t *gh = hist + ((int64_t)m * hist_rep + blockIdx.x % hist_rep) * kHistBins;
   for (int i = threadIdx.x; i < nb_here; i += blockDim.x) {
     const uint32_t bin = f2key(s_bmax[i]) >> (32 - kHistBits);
     const uint32_t cnt = atomicExch(&s_hist[bin], 0u);
@@ -172,37 +188,37 @@ CSA2_DEV void wave_append(bool pred, int32_t value, int *counter, int32_t *list)
   if (pred) list[base + __popcll(mask & ((1ull << l) - 1ull))] = value;
 }
 
-// Pool filter: threshold bin from the histogram; blocks above it are in the
-// pool for sure, blocks in it go to the tie list.  Appends are gathered in
-// LDS and reserved in the global lists with one atomic per list per workgroup.
-__global__ __launch_bounds__(256) void k_pool_filter(const float *__restrict__ bmax, int64_t nb_stride,
-                                                     const uint32_t *__restrict__ hist,
-                                                     const int32_t *__restrict__ seq_len, const int32_t *__restrict__ q_seq,
-                                                     const int32_t *__restrict__ q_pos, int ratio, int P,
-                                                     uint32_t *__restrict__ counters, int32_t *__restrict__ sure,
-                                                     int32_t *__restrict__ tie) {
+// Threshold bin of each query (one workgroup per query): merge the scan's
+// histogram replicas and find the bin that holds the need-th largest block
+// maximum, need = min(P, visible blocks); -1 when every block is taken.
+// Written to counters[4m + 2] for the filter and the finalisation.
+__global__ __launch_bounds__(256) void k_hist_threshold(const uint32_t *__restrict__ hist, int hist_rep,
+                                                        const int32_t *__restrict__ seq_len,
+                                                        const int32_t *__restrict__ q_seq,
+                                                        const int32_t *__restrict__ q_pos, int ratio, int P,
+                                                        uint32_t *__restrict__ counters) {
   __shared__ int s_scan[8];
-  __shared__ int s_T, s_ns, s_nt, s_bs, s_bt;
-  __shared__ int32_t s_sure[kFilterBlocks], s_tie[kFilterBlocks];
-  const int m = blockIdx.y;
+  __shared__ int s_T;
+  const int m = blockIdx.x;
   int s;
   const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
   const int64_t nb = (vis + kBlock - 1) / kBlock;
-  const int64_t b0 = (int64_t)blockIdx.x * kFilterBlocks;
-  if (b0 >= nb) return;
-  const int64_t need = min<int64_t>(P, nb);
-  if (threadIdx.x == 0) { s_T = -1; s_ns = 0; s_nt = 0; }
-  int T = -1;
+  if (threadIdx.x == 0) s_T = -1;
+  __syncthreads();
   if (nb > P) {
-    const uint32_t *h = hist + (int64_t)m * kHistBins;
+    const int64_t need = P;
     // thread t owns bins [4096-16(t+1), 4096-16t) (thread 0 = highest bins)
     const int hi = kHistBins - 16 * threadIdx.x;
-    const uint4 *h4 = reinterpret_cast<const uint4 *>(h + hi - 16);
     int hv[16];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint4 x = h4[k];
-      hv[4 * k] = (int)x.x; hv[4 * k + 1] = (int)x.y; hv[4 * k + 2] = (int)x.z; hv[4 * k + 3] = (int)x.w;
+    for (int k = 0; k < 16; ++k) hv[k] = 0;
+    for (int r = 0; r < hist_rep; ++r) {
+      const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + ((int64_t)m * hist_rep + r) * kHistBins + hi - 16);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 x = h4[k];
+        hv[4 * k] += (int)x.x; hv[4 * k + 1] += (int)x.y; hv[4 * k + 2] += (int)x.z; hv[4 * k + 3] += (int)x.w;
+      }
     }
     int c = 0;
 #pragma unroll
@@ -218,9 +234,28 @@ __global__ __launch_bounds__(256) void k_pool_filter(const float *__restrict__ b
     }
   }
   __syncthreads();
-  T = s_T;
-  // the threshold bin, for the finalisation (every workgroup finds the same one)
-  if (blockIdx.x == 0 && threadIdx.x == 0) counters[m * 4 + 2] = (uint32_t)T;
+  if (threadIdx.x == 0) counters[m * 4 + 2] = (uint32_t)s_T;
+}
+
+// Pool filter: blocks above the threshold bin are in the pool for sure,
+// blocks in it go to the tie list.  Appends are gathered in
+// LDS and reserved in the global lists with one atomic per list per workgroup.
+__global__ __launch_bounds__(256) void k_pool_filter(const float *__restrict__ bmax, int64_t nb_stride,
+                                                     const int32_t *__restrict__ seq_len, const int32_t *__restrict__ q_seq,
+                                                     const int32_t *__restrict__ q_pos, int ratio, int P,
+                                                     uint32_t *__restrict__ counters, int32_t *__restrict__ sure,
+                                                     int32_t *__restrict__ tie) {
+  __shared__ int s_ns, s_nt, s_bs, s_bt;
+  __shared__ int32_t s_sure[kFilterBlocks], s_tie[kFilterBlocks];
+  const int m = blockIdx.y;
+  int s;
+  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
+  const int64_t nb = (vis + kBlock - 1) / kBlock;
+  const int64_t b0 = (int64_t)blockIdx.x * kFilterBlocks;
+  if (b0 >= nb) return;
+  if (threadIdx.x == 0) { s_ns = 0; s_nt = 0; }
+  __syncthreads();
+  const int T = (int)counters[m * 4 + 2];
   const float *bm = bmax + (int64_t)m * nb_stride;
   for (int j = 0; j < kFilterBlocks / 256; ++j) {
     const int64_t b = b0 + j * 256 + threadIdx.x;
@@ -617,16 +652,33 @@ __global__ __launch_bounds__(NT) void k_block_select(const float *__restrict__ b
 // host side
 // ---------------------------------------------------------------------------
 
+// Tiles per scan workgroup: the largest chunk whose grid still gives about
+// one workgroup per CU.
+static int scan_tiles(int64_t max_len, int m) {
+  auto chunks_of = [&](int chunk) { return (max_len + chunk - 1) / chunk; };
+  if (chunks_of(kScanChunk) * m >= kScanMinGrid) return kScanTiles;
+  if (chunks_of(kScanChunk / 4) * m >= kScanMinGrid) return kScanTiles / 4;
+  return kScanTiles / 16;
+}
+
+// Histogram replicas per query: about 8 scan workgroups share each one.
+static int hist_replicas(int64_t max_len, int m) {
+  const int64_t chunk = 16 * (int64_t)scan_tiles(max_len, m);
+  const int64_t wgs = (max_len + chunk - 1) / chunk;  // workgroups per query
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kHistMaxReplicas, wgs / 8));
+}
+
 IndexWs index_ws_layout(int64_t max_len, int m, int pool_blocks, int top_k) {
   (void)top_k;
   IndexWs w{};
+  w.hist_rep = hist_replicas(max_len, m);
   // room for the largest scan chunk's rounding (smaller chunks need less)
   const int64_t chunks = (max_len + kScanChunk - 1) / kScanChunk;
   w.nb_max = (chunks > 0 ? chunks : 1) * kScanBlocks;
   w.slots = 8 * pool_blocks;
   size_t off = 0;
   w.bmax = off;     off = align256(off + sizeof(float) * (size_t)m * w.nb_max);
-  w.hist = off;     off = align256(off + sizeof(uint32_t) * (size_t)m * kHistBins);
+  w.hist = off;     off = align256(off + sizeof(uint32_t) * (size_t)m * w.hist_rep * kHistBins);
   w.counters = off; off = align256(off + sizeof(uint32_t) * (size_t)m * 4);
   w.sure = off;     off = align256(off + sizeof(int32_t) * (size_t)m * pool_blocks);
   w.tie = off;      off = align256(off + sizeof(int32_t) * (size_t)m * w.nb_max);
@@ -673,20 +725,22 @@ static int index_full_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
   const int64_t nz = (int64_t)((L.sure - L.hist) / sizeof(uint32_t));
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
   if (idx.max_len > 0) {
-    // largest chunk whose grid still gives about one workgroup per CU
     auto chunks_of = [&](int chunk) { return (idx.max_len + chunk - 1) / chunk; };
-    const int64_t m = qs.m;
 #define CSA2_SCAN(T)                                                                                        \
   CSA2_TIMED_LAUNCH(kTimedScan, (k_scan<DI, kScanWaves, T>), dim3((unsigned)chunks_of(T * 16), qs.m),    \
                     dim3(64 * kScanWaves), stream, idx.codes, idx.scales, idx.seq_start, idx.seq_len, idx.ratio, \
-                    qs.seq, qs.pos, q_idx, w_idx, heads, bmax, L.nb_max, hist)
-    if (chunks_of(kScanChunk) * m >= kScanMinGrid) CSA2_SCAN(kScanTiles);
-    else if (chunks_of(kScanChunk / 4) * m >= kScanMinGrid) CSA2_SCAN(kScanTiles / 4);
-    else CSA2_SCAN(kScanTiles / 16);
+                    qs.seq, qs.pos, q_idx, w_idx, heads, bmax, L.nb_max, hist, L.hist_rep)
+    switch (scan_tiles(idx.max_len, qs.m)) {
+      case kScanTiles: CSA2_SCAN(kScanTiles); break;
+      case kScanTiles / 4: CSA2_SCAN(kScanTiles / 4); break;
+      default: CSA2_SCAN(kScanTiles / 16); break;
+    }
 #undef CSA2_SCAN
   }
+  hipLaunchKernelGGL(k_hist_threshold, dim3(qs.m), dim3(256), 0, stream, hist, L.hist_rep, idx.seq_len, qs.seq,
+                     qs.pos, idx.ratio, P, counters);
   const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);
-  hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, hist, idx.seq_len, qs.seq, qs.pos,
+  hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, idx.seq_len, qs.seq, qs.pos,
                      idx.ratio, P, counters, sure, tie);
   hipLaunchKernelGGL(k_pool_finalize, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, counters, sure, tie,
                      idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);

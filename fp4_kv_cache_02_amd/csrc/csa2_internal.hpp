@@ -23,6 +23,7 @@ struct IndexWs {
   size_t bmax, hist, counters, sure, tie, pscore, total;
   int64_t nb_max;       // block slots per query
   int32_t slots;        // 8 * pool_blocks
+  int32_t hist_rep;     // first-scan histogram replicas per query
 };
 IndexWs index_ws_layout(int64_t max_len, int m, int pool_blocks, int top_k);
 
