@@ -163,6 +163,13 @@ class DecodeWorkload:
         vis = np.minimum(np.asarray(wl.seq_lens), (self.q_pos_host + 1) // wl.ratio)
         return int(vis.sum()) * row
 
+    def attn_bytes_per_launch(self) -> int:
+        # one layer's attention: selected main rows, window rows, bf16 queries, fp32 outputs and lse
+        wl = self.wl
+        D, H, W, K = wl.dim, wl.heads, wl.window, wl.top_k
+        kv_row = D // 2 + D // 16
+        return self.M * (K * kv_row + W * (D + 4) + H * D * 2 + H * D * 4 + H * 4)
+
     def step_bytes(self) -> int:
         wl = self.wl
         D, H, W, K, P = wl.dim, wl.heads, wl.window, wl.top_k, wl.pool_blocks
@@ -496,6 +503,7 @@ def main():
             raise RuntimeError("graph replay differs from eager execution")
     else:
         csa2.csa2_profile_scan(True)
+        csa2.csa2_profile_attn(True)
 
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
@@ -517,12 +525,16 @@ def main():
         # events cannot be timed inside a graph replay: the first scan's launch
         # duration comes from HIP events stamped by its dispatch in the same steps run eagerly
         csa2.csa2_profile_scan(True)
+        csa2.csa2_profile_attn(True)
         for _ in range(args.steps):
             W.step()
         torch.cuda.synchronize()
     scan_ms_total, scan_launches = csa2.csa2_profile_scan_read()
+    attn_ms_total, attn_launches = csa2.csa2_profile_attn_read()
     csa2.csa2_profile_scan(False)
+    csa2.csa2_profile_attn(False)
     assert scan_launches == args.steps, (scan_launches, args.steps)
+    assert attn_launches == args.steps * wl.n_layers, (attn_launches, args.steps)
 
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
@@ -538,6 +550,8 @@ def main():
     scan_bytes = W.scan_bytes_per_launch()
     achieved = scan_bytes / (scan_avg_ms / 1e3) / 1e9
     step_bytes = W.step_bytes()
+    attn_avg_ms = attn_ms_total / max(1, attn_launches)
+    attn_bytes = W.attn_bytes_per_launch()
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "scan_traffic.json")
     if os.path.exists(tpath):
@@ -569,6 +583,10 @@ def main():
                      "timing": "HIP events stamped by each first-scan dispatch" + (
                          " (same steps run eagerly after the timed graph replay)" if graph is not None else ""),
                      "algorithmic_bytes_per_launch": scan_bytes},
+        "attention": {"kernel": "k_attn_decode", "avg_launch_ms": round(attn_avg_ms, 5),
+                      "algorithmic_bytes_per_launch": attn_bytes,
+                      "achieved_gbs": round(attn_bytes / (attn_avg_ms / 1e3) / 1e9, 1),
+                      "bound": "latency (one layer's reads are ~1.6 MB)"},
         "step_algorithmic_bytes": step_bytes,
         "step_algorithmic_gbs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "wall_s_timed": round(wall, 4),

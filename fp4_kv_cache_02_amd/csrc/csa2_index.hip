@@ -24,7 +24,7 @@ constexpr int kScanWaves = 8;                    // waves per scan workgroup
 constexpr int kScanTiles = 1024;                 // 16-position tiles per scan workgroup (largest chunk)
 constexpr int kScanChunk = kScanTiles * 16;      // 16384 positions
 constexpr int kScanBlocks = kScanChunk / kBlock; // 2048 block maxima
-constexpr int kFilterBlocks = 1024;              // blocks per pool-filter workgroup
+constexpr int kFilterBlocks = 4096;              // blocks per pool-filter workgroup (fewer workgroups share each list counter)
 constexpr int kRescoreEntries = 64;              // pool blocks per re-score workgroup
 
 
@@ -212,12 +212,23 @@ __global__ __launch_bounds__(256) void k_hist_threshold(const uint32_t *__restri
     int hv[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) hv[k] = 0;
-    for (int r = 0; r < hist_rep; ++r) {
-      const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + ((int64_t)m * hist_rep + r) * kHistBins + hi - 16);
+    // every replica's loads in flight at once (a fixed trip count, replicas
+    // past hist_rep read replica 0 and count nothing)
+    uint4 x[kHistMaxReplicas][4];
+#pragma unroll
+    for (int r = 0; r < kHistMaxReplicas; ++r) {
+      const int rr = r < hist_rep ? r : 0;
+      const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + ((int64_t)m * hist_rep + rr) * kHistBins + hi - 16);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[r][k] = h4[k];
+    }
+#pragma unroll
+    for (int r = 0; r < kHistMaxReplicas; ++r) {
+      if (r >= hist_rep) continue;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint4 x = h4[k];
-        hv[4 * k] += (int)x.x; hv[4 * k + 1] += (int)x.y; hv[4 * k + 2] += (int)x.z; hv[4 * k + 3] += (int)x.w;
+        hv[4 * k] += (int)x[r][k].x; hv[4 * k + 1] += (int)x[r][k].y;
+        hv[4 * k + 2] += (int)x[r][k].z; hv[4 * k + 3] += (int)x[r][k].w;
       }
     }
     int c = 0;
