@@ -24,10 +24,14 @@
 //                  64 heads; V^T comes from the LDS tile through the
 //                  transposing LDS load, P^T from the probability tile.
 //
-// The decoded-key tile and the probability tile are double-buffered by chunk
-// parity, so two workgroup barriers per chunk suffice.  The next chunk's key
-// bytes are loaded (buffer loads, invisible or empty slots at out-of-range
-// offsets, which read zeros) while the current chunk is being computed.
+// The probability tile is double-buffered by chunk parity and the decoded-key
+// tile is single, so three workgroup barriers per chunk suffice.  The next
+// chunk's key bytes are loaded (buffer loads, invisible or empty slots at
+// out-of-range offsets, which read zeros) while the current chunk is being
+// computed.  The next query's heads are staged as f16 in LDS by the current
+// query's chunks, two 16-byte parts per thread each, so a query switch reads
+// its B operands from LDS instead of waiting for memory and converting them
+// in every wave.
 //
 // Exactness as in the other schedules: FP4 and E4M3 entries are f16 numbers;
 // bf16 queries convert to f16 exactly inside the f16 normal range; window
@@ -48,8 +52,11 @@ constexpr int kPTs = kPD + 8;      // [key][dim] row stride of a decoded chunk (
 constexpr int kPPs = kPC + 8;      // [head][key] row stride of the probability tile (f16)
 constexpr float kLazyMax = 8.0f;   // log2 headroom before the running maximum is raised
 
-struct PrefillLds {
-  _Float16 t[2][kPC * kPTs];       // decoded keys of a chunk, by item parity
+constexpr int kQParts = kPH * kPD / 8 / 256;  // 16-byte parts of a query's heads per thread (16)
+
+struct alignas(16) PrefillLds {
+  _Float16 t[kPC * kPTs];          // decoded keys of the current chunk
+  _Float16 qn[kPH * kPTs];         // the next query's heads as f16 [head][channel]
   _Float16 p[2][kPH * kPPs];       // probabilities P[head][key], by item parity
   float cmax[2][kPH][4];           // per-wave chunk maxima of each head (log2 units)
   float rmax[2][4];                // per-wave maxima of the key scales
@@ -60,7 +67,7 @@ struct PrefillLds {
 // Loads of one lane's key for a chunk: the lane (key row, quad) holds
 // channels quad*128 .. +127 of its key: 64 FP4 code bytes + 8 scale bytes of
 // a main entry, or the first 64 of the 128 E4M3 bytes of a window row (the
-// other 64 are read when the chunk is scored, from offset o2).
+// other 64 are read at the start of the chunk's item, from offset o2).
 struct KeyBytes {
   uint32_t w[16];
   uint32_t s[2];
@@ -191,14 +198,26 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const uint16_t *__restrict
       kb.o2 = okw ? co + 64u : kOutOfRange;
       kb.ks_main = main ? (okm ? 1.0f : 0.0f) : -1.0f;
     };
-    // the lines of query k's heads h0 .. h0+hq-1 (hq KB), two per thread
-    auto touch_q = [&](int k) -> uint32_t {
+    // Query k's heads h0 .. h0+hq-1 (bf16, hq KB; empty past the batch) and
+    // their staging into L.qn: part p of thread t is the 8 channels
+    // 8 * (i % 64) .. +7 of head i / 64, i = 256 p + t.
+    auto q_rsrc = [&](int k) {
       const bool ok = k < nq;
-      const rsrc_t r = make_rsrc(q + ((int64_t)(mb + (ok ? k : 0) * G) * H + h0) * kPD, (uint32_t)(hq * kPD * 2));
-      const uint32_t o0 = ok ? (threadIdx.x * 2u) * 128u : kOutOfRange;
-      const uint32_t a = __builtin_amdgcn_raw_buffer_load_b32(r, o0, 0, 0);
-      const uint32_t b = __builtin_amdgcn_raw_buffer_load_b32(r, o0 + 128u, 0, 0);
-      return a ^ b;
+      return make_rsrc(q + ((int64_t)(mb + (ok ? k : 0) * G) * H + h0) * kPD, ok ? (uint32_t)(hq * kPD * 2) : 0u);
+    };
+    auto q_part_load = [&](rsrc_t r, int p, bool want) -> u32x4_t {
+      return __builtin_amdgcn_raw_buffer_load_b128(r, want ? (uint32_t)(256 * p + threadIdx.x) * 16u : kOutOfRange, 0, 0);
+    };
+    // (head 4p + t/64, channels 8 (t % 64) ..: one base per thread plus 4p rows)
+    const int qn_base = (int)(threadIdx.x >> 6) * kPTs + 8 * (int)(threadIdx.x & 63);
+    auto q_part_store = [&](int p, const u32x4_t &x) {
+      half8_t h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[2 * e] = (_Float16)__uint_as_float(x[e] << 16);
+        h[2 * e + 1] = (_Float16)__uint_as_float(x[e] & 0xFFFF0000u);
+      }
+      *reinterpret_cast<half8_t *>(&L.qn[qn_base + p * (4 * kPTs)]) = h;
     };
 
     // ---- stream set-up: indices of items 0..3, lines of items 1, 2, bytes of item 0 ----
@@ -218,7 +237,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const uint16_t *__restrict
       next(u); j3 = index_of(u);
       load_keys(Cursor{0, 0}, j0, kb);
     }
-    uint32_t t1, t2, tq = 0u;
+    uint32_t t1, t2;
+    int pf_done = 0;   // parts of the next query's heads already staged in L.qn
     {
       Cursor u{0, 0};
       next(u); t1 = touch_keys(u, j1);
@@ -234,27 +254,29 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const uint16_t *__restrict
       const int buf = it & 1;
       const int m = mb + cur.k * G;
       if (cur.c == 0) {
-        // ---- a new query: its 64 heads as B operands (lane (head 16ct + row,
-        //      quad) holds channels quad*128 + 8kk .. +7 in qb[ct][kk]) ----
-        const rsrc_t r_q = make_rsrc(q + ((int64_t)m * H + h0) * kPD, (uint32_t)(hq * kPD * 2));
+        // ---- a new query: parts of its heads that the previous query's items
+        //      did not stage (all of them for the batch's first query) are
+        //      staged now; then each wave takes its B operands from L.qn:
+        //      lane (head 16ct + row, quad) holds channels quad*128 + 8kk .. +7
+        //      in qb[ct][kk] ----
+        if (pf_done < kQParts) {
+          const rsrc_t r_q = q_rsrc(cur.k);
+          u32x4_t raw[kQParts];
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const uint32_t qo = (uint32_t)((16 * ct + row) * kPD + quad * 128) * 2u;
-          u32x4_t raw[16];  // all loads of the head tile in flight before the first conversion
+          for (int p = 0; p < kQParts; ++p) raw[p] = q_part_load(r_q, p, p >= pf_done);
 #pragma unroll
-          for (int kk = 0; kk < 16; ++kk) raw[kk] = __builtin_amdgcn_raw_buffer_load_b128(r_q, qo + 16u * kk, 0, 0);
+          for (int p = 0; p < kQParts; ++p)
+            if (p >= pf_done) q_part_store(p, raw[p]);
+          __syncthreads();
+        }
+        pf_done = 0;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
           for (int kk = 0; kk < 16; ++kk) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              qb[ct][kk][2 * i] = (_Float16)__uint_as_float(raw[kk][i] << 16);
-              qb[ct][kk][2 * i + 1] = (_Float16)__uint_as_float(raw[kk][i] & 0xFFFF0000u);
-            }
+            qb[ct][kk] = *reinterpret_cast<const half8_t *>(&L.qn[(16 * ct + row) * kPTs + quad * 128 + 8 * kk]);
             asm("" : "+a"(qb[ct][kk]));
           }
-          // one head tile's loads at a time: keeps the staging registers few
-          __builtin_amdgcn_sched_barrier(0);
-        }
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -263,16 +285,35 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const uint16_t *__restrict
         for (int ct = 0; ct < 4; ++ct) { m_run[ct] = kNegInf; l_part[ct] = 0.0f; }
         e_cur = 0;
       }
+      // ---- two parts of the next query's heads, staged after the chunk maxima meet (the
+      //      query's last item stages none) ----
+      const bool pf = cur.c < NC - 1 && pf_done < kQParts;
+      u32x4_t pfr[2];
+      {
+        const rsrc_t r_q = q_rsrc(cur.k + 1);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) pfr[i] = q_part_load(r_q, pf_done + i, pf && pf_done + i < kQParts);
+      }
+      // ---- window items: the second 64 bytes of each row, issued before the
+      //      look-ahead loads so that waiting for them does not also wait for
+      //      those (loads complete in issue order); main items read out of range ----
+      uint32_t w2[16];
+      {
+        const int wc = wcount_of(cur.k);
+        const rsrc_t r_win = make_rsrc(wc ? swa_codes + (int64_t)wstart_of(cur.k) * kPD : nullptr, (uint32_t)(wc * kPD));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r_win, kb.o2 + 16u * i, 0, 0);
+          w2[4 * i] = x[0]; w2[4 * i + 1] = x[1]; w2[4 * i + 2] = x[2]; w2[4 * i + 3] = x[3];
+        }
+      }
       // ---- look-ahead: index of item it+4, lines of item it+3 ----
       const int32_t j4 = index_of(c4);
       const uint32_t t3 = touch_keys(c3, j3);
       asm volatile("" ::"v"(t1));
-      // the next query's heads, touched on every item (after the first touch they hit the caches)
-      asm volatile("" ::"v"(tq));
-      tq = touch_q(cur.k + 1);
 
       // ---- this wave's 16 keys: scales to LDS, S^T = K Q^T, decoded keys to the tile ----
-      _Float16 *tile = L.t[buf];
+      _Float16 *tile = L.t;
       const float kbs = key_scale(kb);
       if (quad == 0) L.ks[buf][16 * wv + row] = kbs;
       const float kbm = max16_lanes(kbs);
@@ -292,15 +333,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const uint16_t *__restrict
           for (int ct = 0; ct < 4; ++ct) sacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[ct][kk], sacc[ct], 0, 0, 0);
         }
       } else {
-        // window rows: the second 64 bytes arrive while the first are scored
-        const int wc = wcount_of(cur.k);
-        const rsrc_t r_win = make_rsrc(wc ? swa_codes + (int64_t)wstart_of(cur.k) * kPD : nullptr, (uint32_t)(wc * kPD));
-        uint32_t w2[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r_win, kb.o2 + 16u * i, 0, 0);
-          w2[4 * i] = x[0]; w2[4 * i + 1] = x[1]; w2[4 * i + 2] = x[2]; w2[4 * i + 3] = x[3];
-        }
+        // window rows: E4M3 codes, the first 64 bytes from kb, the rest from w2
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
           const half8_t a = kk < 8 ? e4m3x8_to_f16(kb.w[2 * kk], kb.w[2 * kk + 1])
@@ -329,6 +362,14 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const uint16_t *__restrict
         if (quad == 0) L.cmax[buf][16 * ct + row][wv] = mx;
       }
       __syncthreads();
+      // ---- the staged parts of the next query's heads (every wave has read
+      //      the current query's from L.qn before the barrier above) ----
+      if (pf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (pf_done + i < kQParts) q_part_store(pf_done + i, pfr[i]);
+        pf_done = min(kQParts, pf_done + 2);
+      }
       // ---- softmax statistics, lazily raised running maximum ----
       const float4 rv = *reinterpret_cast<const float4 *>(&L.rmax[buf][0]);
       float4 cvs[4];
@@ -404,6 +445,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const uint16_t *__restrict
         }
       }
 
+      // the tile is free for the next chunk and the staged heads are complete
+      __syncthreads();
       if (cur.c == NC - 1) {
         // ---- the query's last chunk: denominators across key quarters and waves, outputs ----
 #pragma unroll
@@ -430,7 +473,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const uint16_t *__restrict
       }
       next(cur); next(c1); next(c3); next(c4);
     }
-    asm volatile("" ::"v"(t1), "v"(t2), "v"(tq));
+    asm volatile("" ::"v"(t1), "v"(t2));
     __syncthreads();  // LDS of this batch is free
   }
 }
