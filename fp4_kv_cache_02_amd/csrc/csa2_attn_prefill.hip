@@ -285,15 +285,6 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const uint16_t *__restrict
         for (int ct = 0; ct < 4; ++ct) { m_run[ct] = kNegInf; l_part[ct] = 0.0f; }
         e_cur = 0;
       }
-      // ---- two parts of the next query's heads, staged after the chunk maxima meet (the
-      //      query's last item stages none) ----
-      const bool pf = cur.c < NC - 1 && pf_done < kQParts;
-      u32x4_t pfr[2];
-      {
-        const rsrc_t r_q = q_rsrc(cur.k + 1);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) pfr[i] = q_part_load(r_q, pf_done + i, pf && pf_done + i < kQParts);
-      }
       // ---- window items: the second 64 bytes of each row, issued before the
       //      look-ahead loads so that waiting for them does not also wait for
       //      those (loads complete in issue order); main items read out of range ----
@@ -311,6 +302,15 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const uint16_t *__restrict
       const int32_t j4 = index_of(c4);
       const uint32_t t3 = touch_keys(c3, j3);
       asm volatile("" ::"v"(t1));
+      // ---- two parts of the next query's heads, staged after the chunk maxima meet (the
+      //      query's last item stages none) ----
+      const bool pf = cur.c < NC - 1 && pf_done < kQParts;
+      u32x4_t pfr[2];
+      {
+        const rsrc_t r_q = q_rsrc(cur.k + 1);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) pfr[i] = q_part_load(r_q, pf_done + i, pf && pf_done + i < kQParts);
+      }
 
       // ---- this wave's 16 keys: scales to LDS, S^T = K Q^T, decoded keys to the tile ----
       _Float16 *tile = L.t;
