@@ -65,7 +65,9 @@ __global__ __launch_bounds__(256) void k_quantize_fp4(const T *__restrict__ x, i
 //   phase 3 encode y into the indexer-key planes.
 constexpr int kDeriveLdsFloats = 4096;  // decoded rows per workgroup (16 KiB); needs idx_dim <= dim
 
-template <typename T>
+// JM: row slots per thread in phase 2, at least ceil(rows per workgroup /
+// (256 / idx_dim)) (at most 16, since idx_dim <= dim).
+template <typename T, int JM>
 __global__ __launch_bounds__(256) void k_quantize_fp4_derive(const T *__restrict__ x, int64_t rows, int dim,
                                                               const int64_t *__restrict__ dst_row,
                                                               uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
@@ -109,19 +111,28 @@ __global__ __launch_bounds__(256) void k_quantize_fp4_derive(const T *__restrict
   const int col = threadIdx.x % idx_dim;
   const int rstep = blockDim.x / idx_dim;
   const int rfirst = threadIdx.x / idx_dim;
-  double acc[32];
+  // Channels go in ascending order (fp64 fma per channel), 16 at a time: the
+  // 16 W_ik values of a block are loaded together, so the loop waits for
+  // memory once per block, not once per channel (dim is a multiple of 16).
+  double acc[JM];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) acc[j] = 0.0;
-  for (int c = 0; c < dim; ++c) {
-    const double w = (double)w_ik[(int64_t)c * idx_dim + col];
+  for (int j = 0; j < JM; ++j) acc[j] = 0.0;
+  for (int c0 = 0; c0 < dim; c0 += kGroup) {
+    float wv[kGroup];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int rr = rfirst + j * rstep;
-      if (rr < nr) acc[j] = fma((double)dq[rr * dim + c], w, acc[j]);
+    for (int u = 0; u < kGroup; ++u) wv[u] = w_ik[(int64_t)(c0 + u) * idx_dim + col];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      const double w = (double)wv[u];
+#pragma unroll
+      for (int j = 0; j < JM; ++j) {
+        const int rr = rfirst + j * rstep;
+        if (rr < nr) acc[j] = fma((double)dq[rr * dim + c0 + u], w, acc[j]);
+      }
     }
   }
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
+  for (int j = 0; j < JM; ++j) {
     const int rr = rfirst + j * rstep;
     if (rr < nr) yk[rr * idx_dim + col] = (float)acc[j];
   }
@@ -298,12 +309,17 @@ int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const
   } else {
     const int rb = kDeriveLdsFloats / dim;
     const dim3 grid((unsigned)((rows + rb - 1) / rb));
-    if (x_dtype == CSA2_F32)
-      hipLaunchKernelGGL(k_quantize_fp4_derive<float>, grid, dim3(256), 0, stream, (const float *)x, rows, dim,
-                         dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales);
-    else
-      hipLaunchKernelGGL(k_quantize_fp4_derive<uint16_t>, grid, dim3(256), 0, stream, (const uint16_t *)x, rows,
-                         dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales);
+    const int jm = (rb + 256 / idx_dim - 1) / (256 / idx_dim);  // <= 16 since idx_dim <= dim
+#define CSA2_DERIVE_LAUNCH(T, JM)                                                                            \
+    hipLaunchKernelGGL((k_quantize_fp4_derive<T, JM>), grid, dim3(256), 0, stream, (const T *)x, rows, dim, \
+                       dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales)
+#define CSA2_DERIVE_JM(T)                                                                 \
+    if (jm <= 1) CSA2_DERIVE_LAUNCH(T, 1); else if (jm <= 2) CSA2_DERIVE_LAUNCH(T, 2);    \
+    else if (jm <= 4) CSA2_DERIVE_LAUNCH(T, 4); else if (jm <= 8) CSA2_DERIVE_LAUNCH(T, 8); \
+    else CSA2_DERIVE_LAUNCH(T, 16)
+    if (x_dtype == CSA2_F32) { CSA2_DERIVE_JM(float); } else { CSA2_DERIVE_JM(uint16_t); }
+#undef CSA2_DERIVE_JM
+#undef CSA2_DERIVE_LAUNCH
   }
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
