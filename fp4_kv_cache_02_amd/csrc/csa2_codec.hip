@@ -154,14 +154,18 @@ __global__ __launch_bounds__(256) void k_quantize_fp4_derive(const T *__restrict
   }
 }
 
-// Quantise one row per workgroup and derive its indexer key, for small
-// batches (the decode write path).  1024 threads: thread -> (output column,
-// slice of the channels); every W_ik value a thread needs is loaded before
-// the fp64 dot products start, and the slices are added in slice order.
-constexpr int kRowThreads = 1024;
+// Quantise rows and derive their indexer keys for small batches (the decode
+// write path): grid (rows, idx_dim / 16), one workgroup per (row, 16-column
+// group of the indexer key), 16 * (1024 / idx_dim) threads: thread ->
+// (column of the group, slice of PER channels); every W_ik value a thread
+// needs is loaded before the fp64 dot products start, each slice sums from
+// +0 in channel order and the slices are added in slice order.  Every
+// workgroup of a row encodes the row (the exact decoded values feed its dot
+// products); the first writes its codes.
+constexpr int kRowThreads = 1024;   // (column, slice) pairs per row
 
 template <typename T, int PER>
-__global__ __launch_bounds__(kRowThreads) void k_quantize_fp4_derive_row(const T *__restrict__ x, int dim,
+__global__ __launch_bounds__(512) void k_quantize_fp4_derive_row(const T *__restrict__ x, int dim,
                                                                           const int64_t *__restrict__ dst_row,
                                                                           uint8_t *__restrict__ codes,
                                                                           uint8_t *__restrict__ scales,
@@ -169,14 +173,15 @@ __global__ __launch_bounds__(kRowThreads) void k_quantize_fp4_derive_row(const T
                                                                           int idx_dim, uint8_t *__restrict__ ik_codes,
                                                                           uint8_t *__restrict__ ik_scales) {
   __shared__ float dq[kDeriveLdsFloats];
-  __shared__ double part[kRowThreads];
-  __shared__ float yk[256];
+  __shared__ double part[512];
+  __shared__ float yk[kGroup];
   const int64_t r = blockIdx.x;
+  const int cg = blockIdx.y;              // 16-column group of the indexer key
   const int64_t d = dst_row ? dst_row[r] : r;
   const int gpr = dim / kGroup;
-  const int col = threadIdx.x % idx_dim;
+  const int col = cg * kGroup + (int)(threadIdx.x % kGroup);
   const int nparts = kRowThreads / idx_dim;
-  const int pidx = threadIdx.x / idx_dim;
+  const int pidx = threadIdx.x / kGroup;
   const int c0 = pidx * PER;              // dim == PER * nparts (checked by the launcher)
   float wv[PER];
 #pragma unroll
@@ -189,8 +194,10 @@ __global__ __launch_bounds__(kRowThreads) void k_quantize_fp4_derive_row(const T
     uint2 packed;
     uint8_t sb;
     encode_group(v, &packed, &sb);
-    *reinterpret_cast<uint2 *>(codes + d * (dim / 2) + g * 8) = packed;
-    scales[d * gpr + g] = sb;
+    if (cg == 0) {
+      *reinterpret_cast<uint2 *>(codes + d * (dim / 2) + g * 8) = packed;
+      scales[d * gpr + g] = sb;
+    }
     const float s = e4m3_pos_value(sb);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -207,18 +214,18 @@ __global__ __launch_bounds__(kRowThreads) void k_quantize_fp4_derive_row(const T
   for (int i = 0; i < PER; ++i) acc = fma((double)dq[c0 + i], (double)wv[i], acc);
   part[threadIdx.x] = acc;
   __syncthreads();
-  if (threadIdx.x < idx_dim) {
+  if (threadIdx.x < kGroup) {
     double t = 0.0;
-    for (int k = 0; k < nparts; ++k) t += part[k * idx_dim + threadIdx.x];
+    for (int k = 0; k < nparts; ++k) t += part[k * kGroup + threadIdx.x];
     yk[threadIdx.x] = (float)t;
   }
   __syncthreads();
   const int igpr = idx_dim / kGroup;
-  if (threadIdx.x < igpr) {
-    const int g = threadIdx.x;
+  if (threadIdx.x == 0) {
+    const int g = cg;
     float v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = yk[g * kGroup + i];
+    for (int i = 0; i < 16; ++i) v[i] = yk[i];
     uint2 packed;
     uint8_t sb;
     encode_group(v, &packed, &sb);
@@ -293,10 +300,11 @@ int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const
   } else if (rows <= 1024 && dim % (kRowThreads / idx_dim) == 0 &&
              (dim / (kRowThreads / idx_dim) == 8 || dim / (kRowThreads / idx_dim) == 16 ||
               dim / (kRowThreads / idx_dim) == 32 || dim / (kRowThreads / idx_dim) == 64)) {
-    const dim3 grid((unsigned)rows);
+    const dim3 grid((unsigned)rows, (unsigned)(idx_dim / kGroup));
+    const dim3 block((unsigned)(kGroup * (kRowThreads / idx_dim)));  // 64 .. 512
     const int per = dim / (kRowThreads / idx_dim);
 #define CSA2_ROW_LAUNCH(T, PERV)                                                                                  \
-    hipLaunchKernelGGL((k_quantize_fp4_derive_row<T, PERV>), grid, dim3(kRowThreads), 0, stream, (const T *)x, dim, \
+    hipLaunchKernelGGL((k_quantize_fp4_derive_row<T, PERV>), grid, block, 0, stream, (const T *)x, dim,             \
                        dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales)
     if (x_dtype == CSA2_F32) {
       if (per == 8) CSA2_ROW_LAUNCH(float, 8); else if (per == 16) CSA2_ROW_LAUNCH(float, 16);
