@@ -87,9 +87,14 @@ def test_quantize_bf16_input_and_scattered_rows():
 
 
 @pytest.mark.parametrize("dim,di,rows", [(128, 64, 2000), (512, 128, 2000), (256, 256, 2000), (512, 128, 5),
-                                         (512, 128, 1024), (128, 64, 3)])
+                                         (512, 128, 1024), (128, 64, 3),
+                                         (512, 32, 1500), (512, 64, 1500), (96, 32, 1100),
+                                         (256, 256, 7), (512, 32, 9)])
 def test_derive_indexer_key_bit_exact(dim, di, rows):
-    # up to 1024 rows take the one-row-per-workgroup path, more the multi-row path
+    # Up to 1024 rows take the small-batch path (one workgroup per row and
+    # 16-column group of the key, 64 to 512 threads), more the multi-row path
+    # (4096 / dim rows per workgroup; 1, 2, 4, 8 or 16 row slots per thread,
+    # 96 channels leave a ragged last workgroup).
     announce("derive indexer key", dim, di, rows)
     x = synth.main_kv_rows(0, 0, 0, rows, dim)
     w = synth.w_ik(0, dim, di)
