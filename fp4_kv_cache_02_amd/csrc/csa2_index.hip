@@ -25,7 +25,7 @@ constexpr int kScanTiles = 1024;                 // 16-position tiles per scan w
 constexpr int kScanChunk = kScanTiles * 16;      // 16384 positions
 constexpr int kScanBlocks = kScanChunk / kBlock; // 2048 block maxima
 constexpr int kFilterBlocks = 4096;              // blocks per pool-filter workgroup (fewer workgroups share each list counter)
-constexpr int kRescoreEntries = 64;              // pool blocks per re-score workgroup
+constexpr int kRescoreEntries = 64;              // pool blocks per re-score workgroup (at most)
 
 
 // ---------------------------------------------------------------------------
@@ -431,10 +431,11 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
   if (threadIdx.x == 0) pool_count[m] = need;
 }
 
-// Re-score the positions of 64 pool blocks per workgroup.  Slot 8*e + r of a
-// query holds the score of position 8*pool[e] + r (-inf when not visible).
-// Each wave first loads its pool entries, then all its rows, then scores.
-template <int DI>
+// Re-score the positions of E pool blocks per workgroup (E = 64, or fewer
+// when that leaves most of the chip idle).  Slot 8*e + r of a query holds
+// the score of position 8*pool[e] + r (-inf when not visible).  Each wave
+// first loads its pool entries, then all its rows, then scores.
+template <int DI, int E>
 __global__ __launch_bounds__(256) void k_rescore(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                                  const int64_t *__restrict__ seq_start,
                                                  const int32_t *__restrict__ seq_len, int ratio,
@@ -447,18 +448,18 @@ __global__ __launch_bounds__(256) void k_rescore(const uint8_t *__restrict__ cod
   int s;
   const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
   const int cnt = min(pool_count[m], P);
-  const int e0 = blockIdx.x * kRescoreEntries;
+  const int e0 = blockIdx.x * E;
   if (e0 >= cnt) return;
   float *ps = pscore + (int64_t)m * 8 * P;
   const int l = lane_id(), n = l & 15, qq = l >> 4, wv = threadIdx.x >> 6;
   if (vis == 0) {
-    for (int i = threadIdx.x; i < 8 * kRescoreEntries; i += blockDim.x)
+    for (int i = threadIdx.x; i < 8 * E; i += blockDim.x)
       if (e0 * 8 + i < 8 * cnt) ps[e0 * 8 + i] = -INFINITY;
     return;
   }
   const int64_t row0 = seq_start[s];
   const int32_t *pl = pool + (int64_t)m * P;
-  constexpr int TPW = kRescoreEntries / 2 / 4;  // tiles per wave
+  constexpr int TPW = E / 2 / 4;  // tiles per wave
   int64_t pos[TPW];
   bool valid[TPW];
 #pragma unroll
@@ -703,9 +704,17 @@ static int rescore_and_select(const csa2_fp4_cache &idx, const csa2_queries &qs,
                               const float *w_idx, int heads, const int32_t *pool, const int32_t *pool_count,
                               int P, int K, int32_t *topk_out, float *topk_score, float *pscore,
                               hipStream_t stream) {
-  const dim3 g5((P + kRescoreEntries - 1) / kRescoreEntries, qs.m);
-  hipLaunchKernelGGL(k_rescore<DI>, g5, dim3(256), 0, stream, idx.codes, idx.scales, idx.seq_start, idx.seq_len,
-                     idx.ratio, qs.seq, qs.pos, q_idx, w_idx, heads, pool, pool_count, P, pscore);
+  // 64 blocks per workgroup, or 16 when that would leave most CUs idle (few queries)
+  if ((int64_t)((P + kRescoreEntries - 1) / kRescoreEntries) * qs.m >= 512) {
+    const dim3 g5((P + kRescoreEntries - 1) / kRescoreEntries, qs.m);
+    hipLaunchKernelGGL((k_rescore<DI, kRescoreEntries>), g5, dim3(256), 0, stream, idx.codes, idx.scales,
+                       idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, q_idx, w_idx, heads, pool, pool_count,
+                       P, pscore);
+  } else {
+    const dim3 g5((P + 15) / 16, qs.m);
+    hipLaunchKernelGGL((k_rescore<DI, 16>), g5, dim3(256), 0, stream, idx.codes, idx.scales, idx.seq_start,
+                       idx.seq_len, idx.ratio, qs.seq, qs.pos, q_idx, w_idx, heads, pool, pool_count, P, pscore);
+  }
   // 8P <= 32768 slots (P <= 4096)
   if (8 * P <= 256 * 16)
     hipLaunchKernelGGL((k_topk_select<256, 16>), dim3(qs.m), dim3(256), 0, stream, pscore, pool, pool_count, P, K,
