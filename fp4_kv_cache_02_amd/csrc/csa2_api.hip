@@ -86,6 +86,13 @@ int check_index_common(const csa2_fp4_cache *idx, const csa2_queries *qs, const 
   return CSA2_OK;
 }
 
+// The flat (pool_blocks == 0) indexer keeps every query's block maxima for its
+// block select: at most kBlockSelectMax blocks per sequence.
+int check_flat_limits(const csa2_fp4_cache *idx, int pool_blocks) {
+  if (pool_blocks == 0 && (idx->max_len + kBlock - 1) / kBlock > kBlockSelectMax) return CSA2_ERR_UNSUPPORTED;
+  return CSA2_OK;
+}
+
 size_t index_bytes(const csa2_fp4_cache *idx, int m, int pool_blocks, int top_k) {
   if (pool_blocks == 0) return flat_ws_bytes(idx->max_len, m, top_k);
   return index_ws_layout(idx->max_len, m, pool_blocks, top_k).total;
@@ -178,6 +185,7 @@ int32_t csa2_index_full(const csa2_fp4_cache *idx, const csa2_queries *qs, const
   if (pool_blocks < 0) return CSA2_ERR_BAD_SHAPE;
   if (pool_blocks > 4096) return CSA2_ERR_UNSUPPORTED;
   if (pool_blocks > 0 && qs->m > 0 && (!pool_out || !pool_count)) return CSA2_ERR_NULL_ARG;
+  if ((st = check_flat_limits(idx, pool_blocks))) return st;
   if (qs->m == 0) return CSA2_OK;
   if (!workspace || ws_bytes < index_bytes(idx, qs->m, pool_blocks, top_k)) return CSA2_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return CSA2_ERR_MISALIGNED;
@@ -269,8 +277,10 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
   size_t need = 0;
   if ((st = csa2_group_workspace_size(g, &need))) return st;
   if (!workspace || ws_bytes < need) return CSA2_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_ERR_MISALIGNED;
   // validate every call before enqueueing anything
   if ((st = check_index_common(&g->idx, &g->qs, g->q_idx, g->w_idx, g->idx_heads, g->top_k, g->topk))) return st;
+  if (g->first_mode == CSA2_MODE_FULL && (st = check_flat_limits(&g->idx, g->pool_blocks))) return st;
   if ((st = check_cache(&g->kv, true))) return st;
   if (g->kv.dim != 64 && g->kv.dim != 128 && g->kv.dim != 256 && g->kv.dim != 512) return CSA2_ERR_UNSUPPORTED;
   if (g->q_dtype != CSA2_F32 && g->q_dtype != CSA2_BF16) return CSA2_ERR_BAD_DTYPE;

@@ -9,9 +9,13 @@ layers form 3 groups of 6 at ratio 2, each Full + 5 Reuse.  Every layer of a
 group attends with its own query and window rows over the group's single
 Top-K list (Reuse copies it, P1 CSA2 section).
 
-Parity pin: the Reuse layers' lists are byte-equal to the group's list and
-each layer's output equals the single-layer attention oracle on that list
-(tests/test_oracle_group.py).
+Parity pins (tests/test_oracle_group.py): planted indexer keys whose scores
+are known by construction fix the selected lists of both functions at tokens
+before the cache's last entry and at ratio 2 inside a two-token entry
+(planted winners the token may not see yet must stay out); every layer's
+output equals torch's scaled_dot_product_attention in fp64 over the rows of
+the known list plus the layer's window (tests/test_oracle_attention.py adds
+the Reuse-list and per-layer composition checks).
 """
 from __future__ import annotations
 

@@ -118,6 +118,11 @@ def test_index_validation():
     assert call(wsb=16) == WORKSPACE
     assert call(wsp=FAKE + 64) == MISALIGNED
     assert call(q=csa2.Queries(None, FAKE, 2)) == NULL_ARG
+    # flat (pool 0) indexer: more than 65,536 blocks per sequence is refused
+    # before anything is enqueued, whatever the workspace
+    big = _cache(max_len=65536 * 8 + 1)
+    assert call(cache=big, pool=0) == UNSUPPORTED
+    assert call(cache=big, pool=0, wsp=None) == UNSUPPORTED
     assert call(q=csa2.Queries(None, None, 0)) == 0          # no queries: nothing to do
     assert L.csa2_reindex(ctypes.byref(c), ctypes.byref(qs), FAKE, FAKE, 8, FAKE, FAKE, 0, 64, FAKE, None, FAKE,
                           base, None) == BAD_SHAPE
@@ -158,6 +163,43 @@ def test_group_validation():
     assert L.csa2_group_step(ctypes.byref(g), FAKE, 1 << 20, None) == BAD_SHAPE
     g.first_mode = csa2.CSA2_MODE_FULL
     assert L.csa2_group_step(ctypes.byref(g), FAKE, 1 << 20, None) == NULL_ARG      # per-layer arrays missing
+
+
+def _group_desc(n_layers=2, pool_blocks=64, idx_len=4096):
+    """A Full group descriptor whose pointers are never dereferenced (every
+    call below is refused by the host checks)."""
+    keep = []
+    g = csa2.GroupDesc()
+    g.first_mode, g.n_layers = csa2.CSA2_MODE_FULL, n_layers
+    g.kv = _cache(dim=512)
+    g.idx = _cache(dim=128, max_len=idx_len)
+    g.qs = csa2.Queries(FAKE, FAKE, 1)
+    g.q_idx, g.w_idx, g.idx_heads, g.pool_blocks, g.top_k = FAKE, FAKE, 8, pool_blocks, 64
+    g.pool, g.pool_count, g.topk = FAKE, FAKE, FAKE
+    q = (ctypes.c_void_p * n_layers)(*([FAKE] * n_layers))
+    out = (ctypes.c_void_p * n_layers)(*([FAKE] * n_layers))
+    sw = (csa2.Swa * n_layers)(*([csa2.Swa(FAKE, FAKE, FAKE, FAKE, 512, 128)] * n_layers))
+    keep += [q, out, sw]
+    g.q = ctypes.cast(q, ctypes.POINTER(ctypes.c_void_p))
+    g.out = ctypes.cast(out, ctypes.POINTER(ctypes.c_void_p))
+    g.swa = ctypes.cast(sw, ctypes.POINTER(csa2.Swa))
+    g.q_dtype, g.heads, g.softmax_scale = csa2.CSA2_BF16, 64, 0.04
+    return g, keep
+
+
+def test_group_validation_runs_before_any_enqueue():
+    L = _lib()
+    g, keep = _group_desc()
+    n = ctypes.c_size_t(0)
+    assert L.csa2_group_workspace_size(ctypes.byref(g), ctypes.byref(n)) == 0
+    # a workspace that is large enough but not 256-byte aligned
+    assert L.csa2_group_step(ctypes.byref(g), FAKE + 64, n.value, None) == MISALIGNED
+    # a flat Full group over a cache with more blocks than the flat indexer
+    # keeps: refused up front (its write path must not run)
+    g2, keep2 = _group_desc(pool_blocks=0, idx_len=65536 * 8 + 1)
+    g2.new_rows, g2.new_kv, g2.new_dst_row, g2.w_ik, g2.new_kv_dtype = 16, FAKE, FAKE, FAKE, csa2.CSA2_BF16
+    assert L.csa2_group_workspace_size(ctypes.byref(g2), ctypes.byref(n)) == 0
+    assert L.csa2_group_step(ctypes.byref(g2), FAKE, n.value, None) == UNSUPPORTED
 
 
 def test_binding_refuses_missing_library(monkeypatch, tmp_path):

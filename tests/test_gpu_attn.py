@@ -122,11 +122,11 @@ def test_attn_no_window_padded_slots():
 
 def test_attn_prefill_schedule_sampled():
     # 320 queries x 64 heads: the one-workgroup-per-query (flash) schedule;
-    # every query runs on the GPU, 12 sampled queries are checked
+    # every query runs on the GPU, 64 sampled queries are checked
     M = 320
     rng = np.random.default_rng(207)
     _run(207, 6000, 512, 64, "bf16", 512, 128, M, [5999] * M, [512] * M, [0] * M, [0] * M,
-         rng.integers(1, 129, M).tolist(), sample=sorted(rng.choice(M, 12, replace=False).tolist()))
+         rng.integers(1, 129, M).tolist(), sample=sorted(rng.choice(M, 64, replace=False).tolist()))
 
 
 def _run_prefill(cfg, n_rows, H, K, W, M, q_pos, n_valid, n_pad, n_invalid, counts, sample, q_mult=1.0):
@@ -184,10 +184,12 @@ def _run_prefill(cfg, n_rows, H, K, W, M, q_pos, n_valid, n_pad, n_invalid, coun
 
 def test_attn_prefill_chunk_4096_queries_sampled():
     # a 4,096-query chunk (tokens 4096 .. 8191 of an 8,192-entry cache), Top-512
-    # lists and 128-row sliding windows; ten queries checked
+    # lists and 128-row sliding windows; 256 queries checked (the first, the
+    # last and 254 drawn at random)
     M, n = 4096, 8192
     rng = np.random.default_rng(208)
-    sample = sorted(set([0, M - 1] + rng.choice(M, 8, replace=False).tolist()))
+    sample = sorted(set([0, M - 1] + rng.choice(np.arange(1, M - 1), 254, replace=False).tolist()))
+    assert len(sample) == 256
     _run_prefill(208, n, 64, 512, 128, M, list(range(n - M, n)), [512] * M, [0] * M, [0] * M, [128] * M, sample)
 
 

@@ -94,6 +94,39 @@ def test_index_full_matches_oracle(case):
         _check_query(rc, rs, starts[s_], vis, qf[i], wi[i], P, K, gpool[i], gcnt[i], gtopk[i], gsc[i])
 
 
+@pytest.mark.parametrize("shape", ["c4_4x1m", "c4_one_seq_4_queries"])
+def test_index_c4_full_oracle_pass(shape):
+    """The 4 x 1M decode shape against a full fp64 oracle pass of every query.
+
+    Four sequences of 1,048,576 entries (or four queries at different tokens
+    of one such sequence) take the 16,384-position scan chunks, the 8
+    histogram replicas and the bitmap pool finalisation over 131,072 blocks.
+    The oracle scores every visible entry of every query; pool and Top-K are
+    compared element by element modulo the near-tie band with no other slack,
+    and the returned scores within 1e-5.  The caches are raw FP4 bytes (seeded
+    code and scale bytes), which both sides decode.
+    """
+    n = 1 << 20
+    if shape == "c4_4x1m":
+        lens, q_seq, q_pos, cfg = [n] * 4, [0, 1, 2, 3], [n - 1] * 4, 110
+    else:
+        lens, q_seq, q_pos, cfg = [n], [0, 0, 0, 0], [n - 1, 777776, 524290, 262149], 111
+    di, H, P, K = 128, 8, 2048, 512
+    announce("index full oracle pass", shape)
+    rc, rs = synth.fp4_bytes(cfg, 0, sum(lens), di)
+    codes, scales = t(rc), t(rs)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    M = len(q_seq)
+    qi, wi = synth.q_idx(cfg, 0, M, H, di), synth.w_idx(cfg, 0, M, H)
+    gpool, gcnt, gtopk, gsc, _ = _run_full(codes, scales, starts, lens, di, q_seq, q_pos, qi, wi, P, K)
+    qf = synth.bf16_bits_to_f32(qi)
+    for i in range(M):
+        sq = q_seq[i]
+        vis = indexer.visible_count(lens[sq], q_pos[i], 1)
+        assert gcnt[i] == min(P, (vis + 7) // 8)
+        _check_query(rc, rs, starts[sq], vis, qf[i], wi[i], P, K, gpool[i], gcnt[i], gtopk[i], gsc[i])
+
+
 def test_index_all_equal_scores_take_lowest_ids():
     announce("index_full ties")
     lens, di, H, P, K = [3001], 64, 4, 10, 50

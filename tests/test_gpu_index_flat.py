@@ -101,10 +101,11 @@ def test_index_flat_ties_take_lowest_positions():
 def test_index_flat_prefill_chunk_full_size_sampled():
     """A 4,096-query prefill chunk over 65,536 entries at ratio 2 (tokens
     126,976 .. 131,071 of a 131,072-token prompt), 8 heads x 128 dims, Top-512,
-    in one call.  Raw cache bytes come from the seeded byte generator; twelve
-    queries (the first, the last and ten drawn at random) are checked against
-    the oracle's flat Top-K over every visible entry, every query against the
-    structural properties."""
+    in one call.  Raw cache bytes come from the seeded byte generator; 256
+    queries (the first, the last and 254 drawn at random, spanning the chunk's
+    visible counts 63,488 .. 65,536) are checked against the oracle's flat
+    Top-K over every visible entry, every query against the structural
+    properties."""
     announce("index_flat prefill 4096 x 65536")
     cfg, n, di, H, K, ratio, M = 330, 65536, 128, 8, 512, 2, 4096
     rc, rs = synth.fp4_bytes(cfg, 0, n, di)
@@ -121,6 +122,7 @@ def test_index_flat_prefill_chunk_full_size_sampled():
     keys = codec.fp4_decode(rc, rs)
     qf = synth.bf16_bits_to_f32(qi)
     rng = np.random.default_rng(5)
-    sample = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 10, replace=False)]))
+    sample = np.unique(np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), 254, replace=False)]))
+    assert len(sample) == 256
     for i in sample.tolist():
         _check_flat(keys[:vis[i]], qf[i], wi[i], K, gtopk[i], gsc[i])
