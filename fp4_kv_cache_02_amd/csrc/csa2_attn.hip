@@ -175,39 +175,41 @@ CSA2_DEV void qk_tile(const _Float16 *kt, int KT, const half8_t *qa, const half8
 // decode schedule: one fused kernel per layer
 // ===========================================================================
 
-constexpr int kDW = 8;                 // waves per decode workgroup
-constexpr int kDH = 16;                // heads per decode workgroup
-constexpr int kDD = 64;                // output dims per decode workgroup
-constexpr int kDC = 320;               // key slots per chunk (20 tiles of 16)
-constexpr int kDMaxSplit = 4;          // key splits per (query, head block, output slice)
+constexpr int kDW = 8;                   // waves per decode workgroup
+constexpr int kDH = 16;                  // heads per decode workgroup
+constexpr int kDD = 64;                  // output dims per decode workgroup
+constexpr int kDMainT = 4;               // Top-K tiles of 16 slots per wave and chunk
+constexpr int kDTm = kDW * kDMainT;      // Top-K tiles per chunk (512 slots)
+constexpr int kDTw = kDW;                // window tiles per chunk, one per wave (128 rows)
+constexpr int kDSlots = 16 * (kDTm + kDTw);  // key slots per chunk (640)
 
-template <int D, bool QF32>
 struct DecLds {
-  static constexpr int VT = kDD + 8;   // [key][dim] row stride of the V slice (f16)
-  static constexpr int PT = kDC + 8;   // [head][key] row stride of P (f16)
-  static constexpr int QT = D + 8;     // [head][dim] row stride of the staged queries (f16)
-  _Float16 vt[kDC * VT];
+  static constexpr int VT = kDD + 8;       // [key][dim] row stride of the V slice (f16)
+  static constexpr int PT = kDSlots + 8;   // [head][key] row stride of P (f16)
+  _Float16 vt[kDSlots * VT];
   _Float16 p[kDH * PT];
-  _Float16 q[(QF32 ? 2 : 1) * kDH * QT];  // hi parts, then lo parts (fp32 queries)
   float wmax[kDW][kDH];
   float wsum[kDW][kDH];
   float wr[kDW];
   float4_t ored[4][64];
 };
 
-// One pipeline unit of a lane's key data: D/8 bytes = D/32 words, i.e. the
-// lane's whole FP4 quarter of a main row (dims quad*(D/4) .. +D/4, plus its
-// D/64 E4M3 scale bytes) or half of its FP8 quarter of a window row.
+// A lane's share of one key tile for S = Q K^T: the lane (key row, quad)
+// holds dims quad*(D/4) .. +D/4 of its key.  Main rows: D/8 FP4 code bytes
+// plus D/64 E4M3 scale bytes; window rows: D/4 FP8 code bytes.
 template <int D>
-struct KeyUnit {
+struct MainUnit {
   uint32_t w[D / 32];
   uint32_t s[(D / 64 + 3) / 4];
+};
+template <int D>
+struct WinUnit {
+  uint32_t w[D / 16];
 };
 
 // Buffer loads (make_rsrc, kOutOfRange) make every load unconditional: the
 // decode kernel reads empty, padded or invisible keys and heads beyond H at
 // out-of-range offsets, which return zeros.
-
 template <int BYTES>
 CSA2_DEV void buffer_load_words(uint32_t *dst, rsrc_t r, uint32_t off) {
   if constexpr (BYTES >= 16) {
@@ -228,66 +230,49 @@ CSA2_DEV void buffer_load_words(uint32_t *dst, rsrc_t r, uint32_t off) {
   }
 }
 
-// Unit `half` of the lane's key quarter: main tiles read the FP4 codes at
-// `code_off` of `codes` and the scales at `scale_off` of `scales`; window
-// tiles read FP8 codes at `code_off` of `win` (scale_off is out of range).
-template <int D>
-CSA2_DEV void load_key_unit(KeyUnit<D> &u, bool main, rsrc_t codes, rsrc_t win, rsrc_t scales, uint32_t code_off,
-                            uint32_t scale_off) {
-  buffer_load_words<D / 8>(u.w, main ? codes : win, code_off);
-  buffer_load_words<D / 64>(u.s, scales, scale_off);
-}
-
-// S += Q K^T for one unit.  Main unit: steps kk = 0 .. D/32-1; window unit
-// `half`: steps half*D/64 .. +D/64.  The B operand of step kk is dims
-// quad*(D/4) + 8*kk .. +7 of the lane's key.  Called only under
-// wave-uniform conditions: an MFMA reads the operands of every lane whatever
-// the exec mask.
+// S += Q K^T over every k-step of a main tile.  The B operand of step kk is
+// dims quad*(D/4) + 8*kk .. +7 of the lane's key.  Called under wave-uniform
+// conditions only: an MFMA reads the operands of every lane whatever the
+// exec mask.
 template <int D, bool QF32>
-CSA2_DEV void score_unit(const KeyUnit<D> &u, bool main, int half, const half8_t *qa, const half8_t *qb,
-                         float4_t &sa) {
-  if (main) {
-    // the unit's D/64 group scales, two per conversion
-    half2_t sc[(D / 64 + 1) / 2];
+CSA2_DEV void score_main(const MainUnit<D> &u, const half8_t *qa, const half8_t *qb, float4_t &sa) {
+  half2_t sc[(D / 64 + 1) / 2];
 #pragma unroll
-    for (int g = 0; g < (D / 64 + 1) / 2; ++g) sc[g] = e4m3x2_to_f16(u.s[g / 2] >> (16 * (g % 2)));
+  for (int g = 0; g < (D / 64 + 1) / 2; ++g) sc[g] = e4m3x2_to_f16(u.s[g / 2] >> (16 * (g % 2)));
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const half8_t b = fp4x8_dequant_f16(u.w[kk], sc[kk / 4][(kk / 2) % 2]);
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sa, 0, 0, 0);
-      if constexpr (QF32) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sa, 0, 0, 0);
-    }
-  } else {
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const half8_t b = fp4x8_dequant_f16(u.w[kk], sc[kk / 4][(kk / 2) % 2]);
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sa, 0, 0, 0);
+    if constexpr (QF32) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sa, 0, 0, 0);
+  }
+}
+template <int D, bool QF32>
+CSA2_DEV void score_win(const WinUnit<D> &u, const half8_t *qa, const half8_t *qb, float4_t &sa) {
 #pragma unroll
-    for (int k2 = 0; k2 < D / 64; ++k2) {
-      const int kk = half * (D / 64) + k2;
-      const half8_t b = e4m3x8_to_f16(u.w[2 * k2], u.w[2 * k2 + 1]);
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sa, 0, 0, 0);
-      if constexpr (QF32) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sa, 0, 0, 0);
-    }
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const half8_t b = e4m3x8_to_f16(u.w[2 * kk], u.w[2 * kk + 1]);
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sa, 0, 0, 0);
+    if constexpr (QF32) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sa, 0, 0, 0);
   }
 }
 
 // The V slice of one key tile: lane (key n, part p) holds dims d0 + 16p ..
-// +15 of key n (D >= 64: four parts cover the 64-dim slice), loaded apart
-// from the scoring units (a cached re-read of 8 code bytes + 1 scale byte, or
-// 16 FP8 bytes) and stored as f16 into row n of the tile's LDS rows.
+// +15 of key n (four parts cover the 64-dim slice), loaded apart from the
+// scoring units (a cached re-read of 8 code bytes + 1 scale byte, or 16 FP8
+// bytes) and stored as f16 into row n of the tile's LDS rows.
 struct VPiece {
   uint32_t w[4];
 };
-template <int D>
-CSA2_DEV void load_vpiece(VPiece &v, bool main, rsrc_t codes, rsrc_t win, rsrc_t scales, uint32_t code_off,
-                          uint32_t scale_off) {
-  if (main) {
-    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(codes, code_off, 0, 0);
-    v.w[0] = x[0];
-    v.w[1] = x[1];
-    v.w[2] = __builtin_amdgcn_raw_buffer_load_b8(scales, scale_off, 0, 0);
-    v.w[3] = 0u;
-  } else {
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(win, code_off, 0, 0);
-    v.w[0] = x[0]; v.w[1] = x[1]; v.w[2] = x[2]; v.w[3] = x[3];
-  }
+CSA2_DEV void load_vpiece_main(VPiece &v, rsrc_t codes, rsrc_t scales, uint32_t code_off, uint32_t scale_off) {
+  const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(codes, code_off, 0, 0);
+  v.w[0] = x[0];
+  v.w[1] = x[1];
+  v.w[2] = __builtin_amdgcn_raw_buffer_load_b8(scales, scale_off, 0, 0);
+  v.w[3] = 0u;
+}
+CSA2_DEV void load_vpiece_win(VPiece &v, rsrc_t win, uint32_t code_off) {
+  const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(win, code_off, 0, 0);
+  v.w[0] = x[0]; v.w[1] = x[1]; v.w[2] = x[2]; v.w[3] = x[3];
 }
 CSA2_DEV void store_vpiece(const VPiece &v, bool main, _Float16 *dst) {
   half8_t a, b;
@@ -304,14 +289,20 @@ CSA2_DEV void store_vpiece(const VPiece &v, bool main, _Float16 *dst) {
 }
 
 // grid (D / 64 output slices, queries, head blocks of 16), 8 waves.
-// Channels are assigned to MFMA k-steps by quarter: lane quad q feeds dims
-// q*(D/4) + 8*kk .. +7 at step kk, for both the query (A) and the key (B), so
-// a lane streams contiguous bytes of its key straight into registers.  Key
-// tiles go in chunks of 40 (one chunk for Top-512 + 128 window rows): wave w
-// scores tiles w, w+8, ... of the chunk for the workgroup's 16 heads, loading
-// one unit ahead, keeping the logits in registers and storing its tiles'
-// 64-dim V slice into LDS; the chunk's softmax statistics meet in LDS; P (f16)
-// goes to LDS; then wave w multiplies P by V for dims 16*(w%4) .. +15 over
+//
+// A workgroup computes the logits of its 16 heads against every key of the
+// query (replicated across the output slices: spare MFMA time buys a kernel
+// with no partial outputs to merge) and P V for its 64 output dims.  Keys go
+// in chunks of 32 Top-K tiles + 8 window tiles (one chunk for Top-512 + 128
+// window rows): wave w owns Top-K tiles w, w+8, w+16, w+24 and window tile w
+// of the chunk.  Every load of a chunk is issued before any key is scored, so
+// a wave waits for memory once per chunk: the Top-K indices and window
+// scales first, then (while they are in flight) the query operands straight
+// into registers, then all key rows and V pieces.  Channels are assigned to
+// MFMA k-steps by quarter (lane quad q feeds dims q*(D/4) + 8*kk .. +7 for
+// both query and key), so a lane streams contiguous bytes of its key.  The
+// chunk's softmax statistics meet in LDS; P (f16) and the 64-dim V slice
+// pass through LDS; wave w multiplies P by V for dims 16*(w%4) .. +15 over
 // every second 32-key step, the two halves being added at the end.  Chunks
 // combine online.
 template <int D, bool QF32>
@@ -327,28 +318,17 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
                                                           const float *__restrict__ swa_scale,
                                                           const int32_t *__restrict__ swa_start,
                                                           const int32_t *__restrict__ swa_count, int W, float tau2,
-                                                          float *__restrict__ out, float *__restrict__ lse,
-                                                          int nsplit, float *__restrict__ part_o,
-                                                          float *__restrict__ part_lse,
-                                                          uint32_t *__restrict__ counters) {
-  using Lds = DecLds<D, QF32>;
-  __shared__ Lds L;
+                                                          float *__restrict__ out, float *__restrict__ lse) {
+  __shared__ DecLds L;
   constexpr int NK = D / 32;             // MFMA k-steps per key
   constexpr int DD = D < kDD ? D : kDD;  // dims of this workgroup's output slice
-  constexpr int CT = kDC / 16;                 // tiles per chunk
-  constexpr int MAXT = (CT + kDW - 1) / kDW;   // tiles per wave per chunk
+  constexpr int NT = kDMainT + 1;        // tiles per wave per chunk (Top-K tiles, then the window tile)
   const int m = blockIdx.y, hb = blockIdx.z;
-  const int ds = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;  // output slice, key split
-  const int d0 = ds * kDD;
+  const int d0 = blockIdx.x * kDD;
   // the wave index as a scalar: per-tile conditions (and the descriptor choice)
   // are then wave-uniform branches, not exec-masked ones
   const int tid = threadIdx.x, l = lane_id(), wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = l & 15, quad = l >> 4;
-  const int TM = (K + 15) / 16;                     // Top-K tiles
-  const int TT = (TM + (W + 15) / 16 + 1) / 2 * 2;  // all tiles, even
-  // this workgroup's tiles [tb, te): an even share of the key split
-  const int tps = (TT / 2 + nsplit - 1) / nsplit * 2;
-  const int tb = min(TT, sp * tps), te = min(TT, tb + tps);
 
   const int s = q_seq[m];
   const int64_t lim = ((int64_t)q_pos[m] + 1) / ratio;
@@ -357,6 +337,9 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
   // with no window the window arrays may be null (their descriptors are empty)
   const int wcount = (W > 0) ? max(0, min(swa_count[m], W)) : 0;
   const int64_t wstart = (W > 0) ? swa_start[m] : 0;
+  const int TM = (K + 15) / 16;        // Top-K tiles
+  const int TW = (wcount + 15) / 16;   // window tiles of this query
+  const int nchunk = max((TM + kDTm - 1) / kDTm, (TW + kDTw - 1) / kDTw);
   // descriptors: this query's visible rows, window rows, Top-K list and queries
   const rsrc_t r_codes = make_rsrc(kv_codes + row0 * (D / 2), (uint32_t)(vis * (D / 2)));
   const rsrc_t r_scales = make_rsrc(kv_scales + row0 * (D / 16), (uint32_t)(vis * (D / 16)));
@@ -366,90 +349,8 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
   constexpr int QE = QF32 ? 4 : 2;  // query element bytes
   const rsrc_t r_q = make_rsrc(static_cast<const char *>(q_any) + (int64_t)m * H * D * QE, (uint32_t)(H * D * QE));
 
-  // ---- per chunk: sources of this wave's tiles (all index loads in one
-  // batch) and the first unit's loads; the first chunk's go out before the
-  // query staging so their latency overlaps it ----
-  uint32_t coff[MAXT], soff[MAXT], vcoff[MAXT], vsoff[MAXT];
-  float sks[MAXT];
-  KeyUnit<D> cur;
-  VPiece vp;
-  auto prepare_chunk = [&](int ct0) {
-    const int ntiles = min(CT, te - ct0);
-    // ---- sources of this wave's tiles: all index loads of the chunk in one batch ----
-    int32_t jv[MAXT];
-    float rv[MAXT];
-#pragma unroll
-    for (int i = 0; i < MAXT; ++i) {
-      const int t = ct0 + wv + kDW * i;
-      jv[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_topk, (uint32_t)(16 * t + row) * 4u, 0, 0);
-      rv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_wsc, (uint32_t)(16 * (t - TM) + row) * 4u, 0, 0));
-    }
-    // (selects, not branches: a branch would pull each load down to its use)
-#pragma unroll
-    for (int i = 0; i < MAXT; ++i) {
-      const int t = ct0 + wv + kDW * i;
-      const int slot = 16 * t + row;             // Top-K slot (main tiles)
-      const int wi = 16 * (t - TM) + row;        // window row (window tiles)
-      const int32_t j = jv[i];
-      const bool is_main = t < TM;
-      const bool okm = slot < K && j >= 0 && j < vis;
-      const uint32_t cm = okm ? (uint32_t)j * (D / 2) + quad * (D / 8) : kOutOfRange;
-      const uint32_t cw = (uint32_t)wi * D + quad * (D / 4);  // past the window rows: out of range
-      coff[i] = is_main ? cm : cw;
-      soff[i] = (is_main && okm) ? (uint32_t)j * (D / 16) + quad * (D / 64) : kOutOfRange;
-      // V slice piece of lane (key row, part quad): dims d0 + 16*quad .. +15
-      const int vd = d0 + 16 * quad;
-      vcoff[i] = is_main ? (okm ? (uint32_t)j * (D / 2) + vd / 2 : kOutOfRange) : (uint32_t)wi * D + vd;
-      vsoff[i] = (is_main && okm) ? (uint32_t)j * (D / 16) + vd / 16 : kOutOfRange;
-      sks[i] = is_main ? (okm ? 1.0f : 0.0f) : ((wi < wcount) ? rv[i] : 0.0f);
-    }
-    if (wv < ntiles) {
-      load_key_unit<D>(cur, ct0 + wv < TM, r_codes, r_win, r_scales, coff[0], soff[0]);
-      load_vpiece<D>(vp, ct0 + wv < TM, r_codes, r_win, r_scales, vcoff[0], vsoff[0]);
-    }
-  };
-  if (tb < te) prepare_chunk(tb);
-
-  // ---- queries: staged once per workgroup as f16 [head][dim] in LDS (fp32:
-  // hi and lo parts), then each wave keeps its MFMA A operands in registers:
-  // lane (head row, quad) holds dims quad*(D/4) + 8*kk .. +7 ----
-  {
-    constexpr int PIECES = kDH * D / 8;  // 8 dims per piece
-    for (int pc = tid; pc < PIECES; pc += 64 * kDW) {
-      const int h = pc / (D / 8), d = 8 * (pc % (D / 8));
-      const uint32_t off = (uint32_t)(((hb * kDH + h) * D + d) * QE);
-      half8_t hi, lo;
-      if constexpr (QF32) {
-        uint32_t x[8];
-        buffer_load_words<32>(x, r_q, off);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float v = __uint_as_float(x[i]);
-          hi[i] = (_Float16)v;
-          lo[i] = (_Float16)(v - (float)hi[i]);
-        }
-        *reinterpret_cast<half8_t *>(&L.q[kDH * Lds::QT + h * Lds::QT + d]) = lo;
-      } else {
-        uint32_t x[4];
-        buffer_load_words<16>(x, r_q, off);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hi[2 * i] = (_Float16)__uint_as_float(x[i] << 16);
-          hi[2 * i + 1] = (_Float16)__uint_as_float(x[i] & 0xFFFF0000u);
-        }
-      }
-      *reinterpret_cast<half8_t *>(&L.q[h * Lds::QT + d]) = hi;
-    }
-  }
-  __syncthreads();
   half8_t qa[NK];
   half8_t qb[QF32 ? NK : 1];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    qa[kk] = *reinterpret_cast<const half8_t *>(&L.q[row * Lds::QT + quad * (D / 4) + 8 * kk]);
-    if constexpr (QF32) qb[kk] = *reinterpret_cast<const half8_t *>(&L.q[(kDH + row) * Lds::QT + quad * (D / 4) + 8 * kk]);
-  }
-
   float m_run[4], l_part[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) { m_run[j] = -INFINITY; l_part[j] = 0.0f; }
@@ -457,47 +358,100 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
   int e_cur = 0;                          // accumulator exponent: true O = acc * 2^-e_cur
   const int dt = wv & 3, khalf = wv >> 2;  // P V: dims 16*dt .., k-steps khalf, khalf + 2, ...
 
-  for (int ct0 = tb; ct0 < te; ct0 += CT) {
-    const int ntiles = min(CT, te - ct0);  // even
-    const int nc = 16 * ntiles;
-    if (ct0 > tb) {
-      __syncthreads();                     // previous chunk's LDS reads are done
-      prepare_chunk(ct0);
+  for (int c = 0; c < nchunk; ++c) {
+    const int nmc = max(0, min(kDTm, TM - kDTm * c));   // Top-K tiles of the chunk
+    const int nwc = max(0, min(kDTw, TW - kDTw * c));   // window tiles of the chunk
+    const int nme = (nmc + 1) & ~1, nwe = (nwc + 1) & ~1;  // rounded to whole 32-key steps
+    if (c > 0) __syncthreads();           // the previous chunk's LDS reads are done
+    // ---- sources of this wave's tiles: the index and window-scale loads go
+    // first, the first chunk's query operands behind them ----
+    int32_t jv[kDMainT];
+#pragma unroll
+    for (int i = 0; i < kDMainT; ++i) {
+      const int slot = 16 * (kDTm * c + wv + kDW * i) + row;
+      jv[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_topk, (uint32_t)slot * 4u, 0, 0);
     }
-    // ---- S for this wave's tiles, one unit ahead in flight; V slice into LDS ----
-    float4_t sacc[MAXT];
+    const int wi = 16 * (kDTw * c + wv) + row;   // window row of this lane (window tile)
+    const float rv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_wsc, (uint32_t)wi * 4u, 0, 0));
+    uint32_t qraw[QF32 ? D / 8 : D / 16];
+    if (c == 0) {
+      // lane (head row, quad): dims quad*(D/4) .. +D/4 of head hb*16 + row
+      const uint32_t qoff = (uint32_t)(((hb * kDH + row) * D + quad * (D / 4)) * QE);
+      buffer_load_words<(D / 4) * QE>(qraw, r_q, qoff);
+    }
+    // offsets (selects, not branches: a branch would pull each load down to its use)
+    uint32_t coff[kDMainT], soff[kDMainT], vcoff[kDMainT], vsoff[kDMainT];
+    float sks[NT];
+    const int vd = d0 + 16 * quad;  // V piece of lane (key row, part quad): dims vd .. vd+15
 #pragma unroll
-    for (int i = 0; i < MAXT; ++i) sacc[i] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < kDMainT; ++i) {
+      const int slot = 16 * (kDTm * c + wv + kDW * i) + row;
+      const int32_t j = jv[i];
+      const bool ok = slot < K && j >= 0 && j < vis;
+      coff[i] = ok ? (uint32_t)j * (D / 2) + quad * (D / 8) : kOutOfRange;
+      soff[i] = ok ? (uint32_t)j * (D / 16) + quad * (D / 64) : kOutOfRange;
+      vcoff[i] = ok ? (uint32_t)j * (D / 2) + vd / 2 : kOutOfRange;
+      vsoff[i] = ok ? (uint32_t)j * (D / 16) + vd / 16 : kOutOfRange;
+      sks[i] = ok ? 1.0f : 0.0f;
+    }
+    sks[kDMainT] = (wi < wcount) ? rv : 0.0f;
+    // ---- every key load of the chunk (rows past the window read as zeros) ----
+    MainUnit<D> mu[kDMainT];
+    VPiece vp[NT];
 #pragma unroll
-    for (int k = 0; k < 2 * MAXT; ++k) {
-      const int i = k >> 1, h = k & 1;
-      const int tl = wv + kDW * i;             // tile within the chunk
-      if (tl >= ntiles) break;
-      const bool main = ct0 + tl < TM;
-      if (main && h == 1) continue;            // a main tile is a single unit
-      const int ni = (!main && h == 0) ? i : i + 1;
-      const int nh = (!main && h == 0) ? 1 : 0;
-      const int ntl = wv + kDW * ni;
-      const bool more = ni < MAXT && ntl < ntiles;
-      const bool more_v = more && nh == 0;     // the next unit starts a new tile
-      KeyUnit<D> nxt;
-      VPiece nvp;
-      if (more) {
-        const int nn = ni < MAXT ? ni : 0;
-        load_key_unit<D>(nxt, ct0 + ntl < TM, r_codes, r_win, r_scales, coff[nn] + nh * (D / 8), soff[nn]);
-        if (more_v) load_vpiece<D>(nvp, ct0 + ntl < TM, r_codes, r_win, r_scales, vcoff[nn], vsoff[nn]);
+    for (int i = 0; i < kDMainT; ++i) {
+      if (wv + kDW * i < nme) {
+        buffer_load_words<D / 8>(mu[i].w, r_codes, coff[i]);
+        buffer_load_words<D / 64>(mu[i].s, r_scales, soff[i]);
+        load_vpiece_main(vp[i], r_codes, r_scales, vcoff[i], vsoff[i]);
       }
-      score_unit<D, QF32>(cur, main, h, qa, qb, sacc[i]);
-      if (main || h == 1) store_vpiece(vp, main, &L.vt[(16 * tl + row) * Lds::VT + 16 * quad]);
-      if (more) cur = nxt;
-      if (more_v) vp = nvp;
     }
+    WinUnit<D> wu;
+    if (wv < nwe) {
+      buffer_load_words<D / 4>(wu.w, r_win, (uint32_t)wi * D + quad * (D / 4));
+      load_vpiece_win(vp[kDMainT], r_win, (uint32_t)wi * D + vd);
+    }
+    if (c == 0) {
+      // queries as f16 MFMA A operands (bf16 converts exactly in the f16 range;
+      // fp32 splits into hi + lo parts)
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        if constexpr (QF32) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float v = __uint_as_float(qraw[8 * kk + i]);
+            const _Float16 hi = (_Float16)v;
+            qa[kk][i] = hi;
+            qb[kk][i] = (_Float16)(v - (float)hi);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t x = qraw[4 * kk + i];
+            qa[kk][2 * i] = (_Float16)__uint_as_float(x << 16);
+            qa[kk][2 * i + 1] = (_Float16)__uint_as_float(x & 0xFFFF0000u);
+          }
+        }
+      }
+    }
+    // ---- S for this wave's tiles; V slices into LDS ----
+    float4_t sacc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) sacc[i] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < kDMainT; ++i) {
+      const int lt = wv + kDW * i;
+      if (lt < nmc) score_main<D, QF32>(mu[i], qa, qb, sacc[i]);
+      if (lt < nme) store_vpiece(vp[i], true, &L.vt[(16 * lt + row) * DecLds::VT + 16 * quad]);
+    }
+    if (wv < nwc) score_win<D, QF32>(wu, qa, qb, sacc[kDMainT]);
+    if (wv < nwe) store_vpiece(vp[kDMainT], false, &L.vt[(16 * (kDTm + wv) + row) * DecLds::VT + 16 * quad]);
     // ---- chunk statistics: lane holds key (16*tile + row) of heads 4*quad + j ----
-    float zz[MAXT][4];
+    float zz[NT][4];
     float rm = 0.0f;
 #pragma unroll
-    for (int i = 0; i < MAXT; ++i) {
-      const bool live = wv + kDW * i < ntiles;
+    for (int i = 0; i < NT; ++i) {
+      const bool live = (i < kDMainT) ? (wv + kDW * i < nmc) : (wv < nwc);
       const float ks = live ? sks[i] : 0.0f;
       rm = fmaxf(rm, ks);
 #pragma unroll
@@ -509,7 +463,7 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
     for (int j = 0; j < 4; ++j) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < MAXT; ++i) mx = fmaxf(mx, zz[i][j]);
+      for (int i = 0; i < NT; ++i) mx = fmaxf(mx, zz[i][j]);
       mx = max16_lanes(mx);
       if (row == 0) L.wmax[wv][4 * quad + j] = mx;
     }
@@ -536,33 +490,38 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
 #pragma unroll
     for (int j = 0; j < 4; ++j) l_part[j] *= alpha[j];
 #pragma unroll
-    for (int i = 0; i < MAXT; ++i) {
-      const int tl = wv + kDW * i;
-      if (tl >= ntiles) continue;
+    for (int i = 0; i < NT; ++i) {
+      const int lt = (i < kDMainT) ? wv + kDW * i : kDTm + wv;
+      const bool stored = (i < kDMainT) ? (wv + kDW * i < nme) : (wv < nwe);
+      if (!stored) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float pr = (zz[i][j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(zz[i][j] - mnew[j]);
         l_part[j] += pr;
-        L.p[(4 * quad + j) * Lds::PT + 16 * tl + row] = (_Float16)ldexpf(pr * sks[i], e_new);
+        L.p[(4 * quad + j) * DecLds::PT + 16 * lt + row] = (_Float16)ldexpf(pr * sks[i], e_new);
       }
     }
-    if (ct0 > tb) {
+    if (c > 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[j] *= ldexpf(alpha[j], e_new - e_cur);
     }
     e_cur = e_new;
     __syncthreads();
-    // ---- acc += P V for dims 16*dt .. over k-steps khalf, khalf + 2, ... ----
+    // ---- acc += P V for dims 16*dt .. over this wave's half of the 32-key
+    // steps: the chunk's Top-K steps, then its window steps ----
     if (16 * dt < DD) {
-      for (int k0 = 32 * khalf; k0 < nc; k0 += 64) {
-        const half8_t a = *reinterpret_cast<const half8_t *>(&L.p[row * Lds::PT + k0 + 8 * quad]);
-        const half8_t b = v_operand_tr(L.vt, Lds::VT, k0, 16 * dt, row, quad);
+      const int nsm = nme / 2, nst = nsm + nwe / 2;
+      for (int st = khalf; st < nst; st += 2) {
+        const int k0 = (st < nsm) ? 32 * st : 16 * kDTm + 32 * (st - nsm);
+        const half8_t a = *reinterpret_cast<const half8_t *>(&L.p[row * DecLds::PT + k0 + 8 * quad]);
+        const half8_t b = v_operand_tr(L.vt, DecLds::VT, k0, 16 * dt, row, quad);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
       }
     }
   }
 
-  // ---- softmax denominators: lane partials -> rows -> waves ----
+  // ---- softmax denominators: lane partials -> rows -> waves; the two
+  // k-step halves of each dim tile meet in LDS ----
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float v = sum16_lanes(l_part[j]);
@@ -570,82 +529,18 @@ __global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict
   }
   if (khalf == 1) L.ored[dt][l] = acc;
   __syncthreads();
-  if (nsplit == 1) {
-    if (khalf == 1 || 16 * dt >= DD) return;
-    acc += L.ored[dt][l];
+  if (khalf == 1 || 16 * dt >= DD) return;
+  acc += L.ored[dt][l];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int hh = 4 * quad + j, h = hb * kDH + hh;
-      float lt = 0.0f;
+  for (int j = 0; j < 4; ++j) {
+    const int hh = 4 * quad + j, h = hb * kDH + hh;
+    float lt = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kDW; ++w) lt += L.wsum[w][hh];
-      if (h >= H) continue;
-      out[((int64_t)m * H + h) * D + d0 + 16 * dt + row] = (lt > 0.0f) ? ldexpf(acc[j] / lt, -e_cur) : 0.0f;
-      if (ds == 0 && dt == 0 && row == 0 && lse)
-        lse[(int64_t)m * H + h] = (lt > 0.0f) ? (m_run[j] + log2f(lt)) * 0.6931471805599453f : -INFINITY;
-    }
-    return;
-  }
-  // ---- key split: write this split's normalised partial and its log2-domain
-  // lse; the last split of the (query, head block, slice) to arrive merges.
-  // The partials go through device-coherent stores and loads (they bypass the
-  // per-XCD L2s), so no cache-wide fence is needed: the stores are complete
-  // (s_waitcnt) before the arrival is counted, and the merging workgroup loads
-  // them only after it has seen the count. ----
-  const int64_t grp = ((int64_t)m * gridDim.z + hb) * (gridDim.x / nsplit) + ds;
-  float *po = part_o + (grp * nsplit + sp) * (kDH * kDD);
-  float *pl = part_lse + (grp * nsplit + sp) * kDH;
-  if (khalf == 0 && 16 * dt < DD) {
-    acc += L.ored[dt][l];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int hh = 4 * quad + j;
-      float lt = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kDW; ++w) lt += L.wsum[w][hh];
-      const float o = (lt > 0.0f) ? ldexpf(acc[j] / lt, -e_cur) : 0.0f;
-      __hip_atomic_store(&po[hh * kDD + 16 * dt + row], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (dt == 0 && row == 0)
-        __hip_atomic_store(&pl[hh], (lt > 0.0f) ? m_run[j] + log2f(lt) : -INFINITY, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // every store of this workgroup has completed
-  __syncthreads();
-  __shared__ uint32_t s_prev;
-  if (tid == 0) s_prev = atomicInc(&counters[grp], (uint32_t)nsplit - 1u);  // wraps back to 0
-  __syncthreads();
-  if (s_prev != (uint32_t)nsplit - 1u) return;
-  const float *pg = part_o + grp * nsplit * (kDH * kDD);
-  const float *lg = part_lse + grp * nsplit * kDH;
-  for (int idx = tid; idx < kDH * DD; idx += 64 * kDW) {
-    const int hh = idx / DD, dd = idx % DD, h = hb * kDH + hh;
+    for (int w = 0; w < kDW; ++w) lt += L.wsum[w][hh];
     if (h >= H) continue;
-    float ls[kDMaxSplit], os[kDMaxSplit];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int s2 = 0; s2 < kDMaxSplit; ++s2) {
-      ls[s2] = -INFINITY;
-      os[s2] = 0.0f;
-      if (s2 < nsplit) {
-        ls[s2] = __hip_atomic_load(&lg[s2 * kDH + hh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        os[s2] = __hip_atomic_load(&pg[(s2 * kDH + hh) * kDD + dd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-#pragma unroll
-    for (int s2 = 0; s2 < kDMaxSplit; ++s2) mx = fmaxf(mx, ls[s2]);
-    float wsum = 0.0f, o = 0.0f;
-    if (mx > -INFINITY) {
-#pragma unroll
-      for (int s2 = 0; s2 < kDMaxSplit; ++s2) {
-        const float wgt = (ls[s2] == -INFINITY) ? 0.0f : exp2f(ls[s2] - mx);
-        wsum += wgt;
-        o = fmaf(wgt, os[s2], o);
-      }
-    }
-    out[((int64_t)m * H + h) * D + d0 + dd] = (wsum > 0.0f) ? o / wsum : 0.0f;
-    if (ds == 0 && dd == 0 && lse)
-      lse[(int64_t)m * H + h] = (wsum > 0.0f) ? (mx + log2f(wsum)) * 0.6931471805599453f : -INFINITY;
+    out[((int64_t)m * H + h) * D + d0 + 16 * dt + row] = (lt > 0.0f) ? ldexpf(acc[j] / lt, -e_cur) : 0.0f;
+    if (blockIdx.x == 0 && dt == 0 && row == 0 && lse)
+      lse[(int64_t)m * H + h] = (lt > 0.0f) ? (m_run[j] + log2f(lt)) * 0.6931471805599453f : -INFINITY;
   }
 }
 
@@ -815,41 +710,11 @@ static bool use_decode_kernel(int m, int heads, int dim, int64_t max_len) {
   return (int64_t)m * ((heads + kHB - 1) / kHB) < 256;
 }
 
-// Key splits of the decode kernel: about one workgroup per CU (one 8-wave
-// workgroup fits a CU at this register use; a second round of workgroups
-// costs more than it saves), at least two tiles per split.
-static int decode_splits(int m, int heads, int dim, int top_k, int window) {
-  const int64_t base = (int64_t)m * ((heads + kDH - 1) / kDH) * ((dim + kDD - 1) / kDD);
-  const int tiles = ((top_k + 15) / 16 + (window + 15) / 16 + 1) / 2 * 2;
-  int64_t ns = 256 / (base > 0 ? base : 1);
-  if (ns > kDMaxSplit) ns = kDMaxSplit;
-  if (ns < 1) ns = 1;
-  while (ns > 1 && tiles / ns < 2) --ns;
-  return (int)ns;
-}
-
-// Decode-schedule workspace with key splits: arrival counters (zero before
-// the first call, left zero by every call), partial outputs, partial lse.
-struct AttnWs {
-  size_t counters, part_o, part_lse, total;
-};
-static AttnWs attn_ws_layout(int m, int heads, int dim, int nsplit) {
-  const size_t groups = (size_t)m * ((heads + kDH - 1) / kDH) * ((dim + kDD - 1) / kDD);
-  AttnWs w{};
-  size_t off = 0;
-  w.counters = off; off = align256(off + sizeof(uint32_t) * groups);
-  w.part_o = off;   off = align256(off + sizeof(float) * groups * nsplit * kDH * kDD);
-  w.part_lse = off; off = align256(off + sizeof(float) * groups * nsplit * kDH);
-  w.total = off;
-  return w;
-}
-
-// Sized for the decode kernel whenever the query count may select it (a
-// cache too long for it falls back to the flash kernel, which needs none).
+// Neither schedule needs a workspace: the decode kernel keeps every key of a
+// (query, head block) in one workgroup, so there are no partial outputs.
 size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int window) {
-  if (!use_decode_kernel(m, heads, dim, 0)) return 256;
-  const int ns = decode_splits(m, heads, dim, top_k, window);
-  return ns > 1 ? attn_ws_layout(m, heads, dim, ns).total : 256;
+  (void)m; (void)heads; (void)dim; (void)top_k; (void)window;
+  return 256;
 }
 
 template <int D, bool QF32>
@@ -859,20 +724,10 @@ static int attn_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, const voi
   const int W = swa.window;
   const float tau2 = scale * 1.4426950408889634f;  // log2-domain softmax: p = 2^(z - max)
   if (use_decode_kernel(qs.m, heads, D, kv.max_len)) {
-    const int ns = decode_splits(qs.m, heads, D, K, W);
-    float *po = nullptr, *pl = nullptr;
-    uint32_t *ctr = nullptr;
-    if (ns > 1) {
-      const AttnWs L = attn_ws_layout(qs.m, heads, D, ns);
-      char *base = static_cast<char *>(ws);
-      ctr = reinterpret_cast<uint32_t *>(base + L.counters);
-      po = reinterpret_cast<float *>(base + L.part_o);
-      pl = reinterpret_cast<float *>(base + L.part_lse);
-    }
-    const dim3 grid(((D + kDD - 1) / kDD) * ns, qs.m, (heads + kDH - 1) / kDH);
+    const dim3 grid((D + kDD - 1) / kDD, qs.m, (heads + kDH - 1) / kDH);
     CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_decode<D, QF32>), grid, dim3(64 * kDW), stream, q, heads, kv.codes,
                       kv.scales, kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, swa.codes, swa.scale,
-                      swa.start, swa.count, W, tau2, out, lse, ns, po, pl, ctr);
+                      swa.start, swa.count, W, tau2, out, lse);
   } else if (attn_prefill_supported(kv, QF32 ? CSA2_F32 : CSA2_BF16, K)) {
     return launch_attn_prefill(kv, qs, q, heads, topk, K, swa, scale, out, lse, stream);
   } else {
