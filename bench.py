@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
-"""Benchmark of the CSA2 decode hot path on one MI355X.
+"""Benchmark of the CSA2 hot path on one MI355X.
 
-Workload (default): 4 sequences x 1,048,576 visible entries, one decode token
+Headline (default): 4 sequences x 1,048,576 visible entries, one decode token
 per sequence through the 20-layer decoder (group 1 = Full + 3 Reuse, groups
 2-5 = Reindex + 3 Reuse), 512-channel FP4 latent, 64 bf16 query heads,
 indexer 8 x 128, pool 2,048 blocks, Top-512, FP8 window 128.  A step is one
@@ -10,10 +10,15 @@ its indexer key, the Full layer's first scan + pool + Top-K, four Reindex
 selections and twenty attention layers.  Inputs are seeded synthetic tensors
 already resident in HBM when timing starts.
 
---workload 2 times the encoder prefill chunk instead: 4,096 query tokens
-(tokens 126,976 .. 131,072 of a 131,072-token prompt, ratio 2, 65,536
-compressed entries) through the 18 encoder layers (3 groups of Full + 5
-Reuse, flat Top-512), each Full group re-writing the chunk's 2,048 entries.
+The same JSON line carries, under "workloads", the other configurations:
+the 4 x 1M decode timed eagerly and cold (a 1 GiB scratch write before each
+step evicts the caches), the 64K decoder (graph and eager), the ragged batch
+of 32 sequences (32K..256K entries) and the encoder prefill chunk (4,096
+query tokens of a 131,072-token prompt at ratio 2 through 18 layers, each
+Full group writing its 2,048 new entries into its own caches).  Each carries
+its step time, query-tokens/s, the roofline fraction of its dominant kernel
+and the oracle's CPU baseline.  --no-extras times the headline only;
+--workload 2 makes the prefill chunk the headline.
 
 Prints one JSON line (see the `result` dict below).
 """
@@ -43,10 +48,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4,
-                    help="workload index (4 = 4 x 1M decode; 2 = encoder prefill chunk)")
+                    help="headline workload index (4 = 4 x 1M decode; 2 = encoder prefill chunk)")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="graph: the timed steps replay one captured HIP graph; eager: launched one by one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="time the headline workload only")
+    ap.add_argument("--cold-reps", type=int, default=10, help="steps of the cold-cache variant")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, copy a buffer of this size once (counter calibration under --pmc)")
     return ap.parse_args()
@@ -186,8 +193,10 @@ class DecodeWorkload:
 
 
 class PrefillWorkload:
-    """Encoder prefill chunk: every Full group writes the chunk's entries,
-    selects flat Top-K lists for all its queries and runs its layers."""
+    """Encoder prefill chunk: each Full group has its own main-KV and indexer
+    caches (a Full layer computes its own main KV), writes the chunk's new
+    entries into them, selects flat Top-K lists for all its queries and runs
+    its layers."""
 
     def __init__(self, wl, torch, csa2, synth):
         self.wl, self.torch, self.csa2 = wl, torch, csa2
@@ -195,23 +204,24 @@ class PrefillWorkload:
         E, D, DI, ratio = int(wl.seq_lens[0]), wl.dim, wl.idx_dim, wl.ratio
         M, t0 = wl.n_queries, wl.first_query_token
         R = M // ratio                                    # entries completed by the chunk's tokens
+        self.R = R
         u8 = dict(dtype=torch.uint8, device=dev)
-        self.kv_codes = torch.empty((E, D // 2), **u8)
-        self.kv_scales = torch.empty((E, D // 16), **u8)
-        self.ik_codes = torch.empty((E, DI // 2), **u8)
-        self.ik_scales = torch.empty((E, DI // 16), **u8)
         w_ik = torch.from_numpy(synth.w_ik(wl.cfg, D, DI)).to(dev)
-        x = torch.from_numpy(synth.main_kv_rows(wl.cfg, 0, 0, E, D)).to(dev)
-        csa2.csa2_quantize_fp4(x, self.kv_codes, self.kv_scales, w_ik=w_ik, ik_codes=self.ik_codes,
-                               ik_scales=self.ik_scales)
-        self.new_kv = x[E - R:].clone()
-        del x
-        self.new_dst = torch.arange(E - R, E, dtype=torch.int64, device=dev)
         self.w_ik = w_ik
+        self.new_dst = torch.arange(E - R, E, dtype=torch.int64, device=dev)
         seq_start = torch.zeros(1, dtype=torch.int64, device=dev)
         seq_len = torch.tensor([E], dtype=torch.int32, device=dev)
-        self.kv = csa2.fp4_cache(self.kv_codes, self.kv_scales, seq_start, seq_len, D, E, ratio)
-        self.idx = csa2.fp4_cache(self.ik_codes, self.ik_scales, seq_start, seq_len, DI, E, ratio)
+        self.caches = []                                  # per Full group: (kv, idx, new rows, tensors)
+        for gi in range(len(wl.groups)):
+            kc, ks = torch.empty((E, D // 2), **u8), torch.empty((E, D // 16), **u8)
+            ic, is_ = torch.empty((E, DI // 2), **u8), torch.empty((E, DI // 16), **u8)
+            x = torch.from_numpy(synth.main_kv_rows(wl.cfg, gi, 0, E, D)).to(dev)
+            csa2.csa2_quantize_fp4(x, kc, ks, w_ik=w_ik, ik_codes=ic, ik_scales=is_)
+            new_kv = x[E - R:].clone()
+            del x
+            kv = csa2.fp4_cache(kc, ks, seq_start, seq_len, D, E, ratio)
+            idx = csa2.fp4_cache(ic, is_, seq_start, seq_len, DI, E, ratio)
+            self.caches.append((kv, idx, new_kv, (kc, ks, ic, is_)))
         self.M = M
         self.q_pos_host = np.arange(t0, t0 + M, dtype=np.int64)
         self.qs = csa2.queries(torch.zeros(M, dtype=torch.int32, device=dev),
@@ -224,6 +234,7 @@ class PrefillWorkload:
         for layer in range(L):
             qb = synth.q_main(wl.cfg, layer, M, H, D, "bf16")
             self.q.append(torch.from_numpy(qb.view(np.int16)).to(dev).view(torch.bfloat16))
+            del qb
             sc = torch.empty((nsw, D), **u8)
             ss = torch.empty((nsw,), dtype=torch.float32, device=dev)
             csa2.csa2_quantize_fp8_rows(torch.from_numpy(synth.swa_rows(wl.cfg, layer, 0, nsw, D)).to(dev), sc, ss)
@@ -232,17 +243,18 @@ class PrefillWorkload:
             self.lse.append(torch.empty((M, H), dtype=torch.float32, device=dev))
         self.groups = []
         layer = 0
-        for modes in wl.groups:
+        for gi, modes in enumerate(wl.groups):
             n = len(modes)
+            kv, idx, new_kv, _ = self.caches[gi]
             qi = synth.q_idx(wl.cfg, layer, M, wl.idx_heads, DI)
             wi = synth.w_idx(wl.cfg, layer, M, wl.idx_heads)
             topk = torch.empty((M, K), dtype=torch.int32, device=dev)
-            g = csa2.Group(csa2.CSA2_MODE_FULL, self.kv, self.idx, self.qs,
+            g = csa2.Group(csa2.CSA2_MODE_FULL, kv, idx, self.qs,
                            torch.from_numpy(qi.view(np.int16)).to(dev).view(torch.bfloat16),
                            torch.from_numpy(wi).to(dev), 0, K, None, None, topk, None,
                            self.q[layer:layer + n], csa2.CSA2_BF16, H, self.swa[layer:layer + n],
                            self.out[layer:layer + n], self.lse[layer:layer + n], D ** -0.5,
-                           new_kv=self.new_kv, new_dst_row=self.new_dst, w_ik=self.w_ik)
+                           new_kv=new_kv, new_dst_row=self.new_dst, w_ik=self.w_ik)
             g.topk_tensor = topk
             self.groups.append(g)
             layer += n
@@ -272,72 +284,92 @@ class PrefillWorkload:
         wl = self.wl
         return 4.0 * self.M * wl.heads * wl.dim * (wl.top_k + wl.window)
 
+    def write_bytes_per_launch(self) -> int:
+        # fp32 input rows, their FP4 rows and derived FP4 indexer keys, the destination rows, W_ik once
+        wl = self.wl
+        D, DI = wl.dim, wl.idx_dim
+        return self.R * (4 * D + D // 2 + D // 16 + DI // 2 + DI // 16 + 8) + 4 * D * DI
+
 
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wl, synth) -> dict:
-    from oracle import attention, codec, indexer
+def _blas_cores() -> int:
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count() or 1
-    ns = 65536                                   # prefix of sequence 0 used by the sample
-    D, DI = wl.dim, wl.idx_dim
-    x = synth.main_kv_rows(wl.cfg, 0, 0, ns, D)
-    kc, ks = codec.fp4_encode(x)
-    ikc, iks = codec.indexer_key(kc, ks, synth.w_ik(wl.cfg, D, DI))
-    del x
-    W, H = wl.window, wl.heads
-    q_layers = [synth.bf16_bits_to_f32(synth.q_main(wl.cfg, l, 1, H, D, "bf16"))[0] for l in range(wl.n_layers)]
-    swa = [codec.fp8_rows_encode(synth.swa_rows(wl.cfg, l, 0, W, D)) for l in range(wl.n_layers)]
-    tau = D ** -0.5
+        return os.cpu_count() or 1
 
-    def one_token():
-        t0 = time.perf_counter()
-        keys = codec.fp4_decode(ikc, iks)
-        layer = 0
-        pool = None
-        t_scan = 0.0
-        for modes in wl.groups:
-            qi = synth.bf16_bits_to_f32(synth.q_idx(wl.cfg, layer, 1, wl.idx_heads, DI))[0]
-            wi = synth.w_idx(wl.cfg, layer, 1, wl.idx_heads)[0]
-            if modes[0] == "full":
-                ts = time.perf_counter()
-                s = indexer.scores(qi, wi, keys)
-                t_scan += time.perf_counter() - ts
-                pool = indexer.pool_select(indexer.block_max(s), wl.pool_blocks)
-                cand = indexer.pool_positions(pool, ns)
-                sel = indexer.top_ids(s[cand], cand, min(wl.top_k, len(cand)))
-            else:
-                sel, _ = indexer.reindex(qi, wi, keys, pool, wl.top_k)
-            for _ in modes:
-                attention.sparse_swa_attention(q_layers[layer], kc, ks, sel, ns, swa[layer][0], swa[layer][1], tau)
-                layer += 1
-        return time.perf_counter() - t0, t_scan
 
-    one_token()
-    runs = [one_token() for _ in range(3)]
-    t_tok, t_scan = sorted(runs)[1]
-    # the first scan (decode of all visible keys + their scores) grows linearly with
-    # the context; everything else is bounded by the pool, the Top-K and the window
-    n_full = max(wl.seq_lens)
-    t_full_ctx = t_tok + t_scan * (n_full / ns - 1.0)
-    return {"value": 1.0 / t_full_ctx, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"NumPy fp64 oracle, one decode token of sequence 0 through all {wl.n_layers} layers "
-                       f"over its first {ns} entries (median of 3: {t_tok * 1e3:.0f} ms, first scan "
-                       f"{t_scan * 1e3:.0f} ms); the first scan scaled linearly to {n_full} entries")}
+class CpuDecodeModel:
+    """The oracle's cost of one decode token through the 20-layer decoder,
+    measured on the first 65,536 entries of a sequence and split into the part
+    that grows with the visible context (FP4 decode of every indexer key, its
+    scores, the block maxima and the pool ranking) and the part bounded by the
+    pool, the Top-K and the window (re-scoring, Top-K, attention)."""
+
+    NS = 65536
+
+    def __init__(self, wl, synth):
+        from oracle import attention, codec, indexer
+        ns, D, DI = self.NS, wl.dim, wl.idx_dim
+        x = synth.main_kv_rows(wl.cfg, 0, 0, ns, D)
+        kc, ks = codec.fp4_encode(x)
+        ikc, iks = codec.indexer_key(kc, ks, synth.w_ik(wl.cfg, D, DI))
+        del x
+        W, H = wl.window, wl.heads
+        q_layers = [synth.bf16_bits_to_f32(synth.q_main(wl.cfg, l, 1, H, D, "bf16"))[0]
+                    for l in range(wl.n_layers)]
+        swa = [codec.fp8_rows_encode(synth.swa_rows(wl.cfg, l, 0, W, D)) for l in range(wl.n_layers)]
+        tau = D ** -0.5
+
+        def one_token():
+            t0 = time.perf_counter()
+            t_ctx = 0.0
+            layer = 0
+            pool = keys = None
+            for modes in wl.groups:
+                qi = synth.bf16_bits_to_f32(synth.q_idx(wl.cfg, layer, 1, wl.idx_heads, DI))[0]
+                wi = synth.w_idx(wl.cfg, layer, 1, wl.idx_heads)[0]
+                if modes[0] == "full":
+                    ts = time.perf_counter()
+                    keys = codec.fp4_decode(ikc, iks)
+                    s = indexer.scores(qi, wi, keys)
+                    pool = indexer.pool_select(indexer.block_max(s), wl.pool_blocks)
+                    t_ctx += time.perf_counter() - ts
+                    cand = indexer.pool_positions(pool, ns)
+                    sel = indexer.top_ids(s[cand], cand, min(wl.top_k, len(cand)))
+                else:
+                    sel, _ = indexer.reindex(qi, wi, keys, pool, wl.top_k)
+                for _ in modes:
+                    attention.sparse_swa_attention(q_layers[layer], kc, ks, sel, ns, swa[layer][0], swa[layer][1],
+                                                   tau)
+                    layer += 1
+            return time.perf_counter() - t0, t_ctx
+
+        one_token()
+        runs = sorted(one_token() for _ in range(3))
+        self.t_tok, self.t_ctx = runs[1]
+        self.t_fixed = self.t_tok - self.t_ctx
+        self.per_entry = self.t_ctx / ns
+        self.cores = _blas_cores()
+
+    def baseline(self, wl) -> dict:
+        lens = np.asarray(wl.seq_lens, np.float64)
+        t = float(np.sum(self.t_fixed + self.per_entry * lens))
+        return {"value": len(lens) / t, "unit": "query-tokens/s", "cores": int(self.cores), "kind": "oracle",
+                "sample": (f"NumPy fp64 oracle, one decode token through all {wl.n_layers} layers over the first "
+                           f"{self.NS} entries of a sequence (median of 3: {self.t_tok * 1e3:.0f} ms, of which "
+                           f"{self.t_ctx * 1e3:.0f} ms grow with the context: FP4 decode of the indexer keys, "
+                           f"scores, block maxima and pool ranking); that part scaled linearly to each of the "
+                           f"{len(lens)} sequences' visible entries ({int(lens.sum())} in all), the rest counted "
+                           f"once per token")}
 
 
 def cpu_baseline_prefill(wl, synth) -> dict:
     from oracle import attention, codec, indexer
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
     ns = 8192                                    # prefix of the prompt's entries used by the sample
     D, DI, W, H, K = wl.dim, wl.idx_dim, wl.window, wl.heads, wl.top_k
     x = synth.main_kv_rows(wl.cfg, 0, 0, ns, D)
@@ -368,53 +400,150 @@ def cpu_baseline_prefill(wl, synth) -> dict:
     t_tok, t_scan = sorted(runs)[1]
     n_full = int(wl.seq_lens[0])
     t_full_ctx = t_tok + t_scan * (n_full / ns - 1.0)
-    return {"value": 1.0 / t_full_ctx, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": 1.0 / t_full_ctx, "unit": "query-tokens/s", "cores": int(_blas_cores()), "kind": "oracle",
             "sample": (f"NumPy fp64 oracle, one prefill query through all {wl.n_layers} encoder layers over the "
-                       f"first {ns} entries (median of 3: {t_tok * 1e3:.0f} ms, flat Top-K {t_scan * 1e3:.0f} ms); "
-                       f"the flat Top-K scaled linearly to {n_full} entries")}
+                       f"first {ns} entries (median of 3: {t_tok * 1e3:.0f} ms, flat Top-K incl. FP4 decode of the "
+                       f"keys {t_scan * 1e3:.0f} ms); the flat Top-K scaled linearly to {n_full} entries")}
 
 
-def run_prefill(args, wl, torch, csa2, synth):
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+
+def same_snapshot(torch, a, b):
+    return all(torch.equal(x, y) for x, y in zip(a[0] + [a[1]] + a[2] + a[3], b[0] + [b[1]] + b[2] + b[3]))
+
+
+def capture(torch, W, steps):
+    """One HIP graph holding `steps` steps of W (kernel launches only)."""
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for _ in range(steps):
+                W.step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return graph
+
+
+def time_steps(torch, W, steps, warmup, mode):
+    """Milliseconds per step over `steps` timed steps (graph replay or eager
+    launches), checked equal to an eager reference step."""
+    for _ in range(warmup):
+        W.step()
+    torch.cuda.synchronize()
+    ref = W.snapshot()
+    graph = None
+    if mode == "graph":
+        graph = capture(torch, W, steps)
+        graph.replay()                     # untimed replay, checked against eager
+        torch.cuda.synchronize()
+        if not same_snapshot(torch, ref, W.snapshot()):
+            raise RuntimeError("graph replay differs from eager execution")
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(steps):
+            W.step()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    if not same_snapshot(torch, ref, W.snapshot()):
+        raise RuntimeError("timed steps differ from the eager reference")
+    del graph
+    return t0.elapsed_time(t1) / steps, wall
+
+
+def kernel_times(torch, csa2, W, steps):
+    """Average launch durations of the first scan, the attention and the
+    quantise-on-write kernels from HIP events stamped by their own dispatches,
+    over `steps` eager steps (events cannot be timed inside a graph replay)."""
+    csa2.csa2_profile_scan(True)
+    csa2.csa2_profile_attn(True)
+    csa2.csa2_profile_write(True)
+    try:
+        for _ in range(steps):
+            W.step()
+        torch.cuda.synchronize()
+        sc = csa2.csa2_profile_scan_read()
+        at = csa2.csa2_profile_attn_read()
+        wr = csa2.csa2_profile_write_read()
+    finally:
+        csa2.csa2_profile_scan(False)
+        csa2.csa2_profile_attn(False)
+        csa2.csa2_profile_write(False)
+    return {"scan": sc, "attn": at, "write": wr}
+
+
+def time_cold(torch, W, reps):
+    """Median milliseconds of one step (a one-step graph replay) when a 1 GiB
+    scratch write just before it has evicted the L2s and the 256 MB Infinity
+    Cache."""
+    graph = capture(torch, W, 1)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    times = []
+    for r in range(reps):
+        scratch.fill_(r & 0xFF)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1))
+    del scratch, graph
+    return float(np.median(times)), float(np.min(times)), float(np.max(times))
+
+
+def avg_ms(rec):
+    ms, n = rec
+    return ms / n if n else float("nan")
+
+
+def decode_record(wl, W, ms_per_step, kt, mode) -> dict:
+    """Step time, query-tokens/s and the first scan's roofline for a decode workload."""
+    scan_ms = avg_ms(kt["scan"])
+    scan_bytes = W.scan_bytes_per_launch()
+    achieved = scan_bytes / (scan_ms / 1e3) / 1e9
+    attn_ms = avg_ms(kt["attn"])
+    attn_bytes = W.attn_bytes_per_launch()
+    step_bytes = W.step_bytes()
+    return {
+        "workload": wl.name, "mode": mode, "ms_per_step": round(ms_per_step, 4),
+        "value": round(W.M / (ms_per_step / 1e3), 1), "unit": "query-tokens/s",
+        "sequences": len(wl.seq_lens), "visible_entries": int(np.sum(wl.seq_lens)),
+        "roofline": {"bound": "hbm", "kernel": "first scan (k_scan)", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "avg_launch_ms": round(scan_ms, 5), "algorithmic_bytes_per_launch": scan_bytes},
+        "attention": {"kernel": "k_attn_decode", "avg_launch_ms": round(attn_ms, 5),
+                      "algorithmic_bytes_per_launch": attn_bytes,
+                      "achieved_gbs": round(attn_bytes / (attn_ms / 1e3) / 1e9, 1)},
+        "write_path_avg_launch_ms": round(avg_ms(kt["write"]), 5),
+        "step_algorithmic_bytes": step_bytes,
+        "step_algorithmic_gbs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "step_frac_of_hbm_peak": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
+def run_prefill(args, wl, torch, csa2, synth) -> dict:
     t0 = time.time()
     W = PrefillWorkload(wl, torch, csa2, synth)
     setup_s = time.time() - t0
     print(f"[bench] setup {setup_s:.1f}s: {wl.name}, {W.M} queries over {wl.seq_lens[0]} entries",
           file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        W.step()
-    torch.cuda.synchronize()
-    ref = W.snapshot()
-
-    def same(a, b):
-        return all(torch.equal(x, y) for x, y in zip(a[0] + [a[1]] + a[2] + a[3], b[0] + [b[1]] + b[2] + b[3]))
-
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    for _ in range(args.steps):
-        W.step()
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_end)
-    if not same(ref, W.snapshot()):
-        raise RuntimeError("timed steps differ from the warm-up step")
-    # kernel durations: HIP events stamped by each scoring / attention dispatch, same steps again
-    csa2.csa2_profile_scan(True)
-    csa2.csa2_profile_attn(True)
-    for _ in range(args.steps):
-        W.step()
-    torch.cuda.synchronize()
-    sc_ms, sc_n = csa2.csa2_profile_scan_read()
-    at_ms, at_n = csa2.csa2_profile_attn_read()
-    csa2.csa2_profile_scan(False)
-    csa2.csa2_profile_attn(False)
-    assert sc_n == args.steps * len(wl.groups) and at_n == args.steps * wl.n_layers, (sc_n, at_n)
-    ms_per_step = ms_total / args.steps
-    at_avg, sc_avg = at_ms / at_n, sc_ms / sc_n
+    ms_per_step, wall = time_steps(torch, W, args.steps, args.warmup, "eager")
+    kt = kernel_times(torch, csa2, W, args.steps)
+    assert kt["scan"][1] == args.steps * len(wl.groups) and kt["attn"][1] == args.steps * wl.n_layers, kt
+    assert kt["write"][1] == args.steps * len(wl.groups), kt
+    at_avg, sc_avg, wr_avg = avg_ms(kt["attn"]), avg_ms(kt["scan"]), avg_ms(kt["write"])
     at_tf = W.attn_flops_per_launch() / (at_avg / 1e3) / 1e12
     sc_tf = W.scoring_flops_per_launch() / (sc_avg / 1e3) / 1e12
+    wr_b = W.write_bytes_per_launch()
     result = {
         "metric": METRIC_PREFILL,
         "value": round(W.M / (ms_per_step / 1e3), 1),
@@ -429,9 +558,10 @@ def run_prefill(args, wl, torch, csa2, synth):
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": wl.name, "queries": W.M, "entries": int(wl.seq_lens[0]), "ratio": wl.ratio,
-                   "layers": wl.n_layers, "layout": "3x(Full+5Reuse), flat Top-K", "latent_dim": wl.dim,
-                   "heads": wl.heads, "idx_heads": wl.idx_heads, "idx_dim": wl.idx_dim, "top_k": wl.top_k,
-                   "window": wl.window, "storage": "FP4 E2M1/E4M3x16 main+indexer, FP8 E4M3 window"},
+                   "layers": wl.n_layers, "layout": "3x(Full+5Reuse), flat Top-K, caches per Full group",
+                   "latent_dim": wl.dim, "heads": wl.heads, "idx_heads": wl.idx_heads, "idx_dim": wl.idx_dim,
+                   "top_k": wl.top_k, "window": wl.window,
+                   "storage": "FP4 E2M1/E4M3x16 main+indexer, FP8 E4M3 window"},
         "roofline": {"bound": "mfma", "kernel": "prefill attention (k_attn_prefill)", "achieved": round(at_tf, 1),
                      "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(at_tf / F16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": None, "avg_launch_ms": round(at_avg, 4),
@@ -441,14 +571,29 @@ def run_prefill(args, wl, torch, csa2, synth):
                             "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(sc_tf / F16_MFMA_PEAK_TFLOPS, 4), "avg_launch_ms": round(sc_avg, 4),
                             "algorithmic_flops_per_launch": W.scoring_flops_per_launch()},
+        "quantize_on_write": {"bound": "hbm", "kernel": "k_quantize_fp4_derive", "rows_per_launch": W.R,
+                              "avg_launch_ms": round(wr_avg, 5), "algorithmic_bytes_per_launch": wr_b,
+                              "achieved_gbs": round(wr_b / (wr_avg / 1e3) / 1e9, 1),
+                              "frac": round(wr_b / (wr_avg / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
         "wall_s_timed": round(wall, 4),
         "setup_s": round(setup_s, 1),
     }
     if not args.no_cpu_baseline:
         t0 = time.time()
         result["cpu_baseline"] = cpu_baseline_prefill(wl, synth)
-        print(f"[bench] cpu baseline {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    print(json.dumps(result), flush=True)
+        print(f"[bench] prefill cpu baseline {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    del W
+    torch.cuda.empty_cache()
+    return result
+
+
+def setup_decode(wl, torch, csa2, synth):
+    t0 = time.time()
+    W = DecodeWorkload(wl, torch, csa2, synth)
+    setup_s = time.time() - t0
+    print(f"[bench] setup {setup_s:.1f}s: {wl.name}, {len(wl.seq_lens)} seqs, {sum(wl.seq_lens)} entries",
+          file=sys.stderr, flush=True)
+    return W, setup_s
 
 
 # ---------------------------------------------------------------------------
@@ -468,73 +613,14 @@ def main():
     csa2.lib()
     wl = synth.workload(args.workload)
     if wl.phase == "prefill":
-        run_prefill(args, wl, torch, csa2, synth)
+        result = run_prefill(args, wl, torch, csa2, synth)
+        print(json.dumps(result), flush=True)
         return
     assert wl.phase == "decode", wl.phase
-    t0 = time.time()
-    W = DecodeWorkload(wl, torch, csa2, synth)
-    setup_s = time.time() - t0
-    print(f"[bench] setup {setup_s:.1f}s: {wl.name}, {len(wl.seq_lens)} seqs, {sum(wl.seq_lens)} entries",
-          file=sys.stderr, flush=True)
-
-    for _ in range(args.warmup):
-        W.step()
-    torch.cuda.synchronize()
-    ref = W.snapshot()
-
-    def same(a, b):
-        return all(torch.equal(x, y) for x, y in zip(a[0] + [a[1]] + a[2] + a[3], b[0] + [b[1]] + b[2] + b[3]))
-
-    graph = None
-    if args.mode == "graph":
-        # all timed steps in one captured graph (kernel launches only)
-        graph = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(graph, stream=s):
-                for _ in range(args.steps):
-                    W.step()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        graph.replay()                     # untimed replay, checked against eager
-        torch.cuda.synchronize()
-        if not same(ref, W.snapshot()):
-            raise RuntimeError("graph replay differs from eager execution")
-    else:
-        csa2.csa2_profile_scan(True)
-        csa2.csa2_profile_attn(True)
-
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    if graph is not None:
-        graph.replay()
-    else:
-        for _ in range(args.steps):
-            W.step()
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_end)
-    if not same(ref, W.snapshot()):
-        raise RuntimeError("timed steps differ from the eager reference")
-    if graph is not None:
-        # events cannot be timed inside a graph replay: the first scan's launch
-        # duration comes from HIP events stamped by its dispatch in the same steps run eagerly
-        csa2.csa2_profile_scan(True)
-        csa2.csa2_profile_attn(True)
-        for _ in range(args.steps):
-            W.step()
-        torch.cuda.synchronize()
-    scan_ms_total, scan_launches = csa2.csa2_profile_scan_read()
-    attn_ms_total, attn_launches = csa2.csa2_profile_attn_read()
-    csa2.csa2_profile_scan(False)
-    csa2.csa2_profile_attn(False)
-    assert scan_launches == args.steps, (scan_launches, args.steps)
-    assert attn_launches == args.steps * wl.n_layers, (attn_launches, args.steps)
+    W, setup_s = setup_decode(wl, torch, csa2, synth)
+    ms_per_step, wall = time_steps(torch, W, args.steps, args.warmup, args.mode)
+    kt = kernel_times(torch, csa2, W, args.steps)
+    assert kt["scan"][1] == args.steps and kt["attn"][1] == args.steps * wl.n_layers, kt
 
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
@@ -542,31 +628,27 @@ def main():
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
-    ms_per_step = ms_total / args.steps
-    tokens_per_step = W.M
-    value = tokens_per_step / (ms_per_step / 1e3)
-    scan_avg_ms = scan_ms_total / max(1, scan_launches)
-    scan_bytes = W.scan_bytes_per_launch()
-    achieved = scan_bytes / (scan_avg_ms / 1e3) / 1e9
-    step_bytes = W.step_bytes()
-    attn_avg_ms = attn_ms_total / max(1, attn_launches)
-    attn_bytes = W.attn_bytes_per_launch()
+    rec = decode_record(wl, W, ms_per_step, kt, args.mode)
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "scan_traffic.json")
     if os.path.exists(tpath):
-        import hashlib
-        rec = json.load(open(tpath))
-        if rec.get("source_sha256") == scan_source_sha256() and rec.get("workload") == wl.name:
-            traffic = rec.get("bytes_per_launch")
+        trec = json.load(open(tpath))
+        if trec.get("source_sha256") == scan_source_sha256() and trec.get("workload") == wl.name:
+            traffic = trec.get("bytes_per_launch")
+    roofline = dict(rec["roofline"])
+    roofline["traffic"] = traffic
+    roofline["timing"] = "HIP events stamped by each first-scan dispatch" + (
+        " (same steps run eagerly after the timed graph replay)" if args.mode == "graph" else "")
     result = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": rec["value"],
         "unit": "query-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -577,25 +659,54 @@ def main():
                    "heads": wl.heads, "idx_heads": wl.idx_heads, "idx_dim": wl.idx_dim,
                    "pool_blocks": wl.pool_blocks, "top_k": wl.top_k, "window": wl.window,
                    "storage": "FP4 E2M1/E4M3x16 main+indexer, FP8 E4M3 window", "mode": args.mode},
-        "roofline": {"bound": "hbm", "kernel": "first scan (k_scan)", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "avg_launch_ms": round(scan_avg_ms, 5),
-                     "timing": "HIP events stamped by each first-scan dispatch" + (
-                         " (same steps run eagerly after the timed graph replay)" if graph is not None else ""),
-                     "algorithmic_bytes_per_launch": scan_bytes},
-        "attention": {"kernel": "k_attn_decode", "avg_launch_ms": round(attn_avg_ms, 5),
-                      "algorithmic_bytes_per_launch": attn_bytes,
-                      "achieved_gbs": round(attn_bytes / (attn_avg_ms / 1e3) / 1e9, 1),
-                      "bound": "latency (one layer's reads are ~1.6 MB)"},
-        "step_algorithmic_bytes": step_bytes,
-        "step_algorithmic_gbs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "roofline": roofline,
+        "attention": dict(rec["attention"], bound="latency (one layer's reads are ~1.6 MB)"),
+        "write_path_avg_launch_ms": rec["write_path_avg_launch_ms"],
+        "step_algorithmic_bytes": rec["step_algorithmic_bytes"],
+        "step_algorithmic_gbs": rec["step_algorithmic_gbs"],
+        "step_frac_of_hbm_peak": rec["step_frac_of_hbm_peak"],
         "wall_s_timed": round(wall, 4),
         "setup_s": round(setup_s, 1),
     }
+    model = None
     if not args.no_cpu_baseline:
         t0 = time.time()
-        result["cpu_baseline"] = cpu_baseline(wl, synth)
+        model = CpuDecodeModel(wl, synth)
+        result["cpu_baseline"] = model.baseline(wl)
         print(f"[bench] cpu baseline {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    if not args.no_extras:
+        extras = {}
+        # the headline workload: the other launch mode, and cold caches
+        other = "eager" if args.mode == "graph" else "graph"
+        ms_o, _ = time_steps(torch, W, args.steps, 1, other)
+        extras[f"{wl.name}/{other}"] = decode_record(wl, W, ms_o, kt, other)
+        med, lo, hi = time_cold(torch, W, args.cold_reps)
+        cold = decode_record(wl, W, med, kt, "graph, cold caches")
+        cold["cold"] = {"reps": args.cold_reps, "median_ms": round(med, 4), "min_ms": round(lo, 4),
+                        "max_ms": round(hi, 4),
+                        "method": "1 GiB scratch written before each one-step graph replay"}
+        extras[f"{wl.name}/cold"] = cold
+        del W
+        torch.cuda.empty_cache()
+        for cfg in (1, 3):
+            wx = synth.workload(cfg)
+            Wx, _ = setup_decode(wx, torch, csa2, synth)
+            ktx = kernel_times(torch, csa2, Wx, args.steps)
+            for mode in (("graph", "eager") if cfg == 1 else ("graph",)):
+                msx, _ = time_steps(torch, Wx, args.steps, args.warmup, mode)
+                r = decode_record(wx, Wx, msx, ktx, mode)
+                if model is not None:
+                    r["cpu_baseline"] = model.baseline(wx)
+                extras[f"{wx.name}/{mode}"] = r
+            del Wx
+            torch.cuda.empty_cache()
+        wp = synth.workload(2)
+        pre = run_prefill(args, wp, torch, csa2, synth)
+        extras[wp.name] = {k: pre[k] for k in ("metric", "value", "unit", "ms_per_step", "config", "roofline",
+                                                "indexer_scoring", "quantize_on_write", "cpu_baseline")
+                           if k in pre}
+        result["workloads"] = extras
     print(json.dumps(result), flush=True)
 
 

@@ -23,6 +23,7 @@ EXPORTS = [
     "csa2_dequant_fp4", "csa2_index_workspace_size", "csa2_index_full", "csa2_reindex",
     "csa2_attn_workspace_size", "csa2_sparse_swa_attn", "csa2_group_workspace_size", "csa2_group_step",
     "csa2_profile_scan", "csa2_profile_scan_read", "csa2_profile_attn", "csa2_profile_attn_read",
+    "csa2_profile_write", "csa2_profile_write_read",
 ]
 
 
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
             "csa2_profile_scan_read": (i32, [POINTER(ctypes.c_double), POINTER(c_int64)]),
             "csa2_profile_attn": (i32, [i32]),
             "csa2_profile_attn_read": (i32, [POINTER(ctypes.c_double), POINTER(c_int64)]),
+            "csa2_profile_write": (i32, [i32]),
+            "csa2_profile_write_read": (i32, [POINTER(ctypes.c_double), POINTER(c_int64)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -302,4 +305,15 @@ def csa2_profile_attn_read() -> tuple[float, int]:
     """(summed attention kernel milliseconds, launches) since attention timing was enabled."""
     ms, n = ctypes.c_double(0.0), c_int64(0)
     _check(lib().csa2_profile_attn_read(ctypes.byref(ms), ctypes.byref(n)), "csa2_profile_attn_read")
+    return float(ms.value), int(n.value)
+
+
+def csa2_profile_write(enable: bool) -> None:
+    _check(lib().csa2_profile_write(1 if enable else 0), "csa2_profile_write")
+
+
+def csa2_profile_write_read() -> tuple[float, int]:
+    """(summed quantise-on-write kernel milliseconds, launches) since write timing was enabled."""
+    ms, n = ctypes.c_double(0.0), c_int64(0)
+    _check(lib().csa2_profile_write_read(ctypes.byref(ms), ctypes.byref(n)), "csa2_profile_write_read")
     return float(ms.value), int(n.value)

@@ -15,7 +15,7 @@ struct Timing {
   bool on = false;
   std::vector<hipEvent_t> events;   // begin/end pairs in launch order
 };
-Timing g_timing[2];                 // 0: first scan, 1: attention
+Timing g_timing[3];                 // 0: first scan, 1: attention, 2: quantise-on-write
 
 void clear_events(Timing &t) {
   for (hipEvent_t e : t.events) (void)hipEventDestroy(e);
@@ -342,6 +342,16 @@ int32_t csa2_profile_attn(int32_t enable) {
 
 int32_t csa2_profile_attn_read(double *total_ms, int64_t *launches) {
   return read_events(g_timing[1], total_ms, launches);
+}
+
+int32_t csa2_profile_write(int32_t enable) {
+  clear_events(g_timing[2]);
+  g_timing[2].on = enable != 0;
+  return CSA2_OK;
+}
+
+int32_t csa2_profile_write_read(double *total_ms, int64_t *launches) {
+  return read_events(g_timing[2], total_ms, launches);
 }
 
 }  // extern "C"

@@ -172,44 +172,26 @@ CSA2_DEV void qk_tile(const _Float16 *kt, int KT, const half8_t *qa, const half8
 }
 
 // ===========================================================================
-// decode schedule: one fused kernel per layer
+// decode schedule: key splits + merge
 // ===========================================================================
 
-constexpr int kDW = 8;                   // waves per decode workgroup
-constexpr int kDH = 16;                  // heads per decode workgroup
-constexpr int kDD = 64;                  // output dims per decode workgroup
-constexpr int kDMainT = 4;               // Top-K tiles of 16 slots per wave and chunk
-constexpr int kDTm = kDW * kDMainT;      // Top-K tiles per chunk (512 slots)
-constexpr int kDTw = kDW;                // window tiles per chunk, one per wave (128 rows)
-constexpr int kDSlots = 16 * (kDTm + kDTw);  // key slots per chunk (640)
+constexpr int kSW = 4;                   // waves per split workgroup (one per SIMD)
+constexpr int kSH = 16;                  // heads per split workgroup
+constexpr int kSKeys = 128;              // key slots per split: 8 tiles of 16, two per wave
 
-struct DecLds {
-  static constexpr int VT = kDD + 8;       // [key][dim] row stride of the V slice (f16)
-  static constexpr int PT = kDSlots + 8;   // [head][key] row stride of P (f16)
-  _Float16 vt[kDSlots * VT];
-  _Float16 p[kDH * PT];
-  float wmax[kDW][kDH];
-  float wsum[kDW][kDH];
-  float wr[kDW];
-  float4_t ored[4][64];
-};
-
-// A lane's share of one key tile for S = Q K^T: the lane (key row, quad)
-// holds dims quad*(D/4) .. +D/4 of its key.  Main rows: D/8 FP4 code bytes
-// plus D/64 E4M3 scale bytes; window rows: D/4 FP8 code bytes.
 template <int D>
-struct MainUnit {
-  uint32_t w[D / 32];
-  uint32_t s[(D / 64 + 3) / 4];
-};
-template <int D>
-struct WinUnit {
-  uint32_t w[D / 16];
+struct SplitLds {
+  static constexpr int VT = D + 8;       // [key][dim] row stride of the decoded keys (f16)
+  static constexpr int PT = kSKeys + 8;  // [head][key] row stride of P (f16)
+  _Float16 vt[kSKeys * VT];
+  _Float16 p[kSH * PT];
+  float wmax[kSW][kSH];
+  float wsum[kSW][kSH];
 };
 
-// Buffer loads (make_rsrc, kOutOfRange) make every load unconditional: the
-// decode kernel reads empty, padded or invisible keys and heads beyond H at
-// out-of-range offsets, which return zeros.
+// Buffer loads (make_rsrc, kOutOfRange) make every load unconditional: empty,
+// padded or invisible keys and heads beyond H are read at out-of-range
+// offsets, which return zeros.
 template <int BYTES>
 CSA2_DEV void buffer_load_words(uint32_t *dst, rsrc_t r, uint32_t off) {
   if constexpr (BYTES >= 16) {
@@ -230,318 +212,250 @@ CSA2_DEV void buffer_load_words(uint32_t *dst, rsrc_t r, uint32_t off) {
   }
 }
 
-// S += Q K^T over every k-step of a main tile.  The B operand of step kk is
-// dims quad*(D/4) + 8*kk .. +7 of the lane's key.  Called under wave-uniform
-// conditions only: an MFMA reads the operands of every lane whatever the
-// exec mask.
-template <int D, bool QF32>
-CSA2_DEV void score_main(const MainUnit<D> &u, const half8_t *qa, const half8_t *qb, float4_t &sa) {
-  half2_t sc[(D / 64 + 1) / 2];
-#pragma unroll
-  for (int g = 0; g < (D / 64 + 1) / 2; ++g) sc[g] = e4m3x2_to_f16(u.s[g / 2] >> (16 * (g % 2)));
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-    const half8_t b = fp4x8_dequant_f16(u.w[kk], sc[kk / 4][(kk / 2) % 2]);
-    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sa, 0, 0, 0);
-    if constexpr (QF32) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sa, 0, 0, 0);
-  }
-}
-template <int D, bool QF32>
-CSA2_DEV void score_win(const WinUnit<D> &u, const half8_t *qa, const half8_t *qb, float4_t &sa) {
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-    const half8_t b = e4m3x8_to_f16(u.w[2 * kk], u.w[2 * kk + 1]);
-    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sa, 0, 0, 0);
-    if constexpr (QF32) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sa, 0, 0, 0);
-  }
-}
-
-// The V slice of one key tile: lane (key n, part p) holds dims d0 + 16p ..
-// +15 of key n (four parts cover the 64-dim slice), loaded apart from the
-// scoring units (a cached re-read of 8 code bytes + 1 scale byte, or 16 FP8
-// bytes) and stored as f16 into row n of the tile's LDS rows.
-struct VPiece {
-  uint32_t w[4];
+// The lane's share of one 16-key tile: lane (key row, quad) holds dims
+// quad*(D/4) .. +D/4 of its key - D/8 FP4 code bytes plus D/64 E4M3 scale
+// bytes of a Top-K row, or D/4 FP8 code bytes of a window row.
+template <int D>
+struct KeyShare {
+  uint32_t w[D / 16];
+  uint32_t s[(D / 64 + 3) / 4];
 };
-CSA2_DEV void load_vpiece_main(VPiece &v, rsrc_t codes, rsrc_t scales, uint32_t code_off, uint32_t scale_off) {
-  const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(codes, code_off, 0, 0);
-  v.w[0] = x[0];
-  v.w[1] = x[1];
-  v.w[2] = __builtin_amdgcn_raw_buffer_load_b8(scales, scale_off, 0, 0);
-  v.w[3] = 0u;
-}
-CSA2_DEV void load_vpiece_win(VPiece &v, rsrc_t win, uint32_t code_off) {
-  const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(win, code_off, 0, 0);
-  v.w[0] = x[0]; v.w[1] = x[1]; v.w[2] = x[2]; v.w[3] = x[3];
-}
-CSA2_DEV void store_vpiece(const VPiece &v, bool main, _Float16 *dst) {
-  half8_t a, b;
-  if (main) {
-    const _Float16 sc = e4m3x2_to_f16(v.w[2])[0];
-    a = fp4x8_dequant_f16(v.w[0], sc);
-    b = fp4x8_dequant_f16(v.w[1], sc);
+
+// The f16 B operand of k-step kk (dims quad*(D/4) + 8*kk .. +7 of the lane's key).
+template <int D, bool MAIN>
+CSA2_DEV half8_t key_operand(const KeyShare<D> &u, int kk) {
+  if constexpr (MAIN) {
+    const uint32_t sw = u.s[kk / 8] >> (8 * ((kk / 2) % 4));   // scale byte kk/2 of the lane's share
+    return fp4x8_dequant_f16(u.w[kk], e4m3x2_to_f16(sw)[0]);
   } else {
-    a = e4m3x8_to_f16(v.w[0], v.w[1]);
-    b = e4m3x8_to_f16(v.w[2], v.w[3]);
+    return e4m3x8_to_f16(u.w[2 * kk], u.w[2 * kk + 1]);
   }
-  *reinterpret_cast<half8_t *>(dst) = a;
-  *reinterpret_cast<half8_t *>(dst + 8) = b;
 }
 
-// grid (D / 64 output slices, queries, head blocks of 16), 8 waves.
-//
-// A workgroup computes the logits of its 16 heads against every key of the
-// query (replicated across the output slices: spare MFMA time buys a kernel
-// with no partial outputs to merge) and P V for its 64 output dims.  Keys go
-// in chunks of 32 Top-K tiles + 8 window tiles (one chunk for Top-512 + 128
-// window rows): wave w owns Top-K tiles w, w+8, w+16, w+24 and window tile w
-// of the chunk.  Every load of a chunk is issued before any key is scored, so
-// a wave waits for memory once per chunk: the Top-K indices and window
-// scales first, then (while they are in flight) the query operands straight
-// into registers, then all key rows and V pieces.  Channels are assigned to
-// MFMA k-steps by quarter (lane quad q feeds dims q*(D/4) + 8*kk .. +7 for
-// both query and key), so a lane streams contiguous bytes of its key.  The
-// chunk's softmax statistics meet in LDS; P (f16) and the 64-dim V slice
-// pass through LDS; wave w multiplies P by V for dims 16*(w%4) .. +15 over
-// every second 32-key step, the two halves being added at the end.  Chunks
-// combine online.
+// grid (key splits, queries, head blocks of 16), 4 waves.  Split s covers
+// key slots 128s .. 128s+127 of the Top-K list (s < n_main) or window rows
+// 128(s - n_main) .. of the query's window.  Wave w owns tiles 2w and 2w+1 of
+// the split: it issues the Top-K index loads (or window scale loads), its
+// query operands (16 heads, straight into registers) and then every key row of
+// its tiles at once; it computes S = Q K^T for its 32 keys from registers
+// (channels assigned to k-steps by quarter: lane quad q feeds dims q*(D/4) +
+// 8*kk for both operands) and writes the decoded keys into an LDS tile for
+// P V.  The split's softmax statistics meet in LDS; P (f16) goes to LDS; wave
+// w computes O for dims w*(D/4) .. +D/4 over the split's 128 keys.  The
+// normalised partial O and its log2-domain lse go to the workspace for
+// k_attn_merge.
 template <int D, bool QF32>
-__global__ __launch_bounds__(64 * kDW) void k_attn_decode(const void *__restrict__ q_any, int H,
-                                                          const uint8_t *__restrict__ kv_codes,
-                                                          const uint8_t *__restrict__ kv_scales,
-                                                          const int64_t *__restrict__ seq_start,
-                                                          const int32_t *__restrict__ seq_len, int ratio,
-                                                          const int32_t *__restrict__ q_seq,
-                                                          const int32_t *__restrict__ q_pos,
-                                                          const int32_t *__restrict__ topk, int K,
-                                                          const uint8_t *__restrict__ swa_codes,
-                                                          const float *__restrict__ swa_scale,
-                                                          const int32_t *__restrict__ swa_start,
-                                                          const int32_t *__restrict__ swa_count, int W, float tau2,
-                                                          float *__restrict__ out, float *__restrict__ lse) {
-  __shared__ DecLds L;
+__global__ __launch_bounds__(64 * kSW) void k_attn_split(const void *__restrict__ q_any, int H,
+                                                         const uint8_t *__restrict__ kv_codes,
+                                                         const uint8_t *__restrict__ kv_scales,
+                                                         const int64_t *__restrict__ seq_start,
+                                                         const int32_t *__restrict__ seq_len, int ratio,
+                                                         const int32_t *__restrict__ q_seq,
+                                                         const int32_t *__restrict__ q_pos,
+                                                         const int32_t *__restrict__ topk, int K, int n_main,
+                                                         const uint8_t *__restrict__ swa_codes,
+                                                         const float *__restrict__ swa_scale,
+                                                         const int32_t *__restrict__ swa_start,
+                                                         const int32_t *__restrict__ swa_count, int W, float tau2,
+                                                         float *__restrict__ part_o, float *__restrict__ part_lse) {
+  using Lds = SplitLds<D>;
+  __shared__ Lds L;
   constexpr int NK = D / 32;             // MFMA k-steps per key
-  constexpr int DD = D < kDD ? D : kDD;  // dims of this workgroup's output slice
-  constexpr int NT = kDMainT + 1;        // tiles per wave per chunk (Top-K tiles, then the window tile)
-  const int m = blockIdx.y, hb = blockIdx.z;
-  const int d0 = blockIdx.x * kDD;
-  // the wave index as a scalar: per-tile conditions (and the descriptor choice)
-  // are then wave-uniform branches, not exec-masked ones
-  const int tid = threadIdx.x, l = lane_id(), wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int NDT = D / 64;            // 16-dim output tiles per wave
+  const int sp = blockIdx.x, m = blockIdx.y, hb = blockIdx.z;
+  const int S = gridDim.x;
+  const int l = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = l & 15, quad = l >> 4;
+  const bool main = sp < n_main;          // workgroup-uniform: Top-K keys or window rows
 
   const int s = q_seq[m];
   const int64_t lim = ((int64_t)q_pos[m] + 1) / ratio;
   const int64_t vis = max<int64_t>(0, min<int64_t>(seq_len[s], lim));
   const int64_t row0 = seq_start[s];
-  // with no window the window arrays may be null (their descriptors are empty)
   const int wcount = (W > 0) ? max(0, min(swa_count[m], W)) : 0;
   const int64_t wstart = (W > 0) ? swa_start[m] : 0;
-  const int TM = (K + 15) / 16;        // Top-K tiles
-  const int TW = (wcount + 15) / 16;   // window tiles of this query
-  const int nchunk = max((TM + kDTm - 1) / kDTm, (TW + kDTw - 1) / kDTw);
-  // descriptors: this query's visible rows, window rows, Top-K list and queries
   const rsrc_t r_codes = make_rsrc(kv_codes + row0 * (D / 2), (uint32_t)(vis * (D / 2)));
   const rsrc_t r_scales = make_rsrc(kv_scales + row0 * (D / 16), (uint32_t)(vis * (D / 16)));
   const rsrc_t r_win = make_rsrc(wcount ? swa_codes + wstart * D : nullptr, (uint32_t)(wcount * D));
   const rsrc_t r_wsc = make_rsrc(wcount ? swa_scale + wstart : nullptr, (uint32_t)(wcount * 4));
   const rsrc_t r_topk = make_rsrc(K ? topk + (int64_t)m * K : nullptr, (uint32_t)(K * 4));
-  constexpr int QE = QF32 ? 4 : 2;  // query element bytes
+  constexpr int QE = QF32 ? 4 : 2;
   const rsrc_t r_q = make_rsrc(static_cast<const char *>(q_any) + (int64_t)m * H * D * QE, (uint32_t)(H * D * QE));
 
-  half8_t qa[NK];
-  half8_t qb[QF32 ? NK : 1];
-  float m_run[4], l_part[4];
+  // ---- the key slots of this lane's two tiles: index (or window scale) loads first ----
+  const int slot0 = 128 * (main ? sp : sp - n_main) + 32 * wv + row;   // tile i: slot0 + 16 i
+  int32_t jv[2];
+  float rv[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) { m_run[j] = -INFINITY; l_part[j] = 0.0f; }
-  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  int e_cur = 0;                          // accumulator exponent: true O = acc * 2^-e_cur
-  const int dt = wv & 3, khalf = wv >> 2;  // P V: dims 16*dt .., k-steps khalf, khalf + 2, ...
-
-  for (int c = 0; c < nchunk; ++c) {
-    const int nmc = max(0, min(kDTm, TM - kDTm * c));   // Top-K tiles of the chunk
-    const int nwc = max(0, min(kDTw, TW - kDTw * c));   // window tiles of the chunk
-    const int nme = (nmc + 1) & ~1, nwe = (nwc + 1) & ~1;  // rounded to whole 32-key steps
-    if (c > 0) __syncthreads();           // the previous chunk's LDS reads are done
-    // ---- sources of this wave's tiles: the index and window-scale loads go
-    // first, the first chunk's query operands behind them ----
-    int32_t jv[kDMainT];
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t so = (uint32_t)(slot0 + 16 * i) * 4u;
+    jv[i] = main ? (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_topk, so, 0, 0) : 0;
+    rv[i] = main ? 0.0f : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_wsc, so, 0, 0));
+  }
+  // ---- query operands: lane (head row, quad) holds dims quad*(D/4) .. +D/4 ----
+  uint32_t qraw[(D / 4) * QE / 4];
+  buffer_load_words<(D / 4) * QE>(qraw, r_q, (uint32_t)(((hb * kSH + row) * D + quad * (D / 4)) * QE));
+  // ---- every key row of the lane's tiles ----
+  float ks[2];
+  KeyShare<D> ku[2];
 #pragma unroll
-    for (int i = 0; i < kDMainT; ++i) {
-      const int slot = 16 * (kDTm * c + wv + kDW * i) + row;
-      jv[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_topk, (uint32_t)slot * 4u, 0, 0);
-    }
-    const int wi = 16 * (kDTw * c + wv) + row;   // window row of this lane (window tile)
-    const float rv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_wsc, (uint32_t)wi * 4u, 0, 0));
-    uint32_t qraw[QF32 ? D / 8 : D / 16];
-    if (c == 0) {
-      // lane (head row, quad): dims quad*(D/4) .. +D/4 of head hb*16 + row
-      const uint32_t qoff = (uint32_t)(((hb * kDH + row) * D + quad * (D / 4)) * QE);
-      buffer_load_words<(D / 4) * QE>(qraw, r_q, qoff);
-    }
-    // offsets (selects, not branches: a branch would pull each load down to its use)
-    uint32_t coff[kDMainT], soff[kDMainT], vcoff[kDMainT], vsoff[kDMainT];
-    float sks[NT];
-    const int vd = d0 + 16 * quad;  // V piece of lane (key row, part quad): dims vd .. vd+15
-#pragma unroll
-    for (int i = 0; i < kDMainT; ++i) {
-      const int slot = 16 * (kDTm * c + wv + kDW * i) + row;
+  for (int i = 0; i < 2; ++i) {
+    const int slot = slot0 + 16 * i;
+    if (main) {
       const int32_t j = jv[i];
       const bool ok = slot < K && j >= 0 && j < vis;
-      coff[i] = ok ? (uint32_t)j * (D / 2) + quad * (D / 8) : kOutOfRange;
-      soff[i] = ok ? (uint32_t)j * (D / 16) + quad * (D / 64) : kOutOfRange;
-      vcoff[i] = ok ? (uint32_t)j * (D / 2) + vd / 2 : kOutOfRange;
-      vsoff[i] = ok ? (uint32_t)j * (D / 16) + vd / 16 : kOutOfRange;
-      sks[i] = ok ? 1.0f : 0.0f;
+      ks[i] = ok ? 1.0f : 0.0f;
+      buffer_load_words<D / 8>(ku[i].w, r_codes, ok ? (uint32_t)j * (D / 2) + quad * (D / 8) : kOutOfRange);
+      buffer_load_words<D / 64>(ku[i].s, r_scales, ok ? (uint32_t)j * (D / 16) + quad * (D / 64) : kOutOfRange);
+    } else {
+      ks[i] = (slot < wcount) ? rv[i] : 0.0f;   // rows past the window read as zeros
+      buffer_load_words<D / 4>(ku[i].w, r_win, (uint32_t)slot * D + quad * (D / 4));
     }
-    sks[kDMainT] = (wi < wcount) ? rv : 0.0f;
-    // ---- every key load of the chunk (rows past the window read as zeros) ----
-    MainUnit<D> mu[kDMainT];
-    VPiece vp[NT];
+  }
+  // ---- queries as f16 (bf16 converts exactly in the f16 range; fp32 splits into hi + lo) ----
+  half8_t qa[NK];
+  half8_t qb[QF32 ? NK : 1];
 #pragma unroll
-    for (int i = 0; i < kDMainT; ++i) {
-      if (wv + kDW * i < nme) {
-        buffer_load_words<D / 8>(mu[i].w, r_codes, coff[i]);
-        buffer_load_words<D / 64>(mu[i].s, r_scales, soff[i]);
-        load_vpiece_main(vp[i], r_codes, r_scales, vcoff[i], vsoff[i]);
+  for (int kk = 0; kk < NK; ++kk) {
+    if constexpr (QF32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = __uint_as_float(qraw[8 * kk + i]);
+        const _Float16 hi = (_Float16)v;
+        qa[kk][i] = hi;
+        qb[kk][i] = (_Float16)(v - (float)hi);
       }
-    }
-    WinUnit<D> wu;
-    if (wv < nwe) {
-      buffer_load_words<D / 4>(wu.w, r_win, (uint32_t)wi * D + quad * (D / 4));
-      load_vpiece_win(vp[kDMainT], r_win, (uint32_t)wi * D + vd);
-    }
-    if (c == 0) {
-      // queries as f16 MFMA A operands (bf16 converts exactly in the f16 range;
-      // fp32 splits into hi + lo parts)
+    } else {
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        if constexpr (QF32) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float v = __uint_as_float(qraw[8 * kk + i]);
-            const _Float16 hi = (_Float16)v;
-            qa[kk][i] = hi;
-            qb[kk][i] = (_Float16)(v - (float)hi);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t x = qraw[4 * kk + i];
-            qa[kk][2 * i] = (_Float16)__uint_as_float(x << 16);
-            qa[kk][2 * i + 1] = (_Float16)__uint_as_float(x & 0xFFFF0000u);
-          }
-        }
-      }
-    }
-    // ---- S for this wave's tiles; V slices into LDS ----
-    float4_t sacc[NT];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) sacc[i] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < kDMainT; ++i) {
-      const int lt = wv + kDW * i;
-      if (lt < nmc) score_main<D, QF32>(mu[i], qa, qb, sacc[i]);
-      if (lt < nme) store_vpiece(vp[i], true, &L.vt[(16 * lt + row) * DecLds::VT + 16 * quad]);
-    }
-    if (wv < nwc) score_win<D, QF32>(wu, qa, qb, sacc[kDMainT]);
-    if (wv < nwe) store_vpiece(vp[kDMainT], false, &L.vt[(16 * (kDTm + wv) + row) * DecLds::VT + 16 * quad]);
-    // ---- chunk statistics: lane holds key (16*tile + row) of heads 4*quad + j ----
-    float zz[NT][4];
-    float rm = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const bool live = (i < kDMainT) ? (wv + kDW * i < nmc) : (wv < nwc);
-      const float ks = live ? sks[i] : 0.0f;
-      rm = fmaxf(rm, ks);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) zz[i][j] = (ks != 0.0f) ? sacc[i][j] * tau2 * ks : -INFINITY;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) rm = fmaxf(rm, __shfl_xor(rm, o, 64));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < NT; ++i) mx = fmaxf(mx, zz[i][j]);
-      mx = max16_lanes(mx);
-      if (row == 0) L.wmax[wv][4 * quad + j] = mx;
-    }
-    if (l == 0) L.wr[wv] = rm;
-    __syncthreads();
-    float mnew[4], alpha[4];
-    rm = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kDW; ++w) rm = fmaxf(rm, L.wr[w]);
-    int e_new = 0;
-    (void)frexpf(rm, &e_new);
-    e_new = (rm > 0.0f) ? 1 - e_new : 0;  // chunk's largest r * 2^e_new in [1, 2)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float cm = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kDW; ++w) cm = fmaxf(cm, L.wmax[w][4 * quad + j]);
-      mnew[j] = fmaxf(m_run[j], cm);
-      alpha[j] = (m_run[j] == -INFINITY) ? 0.0f : exp2f(m_run[j] - mnew[j]);
-      m_run[j] = mnew[j];
-    }
-    // ---- P' = 2^(z - max) * r * 2^e_new as f16 into LDS [head][key] ----
-    // the denominator sums 2^(z - max); the window scale r enters only P'
-#pragma unroll
-    for (int j = 0; j < 4; ++j) l_part[j] *= alpha[j];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int lt = (i < kDMainT) ? wv + kDW * i : kDTm + wv;
-      const bool stored = (i < kDMainT) ? (wv + kDW * i < nme) : (wv < nwe);
-      if (!stored) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float pr = (zz[i][j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(zz[i][j] - mnew[j]);
-        l_part[j] += pr;
-        L.p[(4 * quad + j) * DecLds::PT + 16 * lt + row] = (_Float16)ldexpf(pr * sks[i], e_new);
-      }
-    }
-    if (c > 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] *= ldexpf(alpha[j], e_new - e_cur);
-    }
-    e_cur = e_new;
-    __syncthreads();
-    // ---- acc += P V for dims 16*dt .. over this wave's half of the 32-key
-    // steps: the chunk's Top-K steps, then its window steps ----
-    if (16 * dt < DD) {
-      const int nsm = nme / 2, nst = nsm + nwe / 2;
-      for (int st = khalf; st < nst; st += 2) {
-        const int k0 = (st < nsm) ? 32 * st : 16 * kDTm + 32 * (st - nsm);
-        const half8_t a = *reinterpret_cast<const half8_t *>(&L.p[row * DecLds::PT + k0 + 8 * quad]);
-        const half8_t b = v_operand_tr(L.vt, DecLds::VT, k0, 16 * dt, row, quad);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t x = qraw[4 * kk + i];
+        qa[kk][2 * i] = (_Float16)__uint_as_float(x << 16);
+        qa[kk][2 * i + 1] = (_Float16)__uint_as_float(x & 0xFFFF0000u);
       }
     }
   }
-
-  // ---- softmax denominators: lane partials -> rows -> waves; the two
-  // k-step halves of each dim tile meet in LDS ----
+  // ---- S = Q K^T for the wave's two tiles; the decoded keys go to LDS ----
+  float4_t sacc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) sacc[i] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const half8_t b = main ? key_operand<D, true>(ku[i], kk) : key_operand<D, false>(ku[i], kk);
+      sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sacc[i], 0, 0, 0);
+      if constexpr (QF32) sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sacc[i], 0, 0, 0);
+      *reinterpret_cast<half8_t *>(&L.vt[(32 * wv + 16 * i + row) * Lds::VT + quad * (D / 4) + 8 * kk]) = b;
+    }
+  }
+  // ---- split statistics: lane holds key (16*tile + row) of heads 4*quad + j ----
+  float zz[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) zz[i][j] = (ks[i] != 0.0f) ? sacc[i][j] * tau2 * ks[i] : -INFINITY;
+  // the window scale r enters P' = p * r * 2^e, with r * 2^e in [1, 2) for
+  // the split's largest r (keeps small products out of the f16 subnormals)
+  float rm = fmaxf(ks[0], ks[1]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) rm = fmaxf(rm, __shfl_xor(rm, o, 64));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float v = sum16_lanes(l_part[j]);
+    const float mx = max16_lanes(fmaxf(zz[0][j], zz[1][j]));
+    if (row == 0) L.wmax[wv][4 * quad + j] = mx;
+  }
+  __shared__ float s_rm[kSW];
+  if (l == 0) s_rm[wv] = rm;
+  __syncthreads();
+  float mx[4];
+  rm = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kSW; ++w) rm = fmaxf(rm, s_rm[w]);
+  int e = 0;
+  (void)frexpf(rm, &e);
+  e = (rm > 0.0f) ? 1 - e : 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float v = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kSW; ++w) v = fmaxf(v, L.wmax[w][4 * quad + j]);
+    mx[j] = v;
+  }
+  float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float pr = (zz[i][j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(zz[i][j] - mx[j]);
+      lp[j] += pr;
+      L.p[(4 * quad + j) * Lds::PT + 32 * wv + 16 * i + row] = (_Float16)ldexpf(pr * ks[i], e);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float v = sum16_lanes(lp[j]);
     if (row == 0) L.wsum[wv][4 * quad + j] = v;
   }
-  if (khalf == 1) L.ored[dt][l] = acc;
   __syncthreads();
-  if (khalf == 1 || 16 * dt >= DD) return;
-  acc += L.ored[dt][l];
+  // ---- O = P V for dims wv*(D/4) + 16*t over the split's 128 keys ----
+  float4_t acc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) acc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k0 = 0; k0 < kSKeys; k0 += 32) {
+    const half8_t a = *reinterpret_cast<const half8_t *>(&L.p[row * Lds::PT + k0 + 8 * quad]);
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+      const half8_t b = v_operand_tr(L.vt, Lds::VT, k0, wv * (D / 4) + 16 * t, row, quad);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+    }
+  }
+  // ---- normalised partial and its log2-domain lse (-inf: no key) ----
+  const int64_t grp = ((int64_t)m * gridDim.z + hb) * S + sp;
+  float *po = part_o + grp * (kSH * D);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int hh = 4 * quad + j, h = hb * kDH + hh;
+    const int hh = 4 * quad + j;
     float lt = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kDW; ++w) lt += L.wsum[w][hh];
-    if (h >= H) continue;
-    out[((int64_t)m * H + h) * D + d0 + 16 * dt + row] = (lt > 0.0f) ? ldexpf(acc[j] / lt, -e_cur) : 0.0f;
-    if (blockIdx.x == 0 && dt == 0 && row == 0 && lse)
-      lse[(int64_t)m * H + h] = (lt > 0.0f) ? (m_run[j] + log2f(lt)) * 0.6931471805599453f : -INFINITY;
+    for (int w = 0; w < kSW; ++w) lt += L.wsum[w][hh];
+    const float inv = (lt > 0.0f) ? ldexpf(1.0f / lt, -e) : 0.0f;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) po[hh * D + wv * (D / 4) + 16 * t + row] = acc[t][j] * inv;
+    if (wv == 0 && row == 0) part_lse[grp * kSH + hh] = (lt > 0.0f) ? mx[j] + log2f(lt) : -INFINITY;
   }
+}
+
+// Merge of the key splits by log-sum-exp: grid (queries x head blocks, D/64),
+// 256 threads; thread t combines head t/16 of the block at dims 4*(t%16) ..
+// +3 of the workgroup's 64-dim slice.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ part_o,
+                                                    const float *__restrict__ part_lse, int S, int H, int HB,
+                                                    float *__restrict__ out, float *__restrict__ lse) {
+  const int m = blockIdx.x / HB, hb = blockIdx.x % HB;
+  const int hh = threadIdx.x >> 4, d = blockIdx.y * 64 + 4 * (threadIdx.x & 15);
+  const int h = hb * kSH + hh;
+  const int64_t g0 = ((int64_t)m * HB + hb) * S;
+  float mx = -INFINITY;
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, part_lse[(g0 + s) * kSH + hh]);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float wsum = 0.0f;
+  if (mx > -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const float ls = part_lse[(g0 + s) * kSH + hh];
+      const float w = (ls == -INFINITY) ? 0.0f : exp2f(ls - mx);
+      const float4 v = *reinterpret_cast<const float4 *>(part_o + (g0 + s) * (kSH * D) + hh * D + d);
+      wsum += w;
+      o.x = fmaf(w, v.x, o.x); o.y = fmaf(w, v.y, o.y); o.z = fmaf(w, v.z, o.z); o.w = fmaf(w, v.w, o.w);
+    }
+  }
+  if (h >= H) return;
+  const float inv = (wsum > 0.0f) ? 1.0f / wsum : 0.0f;
+  *reinterpret_cast<float4 *>(out + ((int64_t)m * H + h) * D + d) = make_float4(o.x * inv, o.y * inv, o.z * inv,
+                                                                              o.w * inv);
+  if (lse && blockIdx.y == 0 && (threadIdx.x & 15) == 0)
+    lse[(int64_t)m * H + h] = (wsum > 0.0f) ? (mx + log2f(wsum)) * 0.6931471805599453f : -INFINITY;
 }
 
 // ===========================================================================
@@ -701,20 +615,39 @@ __global__ __launch_bounds__(256) void k_attn(const void *__restrict__ q_any, in
 // host side
 // ---------------------------------------------------------------------------
 
-// The fused decode kernel fills the chip when there are few queries; with
-// many queries (prefill) the flash kernel's one-workgroup-per-query grid is
-// already large and computes each logit once.
+// The split schedule fills the chip when there are few queries; with many
+// queries (prefill) the flash kernel's one-workgroup-per-query grid is
+// already large and needs no partial outputs.
 static bool use_decode_kernel(int m, int heads, int dim, int64_t max_len) {
   // its buffer descriptors span one sequence's rows: byte offsets must fit
   if (max_len * (dim / 2) >= kMaxRsrcBytes) return false;
   return (int64_t)m * ((heads + kHB - 1) / kHB) < 256;
 }
 
-// Neither schedule needs a workspace: the decode kernel keeps every key of a
-// (query, head block) in one workgroup, so there are no partial outputs.
+// Key splits of the decode schedule: 128 Top-K slots or window rows each.
+static int split_main(int top_k) { return (top_k + kSKeys - 1) / kSKeys; }
+static int split_count(int top_k, int window) { return split_main(top_k) + (window + kSKeys - 1) / kSKeys; }
+
+// Decode-schedule workspace: normalised partial outputs [query][head block]
+// [split][16][dim] and their log2-domain lse.
+struct AttnWs {
+  size_t part_o, part_lse, total;
+};
+static AttnWs attn_ws_layout(int m, int heads, int dim, int top_k, int window) {
+  const size_t groups = (size_t)m * ((heads + kSH - 1) / kSH) * split_count(top_k, window);
+  AttnWs w{};
+  size_t off = 0;
+  w.part_o = off;   off = align256(off + sizeof(float) * groups * kSH * dim);
+  w.part_lse = off; off = align256(off + sizeof(float) * groups * kSH);
+  w.total = off;
+  return w;
+}
+
+// Sized for the decode schedule whenever the query count may select it (a
+// cache too long for it falls back to the flash kernel, which needs none).
 size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int window) {
-  (void)m; (void)heads; (void)dim; (void)top_k; (void)window;
-  return 256;
+  if (!use_decode_kernel(m, heads, dim, 0)) return 256;
+  return attn_ws_layout(m, heads, dim, top_k, window).total;
 }
 
 template <int D, bool QF32>
@@ -724,10 +657,16 @@ static int attn_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, const voi
   const int W = swa.window;
   const float tau2 = scale * 1.4426950408889634f;  // log2-domain softmax: p = 2^(z - max)
   if (use_decode_kernel(qs.m, heads, D, kv.max_len)) {
-    const dim3 grid((D + kDD - 1) / kDD, qs.m, (heads + kDH - 1) / kDH);
-    CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_decode<D, QF32>), grid, dim3(64 * kDW), stream, q, heads, kv.codes,
-                      kv.scales, kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, swa.codes, swa.scale,
-                      swa.start, swa.count, W, tau2, out, lse);
+    const AttnWs L = attn_ws_layout(qs.m, heads, D, K, W);
+    float *po = reinterpret_cast<float *>(static_cast<char *>(ws) + L.part_o);
+    float *pl = reinterpret_cast<float *>(static_cast<char *>(ws) + L.part_lse);
+    const int HB = (heads + kSH - 1) / kSH;
+    const dim3 grid(split_count(K, W), qs.m, HB);
+    CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_split<D, QF32>), grid, dim3(64 * kSW), stream, q, heads, kv.codes,
+                      kv.scales, kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, split_main(K),
+                      swa.codes, swa.scale, swa.start, swa.count, W, tau2, po, pl);
+    hipLaunchKernelGGL((k_attn_merge<D>), dim3(qs.m * HB, D / 64), dim3(256), 0, stream, po, pl,
+                       split_count(K, W), heads, HB, out, lse);
   } else if (attn_prefill_supported(kv, QF32 ? CSA2_F32 : CSA2_BF16, K)) {
     return launch_attn_prefill(kv, qs, q, heads, topk, K, swa, scale, out, lse, stream);
   } else {

@@ -292,10 +292,10 @@ int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const
     const int64_t groups = rows * (dim / kGroup);
     const dim3 grid((unsigned)((groups + 255) / 256));
     if (x_dtype == CSA2_F32)
-      hipLaunchKernelGGL(k_quantize_fp4<float>, grid, dim3(256), 0, stream, (const float *)x, rows, dim, dst_row,
+      CSA2_TIMED_LAUNCH(kTimedWrite, k_quantize_fp4<float>, grid, dim3(256), stream, (const float *)x, rows, dim, dst_row,
                          codes, scales);
     else
-      hipLaunchKernelGGL(k_quantize_fp4<uint16_t>, grid, dim3(256), 0, stream, (const uint16_t *)x, rows, dim,
+      CSA2_TIMED_LAUNCH(kTimedWrite, k_quantize_fp4<uint16_t>, grid, dim3(256), stream, (const uint16_t *)x, rows, dim,
                          dst_row, codes, scales);
   } else if (rows <= 1024 && dim % (kRowThreads / idx_dim) == 0 &&
              (dim / (kRowThreads / idx_dim) == 8 || dim / (kRowThreads / idx_dim) == 16 ||
@@ -304,7 +304,7 @@ int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const
     const dim3 block((unsigned)(kGroup * (kRowThreads / idx_dim)));  // 64 .. 512
     const int per = dim / (kRowThreads / idx_dim);
 #define CSA2_ROW_LAUNCH(T, PERV)                                                                                  \
-    hipLaunchKernelGGL((k_quantize_fp4_derive_row<T, PERV>), grid, block, 0, stream, (const T *)x, dim,             \
+    CSA2_TIMED_LAUNCH(kTimedWrite, (k_quantize_fp4_derive_row<T, PERV>), grid, block, stream, (const T *)x, dim,             \
                        dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales)
     if (x_dtype == CSA2_F32) {
       if (per == 8) CSA2_ROW_LAUNCH(float, 8); else if (per == 16) CSA2_ROW_LAUNCH(float, 16);
@@ -319,7 +319,7 @@ int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const
     const dim3 grid((unsigned)((rows + rb - 1) / rb));
     const int jm = (rb + 256 / idx_dim - 1) / (256 / idx_dim);  // <= 16 since idx_dim <= dim
 #define CSA2_DERIVE_LAUNCH(T, JM)                                                                            \
-    hipLaunchKernelGGL((k_quantize_fp4_derive<T, JM>), grid, dim3(256), 0, stream, (const T *)x, rows, dim, \
+    CSA2_TIMED_LAUNCH(kTimedWrite, (k_quantize_fp4_derive<T, JM>), grid, dim3(256), stream, (const T *)x, rows, dim, \
                        dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales)
 #define CSA2_DERIVE_JM(T)                                                                 \
     if (jm <= 1) CSA2_DERIVE_LAUNCH(T, 1); else if (jm <= 2) CSA2_DERIVE_LAUNCH(T, 2);    \

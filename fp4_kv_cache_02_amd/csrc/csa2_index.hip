@@ -431,6 +431,176 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
   if (threadIdx.x == 0) pool_count[m] = need;
 }
 
+// Fused pool selection, one workgroup of 1024 threads per query (queries whose
+// blocks fit the LDS bitmap): the first scan's histogram replicas give the
+// threshold bin T (the bin holding the need-th largest block maximum,
+// need = min(P, blocks)); one pass over the block maxima sets the bitmap bit
+// of every block above T and gathers the blocks of bin T into an LDS list;
+// radix passes over that list on (key desc, block asc) below the bin's 12
+// bits pick the entries of bin T still needed; the bitmap is then compacted
+// into the ascending pool.  When bin T holds more entries than the LDS list,
+// the passes re-read the block maxima instead.
+constexpr int kPoolSelTies = 8192;
+
+__global__ __launch_bounds__(1024) void k_pool_select(const float *__restrict__ bmax, int64_t nb_stride,
+                                                      const uint32_t *__restrict__ hist, int hist_rep,
+                                                      const int32_t *__restrict__ seq_len,
+                                                      const int32_t *__restrict__ q_seq,
+                                                      const int32_t *__restrict__ q_pos, int ratio, int P,
+                                                      int32_t *__restrict__ pool_out,
+                                                      int32_t *__restrict__ pool_count) {
+  __shared__ uint32_t s_bits[kBitmapWords];
+  __shared__ uint32_t s_tkey[kPoolSelTies];
+  __shared__ int32_t s_tblk[kPoolSelTies];
+  __shared__ uint32_t s_h[256];
+  __shared__ int s_scan[17];
+  __shared__ int s_T, s_above, s_nT, s_ntie, s_digit, s_rem, s_cnt;
+  const int m = blockIdx.x, tid = threadIdx.x;
+  int s;
+  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
+  const int nb = (int)((vis + kBlock - 1) / kBlock);   // <= 32 * kBitmapWords (checked on the host)
+  const int need = min(P, nb);
+  const int words = (nb + 31) / 32;
+  // ---- threshold bin: thread t holds bins [4096 - 4(t+1), 4096 - 4t), every
+  // replica's loads in flight at once ----
+  const int bin0 = kHistBins - 4 * (tid + 1);
+  uint4 x[kHistMaxReplicas];
+#pragma unroll
+  for (int r = 0; r < kHistMaxReplicas; ++r) {
+    const int rr = r < hist_rep ? r : 0;
+    x[r] = *reinterpret_cast<const uint4 *>(hist + ((int64_t)m * hist_rep + rr) * kHistBins + bin0);
+  }
+  uint32_t hv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int r = 0; r < kHistMaxReplicas; ++r) {
+    if (r >= hist_rep) continue;
+    hv[0] += x[r].x; hv[1] += x[r].y; hv[2] += x[r].z; hv[3] += x[r].w;
+  }
+  const int c = (int)(hv[0] + hv[1] + hv[2] + hv[3]);
+  if (tid == 0) { s_T = -1; s_above = 0; s_nT = 0; s_ntie = 0; }
+  for (int i = tid; i < words; i += 1024) s_bits[i] = 0u;
+  int tot;
+  const int before = block_exclusive_scan<1024>(c, s_scan, &tot);   // blocks in higher bins
+  if (nb > P && before < need && before + c >= need) {
+    int cum = before;
+    for (int k = 3; k >= 0; --k) {
+      if (cum + (int)hv[k] >= need) { s_T = bin0 + k; s_above = cum; s_nT = (int)hv[k]; break; }
+      cum += (int)hv[k];
+    }
+  }
+  __syncthreads();
+  const int T = s_T, rem_t = need - s_above, nT = s_nT;
+  const bool all_t = T < 0 || rem_t >= nT;              // every block of bin T is taken
+  const bool in_lds = !all_t && nT <= kPoolSelTies;
+  // ---- filter: thread t owns bitmap words t, t + 1024, ... (32 blocks each),
+  // two words' loads in flight per round ----
+  const float *bm = bmax + (int64_t)m * nb_stride;
+  for (int w0 = 0; w0 < words; w0 += 2048) {
+    float4 v[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int w = min(w0 + tid + 1024 * u, words - 1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[u][k] = *reinterpret_cast<const float4 *>(bm + 32 * w + 4 * k);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int w = w0 + tid + 1024 * u;
+      if (w >= words) continue;
+      uint32_t bits = 0u;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float e4[4] = {v[u][k].x, v[u][k].y, v[u][k].z, v[u][k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int b = 32 * w + 4 * k + e;
+          if (b >= nb) continue;
+          const uint32_t key = f2key(e4[e]);
+          const int bin = (int)(key >> (32 - kHistBits));
+          if (T < 0 || bin > T || (bin == T && all_t)) {
+            bits |= 1u << (4 * k + e);
+          } else if (bin == T && in_lds) {
+            const int slot = atomicAdd(&s_ntie, 1);
+            if (slot < kPoolSelTies) { s_tkey[slot] = key; s_tblk[slot] = b; }
+          }
+        }
+      }
+      s_bits[w] = bits;
+    }
+  }
+  __syncthreads();
+  // ---- the rem_t best blocks of bin T on (key desc, block asc): composite
+  // c = key << 32 | ~block, top kHistBits bits known ----
+  if (!all_t) {
+    const int ntie = in_lds ? min(s_ntie, kPoolSelTies) : 0;
+    auto composite = [](uint32_t key, int32_t b) { return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)b); };
+    uint64_t prefix = (uint64_t)T << (64 - kHistBits);
+    uint64_t mask = ((1ull << kHistBits) - 1ull) << (64 - kHistBits);
+    int rem = rem_t;
+    for (int hi = 64 - kHistBits; hi > 0; hi -= 8) {
+      const int width = hi < 8 ? hi : 8;
+      const int shift = hi - width;
+      const uint64_t dmask = (1ull << width) - 1ull;
+      for (int i = tid; i < 256; i += 1024) s_h[i] = 0u;
+      __syncthreads();
+      if (in_lds) {
+        for (int i = tid; i < ntie; i += 1024) {
+          const uint64_t cc = composite(s_tkey[i], s_tblk[i]);
+          if ((cc & mask) == prefix) atomicAdd(&s_h[(cc >> shift) & dmask], 1u);
+        }
+      } else {
+        for (int b = tid; b < nb; b += 1024) {
+          const uint64_t cc = composite(f2key(bm[b]), b);
+          if ((cc & mask) == prefix) atomicAdd(&s_h[(cc >> shift) & dmask], 1u);
+        }
+      }
+      __syncthreads();
+      find_digit(s_h, rem, &s_digit, &s_rem, &s_cnt);
+      __syncthreads();
+      prefix |= (uint64_t)s_digit << shift;
+      mask |= dmask << shift;
+      rem = s_rem;
+      if (s_cnt == rem) break;   // every entry left in the cut's bin is taken
+    }
+    if (in_lds) {
+      for (int i = tid; i < ntie; i += 1024) {
+        const int32_t b = s_tblk[i];
+        if ((composite(s_tkey[i], b) & mask) >= prefix) atomicOr(&s_bits[b >> 5], 1u << (b & 31));
+      }
+    } else {
+      const uint64_t tmask = ((1ull << kHistBits) - 1ull) << (64 - kHistBits);
+      const uint64_t tpre = (uint64_t)T << (64 - kHistBits);
+      for (int b = tid; b < nb; b += 1024) {
+        const uint64_t cc = composite(f2key(bm[b]), b);
+        if ((cc & tmask) == tpre && (cc & mask) >= prefix) atomicOr(&s_bits[b >> 5], 1u << (b & 31));
+      }
+    }
+  }
+  __syncthreads();
+  // ---- compaction: thread t takes words [t*wpt, (t+1)*wpt) ----
+  int32_t *out = pool_out + (int64_t)m * P;
+  const int wpt = (words + 1023) / 1024;
+  int cnt = 0;
+  for (int k = 0; k < wpt; ++k) {
+    const int w = tid * wpt + k;
+    if (w < words) cnt += __popc(s_bits[w]);
+  }
+  int pos = block_exclusive_scan<1024>(cnt, s_scan, &tot);
+  for (int k = 0; k < wpt; ++k) {
+    const int w = tid * wpt + k;
+    if (w >= words) break;
+    uint32_t bits = s_bits[w];
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (pos < P) out[pos] = w * 32 + bit;
+      ++pos;
+    }
+  }
+  for (int i = min(tot, P) + tid; i < P; i += 1024) out[i] = -1;
+  if (tid == 0) pool_count[m] = min(tot, need);
+}
+
 // Re-score the positions of E pool blocks per workgroup (E = 64, or fewer
 // when that leaves most of the chip idle).  Slot 8*e + r of a query holds
 // the score of position 8*pool[e] + r (-inf when not visible).  Each wave
@@ -757,13 +927,19 @@ static int index_full_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
     }
 #undef CSA2_SCAN
   }
-  hipLaunchKernelGGL(k_hist_threshold, dim3(qs.m), dim3(256), 0, stream, hist, L.hist_rep, idx.seq_len, qs.seq,
-                     qs.pos, idx.ratio, P, counters);
-  const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);
-  hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, idx.seq_len, qs.seq, qs.pos,
-                     idx.ratio, P, counters, sure, tie);
-  hipLaunchKernelGGL(k_pool_finalize, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, counters, sure, tie,
-                     idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
+  if ((idx.max_len + kBlock - 1) / kBlock <= 32 * (int64_t)kBitmapWords) {
+    hipLaunchKernelGGL(k_pool_select, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, hist, L.hist_rep,
+                       idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
+  } else {
+    // more blocks than the bitmap holds: threshold, filter into global lists, finalise
+    hipLaunchKernelGGL(k_hist_threshold, dim3(qs.m), dim3(256), 0, stream, hist, L.hist_rep, idx.seq_len, qs.seq,
+                       qs.pos, idx.ratio, P, counters);
+    const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);
+    hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, idx.seq_len, qs.seq, qs.pos,
+                       idx.ratio, P, counters, sure, tie);
+    hipLaunchKernelGGL(k_pool_finalize, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, counters, sure, tie,
+                       idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
+  }
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
   return rescore_and_select<DI>(idx, qs, q_idx, w_idx, heads, pool_out, pool_count, P, K, topk_out, topk_score,
                                 pscore, stream);

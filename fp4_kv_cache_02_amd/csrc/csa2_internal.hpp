@@ -71,11 +71,11 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---- kernel timing (csa2_api.hip) ----
 // Timed kernels: the first scan of an index call (decode scan or prefill
-// scoring) and each attention launch.  timing_events hands out a fresh
+// scoring), each attention launch and each quantise-on-write launch.  timing_events hands out a fresh
 // start/stop pair when that timing is on (both null otherwise); launched with
 // hipExtLaunchKernelGGL, the pair takes the dispatch's own start and end
 // times, so no marker packets sit between the events and the kernel.
-enum TimedKernel { kTimedScan = 0, kTimedAttn = 1 };
+enum TimedKernel { kTimedScan = 0, kTimedAttn = 1, kTimedWrite = 2 };
 void timing_events(int which, hipEvent_t *start, hipEvent_t *stop);
 
 #define CSA2_TIMED_LAUNCH(which, kernel, grid, block, stream, ...)                                  \

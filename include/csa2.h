@@ -317,6 +317,14 @@ int32_t csa2_profile_scan_read(double *total_ms, int64_t *launches);
 int32_t csa2_profile_attn(int32_t enable);
 int32_t csa2_profile_attn_read(double *total_ms, int64_t *launches);
 
+/* csa2_profile_write / csa2_profile_write_read - the same timing for every
+ * FP4 quantise-on-write kernel launched by csa2_quantize_fp4 /
+ * csa2_group_step (one launch per call or Full group with new rows; the FP8
+ * window write is not included).  Same contract and errors as
+ * csa2_profile_scan. */
+int32_t csa2_profile_write(int32_t enable);
+int32_t csa2_profile_write_read(double *total_ms, int64_t *launches);
+
 #ifdef __cplusplus
 }
 #endif
