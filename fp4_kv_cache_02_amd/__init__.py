@@ -17,13 +17,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so"
 CSA2_OK = 0
 CSA2_F32, CSA2_BF16 = 0, 1
 CSA2_MODE_FULL, CSA2_MODE_REINDEX = 0, 1
+CSA2_STATIC_SCRATCH_BYTES = 64 << 20   # include/csa2.h
 
 EXPORTS = [
     "csa2_abi_version", "csa2_status_string", "csa2_quantize_fp4", "csa2_quantize_fp8_rows",
     "csa2_dequant_fp4", "csa2_index_workspace_size", "csa2_index_full", "csa2_reindex",
     "csa2_attn_workspace_size", "csa2_sparse_swa_attn", "csa2_group_workspace_size", "csa2_group_step",
     "csa2_profile_scan", "csa2_profile_scan_read", "csa2_profile_attn", "csa2_profile_attn_read",
-    "csa2_profile_write", "csa2_profile_write_read",
+    "csa2_profile_write", "csa2_profile_write_read", "csa2_group_step_static",
 ]
 
 
@@ -95,6 +96,7 @@ def lib() -> ctypes.CDLL:
             "csa2_profile_attn_read": (i32, [POINTER(ctypes.c_double), POINTER(c_int64)]),
             "csa2_profile_write": (i32, [i32]),
             "csa2_profile_write_read": (i32, [POINTER(ctypes.c_double), POINTER(c_int64)]),
+            "csa2_group_step_static": (i32, [POINTER(GroupDesc), vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -284,6 +286,11 @@ def csa2_group_step(group: Group, workspace, stream=None):
     _check(lib().csa2_group_step(ctypes.byref(group.desc), _ptr(workspace),
                                  int(workspace.numel()) if workspace is not None else 0, _stream(stream)),
            "csa2_group_step")
+
+
+def csa2_group_step_static(group: Group, stream=None):
+    """csa2_group_step on the library's own scratch array (no workspace argument)."""
+    _check(lib().csa2_group_step_static(ctypes.byref(group.desc), _stream(stream)), "csa2_group_step_static")
 
 
 def csa2_profile_scan(enable: bool) -> None:

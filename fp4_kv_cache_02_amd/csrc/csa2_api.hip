@@ -2,6 +2,7 @@
 // dispatch.  Every check runs before anything is enqueued.
 #include "csa2_internal.hpp"
 
+#include <mutex>
 #include <vector>
 
 using namespace csa2;
@@ -322,6 +323,46 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
     if (st) return st;
   }
   return CSA2_OK;
+}
+
+// ---------------------------------------------------------------------------
+// csa2_group_step_static: the group step on a library-owned scratch array
+// ---------------------------------------------------------------------------
+// One copy per GPU, held until the process ends.  In host code `scratch` is a
+// host-side stand-in for the device symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[CSA2_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device
+
+int static_scratch(void **ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CSA2_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return CSA2_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CSA2_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return CSA2_OK;
+}
+}  // namespace
+
+int32_t csa2_group_step_static(const csa2_group_desc *g, void *stream) {
+  if (!g) return CSA2_ERR_NULL_ARG;
+  size_t need = 0;
+  int st = csa2_group_workspace_size(g, &need);
+  if (st) return st;
+  if (need > (size_t)CSA2_STATIC_SCRATCH_BYTES) return CSA2_ERR_WORKSPACE;
+  void *p = nullptr;
+  if ((st = static_scratch(&p))) return st;
+  // the scratch needs no initial contents: every call clears what it counts into
+  return csa2_group_step(g, p, (size_t)CSA2_STATIC_SCRATCH_BYTES, stream);
 }
 
 int32_t csa2_profile_scan(int32_t enable) {

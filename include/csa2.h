@@ -292,6 +292,27 @@ int32_t csa2_group_workspace_size(const csa2_group_desc *g, size_t *bytes);
 int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------
+ * csa2_group_step_static - csa2_group_step without a caller workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Runs exactly csa2_group_step(g, scratch, CSA2_STATIC_SCRATCH_BYTES,
+ * stream) on a scratch array the library owns: one copy of
+ * CSA2_STATIC_SCRATCH_BYTES per GPU, held from the first call on that GPU
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine) and needs no initial scratch contents.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and must be ordered
+ * by the caller, e.g. on one stream.
+ * Errors: those of csa2_group_step; CSA2_ERR_WORKSPACE when the group's
+ * csa2_group_workspace_size exceeds CSA2_STATIC_SCRATCH_BYTES (large prefill
+ * chunks do; decode batches of a few dozen sequences at 1M entries fit);
+ * CSA2_ERR_HIP if the scratch address cannot be obtained.
+ * ------------------------------------------------------------------- */
+#define CSA2_STATIC_SCRATCH_BYTES (64u << 20)
+int32_t csa2_group_step_static(const csa2_group_desc *g, void *stream);
+
+/* ---------------------------------------------------------------------
  * csa2_profile_scan / csa2_profile_scan_read - timing of the Full layer's
  * first scan (the step whose cost grows with the context, P4 section 二):
  * the decoder's scan over every visible entry, or the multi-query scoring

@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = csa2.lib()
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     assert sorted(names) == sorted(csa2.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", csa2.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (csa2_\w+)$", out, re.M))
