@@ -102,27 +102,34 @@ class DecodeWorkload:
         max_len = int(lens.max())
         self.kv = csa2.fp4_cache(self.kv_codes, self.kv_scales, seq_start, seq_len, D, max_len, wl.ratio)
         self.idx = csa2.fp4_cache(self.ik_codes, self.ik_scales, seq_start, seq_len, DI, max_len, wl.ratio)
-        M = S
+        # T tokens per sequence (the last T of each), one query each, in runs per sequence
+        T = int(wl.extra.get("tokens_per_seq", 1))
+        self.T = T
+        M = S * T
         self.M = M
-        self.q_pos_host = (lens - 1).astype(np.int32)
-        self.qs = csa2.queries(torch.arange(M, dtype=torch.int32, device=dev),
-                               torch.from_numpy(self.q_pos_host).to(dev))
-        # the decode token's own entry (position len-1) is (re)written by the Full group
-        new = np.stack([synth.main_kv_rows(wl.cfg, s, int(lens[s]) - 1, 1, D)[0] for s in range(S)])
+        q_seq = np.repeat(np.arange(S), T).astype(np.int32)
+        self.q_seq_host = q_seq
+        self.q_pos_host = (np.repeat(lens, T) - T + np.tile(np.arange(T), S)).astype(np.int32)
+        self.qs = csa2.queries(torch.from_numpy(q_seq).to(dev), torch.from_numpy(self.q_pos_host).to(dev), run=T)
+        # the tokens' own entries (positions len-T .. len-1) are (re)written by the Full group
+        new = np.concatenate([synth.main_kv_rows(wl.cfg, s, int(lens[s]) - T, T, D) for s in range(S)])
         self.new_kv = torch.from_numpy(new).to(dev)
-        self.new_dst = torch.from_numpy(starts + lens - 1).to(dev)
+        self.new_dst = torch.from_numpy(np.repeat(starts + lens, T) - T + np.tile(np.arange(T), S)).to(dev)
         self.w_ik = w_ik
         # per-layer queries, window rows and outputs
         L, H, W = wl.n_layers, wl.heads, wl.window
         self.q, self.swa, self.out, self.lse = [], [], [], []
-        swa_start = torch.from_numpy((np.arange(M) * W).astype(np.int32)).to(dev)
-        swa_count = torch.from_numpy(np.minimum(W, lens).astype(np.int32)).to(dev)
+        # window rows: per sequence the W + T - 1 rows ending at its last token; token k of a
+        # run sees the W rows ending at itself
+        NW = W + T - 1
+        swa_start = torch.from_numpy((np.repeat(np.arange(S) * NW, T) + np.tile(np.arange(T), S)).astype(np.int32)).to(dev)
+        swa_count = torch.from_numpy(np.minimum(W, self.q_pos_host.astype(np.int64) + 1).astype(np.int32)).to(dev)
         for layer in range(L):
             qb = synth.q_main(wl.cfg, layer, M, H, D, "bf16")
             self.q.append(torch.from_numpy(qb.view(np.int16)).to(dev).view(torch.bfloat16))
-            rows = np.concatenate([synth.swa_rows(wl.cfg, layer, s, W, D) for s in range(M)])
-            sc = torch.empty((M * W, D), **u8)
-            ss = torch.empty((M * W,), dtype=torch.float32, device=dev)
+            rows = np.concatenate([synth.swa_rows(wl.cfg, layer, s, NW, D) for s in range(S)])
+            sc = torch.empty((S * NW, D), **u8)
+            ss = torch.empty((S * NW,), dtype=torch.float32, device=dev)
             csa2.csa2_quantize_fp8_rows(torch.from_numpy(rows).to(dev), sc, ss)
             self.swa.append(csa2.swa(sc, ss, swa_start, swa_count, D, W))
             self.out.append(torch.empty((M, H, D), dtype=torch.float32, device=dev))
@@ -165,10 +172,14 @@ class DecodeWorkload:
 
     # algorithmic bytes
     def scan_bytes_per_launch(self) -> int:
+        # each sequence's visible indexer rows once (the tokens of a run share them)
         wl = self.wl
         row = wl.idx_dim // 2 + wl.idx_dim // 16
-        vis = np.minimum(np.asarray(wl.seq_lens), (self.q_pos_host + 1) // wl.ratio)
-        return int(vis.sum()) * row
+        lens = np.asarray(wl.seq_lens)
+        vis = np.minimum(lens[self.q_seq_host], (self.q_pos_host.astype(np.int64) + 1) // wl.ratio)
+        per_seq = np.zeros(len(lens), np.int64)
+        np.maximum.at(per_seq, self.q_seq_host, vis)
+        return int(per_seq.sum()) * row
 
     def attn_bytes_per_launch(self) -> int:
         # one layer's attention: selected main rows, window rows, bf16 queries, fp32 outputs and lse
@@ -182,7 +193,8 @@ class DecodeWorkload:
         D, H, W, K, P = wl.dim, wl.heads, wl.window, wl.top_k, wl.pool_blocks
         idx_row = wl.idx_dim // 2 + wl.idx_dim // 16
         kv_row = D // 2 + D // 16
-        vis = np.minimum(np.asarray(wl.seq_lens), (self.q_pos_host + 1) // wl.ratio)
+        lens = np.asarray(wl.seq_lens)
+        vis = np.minimum(lens[self.q_seq_host], (self.q_pos_host.astype(np.int64) + 1) // wl.ratio)
         n_sel = sum(1 for g in wl.groups)                                # Full + Reindex selections
         pool_pos = np.minimum(vis, 8 * P)
         sel = int(n_sel * pool_pos.sum()) * idx_row
@@ -190,6 +202,148 @@ class DecodeWorkload:
         attn = wl.n_layers * self.M * attn_per_q
         write = self.M * (D * 4 + kv_row + idx_row)
         return self.scan_bytes_per_launch() + sel + attn + write
+
+
+class CedDecodeWorkload:
+    """One decode token per sequence through the whole encoder-decoder: the
+    encoder's 2 window-only layers, its 3 CSA2 groups (Full + 5 Reuse) at
+    ratio 2 over the tokens' compressed entries (each Full layer with its own
+    caches, writing the entry the token completes; the flat Top-K is taken
+    from a pool of K blocks, which holds every flat Top-K position), then the
+    20-layer decoder."""
+
+    def __init__(self, wl, torch, csa2, synth):
+        self.wl, self.torch, self.csa2 = wl, torch, csa2
+        dev = torch.device("cuda:0")
+        self.dec = DecodeWorkload(wl, torch, csa2, synth)
+        ex = wl.extra
+        S, D, DI, H, W, K = len(wl.seq_lens), wl.dim, wl.idx_dim, wl.heads, wl.window, wl.top_k
+        r = ex["encoder_ratio"]
+        tokens = np.asarray(wl.seq_lens, np.int64)          # the decode token is token len-1
+        elens = tokens // r                                 # entries complete at that token
+        self.elens = elens
+        starts = np.concatenate([[0], np.cumsum(elens)[:-1]]).astype(np.int64)
+        R = int(elens.sum())
+        u8 = dict(dtype=torch.uint8, device=dev)
+        w_ik = torch.from_numpy(synth.w_ik(wl.cfg + 100, D, DI)).to(dev)
+        seq_start = torch.from_numpy(starts).to(dev)
+        seq_len = torch.from_numpy(elens.astype(np.int32)).to(dev)
+        qs = self.dec.qs                                    # same tokens: pos = len - 1
+        M = self.dec.M
+        P = ex["encoder_pool_blocks"]
+        self.enc_groups, self.enc_tensors = [], []
+        swa_start = torch.from_numpy((np.arange(M) * W).astype(np.int32)).to(dev)
+        swa_count = torch.from_numpy(np.minimum(W, tokens).astype(np.int32)).to(dev)
+
+        def layer_tensors(layer):
+            qb = synth.q_main(wl.cfg, layer, M, H, D, "bf16")
+            q = torch.from_numpy(qb.view(np.int16)).to(dev).view(torch.bfloat16)
+            rows = np.concatenate([synth.swa_rows(wl.cfg, layer, s, W, D) for s in range(M)])
+            sc = torch.empty((M * W, D), **u8)
+            ss = torch.empty((M * W,), dtype=torch.float32, device=dev)
+            csa2.csa2_quantize_fp8_rows(torch.from_numpy(rows).to(dev), sc, ss)
+            sw = csa2.swa(sc, ss, swa_start, swa_count, D, W)
+            return q, sw, torch.empty((M, H, D), dtype=torch.float32, device=dev), \
+                torch.empty((M, H), dtype=torch.float32, device=dev)
+
+        # encoder layers 0-1: window only
+        self.swa_only = [layer_tensors(100 + l) for l in range(ex["swa_only_layers"])]
+        layer = 100 + ex["swa_only_layers"]
+        for gi, modes in enumerate(ex["encoder_groups"]):
+            kc, ks = torch.empty((R, D // 2), **u8), torch.empty((R, D // 16), **u8)
+            ic, is_ = torch.empty((R, DI // 2), **u8), torch.empty((R, DI // 16), **u8)
+            chunk = 1 << 20
+            for s in range(S):
+                for c0 in range(0, int(elens[s]), chunk):
+                    n = min(chunk, int(elens[s]) - c0)
+                    x = torch.from_numpy(synth.main_kv_rows(wl.cfg + 100 + gi, s, c0, n, D)).to(dev)
+                    r0 = int(starts[s]) + c0
+                    csa2.csa2_quantize_fp4(x, kc[r0:r0 + n], ks[r0:r0 + n], w_ik=w_ik, ik_codes=ic[r0:r0 + n],
+                                           ik_scales=is_[r0:r0 + n])
+                    del x
+            kv = csa2.fp4_cache(kc, ks, seq_start, seq_len, D, int(elens.max()), r)
+            idx = csa2.fp4_cache(ic, is_, seq_start, seq_len, DI, int(elens.max()), r)
+            new = np.stack([synth.main_kv_rows(wl.cfg + 100 + gi, s, int(elens[s]) - 1, 1, D)[0] for s in range(S)])
+            new_kv = torch.from_numpy(new).to(dev)
+            new_dst = torch.from_numpy(starts + elens - 1).to(dev)
+            lt = [layer_tensors(layer + i) for i in range(len(modes))]
+            qi = synth.q_idx(wl.cfg, layer, M, wl.idx_heads, DI)
+            wi = synth.w_idx(wl.cfg, layer, M, wl.idx_heads)
+            topk = torch.empty((M, K), dtype=torch.int32, device=dev)
+            pool = torch.empty((M, P), dtype=torch.int32, device=dev)
+            cnt = torch.empty((M,), dtype=torch.int32, device=dev)
+            g = csa2.Group(csa2.CSA2_MODE_FULL, kv, idx, qs,
+                           torch.from_numpy(qi.view(np.int16)).to(dev).view(torch.bfloat16),
+                           torch.from_numpy(wi).to(dev), P, K, pool, cnt, topk, None,
+                           [t[0] for t in lt], csa2.CSA2_BF16, H, [t[1] for t in lt], [t[2] for t in lt],
+                           [t[3] for t in lt], D ** -0.5, new_kv=new_kv, new_dst_row=new_dst, w_ik=w_ik)
+            g.topk_tensor = topk
+            self.enc_groups.append(g)
+            self.enc_tensors.append((kc, ks, ic, is_, new_kv, new_dst, lt))
+            layer += len(modes)
+        ws_bytes = max([csa2.csa2_group_workspace_size(g) for g in self.enc_groups] +
+                       [csa2.csa2_attn_workspace_size(M, H, D, 0, W), self.dec.ws.numel()])
+        self.ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)  # zero before first use
+        self.M = M
+        self.q_pos_host = self.dec.q_pos_host
+        torch.cuda.synchronize()
+
+    def step(self):
+        csa2, dec = self.csa2, self.dec
+        for q, sw, out, lse in self.swa_only:
+            csa2.csa2_sparse_swa_attn(dec.kv, dec.qs, q, None, 0, sw, self.wl.dim ** -0.5, out, lse, self.ws)
+        for g in self.enc_groups:
+            csa2.csa2_group_step(g, self.ws)
+        for g in dec.groups:
+            csa2.csa2_group_step(g, self.ws)
+
+    def snapshot(self):
+        t = self.torch
+        a = self.dec.snapshot()
+        enc = [g.topk_tensor.clone() for g in self.enc_groups]
+        outs = [o.clone() for _, _, o, _ in self.swa_only] + [lt[2].clone() for e in self.enc_tensors for lt in e[6]]
+        return (a[0] + enc, a[1], a[2] + outs, a[3])
+
+    def scan_bytes_per_launch(self) -> int:
+        # averaged over the step's first scans: the decoder's and the encoder groups'
+        wl = self.wl
+        idx_row = wl.idx_dim // 2 + wl.idx_dim // 16
+        n_enc = len(wl.extra["encoder_groups"])
+        return (self.dec.scan_bytes_per_launch() + n_enc * int(self.elens.sum()) * idx_row) // (1 + n_enc)
+
+    def attn_bytes_per_launch(self) -> int:
+        # averaged over the step's attention launches (the window-only ones read no selected rows)
+        wl = self.wl
+        ex = wl.extra
+        D, H, W = wl.dim, wl.heads, wl.window
+        n_sparse = wl.n_layers + sum(len(g) for g in ex["encoder_groups"])
+        swa_per_q = W * (D + 4) + H * D * 2 + H * D * 4 + H * 4
+        tot = n_sparse * self.dec.attn_bytes_per_launch() + ex["swa_only_layers"] * self.M * swa_per_q
+        return tot // (n_sparse + ex["swa_only_layers"])
+
+    def step_bytes(self) -> int:
+        wl = self.wl
+        D, H, W, K = wl.dim, wl.heads, wl.window, wl.top_k
+        ex = wl.extra
+        idx_row = wl.idx_dim // 2 + wl.idx_dim // 16
+        kv_row = D // 2 + D // 16
+        attn_per_q = K * kv_row + W * (D + 4) + H * D * 2 + H * D * 4 + H * 4
+        swa_per_q = W * (D + 4) + H * D * 2 + H * D * 4 + H * 4
+        n_enc_layers = sum(len(g) for g in ex["encoder_groups"])
+        enc = 0
+        for _ in ex["encoder_groups"]:
+            enc += int(self.elens.sum()) * idx_row                              # first scan
+            enc += self.M * 8 * ex["encoder_pool_blocks"] * idx_row             # re-score of the pool
+            enc += self.M * (D * 4 + kv_row + idx_row)                          # write path
+        enc += n_enc_layers * self.M * attn_per_q + ex["swa_only_layers"] * self.M * swa_per_q
+        return self.dec.step_bytes() + enc
+
+    def cache_bytes_per_token(self) -> float:
+        # global (FP4) entries per token: the decoder's at ratio 1, each encoder Full layer's at its ratio
+        wl = self.wl
+        row = wl.dim // 2 + wl.dim // 16 + wl.idx_dim // 2 + wl.idx_dim // 16
+        ex = wl.extra
+        return row + len(ex["encoder_groups"]) * row / ex["encoder_ratio"]
 
 
 class PrefillWorkload:
@@ -701,6 +855,30 @@ def main():
                 extras[f"{wx.name}/{mode}"] = r
             del Wx
             torch.cuda.empty_cache()
+        for cfg in (6, 7):
+            wx = synth.workload(cfg)
+            Wx, _ = setup_decode(wx, torch, csa2, synth)
+            ktx = kernel_times(torch, csa2, Wx, args.steps)
+            msx, _ = time_steps(torch, Wx, args.steps, args.warmup, "graph")
+            r = decode_record(wx, Wx, msx, ktx, "graph")
+            r["tokens_per_sequence"] = Wx.T
+            r["scan_bytes_per_token"] = Wx.scan_bytes_per_launch() / Wx.M
+            r["roofline"]["kernel"] = "first scan (k_score_mq: every row scored against the run's tokens)"
+            extras[f"{wx.name}/graph"] = r
+            del Wx
+            torch.cuda.empty_cache()
+        wc = synth.workload(5)
+        t0 = time.time()
+        Wc = CedDecodeWorkload(wc, torch, csa2, synth)
+        print(f"[bench] setup {time.time() - t0:.1f}s: {wc.name}", file=sys.stderr, flush=True)
+        ktc = kernel_times(torch, csa2, Wc, args.steps)
+        msc, _ = time_steps(torch, Wc, args.steps, args.warmup, "graph")
+        rc = decode_record(wc, Wc, msc, ktc, "graph")
+        rc["layers"] = "2 window-only + 3x(Full+5Reuse) at ratio 2 + decoder 20"
+        rc["global_cache_bytes_per_token"] = Wc.cache_bytes_per_token()
+        extras[f"{wc.name}/graph"] = rc
+        del Wc
+        torch.cuda.empty_cache()
         wp = synth.workload(2)
         pre = run_prefill(args, wp, torch, csa2, synth)
         extras[wp.name] = {k: pre[k] for k in ("metric", "value", "unit", "ms_per_step", "config", "roofline",

@@ -18,6 +18,7 @@ CSA2_OK = 0
 CSA2_F32, CSA2_BF16 = 0, 1
 CSA2_MODE_FULL, CSA2_MODE_REINDEX = 0, 1
 CSA2_STATIC_SCRATCH_BYTES = 64 << 20   # include/csa2.h
+CSA2_ATTN_COUNTER_BYTES = 4096          # include/csa2.h
 
 EXPORTS = [
     "csa2_abi_version", "csa2_status_string", "csa2_quantize_fp4", "csa2_quantize_fp8_rows",
@@ -40,7 +41,7 @@ class Fp4Cache(ctypes.Structure):
 
 
 class Queries(ctypes.Structure):
-    _fields_ = [("seq", c_void_p), ("pos", c_void_p), ("m", c_int32)]
+    _fields_ = [("seq", c_void_p), ("pos", c_void_p), ("m", c_int32), ("run", c_int32)]
 
 
 class Swa(ctypes.Structure):
@@ -154,8 +155,9 @@ def fp4_cache(codes, scales, seq_start, seq_len, dim: int, max_len: int, ratio: 
     return c
 
 
-def queries(seq, pos) -> Queries:
-    q = Queries(_ptr(seq), _ptr(pos), int(seq.numel()))
+def queries(seq, pos, run: int = 1) -> Queries:
+    """Queries (device int32 tensors); `run` = queries per run of one sequence (a schedule hint)."""
+    q = Queries(_ptr(seq), _ptr(pos), int(seq.numel()), int(run))
     q._keep = (seq, pos)
     return q
 

@@ -69,7 +69,7 @@ int check_cache(const csa2_fp4_cache *c, bool need_dim32) {
 
 int check_queries(const csa2_queries *q) {
   if (!q) return CSA2_ERR_NULL_ARG;
-  if (q->m < 0) return CSA2_ERR_BAD_SHAPE;
+  if (q->m < 0 || q->run < 0) return CSA2_ERR_BAD_SHAPE;
   if (q->m > 0 && (!q->seq || !q->pos)) return CSA2_ERR_NULL_ARG;
   if (q->m > 65535) return CSA2_ERR_UNSUPPORTED;
   return CSA2_OK;
@@ -245,11 +245,20 @@ int32_t csa2_sparse_swa_attn(const csa2_fp4_cache *kv, const csa2_queries *qs, c
                      (hipStream_t)stream);
 }
 
-// Group workspace: the indexer's region, then the attention region (whose
-// arrival counters must keep their zeros between calls, so the indexer never
-// writes there).
-static size_t group_attn_offset(const csa2_group_desc *g) {
-  return align256(index_bytes(&g->idx, g->qs.m, g->pool_blocks, g->top_k));
+// Group workspace: the attention region at offset 0 (its arrival counters sit
+// in the first kAttnCounterBytes of every group workspace whatever the group's
+// shape, so calls of different shapes on one workspace all find them zero),
+// then the indexer's region, which every index call initialises itself.
+static_assert(kAttnCounterBytes == CSA2_ATTN_COUNTER_BYTES, "counter region of the header");
+
+static size_t group_index_offset(const csa2_group_desc *g) {
+  size_t b = kAttnCounterBytes;
+  for (int i = 0; i < g->n_layers; ++i) {
+    const int w = g->swa ? g->swa[i].window : 0;
+    const size_t x = attn_ws_bytes(g->qs.m > 0 ? g->qs.m : 1, g->heads, g->kv.dim, g->top_k, w);
+    if (x > b) b = x;
+  }
+  return align256(b);
 }
 
 int32_t csa2_group_workspace_size(const csa2_group_desc *g, size_t *bytes) {
@@ -257,13 +266,7 @@ int32_t csa2_group_workspace_size(const csa2_group_desc *g, size_t *bytes) {
   if (g->qs.m < 0 || g->n_layers < 1 || g->heads < 1 || g->top_k < 1 || g->pool_blocks < 0)
     return CSA2_ERR_BAD_SHAPE;
   if (g->pool_blocks > 4096 || g->top_k > 2048) return CSA2_ERR_UNSUPPORTED;
-  size_t b = 256;
-  for (int i = 0; i < g->n_layers; ++i) {
-    const int w = g->swa ? g->swa[i].window : 0;
-    const size_t x = attn_ws_bytes(g->qs.m > 0 ? g->qs.m : 1, g->heads, g->kv.dim, g->top_k, w);
-    if (x > b) b = x;
-  }
-  *bytes = group_attn_offset(g) + b;
+  *bytes = group_index_offset(g) + align256(index_bytes(&g->idx, g->qs.m, g->pool_blocks, g->top_k));
   return CSA2_OK;
 }
 
@@ -299,6 +302,7 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
   }
   if (g->qs.m == 0) return CSA2_OK;
   hipStream_t s = (hipStream_t)stream;
+  void *iws = static_cast<char *>(workspace) + group_index_offset(g);
   if (g->first_mode == CSA2_MODE_FULL && g->new_rows > 0) {
     st = launch_quantize_fp4(g->new_kv, g->new_kv_dtype, g->new_rows, g->kv.dim, g->new_dst_row, g->kv.codes,
                              g->kv.scales, g->w_ik, g->idx.dim, g->idx.codes, g->idx.scales, s);
@@ -307,19 +311,18 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
   if (g->first_mode == CSA2_MODE_FULL) {
     if (g->pool_blocks == 0)
       st = launch_index_flat(g->idx, g->qs, g->q_idx, g->w_idx, g->idx_heads, g->top_k, g->topk, g->topk_score,
-                             workspace, s);
+                             iws, s);
     else
       st = launch_index_full(g->idx, g->qs, g->q_idx, g->w_idx, g->idx_heads, g->pool_blocks, g->top_k, g->pool,
-                             g->pool_count, g->topk, g->topk_score, workspace, s);
+                             g->pool_count, g->topk, g->topk_score, iws, s);
   } else {
     st = launch_reindex(g->idx, g->qs, g->q_idx, g->w_idx, g->idx_heads, g->pool, g->pool_count, g->pool_blocks,
-                        g->top_k, g->topk, g->topk_score, workspace, s);
+                        g->top_k, g->topk, g->topk_score, iws, s);
   }
   if (st) return st;
   for (int i = 0; i < g->n_layers; ++i) {
     st = launch_attn(g->kv, g->qs, g->q[i], g->q_dtype, g->heads, g->topk, g->top_k, g->swa[i], g->softmax_scale,
-                     g->out[i], g->lse ? g->lse[i] : nullptr,
-                     static_cast<char *>(workspace) + group_attn_offset(g), s);
+                     g->out[i], g->lse ? g->lse[i] : nullptr, workspace, s);
     if (st) return st;
   }
   return CSA2_OK;
@@ -361,7 +364,8 @@ int32_t csa2_group_step_static(const csa2_group_desc *g, void *stream) {
   if (need > (size_t)CSA2_STATIC_SCRATCH_BYTES) return CSA2_ERR_WORKSPACE;
   void *p = nullptr;
   if ((st = static_scratch(&p))) return st;
-  // the scratch needs no initial contents: every call clears what it counts into
+  // the array starts zero (.bss); every call leaves its attention counters,
+  // which sit at offset 0 whatever the group's shape, zero again
   return csa2_group_step(g, p, (size_t)CSA2_STATIC_SCRATCH_BYTES, stream);
 }
 

@@ -178,15 +178,21 @@ CSA2_DEV void qk_tile(const _Float16 *kt, int KT, const half8_t *qa, const half8
 constexpr int kSW = 4;                   // waves per split workgroup (one per SIMD)
 constexpr int kSH = 16;                  // heads per split workgroup
 constexpr int kSKeys = 128;              // key slots per split: 8 tiles of 16, two per wave
+constexpr int kMaxSplits = (2048 + 1024) / kSKeys;   // Top-K <= 2048 slots, window <= 1024 rows
 
-template <int D>
+template <int D, bool QF32>
 struct SplitLds {
   static constexpr int VT = D + 8;       // [key][dim] row stride of the decoded keys (f16)
   static constexpr int PT = kSKeys + 8;  // [head][key] row stride of P (f16)
+  static constexpr int QT = D + 8;       // [head][dim] row stride of the staged queries (f16)
   _Float16 vt[kSKeys * VT];
   _Float16 p[kSH * PT];
+  _Float16 q[(QF32 ? 2 : 1) * kSH * QT];  // hi parts, then lo parts (fp32 queries)
   float wmax[kSW][kSH];
   float wsum[kSW][kSH];
+  float rm[kSW];
+  float lsall[kMaxSplits * kSH];         // every split's lse (the merging workgroup)
+  uint32_t prev;                         // arrival count seen by this workgroup
 };
 
 // Buffer loads (make_rsrc, kOutOfRange) make every load unconditional: empty,
@@ -215,15 +221,15 @@ CSA2_DEV void buffer_load_words(uint32_t *dst, rsrc_t r, uint32_t off) {
 // The lane's share of one 16-key tile: lane (key row, quad) holds dims
 // quad*(D/4) .. +D/4 of its key - D/8 FP4 code bytes plus D/64 E4M3 scale
 // bytes of a Top-K row, or D/4 FP8 code bytes of a window row.
-template <int D>
+template <int D, bool MAIN>
 struct KeyShare {
-  uint32_t w[D / 16];
-  uint32_t s[(D / 64 + 3) / 4];
+  uint32_t w[MAIN ? D / 32 : D / 16];
+  uint32_t s[MAIN ? (D / 64 + 3) / 4 : 1];
 };
 
 // The f16 B operand of k-step kk (dims quad*(D/4) + 8*kk .. +7 of the lane's key).
 template <int D, bool MAIN>
-CSA2_DEV half8_t key_operand(const KeyShare<D> &u, int kk) {
+CSA2_DEV half8_t key_operand(const KeyShare<D, MAIN> &u, int kk) {
   if constexpr (MAIN) {
     const uint32_t sw = u.s[kk / 8] >> (8 * ((kk / 2) % 4));   // scale byte kk/2 of the lane's share
     return fp4x8_dequant_f16(u.w[kk], e4m3x2_to_f16(sw)[0]);
@@ -232,76 +238,79 @@ CSA2_DEV half8_t key_operand(const KeyShare<D> &u, int kk) {
   }
 }
 
-// grid (key splits, queries, head blocks of 16), 4 waves.  Split s covers
-// key slots 128s .. 128s+127 of the Top-K list (s < n_main) or window rows
-// 128(s - n_main) .. of the query's window.  Wave w owns tiles 2w and 2w+1 of
-// the split: it issues the Top-K index loads (or window scale loads), its
-// query operands (16 heads, straight into registers) and then every key row of
-// its tiles at once; it computes S = Q K^T for its 32 keys from registers
-// (channels assigned to k-steps by quarter: lane quad q feeds dims q*(D/4) +
-// 8*kk for both operands) and writes the decoded keys into an LDS tile for
-// P V.  The split's softmax statistics meet in LDS; P (f16) goes to LDS; wave
-// w computes O for dims w*(D/4) .. +D/4 over the split's 128 keys.  The
-// normalised partial O and its log2-domain lse go to the workspace for
-// k_attn_merge.
-template <int D, bool QF32>
-__global__ __launch_bounds__(64 * kSW) void k_attn_split(const void *__restrict__ q_any, int H,
-                                                         const uint8_t *__restrict__ kv_codes,
-                                                         const uint8_t *__restrict__ kv_scales,
-                                                         const int64_t *__restrict__ seq_start,
-                                                         const int32_t *__restrict__ seq_len, int ratio,
-                                                         const int32_t *__restrict__ q_seq,
-                                                         const int32_t *__restrict__ q_pos,
-                                                         const int32_t *__restrict__ topk, int K, int n_main,
-                                                         const uint8_t *__restrict__ swa_codes,
-                                                         const float *__restrict__ swa_scale,
-                                                         const int32_t *__restrict__ swa_start,
-                                                         const int32_t *__restrict__ swa_count, int W, float tau2,
-                                                         float *__restrict__ part_o, float *__restrict__ part_lse) {
-  using Lds = SplitLds<D>;
-  __shared__ Lds L;
+// Partial outputs are kept in the MFMA accumulator layout: per (query, head
+// block, split) a block of 4 waves x 64 lanes x (D/64 tiles x 4) floats, each
+// lane's floats contiguous, so both the split kernel and the merge move them
+// as 16-byte vectors.
+template <int D>
+CSA2_DEV int64_t part_offset(int64_t grp, int wave, int lane) {
+  return ((grp * kSW + wave) * 64 + lane) * (D / 16);
+}
+
+// The workgroup's final output: lane (dim row, quad) of wave w holds heads
+// 4*quad + j at dims w*(D/4) + 16*t + row; lse (natural log) from wave 0.
+template <int D>
+CSA2_DEV void store_output(const float4_t (&acc)[D / 64], const float (&ls2)[4], float *__restrict__ out,
+                           float *__restrict__ lse, int H, int m, int hb, int wv, int row, int quad) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = hb * kSH + 4 * quad + j;
+    if (h >= H) continue;
+#pragma unroll
+    for (int t = 0; t < D / 64; ++t) out[((int64_t)m * H + h) * D + wv * (D / 4) + 16 * t + row] = acc[t][j];
+    if (lse && wv == 0 && row == 0) lse[(int64_t)m * H + h] = ls2[j] * 0.6931471805599453f;
+  }
+}
+
+// One split: wave w owns tiles 2w and 2w+1 of the split's 128 key slots.
+template <int D, bool QF32, bool MAIN>
+CSA2_DEV void attn_split_body(SplitLds<D, QF32> &L, const void *__restrict__ q_any, int H,
+                              const uint8_t *__restrict__ kv_codes, const uint8_t *__restrict__ kv_scales,
+                              int64_t row0, int64_t vis, const int32_t *__restrict__ topk, int K, int sp0, int m,
+                              int hb, const uint8_t *__restrict__ swa_codes, const float *__restrict__ swa_scale,
+                              int64_t wstart, int wcount, float tau2, float *__restrict__ part_o,
+                              float *__restrict__ part_lse, uint32_t *__restrict__ counters, int64_t grp, int sp,
+                              int S, int HB, float *__restrict__ out, float *__restrict__ lse) {
+  using Lds = SplitLds<D, QF32>;
   constexpr int NK = D / 32;             // MFMA k-steps per key
   constexpr int NDT = D / 64;            // 16-dim output tiles per wave
-  const int sp = blockIdx.x, m = blockIdx.y, hb = blockIdx.z;
-  const int S = gridDim.x;
-  const int l = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int QE = QF32 ? 4 : 2;
+  const int tid = threadIdx.x, l = lane_id(), wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = l & 15, quad = l >> 4;
-  const bool main = sp < n_main;          // workgroup-uniform: Top-K keys or window rows
-
-  const int s = q_seq[m];
-  const int64_t lim = ((int64_t)q_pos[m] + 1) / ratio;
-  const int64_t vis = max<int64_t>(0, min<int64_t>(seq_len[s], lim));
-  const int64_t row0 = seq_start[s];
-  const int wcount = (W > 0) ? max(0, min(swa_count[m], W)) : 0;
-  const int64_t wstart = (W > 0) ? swa_start[m] : 0;
   const rsrc_t r_codes = make_rsrc(kv_codes + row0 * (D / 2), (uint32_t)(vis * (D / 2)));
   const rsrc_t r_scales = make_rsrc(kv_scales + row0 * (D / 16), (uint32_t)(vis * (D / 16)));
   const rsrc_t r_win = make_rsrc(wcount ? swa_codes + wstart * D : nullptr, (uint32_t)(wcount * D));
   const rsrc_t r_wsc = make_rsrc(wcount ? swa_scale + wstart : nullptr, (uint32_t)(wcount * 4));
   const rsrc_t r_topk = make_rsrc(K ? topk + (int64_t)m * K : nullptr, (uint32_t)(K * 4));
-  constexpr int QE = QF32 ? 4 : 2;
   const rsrc_t r_q = make_rsrc(static_cast<const char *>(q_any) + (int64_t)m * H * D * QE, (uint32_t)(H * D * QE));
 
   // ---- the key slots of this lane's two tiles: index (or window scale) loads first ----
-  const int slot0 = 128 * (main ? sp : sp - n_main) + 32 * wv + row;   // tile i: slot0 + 16 i
+  const int slot0 = 128 * sp0 + 32 * wv + row;   // tile i: slot0 + 16 i
   int32_t jv[2];
   float rv[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const uint32_t so = (uint32_t)(slot0 + 16 * i) * 4u;
-    jv[i] = main ? (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_topk, so, 0, 0) : 0;
-    rv[i] = main ? 0.0f : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_wsc, so, 0, 0));
+    if constexpr (MAIN) jv[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_topk, so, 0, 0);
+    else rv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_wsc, so, 0, 0));
   }
-  // ---- query operands: lane (head row, quad) holds dims quad*(D/4) .. +D/4 ----
-  uint32_t qraw[(D / 4) * QE / 4];
-  buffer_load_words<(D / 4) * QE>(qraw, r_q, (uint32_t)(((hb * kSH + row) * D + quad * (D / 4)) * QE));
+  // ---- the workgroup's 16 heads of queries, 8 dims per piece, loaded once ----
+  constexpr int QPIECES = kSH * D / 8;
+  constexpr int QPT = (QPIECES + 64 * kSW - 1) / (64 * kSW);   // pieces per thread
+  uint32_t qraw[QPT][2 * QE];
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) {
+    const int pc = tid + 64 * kSW * u;
+    const uint32_t off = (pc < QPIECES) ? (uint32_t)((hb * kSH * D + 8 * pc) * QE) : kOutOfRange;
+    buffer_load_words<8 * QE>(qraw[u], r_q, off);
+  }
   // ---- every key row of the lane's tiles ----
   float ks[2];
-  KeyShare<D> ku[2];
+  KeyShare<D, MAIN> ku[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int slot = slot0 + 16 * i;
-    if (main) {
+    if constexpr (MAIN) {
       const int32_t j = jv[i];
       const bool ok = slot < K && j >= 0 && j < vis;
       ks[i] = ok ? 1.0f : 0.0f;
@@ -312,41 +321,59 @@ __global__ __launch_bounds__(64 * kSW) void k_attn_split(const void *__restrict_
       buffer_load_words<D / 4>(ku[i].w, r_win, (uint32_t)slot * D + quad * (D / 4));
     }
   }
-  // ---- queries as f16 (bf16 converts exactly in the f16 range; fp32 splits into hi + lo) ----
+  // ---- queries to LDS as f16 [head][dim] (bf16 converts exactly in the f16
+  // range; fp32 splits into hi + lo parts) ----
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) {
+    const int pc = tid + 64 * kSW * u;
+    if (pc >= QPIECES) continue;
+    const int h = pc / (D / 8), d = 8 * (pc % (D / 8));
+    half8_t hi, lo;
+    if constexpr (QF32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = __uint_as_float(qraw[u][i]);
+        hi[i] = (_Float16)v;
+        lo[i] = (_Float16)(v - (float)hi[i]);
+      }
+      *reinterpret_cast<half8_t *>(&L.q[(kSH + h) * Lds::QT + d]) = lo;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[2 * i] = (_Float16)__uint_as_float(qraw[u][i] << 16);
+        hi[2 * i + 1] = (_Float16)__uint_as_float(qraw[u][i] & 0xFFFF0000u);
+      }
+    }
+    *reinterpret_cast<half8_t *>(&L.q[h * Lds::QT + d]) = hi;
+  }
+  __syncthreads();
+  // ---- S = Q K^T for the wave's two tiles: the query operands (lane (head
+  // row, quad): dims quad*(D/4) + 8*kk) come from LDS all at once; the
+  // decoded keys go to LDS for P V ----
   half8_t qa[NK];
   half8_t qb[QF32 ? NK : 1];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
-    if constexpr (QF32) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = __uint_as_float(qraw[8 * kk + i]);
-        const _Float16 hi = (_Float16)v;
-        qa[kk][i] = hi;
-        qb[kk][i] = (_Float16)(v - (float)hi);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t x = qraw[4 * kk + i];
-        qa[kk][2 * i] = (_Float16)__uint_as_float(x << 16);
-        qa[kk][2 * i + 1] = (_Float16)__uint_as_float(x & 0xFFFF0000u);
-      }
-    }
+    const int qo = row * Lds::QT + quad * (D / 4) + 8 * kk;
+    qa[kk] = *reinterpret_cast<const half8_t *>(&L.q[qo]);
+    if constexpr (QF32) qb[kk] = *reinterpret_cast<const half8_t *>(&L.q[kSH * Lds::QT + qo]);
   }
-  // ---- S = Q K^T for the wave's two tiles; the decoded keys go to LDS ----
   float4_t sacc[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) sacc[i] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  _Float16 *vrow = &L.vt[(32 * wv + row) * Lds::VT + quad * (D / 4)];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const half8_t b = main ? key_operand<D, true>(ku[i], kk) : key_operand<D, false>(ku[i], kk);
-      sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b, sacc[i], 0, 0, 0);
-      if constexpr (QF32) sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b, sacc[i], 0, 0, 0);
-      *reinterpret_cast<half8_t *>(&L.vt[(32 * wv + 16 * i + row) * Lds::VT + quad * (D / 4) + 8 * kk]) = b;
+    const half8_t b0 = key_operand<D, MAIN>(ku[0], kk);
+    const half8_t b1 = key_operand<D, MAIN>(ku[1], kk);
+    sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b0, sacc[0], 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b1, sacc[1], 0, 0, 0);
+    if constexpr (QF32) {
+      sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b0, sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b1, sacc[1], 0, 0, 0);
     }
+    *reinterpret_cast<half8_t *>(vrow + 8 * kk) = b0;
+    *reinterpret_cast<half8_t *>(vrow + 16 * Lds::VT + 8 * kk) = b1;
   }
   // ---- split statistics: lane holds key (16*tile + row) of heads 4*quad + j ----
   float zz[2][4];
@@ -364,13 +391,12 @@ __global__ __launch_bounds__(64 * kSW) void k_attn_split(const void *__restrict_
     const float mx = max16_lanes(fmaxf(zz[0][j], zz[1][j]));
     if (row == 0) L.wmax[wv][4 * quad + j] = mx;
   }
-  __shared__ float s_rm[kSW];
-  if (l == 0) s_rm[wv] = rm;
+  if (l == 0) L.rm[wv] = rm;
   __syncthreads();
   float mx[4];
   rm = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kSW; ++w) rm = fmaxf(rm, s_rm[w]);
+  for (int w = 0; w < kSW; ++w) rm = fmaxf(rm, L.rm[w]);
   int e = 0;
   (void)frexpf(rm, &e);
   e = (rm > 0.0f) ? 1 - e : 0;
@@ -410,52 +436,138 @@ __global__ __launch_bounds__(64 * kSW) void k_attn_split(const void *__restrict_
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
     }
   }
-  // ---- normalised partial and its log2-domain lse (-inf: no key) ----
-  const int64_t grp = ((int64_t)m * gridDim.z + hb) * S + sp;
-  float *po = part_o + grp * (kSH * D);
+  // ---- normalised partial (accumulator layout) and its log2-domain lse ----
+  float inv[4], ls[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int hh = 4 * quad + j;
     float lt = 0.0f;
 #pragma unroll
     for (int w = 0; w < kSW; ++w) lt += L.wsum[w][hh];
-    const float inv = (lt > 0.0f) ? ldexpf(1.0f / lt, -e) : 0.0f;
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) po[hh * D + wv * (D / 4) + 16 * t + row] = acc[t][j] * inv;
-    if (wv == 0 && row == 0) part_lse[grp * kSH + hh] = (lt > 0.0f) ? mx[j] + log2f(lt) : -INFINITY;
+    inv[j] = (lt > 0.0f) ? ldexpf(1.0f / lt, -e) : 0.0f;
+    ls[j] = (lt > 0.0f) ? mx[j] + log2f(lt) : -INFINITY;
   }
-}
-
-// Merge of the key splits by log-sum-exp: grid (queries x head blocks, D/64),
-// 256 threads; thread t combines head t/16 of the block at dims 4*(t%16) ..
-// +3 of the workgroup's 64-dim slice.
-template <int D>
-__global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ part_o,
-                                                    const float *__restrict__ part_lse, int S, int H, int HB,
-                                                    float *__restrict__ out, float *__restrict__ lse) {
-  const int m = blockIdx.x / HB, hb = blockIdx.x % HB;
-  const int hh = threadIdx.x >> 4, d = blockIdx.y * 64 + 4 * (threadIdx.x & 15);
-  const int h = hb * kSH + hh;
-  const int64_t g0 = ((int64_t)m * HB + hb) * S;
-  float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, part_lse[(g0 + s) * kSH + hh]);
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  float wsum = 0.0f;
-  if (mx > -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float ls = part_lse[(g0 + s) * kSH + hh];
-      const float w = (ls == -INFINITY) ? 0.0f : exp2f(ls - mx);
-      const float4 v = *reinterpret_cast<const float4 *>(part_o + (g0 + s) * (kSH * D) + hh * D + d);
-      wsum += w;
-      o.x = fmaf(w, v.x, o.x); o.y = fmaf(w, v.y, o.y); o.z = fmaf(w, v.z, o.z); o.w = fmaf(w, v.w, o.w);
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[t][j] *= inv[j];
+  if (S == 1) {
+    store_output<D>(acc, ls, out, lse, H, m, hb, wv, row, quad);
+    return;
+  }
+  // ---- key splits: this split's partial and lse go out through stores that
+  // write through the caches (sc0 sc1), so every XCD reads them from memory;
+  // they are complete (s_waitcnt) before the arrival is counted, and the last
+  // split to arrive loads the others (again past the caches) only after it
+  // has seen the count, then merges them by log-sum-exp ----
+  const int64_t g0 = grp - sp;                       // split 0 of this (query, head block)
+  const rsrc_t r_po = make_rsrc(part_o + part_offset<D>(g0, 0, 0), (uint32_t)(S * kSW * 64 * (D / 16) * 4));
+  const rsrc_t r_pl = make_rsrc(part_lse + g0 * kSH, (uint32_t)(S * kSH * 4));
+  constexpr int kThrough = 17;                       // cache policy sc0 | sc1: write through to memory
+  const uint32_t slot_off = (uint32_t)(((sp * kSW + wv) * 64 + l) * (D / 16) * 4);
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[t]), r_po, slot_off + 16 * t, 0,
+                                           kThrough);
+  if (wv == 0 && row == 0)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, (float4_t){ls[0], ls[1], ls[2], ls[3]}),
+                                           r_pl, (uint32_t)((sp * kSH + 4 * quad) * 4), 0, kThrough);
+  __builtin_amdgcn_s_waitcnt(0);                     // every store of this workgroup has completed
+  __syncthreads();
+  if (threadIdx.x == 0) L.prev = atomicInc(&counters[(int64_t)m * HB + hb], (uint32_t)S - 1u);  // wraps to 0
+  __syncthreads();
+  if (L.prev != (uint32_t)S - 1u) return;
+  // every split's lse into LDS, then the maximum per head
+  if (threadIdx.x < S * kSH)
+    L.lsall[threadIdx.x] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_pl, threadIdx.x * 4u, 0, kThrough));
+  __syncthreads();
+  float mxs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mxs[j] = ls[j];
+  for (int s2 = 0; s2 < S; ++s2)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mxs[j] = fmaxf(mxs[j], L.lsall[s2 * kSH + 4 * quad + j]);
+  // splits are added in split order whichever arrived last (this workgroup's
+  // own partial comes from its registers), so the result is deterministic
+  float wsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float4_t own[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) { own[t] = acc[t]; acc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f}; }
+  for (int s2 = 0; s2 < S; ++s2) {
+    float wt[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float l2 = L.lsall[s2 * kSH + 4 * quad + j];
+      wt[j] = (l2 == -INFINITY) ? 0.0f : exp2f(l2 - mxs[j]);
+      wsum[j] += wt[j];
+    }
+    const uint32_t so = (uint32_t)(((s2 * kSW + wv) * 64 + l) * (D / 16) * 4);
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+      float4_t v = own[t];
+      if (s2 != sp)
+        v = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r_po, so + 16 * t, 0, kThrough));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[t][j] = fmaf(wt[j], v[j], acc[t][j]);
     }
   }
-  if (h >= H) return;
-  const float inv = (wsum > 0.0f) ? 1.0f / wsum : 0.0f;
-  *reinterpret_cast<float4 *>(out + ((int64_t)m * H + h) * D + d) = make_float4(o.x * inv, o.y * inv, o.z * inv,
-                                                                              o.w * inv);
-  if (lse && blockIdx.y == 0 && (threadIdx.x & 15) == 0)
-    lse[(int64_t)m * H + h] = (wsum > 0.0f) ? (mx + log2f(wsum)) * 0.6931471805599453f : -INFINITY;
+  float lsm[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float iw = (wsum[j] > 0.0f) ? 1.0f / wsum[j] : 0.0f;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) acc[t][j] *= iw;
+    lsm[j] = (wsum[j] > 0.0f) ? mxs[j] + log2f(wsum[j]) : -INFINITY;
+  }
+  store_output<D>(acc, lsm, out, lse, H, m, hb, wv, row, quad);
+}
+
+// grid (key splits, queries, head blocks of 16), 4 waves.  Split s covers
+// key slots 128s .. 128s+127 of the Top-K list (s < n_main) or window rows
+// 128(s - n_main) .. of the query's window.  Wave w owns tiles 2w and 2w+1 of
+// the split: it issues the Top-K index loads (or window scale loads), its
+// share of the workgroup's 16 query heads (staged once in LDS as f16) and
+// then every key row of its tiles at once; it computes S = Q K^T for its 32
+// keys from registers (channels assigned to k-steps by quarter: lane quad q
+// feeds dims q*(D/4) + 8*kk for both operands) and writes the decoded keys
+// into an LDS tile for P V.  The split's softmax statistics meet in LDS; P
+// (f16) goes to LDS; wave w computes O for dims w*(D/4) .. +D/4 over the
+// split's 128 keys.  The normalised partial O and its log2-domain lse go to
+// the workspace for k_attn_merge.
+template <int D, bool QF32>
+__global__ __launch_bounds__(64 * kSW) void k_attn_split(const void *__restrict__ q_any, int H,
+                                                         const uint8_t *__restrict__ kv_codes,
+                                                         const uint8_t *__restrict__ kv_scales,
+                                                         const int64_t *__restrict__ seq_start,
+                                                         const int32_t *__restrict__ seq_len, int ratio,
+                                                         const int32_t *__restrict__ q_seq,
+                                                         const int32_t *__restrict__ q_pos,
+                                                         const int32_t *__restrict__ topk, int K, int n_main,
+                                                         const uint8_t *__restrict__ swa_codes,
+                                                         const float *__restrict__ swa_scale,
+                                                         const int32_t *__restrict__ swa_start,
+                                                         const int32_t *__restrict__ swa_count, int W, float tau2,
+                                                         float *__restrict__ part_o, float *__restrict__ part_lse,
+                                                         uint32_t *__restrict__ counters, float *__restrict__ out,
+                                                         float *__restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) SplitLds<D, QF32> L;
+  const int sp = blockIdx.x, m = blockIdx.y, hb = blockIdx.z;
+  const int s = q_seq[m];
+  const int64_t lim = ((int64_t)q_pos[m] + 1) / ratio;
+  const int64_t vis = max<int64_t>(0, min<int64_t>(seq_len[s], lim));
+  const int64_t row0 = seq_start[s];
+  const int wcount = (W > 0) ? max(0, min(swa_count[m], W)) : 0;
+  const int64_t wstart = (W > 0) ? swa_start[m] : 0;
+  const int64_t grp = ((int64_t)m * gridDim.z + hb) * gridDim.x + sp;
+  const int S = gridDim.x, HB = gridDim.z;
+  if (sp < n_main)   // workgroup-uniform: Top-K keys or window rows
+    attn_split_body<D, QF32, true>(L, q_any, H, kv_codes, kv_scales, row0, vis, topk, K, sp, m, hb, swa_codes,
+                                   swa_scale, wstart, wcount, tau2, part_o, part_lse, counters, grp, sp, S, HB, out,
+                                   lse);
+  else
+    attn_split_body<D, QF32, false>(L, q_any, H, kv_codes, kv_scales, row0, vis, topk, K, sp - n_main, m, hb,
+                                    swa_codes, swa_scale, wstart, wcount, tau2, part_o, part_lse, counters, grp, sp,
+                                    S, HB, out, lse);
 }
 
 // ===========================================================================
@@ -628,15 +740,22 @@ static bool use_decode_kernel(int m, int heads, int dim, int64_t max_len) {
 static int split_main(int top_k) { return (top_k + kSKeys - 1) / kSKeys; }
 static int split_count(int top_k, int window) { return split_main(top_k) + (window + kSKeys - 1) / kSKeys; }
 
-// Decode-schedule workspace: normalised partial outputs [query][head block]
-// [split][16][dim] and their log2-domain lse.
+// Decode-schedule workspace: arrival counters [query][head block] in a region
+// of fixed size at offset 0 (zero before the first call, left zero by every
+// call, never written by anything else: a later call of another shape finds
+// its counters at the same place and still zero), normalised partial outputs
+// [query][head block][split] in the accumulator layout, and their log2-domain
+// lse.  The schedule's gate keeps m * ceil(heads/16) below 1024 counters.
 struct AttnWs {
-  size_t part_o, part_lse, total;
+  size_t counters, part_o, part_lse, total;
 };
+static_assert(kAttnCounterBytes >= sizeof(uint32_t) * 1024, "counter region holds every decode-schedule counter");
 static AttnWs attn_ws_layout(int m, int heads, int dim, int top_k, int window) {
-  const size_t groups = (size_t)m * ((heads + kSH - 1) / kSH) * split_count(top_k, window);
+  const size_t qh = (size_t)m * ((heads + kSH - 1) / kSH);
+  const size_t groups = qh * split_count(top_k, window);
   AttnWs w{};
   size_t off = 0;
+  w.counters = off; off = kAttnCounterBytes;
   w.part_o = off;   off = align256(off + sizeof(float) * groups * kSH * dim);
   w.part_lse = off; off = align256(off + sizeof(float) * groups * kSH);
   w.total = off;
@@ -658,15 +777,14 @@ static int attn_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, const voi
   const float tau2 = scale * 1.4426950408889634f;  // log2-domain softmax: p = 2^(z - max)
   if (use_decode_kernel(qs.m, heads, D, kv.max_len)) {
     const AttnWs L = attn_ws_layout(qs.m, heads, D, K, W);
-    float *po = reinterpret_cast<float *>(static_cast<char *>(ws) + L.part_o);
-    float *pl = reinterpret_cast<float *>(static_cast<char *>(ws) + L.part_lse);
-    const int HB = (heads + kSH - 1) / kSH;
-    const dim3 grid(split_count(K, W), qs.m, HB);
+    char *base = static_cast<char *>(ws);
+    uint32_t *ctr = reinterpret_cast<uint32_t *>(base + L.counters);
+    float *po = reinterpret_cast<float *>(base + L.part_o);
+    float *pl = reinterpret_cast<float *>(base + L.part_lse);
+    const dim3 grid(split_count(K, W), qs.m, (heads + kSH - 1) / kSH);
     CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_split<D, QF32>), grid, dim3(64 * kSW), stream, q, heads, kv.codes,
                       kv.scales, kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, split_main(K),
-                      swa.codes, swa.scale, swa.start, swa.count, W, tau2, po, pl);
-    hipLaunchKernelGGL((k_attn_merge<D>), dim3(qs.m * HB, D / 64), dim3(256), 0, stream, po, pl,
-                       split_count(K, W), heads, HB, out, lse);
+                      swa.codes, swa.scale, swa.start, swa.count, W, tau2, po, pl, ctr, out, lse);
   } else if (attn_prefill_supported(kv, QF32 ? CSA2_F32 : CSA2_BF16, K)) {
     return launch_attn_prefill(kv, qs, q, heads, topk, K, swa, scale, out, lse, stream);
   } else {

@@ -248,6 +248,36 @@ __global__ __launch_bounds__(256) void k_hist_threshold(const uint32_t *__restri
   if (threadIdx.x == 0) counters[m * 4 + 2] = (uint32_t)s_T;
 }
 
+// Histogram of block-maximum keys (top kHistBits bits) when the block
+// maxima come from the multi-query scoring kernel: grid (chunks of
+// kFilterBlocks blocks, queries), one LDS histogram per workgroup whose
+// non-zero bins are added to replica (chunk % hist_rep) of the query's
+// histogram - the same histogram the decode scan builds as it goes.
+__global__ __launch_bounds__(256) void k_bmax_hist(const float *__restrict__ bmax, int64_t nb_stride,
+                                                   const int32_t *__restrict__ seq_len,
+                                                   const int32_t *__restrict__ q_seq,
+                                                   const int32_t *__restrict__ q_pos, int ratio,
+                                                   uint32_t *__restrict__ hist, int hist_rep) {
+  __shared__ uint32_t s_hist[kHistBins];
+  const int m = blockIdx.y;
+  int s;
+  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
+  const int64_t nb = (vis + kBlock - 1) / kBlock;
+  const int64_t b0 = (int64_t)blockIdx.x * kFilterBlocks;
+  if (b0 >= nb) return;
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) s_hist[i] = 0u;
+  __syncthreads();
+  const float *bm = bmax + (int64_t)m * nb_stride;
+  for (int j = 0; j < kFilterBlocks / 256; ++j) {
+    const int64_t b = b0 + j * 256 + threadIdx.x;
+    if (b < nb) atomicAdd(&s_hist[f2key(bm[b]) >> (32 - kHistBits)], 1u);
+  }
+  __syncthreads();
+  uint32_t *hq = hist + ((int64_t)m * hist_rep + (int)(blockIdx.x % hist_rep)) * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x)
+    if (s_hist[i]) atomicAdd(&hq[i], s_hist[i]);
+}
+
 // Pool filter: blocks above the threshold bin are in the pool for sure,
 // blocks in it go to the tie list.  Appends are gathered in
 // LDS and reserved in the global lists with one atomic per list per workgroup.
@@ -431,176 +461,6 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
   if (threadIdx.x == 0) pool_count[m] = need;
 }
 
-// Fused pool selection, one workgroup of 1024 threads per query (queries whose
-// blocks fit the LDS bitmap): the first scan's histogram replicas give the
-// threshold bin T (the bin holding the need-th largest block maximum,
-// need = min(P, blocks)); one pass over the block maxima sets the bitmap bit
-// of every block above T and gathers the blocks of bin T into an LDS list;
-// radix passes over that list on (key desc, block asc) below the bin's 12
-// bits pick the entries of bin T still needed; the bitmap is then compacted
-// into the ascending pool.  When bin T holds more entries than the LDS list,
-// the passes re-read the block maxima instead.
-constexpr int kPoolSelTies = 8192;
-
-__global__ __launch_bounds__(1024) void k_pool_select(const float *__restrict__ bmax, int64_t nb_stride,
-                                                      const uint32_t *__restrict__ hist, int hist_rep,
-                                                      const int32_t *__restrict__ seq_len,
-                                                      const int32_t *__restrict__ q_seq,
-                                                      const int32_t *__restrict__ q_pos, int ratio, int P,
-                                                      int32_t *__restrict__ pool_out,
-                                                      int32_t *__restrict__ pool_count) {
-  __shared__ uint32_t s_bits[kBitmapWords];
-  __shared__ uint32_t s_tkey[kPoolSelTies];
-  __shared__ int32_t s_tblk[kPoolSelTies];
-  __shared__ uint32_t s_h[256];
-  __shared__ int s_scan[17];
-  __shared__ int s_T, s_above, s_nT, s_ntie, s_digit, s_rem, s_cnt;
-  const int m = blockIdx.x, tid = threadIdx.x;
-  int s;
-  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
-  const int nb = (int)((vis + kBlock - 1) / kBlock);   // <= 32 * kBitmapWords (checked on the host)
-  const int need = min(P, nb);
-  const int words = (nb + 31) / 32;
-  // ---- threshold bin: thread t holds bins [4096 - 4(t+1), 4096 - 4t), every
-  // replica's loads in flight at once ----
-  const int bin0 = kHistBins - 4 * (tid + 1);
-  uint4 x[kHistMaxReplicas];
-#pragma unroll
-  for (int r = 0; r < kHistMaxReplicas; ++r) {
-    const int rr = r < hist_rep ? r : 0;
-    x[r] = *reinterpret_cast<const uint4 *>(hist + ((int64_t)m * hist_rep + rr) * kHistBins + bin0);
-  }
-  uint32_t hv[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int r = 0; r < kHistMaxReplicas; ++r) {
-    if (r >= hist_rep) continue;
-    hv[0] += x[r].x; hv[1] += x[r].y; hv[2] += x[r].z; hv[3] += x[r].w;
-  }
-  const int c = (int)(hv[0] + hv[1] + hv[2] + hv[3]);
-  if (tid == 0) { s_T = -1; s_above = 0; s_nT = 0; s_ntie = 0; }
-  for (int i = tid; i < words; i += 1024) s_bits[i] = 0u;
-  int tot;
-  const int before = block_exclusive_scan<1024>(c, s_scan, &tot);   // blocks in higher bins
-  if (nb > P && before < need && before + c >= need) {
-    int cum = before;
-    for (int k = 3; k >= 0; --k) {
-      if (cum + (int)hv[k] >= need) { s_T = bin0 + k; s_above = cum; s_nT = (int)hv[k]; break; }
-      cum += (int)hv[k];
-    }
-  }
-  __syncthreads();
-  const int T = s_T, rem_t = need - s_above, nT = s_nT;
-  const bool all_t = T < 0 || rem_t >= nT;              // every block of bin T is taken
-  const bool in_lds = !all_t && nT <= kPoolSelTies;
-  // ---- filter: thread t owns bitmap words t, t + 1024, ... (32 blocks each),
-  // two words' loads in flight per round ----
-  const float *bm = bmax + (int64_t)m * nb_stride;
-  for (int w0 = 0; w0 < words; w0 += 2048) {
-    float4 v[2][8];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int w = min(w0 + tid + 1024 * u, words - 1);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[u][k] = *reinterpret_cast<const float4 *>(bm + 32 * w + 4 * k);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int w = w0 + tid + 1024 * u;
-      if (w >= words) continue;
-      uint32_t bits = 0u;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float e4[4] = {v[u][k].x, v[u][k].y, v[u][k].z, v[u][k].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int b = 32 * w + 4 * k + e;
-          if (b >= nb) continue;
-          const uint32_t key = f2key(e4[e]);
-          const int bin = (int)(key >> (32 - kHistBits));
-          if (T < 0 || bin > T || (bin == T && all_t)) {
-            bits |= 1u << (4 * k + e);
-          } else if (bin == T && in_lds) {
-            const int slot = atomicAdd(&s_ntie, 1);
-            if (slot < kPoolSelTies) { s_tkey[slot] = key; s_tblk[slot] = b; }
-          }
-        }
-      }
-      s_bits[w] = bits;
-    }
-  }
-  __syncthreads();
-  // ---- the rem_t best blocks of bin T on (key desc, block asc): composite
-  // c = key << 32 | ~block, top kHistBits bits known ----
-  if (!all_t) {
-    const int ntie = in_lds ? min(s_ntie, kPoolSelTies) : 0;
-    auto composite = [](uint32_t key, int32_t b) { return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)b); };
-    uint64_t prefix = (uint64_t)T << (64 - kHistBits);
-    uint64_t mask = ((1ull << kHistBits) - 1ull) << (64 - kHistBits);
-    int rem = rem_t;
-    for (int hi = 64 - kHistBits; hi > 0; hi -= 8) {
-      const int width = hi < 8 ? hi : 8;
-      const int shift = hi - width;
-      const uint64_t dmask = (1ull << width) - 1ull;
-      for (int i = tid; i < 256; i += 1024) s_h[i] = 0u;
-      __syncthreads();
-      if (in_lds) {
-        for (int i = tid; i < ntie; i += 1024) {
-          const uint64_t cc = composite(s_tkey[i], s_tblk[i]);
-          if ((cc & mask) == prefix) atomicAdd(&s_h[(cc >> shift) & dmask], 1u);
-        }
-      } else {
-        for (int b = tid; b < nb; b += 1024) {
-          const uint64_t cc = composite(f2key(bm[b]), b);
-          if ((cc & mask) == prefix) atomicAdd(&s_h[(cc >> shift) & dmask], 1u);
-        }
-      }
-      __syncthreads();
-      find_digit(s_h, rem, &s_digit, &s_rem, &s_cnt);
-      __syncthreads();
-      prefix |= (uint64_t)s_digit << shift;
-      mask |= dmask << shift;
-      rem = s_rem;
-      if (s_cnt == rem) break;   // every entry left in the cut's bin is taken
-    }
-    if (in_lds) {
-      for (int i = tid; i < ntie; i += 1024) {
-        const int32_t b = s_tblk[i];
-        if ((composite(s_tkey[i], b) & mask) >= prefix) atomicOr(&s_bits[b >> 5], 1u << (b & 31));
-      }
-    } else {
-      const uint64_t tmask = ((1ull << kHistBits) - 1ull) << (64 - kHistBits);
-      const uint64_t tpre = (uint64_t)T << (64 - kHistBits);
-      for (int b = tid; b < nb; b += 1024) {
-        const uint64_t cc = composite(f2key(bm[b]), b);
-        if ((cc & tmask) == tpre && (cc & mask) >= prefix) atomicOr(&s_bits[b >> 5], 1u << (b & 31));
-      }
-    }
-  }
-  __syncthreads();
-  // ---- compaction: thread t takes words [t*wpt, (t+1)*wpt) ----
-  int32_t *out = pool_out + (int64_t)m * P;
-  const int wpt = (words + 1023) / 1024;
-  int cnt = 0;
-  for (int k = 0; k < wpt; ++k) {
-    const int w = tid * wpt + k;
-    if (w < words) cnt += __popc(s_bits[w]);
-  }
-  int pos = block_exclusive_scan<1024>(cnt, s_scan, &tot);
-  for (int k = 0; k < wpt; ++k) {
-    const int w = tid * wpt + k;
-    if (w >= words) break;
-    uint32_t bits = s_bits[w];
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      bits &= bits - 1;
-      if (pos < P) out[pos] = w * 32 + bit;
-      ++pos;
-    }
-  }
-  for (int i = min(tot, P) + tid; i < P; i += 1024) out[i] = -1;
-  if (tid == 0) pool_count[m] = min(tot, need);
-}
-
 // Re-score the positions of E pool blocks per workgroup (E = 64, or fewer
 // when that leaves most of the chip idle).  Slot 8*e + r of a query holds
 // the score of position 8*pool[e] + r (-inf when not visible).  Each wave
@@ -657,93 +517,116 @@ __global__ __launch_bounds__(256) void k_rescore(const uint8_t *__restrict__ cod
 // workgroup of NT threads: thread t owns slots [t*PER, (t+1)*PER), sv[] their
 // scores (-inf: no candidate).  The ranking is (score desc, slot asc); the
 // selected slots are handed to emit(rank, i, score) in ascending slot order
-// (i the thread-local slot index, rank the output position).  Radix passes
-// count into one 256-bin histogram per wave, then merge.  Returns the number
-// selected, min(K, #candidates).
+// (i the thread-local slot index, rank the output position).  A first pass
+// counts the top 12 bits of every key into a 4096-bin histogram and finds
+// the bin T holding the K-th key; only the keys of bin T take further radix
+// passes, on the composite (key, ~slot) below those 12 bits, until the cut's
+// bin holds exactly the entries still needed.  Returns the number selected,
+// min(K, #candidates).
 template <int NT>
 struct SelectLds {
-  uint32_t wh[NT / 64 * 256];
+  uint32_t hist[kHistBins];
   uint32_t h[256];
   int scan[NT / 64 + 1];
-  int digit, rem, cnt;
+  int T, above, nT, digit, rem, cnt;
+};
+
+// Count `d` of every key into hist: each thread first folds its keys into at
+// most two (digit, count) pairs - the keys of a query cluster in a few
+// digits, and the lanes of a wave would otherwise hit one LDS counter together.
+struct DigitFold {
+  uint32_t d0 = 0u, c0 = 0u, d1 = 0u, c1 = 0u;
+  CSA2_DEV void add(uint32_t *hist, uint32_t d) {
+    if (c0 == 0u || d == d0) { d0 = d; ++c0; }
+    else if (c1 == 0u || d == d1) { d1 = d; ++c1; }
+    else atomicAdd(&hist[d], 1u);
+  }
+  CSA2_DEV void flush(uint32_t *hist) {
+    if (c0) atomicAdd(&hist[d0], c0);
+    if (c1) atomicAdd(&hist[d1], c1);
+  }
 };
 
 template <int NT, int PER, typename Emit>
 CSA2_DEV int select_topk(const float (&sv)[PER], int K, SelectLds<NT> &sm, Emit emit) {
-  constexpr int NW = NT / 64;
-  const int wv = threadIdx.x >> 6;
+  constexpr int BPT = kHistBins / NT;   // histogram bins per thread in the threshold scan
+  constexpr int KB = 32 - kHistBits;    // key bits below the histogram's
+  const int tid = threadIdx.x;
   uint32_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) key[i] = (sv[i] > -INFINITY) ? f2key(sv[i]) : 0u;
-  int nvalid = 0;
+  for (int i = tid; i < kHistBins / 4; i += NT) reinterpret_cast<uint4 *>(sm.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid == 0) { sm.T = -1; sm.above = 0; sm.nT = 0; }
+  __syncthreads();
+  {
+    DigitFold f;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) nvalid += key[i] != 0u;
-  int total;
-  (void)block_exclusive_scan<NT>(nvalid, sm.scan, &total);
-  const int Kp = min(K, total);
-  uint32_t kstar = 0xFFFFFFFFu, kmask = 0xFFFFFFFFu;
-  int rem = 0;
-  if (Kp > 0) {
-    uint32_t prefix = 0, mask = 0;
-    rem = Kp;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = threadIdx.x; i < NW * 256 / 4; i += NT)
-        reinterpret_cast<uint4 *>(sm.wh)[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < PER; ++i)
+      if (key[i] != 0u) f.add(sm.hist, key[i] >> KB);
+    f.flush(sm.hist);
+  }
+  __syncthreads();
+  // ---- threshold bin: thread t owns bins [4096 - BPT(t+1), 4096 - BPT t) ----
+  const int bin0 = kHistBins - BPT * (tid + 1);
+  uint32_t hv[BPT];
+  int c = 0;
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) { hv[k] = sm.hist[bin0 + k]; c += (int)hv[k]; }
+  int tot;
+  const int before = block_exclusive_scan<NT>(c, sm.scan, &tot);   // keys in higher bins
+  const int Kp = min(K, tot);
+  if (Kp > 0 && before < Kp && before + c >= Kp) {
+    int cum = before;
+#pragma unroll
+    for (int k = BPT - 1; k >= 0; --k) {
+      if (cum + (int)hv[k] >= Kp) { sm.T = bin0 + k; sm.above = cum; sm.nT = (int)hv[k]; break; }
+      cum += (int)hv[k];
+    }
+  }
+  __syncthreads();
+  const int T = sm.T;
+  int rem = Kp - sm.above;
+  const bool all_t = rem >= sm.nT;      // every key of bin T is taken
+  // ---- the rem best keys of bin T on c = key << 32 | ~slot ----
+  auto comp = [&](int i) {
+    return ((uint64_t)key[i] << 32) | (uint64_t)(~(uint32_t)(tid * PER + i));
+  };
+  uint64_t prefix = (uint64_t)(uint32_t)max(T, 0) << (64 - kHistBits);
+  uint64_t mask = ((1ull << kHistBits) - 1ull) << (64 - kHistBits);
+  if (Kp > 0 && !all_t) {
+    for (int hi = 64 - kHistBits; hi > 0; hi -= 8) {
+      const int width = hi < 8 ? hi : 8;
+      const int shift = hi - width;
+      const uint64_t dmask = (1ull << width) - 1ull;
+      for (int i = tid; i < 256; i += NT) sm.h[i] = 0u;
       __syncthreads();
-      uint32_t *wh = sm.wh + wv * 256;
-      // Scores cluster in a few digit values (the high digits especially), so
-      // the lanes of a wave would hit one LDS counter together: each thread
-      // first folds its keys into at most two (digit, count) pairs.
-      uint32_t d0 = 0u, c0 = 0u, d1 = 0u, c1 = 0u;
+      DigitFold f;
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        if (key[i] == 0u || (key[i] & mask) != prefix) continue;
-        const uint32_t d = (key[i] >> shift) & 255u;
-        if (c0 == 0u || d == d0) { d0 = d; ++c0; }
-        else if (c1 == 0u || d == d1) { d1 = d; ++c1; }
-        else atomicAdd(&wh[d], 1u);
+        const uint64_t cc = comp(i);
+        if (key[i] != 0u && (cc & mask) == prefix) f.add(sm.h, (uint32_t)((cc >> shift) & dmask));
       }
-      if (c0) atomicAdd(&wh[d0], c0);
-      if (c1) atomicAdd(&wh[d1], c1);
-      __syncthreads();
-      for (int i = threadIdx.x; i < 256; i += NT) {
-        uint32_t t = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) t += sm.wh[w * 256 + i];
-        sm.h[i] = t;
-      }
+      f.flush(sm.h);
       __syncthreads();
       find_digit(sm.h, rem, &sm.digit, &sm.rem, &sm.cnt);
       __syncthreads();
-      prefix |= (uint32_t)sm.digit << shift;
-      mask |= 255u << shift;
+      prefix |= (uint64_t)sm.digit << shift;
+      mask |= dmask << shift;
       rem = sm.rem;
-      // every key left in the cut's bin is taken: the lower digits cannot matter
-      if (sm.cnt == rem) break;
+      if (sm.cnt == rem) break;   // every entry left in the cut's bin is taken
     }
-    kstar = prefix;
-    kmask = mask;
   }
-  // keys above the cut (on the decided digits) are taken; keys equal to it
-  // are ranked by slot (lowest first), then compaction
-  int neq = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) neq += (Kp > 0 && (key[i] & kmask) == kstar);
-  int tmp;
-  int eq_before = block_exclusive_scan<NT>(neq, sm.scan, &tmp);
+  // ---- selection in ascending slot order ----
   bool sel[PER];
   int nsel = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    bool takeit = false;
-    if (Kp > 0 && key[i] != 0u) {
-      const uint32_t km = key[i] & kmask;
-      if (km > kstar) takeit = true;
-      else if (km == kstar) { takeit = eq_before < rem; ++eq_before; }
-    }
-    sel[i] = takeit;
-    nsel += takeit;
+    const int bin = (int)(key[i] >> KB);
+    sel[i] = Kp > 0 && key[i] != 0u &&
+             (bin > T || (bin == T && (all_t || (comp(i) & mask) >= prefix)));
+    nsel += sel[i];
   }
+  int tmp;
   int rank = block_exclusive_scan<NT>(nsel, sm.scan, &tmp);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -913,6 +796,32 @@ static int index_full_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
 
   // hist and counters are adjacent: clear both with one fill kernel
   const int64_t nz = (int64_t)((L.sure - L.hist) / sizeof(uint32_t));
+  const int64_t nbq = (idx.max_len + kBlock - 1) / kBlock;   // blocks of the longest sequence
+  if (qs.run >= 2) {
+    // queries in runs of one sequence: every streamed indexer entry is scored
+    // against all the queries of its sequence at once (multi-query MFMA
+    // kernel), then each query's pool comes from its block maxima
+    int st = launch_score_blocks(idx, qs, q_idx, w_idx, heads, bmax, L.nb_max, stream);
+    if (st != CSA2_OK) return st;
+    if (nbq <= kBlockSelectMax) {
+      st = launch_block_select(bmax, L.nb_max, nbq > 0 ? nbq : 1, idx, qs, P, pool_out, pool_count, stream);
+      if (st != CSA2_OK) return st;
+    } else {
+      hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
+      hipLaunchKernelGGL(k_bmax_hist, dim3((unsigned)((nbq + kFilterBlocks - 1) / kFilterBlocks), qs.m), dim3(256),
+                         0, stream, bmax, L.nb_max, idx.seq_len, qs.seq, qs.pos, idx.ratio, hist, L.hist_rep);
+      hipLaunchKernelGGL(k_hist_threshold, dim3(qs.m), dim3(256), 0, stream, hist, L.hist_rep, idx.seq_len, qs.seq,
+                         qs.pos, idx.ratio, P, counters);
+      const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);
+      hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, idx.seq_len, qs.seq, qs.pos,
+                         idx.ratio, P, counters, sure, tie);
+      hipLaunchKernelGGL(k_pool_finalize, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, counters, sure, tie,
+                         idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
+    }
+    if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
+    return rescore_and_select<DI>(idx, qs, q_idx, w_idx, heads, pool_out, pool_count, P, K, topk_out, topk_score,
+                                  pscore, stream);
+  }
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
   if (idx.max_len > 0) {
     auto chunks_of = [&](int chunk) { return (idx.max_len + chunk - 1) / chunk; };
@@ -927,19 +836,13 @@ static int index_full_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
     }
 #undef CSA2_SCAN
   }
-  if ((idx.max_len + kBlock - 1) / kBlock <= 32 * (int64_t)kBitmapWords) {
-    hipLaunchKernelGGL(k_pool_select, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, hist, L.hist_rep,
-                       idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
-  } else {
-    // more blocks than the bitmap holds: threshold, filter into global lists, finalise
-    hipLaunchKernelGGL(k_hist_threshold, dim3(qs.m), dim3(256), 0, stream, hist, L.hist_rep, idx.seq_len, qs.seq,
-                       qs.pos, idx.ratio, P, counters);
-    const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);
-    hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, idx.seq_len, qs.seq, qs.pos,
-                       idx.ratio, P, counters, sure, tie);
-    hipLaunchKernelGGL(k_pool_finalize, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, counters, sure, tie,
-                       idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
-  }
+  hipLaunchKernelGGL(k_hist_threshold, dim3(qs.m), dim3(256), 0, stream, hist, L.hist_rep, idx.seq_len, qs.seq,
+                     qs.pos, idx.ratio, P, counters);
+  const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);
+  hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, idx.seq_len, qs.seq, qs.pos,
+                     idx.ratio, P, counters, sure, tie);
+  hipLaunchKernelGGL(k_pool_finalize, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, counters, sure, tie,
+                     idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
   return rescore_and_select<DI>(idx, qs, q_idx, w_idx, heads, pool_out, pool_count, P, K, topk_out, topk_score,
                                 pscore, stream);

@@ -46,6 +46,13 @@ int launch_rescore_select(const csa2_fp4_cache &idx, const csa2_queries &qs, con
                           const float *w_idx, int heads, const int32_t *pool, const int32_t *pool_count, int P, int K,
                           int32_t *topk_out, float *topk_score, float *pscore, hipStream_t stream);
 
+// ---- multi-query scoring (csa2_prefill.hip) ----
+// Block maxima bmax[m * nb_stride + b] of every query's visible entries from
+// the multi-query MFMA kernel (each streamed indexer entry scored against all
+// the queries of its sequence in a workgroup's query block).
+int launch_score_blocks(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
+                        const float *w_idx, int heads, float *bmax, int64_t nb_stride, hipStream_t stream);
+
 // ---- flat (prefill) indexer (csa2_prefill.hip) ----
 size_t flat_ws_bytes(int64_t max_len, int m, int top_k);
 int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
@@ -53,8 +60,10 @@ int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const u
                       hipStream_t stream);
 
 // ---- attention (csa2_attn.hip) ----
-// workspace of an attention call; its first bytes hold arrival counters that must be
-// zero before the first call with that workspace (every call leaves them zero)
+// workspace of an attention call; its first kAttnCounterBytes hold arrival counters
+// that must be zero before the first call with that workspace (every call leaves
+// them zero, whatever its shape)
+constexpr size_t kAttnCounterBytes = 4096;
 size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int window);
 int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int q_dtype, int heads,
                 const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,

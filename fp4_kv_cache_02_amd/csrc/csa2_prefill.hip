@@ -113,10 +113,13 @@ CSA2_DEV int lane_group(int i) { return NG == 4 ? 2 * (i >> 2) + (i & 1) : NG ==
 template <int NG>
 CSA2_DEV bool lane_stores(int i) { return NG == 4 ? (i & 2) == 0 : NG == 2 ? (i & 3) == 0 : i == 0; }
 
-// Grid: ceil(M / QB) workgroups of 64 * kMqWaves threads.  Rows of the
-// workgroup's A block: row = RPQ * qi + h (query m0 + qi, head h).  The
-// queries of one workgroup may belong to several sequences: each sequence is
-// one pass over its entries with the other queries left out.
+// Grid: (ceil(M / QB), column chunks) workgroups of 64 * kMqWaves threads.
+// Rows of the workgroup's A block: row = RPQ * qi + h (query m0 + qi, head
+// h).  The queries of one workgroup may belong to several sequences: each
+// sequence is one pass over its entries with the other queries left out.
+// Workgroup y of a query block takes the column tiles [y*ct, (y+1)*ct) of
+// every pass (ct = 0: all of them), so a few query blocks - the tokens of a
+// multi-token decode - still spread over the chip.
 template <int DI, int RPQ>
 __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__restrict__ codes,
                                                            const uint8_t *__restrict__ scales,
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__res
                                                            const int32_t *__restrict__ q_pos, int M,
                                                            const uint16_t *__restrict__ q_idx,
                                                            const float *__restrict__ w_idx, int H,
-                                                           float *__restrict__ bmax, int64_t nb_stride) {
+                                                           float *__restrict__ bmax, int64_t nb_stride, int ct) {
   using S = MqShape<DI, RPQ>;
   constexpr int kNone = 0x7FFFFFFF;
   __shared__ int s_seq[S::QB], s_vis[S::QB];
@@ -205,8 +208,10 @@ __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__res
     for (int p = 0; p < S::NG; ++p) vis_l[p] = s_vis[4 * p + row_tile(g)];
     const uint32_t soff = (lane_stores<S::NG>(i8) && ((act >> q_store) & 1u))
                               ? (uint32_t)((q_store * nb_stride + (n >> 3)) * 4) : kOutOfRange;
-    const int ntile = (maxvis + 15) / 16;
-    const int full = minvis / 16;  // tiles every query of the pass sees whole
+    // this workgroup's column tiles of the pass: [cb, ce)
+    const int cb = ct ? (int)blockIdx.y * ct : 0;
+    const int ntile = ct ? min((maxvis + 15) / 16, cb + ct) : (maxvis + 15) / 16;
+    const int full = min(ntile, minvis / 16);  // tiles every query of the pass sees whole
     const int64_t row0 = seq_start[sc];
     const uint8_t *cbase = codes + row0 * (DI / 2);
     const uint8_t *sbase = scales + row0 * (DI / 16);
@@ -250,13 +255,13 @@ __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__res
     // decode of tile i + 1, read from the ring, so the matrix cores and the
     // vector ALUs work on independent data and no registers hold tiles in
     // flight.
-    const int T = (full > wv) ? (full - wv + kMqWaves - 1) / kMqWaves : 0;  // this wave's whole tiles
+    const int T = (full > cb + wv) ? (full - cb - wv + kMqWaves - 1) / kMqWaves : 0;  // this wave's whole tiles
     if (T > 0) {
       using Tl = MqTile<DI>;
       const u32x4_t rc = rsrc_words(cbase, (uint32_t)maxvis * (DI / 2));
       const u32x4_t rs = rsrc_words(sbase, (uint32_t)maxvis * (DI / 16));
       const uint32_t sshift = 8u * ((uint32_t)(g * (DI / 64)) & 3u);
-      auto tile_of = [&](int i) { return wv + kMqWaves * i; };
+      auto tile_of = [&](int i) { return cb + wv + kMqWaves * i; };
       auto issue = [&](int i) {
         Tl &t = ring[wv][i % kMqRing];
         const uint32_t e = (uint32_t)(tile_of(i) * 16 + n);
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__res
       wait_vm<0>();  // the ring is idle before the next pass or the end
     }
     // the last tiles, which some query sees only in part: masked, one at a time
-    for (int c = wv + kMqWaves * T; c < ntile; c += kMqWaves) {
+    for (int c = cb + wv + kMqWaves * T; c < ntile; c += kMqWaves) {
       LaneCodes<DI> cur;
       half8_t B[S::KT];
       float4_t acc[S::RT];
@@ -375,14 +380,44 @@ static FlatWs flat_ws_layout(int64_t max_len, int m, int top_k) {
 
 size_t flat_ws_bytes(int64_t max_len, int m, int top_k) { return flat_ws_layout(max_len, m, top_k).total; }
 
+// Column chunks: enough workgroups to fill the chip when the query blocks
+// alone do not (a multi-token decode), chunks of at least 64 tiles.
 template <int DI, int RPQ>
 static void launch_score_mq(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
                             const float *w_idx, int heads, float *bmax, int64_t nb_stride, hipStream_t stream) {
   using S = MqShape<DI, RPQ>;
-  const dim3 grid((unsigned)((qs.m + S::QB - 1) / S::QB));
+  const int qb = (qs.m + S::QB - 1) / S::QB;
+  const int64_t tiles = (idx.max_len + 15) / 16;
+  int chunks = 1;
+  while ((int64_t)qb * chunks < 256 && tiles / (2 * chunks) >= 64) chunks *= 2;
+  const int ct = chunks > 1 ? (int)((tiles + chunks - 1) / chunks) : 0;
+  const dim3 grid((unsigned)qb, (unsigned)chunks);
   CSA2_TIMED_LAUNCH(kTimedScan, (k_score_mq<DI, RPQ>), grid, dim3(64 * kMqWaves), stream, idx.codes, idx.scales,
                     idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, qs.m, q_idx, w_idx, heads, bmax,
-                    nb_stride);
+                    nb_stride, ct);
+}
+
+int launch_score_blocks(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
+                        const float *w_idx, int heads, float *bmax, int64_t nb_stride, hipStream_t stream) {
+  if (idx.max_len == 0 || qs.m == 0) return CSA2_OK;
+  const bool wide = heads > 8;
+  switch (idx.dim) {
+    case 64:
+      if (wide) launch_score_mq<64, 16>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      else launch_score_mq<64, 8>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      break;
+    case 128:
+      if (wide) launch_score_mq<128, 16>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      else launch_score_mq<128, 8>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      break;
+    case 256:
+      if (wide) launch_score_mq<256, 16>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      else launch_score_mq<256, 8>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      break;
+    default:
+      return CSA2_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 
 int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
@@ -399,25 +434,9 @@ int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const u
   int32_t *pool = reinterpret_cast<int32_t *>(base + L.pool);
   int32_t *pool_count = reinterpret_cast<int32_t *>(base + L.pool_count);
   float *pscore = reinterpret_cast<float *>(base + L.pscore);
-  if (idx.max_len > 0) {
-    const bool wide = heads > 8;
-    switch (idx.dim) {
-      case 64:
-        if (wide) launch_score_mq<64, 16>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
-        else launch_score_mq<64, 8>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
-        break;
-      case 128:
-        if (wide) launch_score_mq<128, 16>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
-        else launch_score_mq<128, 8>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
-        break;
-      default:
-        if (wide) launch_score_mq<256, 16>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
-        else launch_score_mq<256, 8>(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
-        break;
-    }
-    if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
-  }
-  int st = launch_block_select(bmax, L.nb_stride, nb_max > 0 ? nb_max : 1, idx, qs, top_k, pool, pool_count,
+  int st = launch_score_blocks(idx, qs, q_idx, w_idx, heads, bmax, L.nb_stride, stream);
+  if (st != CSA2_OK) return st;
+  st = launch_block_select(bmax, L.nb_stride, nb_max > 0 ? nb_max : 1, idx, qs, top_k, pool, pool_count,
                                stream);
   if (st != CSA2_OK) return st;
   return launch_rescore_select(idx, qs, q_idx, w_idx, heads, pool, pool_count, top_k, top_k, topk_out, topk_score,

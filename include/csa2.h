@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 enum csa2_status {
   CSA2_OK = 0,
@@ -85,11 +85,19 @@ typedef struct csa2_fp4_cache {
 } csa2_fp4_cache;
 
 /* The queries of one call: query i belongs to sequence seq[i] and is token
- * pos[i] of it.  Visible entries: vis = min(seq_len, floor((pos+1)/ratio)). */
+ * pos[i] of it.  Visible entries: vis = min(seq_len, floor((pos+1)/ratio)).
+ * `run` is a host-side schedule hint: the queries come in runs of `run`
+ * consecutive entries of one sequence (several tokens of one sequence decoded
+ * together, P5 section "其他架构扩展" on parallel draft positions; a replayed
+ * window of tokens, P1 section "FP4 KV、Bounded Replay 及其他扩展").  With
+ * run >= 2 the indexers score each streamed indexer entry against all the
+ * queries of its sequence at once.  0 or 1 promises nothing; results never
+ * depend on it. */
 typedef struct csa2_queries {
   const int32_t *seq;         /* device [m] */
   const int32_t *pos;         /* device [m] */
   int32_t m;
+  int32_t run;                /* host: queries per run of one sequence (0/1: no promise) */
 } csa2_queries;
 
 /* Sliding-window KV of one layer: query i attends to rows start[i] ..
@@ -221,12 +229,15 @@ int32_t csa2_reindex(const csa2_fp4_cache *idx, const csa2_queries *qs, const ui
  * Limits: dim in {64, 128, 256, 512}; 1 <= heads <= 256; top_k <= 2048;
  *         window <= 1024.
  * Workspace: csa2_attn_workspace_size bytes (256-byte aligned), owned by
- *   the caller.  It must be zero-filled before its first use; every call
- *   leaves its counter words zero again, so a workspace reused by calls on
- *   one stream needs no further clearing.  Calls that run at the same time
- *   must not share a workspace.
+ *   the caller.  Its first CSA2_ATTN_COUNTER_BYTES (or all of it, when
+ *   smaller) hold arrival counters: zero-fill them before the workspace's
+ *   first use.  Every call leaves them zero again, whatever its shape, so a
+ *   workspace reused by attention or group calls of any shape on one stream
+ *   needs no further clearing; writing anything else there breaks the next
+ *   call.  Calls that run at the same time must not share a workspace.
  * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED, WORKSPACE, HIP.
  * ------------------------------------------------------------------- */
+#define CSA2_ATTN_COUNTER_BYTES 4096u
 int32_t csa2_attn_workspace_size(int32_t m, int32_t heads, int32_t dim, int32_t top_k,
                                  int32_t window, size_t *bytes);
 int32_t csa2_sparse_swa_attn(const csa2_fp4_cache *kv, const csa2_queries *qs, const void *q,
@@ -285,9 +296,11 @@ typedef struct csa2_group_desc {
 } csa2_group_desc;
 
 /* Workspace of csa2_group_step: csa2_group_workspace_size bytes, 256-byte
- * aligned, zero-filled before its first use (the attention part of it keeps
- * counter words that every call leaves zero); not shared by calls that run
- * at the same time. */
+ * aligned.  Its first CSA2_ATTN_COUNTER_BYTES are the attention calls'
+ * arrival counters, at that offset for every group shape: zero-fill them
+ * before the workspace's first use; every call leaves them zero, so groups
+ * of any shape may then share the workspace on one stream.  The rest needs
+ * no initial contents.  Not shared by calls that run at the same time. */
 int32_t csa2_group_workspace_size(const csa2_group_desc *g, size_t *bytes);
 int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_bytes, void *stream);
 
@@ -300,7 +313,9 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
  * stream) on a scratch array the library owns: one copy of
  * CSA2_STATIC_SCRATCH_BYTES per GPU, held from the first call on that GPU
  * until the process ends.  The call allocates nothing (no hipMalloc, no
- * allocating library routine) and needs no initial scratch contents.
+ * allocating library routine).  The array starts zero and every call leaves
+ * its counter region (the workspace's first CSA2_ATTN_COUNTER_BYTES) zero,
+ * so calls of any shape follow one another with nothing to clear.
  * Every call on one GPU shares that GPU's array: calls that overlap in time
  * on one GPU (other streams, other host threads) race and must be ordered
  * by the caller, e.g. on one stream.

@@ -208,4 +208,20 @@ def workload(cfg: int) -> Workload:
     if cfg == 4:
         return Workload(4, "long-decode-4x1m", "decode", [1 << 20] * 4, 512, 64, "bf16", 8, 128, 2048, 512, 128,
                         1, DECODER_GROUPS)
+    if cfg == 5:
+        # one decode token through the whole 40-layer encoder-decoder: the
+        # encoder's 2 window-only layers and 3 groups at ratio 2 over the
+        # tokens' 524,288 compressed entries, then the 20-layer decoder
+        return Workload(5, "ced-decode-4x1m", "decode", [1 << 20] * 4, 512, 64, "bf16", 8, 128, 2048, 512, 128,
+                        1, DECODER_GROUPS,
+                        extra={"encoder_groups": ENCODER_GROUPS, "encoder_ratio": 2, "encoder_pool_blocks": 512,
+                               "swa_only_layers": 2})
+    if cfg == 6:
+        # several decode tokens per sequence (drafted positions verified together)
+        return Workload(6, "multi-token-decode-4x1m-t4", "decode", [1 << 20] * 4, 512, 64, "bf16", 8, 128, 2048,
+                        512, 128, 1, DECODER_GROUPS, extra={"tokens_per_seq": 4})
+    if cfg == 7:
+        # the decoder's window state rebuilt by replaying the last 128 tokens of a 1M-token prompt
+        return Workload(7, "replay-128-1m", "decode", [1 << 20], 512, 64, "bf16", 8, 128, 2048, 512, 128, 1,
+                        DECODER_GROUPS, extra={"tokens_per_seq": 128})
     raise ValueError(cfg)

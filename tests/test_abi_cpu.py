@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert csa2.csa2_abi_version() == 1
+    assert csa2.csa2_abi_version() == 2
     assert csa2.status_string(0) == "ok"
     assert csa2.status_string(WORKSPACE).startswith("workspace")
     assert csa2.status_string(12345) == "unknown status"

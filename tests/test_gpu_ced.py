@@ -1,0 +1,130 @@
+"""GPU parity of one decode token through the whole causal encoder-decoder.
+
+The encoder runs 2 window-only layers and 3 CSA2 groups at ratio 2 (Full + 5
+Reuse, each Full layer with its own caches, writing the compressed entry the
+token completes), the decoder its 20 layers (P1 sections "Causal
+Encoder-Decoder" and "Compressed Sparse Attention 2 (CSA2)"; P2 section 03:
+every layer except the encoder's first two uses CSA2 for its global branch).
+The encoder's flat Top-K is computed from a pool of K blocks (every flat
+Top-K position lies in the top K blocks); it is compared with the oracle's
+flat Top-K over every visible entry, modulo the near-tie band, and every
+layer's attention is checked on the GPU's own list.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp4_kv_cache_02_amd as csa2
+import synth
+from oracle import attention, codec, group as ogroup, indexer
+from tests._gpu_util import announce, assert_sets_equal_modulo_band, dev, empty_u8, h, t
+from tests.test_gpu_group import _Decoder, _check_attn_one
+
+pytestmark = pytest.mark.gpu
+
+D, H, DI, HI, K, W, R = 512, 64, 128, 8, 512, 128, 2
+
+
+def _window(cfg, layer, M):
+    sw = synth.swa_rows(cfg, layer, 0, M * W, D)
+    sc, ss = empty_u8(M * W, D), torch.empty((M * W,), dtype=torch.float32, device=dev())
+    csa2.csa2_quantize_fp8_rows(t(sw), sc, ss)
+    c8, s8 = codec.fp8_rows_encode(sw)
+    assert np.array_equal(h(sc), c8) and np.array_equal(h(ss), s8)
+    return csa2.swa(sc, ss, t(np.arange(M, dtype=np.int32) * W), t(np.full(M, W, np.int32)), D, W), c8, s8
+
+
+def _query(cfg, layer, M):
+    qb = synth.q_main(cfg, layer, M, H, D, "bf16")
+    return t(qb).view(torch.bfloat16), synth.bf16_bits_to_f32(qb).astype(np.float64)
+
+
+def test_ced_decode_step_40_layers():
+    cfg = 700
+    tokens = [16384, 9000]                     # the decode token is token len-1 (it completes an entry)
+    M = len(tokens)
+    dec = _Decoder(cfg, tokens, D, H, "bf16", DI, HI, 2048, K, W, raw=True)
+    tau = D ** -0.5
+
+    # ---- encoder layers 0-1: window only ----
+    for layer in range(2):
+        announce("CED window-only layer", layer)
+        q, qf = _query(cfg, 100 + layer, M)
+        sw, c8, s8 = _window(cfg, 100 + layer, M)
+        out = torch.full((M, H, D), 7.0, dtype=torch.float32, device=dev())
+        lse = torch.full((M, H), 7.0, dtype=torch.float32, device=dev())
+        ws = torch.zeros((csa2.csa2_attn_workspace_size(M, H, D, 0, W),), dtype=torch.uint8, device=dev())
+        csa2.csa2_sparse_swa_attn(dec.kv, dec.qs, q, None, 0, sw, tau, out, lse, ws)
+        go, gl = h(out), h(lse)
+        for i in range(M):
+            o_ref, l_ref = attention.sparse_swa_attention(qf[i], np.zeros((0, D // 2), np.uint8),
+                                                          np.zeros((0, D // 16), np.uint8), [], 0,
+                                                          c8[i * W:(i + 1) * W], s8[i * W:(i + 1) * W], tau)
+            _check_attn_one(o_ref, l_ref, go[i], gl[i])
+
+    # ---- encoder groups: ratio 2, flat Top-K through a K-block pool ----
+    elens = np.asarray(tokens) // R
+    starts = np.concatenate([[0], np.cumsum(elens)[:-1]]).astype(np.int64)
+    n_ent = int(elens.sum())
+    w_ik = synth.w_ik(cfg + 1, D, DI)
+    layer = 102
+    for gi in range(3):
+        announce("CED encoder group", gi)
+        rc, rs = synth.fp4_bytes(cfg + 10 + gi, 0, n_ent, D)
+        ikc, iks = synth.fp4_bytes(cfg + 10 + gi, 1, n_ent, DI)
+        dst = (starts + elens - 1).astype(np.int64)
+        kv_c, kv_s, ik_c, ik_s = (t(a.copy()) for a in (rc, rs, ikc, iks))
+        new_x = synth.gaussian_rows(cfg + 10 + gi, synth.TAG_MAIN_KV, 1, 0, 0, M, D)
+        nc, ns = codec.fp4_encode(new_x)
+        nic, nis = codec.indexer_key(nc, ns, w_ik)
+        rc[dst], rs[dst], ikc[dst], iks[dst] = nc, ns, nic, nis
+        st, ln = t(starts), t(elens.astype(np.int32))
+        kv = csa2.fp4_cache(kv_c, kv_s, st, ln, D, int(elens.max()), R)
+        ik = csa2.fp4_cache(ik_c, ik_s, st, ln, DI, int(elens.max()), R)
+        qi, wi = synth.q_idx(cfg, layer, M, HI, DI), synth.w_idx(cfg, layer, M, HI)
+        qs_l, ws_l, outs, lses, ref_layers = [], [], [], [], []
+        for l in range(layer, layer + 6):
+            q, qf = _query(cfg, l, M)
+            sw, c8, s8 = _window(cfg, l, M)
+            qs_l.append(q)
+            ws_l.append(sw)
+            outs.append(torch.empty((M, H, D), dtype=torch.float32, device=dev()))
+            lses.append(torch.empty((M, H), dtype=torch.float32, device=dev()))
+            ref_layers.append((qf, c8, s8))
+        topk = torch.full((M, K), -7, dtype=torch.int32, device=dev())
+        pool = torch.full((M, K), -7, dtype=torch.int32, device=dev())
+        cnt = torch.full((M,), -7, dtype=torch.int32, device=dev())
+        g = csa2.Group(csa2.CSA2_MODE_FULL, kv, ik, dec.qs, t(qi).view(torch.bfloat16), t(wi), K, K, pool, cnt, topk,
+                       None, qs_l, csa2.CSA2_BF16, H, ws_l, outs, lses, tau, new_kv=t(new_x), new_dst_row=t(dst),
+                       w_ik=t(w_ik))
+        ws = torch.zeros((csa2.csa2_group_workspace_size(g),), dtype=torch.uint8, device=dev())
+        csa2.csa2_group_step(g, ws)
+        assert np.array_equal(h(kv_c), rc) and np.array_equal(h(kv_s), rs), "encoder cache after the write"
+        assert np.array_equal(h(ik_c), ikc) and np.array_equal(h(ik_s), iks), "encoder keys after the write"
+        gtopk = h(topk)
+        go = [(h(o), h(l)) for o, l in zip(outs, lses)]
+        qf_i = synth.bf16_bits_to_f32(qi)
+        for i in range(M):
+            s0, e = int(starts[i]), int(elens[i])
+            tok = tokens[i] - 1
+            assert indexer.visible_count(e, tok, R) == e
+            layers_i = [(qf[i], c8[i * W:(i + 1) * W], s8[i * W:(i + 1) * W]) for qf, c8, s8 in ref_layers]
+            ref = ogroup.encoder_group_query(rc[s0:s0 + e], rs[s0:s0 + e], ikc[s0:s0 + e], iks[s0:s0 + e], tok, R,
+                                             qf_i[i], wi[i], K, layers_i, tau)
+            sel = gtopk[i][gtopk[i] >= 0]
+            assert len(sel) == K and np.all(np.diff(sel) > 0)
+            s = ref["scores"]
+            assert_sets_equal_modulo_band(sel, ref["idx"][ref["idx"] >= 0], lambda j: s[j], K,
+                                          what=f"encoder group {gi} q{i}")
+            for l, (qf, c8, s8) in enumerate(layers_i):
+                o_ref, l_ref = attention.sparse_swa_attention(qf, rc[s0:s0 + e], rs[s0:s0 + e], gtopk[i], e, c8, s8,
+                                                              tau)
+                _check_attn_one(o_ref, l_ref, go[l][0][i], go[l][1][i])
+        layer += 6
+
+    # ---- decoder: 5 groups, 20 layers ----
+    layer0 = 0
+    for mode in ["full"] + ["reindex"] * 4:
+        announce("CED decoder group", mode, layer0)
+        dec.run_group(mode, layer0, 4)
+        layer0 += 4

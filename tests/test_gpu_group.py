@@ -13,7 +13,7 @@ import torch
 import fp4_kv_cache_02_amd as csa2
 import synth
 from oracle import attention, codec, group as ogroup, indexer
-from tests._gpu_util import announce, assert_sets_equal_modulo_band, dev, empty_u8, h, t
+from tests._gpu_util import announce, assert_sets_equal_modulo_band, dev, empty_u8, h, random_group, t
 
 pytestmark = pytest.mark.gpu
 
@@ -240,3 +240,26 @@ def test_encoder_group_step_matches_oracle():
             o_ref, l_ref = attention.sparse_swa_attention(qm, rc, rs, indexer.reuse(gtopk[i]), vis, c8, s8,
                                                           D ** -0.5)
             _check_attn_one(o_ref, l_ref, outs[layer][0][i], outs[layer][1][i])
+
+
+def test_group_workspace_shared_by_groups_of_other_shapes():
+    """One caller workspace, zeroed once, serves a large group and then a
+    smaller one: the attention counters sit at the same offset for every shape
+    and every call leaves them zero, so each result equals that of a fresh
+    workspace (same kernels, same inputs: bit-identical)."""
+    big, small = random_group(611, [70000, 33333], 3), random_group(612, [9000], 2)
+    g_big, _ = big()
+    shared = torch.zeros((csa2.csa2_group_workspace_size(g_big),), dtype=torch.uint8, device=dev())
+    for label, outputs in (("large group", big), ("smaller group", small), ("large group again", big)):
+        g_ref, ref = outputs()
+        announce("group step, fresh workspace", label)
+        csa2.csa2_group_step(g_ref, torch.zeros((csa2.csa2_group_workspace_size(g_ref),), dtype=torch.uint8,
+                                                device=dev()))
+        g_got, got = outputs()
+        announce("group step, shared workspace", label)
+        csa2.csa2_group_step(g_got, shared)
+        torch.cuda.synchronize()
+        for a, b in zip(ref, got):
+            assert np.array_equal(h(a), h(b), equal_nan=True), label
+        assert not np.any(h(got[4]) == 7.0), label    # every output row written
+        assert np.all(h(shared[:csa2.CSA2_ATTN_COUNTER_BYTES]) == 0), label

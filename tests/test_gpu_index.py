@@ -127,6 +127,48 @@ def test_index_c4_full_oracle_pass(shape):
         _check_query(rc, rs, starts[sq], vis, qf[i], wi[i], P, K, gpool[i], gcnt[i], gtopk[i], gsc[i])
 
 
+@pytest.mark.parametrize("shape", ["decode_4tok_64k", "replay_128tok_256k", "decode_4tok_1m"])
+def test_index_full_runs_of_tokens(shape):
+    """Queries in runs of consecutive tokens of one sequence (run hint >= 2):
+    several decode tokens per sequence (drafted positions verified together)
+    and a replayed window of 128 tokens with a pool per query.  Every streamed
+    indexer entry is scored against all the queries of its sequence at once;
+    the pool comes from the block maxima directly (up to 65,536 blocks) or
+    through the block-maximum histogram (1M entries).  Each query's pool and
+    Top-K are compared element by element with a full fp64 oracle pass,
+    modulo the near-tie band.  Caches are raw FP4 bytes."""
+    if shape == "decode_4tok_64k":
+        lens, cfg, run = [65536, 40000], 120, 4
+    elif shape == "replay_128tok_256k":
+        lens, cfg, run = [262144], 121, 128
+    else:
+        lens, cfg, run = [1 << 20, 700001], 122, 4
+    q_seq = [s for s in range(len(lens)) for _ in range(run)]
+    q_pos = [lens[s] - run + k for s in range(len(lens)) for k in range(run)]
+    di, H, P, K = 128, 8, 2048, 512
+    announce("index runs of tokens", shape)
+    rc, rs = synth.fp4_bytes(cfg, 0, sum(lens), di)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    M = len(q_seq)
+    qi, wi = synth.q_idx(cfg, 0, M, H, di), synth.w_idx(cfg, 0, M, H)
+    cache = csa2.fp4_cache(t(rc), t(rs), t(starts), t(np.asarray(lens, np.int32)), di, max(lens), 1)
+    qs = csa2.queries(t(np.asarray(q_seq, np.int32)), t(np.asarray(q_pos, np.int32)), run=run)
+    ws = workspace(csa2.csa2_index_workspace_size(cache, M, P, K))
+    pool = torch.full((M, P), -7, dtype=torch.int32, device=dev())
+    cnt = torch.full((M,), -7, dtype=torch.int32, device=dev())
+    topk = torch.full((M, K), -7, dtype=torch.int32, device=dev())
+    sc = torch.full((M, K), -7.0, dtype=torch.float32, device=dev())
+    csa2.csa2_index_full(cache, qs, t(qi).view(torch.bfloat16), t(wi), P, K, pool, cnt, topk, sc, ws)
+    gpool, gcnt, gtopk, gsc = h(pool), h(cnt), h(topk), h(sc)
+    qf = synth.bf16_bits_to_f32(qi)
+    # a sample of the 128 replayed tokens (every query for the decode shapes)
+    check = range(M) if run <= 4 else sorted(set([0, M - 1] + list(range(1, M - 1, 9))))
+    for i in check:
+        sq = q_seq[i]
+        vis = indexer.visible_count(lens[sq], q_pos[i], 1)
+        _check_query(rc, rs, starts[sq], vis, qf[i], wi[i], P, K, gpool[i], gcnt[i], gtopk[i], gsc[i])
+
+
 def test_index_all_equal_scores_take_lowest_ids():
     announce("index_full ties")
     lens, di, H, P, K = [3001], 64, 4, 10, 50
