@@ -18,7 +18,6 @@ CSA2_OK = 0
 CSA2_F32, CSA2_BF16 = 0, 1
 CSA2_MODE_FULL, CSA2_MODE_REINDEX = 0, 1
 CSA2_STATIC_SCRATCH_BYTES = 64 << 20   # include/csa2.h
-CSA2_ATTN_COUNTER_BYTES = 4096          # include/csa2.h
 
 EXPORTS = [
     "csa2_abi_version", "csa2_status_string", "csa2_quantize_fp4", "csa2_quantize_fp8_rows",

@@ -217,7 +217,7 @@ int32_t csa2_attn_workspace_size(int32_t m, int32_t heads, int32_t dim, int32_t 
                                  size_t *bytes) {
   if (!bytes) return CSA2_ERR_NULL_ARG;
   if (m < 0 || heads < 1 || dim <= 0 || top_k < 0 || window < 0) return CSA2_ERR_BAD_SHAPE;
-  *bytes = (m == 0) ? 256 : attn_ws_bytes(m, heads, dim, top_k, window);
+  *bytes = (m == 0) ? 256 : attn_ws_bytes(m, heads, dim, top_k, window, 1);
   return CSA2_OK;
 }
 
@@ -238,27 +238,27 @@ int32_t csa2_sparse_swa_attn(const csa2_fp4_cache *kv, const csa2_queries *qs, c
   if (qs->m == 0) return CSA2_OK;
   if (!q || !out) return CSA2_ERR_NULL_ARG;
   if (top_k > 0 && !topk) return CSA2_ERR_NULL_ARG;
-  const size_t need = attn_ws_bytes(qs->m, heads, kv->dim, top_k, swa->window);
+  const size_t need = attn_ws_bytes(qs->m, heads, kv->dim, top_k, swa->window, 1);
   if (need > 256 && (!workspace || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   if (workspace && !aligned(workspace, 256)) return CSA2_ERR_MISALIGNED;
-  return launch_attn(*kv, *qs, q, q_dtype, heads, topk, top_k, *swa, softmax_scale, out, lse, workspace,
-                     (hipStream_t)stream);
+  const AttnLayer layer{q, swa->codes, swa->scale, swa->start, swa->count, swa->window, out, lse};
+  return launch_attn_layers(*kv, *qs, q_dtype, heads, topk, top_k, &layer, 1, softmax_scale, workspace,
+                            (hipStream_t)stream);
 }
 
-// Group workspace: the attention region at offset 0 (its arrival counters sit
-// in the first kAttnCounterBytes of every group workspace whatever the group's
-// shape, so calls of different shapes on one workspace all find them zero),
-// then the indexer's region, which every index call initialises itself.
-static_assert(kAttnCounterBytes == CSA2_ATTN_COUNTER_BYTES, "counter region of the header");
+static_assert(kAttnBatch >= 1, "attention batches");
 
+// Group workspace: the attention region (its layers' intermediates), then the
+// indexer's region.  Neither needs initial contents.
+static int group_max_window(const csa2_group_desc *g) {
+  int w = 0;
+  for (int i = 0; i < g->n_layers; ++i) w = std::max(w, g->swa ? g->swa[i].window : 0);
+  return w;
+}
 static size_t group_index_offset(const csa2_group_desc *g) {
-  size_t b = kAttnCounterBytes;
-  for (int i = 0; i < g->n_layers; ++i) {
-    const int w = g->swa ? g->swa[i].window : 0;
-    const size_t x = attn_ws_bytes(g->qs.m > 0 ? g->qs.m : 1, g->heads, g->kv.dim, g->top_k, w);
-    if (x > b) b = x;
-  }
-  return align256(b);
+  const size_t a = attn_ws_bytes(g->qs.m > 0 ? g->qs.m : 1, g->heads, g->kv.dim, g->top_k, group_max_window(g),
+                                 g->n_layers);
+  return align256(std::max<size_t>(256, a));
 }
 
 int32_t csa2_group_workspace_size(const csa2_group_desc *g, size_t *bytes) {
@@ -320,12 +320,14 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
                         g->top_k, g->topk, g->topk_score, iws, s);
   }
   if (st) return st;
+  AttnLayer layers[64];
   for (int i = 0; i < g->n_layers; ++i) {
-    st = launch_attn(g->kv, g->qs, g->q[i], g->q_dtype, g->heads, g->topk, g->top_k, g->swa[i], g->softmax_scale,
-                     g->out[i], g->lse ? g->lse[i] : nullptr, workspace, s);
-    if (st) return st;
+    const csa2_swa &w = g->swa[i];
+    layers[i] = AttnLayer{g->q[i], w.codes, w.scale, w.start, w.count, w.window, g->out[i],
+                          g->lse ? g->lse[i] : nullptr};
   }
-  return CSA2_OK;
+  return launch_attn_layers(g->kv, g->qs, g->q_dtype, g->heads, g->topk, g->top_k, layers, g->n_layers,
+                            g->softmax_scale, workspace, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -364,8 +366,7 @@ int32_t csa2_group_step_static(const csa2_group_desc *g, void *stream) {
   if (need > (size_t)CSA2_STATIC_SCRATCH_BYTES) return CSA2_ERR_WORKSPACE;
   void *p = nullptr;
   if ((st = static_scratch(&p))) return st;
-  // the array starts zero (.bss); every call leaves its attention counters,
-  // which sit at offset 0 whatever the group's shape, zero again
+  // no call needs initial scratch contents
   return csa2_group_step(g, p, (size_t)CSA2_STATIC_SCRATCH_BYTES, stream);
 }
 

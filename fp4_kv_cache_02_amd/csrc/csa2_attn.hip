@@ -7,18 +7,18 @@
 //
 // Two schedules compute the same thing:
 //
-// * Few queries (decode): k_attn_decode, one workgroup per (64 output dims,
-//   query, 16 heads).  Its waves decode FP4 key rows straight into MFMA
-//   operand registers, keep the logits in registers, and meet only for the
-//   softmax statistics; the 64-dim V slice and P pass through LDS.  The
-//   logits are recomputed by each output slice, which costs spare MFMA time
-//   but makes one short kernel per layer: the grid covers the chip even for
-//   four queries, with no workspace and no partial outputs to merge.
+// * Few queries (decode): two kernels per batch of layers that share the
+//   Top-K list and the main cache (a layer group).  k_attn_logits decodes
+//   each 32-slot key chunk once and computes its logits for every layer and
+//   head, storing p relative to the chunk maximum plus the chunk statistics;
+//   k_attn_pv weights the chunks by those statistics and multiplies P by
+//   its 32-dim slice of V.  No partial outputs are merged.
 // * Many queries (prefill): k_attn, one workgroup per (query, 64 heads),
-//   streams 64-key sub-chunks with an online softmax (flash style).
+//   streams 64-key sub-chunks with an online softmax (flash style); the
+//   512-channel bf16 case runs the prefill kernel of csa2_attn_prefill.hip.
 //
-// A decoded key tile (flash) or V slice (decode) sits in LDS as row-major f16
-// [key][dim]: S = Q K^T reads the tile as the MFMA B operand, and O = P V reads it through the gfx950
+// A decoded key tile sits in LDS as row-major f16 [key][dim]: S = Q K^T
+// reads it as the MFMA B operand, and O = P V reads it through the gfx950
 // transposing LDS load (ds_read_b64_tr_b16), which hands each lane four
 // consecutive keys of one dimension - the B operand of the P V product -
 // without a transposed copy.  Both products run on v_mfma_f32_16x16x32_f16.
@@ -172,32 +172,55 @@ CSA2_DEV void qk_tile(const _Float16 *kt, int KT, const half8_t *qa, const half8
 }
 
 // ===========================================================================
-// decode schedule: key splits + merge
+// decode schedule: logits by key chunk, then P V by output dims
 // ===========================================================================
+//
+// Phase 1, k_attn_logits: one workgroup per (key chunk of 32 slots, query,
+// layer).  It decodes the chunk's 32 keys into LDS - FP4 Top-K rows of the
+// shared main cache or FP8 rows of the layer's window - and computes their
+// logits for every head: p = 2^(z - m_c) stored as f16 (z the log2-domain
+// logit, m_c the chunk's maximum) with the chunk statistics (m_c, sum p).
+// A window row's p carries its row scale r and a power-of-two lift 2^e_c
+// (r_max * 2^e_c in [1, 2)) that keeps p * r clear of the f16 subnormals.
+// The layer-0 workgroups of the Top-K chunks also copy the chunk's raw FP4
+// rows into a gathered array, and the window workgroups their FP8 rows, so
+// phase 2 reads every key at a fixed place: no load of it waits for another.
+//
+// Phase 2, k_attn_pv: one workgroup per (32 output dims, query, layer).
+// The chunk statistics give each head its maximum M and sum L and each chunk
+// the weight w_c = 2^(m_c - M - e_c) / L; the workgroup decodes its 32-dim
+// slice of every key slot (256 per block) into LDS and accumulates
+// O += w_c * (P_c V_c) per 32-slot chunk: the chunk product on MFMA, the
+// weighting in fp32.  No partial outputs, no merge, no atomics.
 
-constexpr int kSW = 4;                   // waves per split workgroup (one per SIMD)
-constexpr int kSH = 16;                  // heads per split workgroup
-constexpr int kSKeys = 128;              // key slots per split: 8 tiles of 16, two per wave
-constexpr int kMaxSplits = (2048 + 1024) / kSKeys;   // Top-K <= 2048 slots, window <= 1024 rows
+constexpr int kChunk = 32;                        // key slots per logit chunk = one P V k-step
+constexpr int kPvKeys = 256;                      // key slots per P V block (one per thread)
+constexpr int kPvHeads = 64;                      // heads per P V workgroup
+constexpr int kMaxChunks = (2048 + 1024) / kChunk;
 
-template <int D, bool QF32>
-struct SplitLds {
-  static constexpr int VT = D + 8;       // [key][dim] row stride of the decoded keys (f16)
-  static constexpr int PT = kSKeys + 8;  // [head][key] row stride of P (f16)
-  static constexpr int QT = D + 8;       // [head][dim] row stride of the staged queries (f16)
-  _Float16 vt[kSKeys * VT];
-  _Float16 p[kSH * PT];
-  _Float16 q[(QF32 ? 2 : 1) * kSH * QT];  // hi parts, then lo parts (fp32 queries)
-  float wmax[kSW][kSH];
-  float wsum[kSW][kSH];
-  float rm[kSW];
-  float lsall[kMaxSplits * kSH];         // every split's lse (the merging workgroup)
-  uint32_t prev;                         // arrival count seen by this workgroup
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+struct AttnBatch {
+  AttnLayer l[kAttnBatch];
 };
+
+// Workgroups go to the 8 XCDs round-robin by linear id, and each XCD has its
+// own L2.  The decode kernels run a grid of (M * per, layers) workgroups and
+// map x to (query m, member k) = (x % M, x / M): the `per` members of a query
+// - the workgroups that read the same queries or the same p values - then
+// sit on the XCDs m + M k (mod 8), a single XCD when M is a multiple of 8 and
+// M | 8 XCDs otherwise when M divides 8.  The layer comes from blockIdx.y.
+CSA2_DEV void xcd_group(int x, int M, int &m, int &k) {
+  m = x % M;
+  k = x / M;
+}
+static unsigned xcd_grid(int per, int groups) { return (unsigned)(per * groups); }
 
 // Buffer loads (make_rsrc, kOutOfRange) make every load unconditional: empty,
 // padded or invisible keys and heads beyond H are read at out-of-range
-// offsets, which return zeros.
+// offsets, which return zeros.  Loads that stay unconditional also keep the
+// number of loads in flight fixed, so the compiler waits only for the ones
+// it needs.
 template <int BYTES>
 CSA2_DEV void buffer_load_words(uint32_t *dst, rsrc_t r, uint32_t off) {
   if constexpr (BYTES >= 16) {
@@ -217,357 +240,493 @@ CSA2_DEV void buffer_load_words(uint32_t *dst, rsrc_t r, uint32_t off) {
     dst[0] = __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
   }
 }
+template <int BYTES>
+CSA2_DEV void buffer_store_words(const uint32_t *src, rsrc_t r, uint32_t off) {
+  if constexpr (BYTES >= 16) {
+#pragma unroll
+    for (int i = 0; i < BYTES / 16; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){src[4 * i], src[4 * i + 1], src[4 * i + 2], src[4 * i + 3]}, r,
+                                             off + 16 * i, 0, 0);
+  } else if constexpr (BYTES == 8) {
+    __builtin_amdgcn_raw_buffer_store_b64((u32x2_t){src[0], src[1]}, r, off, 0, 0);
+  } else if constexpr (BYTES == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32(src[0], r, off, 0, 0);
+  } else if constexpr (BYTES == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)src[0], r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)src[0], r, off, 0, 0);
+  }
+}
 
-// The lane's share of one 16-key tile: lane (key row, quad) holds dims
-// quad*(D/4) .. +D/4 of its key - D/8 FP4 code bytes plus D/64 E4M3 scale
-// bytes of a Top-K row, or D/4 FP8 code bytes of a window row.
-template <int D, bool MAIN>
-struct KeyShare {
-  uint32_t w[MAIN ? D / 32 : D / 16];
-  uint32_t s[MAIN ? (D / 64 + 3) / 4 : 1];
+// Two fp32 values with at most 8 significant bits -> their bf16 pair (low
+// half first), exact: the upper halves of the fp32 bit patterns.
+CSA2_DEV uint32_t bf16_pair(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Raw bytes of N consecutive dims (from dim d0, N % 8 == 0) of one FP4 row:
+// N/2 code bytes and their E4M3 scale bytes.  Decoding gives exact values:
+// e2m1 * e4m3 products have at most 6 significant bits, so they are f16 and
+// bf16 numbers alike.
+template <int D, int N>
+struct Fp4Piece {
+  static constexpr int SB = (N >= 16) ? N / 16 : 1;   // scale bytes loaded
+  uint32_t w[N / 8];
+  uint32_t s[(SB + 3) / 4];
+  CSA2_DEV void load(rsrc_t codes, rsrc_t scales, bool ok, uint32_t j, int d0) {
+    buffer_load_words<N / 2>(w, codes, ok ? j * (D / 2) + d0 / 2 : kOutOfRange);
+    buffer_load_words<SB>(s, scales, ok ? j * (D / 16) + d0 / 16 : kOutOfRange);
+  }
+  CSA2_DEV void store(rsrc_t codes, rsrc_t scales, uint32_t j, int d0) const {
+    buffer_store_words<N / 2>(w, codes, j * (D / 2) + d0 / 2);
+    buffer_store_words<SB>(s, scales, j * (D / 16) + d0 / 16);
+  }
+  // scale byte of dims d0 + 8u .. +7 (d0 % 16 == 0 when N >= 16)
+  CSA2_DEV uint32_t scale_byte(int u) const {
+    const int g = (N >= 16) ? (8 * u) / 16 : 0;
+    return s[g / 4] >> (8 * (g % 4));
+  }
+  // dims d0 + 8u .. +7 as f16
+  CSA2_DEV half8_t get(int u) const { return fp4x8_dequant_f16(w[u], e4m3x2_to_f16(scale_byte(u))[0]); }
+  // dims d0 + 8u .. +7 as bf16 (four pairs)
+  CSA2_DEV u32x4_t get_bf16(int u) const {
+    const float sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(scale_byte(u), 1.0f, false)[0];
+    const float2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 0);
+    const float2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 1);
+    const float2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 2);
+    const float2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 3);
+    return (u32x4_t){bf16_pair(f0[0] * sc, f0[1] * sc), bf16_pair(f1[0] * sc, f1[1] * sc),
+                     bf16_pair(f2[0] * sc, f2[1] * sc), bf16_pair(f3[0] * sc, f3[1] * sc)};
+  }
+};
+// Raw bytes of N consecutive dims of one FP8 window row (E4M3 codes; the row
+// scale is applied elsewhere).
+template <int N>
+struct Fp8Piece {
+  uint32_t w[N / 4];
+  CSA2_DEV void load(rsrc_t codes, bool ok, uint32_t row, int d0, int D) {
+    buffer_load_words<N>(w, codes, ok ? row * (uint32_t)D + d0 : kOutOfRange);
+  }
+  CSA2_DEV void store(rsrc_t codes, uint32_t row, int d0, int D) const {
+    buffer_store_words<N>(w, codes, row * (uint32_t)D + d0);
+  }
+  CSA2_DEV half8_t get(int u) const { return e4m3x8_to_f16(w[2 * u], w[2 * u + 1]); }
+  CSA2_DEV u32x4_t get_bf16(int u) const {
+    const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[2 * u], 1.0f, false);
+    const float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[2 * u], 1.0f, true);
+    const float2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[2 * u + 1], 1.0f, false);
+    const float2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[2 * u + 1], 1.0f, true);
+    return (u32x4_t){bf16_pair(a[0], a[1]), bf16_pair(b[0], b[1]), bf16_pair(c[0], c[1]), bf16_pair(d[0], d[1])};
+  }
 };
 
-// The f16 B operand of k-step kk (dims quad*(D/4) + 8*kk .. +7 of the lane's key).
-template <int D, bool MAIN>
-CSA2_DEV half8_t key_operand(const KeyShare<D, MAIN> &u, int kk) {
-  if constexpr (MAIN) {
-    const uint32_t sw = u.s[kk / 8] >> (8 * ((kk / 2) % 4));   // scale byte kk/2 of the lane's share
-    return fp4x8_dequant_f16(u.w[kk], e4m3x2_to_f16(sw)[0]);
-  } else {
-    return e4m3x8_to_f16(u.w[2 * kk], u.w[2 * kk + 1]);
-  }
-}
-
-// Partial outputs are kept in the MFMA accumulator layout: per (query, head
-// block, split) a block of 4 waves x 64 lanes x (D/64 tiles x 4) floats, each
-// lane's floats contiguous, so both the split kernel and the merge move them
-// as 16-byte vectors.
-template <int D>
-CSA2_DEV int64_t part_offset(int64_t grp, int wave, int lane) {
-  return ((grp * kSW + wave) * 64 + lane) * (D / 16);
-}
-
-// The workgroup's final output: lane (dim row, quad) of wave w holds heads
-// 4*quad + j at dims w*(D/4) + 16*t + row; lse (natural log) from wave 0.
-template <int D>
-CSA2_DEV void store_output(const float4_t (&acc)[D / 64], const float (&ls2)[4], float *__restrict__ out,
-                           float *__restrict__ lse, int H, int m, int hb, int wv, int row, int quad) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int h = hb * kSH + 4 * quad + j;
-    if (h >= H) continue;
-#pragma unroll
-    for (int t = 0; t < D / 64; ++t) out[((int64_t)m * H + h) * D + wv * (D / 4) + 16 * t + row] = acc[t][j];
-    if (lse && wv == 0 && row == 0) lse[(int64_t)m * H + h] = ls2[j] * 0.6931471805599453f;
-  }
-}
-
-// One split: wave w owns tiles 2w and 2w+1 of the split's 128 key slots.
-template <int D, bool QF32, bool MAIN>
-CSA2_DEV void attn_split_body(SplitLds<D, QF32> &L, const void *__restrict__ q_any, int H,
-                              const uint8_t *__restrict__ kv_codes, const uint8_t *__restrict__ kv_scales,
-                              int64_t row0, int64_t vis, const int32_t *__restrict__ topk, int K, int sp0, int m,
-                              int hb, const uint8_t *__restrict__ swa_codes, const float *__restrict__ swa_scale,
-                              int64_t wstart, int wcount, float tau2, float *__restrict__ part_o,
-                              float *__restrict__ part_lse, uint32_t *__restrict__ counters, int64_t grp, int sp,
-                              int S, int HB, float *__restrict__ out, float *__restrict__ lse) {
-  using Lds = SplitLds<D, QF32>;
-  constexpr int NK = D / 32;             // MFMA k-steps per key
-  constexpr int NDT = D / 64;            // 16-dim output tiles per wave
-  constexpr int QE = QF32 ? 4 : 2;
-  const int tid = threadIdx.x, l = lane_id(), wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row = l & 15, quad = l >> 4;
-  const rsrc_t r_codes = make_rsrc(kv_codes + row0 * (D / 2), (uint32_t)(vis * (D / 2)));
-  const rsrc_t r_scales = make_rsrc(kv_scales + row0 * (D / 16), (uint32_t)(vis * (D / 16)));
-  const rsrc_t r_win = make_rsrc(wcount ? swa_codes + wstart * D : nullptr, (uint32_t)(wcount * D));
-  const rsrc_t r_wsc = make_rsrc(wcount ? swa_scale + wstart : nullptr, (uint32_t)(wcount * 4));
-  const rsrc_t r_topk = make_rsrc(K ? topk + (int64_t)m * K : nullptr, (uint32_t)(K * 4));
-  const rsrc_t r_q = make_rsrc(static_cast<const char *>(q_any) + (int64_t)m * H * D * QE, (uint32_t)(H * D * QE));
-
-  // ---- the key slots of this lane's two tiles: index (or window scale) loads first ----
-  const int slot0 = 128 * sp0 + 32 * wv + row;   // tile i: slot0 + 16 i
-  int32_t jv[2];
-  float rv[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t so = (uint32_t)(slot0 + 16 * i) * 4u;
-    if constexpr (MAIN) jv[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_topk, so, 0, 0);
-    else rv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_wsc, so, 0, 0));
-  }
-  // ---- the workgroup's 16 heads of queries, 8 dims per piece, loaded once ----
-  constexpr int QPIECES = kSH * D / 8;
-  constexpr int QPT = (QPIECES + 64 * kSW - 1) / (64 * kSW);   // pieces per thread
-  uint32_t qraw[QPT][2 * QE];
-#pragma unroll
-  for (int u = 0; u < QPT; ++u) {
-    const int pc = tid + 64 * kSW * u;
-    const uint32_t off = (pc < QPIECES) ? (uint32_t)((hb * kSH * D + 8 * pc) * QE) : kOutOfRange;
-    buffer_load_words<8 * QE>(qraw[u], r_q, off);
-  }
-  // ---- every key row of the lane's tiles ----
-  float ks[2];
-  KeyShare<D, MAIN> ku[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int slot = slot0 + 16 * i;
-    if constexpr (MAIN) {
-      const int32_t j = jv[i];
-      const bool ok = slot < K && j >= 0 && j < vis;
-      ks[i] = ok ? 1.0f : 0.0f;
-      buffer_load_words<D / 8>(ku[i].w, r_codes, ok ? (uint32_t)j * (D / 2) + quad * (D / 8) : kOutOfRange);
-      buffer_load_words<D / 64>(ku[i].s, r_scales, ok ? (uint32_t)j * (D / 16) + quad * (D / 64) : kOutOfRange);
-    } else {
-      ks[i] = (slot < wcount) ? rv[i] : 0.0f;   // rows past the window read as zeros
-      buffer_load_words<D / 4>(ku[i].w, r_win, (uint32_t)slot * D + quad * (D / 4));
-    }
-  }
-  // ---- queries to LDS as f16 [head][dim] (bf16 converts exactly in the f16
-  // range; fp32 splits into hi + lo parts) ----
-#pragma unroll
-  for (int u = 0; u < QPT; ++u) {
-    const int pc = tid + 64 * kSW * u;
-    if (pc >= QPIECES) continue;
-    const int h = pc / (D / 8), d = 8 * (pc % (D / 8));
-    half8_t hi, lo;
-    if constexpr (QF32) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = __uint_as_float(qraw[u][i]);
-        hi[i] = (_Float16)v;
-        lo[i] = (_Float16)(v - (float)hi[i]);
-      }
-      *reinterpret_cast<half8_t *>(&L.q[(kSH + h) * Lds::QT + d]) = lo;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hi[2 * i] = (_Float16)__uint_as_float(qraw[u][i] << 16);
-        hi[2 * i + 1] = (_Float16)__uint_as_float(qraw[u][i] & 0xFFFF0000u);
-      }
-    }
-    *reinterpret_cast<half8_t *>(&L.q[h * Lds::QT + d]) = hi;
-  }
-  __syncthreads();
-  // ---- S = Q K^T for the wave's two tiles: the query operands (lane (head
-  // row, quad): dims quad*(D/4) + 8*kk) come from LDS all at once; the
-  // decoded keys go to LDS for P V ----
-  half8_t qa[NK];
-  half8_t qb[QF32 ? NK : 1];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    const int qo = row * Lds::QT + quad * (D / 4) + 8 * kk;
-    qa[kk] = *reinterpret_cast<const half8_t *>(&L.q[qo]);
-    if constexpr (QF32) qb[kk] = *reinterpret_cast<const half8_t *>(&L.q[kSH * Lds::QT + qo]);
-  }
-  float4_t sacc[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) sacc[i] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-  _Float16 *vrow = &L.vt[(32 * wv + row) * Lds::VT + quad * (D / 4)];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    const half8_t b0 = key_operand<D, MAIN>(ku[0], kk);
-    const half8_t b1 = key_operand<D, MAIN>(ku[1], kk);
-    sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b0, sacc[0], 0, 0, 0);
-    sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], b1, sacc[1], 0, 0, 0);
-    if constexpr (QF32) {
-      sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b0, sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb[kk], b1, sacc[1], 0, 0, 0);
-    }
-    *reinterpret_cast<half8_t *>(vrow + 8 * kk) = b0;
-    *reinterpret_cast<half8_t *>(vrow + 16 * Lds::VT + 8 * kk) = b1;
-  }
-  // ---- split statistics: lane holds key (16*tile + row) of heads 4*quad + j ----
-  float zz[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) zz[i][j] = (ks[i] != 0.0f) ? sacc[i][j] * tau2 * ks[i] : -INFINITY;
-  // the window scale r enters P' = p * r * 2^e, with r * 2^e in [1, 2) for
-  // the split's largest r (keeps small products out of the f16 subnormals)
-  float rm = fmaxf(ks[0], ks[1]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) rm = fmaxf(rm, __shfl_xor(rm, o, 64));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float mx = max16_lanes(fmaxf(zz[0][j], zz[1][j]));
-    if (row == 0) L.wmax[wv][4 * quad + j] = mx;
-  }
-  if (l == 0) L.rm[wv] = rm;
-  __syncthreads();
-  float mx[4];
-  rm = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kSW; ++w) rm = fmaxf(rm, L.rm[w]);
-  int e = 0;
-  (void)frexpf(rm, &e);
-  e = (rm > 0.0f) ? 1 - e : 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float v = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kSW; ++w) v = fmaxf(v, L.wmax[w][4 * quad + j]);
-    mx[j] = v;
-  }
-  float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float pr = (zz[i][j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(zz[i][j] - mx[j]);
-      lp[j] += pr;
-      L.p[(4 * quad + j) * Lds::PT + 32 * wv + 16 * i + row] = (_Float16)ldexpf(pr * ks[i], e);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float v = sum16_lanes(lp[j]);
-    if (row == 0) L.wsum[wv][4 * quad + j] = v;
-  }
-  __syncthreads();
-  // ---- O = P V for dims wv*(D/4) + 16*t over the split's 128 keys ----
-  float4_t acc[NDT];
-#pragma unroll
-  for (int t = 0; t < NDT; ++t) acc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int k0 = 0; k0 < kSKeys; k0 += 32) {
-    const half8_t a = *reinterpret_cast<const half8_t *>(&L.p[row * Lds::PT + k0 + 8 * quad]);
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) {
-      const half8_t b = v_operand_tr(L.vt, Lds::VT, k0, wv * (D / 4) + 16 * t, row, quad);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
-    }
-  }
-  // ---- normalised partial (accumulator layout) and its log2-domain lse ----
-  float inv[4], ls[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int hh = 4 * quad + j;
-    float lt = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kSW; ++w) lt += L.wsum[w][hh];
-    inv[j] = (lt > 0.0f) ? ldexpf(1.0f / lt, -e) : 0.0f;
-    ls[j] = (lt > 0.0f) ? mx[j] + log2f(lt) : -INFINITY;
-  }
-#pragma unroll
-  for (int t = 0; t < NDT; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[t][j] *= inv[j];
-  if (S == 1) {
-    store_output<D>(acc, ls, out, lse, H, m, hb, wv, row, quad);
-    return;
-  }
-  // ---- key splits: this split's partial and lse go out through stores that
-  // write through the caches (sc0 sc1), so every XCD reads them from memory;
-  // they are complete (s_waitcnt) before the arrival is counted, and the last
-  // split to arrive loads the others (again past the caches) only after it
-  // has seen the count, then merges them by log-sum-exp ----
-  const int64_t g0 = grp - sp;                       // split 0 of this (query, head block)
-  const rsrc_t r_po = make_rsrc(part_o + part_offset<D>(g0, 0, 0), (uint32_t)(S * kSW * 64 * (D / 16) * 4));
-  const rsrc_t r_pl = make_rsrc(part_lse + g0 * kSH, (uint32_t)(S * kSH * 4));
-  constexpr int kThrough = 17;                       // cache policy sc0 | sc1: write through to memory
-  const uint32_t slot_off = (uint32_t)(((sp * kSW + wv) * 64 + l) * (D / 16) * 4);
-#pragma unroll
-  for (int t = 0; t < NDT; ++t)
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[t]), r_po, slot_off + 16 * t, 0,
-                                           kThrough);
-  if (wv == 0 && row == 0)
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, (float4_t){ls[0], ls[1], ls[2], ls[3]}),
-                                           r_pl, (uint32_t)((sp * kSH + 4 * quad) * 4), 0, kThrough);
-  __builtin_amdgcn_s_waitcnt(0);                     // every store of this workgroup has completed
-  __syncthreads();
-  if (threadIdx.x == 0) L.prev = atomicInc(&counters[(int64_t)m * HB + hb], (uint32_t)S - 1u);  // wraps to 0
-  __syncthreads();
-  if (L.prev != (uint32_t)S - 1u) return;
-  // every split's lse into LDS, then the maximum per head
-  if (threadIdx.x < S * kSH)
-    L.lsall[threadIdx.x] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_pl, threadIdx.x * 4u, 0, kThrough));
-  __syncthreads();
-  float mxs[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) mxs[j] = ls[j];
-  for (int s2 = 0; s2 < S; ++s2)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mxs[j] = fmaxf(mxs[j], L.lsall[s2 * kSH + 4 * quad + j]);
-  // splits are added in split order whichever arrived last (this workgroup's
-  // own partial comes from its registers), so the result is deterministic
-  float wsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float4_t own[NDT];
-#pragma unroll
-  for (int t = 0; t < NDT; ++t) { own[t] = acc[t]; acc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f}; }
-  for (int s2 = 0; s2 < S; ++s2) {
-    float wt[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float l2 = L.lsall[s2 * kSH + 4 * quad + j];
-      wt[j] = (l2 == -INFINITY) ? 0.0f : exp2f(l2 - mxs[j]);
-      wsum[j] += wt[j];
-    }
-    const uint32_t so = (uint32_t)(((s2 * kSW + wv) * 64 + l) * (D / 16) * 4);
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) {
-      float4_t v = own[t];
-      if (s2 != sp)
-        v = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r_po, so + 16 * t, 0, kThrough));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[t][j] = fmaf(wt[j], v[j], acc[t][j]);
-    }
-  }
-  float lsm[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float iw = (wsum[j] > 0.0f) ? 1.0f / wsum[j] : 0.0f;
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) acc[t][j] *= iw;
-    lsm[j] = (wsum[j] > 0.0f) ? mxs[j] + log2f(wsum[j]) : -INFINITY;
-  }
-  store_output<D>(acc, lsm, out, lse, H, m, hb, wv, row, quad);
-}
-
-// grid (key splits, queries, head blocks of 16), 4 waves.  Split s covers
-// key slots 128s .. 128s+127 of the Top-K list (s < n_main) or window rows
-// 128(s - n_main) .. of the query's window.  Wave w owns tiles 2w and 2w+1 of
-// the split: it issues the Top-K index loads (or window scale loads), its
-// share of the workgroup's 16 query heads (staged once in LDS as f16) and
-// then every key row of its tiles at once; it computes S = Q K^T for its 32
-// keys from registers (channels assigned to k-steps by quarter: lane quad q
-// feeds dims q*(D/4) + 8*kk for both operands) and writes the decoded keys
-// into an LDS tile for P V.  The split's softmax statistics meet in LDS; P
-// (f16) goes to LDS; wave w computes O for dims w*(D/4) .. +D/4 over the
-// split's 128 keys.  The normalised partial O and its log2-domain lse go to
-// the workspace for k_attn_merge.
-template <int D, bool QF32>
-__global__ __launch_bounds__(64 * kSW) void k_attn_split(const void *__restrict__ q_any, int H,
-                                                         const uint8_t *__restrict__ kv_codes,
-                                                         const uint8_t *__restrict__ kv_scales,
-                                                         const int64_t *__restrict__ seq_start,
-                                                         const int32_t *__restrict__ seq_len, int ratio,
-                                                         const int32_t *__restrict__ q_seq,
-                                                         const int32_t *__restrict__ q_pos,
-                                                         const int32_t *__restrict__ topk, int K, int n_main,
-                                                         const uint8_t *__restrict__ swa_codes,
-                                                         const float *__restrict__ swa_scale,
-                                                         const int32_t *__restrict__ swa_start,
-                                                         const int32_t *__restrict__ swa_count, int W, float tau2,
-                                                         float *__restrict__ part_o, float *__restrict__ part_lse,
-                                                         uint32_t *__restrict__ counters, float *__restrict__ out,
-                                                         float *__restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) SplitLds<D, QF32> L;
-  const int sp = blockIdx.x, m = blockIdx.y, hb = blockIdx.z;
+// Visible main entries of query m: rows row0 .. row0 + vis - 1.
+struct QueryRows {
+  int64_t row0, vis;
+};
+CSA2_DEV QueryRows query_rows(const int64_t *seq_start, const int32_t *seq_len, int ratio, const int32_t *q_seq,
+                              const int32_t *q_pos, int m) {
   const int s = q_seq[m];
   const int64_t lim = ((int64_t)q_pos[m] + 1) / ratio;
-  const int64_t vis = max<int64_t>(0, min<int64_t>(seq_len[s], lim));
-  const int64_t row0 = seq_start[s];
-  const int wcount = (W > 0) ? max(0, min(swa_count[m], W)) : 0;
-  const int64_t wstart = (W > 0) ? swa_start[m] : 0;
-  const int64_t grp = ((int64_t)m * gridDim.z + hb) * gridDim.x + sp;
-  const int S = gridDim.x, HB = gridDim.z;
-  if (sp < n_main)   // workgroup-uniform: Top-K keys or window rows
-    attn_split_body<D, QF32, true>(L, q_any, H, kv_codes, kv_scales, row0, vis, topk, K, sp, m, hb, swa_codes,
-                                   swa_scale, wstart, wcount, tau2, part_o, part_lse, counters, grp, sp, S, HB, out,
-                                   lse);
-  else
-    attn_split_body<D, QF32, false>(L, q_any, H, kv_codes, kv_scales, row0, vis, topk, K, sp - n_main, m, hb,
-                                    swa_codes, swa_scale, wstart, wcount, tau2, part_o, part_lse, counters, grp, sp,
-                                    S, HB, out, lse);
+  return {seq_start[s], max<int64_t>(0, min<int64_t>(seq_len[s], lim))};
+}
+
+template <int D>
+struct LogitLds {
+  static constexpr int KT = D + 8;   // [key][dim] row stride of the decoded chunk (16-bit elements)
+  uint16_t kt[kChunk * KT];          // bf16 keys (bf16 queries) or f16 keys (fp32 queries)
+  float ks[kChunk];                  // per key: 1 (Top-K row), r (window row) or 0 (empty)
+  float rmax[4];                     // per wave: largest row scale of the query's window
+};
+
+// One wave's queries of 16 heads (from h0) as raw words: lane (head row,
+// quad) holds dims 32 kk + 8 quad .. +7 for every k-step kk, loaded through a
+// descriptor over the query's [H][D] block (heads >= H read zeros).  bf16
+// queries are the MFMA A operands as loaded (bf16 products over bf16 keys);
+// fp32 queries split into hi + lo f16 parts (over f16 keys).
+template <int D, bool QF32>
+struct QRaw {
+  static constexpr int NK = D / 32, WPK = QF32 ? 8 : 4;
+  uint32_t w[NK][WPK];
+  CSA2_DEV void load(rsrc_t rq, int h, int H, int quad, bool valid) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      buffer_load_words<WPK * 4>(w[kk], rq,
+                                 (valid && h < H) ? (uint32_t)((h * D + 32 * kk + 8 * quad) * (QF32 ? 4 : 2))
+                                                  : kOutOfRange);
+  }
+  CSA2_DEV bf16x8_t bf16_operand(int kk) const {
+    return __builtin_bit_cast(bf16x8_t, (u32x4_t){w[kk][0], w[kk][1], w[kk][2], w[kk][3]});
+  }
+  CSA2_DEV void f16_operands(int kk, half8_t &hi, half8_t &lo) const {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = __uint_as_float(w[kk][i]);
+      hi[i] = (_Float16)v;
+      lo[i] = (_Float16)(v - (float)hi[i]);
+    }
+  }
+};
+
+// grid: (queries x (n_main_chunks + n_window_chunks) chunks, XCD-grouped
+// (xcd_group), layers), 256 threads.  The arguments that the first loads
+// need come first: they fit the 16 argument registers preloaded at launch.
+// Thread (key = tid / 8, eighth = tid % 8) decodes dims eighth*D/8 .. of its
+// key; wave w then takes head tiles w, w+4, ...: S = Q K^T over the chunk's
+// two 16-key tiles (queries in registers, keys from LDS), logits, chunk
+// statistics and the f16 p values.  The next tile's queries load while the
+// current one computes; the first tile's load is issued with the key loads.
+template <int D, bool QF32>
+__global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int nwc, const int32_t *__restrict__ q_seq,
+                                                     const int32_t *__restrict__ q_pos,
+                                                     const int32_t *__restrict__ topk,
+                                                     const int64_t *__restrict__ seq_start,
+                                                     const int32_t *__restrict__ seq_len,
+                                                     const uint8_t *__restrict__ kv_codes,
+                                                     const uint8_t *__restrict__ kv_scales, int ratio, int H,
+                                                     float tau2, _Float16 *__restrict__ P, float2 *__restrict__ stats,
+                                                     int32_t *__restrict__ lift, uint8_t *__restrict__ g_codes,
+                                                     uint8_t *__restrict__ g_scales, uint8_t *__restrict__ g_win,
+                                                     AttnBatch lb) {
+  __shared__ __attribute__((aligned(16))) LogitLds<D> L;
+  using Lds = LogitLds<D>;
+  using QR = QRaw<D, QF32>;
+  constexpr int NK = D / 32;
+  constexpr int DP = D / 8;
+  constexpr int QE = QF32 ? 4 : 2;
+  const int nch = nmc + nwc, nkp = kChunk * nch, Kp = kChunk * nmc;
+  int m, c;   // query and chunk
+  xcd_group(blockIdx.x, M, m, c);
+  const int li = blockIdx.y;
+  const int tid = threadIdx.x, l = lane_id(), wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = l & 15, quad = l >> 4;
+  const bool main_chunk = c < nmc;
+  const AttnLayer &ly = lb.l[li];
+  if (!main_chunk && kChunk * (c - nmc) >= ly.window) return;   // past this layer's window
+  const int key = tid >> 3, d0 = (tid & 7) * DP;
+  // a Top-K chunk's index load goes out first, beside the sequence lookup
+  // of query_rows (the row loads need both)
+  const int slot = kChunk * c + key;
+  const rsrc_t r_topk = make_rsrc(K ? topk + (int64_t)m * K : nullptr, (uint32_t)(K * 4));
+  const int32_t j = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      r_topk, (main_chunk && slot < K) ? slot * 4u : kOutOfRange, 0, 0);
+  const QueryRows qr = query_rows(seq_start, seq_len, ratio, q_seq, q_pos, m);
+  const rsrc_t rq = make_rsrc(static_cast<const char *>(ly.q) + (int64_t)m * H * D * QE, (uint32_t)(H * D * QE));
+  // the wave's head tiles: wv + 4 it for it < ntw
+  const int nht = (H + 15) / 16;
+  const int ntw = (wv < nht) ? (nht - 1 - wv) / 4 + 1 : 0;
+  auto q_load = [&](int it, QR &r) { r.load(rq, 16 * (wv + 4 * it) + row, H, quad, it < ntw); };
+
+  // ---- issue the key index, the first tile's queries, then the key row;
+  // decode the chunk's 32 keys into LDS ----
+  QR qA, qB;
+  float ksv = 0.0f;
+  auto put = [&](int u, const u32x4_t &v) {
+    *reinterpret_cast<u32x4_t *>(&L.kt[key * Lds::KT + d0 + 8 * u]) = v;
+  };
+  if (main_chunk) {
+    q_load(0, qA);
+    const bool ok = slot < K && j >= 0 && j < qr.vis;
+    ksv = ok ? 1.0f : 0.0f;
+    Fp4Piece<D, DP> pc;
+    pc.load(make_rsrc(kv_codes + qr.row0 * (D / 2), (uint32_t)(qr.vis * (D / 2))),
+            make_rsrc(kv_scales + qr.row0 * (D / 16), (uint32_t)(qr.vis * (D / 16))), ok, (uint32_t)j, d0);
+    if (li == 0)   // the gathered copy of the chunk's rows (zeros for empty slots)
+      pc.store(make_rsrc(g_codes + (int64_t)m * Kp * (D / 2), (uint32_t)(Kp * (D / 2))),
+               make_rsrc(g_scales + (int64_t)m * Kp * (D / 16), (uint32_t)(Kp * (D / 16))), (uint32_t)slot, d0);
+#pragma unroll
+    for (int u = 0; u < DP / 8; ++u) put(u, QF32 ? __builtin_bit_cast(u32x4_t, pc.get(u)) : pc.get_bf16(u));
+  } else {
+    const int W = ly.window;
+    const int wr = kChunk * (c - nmc) + key;
+    const int wcount = max(0, min(ly.swa_count[m], W));
+    const int64_t wstart = ly.swa_start[m];
+    const bool ok = wr < wcount;
+    q_load(0, qA);
+    // every row scale of the query's window (W <= 1024): the lift is shared
+    // by all window chunks of the query
+    const rsrc_t r_ws = make_rsrc(ly.swa_scale + wstart, (uint32_t)(wcount * 4));
+    float rw = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      rw = fmaxf(rw, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_ws, (uint32_t)(tid + 256 * u) * 4u, 0, 0)));
+    ksv = ok ? ly.swa_scale[wstart + wr] : 0.0f;
+    Fp8Piece<DP> pc;
+    pc.load(make_rsrc(ly.swa_codes + wstart * D, (uint32_t)(wcount * D)), ok, (uint32_t)wr, d0, D);
+    // the gathered copy of the layer's window rows (zeros past the window)
+    const int Wp = kChunk * nwc;
+    pc.store(make_rsrc(g_win + ((int64_t)li * M + m) * Wp * D, (uint32_t)(Wp * D)), (uint32_t)wr, d0, D);
+#pragma unroll
+    for (int u = 0; u < DP / 8; ++u) put(u, QF32 ? __builtin_bit_cast(u32x4_t, pc.get(u)) : pc.get_bf16(u));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) rw = fmaxf(rw, __shfl_xor(rw, o, 64));
+    if (l == 0) L.rmax[wv] = rw;
+  }
+  if ((tid & 7) == 0) L.ks[key] = ksv;
+  __syncthreads();
+  // the window's lift: r_max * 2^e in [1, 2), the same for every chunk of the query's window
+  int e = 0;
+  if (!main_chunk) {
+    const float rmax = fmaxf(fmaxf(L.rmax[0], L.rmax[1]), fmaxf(L.rmax[2], L.rmax[3]));
+    (void)frexpf(rmax, &e);
+    e = (rmax > 0.0f) ? 1 - e : 0;
+  }
+  const float ksr[2] = {L.ks[row], L.ks[16 + row]};
+  if (!main_chunk && tid == 0) lift[((int64_t)li * M + m) * nch + c] = e;
+  // stores through descriptors over the layer's [H] rows: heads past H fall
+  // out of range and are dropped (no branch around a store)
+  const int64_t lrow = ((int64_t)li * M + m) * H;
+  const rsrc_t r_pw = make_rsrc(P + lrow * nkp, (uint32_t)(H * nkp * 2));
+  const rsrc_t r_sw = make_rsrc(stats + lrow * nch, (uint32_t)(H * nch * 8));
+
+  auto tile = [&](int it, const QR &cur, QR &nxt) {
+    q_load(it + 1, nxt);
+    const int ht = wv + 4 * it;
+    float4_t sacc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sacc[i] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const u32x4_t b = *reinterpret_cast<const u32x4_t *>(&L.kt[(16 * i + row) * Lds::KT + 32 * kk + 8 * quad]);
+        if constexpr (QF32) {
+          half8_t qa, qb;
+          cur.f16_operands(kk, qa, qb);
+          const half8_t bh = __builtin_bit_cast(half8_t, b);
+          sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, bh, sacc[i], 0, 0, 0);
+          sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qb, bh, sacc[i], 0, 0, 0);
+        } else {
+          sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.bf16_operand(kk), __builtin_bit_cast(bf16x8_t, b),
+                                                            sacc[i], 0, 0, 0);
+        }
+      }
+    }
+    // lane: key 16 i + row of the chunk, heads 16 ht + 4 quad + j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = 16 * ht + 4 * quad + j;
+      float z[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) z[i] = (ksr[i] != 0.0f) ? sacc[i][j] * tau2 * ksr[i] : -INFINITY;
+      // the chunk's reference: its largest logit rounded up to an integer, so
+      // that phase 2 rescales chunks by exact powers of two (p in (1/2, 1]
+      // for the largest key)
+      const float mc = ceilf(max16_lanes(fmaxf(z[0], z[1])));
+      float p[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) p[i] = (z[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[i] - mc);
+      const float lc = sum16_lanes(p[0] + p[1]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)ldexpf(p[i] * ksr[i], e)), r_pw,
+                                              (uint32_t)((h * nkp + kChunk * c + 16 * i + row) * 2), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64((u32x2_t){__float_as_uint(mc), __float_as_uint(lc)}, r_sw,
+                                            row == 0 ? (uint32_t)((h * nch + c) * 8) : kOutOfRange, 0, 0);
+    }
+  };
+  for (int it = 0; it < ntw; it += 2) {
+    tile(it, qA, qB);
+    if (it + 1 < ntw) tile(it + 1, qB, qA);
+  }
+}
+
+template <int DS>
+struct PvLds {
+  static constexpr int VT = DS + 8;          // [key][dim] row stride of the decoded V slice (f16)
+  _Float16 vt[kPvKeys * VT];
+  _Float16 f[kMaxChunks * kPvHeads];         // [chunk][head]: 2^(m_c - M), the chunk's exact rescale
+  float inv_l[kPvHeads];                     // per head: 1 / L
+};
+
+// grid: (queries x head groups of 64 x D / DS dim slices, XCD-grouped
+// (xcd_group), layers), 256 threads.  The leading arguments fill the 16
+// preloaded argument registers; every load of the first two blocks and of
+// the statistics is addressed from them (the batch's largest window bounds
+// them), so none waits for the layer's own arguments.
+// Wave w owns heads 16 w .. 16 w + 15 of the workgroup's group; thread t
+// decodes key slot t of each 256-slot block; Top-K and window slots both
+// come from the gathered rows of phase 1.  A chunk's
+// p values (f16) are rescaled by 2^(m_c - M) - exact, a power of two - and
+// accumulated on MFMA: Top-K chunks in one accumulator, window chunks (whose
+// p carry the lift 2^e) in another; O = (acc_main + 2^-e acc_win) / L.  The
+// loads of block b + 2 are issued while block b is multiplied (a ring of
+// three register buffers); blocks 0 and 1 are issued with the statistics.
+template <int D, int DS>
+__global__ __launch_bounds__(256) void k_attn_pv(int M, int H, int nmc, int nwc, const _Float16 *__restrict__ P,
+                                                 const float2 *__restrict__ stats, const int32_t *__restrict__ lift,
+                                                 const uint8_t *__restrict__ g_codes,
+                                                 const uint8_t *__restrict__ g_scales,
+                                                 const uint8_t *__restrict__ g_win, AttnBatch lb) {
+  __shared__ __attribute__((aligned(16))) PvLds<DS> L;
+  using Lds = PvLds<DS>;
+  constexpr int NDT = DS / 16;
+  constexpr int NT = kPvKeys / kChunk;                       // k-steps per block
+  constexpr int GPT = (kMaxChunks / 4 + 3) / 4;              // 4-chunk statistics groups per thread
+  constexpr int NS = D / DS;                                  // dim slices
+  const int nhg = (H + kPvHeads - 1) / kPvHeads;
+  int m, k;   // query and (head group, slice) member
+  xcd_group(blockIdx.x, M, m, k);
+  const int li = blockIdx.y, sl = k % NS, hb0 = (k / NS) * kPvHeads;
+  const int tid = threadIdx.x, l = lane_id(), wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = l & 15, quad = l >> 4;
+  const AttnLayer &ly = lb.l[li];
+  const int W = ly.window;
+  const int nchs = nmc + nwc, nkp = kChunk * nchs;          // strides of the phase-1 arrays
+  const int nch = nmc + (W + kChunk - 1) / kChunk;          // this layer's chunks
+  const int nslots = kChunk * nch, Kp = kChunk * nmc;
+  const int hn = min(kPvHeads, H - hb0);
+  const int Wp = kChunk * nwc;                               // gathered window rows of the batch
+  const rsrc_t r_gc = make_rsrc(g_codes + (int64_t)m * Kp * (D / 2), (uint32_t)(Kp * (D / 2)));
+  const rsrc_t r_gs = make_rsrc(g_scales + (int64_t)m * Kp * (D / 16), (uint32_t)(Kp * (D / 16)));
+  const rsrc_t r_win = make_rsrc(g_win + ((int64_t)li * M + m) * Wp * D, (uint32_t)(Wp * D));
+  const int64_t rows0 = ((int64_t)li * M + m) * H + hb0;    // first (layer, query, head) row of the group
+  const rsrc_t r_p = make_rsrc(P + rows0 * nkp, (uint32_t)(hn * nkp * 2));
+  const rsrc_t r_st = make_rsrc(stats + rows0 * nchs, (uint32_t)(hn * nchs * 8));
+
+  struct Blk {
+    Fp4Piece<D, DS> main;
+    Fp8Piece<DS> win;
+    half8_t pa[NT];   // P operands: lane (head row, quad) holds slots 32 t + 8 quad .. +7
+  };
+  const uint32_t prow = (uint32_t)((16 * wv + row) * nkp);
+  // block b's rows and P operands; past the last block every offset is out
+  // of range, so the loads return zeros and their number does not depend on b
+  auto load_block = [&](int b, Blk &r) {
+    const int slot = kPvKeys * b + tid;
+    r.main.load(r_gc, r_gs, slot < Kp, (uint32_t)slot, sl * DS);
+    // rows and p values past this layer's own slots (up to the batch's
+    // largest window) are loaded but never multiplied
+    const int wr = slot - Kp;
+    r.win.load(r_win, slot >= Kp, (uint32_t)wr, sl * DS, D);
+    const bool okp = kPvKeys * b < nkp;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      r.pa[t] = __builtin_bit_cast(
+          half8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                       r_p, okp ? (prow + kPvKeys * b + kChunk * t + 8 * quad) * 2u : kOutOfRange, 0, 0));
+  };
+
+  // ---- issue: this thread's chunk statistics (head tid / 4; chunk groups
+  // 4 g .. 4 g + 3 for g = tid % 4 + 4 k), the window's lift, blocks 0, 1 ----
+  const int nblk = (nslots + kPvKeys - 1) / kPvKeys;
+  const int hh = tid >> 2, q4 = tid & 3;
+  const int kmax = (nchs + 15) / 16;                          // statistics groups per thread in use
+  float2 stv[GPT][4];
+#pragma unroll
+  for (int k = 0; k < GPT; ++k) {
+    stv[k][0] = stv[k][1] = stv[k][2] = stv[k][3] = make_float2(-INFINITY, 0.0f);
+    if (k >= kmax) continue;   // uniform: only the groups that exist are loaded
+    const int g = q4 + 4 * k;
+    const uint32_t off = (hh < hn && 4 * g < nchs) ? (uint32_t)(hh * nchs + 4 * g) * 8u : kOutOfRange;
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r_st, off, 0, 0);
+    const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r_st, off == kOutOfRange ? off : off + 16u, 0, 0);
+    stv[k][0] = make_float2(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    stv[k][1] = make_float2(__uint_as_float(a[2]), __uint_as_float(a[3]));
+    stv[k][2] = make_float2(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    stv[k][3] = make_float2(__uint_as_float(b[2]), __uint_as_float(b[3]));
+  }
+  const int32_t ew_raw = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(lift + ((int64_t)li * M + m) * nchs, (uint32_t)(nchs * 4)), nmc * 4u, 0, 0);
+  Blk ba, bb, bc;
+  load_block(0, ba);
+  load_block(1, bb);
+  // ---- per head: the largest reference M, the sum L, and each chunk's
+  // rescale 2^(m_c - M) (0 below the f16 range) ----
+  float lse2;
+  {
+    auto valid = [&](int k, int i) { return hh < hn && 4 * (q4 + 4 * k) + i < nch; };
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < GPT; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (valid(k, i)) mx = fmaxf(mx, stv[k][i].x);
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+    float sum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < GPT; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int cc = 4 * (q4 + 4 * k) + i;
+        const bool ok = valid(k, i) && stv[k][i].x != -INFINITY;
+        const int sh = ok ? (int)(stv[k][i].x - mx) : -1000;    // an integer <= 0
+        sum += ok ? ldexpf(stv[k][i].y, sh) : 0.0f;
+        if (4 * (q4 + 4 * k) + i < nch) L.f[cc * kPvHeads + hh] = (sh >= -24) ? (_Float16)ldexpf(1.0f, sh) : (_Float16)0.0f;
+      }
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    if (q4 == 0) L.inv_l[hh] = (sum > 0.0f) ? 1.0f / sum : 0.0f;
+    lse2 = (sum > 0.0f) ? mx + log2f(sum) : -INFINITY;
+  }
+
+  const int ew = (nch > nmc) ? ew_raw : 0;   // the window's lift (no window chunk: none)
+  float4_t am[NDT], aw[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) {
+    am[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+    aw[t] = am[t];
+  }
+  const bool active = 16 * wv < hn;
+  // block b: issue block b + 2 into `fut`, then decode `cur` and multiply
+  auto step = [&](int b, const Blk &cur, Blk &fut) {
+    load_block(b + 2, fut);
+    if (b >= nblk) return;
+    __syncthreads();      // the rescales (first block) or the previous block's V reads are done
+    {
+      // a wave's 64 slots are all Top-K or all window unless the list's end
+      // falls inside them: the branch usually runs one decoder per wave
+      _Float16 *vrow = &L.vt[tid * Lds::VT];
+      if (kPvKeys * b + tid < Kp) {
+#pragma unroll
+        for (int u = 0; u < DS / 8; ++u) *reinterpret_cast<half8_t *>(vrow + 8 * u) = cur.main.get(u);
+      } else {
+#pragma unroll
+        for (int u = 0; u < DS / 8; ++u) *reinterpret_cast<half8_t *>(vrow + 8 * u) = cur.win.get(u);
+      }
+    }
+    __syncthreads();
+    if (active) {
+      const int nt = min(kPvKeys, nslots - kPvKeys * b) / kChunk;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t >= nt) break;
+        const int cc = (kPvKeys * b) / kChunk + t;
+        const _Float16 fc = L.f[cc * kPvHeads + 16 * wv + row];   // exact power of two (or 0)
+        const half8_t a = cur.pa[t] * (half8_t){fc, fc, fc, fc, fc, fc, fc, fc};
+        if (cc < nmc) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            am[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, v_operand_tr(L.vt, Lds::VT, kChunk * t, 16 * dt, row, quad),
+                                                            am[dt], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            aw[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, v_operand_tr(L.vt, Lds::VT, kChunk * t, 16 * dt, row, quad),
+                                                            aw[dt], 0, 0, 0);
+        }
+      }
+    }
+  };
+  for (int b = 0; b < nblk; b += 3) {
+    step(b, ba, bc);
+    step(b + 1, bb, ba);
+    step(b + 2, bc, bb);
+  }
+  // ---- output: lane (dim row, quad) holds heads 16 w + 4 quad + j ----
+  if (active) {
+    const float4_t il = *reinterpret_cast<const float4_t *>(&L.inv_l[16 * wv + 4 * quad]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = hb0 + 16 * wv + 4 * quad + j;
+      if (h >= H) continue;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        ly.out[((int64_t)m * H + h) * D + sl * DS + 16 * dt + row] = (am[dt][j] + ldexpf(aw[dt][j], -ew)) * il[j];
+    }
+  }
+  if (sl == 0 && q4 == 0 && hh < hn && ly.lse) ly.lse[(int64_t)m * H + hb0 + hh] = lse2 * 0.6931471805599453f;
 }
 
 // ===========================================================================
@@ -727,80 +886,100 @@ __global__ __launch_bounds__(256) void k_attn(const void *__restrict__ q_any, in
 // host side
 // ---------------------------------------------------------------------------
 
-// The split schedule fills the chip when there are few queries; with many
-// queries (prefill) the flash kernel's one-workgroup-per-query grid is
-// already large and needs no partial outputs.
+// The decode schedule fills the chip when there are few queries; with many
+// queries (prefill) the one-workgroup-per-query kernels already have a large
+// grid and need no intermediates.
 static bool use_decode_kernel(int m, int heads, int dim, int64_t max_len) {
   // its buffer descriptors span one sequence's rows: byte offsets must fit
   if (max_len * (dim / 2) >= kMaxRsrcBytes) return false;
   return (int64_t)m * ((heads + kHB - 1) / kHB) < 256;
 }
 
-// Key splits of the decode schedule: 128 Top-K slots or window rows each.
-static int split_main(int top_k) { return (top_k + kSKeys - 1) / kSKeys; }
-static int split_count(int top_k, int window) { return split_main(top_k) + (window + kSKeys - 1) / kSKeys; }
-
-// Decode-schedule workspace: arrival counters [query][head block] in a region
-// of fixed size at offset 0 (zero before the first call, left zero by every
-// call, never written by anything else: a later call of another shape finds
-// its counters at the same place and still zero), normalised partial outputs
-// [query][head block][split] in the accumulator layout, and their log2-domain
-// lse.  The schedule's gate keeps m * ceil(heads/16) below 1024 counters.
-struct AttnWs {
-  size_t counters, part_o, part_lse, total;
+// Decode-schedule workspace for a batch of `nl` layers: p values (f16)
+// [layer][query][head][slot], chunk statistics (m_c, sum p) [layer][query]
+// [head][chunk], window-chunk lifts [layer][query][chunk], the gathered
+// Top-K rows [query][slot] (FP4 codes and scale bytes) and the gathered
+// window rows [layer][query][row] (FP8 codes).  Slots: the Top-K list padded
+// to whole chunks, then the largest window of the batch.
+struct DecodeWs {
+  int nmc, nwc;
+  size_t p, stats, lift, gcodes, gscales, gwin, total;
 };
-static_assert(kAttnCounterBytes >= sizeof(uint32_t) * 1024, "counter region holds every decode-schedule counter");
-static AttnWs attn_ws_layout(int m, int heads, int dim, int top_k, int window) {
-  const size_t qh = (size_t)m * ((heads + kSH - 1) / kSH);
-  const size_t groups = qh * split_count(top_k, window);
-  AttnWs w{};
+static DecodeWs decode_ws_layout(int m, int heads, int dim, int top_k, int max_window, int nl) {
+  DecodeWs w{};
+  w.nmc = (top_k + kChunk - 1) / kChunk;
+  w.nwc = (max_window + kChunk - 1) / kChunk;
+  const size_t nch = (size_t)(w.nmc + w.nwc), rows = (size_t)nl * m * heads, kp = (size_t)kChunk * w.nmc;
   size_t off = 0;
-  w.counters = off; off = kAttnCounterBytes;
-  w.part_o = off;   off = align256(off + sizeof(float) * groups * kSH * dim);
-  w.part_lse = off; off = align256(off + sizeof(float) * groups * kSH);
+  w.p = off;       off = align256(off + sizeof(_Float16) * rows * nch * kChunk);
+  w.stats = off;   off = align256(off + sizeof(float2) * rows * nch);
+  w.lift = off;    off = align256(off + sizeof(int32_t) * (size_t)nl * m * nch);
+  w.gcodes = off;  off = align256(off + (size_t)m * kp * (dim / 2));
+  w.gscales = off; off = align256(off + (size_t)m * kp * (dim / 16));
+  w.gwin = off;    off = align256(off + (size_t)nl * m * (kChunk * w.nwc) * dim);
   w.total = off;
   return w;
 }
 
-// Sized for the decode schedule whenever the query count may select it (a
-// cache too long for it falls back to the flash kernel, which needs none).
-size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int window) {
-  if (!use_decode_kernel(m, heads, dim, 0)) return 256;
-  return attn_ws_layout(m, heads, dim, top_k, window).total;
+size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int max_window, int n_layers) {
+  if (m < 1 || n_layers < 1 || !use_decode_kernel(m, heads, dim, 0)) return 256;
+  return decode_ws_layout(m, heads, dim, top_k, max_window, std::min(n_layers, kAttnBatch)).total;
 }
 
 template <int D, bool QF32>
-static int attn_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int heads,
-                     const int32_t *topk, int K, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,
-                     hipStream_t stream) {
-  const int W = swa.window;
+static int attn_layers_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, int heads, const int32_t *topk, int K,
+                            const AttnLayer *layers, int n, float scale, void *ws, hipStream_t stream) {
   const float tau2 = scale * 1.4426950408889634f;  // log2-domain softmax: p = 2^(z - max)
   if (use_decode_kernel(qs.m, heads, D, kv.max_len)) {
-    const AttnWs L = attn_ws_layout(qs.m, heads, D, K, W);
-    char *base = static_cast<char *>(ws);
-    uint32_t *ctr = reinterpret_cast<uint32_t *>(base + L.counters);
-    float *po = reinterpret_cast<float *>(base + L.part_o);
-    float *pl = reinterpret_cast<float *>(base + L.part_lse);
-    const dim3 grid(split_count(K, W), qs.m, (heads + kSH - 1) / kSH);
-    CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_split<D, QF32>), grid, dim3(64 * kSW), stream, q, heads, kv.codes,
-                      kv.scales, kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, split_main(K),
-                      swa.codes, swa.scale, swa.start, swa.count, W, tau2, po, pl, ctr, out, lse);
-  } else if (attn_prefill_supported(kv, QF32 ? CSA2_F32 : CSA2_BF16, K)) {
-    return launch_attn_prefill(kv, qs, q, heads, topk, K, swa, scale, out, lse, stream);
-  } else {
-    const dim3 grid(qs.m, (heads + kHB - 1) / kHB);
-    CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn<D, QF32>), grid, dim3(256), stream, q, heads, kv.codes, kv.scales,
-                      kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, swa.codes, swa.scale, swa.start,
-                      swa.count, W, tau2, out, lse);
+    constexpr int DS = D < 32 ? D : 32;
+    for (int b0 = 0; b0 < n; b0 += kAttnBatch) {
+      const int nl = std::min(kAttnBatch, n - b0);
+      AttnBatch lb{};
+      int wmax = 0;
+      for (int i = 0; i < nl; ++i) {
+        lb.l[i] = layers[b0 + i];
+        wmax = std::max(wmax, layers[b0 + i].window);
+      }
+      const DecodeWs L = decode_ws_layout(qs.m, heads, D, K, wmax, nl);
+      char *base = static_cast<char *>(ws);
+      _Float16 *P = reinterpret_cast<_Float16 *>(base + L.p);
+      float2 *st = reinterpret_cast<float2 *>(base + L.stats);
+      int32_t *lf = reinterpret_cast<int32_t *>(base + L.lift);
+      uint8_t *gc = reinterpret_cast<uint8_t *>(base + L.gcodes);
+      uint8_t *gs = reinterpret_cast<uint8_t *>(base + L.gscales);
+      uint8_t *gw = reinterpret_cast<uint8_t *>(base + L.gwin);
+      const dim3 g1(xcd_grid(L.nmc + L.nwc, qs.m), (unsigned)nl);
+      CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_logits<D, QF32>), g1, dim3(256), stream, qs.m, K, L.nmc, L.nwc, qs.seq,
+                        qs.pos, topk, kv.seq_start, kv.seq_len, kv.codes, kv.scales, kv.ratio, heads, tau2, P, st, lf,
+                        gc, gs, gw, lb);
+      const int nhg = (heads + kPvHeads - 1) / kPvHeads;
+      const dim3 g2(xcd_grid((D / DS) * nhg, qs.m), (unsigned)nl);
+      CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_pv<D, DS>), g2, dim3(256), stream, qs.m, heads, L.nmc, L.nwc, P, st, lf, gc,
+                        gs, gw, lb);
+    }
+    return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+  }
+  for (int i = 0; i < n; ++i) {
+    const AttnLayer &ly = layers[i];
+    const csa2_swa swa{ly.swa_codes, ly.swa_scale, ly.swa_start, ly.swa_count, D, ly.window};
+    if (attn_prefill_supported(kv, QF32 ? CSA2_F32 : CSA2_BF16, K)) {
+      const int st = launch_attn_prefill(kv, qs, ly.q, heads, topk, K, swa, scale, ly.out, ly.lse, stream);
+      if (st != CSA2_OK) return st;
+    } else {
+      const dim3 grid(qs.m, (heads + kHB - 1) / kHB);
+      CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn<D, QF32>), grid, dim3(256), stream, ly.q, heads, kv.codes, kv.scales,
+                        kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, ly.swa_codes, ly.swa_scale,
+                        ly.swa_start, ly.swa_count, ly.window, tau2, ly.out, ly.lse);
+    }
   }
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 
-static int launch_attn_kernel(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int q_dtype,
-                              int heads, const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out,
-                              float *lse, void *ws, hipStream_t stream) {
+int launch_attn_layers(const csa2_fp4_cache &kv, const csa2_queries &qs, int q_dtype, int heads,
+                       const int32_t *topk, int top_k, const AttnLayer *layers, int n_layers, float scale, void *ws,
+                       hipStream_t stream) {
   const bool f32 = q_dtype == CSA2_F32;
-#define CSA2_ATTN(D, F) attn_impl<D, F>(kv, qs, q, heads, topk, top_k, swa, scale, out, lse, ws, stream)
+#define CSA2_ATTN(D, F) attn_layers_impl<D, F>(kv, qs, heads, topk, top_k, layers, n_layers, scale, ws, stream)
   switch (kv.dim) {
     case 64: return f32 ? CSA2_ATTN(64, true) : CSA2_ATTN(64, false);
     case 128: return f32 ? CSA2_ATTN(128, true) : CSA2_ATTN(128, false);
@@ -809,12 +988,6 @@ static int launch_attn_kernel(const csa2_fp4_cache &kv, const csa2_queries &qs, 
     default: return CSA2_ERR_UNSUPPORTED;
   }
 #undef CSA2_ATTN
-}
-
-int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int q_dtype, int heads,
-                const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,
-                hipStream_t stream) {
-  return launch_attn_kernel(kv, qs, q, q_dtype, heads, topk, top_k, swa, scale, out, lse, ws, stream);
 }
 
 }  // namespace csa2

@@ -60,14 +60,25 @@ int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const u
                       hipStream_t stream);
 
 // ---- attention (csa2_attn.hip) ----
-// workspace of an attention call; its first kAttnCounterBytes hold arrival counters
-// that must be zero before the first call with that workspace (every call leaves
-// them zero, whatever its shape)
-constexpr size_t kAttnCounterBytes = 4096;
-size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int window);
-int launch_attn(const csa2_fp4_cache &kv, const csa2_queries &qs, const void *q, int q_dtype, int heads,
-                const int32_t *topk, int top_k, const csa2_swa &swa, float scale, float *out, float *lse, void *ws,
-                hipStream_t stream);
+// One layer's attention inputs and outputs (window fields as in csa2_swa).
+struct AttnLayer {
+  const void *q;
+  const uint8_t *swa_codes;
+  const float *swa_scale;
+  const int32_t *swa_start;
+  const int32_t *swa_count;
+  int32_t window;
+  float *out;
+  float *lse;
+};
+constexpr int kAttnBatch = 8;   // layers per launch of the decode schedule
+// Workspace of launch_attn_layers over n_layers layers whose largest window
+// is max_window (no initial contents needed).
+size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int max_window, int n_layers);
+// Attention of n_layers layers that share the main cache and the Top-K list.
+int launch_attn_layers(const csa2_fp4_cache &kv, const csa2_queries &qs, int q_dtype, int heads,
+                       const int32_t *topk, int top_k, const AttnLayer *layers, int n_layers, float scale, void *ws,
+                       hipStream_t stream);
 
 // Prefill schedule for the 512-channel latent with bf16 queries
 // (csa2_attn_prefill.hip); needs top_k % 16 == 0 and no workspace.

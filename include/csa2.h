@@ -229,15 +229,13 @@ int32_t csa2_reindex(const csa2_fp4_cache *idx, const csa2_queries *qs, const ui
  * Limits: dim in {64, 128, 256, 512}; 1 <= heads <= 256; top_k <= 2048;
  *         window <= 1024.
  * Workspace: csa2_attn_workspace_size bytes (256-byte aligned), owned by
- *   the caller.  Its first CSA2_ATTN_COUNTER_BYTES (or all of it, when
- *   smaller) hold arrival counters: zero-fill them before the workspace's
- *   first use.  Every call leaves them zero again, whatever its shape, so a
- *   workspace reused by attention or group calls of any shape on one stream
- *   needs no further clearing; writing anything else there breaks the next
- *   call.  Calls that run at the same time must not share a workspace.
+ *   the caller; no initial contents needed.  With few queries (m * ceil(
+ *   heads/64) < 256) it holds the decode schedule's intermediates: f16
+ *   probabilities per (query, head, key slot) and per-32-slot statistics;
+ *   otherwise 256 bytes suffice.  Calls that run at the same time must not
+ *   share a workspace.
  * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED, WORKSPACE, HIP.
  * ------------------------------------------------------------------- */
-#define CSA2_ATTN_COUNTER_BYTES 4096u
 int32_t csa2_attn_workspace_size(int32_t m, int32_t heads, int32_t dim, int32_t top_k,
                                  int32_t window, size_t *bytes);
 int32_t csa2_sparse_swa_attn(const csa2_fp4_cache *kv, const csa2_queries *qs, const void *q,
@@ -296,11 +294,10 @@ typedef struct csa2_group_desc {
 } csa2_group_desc;
 
 /* Workspace of csa2_group_step: csa2_group_workspace_size bytes, 256-byte
- * aligned.  Its first CSA2_ATTN_COUNTER_BYTES are the attention calls'
- * arrival counters, at that offset for every group shape: zero-fill them
- * before the workspace's first use; every call leaves them zero, so groups
- * of any shape may then share the workspace on one stream.  The rest needs
- * no initial contents.  Not shared by calls that run at the same time. */
+ * aligned, no initial contents needed; not shared by calls that run at the
+ * same time.  The group's layers run their attention together (batches of
+ * up to 8 layers share one decoded copy of each Top-K key chunk), which
+ * gives the same results as csa2_sparse_swa_attn layer by layer. */
 int32_t csa2_group_workspace_size(const csa2_group_desc *g, size_t *bytes);
 int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_bytes, void *stream);
 
@@ -313,9 +310,8 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
  * stream) on a scratch array the library owns: one copy of
  * CSA2_STATIC_SCRATCH_BYTES per GPU, held from the first call on that GPU
  * until the process ends.  The call allocates nothing (no hipMalloc, no
- * allocating library routine).  The array starts zero and every call leaves
- * its counter region (the workspace's first CSA2_ATTN_COUNTER_BYTES) zero,
- * so calls of any shape follow one another with nothing to clear.
+ * allocating library routine) and needs no initial scratch contents, so
+ * calls of any shape follow one another with nothing to clear.
  * Every call on one GPU shares that GPU's array: calls that overlap in time
  * on one GPU (other streams, other host threads) race and must be ordered
  * by the caller, e.g. on one stream.

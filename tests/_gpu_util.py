@@ -39,8 +39,9 @@ def empty_u8(*shape) -> torch.Tensor:
 
 
 def workspace(nbytes: int) -> torch.Tensor:
-    # zero-filled before first use, as the attention and group calls require
-    return torch.zeros(max(256, nbytes), dtype=torch.uint8, device=dev())
+    # no call needs initial workspace contents: fill it with a byte pattern so
+    # that a kernel reading what it did not write shows up in the results
+    return torch.full((max(256, nbytes),), 0xA5, dtype=torch.uint8, device=dev())
 
 
 def gpu_quantize(x: np.ndarray, w_ik: np.ndarray | None = None):

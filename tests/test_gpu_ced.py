@@ -17,7 +17,7 @@ import torch
 import fp4_kv_cache_02_amd as csa2
 import synth
 from oracle import attention, codec, group as ogroup, indexer
-from tests._gpu_util import announce, assert_sets_equal_modulo_band, dev, empty_u8, h, t
+from tests._gpu_util import announce, assert_sets_equal_modulo_band, dev, empty_u8, h, t, workspace
 from tests.test_gpu_group import _Decoder, _check_attn_one
 
 pytestmark = pytest.mark.gpu
@@ -53,7 +53,7 @@ def test_ced_decode_step_40_layers():
         sw, c8, s8 = _window(cfg, 100 + layer, M)
         out = torch.full((M, H, D), 7.0, dtype=torch.float32, device=dev())
         lse = torch.full((M, H), 7.0, dtype=torch.float32, device=dev())
-        ws = torch.zeros((csa2.csa2_attn_workspace_size(M, H, D, 0, W),), dtype=torch.uint8, device=dev())
+        ws = workspace(csa2.csa2_attn_workspace_size(M, H, D, 0, W))
         csa2.csa2_sparse_swa_attn(dec.kv, dec.qs, q, None, 0, sw, tau, out, lse, ws)
         go, gl = h(out), h(lse)
         for i in range(M):
@@ -97,7 +97,7 @@ def test_ced_decode_step_40_layers():
         g = csa2.Group(csa2.CSA2_MODE_FULL, kv, ik, dec.qs, t(qi).view(torch.bfloat16), t(wi), K, K, pool, cnt, topk,
                        None, qs_l, csa2.CSA2_BF16, H, ws_l, outs, lses, tau, new_kv=t(new_x), new_dst_row=t(dst),
                        w_ik=t(w_ik))
-        ws = torch.zeros((csa2.csa2_group_workspace_size(g),), dtype=torch.uint8, device=dev())
+        ws = workspace(csa2.csa2_group_workspace_size(g))
         csa2.csa2_group_step(g, ws)
         assert np.array_equal(h(kv_c), rc) and np.array_equal(h(kv_s), rs), "encoder cache after the write"
         assert np.array_equal(h(ik_c), ikc) and np.array_equal(h(ik_s), iks), "encoder keys after the write"
