@@ -74,8 +74,16 @@ def scan_source_sha256() -> str:
 # ---------------------------------------------------------------------------
 
 class DecodeWorkload:
-    def __init__(self, wl, torch, csa2, synth):
+    """One decode step of the decoder: every group's write path and index,
+    and every layer's attention.  By default each group is one
+    csa2_group_step, which runs its layers' attention together (their
+    queries are inputs here).  With layer_sequential the step issues what a
+    model running layer by layer would: the group step of the group's first
+    layer, then one csa2_sparse_swa_attn call per Reuse layer."""
+
+    def __init__(self, wl, torch, csa2, synth, layer_sequential=False):
         self.wl, self.torch, self.csa2 = wl, torch, csa2
+        self.layer_sequential = layer_sequential
         dev = torch.device("cuda:0")
         S, D, DI = len(wl.seq_lens), wl.dim, wl.idx_dim
         lens = np.asarray(wl.seq_lens, np.int64)
@@ -147,22 +155,31 @@ class DecodeWorkload:
             wi_t = torch.from_numpy(wi).to(dev)
             topk = torch.empty((M, K), dtype=torch.int32, device=dev)
             full = modes[0] == "full"
+            ng = 1 if layer_sequential else n
             g = csa2.Group(csa2.CSA2_MODE_FULL if full else csa2.CSA2_MODE_REINDEX, self.kv, self.idx, self.qs,
                            qi_t, wi_t, P, K, self.pool, self.pool_count, topk, None,
-                           self.q[layer:layer + n], csa2.CSA2_BF16, H, self.swa[layer:layer + n],
-                           self.out[layer:layer + n], self.lse[layer:layer + n], D ** -0.5,
+                           self.q[layer:layer + ng], csa2.CSA2_BF16, H, self.swa[layer:layer + ng],
+                           self.out[layer:layer + ng], self.lse[layer:layer + ng], D ** -0.5,
                            new_kv=self.new_kv if full else None, new_dst_row=self.new_dst if full else None,
                            w_ik=self.w_ik if full else None)
             g.topk_tensor = topk
+            g.reuse_layers = list(range(layer + 1, layer + n)) if layer_sequential else []
             self.groups.append(g)
             layer += n
         ws_bytes = max(csa2.csa2_group_workspace_size(g) for g in self.groups)
-        self.ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)  # zero before first use
+        if layer_sequential:
+            ws_bytes = max(ws_bytes, csa2.csa2_attn_workspace_size(M, H, D, K, W))
+        self.ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)   # no initial contents needed
         torch.cuda.synchronize()
 
     def step(self):
+        c = self.csa2
         for g in self.groups:
-            self.csa2.csa2_group_step(g, self.ws)
+            c.csa2_group_step(g, self.ws)
+            for layer in g.reuse_layers:
+                c.csa2_sparse_swa_attn(self.kv, self.qs, self.q[layer], g.topk_tensor, self.wl.top_k,
+                                       self.swa[layer], self.wl.dim ** -0.5, self.out[layer], self.lse[layer],
+                                       self.ws)
 
     def snapshot(self):
         t = self.torch
@@ -287,7 +304,7 @@ class CedDecodeWorkload:
             layer += len(modes)
         ws_bytes = max([csa2.csa2_group_workspace_size(g) for g in self.enc_groups] +
                        [csa2.csa2_attn_workspace_size(M, H, D, 0, W), self.dec.ws.numel()])
-        self.ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)  # zero before first use
+        self.ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)   # no initial contents needed
         self.M = M
         self.q_pos_host = self.dec.q_pos_host
         torch.cuda.synchronize()
@@ -422,7 +439,7 @@ class PrefillWorkload:
             self.groups.append(g)
             layer += n
         ws_bytes = max(csa2.csa2_group_workspace_size(g) for g in self.groups)
-        self.ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)  # zero before first use
+        self.ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)   # no initial contents needed
         torch.cuda.synchronize()
 
     def step(self):
@@ -754,9 +771,9 @@ def run_prefill(args, wl, torch, csa2, synth) -> dict:
     return result
 
 
-def setup_decode(wl, torch, csa2, synth):
+def setup_decode(wl, torch, csa2, synth, layer_sequential=False):
     t0 = time.time()
-    W = DecodeWorkload(wl, torch, csa2, synth)
+    W = DecodeWorkload(wl, torch, csa2, synth, layer_sequential=layer_sequential)
     setup_s = time.time() - t0
     print(f"[bench] setup {setup_s:.1f}s: {wl.name}, {len(wl.seq_lens)} seqs, {sum(wl.seq_lens)} entries",
           file=sys.stderr, flush=True)
@@ -855,6 +872,16 @@ def main():
                         "method": "1 GiB scratch written before each one-step graph replay"}
         extras[f"{wl.name}/cold"] = cold
         del W
+        torch.cuda.empty_cache()
+        # the same step issued layer by layer (a group step for each group's
+        # first layer, one attention call per Reuse layer), as a model would
+        Ws, _ = setup_decode(wl, torch, csa2, synth, layer_sequential=True)
+        kts = kernel_times(torch, csa2, Ws, args.steps)
+        mss, _ = time_steps(torch, Ws, args.steps, args.warmup, "graph")
+        rs = decode_record(wl, Ws, mss, kts, "graph, layer by layer")
+        rs["attention"]["kernels"] = "k_attn_logits + k_attn_pv per layer"
+        extras[f"{wl.name}/layer-sequential"] = rs
+        del Ws
         torch.cuda.empty_cache()
         for cfg in (1, 3):
             wx = synth.workload(cfg)

@@ -523,12 +523,22 @@ __global__ __launch_bounds__(256) void k_rescore(const uint8_t *__restrict__ cod
 // passes, on the composite (key, ~slot) below those 12 bits, until the cut's
 // bin holds exactly the entries still needed.  Returns the number selected,
 // min(K, #candidates).
+constexpr int kSelectCand = 2048;   // threshold-bin entries refined by one wave
+
 template <int NT>
 struct SelectLds {
   uint32_t hist[kHistBins];
   uint32_t h[256];
   int scan[NT / 64 + 1];
   int T, above, nT, digit, rem, cnt;
+  // the selection by output rank, written out in one coalesced pass (a
+  // wave's scattered masked stores would queue one instruction per slot)
+  int32_t stage[4096];
+  float stage_score[2048];
+  // the composite keys of the threshold bin, refined by one wave
+  uint64_t cand[kSelectCand];
+  int ncand;
+  uint64_t prefix, mask;
 };
 
 // Count `d` of every key into hist: each thread first folds its keys into at
@@ -547,6 +557,40 @@ struct DigitFold {
   }
 };
 
+// Order LDS accesses among the lanes of one wave (no other wave takes part).
+CSA2_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Run by wave 0 alone: radix passes of 8 bits over the n composites cand[]
+// (all inside the threshold bin), narrowing (prefix, mask) to the cut of the
+// rem largest; stops as soon as the cut's digit bin holds exactly the
+// entries still needed.
+CSA2_DEV void wave_refine(const uint64_t *cand, int n, int rem, uint32_t *h, int *s_digit, int *s_rem,
+                          int *s_cnt, uint64_t &prefix, uint64_t &mask) {
+  const int l = lane_id();
+  for (int hi = 64 - kHistBits; hi > 0; hi -= 8) {
+    const int width = hi < 8 ? hi : 8;
+    const int shift = hi - width;
+    const uint64_t dmask = (1ull << width) - 1ull;
+    for (int i = l; i < 256; i += 64) h[i] = 0u;
+    wave_lds_sync();
+    for (int i = l; i < n; i += 64) {
+      const uint64_t c = cand[i];
+      if ((c & mask) == prefix) atomicAdd(&h[(uint32_t)((c >> shift) & dmask)], 1u);
+    }
+    wave_lds_sync();
+    find_digit(h, rem, s_digit, s_rem, s_cnt);
+    wave_lds_sync();
+    prefix |= (uint64_t)*s_digit << shift;
+    mask |= dmask << shift;
+    rem = *s_rem;
+    if (*s_cnt == rem) break;
+  }
+}
+
 template <int NT, int PER, typename Emit>
 CSA2_DEV int select_topk(const float (&sv)[PER], int K, SelectLds<NT> &sm, Emit emit) {
   constexpr int BPT = kHistBins / NT;   // histogram bins per thread in the threshold scan
@@ -556,7 +600,7 @@ CSA2_DEV int select_topk(const float (&sv)[PER], int K, SelectLds<NT> &sm, Emit 
 #pragma unroll
   for (int i = 0; i < PER; ++i) key[i] = (sv[i] > -INFINITY) ? f2key(sv[i]) : 0u;
   for (int i = tid; i < kHistBins / 4; i += NT) reinterpret_cast<uint4 *>(sm.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (tid == 0) { sm.T = -1; sm.above = 0; sm.nT = 0; }
+  if (tid == 0) { sm.T = -1; sm.above = 0; sm.nT = 0; sm.ncand = 0; }
   __syncthreads();
   {
     DigitFold f;
@@ -593,7 +637,37 @@ CSA2_DEV int select_topk(const float (&sv)[PER], int K, SelectLds<NT> &sm, Emit 
   };
   uint64_t prefix = (uint64_t)(uint32_t)max(T, 0) << (64 - kHistBits);
   uint64_t mask = ((1ull << kHistBits) - 1ull) << (64 - kHistBits);
+  // the threshold bin's entries into LDS (one atomic per wave), refined by
+  // wave 0 alone when they fit; otherwise block-wide passes below
+  bool small_bin = false;
   if (Kp > 0 && !all_t) {
+    int nc = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) nc += (key[i] != 0u && (int)(key[i] >> KB) == T);
+    const int incl = wave_incl_scan(nc);
+    int base = 0;
+    if ((tid & 63) == 63) base = atomicAdd(&sm.ncand, incl);
+    base = __shfl(base, 63, 64) + incl - nc;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (key[i] != 0u && (int)(key[i] >> KB) == T) {
+        if (base < kSelectCand) sm.cand[base] = comp(i);
+        ++base;
+      }
+    __syncthreads();
+    small_bin = sm.ncand <= kSelectCand;
+    if (small_bin) {
+      if (tid < 64) {
+        uint64_t pf = prefix, mk = mask;
+        wave_refine(sm.cand, sm.ncand, rem, sm.h, &sm.digit, &sm.rem, &sm.cnt, pf, mk);
+        if (tid == 0) { sm.prefix = pf; sm.mask = mk; }
+      }
+      __syncthreads();
+      prefix = sm.prefix;
+      mask = sm.mask;
+    }
+  }
+  if (Kp > 0 && !all_t && !small_bin) {
     for (int hi = 64 - kHistBits; hi > 0; hi -= 8) {
       const int width = hi < 8 ? hi : 8;
       const int shift = hi - width;
@@ -679,12 +753,13 @@ __global__ __launch_bounds__(NT) void k_topk_select(const float *__restrict__ ps
   int32_t *out = topk_out + (int64_t)m * K;
   float *osc = topk_score ? topk_score + (int64_t)m * K : nullptr;
   const int Kp = select_topk<NT, PER>(sv, K, sm, [&](int rank, int i, float v) {
-    out[rank] = blk[i / kBlock] * kBlock + (i % kBlock);
-    if (osc) osc[rank] = v;
+    sm.stage[rank] = blk[i / kBlock] * kBlock + (i % kBlock);
+    sm.stage_score[rank] = v;
   });
-  for (int i = Kp + threadIdx.x; i < K; i += NT) {
-    out[i] = -1;
-    if (osc) osc[i] = __builtin_nanf("");
+  __syncthreads();
+  for (int i = threadIdx.x; i < K; i += NT) {
+    out[i] = (i < Kp) ? sm.stage[i] : -1;
+    if (osc) osc[i] = (i < Kp) ? sm.stage_score[i] : __builtin_nanf("");
   }
 }
 
@@ -707,9 +782,10 @@ __global__ __launch_bounds__(NT) void k_block_select(const float *__restrict__ b
   load_slot_scores<PER>(bmax + (int64_t)m * nb_stride, nb, sv);
   int32_t *out = pool_out + (int64_t)m * P;
   const int Kp = select_topk<NT, PER>(sv, P, sm, [&](int rank, int i, float) {
-    out[rank] = (int32_t)(threadIdx.x * PER + i);
+    sm.stage[rank] = (int32_t)(threadIdx.x * PER + i);
   });
-  for (int i = Kp + threadIdx.x; i < P; i += NT) out[i] = -1;
+  __syncthreads();
+  for (int i = threadIdx.x; i < P; i += NT) out[i] = (i < Kp) ? sm.stage[i] : -1;
   if (threadIdx.x == 0) pool_count[m] = Kp;
 }
 
