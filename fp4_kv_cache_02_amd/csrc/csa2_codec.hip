@@ -154,83 +154,124 @@ __global__ __launch_bounds__(256) void k_quantize_fp4_derive(const T *__restrict
   }
 }
 
-// Quantise rows and derive their indexer keys for small batches (the decode
-// write path): grid (rows, idx_dim / 16), one workgroup per (row, 16-column
-// group of the indexer key), 16 * (1024 / idx_dim) threads: thread ->
-// (column of the group, slice of PER channels); every W_ik value a thread
-// needs is loaded before the fp64 dot products start, each slice sums from
-// +0 in channel order and the slices are added in slice order.  Every
-// workgroup of a row encodes the row (the exact decoded values feed its dot
-// products); the first writes its codes.
-constexpr int kRowThreads = 1024;   // (column, slice) pairs per row
+// Quantise rows and derive their indexer keys on the fp64 matrix cores, for
+// dim <= 512.  The projection y = W_ik^T DQ4(row) is an fp64 product: every
+// term DQ4(c) * w is exact in fp64 (at most 6 significant bits times fp32's
+// 24), the sum is accumulated in fp64 by v_mfma_f64_16x16x4_f64 and rounded
+// once to fp32, like the oracle's fp64 matrix product (whose summation
+// order is not fixed either; fp64 sums in another order round to the same
+// fp32 unless they straddle an fp32 rounding boundary within ~2^-50).
+//
+// grid (ceil(rows / 16), idx_dim / (16 CT)), 64 CT KS threads.  A workgroup
+// encodes its 16 rows (codes and scales written by the workgroups of the
+// first column group) and keeps their exact values in LDS as fp64; wave
+// (ct, ks) multiplies them by the 16 key columns of tile ct over channel
+// slice ks (W_ik loaded before the encode, so its latency overlaps it).  With
+// KS > 1 (few rows: more waves per tile) the slices' partial tiles are added
+// in slice order.  The 16 columns of a tile are one FP4 group of the key.
+typedef double double4_t __attribute__((ext_vector_type(4)));
+constexpr int kDeriveRows = 16;
+constexpr int kDeriveMaxDim = 512;
 
-template <typename T, int PER>
-__global__ __launch_bounds__(512) void k_quantize_fp4_derive_row(const T *__restrict__ x, int dim,
-                                                                          const int64_t *__restrict__ dst_row,
-                                                                          uint8_t *__restrict__ codes,
-                                                                          uint8_t *__restrict__ scales,
-                                                                          const float *__restrict__ w_ik,
-                                                                          int idx_dim, uint8_t *__restrict__ ik_codes,
-                                                                          uint8_t *__restrict__ ik_scales) {
-  __shared__ float dq[kDeriveLdsFloats];
-  __shared__ double part[512];
-  __shared__ float yk[kGroup];
-  const int64_t r = blockIdx.x;
-  const int cg = blockIdx.y;              // 16-column group of the indexer key
-  const int64_t d = dst_row ? dst_row[r] : r;
+template <typename T, int CT, int KS>
+__global__ __launch_bounds__(64 * CT * KS) void k_quantize_fp4_derive_mfma(
+    const T *__restrict__ x, int64_t rows, int dim, const int64_t *__restrict__ dst_row, uint8_t *__restrict__ codes,
+    uint8_t *__restrict__ scales, const float *__restrict__ w_ik, int idx_dim, uint8_t *__restrict__ ik_codes,
+    uint8_t *__restrict__ ik_scales) {
+  constexpr int NT = 64 * CT * KS;
+  constexpr int DS = kDeriveMaxDim + 1;                 // fp64 row stride: rows fall in different banks
+  constexpr int WPL = kDeriveMaxDim / 4 / KS;           // W_ik values per lane (one per k-step)
+  __shared__ double dq[kDeriveRows * DS];
+  __shared__ double part[KS > 1 ? KS * CT * 256 : 1];
+  __shared__ float yk[CT * 256];
+  const int64_t r0 = (int64_t)blockIdx.x * kDeriveRows;
+  const int nr = (int)min<int64_t>(kDeriveRows, rows - r0);
   const int gpr = dim / kGroup;
-  const int col = cg * kGroup + (int)(threadIdx.x % kGroup);
-  const int nparts = kRowThreads / idx_dim;
-  const int pidx = threadIdx.x / kGroup;
-  const int c0 = pidx * PER;              // dim == PER * nparts (checked by the launcher)
-  float wv[PER];
+  const int tid = threadIdx.x, l = lane_id(), wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ct = wv % CT, ks = wv / CT;
+  const int col0 = (blockIdx.y * CT + ct) * kGroup;
+  const int kper = dim / KS;                            // channels of this wave's slice
+  const int c_begin = ks * kper;
+  // ---- this lane's W_ik column entries: channel c_begin + 4 kk + l / 16 ----
+  const rsrc_t r_w = make_rsrc(w_ik, (uint32_t)(dim * idx_dim * 4));
+  float wreg[WPL];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) wv[i] = w_ik[(int64_t)(c0 + i) * idx_dim + col];
-  for (int g = threadIdx.x; g < gpr; g += blockDim.x) {
+  for (int kk = 0; kk < WPL; ++kk) {
+    const int c = c_begin + 4 * kk + l / 16;
+    const uint32_t off = (4 * kk < kper) ? (uint32_t)((c * idx_dim + col0 + l % 16) * 4) : kOutOfRange;
+    wreg[kk] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_w, off, 0, 0));
+  }
+  // ---- encode the rows, exact values to LDS (rows past the end read as 0) ----
+  for (int t = tid; t < kDeriveRows * gpr; t += NT) {
+    const int rr = t / gpr, g = t - rr * gpr;
+    double *dst = &dq[rr * DS + g * kGroup];
+    if (rr >= nr) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[i] = 0.0;
+      continue;
+    }
     float v[16];
-    const T *src = x + r * dim + g * kGroup;
+    const T *src = x + (r0 + rr) * dim + g * kGroup;
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = load_as_f32<T>(src + i);
     uint2 packed;
     uint8_t sb;
     encode_group(v, &packed, &sb);
-    if (cg == 0) {
+    if (blockIdx.y == 0) {
+      const int64_t d = dst_row ? dst_row[r0 + rr] : r0 + rr;
       *reinterpret_cast<uint2 *>(codes + d * (dim / 2) + g * 8) = packed;
       scales[d * gpr + g] = sb;
     }
-    const float s = e4m3_pos_value(sb);
+    const float sc = e4m3_pos_value(sb);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t c = (i < 8) ? (packed.x >> (4 * i)) & 15u : (packed.y >> (4 * (i - 8))) & 15u;
+      // E2M1 magnitude of code m: 0, .5, 1, 1.5 for m < 4, else 2^((m-2)/2) * (1 or 1.5)
       const uint32_t m = c & 7u;
       const float mag = (m < 4) ? 0.5f * (float)m : (float)(1u << ((m - 2) >> 1)) * ((m & 1u) ? 1.5f : 1.0f);
-      const float val = mag * s;
-      dq[g * kGroup + i] = (c & 8u) ? -val : val;
+      const float val = mag * sc;
+      dst[i] = (double)((c & 8u) ? -val : val);
     }
   }
   __syncthreads();
-  double acc = 0.0;
+  // ---- Y tile = DQ (16 rows x slice) x W (slice x 16 columns), fp64 ----
+  double4_t acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc = fma((double)dq[c0 + i], (double)wv[i], acc);
-  part[threadIdx.x] = acc;
-  __syncthreads();
-  if (threadIdx.x < kGroup) {
-    double t = 0.0;
-    for (int k = 0; k < nparts; ++k) t += part[k * kGroup + threadIdx.x];
-    yk[threadIdx.x] = (float)t;
+  for (int kk = 0; kk < WPL; ++kk) {
+    if (4 * kk >= kper) break;
+    const double a = dq[(l % 16) * DS + c_begin + 4 * kk + l / 16];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)wreg[kk], acc, 0, 0, 0);
   }
-  __syncthreads();
-  const int igpr = idx_dim / kGroup;
-  if (threadIdx.x == 0) {
-    const int g = cg;
+  // lane l holds rows l / 16 + 4 i of column l % 16
+  if constexpr (KS > 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[((ks * CT + ct) * 64 + l) * 4 + i] = acc[i];
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      double t = 0.0;
+      for (int s2 = 0; s2 < KS; ++s2) t += part[((s2 * CT + ct) * 64 + l) * 4 + i];
+      acc[i] = t;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) yk[ct * 256 + (l / 16 + 4 * i) * 16 + l % 16] = (float)(acc[i] + 0.0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // ---- encode each row's 16 key columns (one FP4 group) ----
+  if (l < nr) {
     float v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = yk[i];
+    for (int i = 0; i < 16; ++i) v[i] = yk[ct * 256 + l * 16 + i];
     uint2 packed;
     uint8_t sb;
     encode_group(v, &packed, &sb);
+    const int64_t d = dst_row ? dst_row[r0 + l] : r0 + l;
+    const int g = col0 / kGroup;
     *reinterpret_cast<uint2 *>(ik_codes + d * (idx_dim / 2) + g * 8) = packed;
-    ik_scales[d * igpr + g] = sb;
+    ik_scales[d * (idx_dim / kGroup) + g] = sb;
   }
 }
 
@@ -297,23 +338,22 @@ int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const
     else
       CSA2_TIMED_LAUNCH(kTimedWrite, k_quantize_fp4<uint16_t>, grid, dim3(256), stream, (const uint16_t *)x, rows, dim,
                          dst_row, codes, scales);
-  } else if (rows <= 1024 && dim % (kRowThreads / idx_dim) == 0 &&
-             (dim / (kRowThreads / idx_dim) == 8 || dim / (kRowThreads / idx_dim) == 16 ||
-              dim / (kRowThreads / idx_dim) == 32 || dim / (kRowThreads / idx_dim) == 64)) {
-    const dim3 grid((unsigned)rows, (unsigned)(idx_dim / kGroup));
-    const dim3 block((unsigned)(kGroup * (kRowThreads / idx_dim)));  // 64 .. 512
-    const int per = dim / (kRowThreads / idx_dim);
-#define CSA2_ROW_LAUNCH(T, PERV)                                                                                  \
-    CSA2_TIMED_LAUNCH(kTimedWrite, (k_quantize_fp4_derive_row<T, PERV>), grid, block, stream, (const T *)x, dim,             \
-                       dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales)
-    if (x_dtype == CSA2_F32) {
-      if (per == 8) CSA2_ROW_LAUNCH(float, 8); else if (per == 16) CSA2_ROW_LAUNCH(float, 16);
-      else if (per == 32) CSA2_ROW_LAUNCH(float, 32); else CSA2_ROW_LAUNCH(float, 64);
-    } else {
-      if (per == 8) CSA2_ROW_LAUNCH(uint16_t, 8); else if (per == 16) CSA2_ROW_LAUNCH(uint16_t, 16);
-      else if (per == 32) CSA2_ROW_LAUNCH(uint16_t, 32); else CSA2_ROW_LAUNCH(uint16_t, 64);
-    }
-#undef CSA2_ROW_LAUNCH
+  } else if (dim <= kDeriveMaxDim) {
+    // columns per workgroup: the largest tile count (up to 8) dividing the key's 16-column groups
+    const int cgs = idx_dim / kGroup;
+    const int ct = (cgs % 8 == 0) ? 8 : (cgs % 4 == 0) ? 4 : (cgs % 2 == 0) ? 2 : 1;
+    const bool few = rows <= 64;   // few rows: split the channels over more waves instead
+    const dim3 grid((unsigned)((rows + kDeriveRows - 1) / kDeriveRows), (unsigned)(few ? cgs : cgs / ct));
+#define CSA2_MFMA_LAUNCH(T, CT, KS)                                                                           \
+    CSA2_TIMED_LAUNCH(kTimedWrite, (k_quantize_fp4_derive_mfma<T, CT, KS>), grid, dim3(64 * CT * KS), stream, \
+                      (const T *)x, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales)
+#define CSA2_MFMA_CT(T)                                                           \
+    if (few) CSA2_MFMA_LAUNCH(T, 1, 4);                                           \
+    else if (ct == 8) CSA2_MFMA_LAUNCH(T, 8, 1); else if (ct == 4) CSA2_MFMA_LAUNCH(T, 4, 1); \
+    else if (ct == 2) CSA2_MFMA_LAUNCH(T, 2, 1); else CSA2_MFMA_LAUNCH(T, 1, 1)
+    if (x_dtype == CSA2_F32) { CSA2_MFMA_CT(float); } else { CSA2_MFMA_CT(uint16_t); }
+#undef CSA2_MFMA_CT
+#undef CSA2_MFMA_LAUNCH
   } else {
     const int rb = kDeriveLdsFloats / dim;
     const dim3 grid((unsigned)((rows + rb - 1) / rb));

@@ -91,10 +91,10 @@ def test_quantize_bf16_input_and_scattered_rows():
                                          (512, 32, 1500), (512, 64, 1500), (96, 32, 1100),
                                          (256, 256, 7), (512, 32, 9)])
 def test_derive_indexer_key_bit_exact(dim, di, rows):
-    # Up to 1024 rows take the small-batch path (one workgroup per row and
-    # 16-column group of the key, 64 to 512 threads), more the multi-row path
-    # (4096 / dim rows per workgroup; 1, 2, 4, 8 or 16 row slots per thread,
-    # 96 channels leave a ragged last workgroup).
+    # dim <= 512 runs the fp64 matrix-core kernel: up to 64 rows with the
+    # channels split over 4 waves per 16-column tile, more with 1, 2, 4 or 8
+    # tiles per workgroup (32 .. 256 key columns); 16-row workgroups leave a
+    # ragged last one for every row count here, 96 channels a ragged slice.
     announce("derive indexer key", dim, di, rows)
     x = synth.main_kv_rows(0, 0, 0, rows, dim)
     w = synth.w_ik(0, dim, di)
