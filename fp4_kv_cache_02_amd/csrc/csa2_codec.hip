@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void k_quantize_fp4_derive(const T *__restrict
 // first column group) and keeps their exact values in LDS as fp64; wave
 // (ct, ks) multiplies them by the 16 key columns of tile ct over channel
 // slice ks (W_ik loaded before the encode, so its latency overlaps it).  With
-// KS > 1 (few rows: more waves per tile) the slices' partial tiles are added
+// KS > 1 (few rows: 8 waves per tile) the slices' partial tiles are added
 // in slice order.  The 16 columns of a tile are one FP4 group of the key.
 typedef double double4_t __attribute__((ext_vector_type(4)));
 constexpr int kDeriveRows = 16;
@@ -342,13 +342,14 @@ int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const
     // columns per workgroup: the largest tile count (up to 8) dividing the key's 16-column groups
     const int cgs = idx_dim / kGroup;
     const int ct = (cgs % 8 == 0) ? 8 : (cgs % 4 == 0) ? 4 : (cgs % 2 == 0) ? 2 : 1;
-    const bool few = rows <= 64;   // few rows: split the channels over more waves instead
+    // few rows: split the channels over 8 waves per tile instead (dim % 32 == 0)
+    const bool few = rows <= 64 && dim % 32 == 0;
     const dim3 grid((unsigned)((rows + kDeriveRows - 1) / kDeriveRows), (unsigned)(few ? cgs : cgs / ct));
 #define CSA2_MFMA_LAUNCH(T, CT, KS)                                                                           \
     CSA2_TIMED_LAUNCH(kTimedWrite, (k_quantize_fp4_derive_mfma<T, CT, KS>), grid, dim3(64 * CT * KS), stream, \
                       (const T *)x, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales)
 #define CSA2_MFMA_CT(T)                                                           \
-    if (few) CSA2_MFMA_LAUNCH(T, 1, 4);                                           \
+    if (few) CSA2_MFMA_LAUNCH(T, 1, 8);                                           \
     else if (ct == 8) CSA2_MFMA_LAUNCH(T, 8, 1); else if (ct == 4) CSA2_MFMA_LAUNCH(T, 4, 1); \
     else if (ct == 2) CSA2_MFMA_LAUNCH(T, 2, 1); else CSA2_MFMA_LAUNCH(T, 1, 1)
     if (x_dtype == CSA2_F32) { CSA2_MFMA_CT(float); } else { CSA2_MFMA_CT(uint16_t); }

@@ -32,12 +32,16 @@
  * Storage formats (P1 section "FP4 KV、Bounded Replay 及其他扩展"; P4 section
  * 三; P5 section "缓存精度与持久化分层")
  * ----------------------------------------------------------------------
- * FP4 row of `dim` channels (dim % 16 == 0): `dim/2` code bytes - byte k
+ * FP4 row of `dim` channels: `dim/2` code bytes - byte k
  * holds channel 2k in its low nibble and 2k+1 in its high nibble, each an
  * E2M1 code (sign bit 3, magnitudes 0,.5,1,1.5,2,3,4,6) - plus `dim/16`
  * scale bytes, scale g being an OCP E4M3FN value for channels 16g..16g+15.
  * Codes and scales live in two planes, [rows][dim/2] and [rows][dim/16].
- * Value = e2m1(code) * e4m3(scale); no global scale.
+ * Value = e2m1(code) * e4m3(scale); no global scale.  The format itself
+ * needs dim % 16 == 0 (whole scale groups); this library takes FP4 rows
+ * with dim % 32 == 0 (its kernels move whole 16-byte code words, 32
+ * channels) and rejects other widths with BAD_SHAPE; 512-channel latents
+ * and 128- or 64-channel indexer keys qualify.
  * FP8 window row: `dim` OCP E4M3FN codes plus one fp32 row scale; value =
  * e4m3(code) * scale.
  */
@@ -225,6 +229,15 @@ int32_t csa2_reindex(const csa2_fp4_cache *idx, const csa2_queries *qs, const ui
  * "缓存精度与持久化分层"):
  *     z = softmax_scale * q_h . k ;  o_h = softmax(z) . K ;  lse_h = log sum exp z
  * q    device [m][heads][dim], fp32 or bf16 (q_dtype); kv->dim == swa->dim == dim.
+ *      Arithmetic: keys are exact (FP4/FP8 values are bf16 and f16
+ *      numbers); q.k products are exact and accumulate in fp32; the
+ *      probabilities entering P V are rounded once to f16 (relative
+ *      2^-11).  Query range: with few queries (m * ceil(heads/64) < 256,
+ *      the decode schedule) bf16 queries are used as they are, any bf16
+ *      value; with many queries the kernels convert bf16 to f16, so |q|
+ *      must stay <= 65504 and values below 2^-14 become f16 subnormals
+ *      (absolute error <= 2^-25).  fp32 queries are split into hi + lo f16
+ *      parts (same range).
  * out  device [m][heads][dim] fp32.  lse device [m][heads] fp32 or NULL.
  * Limits: dim in {64, 128, 256, 512}; 1 <= heads <= 256; top_k <= 2048;
  *         window <= 1024.
@@ -336,16 +349,19 @@ int32_t csa2_group_step_static(const csa2_group_desc *g, void *stream);
  * starts recording; 0 stops.
  * _read waits for the recorded events and returns the summed kernel time in
  * milliseconds and the number of launches, then clears the records.  For
- * measurement only; recording is host-side bookkeeping, not thread-safe
- * with concurrent recording calls on other threads.
+ * measurement only.  Not thread-safe: each hook keeps one process-wide
+ * record, so enable, the timed launches and _read belong on one host
+ * thread, with no other thread launching the timed kernels meanwhile.
  * Errors: NULL_ARG (read with a NULL output), HIP.
  * ------------------------------------------------------------------- */
 int32_t csa2_profile_scan(int32_t enable);
 int32_t csa2_profile_scan_read(double *total_ms, int64_t *launches);
 
 /* csa2_profile_attn / csa2_profile_attn_read - the same timing for every
- * attention kernel launched by csa2_sparse_swa_attn / csa2_group_step (one
- * launch per layer).  Same contract and errors as csa2_profile_scan. */
+ * attention kernel launched by csa2_sparse_swa_attn / csa2_group_step (the
+ * decode schedule launches a logits and a P V kernel per batch of up to 8
+ * layers, the many-query schedules one kernel per layer).  Same contract
+ * and errors as csa2_profile_scan. */
 int32_t csa2_profile_attn(int32_t enable);
 int32_t csa2_profile_attn_read(double *total_ms, int64_t *launches);
 
