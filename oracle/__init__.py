@@ -21,4 +21,4 @@ docstring; every reading is listed in the design doc.
 
 Parity status per function (what pins it) is in each module header.
 """
-from . import codec, indexer, attention, group  # noqa: F401
+from . import codec, compressor, indexer, attention, group  # noqa: F401

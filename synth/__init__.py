@@ -37,6 +37,8 @@ TAG_LEN = 7       # ragged sequence lengths
 TAG_IDX_KEY = 8   # pre-quantisation indexer-key rows when the indexer is exercised on its own
 TAG_IDX_LIST = 9  # synthetic Top-K lists when attention is exercised on its own
 TAG_FP4_BYTES = 10  # raw FP4 cache bytes (codes and scale bytes drawn directly)
+TAG_TOKENS = 11   # pre-compression token rows fed to the compressor
+TAG_W_C = 12      # compressor weight
 
 
 def rng(cfg: int, tag: int, layer: int = 0, seq: int = 0, chunk: int = 0) -> np.random.Generator:
@@ -148,6 +150,23 @@ def fp4_bytes(cfg: int, layer: int, nrows: int, dim: int):
     codes = g.integers(0, 256, size=(nrows, dim // 2), dtype=np.uint8)
     scales = g.integers(0x20, 0x40, size=(nrows, dim // 16), dtype=np.uint8)
     return codes, scales
+
+
+def token_rows(cfg: int, layer: int, seq: int, row0: int, nrows: int, d_in: int) -> np.ndarray:
+    """Pre-compression token rows row0.. of one sequence as bf16 bit patterns
+    (uint16 [nrows, d_in]), N(0,1) before rounding."""
+    x = gaussian_rows(cfg, TAG_TOKENS, layer, seq, row0, nrows, d_in)
+    return f32_to_bf16_bits(x).reshape(nrows, d_in)
+
+
+def w_c(cfg: int, layer: int, dim: int, ratio: int, d_in: int) -> np.ndarray:
+    """Compressor weight as bf16 bit patterns, uint16 [dim, ratio * d_in]: row c
+    holds output channel c's weights over the ratio concatenated token rows,
+    N(0, 1/(ratio * d_in)) before rounding."""
+    k = ratio * d_in
+    x = rng(cfg, TAG_W_C, layer).standard_normal((dim, k), dtype=np.float32)
+    x = (x * np.float32(1.0 / math.sqrt(k))).astype(np.float32)
+    return f32_to_bf16_bits(x).reshape(dim, k)
 
 
 def ragged_lengths(cfg: int, n: int, lo: int, hi: int) -> np.ndarray:
