@@ -27,9 +27,12 @@ order or the window-row scaling; the readings taken here are:
   section "CSA2注意力" say the indexer key is projected from the main-KV
   entry; its format is not given, so it reuses this FP4 codec).
 
-"Nearest to the exact quotient" is evaluated without dividing: |a - 6 v| and
-||x| - g s| are exact in fp64 for every candidate that can win (all operands
-are fp32 numbers and 6 v, g s have at most 7 significant bits).
+"Nearest to the exact quotient" is evaluated without dividing: below the top
+of the grid, |a - 6 v| and ||x| - g s| are exact in fp64 wherever the choice
+depends on them (all operands are fp32 numbers and 6 v, g s have at most 7
+significant bits); at or beyond the top (a >= 6 * 448, |x| >= 6 s) the
+largest grid value is taken directly, since there the fp64 distances of huge
+inputs can round to one value.
 
 Parity pins (tests/test_oracle_codec.py): decode table against torch's
 float8_e4m3fn; encode against an exact-rational brute force; E2M1 grid and the
@@ -88,13 +91,18 @@ def _nearest_index(num_abs: np.ndarray, den: np.ndarray | float, grid: np.ndarra
     step = max(1, (1 << 22) // len(grid))
     for lo in range(0, flat_n.size, step):
         n = flat_n[lo:lo + step, None]
+        top = flat_d[lo:lo + step] * grid[-1]
         d = np.abs(n - flat_d[lo:lo + step, None] * grid[None, :])
         best = d.min(axis=1, keepdims=True)
         hit = d == best
         first = hit.argmax(axis=1)
         nxt = np.minimum(first + 1, len(grid) - 1)
         tie = hit[np.arange(hit.shape[0]), nxt] & (nxt != first)
-        out[lo:lo + step] = np.where(tie & (first % 2 == 1), nxt, first)
+        near = np.where(tie & (first % 2 == 1), nxt, first)
+        # at or beyond the top of the grid the largest value is nearest
+        # (saturation); taken explicitly, since for huge inputs the fp64
+        # distances to all candidates round to one value
+        out[lo:lo + step] = np.where(n[:, 0] >= top, len(grid) - 1, near)
     return out.reshape(num_abs.shape)
 
 

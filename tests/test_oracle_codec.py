@@ -56,6 +56,9 @@ def _interesting_f32(rng, n):
         (rng.standard_normal(n) * 300).astype(np.float32),
         (rng.standard_normal(n) * 1e4).astype(np.float32),
         np.ldexp(rng.random(n), rng.integers(-16, 12, n)).astype(np.float32),
+        # far beyond the grid: saturation
+        np.ldexp(rng.random(n) + 0.5, rng.integers(12, 127, n)).astype(np.float32),
+        np.array([np.finfo(np.float32).max, 2.0 ** 100, 449.0, 464.0, 465.0], np.float32),
     ]
     mids = (codec.E4M3_POS[:-1] + codec.E4M3_POS[1:]) / 2
     m32 = mids.astype(np.float32)
@@ -133,7 +136,11 @@ def test_fp4_random_rows_against_exact_bruteforce():
     rows = [rng.standard_normal(64).astype(np.float32),
             (rng.standard_normal(64) * 1e-4).astype(np.float32),
             (rng.standard_normal(64) * 5e3).astype(np.float32),
-            np.ldexp(rng.standard_normal(64), rng.integers(-20, 10, 64)).astype(np.float32)]
+            np.ldexp(rng.standard_normal(64), rng.integers(-20, 10, 64)).astype(np.float32),
+            # groups whose amax / 6 is far beyond the largest scale (saturating scale and codes)
+            np.ldexp(rng.standard_normal(64), rng.integers(20, 125, 64)).astype(np.float32),
+            np.concatenate([np.full(16, np.finfo(np.float32).max), np.full(16, -1e30),
+                            (rng.standard_normal(16) * 1e25), (rng.standard_normal(16) * 3000)]).astype(np.float32)]
     x = np.stack(rows)
     x[1, 5] = -0.0
     x[2, 16:32] = 0.0
