@@ -40,6 +40,7 @@ METRIC = "CSA2 decode query-tokens/s + achieved HBM GB/s vs peak, 20-layer decod
 METRIC_PREFILL = "CSA2 encoder prefill query-tokens/s, 18 layers, 4,096-token chunk @128K tokens"
 HBM_PEAK_GBS = 8000.0
 F16_MFMA_PEAK_TFLOPS = 2500.0   # dense f16/bf16 MFMA, MI355X
+F64_MFMA_PEAK_TFLOPS = 78.6     # fp64 MFMA, MI355X
 
 
 def parse():
@@ -284,8 +285,12 @@ class CedDecodeWorkload:
                     del x
             kv = csa2.fp4_cache(kc, ks, seq_start, seq_len, D, int(elens.max()), r)
             idx = csa2.fp4_cache(ic, is_, seq_start, seq_len, DI, int(elens.max()), r)
-            new = np.stack([synth.main_kv_rows(wl.cfg + 100 + gi, s, int(elens[s]) - 1, 1, D)[0] for s in range(S)])
-            new_kv = torch.from_numpy(new).to(dev)
+            # the entry each token completes comes from the compressor: the
+            # sequence's last r token rows (bf16) times this group's W_c
+            tok = np.concatenate([synth.token_rows(wl.cfg + 100 + gi, 0, s, r * (int(elens[s]) - 1), r, D)
+                                  for s in range(S)])
+            tok = torch.from_numpy(tok.view(np.int16)).to(dev)
+            w_c = torch.from_numpy(synth.w_c(wl.cfg + 100, gi, D, r, D).view(np.int16)).to(dev)
             new_dst = torch.from_numpy(starts + elens - 1).to(dev)
             lt = [layer_tensors(layer + i) for i in range(len(modes))]
             qi = synth.q_idx(wl.cfg, layer, M, wl.idx_heads, DI)
@@ -297,10 +302,11 @@ class CedDecodeWorkload:
                            torch.from_numpy(qi.view(np.int16)).to(dev).view(torch.bfloat16),
                            torch.from_numpy(wi).to(dev), P, K, pool, cnt, topk, None,
                            [t[0] for t in lt], csa2.CSA2_BF16, H, [t[1] for t in lt], [t[2] for t in lt],
-                           [t[3] for t in lt], D ** -0.5, new_kv=new_kv, new_dst_row=new_dst, w_ik=w_ik)
+                           [t[3] for t in lt], D ** -0.5)
             g.topk_tensor = topk
             self.enc_groups.append(g)
-            self.enc_tensors.append((kc, ks, ic, is_, new_kv, new_dst, lt))
+            self.enc_tensors.append((kc, ks, ic, is_, (tok, w_c), new_dst, lt))
+            self.w_ik_enc = w_ik
             layer += len(modes)
         ws_bytes = max([csa2.csa2_group_workspace_size(g) for g in self.enc_groups] +
                        [csa2.csa2_attn_workspace_size(M, H, D, 0, W), self.dec.ws.numel()])
@@ -313,7 +319,9 @@ class CedDecodeWorkload:
         csa2, dec = self.csa2, self.dec
         for q, sw, out, lse in self.swa_only:
             csa2.csa2_sparse_swa_attn(dec.kv, dec.qs, q, None, 0, sw, self.wl.dim ** -0.5, out, lse, self.ws)
-        for g in self.enc_groups:
+        r = self.wl.extra["encoder_ratio"]
+        for g, (kc, ks, ic, is_, (tok, w_c), dst, _) in zip(self.enc_groups, self.enc_tensors):
+            csa2.csa2_compress_fp4(tok, r, w_c, kc, ks, dst_row=dst, w_ik=self.w_ik_enc, ik_codes=ic, ik_scales=is_)
             csa2.csa2_group_step(g, self.ws)
         for g in dec.groups:
             csa2.csa2_group_step(g, self.ws)
@@ -360,7 +368,8 @@ class CedDecodeWorkload:
         for _ in ex["encoder_groups"]:
             enc += int(self.elens.sum()) * idx_row                              # first scan
             enc += self.M * 8 * ex["encoder_pool_blocks"] * idx_row             # re-score of the pool
-            enc += self.M * (D * 4 + kv_row + idx_row)                          # write path
+            r = ex["encoder_ratio"]
+            enc += self.M * (r * D * 2 + 2 * kv_row + idx_row) + 2 * D * r * D  # compressor + key derivation
         enc += n_enc_layers * self.M * attn_per_q + ex["swa_only_layers"] * self.M * swa_per_q
         return self.dec.step_bytes() + enc
 
@@ -391,17 +400,21 @@ class PrefillWorkload:
         self.new_dst = torch.arange(E - R, E, dtype=torch.int64, device=dev)
         seq_start = torch.zeros(1, dtype=torch.int64, device=dev)
         seq_len = torch.tensor([E], dtype=torch.int32, device=dev)
-        self.caches = []                                  # per Full group: (kv, idx, new rows, tensors)
+        # per Full group: its caches (the earlier entries written once at set-up)
+        # and its compressor: the chunk's M token rows (bf16) and W_c, whose
+        # R = M / ratio entries the step writes with their indexer keys
+        self.caches = []
         for gi in range(len(wl.groups)):
             kc, ks = torch.empty((E, D // 2), **u8), torch.empty((E, D // 16), **u8)
             ic, is_ = torch.empty((E, DI // 2), **u8), torch.empty((E, DI // 16), **u8)
-            x = torch.from_numpy(synth.main_kv_rows(wl.cfg, gi, 0, E, D)).to(dev)
-            csa2.csa2_quantize_fp4(x, kc, ks, w_ik=w_ik, ik_codes=ic, ik_scales=is_)
-            new_kv = x[E - R:].clone()
+            x = torch.from_numpy(synth.main_kv_rows(wl.cfg, gi, 0, E - R, D)).to(dev)
+            csa2.csa2_quantize_fp4(x, kc[:E - R], ks[:E - R], w_ik=w_ik, ik_codes=ic[:E - R], ik_scales=is_[:E - R])
             del x
+            tok = torch.from_numpy(synth.token_rows(wl.cfg, gi, 0, t0, M, D).view(np.int16)).to(dev)
+            w_c = torch.from_numpy(synth.w_c(wl.cfg, gi, D, ratio, D).view(np.int16)).to(dev)
             kv = csa2.fp4_cache(kc, ks, seq_start, seq_len, D, E, ratio)
             idx = csa2.fp4_cache(ic, is_, seq_start, seq_len, DI, E, ratio)
-            self.caches.append((kv, idx, new_kv, (kc, ks, ic, is_)))
+            self.caches.append((kv, idx, (tok, w_c), (kc, ks, ic, is_)))
         self.M = M
         self.q_pos_host = np.arange(t0, t0 + M, dtype=np.int64)
         self.qs = csa2.queries(torch.zeros(M, dtype=torch.int32, device=dev),
@@ -425,7 +438,7 @@ class PrefillWorkload:
         layer = 0
         for gi, modes in enumerate(wl.groups):
             n = len(modes)
-            kv, idx, new_kv, _ = self.caches[gi]
+            kv, idx, _, _ = self.caches[gi]
             qi = synth.q_idx(wl.cfg, layer, M, wl.idx_heads, DI)
             wi = synth.w_idx(wl.cfg, layer, M, wl.idx_heads)
             topk = torch.empty((M, K), dtype=torch.int32, device=dev)
@@ -433,8 +446,7 @@ class PrefillWorkload:
                            torch.from_numpy(qi.view(np.int16)).to(dev).view(torch.bfloat16),
                            torch.from_numpy(wi).to(dev), 0, K, None, None, topk, None,
                            self.q[layer:layer + n], csa2.CSA2_BF16, H, self.swa[layer:layer + n],
-                           self.out[layer:layer + n], self.lse[layer:layer + n], D ** -0.5,
-                           new_kv=new_kv, new_dst_row=self.new_dst, w_ik=self.w_ik)
+                           self.out[layer:layer + n], self.lse[layer:layer + n], D ** -0.5)
             g.topk_tensor = topk
             self.groups.append(g)
             layer += n
@@ -443,8 +455,11 @@ class PrefillWorkload:
         torch.cuda.synchronize()
 
     def step(self):
-        for g in self.groups:
-            self.csa2.csa2_group_step(g, self.ws)
+        csa2 = self.csa2
+        for g, (_, _, (tok, w_c), (kc, ks, ic, is_)) in zip(self.groups, self.caches):
+            csa2.csa2_compress_fp4(tok, self.wl.ratio, w_c, kc, ks, dst_row=self.new_dst, w_ik=self.w_ik,
+                                   ik_codes=ic, ik_scales=is_)
+            csa2.csa2_group_step(g, self.ws)
 
     def snapshot(self):
         t = self.torch
@@ -465,10 +480,20 @@ class PrefillWorkload:
         return 4.0 * self.M * wl.heads * wl.dim * (wl.top_k + wl.window)
 
     def write_bytes_per_launch(self) -> int:
-        # fp32 input rows, their FP4 rows and derived FP4 indexer keys, the destination rows, W_ik once
+        # the key derivation: the written FP4 rows read back, their FP4 indexer keys, the destination rows, W_ik
         wl = self.wl
         D, DI = wl.dim, wl.idx_dim
-        return self.R * (4 * D + D // 2 + D // 16 + DI // 2 + DI // 16 + 8) + 4 * D * DI
+        return self.R * (D // 2 + D // 16 + DI // 2 + DI // 16 + 8) + 4 * D * DI
+
+    def compress_flops_per_launch(self) -> float:
+        wl = self.wl
+        return 2.0 * self.R * (wl.ratio * wl.dim) * wl.dim
+
+    def compress_bytes_per_launch(self) -> int:
+        # bf16 token rows and W_c, the FP4 entries written, the destination rows
+        wl = self.wl
+        D, K = wl.dim, wl.ratio * wl.dim
+        return self.R * (2 * K + D // 2 + D // 16 + 8) + 2 * D * K
 
 
 # ---------------------------------------------------------------------------
@@ -579,11 +604,26 @@ def cpu_baseline_prefill(wl, synth) -> dict:
     runs = [one_token() for _ in range(3)]
     t_tok, t_scan = sorted(runs)[1]
     n_full = int(wl.seq_lens[0])
-    t_full_ctx = t_tok + t_scan * (n_full / ns - 1.0)
+    # the write path: the compressor with FP4 write and key derivation for 64
+    # entries, counted as 1/ratio entry per query token and Full group
+    from oracle import compressor
+    ne = 64
+    tok = synth.bf16_bits_to_f32(synth.token_rows(wl.cfg, 0, 0, 0, ne * wl.ratio, D))
+    w_c = synth.bf16_bits_to_f32(synth.w_c(wl.cfg, 0, D, wl.ratio, D))
+    w_ik = synth.w_ik(wl.cfg, D, DI)
+    tw = []
+    for _ in range(3):
+        ts = time.perf_counter()
+        compressor.compress_write(tok, w_c, wl.ratio, w_ik)
+        tw.append(time.perf_counter() - ts)
+    t_write = sorted(tw)[1] / ne / wl.ratio * len(wl.groups)
+    t_full_ctx = t_tok + t_scan * (n_full / ns - 1.0) + t_write
     return {"value": 1.0 / t_full_ctx, "unit": "query-tokens/s", "cores": int(_blas_cores()), "kind": "oracle",
             "sample": (f"NumPy fp64 oracle, one prefill query through all {wl.n_layers} encoder layers over the "
                        f"first {ns} entries (median of 3: {t_tok * 1e3:.0f} ms, flat Top-K incl. FP4 decode of the "
-                       f"keys {t_scan * 1e3:.0f} ms); the flat Top-K scaled linearly to {n_full} entries")}
+                       f"keys {t_scan * 1e3:.0f} ms); the flat Top-K scaled linearly to {n_full} entries; plus "
+                       f"the compressor write of {ne} entries scaled to 1/{wl.ratio} entry per token and Full "
+                       f"group ({t_write * 1e3:.2f} ms)")}
 
 
 # ---------------------------------------------------------------------------
@@ -641,12 +681,13 @@ def time_steps(torch, W, steps, warmup, mode):
 
 
 def kernel_times(torch, csa2, W, steps):
-    """Average launch durations of the first scan, the attention and the
-    quantise-on-write kernels from HIP events stamped by their own dispatches,
+    """Average launch durations of the first scan, the attention, the
+    quantise-on-write and the compressor kernels from HIP events stamped by their own dispatches,
     over `steps` eager steps (events cannot be timed inside a graph replay)."""
     csa2.csa2_profile_scan(True)
     csa2.csa2_profile_attn(True)
     csa2.csa2_profile_write(True)
+    csa2.csa2_profile_compress(True)
     try:
         for _ in range(steps):
             W.step()
@@ -654,11 +695,13 @@ def kernel_times(torch, csa2, W, steps):
         sc = csa2.csa2_profile_scan_read()
         at = csa2.csa2_profile_attn_read()
         wr = csa2.csa2_profile_write_read()
+        cp = csa2.csa2_profile_compress_read()
     finally:
         csa2.csa2_profile_scan(False)
         csa2.csa2_profile_attn(False)
         csa2.csa2_profile_write(False)
-    return {"scan": sc, "attn": at, "write": wr, "steps": steps}
+        csa2.csa2_profile_compress(False)
+    return {"scan": sc, "attn": at, "write": wr, "compress": cp, "steps": steps}
 
 
 def time_cold(torch, W, reps):
@@ -723,8 +766,10 @@ def run_prefill(args, wl, torch, csa2, synth) -> dict:
     ms_per_step, wall = time_steps(torch, W, args.steps, args.warmup, "eager")
     kt = kernel_times(torch, csa2, W, args.steps)
     assert kt["scan"][1] == args.steps * len(wl.groups) and kt["attn"][1] == args.steps * wl.n_layers, kt
-    assert kt["write"][1] == args.steps * len(wl.groups), kt
+    assert kt["write"][1] == args.steps * len(wl.groups) and kt["compress"][1] == args.steps * len(wl.groups), kt
     at_avg, sc_avg, wr_avg = avg_ms(kt["attn"]), avg_ms(kt["scan"]), avg_ms(kt["write"])
+    cp_avg = avg_ms(kt["compress"])
+    cp_tf = W.compress_flops_per_launch() / (cp_avg / 1e3) / 1e12
     at_tf = W.attn_flops_per_launch() / (at_avg / 1e3) / 1e12
     sc_tf = W.scoring_flops_per_launch() / (sc_avg / 1e3) / 1e12
     wr_b = W.write_bytes_per_launch()
@@ -743,6 +788,7 @@ def run_prefill(args, wl, torch, csa2, synth) -> dict:
         "data": "synthetic",
         "config": {"workload": wl.name, "queries": W.M, "entries": int(wl.seq_lens[0]), "ratio": wl.ratio,
                    "layers": wl.n_layers, "layout": "3x(Full+5Reuse), flat Top-K, caches per Full group",
+                   "write_path": "compressor over the chunk's token rows (ratio 2) + FP4 + derived keys",
                    "latent_dim": wl.dim, "heads": wl.heads, "idx_heads": wl.idx_heads, "idx_dim": wl.idx_dim,
                    "top_k": wl.top_k, "window": wl.window,
                    "storage": "FP4 E2M1/E4M3x16 main+indexer, FP8 E4M3 window"},
@@ -755,7 +801,14 @@ def run_prefill(args, wl, torch, csa2, synth) -> dict:
                             "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(sc_tf / F16_MFMA_PEAK_TFLOPS, 4), "avg_launch_ms": round(sc_avg, 4),
                             "algorithmic_flops_per_launch": W.scoring_flops_per_launch()},
-        "quantize_on_write": {"bound": "hbm", "kernel": "k_quantize_fp4_derive", "rows_per_launch": W.R,
+        "compressor": {"bound": "mfma", "kernel": "k_compress_fp4 (fp64 matrix cores, FP4 write fused)",
+                       "entries_per_launch": W.R, "k": wl.ratio * wl.dim, "achieved": round(cp_tf, 2),
+                       "peak": F64_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(cp_tf / F64_MFMA_PEAK_TFLOPS, 4),
+                       "avg_launch_ms": round(cp_avg, 5),
+                       "algorithmic_flops_per_launch": W.compress_flops_per_launch(),
+                       "algorithmic_bytes_per_launch": W.compress_bytes_per_launch()},
+        "quantize_on_write": {"bound": "hbm", "kernel": "k_quantize_fp4_derive_mfma (keys of the rows just written)",
+                              "rows_per_launch": W.R,
                               "avg_launch_ms": round(wr_avg, 5), "algorithmic_bytes_per_launch": wr_b,
                               "achieved_gbs": round(wr_b / (wr_avg / 1e3) / 1e9, 1),
                               "frac": round(wr_b / (wr_avg / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -916,13 +969,17 @@ def main():
         rc = decode_record(wc, Wc, msc, ktc, "graph")
         rc["layers"] = "2 window-only + 3x(Full+5Reuse) at ratio 2 + decoder 20"
         rc["global_cache_bytes_per_token"] = Wc.cache_bytes_per_token()
+        rc["compressor_avg_launch_ms"] = round(avg_ms(ktc["compress"]), 5)
+        rc["write_path"] = ("encoder groups: k_compress_fp4 (ratio 2, one entry per sequence) + key derivation; "
+                            "decoder: quantise-on-write of given rows")
         extras[f"{wc.name}/graph"] = rc
         del Wc
         torch.cuda.empty_cache()
         wp = synth.workload(2)
         pre = run_prefill(args, wp, torch, csa2, synth)
         extras[wp.name] = {k: pre[k] for k in ("metric", "value", "unit", "ms_per_step", "config", "roofline",
-                                                "indexer_scoring", "quantize_on_write", "cpu_baseline")
+                                                "indexer_scoring", "compressor", "quantize_on_write",
+                                                "cpu_baseline")
                            if k in pre}
         result["workloads"] = extras
     print(json.dumps(result), flush=True)

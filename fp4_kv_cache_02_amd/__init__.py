@@ -24,7 +24,8 @@ EXPORTS = [
     "csa2_dequant_fp4", "csa2_index_workspace_size", "csa2_index_full", "csa2_reindex",
     "csa2_attn_workspace_size", "csa2_sparse_swa_attn", "csa2_group_workspace_size", "csa2_group_step",
     "csa2_profile_scan", "csa2_profile_scan_read", "csa2_profile_attn", "csa2_profile_attn_read",
-    "csa2_profile_write", "csa2_profile_write_read", "csa2_group_step_static",
+    "csa2_profile_write", "csa2_profile_write_read", "csa2_group_step_static", "csa2_compress_fp4",
+    "csa2_profile_compress", "csa2_profile_compress_read",
 ]
 
 
@@ -97,6 +98,9 @@ def lib() -> ctypes.CDLL:
             "csa2_profile_write": (i32, [i32]),
             "csa2_profile_write_read": (i32, [POINTER(ctypes.c_double), POINTER(c_int64)]),
             "csa2_group_step_static": (i32, [POINTER(GroupDesc), vp]),
+            "csa2_compress_fp4": (i32, [vp, i64, i32, i32, vp, i32, vp, vp, vp, vp, i32, vp, vp, vp]),
+            "csa2_profile_compress": (i32, [i32]),
+            "csa2_profile_compress_read": (i32, [POINTER(ctypes.c_double), POINTER(c_int64)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -181,6 +185,19 @@ def csa2_quantize_fp4(x, codes, scales, dst_row=None, w_ik=None, ik_codes=None, 
     _check(lib().csa2_quantize_fp4(_ptr(x), _dtype_code(x), rows, dim, _ptr(dst_row), _ptr(codes), _ptr(scales),
                                    _ptr(w_ik), idx_dim, _ptr(ik_codes), _ptr(ik_scales), _stream(stream)),
            "csa2_quantize_fp4")
+
+
+def csa2_compress_fp4(tokens, ratio, w_c, codes, scales, dst_row=None, w_ik=None, ik_codes=None, ik_scales=None,
+                      stream=None):
+    """tokens: bf16 bits (int16/uint16 tensor) [entries * ratio, d_in]; w_c: bf16 bits [dim, ratio * d_in]."""
+    n_tok, d_in = int(tokens.shape[0]), int(tokens.shape[1])
+    if ratio < 1 or n_tok % ratio:
+        raise ValueError("token rows must be a whole number of entries")
+    dim = int(w_c.shape[0])
+    idx_dim = int(w_ik.shape[1]) if w_ik is not None else 0
+    _check(lib().csa2_compress_fp4(_ptr(tokens), n_tok // ratio, int(ratio), d_in, _ptr(w_c), dim, _ptr(dst_row),
+                                   _ptr(codes), _ptr(scales), _ptr(w_ik), idx_dim, _ptr(ik_codes), _ptr(ik_scales),
+                                   _stream(stream)), "csa2_compress_fp4")
 
 
 def csa2_quantize_fp8_rows(x, codes, scale, dst_row=None, stream=None):
@@ -324,4 +341,15 @@ def csa2_profile_write_read() -> tuple[float, int]:
     """(summed quantise-on-write kernel milliseconds, launches) since write timing was enabled."""
     ms, n = ctypes.c_double(0.0), c_int64(0)
     _check(lib().csa2_profile_write_read(ctypes.byref(ms), ctypes.byref(n)), "csa2_profile_write_read")
+    return float(ms.value), int(n.value)
+
+
+def csa2_profile_compress(enable: bool) -> None:
+    _check(lib().csa2_profile_compress(1 if enable else 0), "csa2_profile_compress")
+
+
+def csa2_profile_compress_read() -> tuple[float, int]:
+    """(summed compressor kernel milliseconds, launches) since compressor timing was enabled."""
+    ms, n = ctypes.c_double(0.0), c_int64(0)
+    _check(lib().csa2_profile_compress_read(ctypes.byref(ms), ctypes.byref(n)), "csa2_profile_compress_read")
     return float(ms.value), int(n.value)

@@ -16,7 +16,7 @@ struct Timing {
   bool on = false;
   std::vector<hipEvent_t> events;   // begin/end pairs in launch order
 };
-Timing g_timing[3];                 // 0: first scan, 1: attention, 2: quantise-on-write
+Timing g_timing[4];                 // 0: first scan, 1: attention, 2: quantise-on-write, 3: compressor
 
 void clear_events(Timing &t) {
   for (hipEvent_t e : t.events) (void)hipEventDestroy(e);
@@ -147,6 +147,27 @@ int32_t csa2_quantize_fp4(const void *x, int32_t x_dtype, int64_t rows, int32_t 
   }
   return launch_quantize_fp4(x, x_dtype, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales,
                              (hipStream_t)stream);
+}
+
+int32_t csa2_compress_fp4(const uint16_t *tokens, int64_t entries, int32_t ratio, int32_t d_in, const uint16_t *w_c,
+                          int32_t dim, const int64_t *dst_row, uint8_t *codes, uint8_t *scales, const float *w_ik,
+                          int32_t idx_dim, uint8_t *ik_codes, uint8_t *ik_scales, void *stream) {
+  if (entries < 0 || ratio < 1 || ratio > 16 || d_in <= 0 || d_in % 32 != 0 || d_in > 8192 ||
+      (int64_t)ratio * d_in > 16384 || dim <= 0 || dim % 32 != 0)
+    return CSA2_ERR_BAD_SHAPE;
+  if (dim > 512) return CSA2_ERR_UNSUPPORTED;
+  if (entries == 0) return CSA2_OK;
+  if (entries > ((int64_t)1 << 31)) return CSA2_ERR_UNSUPPORTED;
+  if (!tokens || !w_c || !codes || !scales) return CSA2_ERR_NULL_ARG;
+  if (!aligned(tokens, 16) || !aligned(w_c, 16) || !aligned(codes, 8)) return CSA2_ERR_MISALIGNED;
+  if (w_ik) {
+    if (!ik_codes || !ik_scales) return CSA2_ERR_NULL_ARG;
+    if (idx_dim != 32 && idx_dim != 64 && idx_dim != 128 && idx_dim != 256) return CSA2_ERR_UNSUPPORTED;
+    if (idx_dim > dim) return CSA2_ERR_UNSUPPORTED;
+    if (!aligned(ik_codes, 8)) return CSA2_ERR_MISALIGNED;
+  }
+  return launch_compress_fp4(tokens, entries, ratio, d_in, w_c, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes,
+                             ik_scales, (hipStream_t)stream);
 }
 
 int32_t csa2_quantize_fp8_rows(const void *x, int32_t x_dtype, int64_t rows, int32_t dim, const int64_t *dst_row,
@@ -398,6 +419,16 @@ int32_t csa2_profile_write(int32_t enable) {
 
 int32_t csa2_profile_write_read(double *total_ms, int64_t *launches) {
   return read_events(g_timing[2], total_ms, launches);
+}
+
+int32_t csa2_profile_compress(int32_t enable) {
+  clear_events(g_timing[3]);
+  g_timing[3].on = enable != 0;
+  return CSA2_OK;
+}
+
+int32_t csa2_profile_compress_read(double *total_ms, int64_t *launches) {
+  return read_events(g_timing[3], total_ms, launches);
 }
 
 }  // extern "C"

@@ -173,6 +173,10 @@ typedef double double4_t __attribute__((ext_vector_type(4)));
 constexpr int kDeriveRows = 16;
 constexpr int kDeriveMaxDim = 512;
 
+//
+// T = uint8_t derives the keys of rows already in the cache instead: their
+// codes and scales are read from the destination rows (nothing is encoded or
+// written to the main planes, x is unused).
 template <typename T, int CT, int KS>
 __global__ __launch_bounds__(64 * CT * KS) void k_quantize_fp4_derive_mfma(
     const T *__restrict__ x, int64_t rows, int dim, const int64_t *__restrict__ dst_row, uint8_t *__restrict__ codes,
@@ -210,17 +214,23 @@ __global__ __launch_bounds__(64 * CT * KS) void k_quantize_fp4_derive_mfma(
       for (int i = 0; i < 16; ++i) dst[i] = 0.0;
       continue;
     }
-    float v[16];
-    const T *src = x + (r0 + rr) * dim + g * kGroup;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = load_as_f32<T>(src + i);
     uint2 packed;
     uint8_t sb;
-    encode_group(v, &packed, &sb);
-    if (blockIdx.y == 0) {
+    if constexpr (__is_same(T, uint8_t)) {
       const int64_t d = dst_row ? dst_row[r0 + rr] : r0 + rr;
-      *reinterpret_cast<uint2 *>(codes + d * (dim / 2) + g * 8) = packed;
-      scales[d * gpr + g] = sb;
+      packed = *reinterpret_cast<const uint2 *>(codes + d * (dim / 2) + g * 8);
+      sb = scales[d * gpr + g];
+    } else {
+      float v[16];
+      const T *src = x + (r0 + rr) * dim + g * kGroup;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = load_as_f32<T>(src + i);
+      encode_group(v, &packed, &sb);
+      if (blockIdx.y == 0) {
+        const int64_t d = dst_row ? dst_row[r0 + rr] : r0 + rr;
+        *reinterpret_cast<uint2 *>(codes + d * (dim / 2) + g * 8) = packed;
+        scales[d * gpr + g] = sb;
+      }
     }
     const float sc = e4m3_pos_value(sb);
 #pragma unroll
@@ -275,6 +285,116 @@ __global__ __launch_bounds__(64 * CT * KS) void k_quantize_fp4_derive_mfma(
   }
 }
 
+// Compressor (ratio r) fused with the FP4 write.  Entry j is fp32(W_c^T
+// [x_rj; ...; x_rj+r-1]) (P4 section 二; P5 section "CSA2注意力": adjacent
+// entries do not overlap and no position term is added).  The r token rows
+// of entry j are row j of the token buffer viewed as [entries][K], K = r d_in,
+// so the compressor is that bf16 matrix times W_c^T.  A product of two bf16
+// values is exact in fp64 and v_mfma_f64_16x16x4_f64 accumulates in fp64; the
+// sum is rounded once to fp32, like the fp64 product it restates.
+//
+// grid (ceil(entries / 16), dim / (16 CTC)), 64 KW threads.  A workgroup
+// computes 16 entries x 16 CTC channels.  Its KW waves split K in KW slices;
+// in a wave, k-slot q = l / 16 of the MFMA walks the q-th quarter of the
+// slice in ascending k (8 values per 16-byte load), and lane l supplies the
+// token value of row l % 16 and the weight of column l % 16 at that slot's k,
+// so every slot pairs operands of the same k.  The slices' partial tiles are
+// added in slice order in fp64 and rounded to fp32; each 16-channel column
+// tile is one FP4 group, encoded and written to the entry's cache row.
+constexpr int kCompressRound = 4;   // 16-byte chunks per operand loaded before use
+
+CSA2_DEV double bf16_elem(const u32x4_t &v, int i) {
+  const uint32_t w = v[i / 2];
+  return (double)__uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
+template <int CTC, int KW>
+__global__ __launch_bounds__(64 * KW) void k_compress_fp4(const uint16_t *__restrict__ tokens, int64_t entries,
+                                                          int K, const uint16_t *__restrict__ w_c, int dim,
+                                                          const int64_t *__restrict__ dst_row,
+                                                          uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+  __shared__ double part[KW > 1 ? KW * CTC * 256 : 1];
+  __shared__ float ent[kDeriveRows * 16 * CTC];
+  const int64_t e0 = (int64_t)blockIdx.x * kDeriveRows;
+  const int nr = (int)min<int64_t>(kDeriveRows, entries - e0);
+  const int l = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c0 = blockIdx.y * 16 * CTC;
+  const int kq = K / (4 * KW);                    // k values per lane, a multiple of 8
+  const int nch = kq / 8;
+  const int kbase = wv * (K / KW) + (l / 16) * kq;
+  // rows past the last entry lie outside the resource and read as 0
+  const rsrc_t r_x = make_rsrc(tokens + e0 * K, (uint32_t)(nr * K * 2));
+  const rsrc_t r_w = make_rsrc(w_c + (int64_t)c0 * K, (uint32_t)(16 * CTC * K * 2));
+  const uint32_t xoff = (uint32_t)(((l % 16) * K + kbase) * 2);
+  uint32_t woff[CTC];
+#pragma unroll
+  for (int t = 0; t < CTC; ++t) woff[t] = (uint32_t)(((16 * t + l % 16) * K + kbase) * 2);
+  double4_t acc[CTC];
+#pragma unroll
+  for (int t = 0; t < CTC; ++t) acc[t] = (double4_t){0.0, 0.0, 0.0, 0.0};
+  for (int ch0 = 0; ch0 < nch; ch0 += kCompressRound) {
+    u32x4_t xa[kCompressRound], wb[kCompressRound][CTC];
+#pragma unroll
+    for (int c = 0; c < kCompressRound; ++c) {
+      const bool in = ch0 + c < nch;
+      xa[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                              r_x, in ? xoff + (uint32_t)(ch0 + c) * 16 : kOutOfRange, 0, 0));
+#pragma unroll
+      for (int t = 0; t < CTC; ++t)
+        wb[c][t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   r_w, in ? woff[t] + (uint32_t)(ch0 + c) * 16 : kOutOfRange, 0, 0));
+    }
+    // chunks past the lane's range read as 0 and add +0 (no branch here,
+    // so all the round's loads are in flight before the first product)
+#pragma unroll
+    for (int c = 0; c < kCompressRound; ++c) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double a = bf16_elem(xa[c], i);
+#pragma unroll
+        for (int t = 0; t < CTC; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bf16_elem(wb[c][t], i), acc[t], 0, 0, 0);
+      }
+    }
+  }
+  // lane l holds rows l / 16 + 4 i of column l % 16 of each tile
+  constexpr int EW = 16 * CTC;                    // entry tile row stride (floats)
+  if constexpr (KW > 1) {
+#pragma unroll
+    for (int t = 0; t < CTC; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[((wv * CTC + t) * 64 + l) * 4 + i] = acc[t][i];
+    __syncthreads();
+    for (int t = wv; t < CTC; t += KW) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        double s = 0.0;
+        for (int ks = 0; ks < KW; ++ks) s += part[((ks * CTC + t) * 64 + l) * 4 + i];
+        ent[(l / 16 + 4 * i) * EW + 16 * t + l % 16] = (float)(s + 0.0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < CTC; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ent[(l / 16 + 4 * i) * EW + 16 * t + l % 16] = (float)(acc[t][i] + 0.0);
+  }
+  __syncthreads();
+  for (int u = threadIdx.x; u < nr * CTC; u += 64 * KW) {
+    const int rr = u / CTC, g = u - rr * CTC;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = ent[rr * EW + 16 * g + i];
+    uint2 packed;
+    uint8_t sb;
+    encode_group(v, &packed, &sb);
+    const int64_t d = dst_row ? dst_row[e0 + rr] : e0 + rr;
+    const int gg = c0 / kGroup + g;
+    *reinterpret_cast<uint2 *>(codes + d * (dim / 2) + gg * 8) = packed;
+    scales[d * (dim / kGroup) + gg] = sb;
+  }
+}
+
 // FP8 window rows: one workgroup per row.
 template <typename T>
 __global__ __launch_bounds__(256) void k_quantize_fp8_rows(const T *__restrict__ x, int dim,
@@ -325,6 +445,27 @@ __global__ __launch_bounds__(256) void k_dequant_fp4(const uint8_t *__restrict__
 // launchers
 // ---------------------------------------------------------------------------
 
+// The fp64-MFMA derive (dim <= kDeriveMaxDim); T = uint8_t: keys of rows already in the cache.
+template <typename T>
+void derive_mfma(const void *x, int64_t rows, int dim, const int64_t *dst_row, uint8_t *codes, uint8_t *scales,
+                 const float *w_ik, int idx_dim, uint8_t *ik_codes, uint8_t *ik_scales, hipStream_t stream) {
+  // columns per workgroup: the largest tile count (up to 8) dividing the key's 16-column groups
+  const int cgs = idx_dim / kGroup;
+  const int ct = (cgs % 8 == 0) ? 8 : (cgs % 4 == 0) ? 4 : (cgs % 2 == 0) ? 2 : 1;
+  // few rows: split the channels over 8 waves per tile instead (dim % 32 == 0)
+  const bool few = rows <= 64 && dim % 32 == 0;
+  const dim3 grid((unsigned)((rows + kDeriveRows - 1) / kDeriveRows), (unsigned)(few ? cgs : cgs / ct));
+#define CSA2_MFMA_LAUNCH(CT, KS)                                                                              \
+  CSA2_TIMED_LAUNCH(kTimedWrite, (k_quantize_fp4_derive_mfma<T, CT, KS>), grid, dim3(64 * CT * KS), stream, \
+                    (const T *)x, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales)
+  if (few) CSA2_MFMA_LAUNCH(1, 8);
+  else if (ct == 8) CSA2_MFMA_LAUNCH(8, 1);
+  else if (ct == 4) CSA2_MFMA_LAUNCH(4, 1);
+  else if (ct == 2) CSA2_MFMA_LAUNCH(2, 1);
+  else CSA2_MFMA_LAUNCH(1, 1);
+#undef CSA2_MFMA_LAUNCH
+}
+
 int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const int64_t *dst_row,
                         uint8_t *codes, uint8_t *scales, const float *w_ik, int idx_dim, uint8_t *ik_codes,
                         uint8_t *ik_scales, hipStream_t stream) {
@@ -339,22 +480,10 @@ int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const
       CSA2_TIMED_LAUNCH(kTimedWrite, k_quantize_fp4<uint16_t>, grid, dim3(256), stream, (const uint16_t *)x, rows, dim,
                          dst_row, codes, scales);
   } else if (dim <= kDeriveMaxDim) {
-    // columns per workgroup: the largest tile count (up to 8) dividing the key's 16-column groups
-    const int cgs = idx_dim / kGroup;
-    const int ct = (cgs % 8 == 0) ? 8 : (cgs % 4 == 0) ? 4 : (cgs % 2 == 0) ? 2 : 1;
-    // few rows: split the channels over 8 waves per tile instead (dim % 32 == 0)
-    const bool few = rows <= 64 && dim % 32 == 0;
-    const dim3 grid((unsigned)((rows + kDeriveRows - 1) / kDeriveRows), (unsigned)(few ? cgs : cgs / ct));
-#define CSA2_MFMA_LAUNCH(T, CT, KS)                                                                           \
-    CSA2_TIMED_LAUNCH(kTimedWrite, (k_quantize_fp4_derive_mfma<T, CT, KS>), grid, dim3(64 * CT * KS), stream, \
-                      (const T *)x, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales)
-#define CSA2_MFMA_CT(T)                                                           \
-    if (few) CSA2_MFMA_LAUNCH(T, 1, 8);                                           \
-    else if (ct == 8) CSA2_MFMA_LAUNCH(T, 8, 1); else if (ct == 4) CSA2_MFMA_LAUNCH(T, 4, 1); \
-    else if (ct == 2) CSA2_MFMA_LAUNCH(T, 2, 1); else CSA2_MFMA_LAUNCH(T, 1, 1)
-    if (x_dtype == CSA2_F32) { CSA2_MFMA_CT(float); } else { CSA2_MFMA_CT(uint16_t); }
-#undef CSA2_MFMA_CT
-#undef CSA2_MFMA_LAUNCH
+    if (x_dtype == CSA2_F32)
+      derive_mfma<float>(x, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales, stream);
+    else
+      derive_mfma<uint16_t>(x, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales, stream);
   } else {
     const int rb = kDeriveLdsFloats / dim;
     const dim3 grid((unsigned)((rows + rb - 1) / rb));
@@ -370,6 +499,34 @@ int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const
 #undef CSA2_DERIVE_JM
 #undef CSA2_DERIVE_LAUNCH
   }
+  return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+}
+
+int launch_compress_fp4(const uint16_t *tokens, int64_t entries, int ratio, int d_in, const uint16_t *w_c, int dim,
+                        const int64_t *dst_row, uint8_t *codes, uint8_t *scales, const float *w_ik, int idx_dim,
+                        uint8_t *ik_codes, uint8_t *ik_scales, hipStream_t stream) {
+  if (entries == 0) return CSA2_OK;
+  const int K = ratio * d_in;
+  // few entries: one FP4 group per workgroup and 8 waves over K (more
+  // workgroups and shorter chains); many: 4 groups per workgroup, 4 waves
+  const bool few = entries <= 64;
+  const int gpr = dim / kGroup;
+  const int ctc = few ? 1 : (gpr % 4 == 0) ? 4 : (gpr % 2 == 0) ? 2 : 1;
+  int kw = few ? 8 : 4;
+  while (K % (32 * kw) != 0) kw /= 2;
+  const dim3 grid((unsigned)((entries + kDeriveRows - 1) / kDeriveRows), (unsigned)(gpr / ctc));
+#define CSA2_COMPRESS_LAUNCH(CTC, KW)                                                                      \
+  CSA2_TIMED_LAUNCH(kTimedCompress, (k_compress_fp4<CTC, KW>), grid, dim3(64 * KW), stream, tokens, entries, K, \
+                    w_c, dim, dst_row, codes, scales)
+#define CSA2_COMPRESS_KW(CTC)                                                                    \
+  if (kw == 8) CSA2_COMPRESS_LAUNCH(CTC, 8); else if (kw == 4) CSA2_COMPRESS_LAUNCH(CTC, 4);     \
+  else if (kw == 2) CSA2_COMPRESS_LAUNCH(CTC, 2); else CSA2_COMPRESS_LAUNCH(CTC, 1)
+  if (ctc == 4) { CSA2_COMPRESS_KW(4); } else if (ctc == 2) { CSA2_COMPRESS_KW(2); } else { CSA2_COMPRESS_KW(1); }
+#undef CSA2_COMPRESS_KW
+#undef CSA2_COMPRESS_LAUNCH
+  if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
+  if (w_ik) derive_mfma<uint8_t>(nullptr, entries, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales,
+                                 stream);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 

@@ -12,6 +12,11 @@ namespace csa2 {
 int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const int64_t *dst_row,
                         uint8_t *codes, uint8_t *scales, const float *w_ik, int idx_dim, uint8_t *ik_codes,
                         uint8_t *ik_scales, hipStream_t stream);
+// Compressor fused with the FP4 write (and the indexer keys of the written
+// rows when w_ik is given); dim <= 512, (ratio * d_in) % 32 == 0.
+int launch_compress_fp4(const uint16_t *tokens, int64_t entries, int ratio, int d_in, const uint16_t *w_c, int dim,
+                        const int64_t *dst_row, uint8_t *codes, uint8_t *scales, const float *w_ik, int idx_dim,
+                        uint8_t *ik_codes, uint8_t *ik_scales, hipStream_t stream);
 int launch_quantize_fp8_rows(const void *x, int x_dtype, int64_t rows, int dim, const int64_t *dst_row,
                              uint8_t *codes, float *scale, hipStream_t stream);
 int launch_dequant_fp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int dim, float *out,
@@ -91,11 +96,12 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---- kernel timing (csa2_api.hip) ----
 // Timed kernels: the first scan of an index call (decode scan or prefill
-// scoring), each attention launch and each quantise-on-write launch.  timing_events hands out a fresh
+// scoring), each attention launch, each quantise-on-write launch and each
+// compressor launch.  timing_events hands out a fresh
 // start/stop pair when that timing is on (both null otherwise); launched with
 // hipExtLaunchKernelGGL, the pair takes the dispatch's own start and end
 // times, so no marker packets sit between the events and the kernel.
-enum TimedKernel { kTimedScan = 0, kTimedAttn = 1, kTimedWrite = 2 };
+enum TimedKernel { kTimedScan = 0, kTimedAttn = 1, kTimedWrite = 2, kTimedCompress = 3 };
 void timing_events(int which, hipEvent_t *start, hipEvent_t *stop);
 
 #define CSA2_TIMED_LAUNCH(which, kernel, grid, block, stream, ...)                                  \

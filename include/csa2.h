@@ -148,6 +148,41 @@ int32_t csa2_quantize_fp4(const void *x, int32_t x_dtype, int64_t rows, int32_t 
                           uint8_t *ik_scales, void *stream);
 
 /* ---------------------------------------------------------------------
+ * csa2_compress_fp4 - the compressor at ratio r fused with quantise-on-write
+ * and the indexer-key derivation.
+ *
+ * P4 section 二 / P5 section "CSA2注意力": CSA2's compressor has no overlap
+ * between adjacent compressed entries and no absolute position embedding,
+ * and the indexer key is projected from the main-KV entry.  Entry j is a
+ * linear map of its own r token rows only:
+ *     c_j = fp32(W_c^T [x_{r j}; x_{r j + 1}; ...; x_{r j + r - 1}]),
+ * every bf16 x bf16 product exact, accumulated in fp64, rounded once to fp32
+ * (a zero sum is +0).  c_j is then written exactly as csa2_quantize_fp4
+ * writes an fp32 row (same FP4 rounding, same indexer key).
+ *
+ * tokens   device bf16 [entries * ratio][d_in], row-major, dense: token rows
+ *          in sequence order; entry j reads rows ratio*j .. ratio*j+ratio-1.
+ * w_c      device bf16 [dim][ratio * d_in], row-major: row c holds output
+ *          channel c's weights over the concatenated rows (x_{rj} first).
+ * dst_row  device [entries] int64: cache row entry j is written to; NULL
+ *          writes entry j to row j.
+ * codes/scales, w_ik, idx_dim, ik_codes/ik_scales  as in csa2_quantize_fp4
+ *          (w_ik NULL: no indexer keys).
+ * Enqueues two kernels on the stream: the compressor with the FP4 write,
+ * then (w_ik given) the key derivation, which reads the rows just written.
+ * tokens, w_c and the cache planes must not overlap.
+ * Errors: BAD_SHAPE (entries < 0, ratio outside 1..16, d_in % 32 != 0,
+ *         d_in > 8192, ratio * d_in > 16384, dim % 32 != 0), UNSUPPORTED
+ *         (dim > 512, entries > 2^31, idx_dim), NULL_ARG, MISALIGNED (tokens
+ *         or w_c not 16-byte aligned, codes or ik_codes not 8-byte aligned),
+ *         HIP.
+ * ------------------------------------------------------------------- */
+int32_t csa2_compress_fp4(const uint16_t *tokens, int64_t entries, int32_t ratio, int32_t d_in,
+                          const uint16_t *w_c, int32_t dim, const int64_t *dst_row, uint8_t *codes,
+                          uint8_t *scales, const float *w_ik, int32_t idx_dim, uint8_t *ik_codes,
+                          uint8_t *ik_scales, void *stream);
+
+/* ---------------------------------------------------------------------
  * csa2_quantize_fp8_rows - window-KV write (P2 section 03 / P5 section
  * "缓存精度与持久化分层": the sliding-window KV stays FP8).
  *
@@ -368,10 +403,18 @@ int32_t csa2_profile_attn_read(double *total_ms, int64_t *launches);
 /* csa2_profile_write / csa2_profile_write_read - the same timing for every
  * FP4 quantise-on-write kernel launched by csa2_quantize_fp4 /
  * csa2_group_step (one launch per call or Full group with new rows; the FP8
- * window write is not included).  Same contract and errors as
+ * window write is not included) and every key-derivation launch of
+ * csa2_compress_fp4.  Same contract and errors as
  * csa2_profile_scan. */
 int32_t csa2_profile_write(int32_t enable);
 int32_t csa2_profile_write_read(double *total_ms, int64_t *launches);
+
+/* csa2_profile_compress / csa2_profile_compress_read - the same timing for
+ * every compressor kernel launched by csa2_compress_fp4 (one per call; its
+ * key-derivation launch counts under csa2_profile_write).  Same contract and
+ * errors as csa2_profile_scan. */
+int32_t csa2_profile_compress(int32_t enable);
+int32_t csa2_profile_compress_read(double *total_ms, int64_t *launches);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = csa2.lib()
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 22
     assert sorted(names) == sorted(csa2.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", csa2.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (csa2_\w+)$", out, re.M))
@@ -89,6 +89,34 @@ def test_quantize_validation():
 
 def _cache(dim=128, max_len=4096, ratio=1, codes=FAKE):
     return csa2.Fp4Cache(codes, FAKE, FAKE, FAKE, 1, dim, max_len, ratio)
+
+
+def test_compress_validation():
+    L = csa2.lib()
+    ok = dict(tokens=FAKE, entries=10, ratio=2, d_in=512, w_c=FAKE, dim=512, dst=None, codes=FAKE, scales=FAKE,
+              w_ik=FAKE, di=128, ikc=FAKE, iks=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.csa2_compress_fp4(a["tokens"], a["entries"], a["ratio"], a["d_in"], a["w_c"], a["dim"], a["dst"],
+                                   a["codes"], a["scales"], a["w_ik"], a["di"], a["ikc"], a["iks"], None)
+
+    assert call(entries=-1) == BAD_SHAPE
+    assert call(ratio=0) == BAD_SHAPE
+    assert call(ratio=17) == BAD_SHAPE
+    assert call(d_in=48) == BAD_SHAPE
+    assert call(d_in=8192, ratio=4) == BAD_SHAPE          # ratio * d_in > 16384
+    assert call(dim=100) == BAD_SHAPE
+    assert call(dim=1024) == UNSUPPORTED
+    assert call(tokens=None) == NULL_ARG
+    assert call(w_c=None) == NULL_ARG
+    assert call(ikc=None) == NULL_ARG
+    assert call(tokens=FAKE + 8) == MISALIGNED
+    assert call(w_c=FAKE + 2) == MISALIGNED
+    assert call(codes=FAKE + 4) == MISALIGNED
+    assert call(di=48) == UNSUPPORTED
+    assert call(di=256, dim=128) == UNSUPPORTED           # key wider than the entry
+    assert call(entries=0, tokens=None, w_c=None) == 0    # empty = no-op
 
 
 def test_index_validation():

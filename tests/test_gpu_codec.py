@@ -49,12 +49,15 @@ def _adversarial_rows(dim=128):
             r = (rng.standard_normal(dim) * float(v) / 8).astype(np.float32)
             r[::16] = v
             rows.append(r)
-    special = np.zeros((6, dim), np.float32)
+    special = np.zeros((8, dim), np.float32)
     special[1, 3] = -0.0
     special[2] = -0.0
     special[3] = np.float32(6 * 2.0 ** -10)              # scale rounds to 0
     special[4] = (rng.standard_normal(dim) * 1e5).astype(np.float32)   # scale saturates
     special[5] = (rng.standard_normal(dim) * 1e-8).astype(np.float32)
+    special[6] = np.ldexp(rng.standard_normal(dim), rng.integers(20, 125, dim)).astype(np.float32)  # far beyond
+    special[7, ::2] = np.finfo(np.float32).max
+    special[7, 1::2] = -np.finfo(np.float32).max
     return np.concatenate([np.stack(rows), special]).astype(np.float32)
 
 
