@@ -76,15 +76,20 @@ def scan_source_sha256() -> str:
 
 class DecodeWorkload:
     """One decode step of the decoder: every group's write path and index,
-    and every layer's attention.  By default each group is one
-    csa2_group_step, which runs its layers' attention together (their
-    queries are inputs here).  With layer_sequential the step issues what a
-    model running layer by layer would: the group step of the group's first
-    layer, then one csa2_sparse_swa_attn call per Reuse layer."""
+    and every layer's attention.  Schedules:
+      "steps"  - one csa2_group_steps call over all groups: their indexers in
+                 group order, then every layer's attention batched across
+                 groups (the queries of all layers are inputs here);
+      "groups" - one csa2_group_step per group (its layers' attention batched);
+      "layers" - what a model running layer by layer would issue: the group
+                 step of each group's first layer, then one
+                 csa2_sparse_swa_attn call per Reuse layer."""
 
-    def __init__(self, wl, torch, csa2, synth, layer_sequential=False):
+    def __init__(self, wl, torch, csa2, synth, schedule="steps"):
         self.wl, self.torch, self.csa2 = wl, torch, csa2
-        self.layer_sequential = layer_sequential
+        assert schedule in ("steps", "groups", "layers"), schedule
+        self.schedule = schedule
+        layer_sequential = schedule == "layers"
         dev = torch.device("cuda:0")
         S, D, DI = len(wl.seq_lens), wl.dim, wl.idx_dim
         lens = np.asarray(wl.seq_lens, np.int64)
@@ -170,11 +175,16 @@ class DecodeWorkload:
         ws_bytes = max(csa2.csa2_group_workspace_size(g) for g in self.groups)
         if layer_sequential:
             ws_bytes = max(ws_bytes, csa2.csa2_attn_workspace_size(M, H, D, K, W))
+        if schedule == "steps":
+            ws_bytes = max(ws_bytes, csa2.csa2_group_steps_workspace_size(self.groups))
         self.ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)   # no initial contents needed
         torch.cuda.synchronize()
 
     def step(self):
         c = self.csa2
+        if self.schedule == "steps":
+            c.csa2_group_steps(self.groups, self.ws)
+            return
         for g in self.groups:
             c.csa2_group_step(g, self.ws)
             for layer in g.reuse_layers:
@@ -309,7 +319,8 @@ class CedDecodeWorkload:
             self.w_ik_enc = w_ik
             layer += len(modes)
         ws_bytes = max([csa2.csa2_group_workspace_size(g) for g in self.enc_groups] +
-                       [csa2.csa2_attn_workspace_size(M, H, D, 0, W), self.dec.ws.numel()])
+                       [csa2.csa2_attn_workspace_size(M, H, D, 0, W), self.dec.ws.numel(),
+                        csa2.csa2_group_steps_workspace_size(self.dec.groups)])
         self.ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)   # no initial contents needed
         self.M = M
         self.q_pos_host = self.dec.q_pos_host
@@ -323,8 +334,7 @@ class CedDecodeWorkload:
         for g, (kc, ks, ic, is_, (tok, w_c), dst, _) in zip(self.enc_groups, self.enc_tensors):
             csa2.csa2_compress_fp4(tok, r, w_c, kc, ks, dst_row=dst, w_ik=self.w_ik_enc, ik_codes=ic, ik_scales=is_)
             csa2.csa2_group_step(g, self.ws)
-        for g in dec.groups:
-            csa2.csa2_group_step(g, self.ws)
+        csa2.csa2_group_steps(dec.groups, self.ws)
 
     def snapshot(self):
         t = self.torch
@@ -745,7 +755,7 @@ def decode_record(wl, W, ms_per_step, kt, mode) -> dict:
         "roofline": {"bound": "hbm", "kernel": "first scan (k_scan)", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "avg_launch_ms": round(scan_ms, 5), "algorithmic_bytes_per_launch": scan_bytes},
-        "attention": {"kernels": "k_attn_logits + k_attn_pv per group of layers",
+        "attention": {"kernels": "k_attn_logits + k_attn_pv per batch of up to 24 layers across groups",
                       "launches_per_step": kt["attn"][1] // kt["steps"],
                       "ms_per_layer": round(attn_ms, 5),
                       "algorithmic_bytes_per_layer": attn_bytes,
@@ -824,9 +834,9 @@ def run_prefill(args, wl, torch, csa2, synth) -> dict:
     return result
 
 
-def setup_decode(wl, torch, csa2, synth, layer_sequential=False):
+def setup_decode(wl, torch, csa2, synth, schedule="steps"):
     t0 = time.time()
-    W = DecodeWorkload(wl, torch, csa2, synth, layer_sequential=layer_sequential)
+    W = DecodeWorkload(wl, torch, csa2, synth, schedule=schedule)
     setup_s = time.time() - t0
     print(f"[bench] setup {setup_s:.1f}s: {wl.name}, {len(wl.seq_lens)} seqs, {sum(wl.seq_lens)} entries",
           file=sys.stderr, flush=True)
@@ -893,6 +903,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "sequences": len(wl.seq_lens), "context": max(wl.seq_lens),
                    "layers": wl.n_layers, "layout": "Full+3Reuse, 4x(Reindex+3Reuse)", "latent_dim": wl.dim,
+                   "schedule": "csa2_group_steps: indexers in group order, then attention batched across groups",
                    "heads": wl.heads, "idx_heads": wl.idx_heads, "idx_dim": wl.idx_dim,
                    "pool_blocks": wl.pool_blocks, "top_k": wl.top_k, "window": wl.window,
                    "storage": "FP4 E2M1/E4M3x16 main+indexer, FP8 E4M3 window", "mode": args.mode},
@@ -926,16 +937,19 @@ def main():
         extras[f"{wl.name}/cold"] = cold
         del W
         torch.cuda.empty_cache()
-        # the same step issued layer by layer (a group step for each group's
-        # first layer, one attention call per Reuse layer), as a model would
-        Ws, _ = setup_decode(wl, torch, csa2, synth, layer_sequential=True)
-        kts = kernel_times(torch, csa2, Ws, args.steps)
-        mss, _ = time_steps(torch, Ws, args.steps, args.warmup, "graph")
-        rs = decode_record(wl, Ws, mss, kts, "graph, layer by layer")
-        rs["attention"]["kernels"] = "k_attn_logits + k_attn_pv per layer"
-        extras[f"{wl.name}/layer-sequential"] = rs
-        del Ws
-        torch.cuda.empty_cache()
+        # the same step group by group (csa2_group_step per group), and issued
+        # layer by layer (a group step for each group's first layer, one
+        # attention call per Reuse layer), as a model would
+        for sched, label, kern in (("groups", "group-by-group", "k_attn_logits + k_attn_pv per group"),
+                                   ("layers", "layer-sequential", "k_attn_logits + k_attn_pv per layer")):
+            Ws, _ = setup_decode(wl, torch, csa2, synth, schedule=sched)
+            kts = kernel_times(torch, csa2, Ws, args.steps)
+            mss, _ = time_steps(torch, Ws, args.steps, args.warmup, "graph")
+            rs = decode_record(wl, Ws, mss, kts, f"graph, {label}")
+            rs["attention"]["kernels"] = kern
+            extras[f"{wl.name}/{label}"] = rs
+            del Ws
+            torch.cuda.empty_cache()
         for cfg in (1, 3):
             wx = synth.workload(cfg)
             Wx, _ = setup_decode(wx, torch, csa2, synth)

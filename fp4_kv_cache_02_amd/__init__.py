@@ -25,7 +25,7 @@ EXPORTS = [
     "csa2_attn_workspace_size", "csa2_sparse_swa_attn", "csa2_group_workspace_size", "csa2_group_step",
     "csa2_profile_scan", "csa2_profile_scan_read", "csa2_profile_attn", "csa2_profile_attn_read",
     "csa2_profile_write", "csa2_profile_write_read", "csa2_group_step_static", "csa2_compress_fp4",
-    "csa2_profile_compress", "csa2_profile_compress_read",
+    "csa2_profile_compress", "csa2_profile_compress_read", "csa2_group_steps_workspace_size", "csa2_group_steps",
 ]
 
 
@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
             "csa2_compress_fp4": (i32, [vp, i64, i32, i32, vp, i32, vp, vp, vp, vp, i32, vp, vp, vp]),
             "csa2_profile_compress": (i32, [i32]),
             "csa2_profile_compress_read": (i32, [POINTER(ctypes.c_double), POINTER(c_int64)]),
+            "csa2_group_steps_workspace_size": (i32, [POINTER(GroupDesc), i32, POINTER(c_size_t)]),
+            "csa2_group_steps": (i32, [POINTER(GroupDesc), i32, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -304,6 +306,25 @@ def csa2_group_step(group: Group, workspace, stream=None):
     _check(lib().csa2_group_step(ctypes.byref(group.desc), _ptr(workspace),
                                  int(workspace.numel()) if workspace is not None else 0, _stream(stream)),
            "csa2_group_step")
+
+
+def _desc_array(groups):
+    return (GroupDesc * len(groups))(*[g.desc for g in groups])
+
+
+def csa2_group_steps_workspace_size(groups) -> int:
+    n = c_size_t(0)
+    _check(lib().csa2_group_steps_workspace_size(_desc_array(groups), len(groups), ctypes.byref(n)),
+           "csa2_group_steps_workspace_size")
+    return int(n.value)
+
+
+def csa2_group_steps(groups, workspace, stream=None):
+    """Several group steps in one call: every group's write and index, then
+    the attention of all their layers batched across groups."""
+    _check(lib().csa2_group_steps(_desc_array(groups), len(groups), _ptr(workspace),
+                                  int(workspace.numel()) if workspace is not None else 0, _stream(stream)),
+           "csa2_group_steps")
 
 
 def csa2_group_step_static(group: Group, stream=None):

@@ -238,7 +238,7 @@ int32_t csa2_attn_workspace_size(int32_t m, int32_t heads, int32_t dim, int32_t 
                                  size_t *bytes) {
   if (!bytes) return CSA2_ERR_NULL_ARG;
   if (m < 0 || heads < 1 || dim <= 0 || top_k < 0 || window < 0) return CSA2_ERR_BAD_SHAPE;
-  *bytes = (m == 0) ? 256 : attn_ws_bytes(m, heads, dim, top_k, window, 1);
+  *bytes = (m == 0) ? 256 : attn_ws_bytes(m, heads, dim, top_k, window, 1, 1);
   return CSA2_OK;
 }
 
@@ -259,11 +259,11 @@ int32_t csa2_sparse_swa_attn(const csa2_fp4_cache *kv, const csa2_queries *qs, c
   if (qs->m == 0) return CSA2_OK;
   if (!q || !out) return CSA2_ERR_NULL_ARG;
   if (top_k > 0 && !topk) return CSA2_ERR_NULL_ARG;
-  const size_t need = attn_ws_bytes(qs->m, heads, kv->dim, top_k, swa->window, 1);
+  const size_t need = attn_ws_bytes(qs->m, heads, kv->dim, top_k, swa->window, 1, 1);
   if (need > 256 && (!workspace || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
   if (workspace && !aligned(workspace, 256)) return CSA2_ERR_MISALIGNED;
-  const AttnLayer layer{q, swa->codes, swa->scale, swa->start, swa->count, swa->window, out, lse};
-  return launch_attn_layers(*kv, *qs, q_dtype, heads, topk, top_k, &layer, 1, softmax_scale, workspace,
+  const AttnLayer layer{q, swa->codes, swa->scale, swa->start, swa->count, swa->window, out, lse, topk, 0, 0};
+  return launch_attn_layers(*kv, *qs, q_dtype, heads, top_k, &layer, 1, softmax_scale, workspace,
                             (hipStream_t)stream);
 }
 
@@ -278,7 +278,7 @@ static int group_max_window(const csa2_group_desc *g) {
 }
 static size_t group_index_offset(const csa2_group_desc *g) {
   const size_t a = attn_ws_bytes(g->qs.m > 0 ? g->qs.m : 1, g->heads, g->kv.dim, g->top_k, group_max_window(g),
-                                 g->n_layers);
+                                 g->n_layers, 1);
   return align256(std::max<size_t>(256, a));
 }
 
@@ -291,7 +291,8 @@ int32_t csa2_group_workspace_size(const csa2_group_desc *g, size_t *bytes) {
   return CSA2_OK;
 }
 
-int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_bytes, void *stream) {
+// Every check of a group step except the workspace's, before anything is enqueued.
+static int check_group(const csa2_group_desc *g) {
   if (!g) return CSA2_ERR_NULL_ARG;
   if (g->first_mode != CSA2_MODE_FULL && g->first_mode != CSA2_MODE_REINDEX) return CSA2_ERR_BAD_SHAPE;
   if (g->n_layers < 1 || g->n_layers > 64) return CSA2_ERR_BAD_SHAPE;
@@ -301,9 +302,6 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
   int st;
   size_t need = 0;
   if ((st = csa2_group_workspace_size(g, &need))) return st;
-  if (!workspace || ws_bytes < need) return CSA2_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return CSA2_ERR_MISALIGNED;
-  // validate every call before enqueueing anything
   if ((st = check_index_common(&g->idx, &g->qs, g->q_idx, g->w_idx, g->idx_heads, g->top_k, g->topk))) return st;
   if (g->first_mode == CSA2_MODE_FULL && (st = check_flat_limits(&g->idx, g->pool_blocks))) return st;
   if ((st = check_cache(&g->kv, true))) return st;
@@ -321,9 +319,12 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
     if (g->new_kv_dtype != CSA2_F32 && g->new_kv_dtype != CSA2_BF16) return CSA2_ERR_BAD_DTYPE;
     if (g->idx.dim > g->kv.dim) return CSA2_ERR_UNSUPPORTED;
   }
-  if (g->qs.m == 0) return CSA2_OK;
-  hipStream_t s = (hipStream_t)stream;
-  void *iws = static_cast<char *>(workspace) + group_index_offset(g);
+  return CSA2_OK;
+}
+
+// The group's write path and its first layer's indexer (m > 0).
+static int enqueue_group_index(const csa2_group_desc *g, void *iws, hipStream_t s) {
+  int st = CSA2_OK;
   if (g->first_mode == CSA2_MODE_FULL && g->new_rows > 0) {
     st = launch_quantize_fp4(g->new_kv, g->new_kv_dtype, g->new_rows, g->kv.dim, g->new_dst_row, g->kv.codes,
                              g->kv.scales, g->w_ik, g->idx.dim, g->idx.codes, g->idx.scales, s);
@@ -340,15 +341,132 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
     st = launch_reindex(g->idx, g->qs, g->q_idx, g->w_idx, g->idx_heads, g->pool, g->pool_count, g->pool_blocks,
                         g->top_k, g->topk, g->topk_score, iws, s);
   }
-  if (st) return st;
-  AttnLayer layers[64];
+  return st;
+}
+
+static void group_layers(const csa2_group_desc *g, AttnLayer *out) {
   for (int i = 0; i < g->n_layers; ++i) {
     const csa2_swa &w = g->swa[i];
-    layers[i] = AttnLayer{g->q[i], w.codes, w.scale, w.start, w.count, w.window, g->out[i],
-                          g->lse ? g->lse[i] : nullptr};
+    out[i] = AttnLayer{g->q[i], w.codes, w.scale, w.start, w.count, w.window, g->out[i],
+                       g->lse ? g->lse[i] : nullptr, g->topk, 0, 0};
   }
-  return launch_attn_layers(g->kv, g->qs, g->q_dtype, g->heads, g->topk, g->top_k, layers, g->n_layers,
-                            g->softmax_scale, workspace, s);
+}
+
+int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_bytes, void *stream) {
+  int st = check_group(g);
+  if (st) return st;
+  size_t need = 0;
+  if ((st = csa2_group_workspace_size(g, &need))) return st;
+  if (!workspace || ws_bytes < need) return CSA2_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_ERR_MISALIGNED;
+  if (g->qs.m == 0) return CSA2_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = enqueue_group_index(g, static_cast<char *>(workspace) + group_index_offset(g), s))) return st;
+  AttnLayer layers[64];
+  group_layers(g, layers);
+  return launch_attn_layers(g->kv, g->qs, g->q_dtype, g->heads, g->top_k, layers, g->n_layers, g->softmax_scale,
+                            workspace, s);
+}
+
+// ---------------------------------------------------------------------------
+// csa2_group_steps: several groups, their attention batched across groups
+// ---------------------------------------------------------------------------
+// Consecutive groups whose layers can share one attention launch: the same
+// main cache, queries, query format, heads, Top-K length and softmax scale.
+static bool same_attention(const csa2_group_desc *a, const csa2_group_desc *b) {
+  const csa2_fp4_cache &x = a->kv, &y = b->kv;
+  return x.codes == y.codes && x.scales == y.scales && x.seq_start == y.seq_start && x.seq_len == y.seq_len &&
+         x.n_seq == y.n_seq && x.dim == y.dim && x.max_len == y.max_len && x.ratio == y.ratio &&
+         a->qs.seq == b->qs.seq && a->qs.pos == b->qs.pos && a->qs.m == b->qs.m && a->q_dtype == b->q_dtype &&
+         a->heads == b->heads && a->top_k == b->top_k && a->softmax_scale == b->softmax_scale;
+}
+
+constexpr int kMaxGroups = 32;
+
+// Workspace: the attention region (any batch of the call), then the region
+// the groups' indexers use one after another.
+static size_t steps_index_offset(const csa2_group_desc *groups, int n) {
+  int wmax = 0, layers = 0;
+  for (int i = 0; i < n; ++i) {
+    wmax = std::max(wmax, group_max_window(&groups[i]));
+    layers += groups[i].n_layers;
+  }
+  size_t a = 256;
+  for (int i = 0; i < n; ++i) {
+    const csa2_group_desc *g = &groups[i];
+    a = std::max(a, attn_ws_bytes(g->qs.m > 0 ? g->qs.m : 1, g->heads, g->kv.dim, g->top_k, wmax, layers, n));
+  }
+  return align256(a);
+}
+
+int32_t csa2_group_steps_workspace_size(const csa2_group_desc *groups, int32_t n_groups, size_t *bytes) {
+  if (!groups || !bytes) return CSA2_ERR_NULL_ARG;
+  if (n_groups < 1 || n_groups > kMaxGroups) return CSA2_ERR_BAD_SHAPE;
+  size_t idx = 0;
+  for (int i = 0; i < n_groups; ++i) {
+    size_t one = 0;
+    const int st = csa2_group_workspace_size(&groups[i], &one);
+    if (st) return st;
+    if (groups[i].n_layers > 64) return CSA2_ERR_BAD_SHAPE;
+    idx = std::max(idx, align256(index_bytes(&groups[i].idx, groups[i].qs.m, groups[i].pool_blocks,
+                                             groups[i].top_k)));
+  }
+  *bytes = steps_index_offset(groups, n_groups) + idx;
+  return CSA2_OK;
+}
+
+int32_t csa2_group_steps(const csa2_group_desc *groups, int32_t n_groups, void *workspace, size_t ws_bytes,
+                         void *stream) {
+  if (!groups) return CSA2_ERR_NULL_ARG;
+  if (n_groups < 1 || n_groups > kMaxGroups) return CSA2_ERR_BAD_SHAPE;
+  int st;
+  for (int i = 0; i < n_groups; ++i)
+    if ((st = check_group(&groups[i]))) return st;
+  size_t need = 0;
+  if ((st = csa2_group_steps_workspace_size(groups, n_groups, &need))) return st;
+  if (!workspace || ws_bytes < need) return CSA2_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_ERR_MISALIGNED;
+  hipStream_t s = (hipStream_t)stream;
+  void *iws = static_cast<char *>(workspace) + steps_index_offset(groups, n_groups);
+  std::vector<AttnLayer> layers;
+  // the attention of groups [a, b), one launch sequence per run of groups
+  // that can share it
+  auto flush = [&](int a, int b) -> int {
+    for (int i = a; i < b;) {
+      int j = i + 1;
+      while (j < b && same_attention(&groups[i], &groups[j])) ++j;
+      const csa2_group_desc *g = &groups[i];
+      if (g->qs.m > 0) {
+        layers.clear();
+        for (int k = i; k < j; ++k) {
+          const size_t at = layers.size();
+          layers.resize(at + groups[k].n_layers);
+          group_layers(&groups[k], layers.data() + at);
+        }
+        const int r = launch_attn_layers(g->kv, g->qs, g->q_dtype, g->heads, g->top_k, layers.data(),
+                                         (int)layers.size(), g->softmax_scale, workspace, s);
+        if (r) return r;
+      }
+      i = j;
+    }
+    return CSA2_OK;
+  };
+  int pending = 0;   // first group whose attention has not been enqueued
+  for (int i = 0; i < n_groups; ++i) {
+    const csa2_group_desc *g = &groups[i];
+    // a group that writes into a main cache which pending attention still
+    // reads runs after that attention, as it would group by group
+    if (g->first_mode == CSA2_MODE_FULL && g->new_rows > 0) {
+      for (int k = pending; k < i; ++k)
+        if (groups[k].kv.codes == g->kv.codes || groups[k].kv.scales == g->kv.scales) {
+          if ((st = flush(pending, i))) return st;
+          pending = i;
+          break;
+        }
+    }
+    if (g->qs.m > 0 && (st = enqueue_group_index(g, iws, s))) return st;
+  }
+  return flush(pending, n_groups);
 }
 
 // ---------------------------------------------------------------------------

@@ -379,7 +379,6 @@ struct QRaw {
 template <int D, bool QF32>
 __global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int nwc, const int32_t *__restrict__ q_seq,
                                                      const int32_t *__restrict__ q_pos,
-                                                     const int32_t *__restrict__ topk,
                                                      const int64_t *__restrict__ seq_start,
                                                      const int32_t *__restrict__ seq_len,
                                                      const uint8_t *__restrict__ kv_codes,
@@ -402,6 +401,7 @@ __global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int 
   const int row = l & 15, quad = l >> 4;
   const bool main_chunk = c < nmc;
   const AttnLayer &ly = lb.l[li];
+  const int32_t *topk = ly.topk;
   if (!main_chunk && kChunk * (c - nmc) >= ly.window) return;   // past this layer's window
   const int key = tid >> 3, d0 = (tid & 7) * DP;
   // a Top-K chunk's index load goes out first, beside the sequence lookup
@@ -431,9 +431,11 @@ __global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int 
     Fp4Piece<D, DP> pc;
     pc.load(make_rsrc(kv_codes + qr.row0 * (D / 2), (uint32_t)(qr.vis * (D / 2))),
             make_rsrc(kv_scales + qr.row0 * (D / 16), (uint32_t)(qr.vis * (D / 16))), ok, (uint32_t)j, d0);
-    if (li == 0)   // the gathered copy of the chunk's rows (zeros for empty slots)
-      pc.store(make_rsrc(g_codes + (int64_t)m * Kp * (D / 2), (uint32_t)(Kp * (D / 2))),
-               make_rsrc(g_scales + (int64_t)m * Kp * (D / 16), (uint32_t)(Kp * (D / 16))), (uint32_t)slot, d0);
+    if (ly.gather) {   // the gathered copy of the chunk's rows (zeros for empty slots)
+      const int64_t gr = ((int64_t)ly.list * M + m) * Kp;
+      pc.store(make_rsrc(g_codes + gr * (D / 2), (uint32_t)(Kp * (D / 2))),
+               make_rsrc(g_scales + gr * (D / 16), (uint32_t)(Kp * (D / 16))), (uint32_t)slot, d0);
+    }
 #pragma unroll
     for (int u = 0; u < DP / 8; ++u) put(u, QF32 ? __builtin_bit_cast(u32x4_t, pc.get(u)) : pc.get_bf16(u));
   } else {
@@ -577,8 +579,9 @@ __global__ __launch_bounds__(256) void k_attn_pv(int M, int H, int nmc, int nwc,
   const int nslots = kChunk * nch, Kp = kChunk * nmc;
   const int hn = min(kPvHeads, H - hb0);
   const int Wp = kChunk * nwc;                               // gathered window rows of the batch
-  const rsrc_t r_gc = make_rsrc(g_codes + (int64_t)m * Kp * (D / 2), (uint32_t)(Kp * (D / 2)));
-  const rsrc_t r_gs = make_rsrc(g_scales + (int64_t)m * Kp * (D / 16), (uint32_t)(Kp * (D / 16)));
+  const int64_t gr = ((int64_t)ly.list * M + m) * Kp;   // the layer's gathered Top-K rows
+  const rsrc_t r_gc = make_rsrc(g_codes + gr * (D / 2), (uint32_t)(Kp * (D / 2)));
+  const rsrc_t r_gs = make_rsrc(g_scales + gr * (D / 16), (uint32_t)(Kp * (D / 16)));
   const rsrc_t r_win = make_rsrc(g_win + ((int64_t)li * M + m) * Wp * D, (uint32_t)(Wp * D));
   const int64_t rows0 = ((int64_t)li * M + m) * H + hb0;    // first (layer, query, head) row of the group
   const rsrc_t r_p = make_rsrc(P + rows0 * nkp, (uint32_t)(hn * nkp * 2));
@@ -895,17 +898,18 @@ static bool use_decode_kernel(int m, int heads, int dim, int64_t max_len) {
   return (int64_t)m * ((heads + kHB - 1) / kHB) < 256;
 }
 
-// Decode-schedule workspace for a batch of `nl` layers: p values (f16)
-// [layer][query][head][slot], chunk statistics (m_c, sum p) [layer][query]
-// [head][chunk], window-chunk lifts [layer][query][chunk], the gathered
-// Top-K rows [query][slot] (FP4 codes and scale bytes) and the gathered
-// window rows [layer][query][row] (FP8 codes).  Slots: the Top-K list padded
-// to whole chunks, then the largest window of the batch.
+// Decode-schedule workspace for a batch of `nl` layers over `nlists` Top-K
+// lists: p values (f16) [layer][query][head][slot], chunk statistics (m_c,
+// sum p) [layer][query][head][chunk], window-chunk lifts [layer][query]
+// [chunk], the gathered Top-K rows [list][query][slot] (FP4 codes and scale
+// bytes) and the gathered window rows [layer][query][row] (FP8 codes).
+// Slots: the Top-K list padded to whole chunks, then the largest window of
+// the batch.
 struct DecodeWs {
   int nmc, nwc;
   size_t p, stats, lift, gcodes, gscales, gwin, total;
 };
-static DecodeWs decode_ws_layout(int m, int heads, int dim, int top_k, int max_window, int nl) {
+static DecodeWs decode_ws_layout(int m, int heads, int dim, int top_k, int max_window, int nl, int nlists) {
   DecodeWs w{};
   w.nmc = (top_k + kChunk - 1) / kChunk;
   w.nwc = (max_window + kChunk - 1) / kChunk;
@@ -914,20 +918,21 @@ static DecodeWs decode_ws_layout(int m, int heads, int dim, int top_k, int max_w
   w.p = off;       off = align256(off + sizeof(_Float16) * rows * nch * kChunk);
   w.stats = off;   off = align256(off + sizeof(float2) * rows * nch);
   w.lift = off;    off = align256(off + sizeof(int32_t) * (size_t)nl * m * nch);
-  w.gcodes = off;  off = align256(off + (size_t)m * kp * (dim / 2));
-  w.gscales = off; off = align256(off + (size_t)m * kp * (dim / 16));
+  w.gcodes = off;  off = align256(off + (size_t)nlists * m * kp * (dim / 2));
+  w.gscales = off; off = align256(off + (size_t)nlists * m * kp * (dim / 16));
   w.gwin = off;    off = align256(off + (size_t)nl * m * (kChunk * w.nwc) * dim);
   w.total = off;
   return w;
 }
 
-size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int max_window, int n_layers) {
+size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int max_window, int n_layers, int n_lists) {
   if (m < 1 || n_layers < 1 || !use_decode_kernel(m, heads, dim, 0)) return 256;
-  return decode_ws_layout(m, heads, dim, top_k, max_window, std::min(n_layers, kAttnBatch)).total;
+  const int nl = std::min(n_layers, kAttnBatch);
+  return decode_ws_layout(m, heads, dim, top_k, max_window, nl, std::max(1, std::min(n_lists, nl))).total;
 }
 
 template <int D, bool QF32>
-static int attn_layers_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, int heads, const int32_t *topk, int K,
+static int attn_layers_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, int heads, int K,
                             const AttnLayer *layers, int n, float scale, void *ws, hipStream_t stream) {
   const float tau2 = scale * 1.4426950408889634f;  // log2-domain softmax: p = 2^(z - max)
   if (use_decode_kernel(qs.m, heads, D, kv.max_len)) {
@@ -935,12 +940,17 @@ static int attn_layers_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, in
     for (int b0 = 0; b0 < n; b0 += kAttnBatch) {
       const int nl = std::min(kAttnBatch, n - b0);
       AttnBatch lb{};
-      int wmax = 0;
+      int wmax = 0, nlists = 0;
       for (int i = 0; i < nl; ++i) {
         lb.l[i] = layers[b0 + i];
         wmax = std::max(wmax, layers[b0 + i].window);
+        // one gathered copy per distinct list, written by its first layer
+        int li = 0;
+        while (li < i && lb.l[li].topk != lb.l[i].topk) ++li;
+        lb.l[i].list = (li < i) ? lb.l[li].list : nlists++;
+        lb.l[i].gather = li == i;
       }
-      const DecodeWs L = decode_ws_layout(qs.m, heads, D, K, wmax, nl);
+      const DecodeWs L = decode_ws_layout(qs.m, heads, D, K, wmax, nl, nlists);
       char *base = static_cast<char *>(ws);
       _Float16 *P = reinterpret_cast<_Float16 *>(base + L.p);
       float2 *st = reinterpret_cast<float2 *>(base + L.stats);
@@ -950,7 +960,7 @@ static int attn_layers_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, in
       uint8_t *gw = reinterpret_cast<uint8_t *>(base + L.gwin);
       const dim3 g1(xcd_grid(L.nmc + L.nwc, qs.m), (unsigned)nl);
       CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_logits<D, QF32>), g1, dim3(256), stream, qs.m, K, L.nmc, L.nwc, qs.seq,
-                        qs.pos, topk, kv.seq_start, kv.seq_len, kv.codes, kv.scales, kv.ratio, heads, tau2, P, st, lf,
+                        qs.pos, kv.seq_start, kv.seq_len, kv.codes, kv.scales, kv.ratio, heads, tau2, P, st, lf,
                         gc, gs, gw, lb);
       const int nhg = (heads + kPvHeads - 1) / kPvHeads;
       const dim3 g2(xcd_grid((D / DS) * nhg, qs.m), (unsigned)nl);
@@ -963,23 +973,22 @@ static int attn_layers_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, in
     const AttnLayer &ly = layers[i];
     const csa2_swa swa{ly.swa_codes, ly.swa_scale, ly.swa_start, ly.swa_count, D, ly.window};
     if (attn_prefill_supported(kv, QF32 ? CSA2_F32 : CSA2_BF16, K)) {
-      const int st = launch_attn_prefill(kv, qs, ly.q, heads, topk, K, swa, scale, ly.out, ly.lse, stream);
+      const int st = launch_attn_prefill(kv, qs, ly.q, heads, ly.topk, K, swa, scale, ly.out, ly.lse, stream);
       if (st != CSA2_OK) return st;
     } else {
       const dim3 grid(qs.m, (heads + kHB - 1) / kHB);
       CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn<D, QF32>), grid, dim3(256), stream, ly.q, heads, kv.codes, kv.scales,
-                        kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, topk, K, ly.swa_codes, ly.swa_scale,
+                        kv.seq_start, kv.seq_len, kv.ratio, qs.seq, qs.pos, ly.topk, K, ly.swa_codes, ly.swa_scale,
                         ly.swa_start, ly.swa_count, ly.window, tau2, ly.out, ly.lse);
     }
   }
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 
-int launch_attn_layers(const csa2_fp4_cache &kv, const csa2_queries &qs, int q_dtype, int heads,
-                       const int32_t *topk, int top_k, const AttnLayer *layers, int n_layers, float scale, void *ws,
-                       hipStream_t stream) {
+int launch_attn_layers(const csa2_fp4_cache &kv, const csa2_queries &qs, int q_dtype, int heads, int top_k,
+                       const AttnLayer *layers, int n_layers, float scale, void *ws, hipStream_t stream) {
   const bool f32 = q_dtype == CSA2_F32;
-#define CSA2_ATTN(D, F) attn_layers_impl<D, F>(kv, qs, heads, topk, top_k, layers, n_layers, scale, ws, stream)
+#define CSA2_ATTN(D, F) attn_layers_impl<D, F>(kv, qs, heads, top_k, layers, n_layers, scale, ws, stream)
   switch (kv.dim) {
     case 64: return f32 ? CSA2_ATTN(64, true) : CSA2_ATTN(64, false);
     case 128: return f32 ? CSA2_ATTN(128, true) : CSA2_ATTN(128, false);

@@ -513,49 +513,53 @@ __global__ __launch_bounds__(256) void k_rescore(const uint8_t *__restrict__ cod
   }
 }
 
-// Top-K by radix select over the scores of one query's slots, run by a
-// workgroup of NT threads: thread t owns slots [t*PER, (t+1)*PER), sv[] their
-// scores (-inf: no candidate).  The ranking is (score desc, slot asc); the
+// Top-K of the scores of one query's slots, run by a workgroup of NT
+// threads: thread t owns slots [t*PER, (t+1)*PER), sv[] their scores (-inf:
+// no candidate).  The ranking is (score desc, slot asc): on the composite
+// G = key << 32 | ~slot (key the order-preserving image of the score), the
+// selection is every G >= cut with cut the composite of the K-th entry.  The
 // selected slots are handed to emit(rank, i, score) in ascending slot order
-// (i the thread-local slot index, rank the output position).  A first pass
-// counts the top 12 bits of every key into a 4096-bin histogram and finds
-// the bin T holding the K-th key; only the keys of bin T take further radix
-// passes, on the composite (key, ~slot) below those 12 bits, until the cut's
-// bin holds exactly the entries still needed.  Returns the number selected,
-// min(K, #candidates).
+// (i the thread-local slot index, rank the output position).  Returns the
+// number selected, min(K, #candidates).
+//
+// Finding the cut: a 4096-bin histogram of d = kmax - key over a window
+// anchored at the largest key (bins of 2^13 key units, 1/1024 of an octave;
+// the whole key range when the window holds fewer than K keys) gives the bin
+// T holding the K-th entry.  Fine bins keep both the LDS atomics (the keys of
+// a query cluster within a few octaves) and bin T small: its entries are
+// ranked against each other by one wave when at most 64, else narrowed by
+// radix passes over their composites.
 constexpr int kSelectCand = 2048;   // threshold-bin entries refined by one wave
+constexpr int kSelectShift = 13;    // log2 key units per bin of the first window
+constexpr int kSelectShiftAll = 32 - kHistBits;
 
 template <int NT>
 struct SelectLds {
   uint32_t hist[kHistBins];
   uint32_t h[256];
-  int scan[NT / 64 + 1];
+  uint32_t wmax[NT / 64];
+  int wcnt[NT / 64];
+  int wsum[NT / 64];
   int T, above, nT, digit, rem, cnt;
   // the selection by output rank, written out in one coalesced pass (a
   // wave's scattered masked stores would queue one instruction per slot)
   int32_t stage[4096];
   float stage_score[2048];
-  // the composite keys of the threshold bin, refined by one wave
+  // the composites of the threshold bin
   uint64_t cand[kSelectCand];
   int ncand;
-  uint64_t prefix, mask;
+  uint64_t cut;
 };
 
-// Count `d` of every key into hist: each thread first folds its keys into at
-// most two (digit, count) pairs - the keys of a query cluster in a few
-// digits, and the lanes of a wave would otherwise hit one LDS counter together.
-struct DigitFold {
-  uint32_t d0 = 0u, c0 = 0u, d1 = 0u, c1 = 0u;
-  CSA2_DEV void add(uint32_t *hist, uint32_t d) {
-    if (c0 == 0u || d == d0) { d0 = d; ++c0; }
-    else if (c1 == 0u || d == d1) { d1 = d; ++c1; }
-    else atomicAdd(&hist[d], 1u);
-  }
-  CSA2_DEV void flush(uint32_t *hist) {
-    if (c0) atomicAdd(&hist[d0], c0);
-    if (c1) atomicAdd(&hist[d1], c1);
-  }
-};
+CSA2_DEV uint32_t wave_incl_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return v;
+}
 
 // Order LDS accesses among the lanes of one wave (no other wave takes part).
 CSA2_DEV void wave_lds_sync() {
@@ -564,28 +568,26 @@ CSA2_DEV void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Run by wave 0 alone: radix passes of 8 bits over the n composites cand[]
-// (all inside the threshold bin), narrowing (prefix, mask) to the cut of the
-// rem largest; stops as soon as the cut's digit bin holds exactly the
-// entries still needed.
+// Run by wave 0 alone: radix passes of 8 bits from the top over the n
+// composites cand[], narrowing (prefix, mask) to the cut of the rem largest;
+// stops as soon as the cut's digit bin holds exactly the entries still
+// needed.  Afterwards the rem largest are exactly those >= prefix.
 CSA2_DEV void wave_refine(const uint64_t *cand, int n, int rem, uint32_t *h, int *s_digit, int *s_rem,
                           int *s_cnt, uint64_t &prefix, uint64_t &mask) {
   const int l = lane_id();
-  for (int hi = 64 - kHistBits; hi > 0; hi -= 8) {
-    const int width = hi < 8 ? hi : 8;
-    const int shift = hi - width;
-    const uint64_t dmask = (1ull << width) - 1ull;
+  for (int hi = 64; hi > 0; hi -= 8) {
+    const int shift = hi - 8;
     for (int i = l; i < 256; i += 64) h[i] = 0u;
     wave_lds_sync();
     for (int i = l; i < n; i += 64) {
       const uint64_t c = cand[i];
-      if ((c & mask) == prefix) atomicAdd(&h[(uint32_t)((c >> shift) & dmask)], 1u);
+      if ((c & mask) == prefix) atomicAdd(&h[(uint32_t)((c >> shift) & 0xFFull)], 1u);
     }
     wave_lds_sync();
     find_digit(h, rem, s_digit, s_rem, s_cnt);
     wave_lds_sync();
     prefix |= (uint64_t)*s_digit << shift;
-    mask |= dmask << shift;
+    mask |= 0xFFull << shift;
     rem = *s_rem;
     if (*s_cnt == rem) break;
   }
@@ -593,118 +595,161 @@ CSA2_DEV void wave_refine(const uint64_t *cand, int n, int rem, uint32_t *h, int
 
 template <int NT, int PER, typename Emit>
 CSA2_DEV int select_topk(const float (&sv)[PER], int K, SelectLds<NT> &sm, Emit emit) {
+  constexpr int NW = NT / 64;
   constexpr int BPT = kHistBins / NT;   // histogram bins per thread in the threshold scan
-  constexpr int KB = 32 - kHistBits;    // key bits below the histogram's
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t key[PER];
+  uint32_t kmx = 0u;
+  int nv = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) key[i] = (sv[i] > -INFINITY) ? f2key(sv[i]) : 0u;
+  for (int i = 0; i < PER; ++i) {
+    key[i] = (sv[i] > -INFINITY) ? f2key(sv[i]) : 0u;
+    kmx = max(kmx, key[i]);
+    nv += key[i] != 0u;
+  }
+  auto G = [&](int i) { return ((uint64_t)key[i] << 32) | (uint64_t)(~(uint32_t)(tid * PER + i)); };
   for (int i = tid; i < kHistBins / 4; i += NT) reinterpret_cast<uint4 *>(sm.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (tid == 0) { sm.T = -1; sm.above = 0; sm.nT = 0; sm.ncand = 0; }
+  kmx = wave_incl_max(kmx);
+  nv = wave_incl_scan(nv);
+  if (lane == 63) { sm.wmax[wv] = kmx; sm.wcnt[wv] = nv; }
+  if (tid == 0) sm.ncand = 0;
   __syncthreads();
-  {
-    DigitFold f;
+  kmx = 0u;
+  int tot_valid = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (key[i] != 0u) f.add(sm.hist, key[i] >> KB);
-    f.flush(sm.hist);
-  }
-  __syncthreads();
-  // ---- threshold bin: thread t owns bins [4096 - BPT(t+1), 4096 - BPT t) ----
-  const int bin0 = kHistBins - BPT * (tid + 1);
-  uint32_t hv[BPT];
-  int c = 0;
-#pragma unroll
-  for (int k = 0; k < BPT; ++k) { hv[k] = sm.hist[bin0 + k]; c += (int)hv[k]; }
-  int tot;
-  const int before = block_exclusive_scan<NT>(c, sm.scan, &tot);   // keys in higher bins
-  const int Kp = min(K, tot);
-  if (Kp > 0 && before < Kp && before + c >= Kp) {
-    int cum = before;
-#pragma unroll
-    for (int k = BPT - 1; k >= 0; --k) {
-      if (cum + (int)hv[k] >= Kp) { sm.T = bin0 + k; sm.above = cum; sm.nT = (int)hv[k]; break; }
-      cum += (int)hv[k];
-    }
-  }
-  __syncthreads();
-  const int T = sm.T;
-  int rem = Kp - sm.above;
-  const bool all_t = rem >= sm.nT;      // every key of bin T is taken
-  // ---- the rem best keys of bin T on c = key << 32 | ~slot ----
-  auto comp = [&](int i) {
-    return ((uint64_t)key[i] << 32) | (uint64_t)(~(uint32_t)(tid * PER + i));
-  };
-  uint64_t prefix = (uint64_t)(uint32_t)max(T, 0) << (64 - kHistBits);
-  uint64_t mask = ((1ull << kHistBits) - 1ull) << (64 - kHistBits);
-  // the threshold bin's entries into LDS (one atomic per wave), refined by
-  // wave 0 alone when they fit; otherwise block-wide passes below
-  bool small_bin = false;
-  if (Kp > 0 && !all_t) {
-    int nc = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) nc += (key[i] != 0u && (int)(key[i] >> KB) == T);
-    const int incl = wave_incl_scan(nc);
-    int base = 0;
-    if ((tid & 63) == 63) base = atomicAdd(&sm.ncand, incl);
-    base = __shfl(base, 63, 64) + incl - nc;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (key[i] != 0u && (int)(key[i] >> KB) == T) {
-        if (base < kSelectCand) sm.cand[base] = comp(i);
-        ++base;
-      }
-    __syncthreads();
-    small_bin = sm.ncand <= kSelectCand;
-    if (small_bin) {
-      if (tid < 64) {
-        uint64_t pf = prefix, mk = mask;
-        wave_refine(sm.cand, sm.ncand, rem, sm.h, &sm.digit, &sm.rem, &sm.cnt, pf, mk);
-        if (tid == 0) { sm.prefix = pf; sm.mask = mk; }
-      }
-      __syncthreads();
-      prefix = sm.prefix;
-      mask = sm.mask;
-    }
-  }
-  if (Kp > 0 && !all_t && !small_bin) {
-    for (int hi = 64 - kHistBits; hi > 0; hi -= 8) {
-      const int width = hi < 8 ? hi : 8;
-      const int shift = hi - width;
-      const uint64_t dmask = (1ull << width) - 1ull;
-      for (int i = tid; i < 256; i += NT) sm.h[i] = 0u;
-      __syncthreads();
-      DigitFold f;
+  for (int w = 0; w < NW; ++w) { kmx = max(kmx, sm.wmax[w]); tot_valid += sm.wcnt[w]; }
+  const int Kp = min(K, tot_valid);
+  uint64_t cut = ~0ull;
+  if (Kp > 0) {
+    // ---- threshold bin T over the window, widened once if it holds < Kp keys ----
+    int SH = kSelectShift;
+    int T = 0, above = 0, nT = 0;
+    for (;;) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        const uint64_t cc = comp(i);
-        if (key[i] != 0u && (cc & mask) == prefix) f.add(sm.h, (uint32_t)((cc >> shift) & dmask));
+        const uint32_t bin = (kmx - key[i]) >> SH;
+        if (key[i] != 0u && bin < (uint32_t)kHistBins) atomicAdd(&sm.hist[bin], 1u);
       }
-      f.flush(sm.h);
       __syncthreads();
-      find_digit(sm.h, rem, &sm.digit, &sm.rem, &sm.cnt);
+      uint32_t hv[BPT];
+      int c = 0;
+#pragma unroll
+      for (int k = 0; k < BPT; k += 4) {
+        const uint4 q = reinterpret_cast<const uint4 *>(sm.hist)[(tid * BPT + k) / 4];
+        hv[k] = q.x; hv[k + 1] = q.y; hv[k + 2] = q.z; hv[k + 3] = q.w;
+        c += (int)(q.x + q.y + q.z + q.w);
+      }
+      const int incl = wave_incl_scan(c);
+      if (lane == 63) sm.wsum[wv] = incl;
       __syncthreads();
-      prefix |= (uint64_t)sm.digit << shift;
-      mask |= dmask << shift;
-      rem = sm.rem;
-      if (sm.cnt == rem) break;   // every entry left in the cut's bin is taken
+      int before = incl - c, tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int x = sm.wsum[w];
+        before += (w < wv) ? x : 0;
+        tot += x;
+      }
+      if (tot >= Kp) {
+        if (before < Kp && before + c >= Kp) {
+          int cum = before;
+#pragma unroll
+          for (int k = 0; k < BPT; ++k) {
+            if (cum + (int)hv[k] >= Kp) { sm.T = tid * BPT + k; sm.above = cum; sm.nT = (int)hv[k]; break; }
+            cum += (int)hv[k];
+          }
+        }
+        __syncthreads();
+        T = sm.T; above = sm.above; nT = sm.nT;
+        break;
+      }
+      // fewer than Kp keys in the window: one pass over the whole key range
+      for (int i = tid; i < kHistBins / 4; i += NT) reinterpret_cast<uint4 *>(sm.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+      SH = kSelectShiftAll;
+      __syncthreads();
+    }
+    const int rem = Kp - above;
+    // keys of bin T: d in [T << SH, (T + 1) << SH), i.e. key in [lo_key, hi_key]
+    const uint64_t span_lo = (uint64_t)(T + 1) << SH;
+    const uint32_t lo_key = (span_lo > (uint64_t)kmx) ? 1u : kmx - (uint32_t)span_lo + 1u;
+    if (rem == nT) {
+      cut = (uint64_t)lo_key << 32;             // the whole bin is taken
+    } else {
+      // ---- bin T's composites into LDS (one atomic per wave) ----
+      const uint32_t hi_key = kmx - (uint32_t)((uint64_t)T << SH);
+      int nc = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) nc += (key[i] >= lo_key && key[i] <= hi_key);
+      const int incl = wave_incl_scan(nc);
+      int base = 0;
+      if (lane == 63) base = atomicAdd(&sm.ncand, incl);
+      base = __builtin_amdgcn_readlane(base, 63) + incl - nc;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (key[i] >= lo_key && key[i] <= hi_key) {
+          if (base < kSelectCand) sm.cand[base] = G(i);
+          ++base;
+        }
+      __syncthreads();
+      const int n = sm.ncand;
+      if (n <= 64) {
+        // rank every candidate against the others; the rem-th largest is the cut
+        if (wv == 0) {
+          const uint64_t c = (lane < n) ? sm.cand[lane] : 0ull;
+          const uint32_t clo = (uint32_t)c, chi = (uint32_t)(c >> 32);
+          int r = 0;
+          for (int j = 0; j < n; ++j) {
+            const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)chi, j) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)clo, j);
+            r += o > c;
+          }
+          if (lane < n && r == rem - 1) sm.cut = c;
+        }
+      } else if (n <= kSelectCand) {
+        if (wv == 0) {
+          uint64_t pf = 0ull, mk = 0ull;
+          wave_refine(sm.cand, n, rem, sm.h, &sm.digit, &sm.rem, &sm.cnt, pf, mk);
+          if (tid == 0) sm.cut = pf;
+        }
+      } else {
+        // block-wide radix passes over bin T's composites held in registers
+        uint64_t prefix = 0ull, mask = 0ull;
+        int r2 = rem;
+        for (int hi = 64; hi > 0; hi -= 8) {
+          const int shift = hi - 8;
+          for (int i = tid; i < 256; i += NT) sm.h[i] = 0u;
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < PER; ++i)
+            if (key[i] >= lo_key && key[i] <= hi_key && (G(i) & mask) == prefix)
+              atomicAdd(&sm.h[(uint32_t)((G(i) >> shift) & 0xFFull)], 1u);
+          __syncthreads();
+          find_digit(sm.h, r2, &sm.digit, &sm.rem, &sm.cnt);
+          __syncthreads();
+          prefix |= (uint64_t)sm.digit << shift;
+          mask |= 0xFFull << shift;
+          r2 = sm.rem;
+          if (sm.cnt == r2) break;
+        }
+        if (tid == 0) sm.cut = prefix;
+      }
+      __syncthreads();
+      cut = sm.cut;
     }
   }
-  // ---- selection in ascending slot order ----
-  bool sel[PER];
+  // ---- selection (G >= cut) in ascending slot order ----
   int nsel = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int bin = (int)(key[i] >> KB);
-    sel[i] = Kp > 0 && key[i] != 0u &&
-             (bin > T || (bin == T && (all_t || (comp(i) & mask) >= prefix)));
-    nsel += sel[i];
-  }
-  int tmp;
-  int rank = block_exclusive_scan<NT>(nsel, sm.scan, &tmp);
+  for (int i = 0; i < PER; ++i) nsel += G(i) >= cut;
+  const int incl = wave_incl_scan(nsel);
+  if (lane == 63) sm.wsum[wv] = incl;
+  __syncthreads();
+  int rank = incl - nsel;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) rank += (w < wv) ? sm.wsum[w] : 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    if (sel[i]) {
+    if (G(i) >= cut) {
       emit(rank, i, sv[i]);
       ++rank;
     }

@@ -75,15 +75,21 @@ struct AttnLayer {
   int32_t window;
   float *out;
   float *lse;
+  const int32_t *topk;   // the layer's Top-K list [m][top_k]
+  // set by launch_attn_layers: which gathered copy of a Top-K list the layer
+  // reads in its batch, and whether it writes that copy
+  int32_t list;
+  int32_t gather;
 };
-constexpr int kAttnBatch = 8;   // layers per launch of the decode schedule
+constexpr int kAttnBatch = 24;  // layers per launch of the decode schedule
 // Workspace of launch_attn_layers over n_layers layers whose largest window
-// is max_window (no initial contents needed).
-size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int max_window, int n_layers);
-// Attention of n_layers layers that share the main cache and the Top-K list.
-int launch_attn_layers(const csa2_fp4_cache &kv, const csa2_queries &qs, int q_dtype, int heads,
-                       const int32_t *topk, int top_k, const AttnLayer *layers, int n_layers, float scale, void *ws,
-                       hipStream_t stream);
+// is max_window and that use at most n_lists distinct Top-K lists (no
+// initial contents needed).
+size_t attn_ws_bytes(int m, int heads, int dim, int top_k, int max_window, int n_layers, int n_lists);
+// Attention of n_layers layers that share the main cache and the queries;
+// each layer has its own Top-K list pointer (layers of one group share it).
+int launch_attn_layers(const csa2_fp4_cache &kv, const csa2_queries &qs, int q_dtype, int heads, int top_k,
+                       const AttnLayer *layers, int n_layers, float scale, void *ws, hipStream_t stream);
 
 // Prefill schedule for the 512-channel latent with bf16 queries
 // (csa2_attn_prefill.hip); needs top_k % 16 == 0 and no workspace.

@@ -344,10 +344,34 @@ typedef struct csa2_group_desc {
 /* Workspace of csa2_group_step: csa2_group_workspace_size bytes, 256-byte
  * aligned, no initial contents needed; not shared by calls that run at the
  * same time.  The group's layers run their attention together (batches of
- * up to 8 layers share one decoded copy of each Top-K key chunk), which
+ * up to 24 layers share one decoded copy of each Top-K key chunk), which
  * gives the same results as csa2_sparse_swa_attn layer by layer. */
 int32_t csa2_group_workspace_size(const csa2_group_desc *g, size_t *bytes);
 int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------
+ * csa2_group_steps - n_groups group steps in one call (P1 CSA2 section /
+ * P4 section 二: a stack of layer groups, e.g. the decoder's 5 groups of 4
+ * layers), with the same results as csa2_group_step on each group in order.
+ *
+ * Every group's write path and first-layer indexer are enqueued in group
+ * order; the attention of all their layers follows in batches of up to 24
+ * layers across groups (one logits and one P V launch per batch; a layer
+ * reads its own group's Top-K list).  Consecutive groups share a batch when
+ * they have the same main cache, queries, query format, heads, top_k and
+ * softmax scale.  The attention of earlier groups is enqueued before a FULL
+ * group whose write path writes into a main cache they read.
+ * groups    host array [n_groups], 1 <= n_groups <= 32, each as documented
+ *           for csa2_group_step (a REINDEX group may read the pool a FULL
+ *           group of the same call writes).
+ * workspace csa2_group_steps_workspace_size bytes, 256-byte aligned, no
+ *           initial contents needed; not shared by concurrent calls.
+ * Errors: those of csa2_group_step for any group (nothing is enqueued
+ * then); BAD_SHAPE for n_groups outside 1..32.
+ * ------------------------------------------------------------------- */
+int32_t csa2_group_steps_workspace_size(const csa2_group_desc *groups, int32_t n_groups, size_t *bytes);
+int32_t csa2_group_steps(const csa2_group_desc *groups, int32_t n_groups, void *workspace, size_t ws_bytes,
+                         void *stream);
 
 /* ---------------------------------------------------------------------
  * csa2_group_step_static - csa2_group_step without a caller workspace, for
@@ -394,7 +418,7 @@ int32_t csa2_profile_scan_read(double *total_ms, int64_t *launches);
 
 /* csa2_profile_attn / csa2_profile_attn_read - the same timing for every
  * attention kernel launched by csa2_sparse_swa_attn / csa2_group_step (the
- * decode schedule launches a logits and a P V kernel per batch of up to 8
+ * decode schedule launches a logits and a P V kernel per batch of up to 24
  * layers, the many-query schedules one kernel per layer).  Same contract
  * and errors as csa2_profile_scan. */
 int32_t csa2_profile_attn(int32_t enable);

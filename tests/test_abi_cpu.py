@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = csa2.lib()
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 24
     assert sorted(names) == sorted(csa2.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", csa2.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (csa2_\w+)$", out, re.M))
@@ -191,6 +191,13 @@ def test_group_validation():
     assert L.csa2_group_step(ctypes.byref(g), FAKE, 1 << 20, None) == BAD_SHAPE
     g.first_mode = csa2.CSA2_MODE_FULL
     assert L.csa2_group_step(ctypes.byref(g), FAKE, 1 << 20, None) == NULL_ARG      # per-layer arrays missing
+    arr = (csa2.GroupDesc * 2)(g, g)
+    n = ctypes.c_size_t(0)
+    assert L.csa2_group_steps(None, 1, FAKE, 1 << 20, None) == NULL_ARG
+    assert L.csa2_group_steps(arr, 0, FAKE, 1 << 20, None) == BAD_SHAPE
+    assert L.csa2_group_steps(arr, 33, FAKE, 1 << 20, None) == BAD_SHAPE
+    assert L.csa2_group_steps(arr, 2, FAKE, 1 << 20, None) == NULL_ARG           # a group's checks apply
+    assert L.csa2_group_steps_workspace_size(arr, 0, ctypes.byref(n)) == BAD_SHAPE
 
 
 def _group_desc(n_layers=2, pool_blocks=64, idx_len=4096):
@@ -228,6 +235,10 @@ def test_group_validation_runs_before_any_enqueue():
     g2.new_rows, g2.new_kv, g2.new_dst_row, g2.w_ik, g2.new_kv_dtype = 16, FAKE, FAKE, FAKE, csa2.CSA2_BF16
     assert L.csa2_group_workspace_size(ctypes.byref(g2), ctypes.byref(n)) == 0
     assert L.csa2_group_step(ctypes.byref(g2), FAKE, n.value, None) == UNSUPPORTED
+    # in a multi-group call every group is checked before the first is enqueued
+    arr = (csa2.GroupDesc * 2)(g, g2)
+    assert L.csa2_group_steps_workspace_size(arr, 2, ctypes.byref(n)) == 0
+    assert L.csa2_group_steps(arr, 2, FAKE, n.value, None) == UNSUPPORTED
 
 
 def test_binding_refuses_missing_library(monkeypatch, tmp_path):

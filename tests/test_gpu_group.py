@@ -262,3 +262,83 @@ def test_group_workspace_shared_by_groups_of_other_shapes():
         for a, b in zip(ref, got):
             assert np.array_equal(h(a), h(b), equal_nan=True), label
         assert not np.any(h(got[4]) == 7.0), label    # every output row written
+
+
+def _stack(cfg, lens, modes, write_groups, P=2048, K=512, D=512, H=64, DI=128, HI=8, W=128, shared_cache=True):
+    """A stack of decode groups over raw FP4 caches; returns a builder of fresh
+    (groups, outputs) on fresh copies of the caches.  write_groups: indices of
+    Full groups that also write one new entry per sequence."""
+    M = len(lens)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    n = int(sum(lens))
+    n_caches = 1 if shared_cache else len(modes)
+    raw = [(synth.fp4_bytes(cfg, 2 * c, n, D), synth.fp4_bytes(cfg, 2 * c + 1, n, DI)) for c in range(n_caches)]
+    st, ln = t(starts), t(np.asarray(lens, np.int32))
+    qs = csa2.queries(t(np.arange(M, dtype=np.int32)), t((np.asarray(lens) - 1).astype(np.int32)))
+    w_ik = t(synth.w_ik(cfg, D, DI))
+    layer_in = []
+    for gi in range(len(modes)):
+        qi, wi = synth.q_idx(cfg, gi, M, HI, DI), synth.w_idx(cfg, gi, M, HI)
+        qs_l, sw_l = [], []
+        for layer in range(4):
+            qs_l.append(t(synth.q_main(cfg, 4 * gi + layer, M, H, D, "bf16")).view(torch.bfloat16))
+            sc, ss = empty_u8(M * W, D), torch.empty((M * W,), dtype=torch.float32, device=dev())
+            csa2.csa2_quantize_fp8_rows(t(synth.swa_rows(cfg, 4 * gi + layer, 0, M * W, D)), sc, ss)
+            sw_l.append(csa2.swa(sc, ss, t(np.arange(M, dtype=np.int32) * W), t(np.full(M, W, np.int32)), D, W))
+        new = t(synth.gaussian_rows(cfg, synth.TAG_MAIN_KV, 10 + gi, 0, 0, M, D))
+        dst = t((starts + np.asarray(lens) - 1 - gi).astype(np.int64))
+        layer_in.append((t(qi).view(torch.bfloat16), t(wi), qs_l, sw_l, new, dst))
+
+    def build():
+        caches = []
+        for (rc, rs), (ic, is_) in raw:
+            caches.append((t(rc), t(rs), t(ic), t(is_)))
+        kvs = [(csa2.fp4_cache(c[0], c[1], st, ln, D, max(lens), 1), csa2.fp4_cache(c[2], c[3], st, ln, DI, max(lens), 1))
+               for c in caches]
+        pool = torch.full((M, P), -7, dtype=torch.int32, device=dev())
+        cnt = torch.full((M,), -7, dtype=torch.int32, device=dev())
+        groups, outs = [], [pool, cnt] + [x for c in caches for x in c]
+        for gi, mode in enumerate(modes):
+            kv, idx = kvs[0 if shared_cache else gi]
+            qi, wi, q_l, sw_l, new, dst = layer_in[gi]
+            topk = torch.full((M, K), -7, dtype=torch.int32, device=dev())
+            score = torch.full((M, K), -7.0, dtype=torch.float32, device=dev())
+            out = [torch.full((M, H, D), 7.0, dtype=torch.float32, device=dev()) for _ in range(4)]
+            lse = [torch.full((M, H), 7.0, dtype=torch.float32, device=dev()) for _ in range(4)]
+            wr = gi in write_groups
+            g = csa2.Group(csa2.CSA2_MODE_FULL if mode == "full" else csa2.CSA2_MODE_REINDEX, kv, idx, qs, qi, wi, P,
+                           K, pool, cnt, topk, score, q_l, csa2.CSA2_BF16, H, sw_l, out, lse, D ** -0.5,
+                           new_kv=new if wr else None, new_dst_row=dst if wr else None, w_ik=w_ik if wr else None)
+            g.keep = (kv, idx)
+            groups.append(g)
+            outs += [topk, score] + out + lse
+        return groups, outs
+
+    return build
+
+
+@pytest.mark.parametrize("case", ["decoder_64k", "decoder_ragged_32", "writes_between", "own_caches"])
+def test_group_steps_equal_group_by_group(case):
+    """csa2_group_steps (every group's index first, then the attention of all
+    layers batched across groups) gives bit-identical results to
+    csa2_group_step called group by group, which the tests above check
+    against the oracle: the decoder's 5 groups at 64K and on the ragged
+    32-sequence batch; a stack where a later Full group writes into the cache
+    the earlier groups attend over; and Full groups with caches of their own."""
+    if case == "decoder_64k":
+        build = _stack(31, [65536], ["full"] + ["reindex"] * 4, {0})
+    elif case == "decoder_ragged_32":
+        build = _stack(32, synth.workload(3).seq_lens, ["full"] + ["reindex"] * 4, {0})
+    elif case == "writes_between":
+        build = _stack(33, [40000, 9000, 70001], ["full", "reindex", "full", "reindex"], {0, 2})
+    else:
+        build = _stack(34, [30000, 50000], ["full", "full", "full"], {0, 1, 2}, P=512, K=256, shared_cache=False)
+    announce("group steps", case)
+    ref_groups, ref_out = build()
+    for g in ref_groups:
+        csa2.csa2_group_step(g, workspace(csa2.csa2_group_workspace_size(g)))
+    ref = [h(x) for x in ref_out]
+    groups, outs = build()
+    csa2.csa2_group_steps(groups, workspace(csa2.csa2_group_steps_workspace_size(groups)))
+    for i, (a, b) in enumerate(zip(ref, [h(x) for x in outs])):
+        assert np.array_equal(a, b), i
