@@ -94,9 +94,9 @@ int check_flat_limits(const csa2_fp4_cache *idx, int pool_blocks) {
   return CSA2_OK;
 }
 
-size_t index_bytes(const csa2_fp4_cache *idx, int m, int pool_blocks, int top_k) {
+size_t index_bytes(const csa2_fp4_cache *idx, int m, int pool_blocks, int top_k, int n_sets = 1) {
   if (pool_blocks == 0) return flat_ws_bytes(idx->max_len, m, top_k);
-  return index_ws_layout(idx->max_len, m, pool_blocks, top_k).total;
+  return index_ws_layout(idx->max_len, m, pool_blocks, top_k, n_sets).total;
 }
 
 int check_swa(const csa2_swa *swa, int dim) {
@@ -399,17 +399,45 @@ static size_t steps_index_offset(const csa2_group_desc *groups, int n) {
   return align256(a);
 }
 
+// A REINDEX group that can join the query sets re-scored and selected
+// together with the groups before it (the first of which is `head`): the
+// same pool, indexer cache, queries and pool / Top-K sizes.
+static bool same_pool(const csa2_group_desc *head, const csa2_group_desc *g) {
+  const csa2_fp4_cache &x = head->idx, &y = g->idx;
+  return g->first_mode == CSA2_MODE_REINDEX && head->pool_blocks > 0 && g->pool == head->pool &&
+         g->pool_count == head->pool_count && g->pool_blocks == head->pool_blocks && g->top_k == head->top_k &&
+         g->idx_heads == head->idx_heads && x.codes == y.codes && x.scales == y.scales &&
+         x.seq_start == y.seq_start && x.seq_len == y.seq_len && x.n_seq == y.n_seq && x.dim == y.dim &&
+         x.max_len == y.max_len && x.ratio == y.ratio && g->qs.seq == head->qs.seq && g->qs.pos == head->qs.pos &&
+         g->qs.m == head->qs.m && g->qs.run == head->qs.run;
+}
+
+// Query-set families: each group starts one unless it joins the previous
+// family; fam[i] = index of the first group of group i's family.
+static void pool_families(const csa2_group_desc *groups, int n, int *fam) {
+  for (int i = 0; i < n; ++i) {
+    fam[i] = i;
+    if (i > 0) {
+      const int h = fam[i - 1];
+      if (i - h < kSelSets && same_pool(&groups[h], &groups[i])) fam[i] = h;
+    }
+  }
+}
+
 int32_t csa2_group_steps_workspace_size(const csa2_group_desc *groups, int32_t n_groups, size_t *bytes) {
   if (!groups || !bytes) return CSA2_ERR_NULL_ARG;
   if (n_groups < 1 || n_groups > kMaxGroups) return CSA2_ERR_BAD_SHAPE;
+  int fam[kMaxGroups];
+  pool_families(groups, n_groups, fam);
   size_t idx = 0;
   for (int i = 0; i < n_groups; ++i) {
     size_t one = 0;
     const int st = csa2_group_workspace_size(&groups[i], &one);
     if (st) return st;
     if (groups[i].n_layers > 64) return CSA2_ERR_BAD_SHAPE;
+    // a family's last group sizes the re-score buffer of all its query sets
     idx = std::max(idx, align256(index_bytes(&groups[i].idx, groups[i].qs.m, groups[i].pool_blocks,
-                                             groups[i].top_k)));
+                                             groups[i].top_k, i - fam[i] + 1)));
   }
   *bytes = steps_index_offset(groups, n_groups) + idx;
   return CSA2_OK;
@@ -451,6 +479,19 @@ int32_t csa2_group_steps(const csa2_group_desc *groups, int32_t n_groups, void *
     }
     return CSA2_OK;
   };
+  int fam[kMaxGroups];
+  pool_families(groups, n_groups, fam);
+  // the re-score and select of family [h, e): one launch pair for all its query sets
+  auto select = [&](int h, int e) -> int {
+    const csa2_group_desc *g = &groups[h];
+    if (g->qs.m == 0) return CSA2_OK;
+    SelSet sets[kSelSets];
+    for (int k = h; k < e; ++k) sets[k - h] = SelSet{groups[k].q_idx, groups[k].w_idx, groups[k].topk,
+                                                       groups[k].topk_score};
+    const IndexWs L = index_ws_layout(g->idx.max_len, g->qs.m, g->pool_blocks, g->top_k, e - h);
+    return launch_rescore_select(g->idx, g->qs, g->idx_heads, g->pool, g->pool_count, g->pool_blocks, g->top_k,
+                                 sets, e - h, reinterpret_cast<float *>(static_cast<char *>(iws) + L.pscore), s);
+  };
   int pending = 0;   // first group whose attention has not been enqueued
   for (int i = 0; i < n_groups; ++i) {
     const csa2_group_desc *g = &groups[i];
@@ -464,7 +505,25 @@ int32_t csa2_group_steps(const csa2_group_desc *groups, int32_t n_groups, void *
           break;
         }
     }
-    if (g->qs.m > 0 && (st = enqueue_group_index(g, iws, s))) return st;
+    if (g->qs.m > 0) {
+      if (g->first_mode == CSA2_MODE_FULL && g->new_rows > 0) {
+        st = launch_quantize_fp4(g->new_kv, g->new_kv_dtype, g->new_rows, g->kv.dim, g->new_dst_row, g->kv.codes,
+                                 g->kv.scales, g->w_ik, g->idx.dim, g->idx.codes, g->idx.scales, s);
+        if (st) return st;
+      }
+      if (g->first_mode == CSA2_MODE_FULL && g->pool_blocks == 0) {
+        st = launch_index_flat(g->idx, g->qs, g->q_idx, g->w_idx, g->idx_heads, g->top_k, g->topk, g->topk_score,
+                               iws, s);
+      } else if (g->first_mode == CSA2_MODE_FULL) {
+        st = launch_index_pool(g->idx, g->qs, g->q_idx, g->w_idx, g->idx_heads, g->pool_blocks, g->top_k, g->pool,
+                               g->pool_count, iws, s);
+      }
+      if (st) return st;
+    }
+    // a family ends where the next group does not join it: its query sets
+    // are re-scored and selected before anything of the next group runs
+    const bool flat = g->first_mode == CSA2_MODE_FULL && g->pool_blocks == 0;
+    if (!flat && (i + 1 == n_groups || fam[i + 1] != fam[i]) && (st = select(fam[i], i + 1))) return st;
   }
   return flush(pending, n_groups);
 }

@@ -465,22 +465,28 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
 // when that leaves most of the chip idle).  Slot 8*e + r of a query holds
 // the score of position 8*pool[e] + r (-inf when not visible).  Each wave
 // first loads its pool entries, then all its rows, then scores.
+struct SelBatch {
+  SelSet s[kSelSets];
+};
+
+// grid (pool chunks, queries, query sets).
 template <int DI, int E>
 __global__ __launch_bounds__(256) void k_rescore(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                                  const int64_t *__restrict__ seq_start,
                                                  const int32_t *__restrict__ seq_len, int ratio,
                                                  const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
-                                                 const uint16_t *__restrict__ q_idx, const float *__restrict__ w_idx,
                                                  int H, const int32_t *__restrict__ pool,
                                                  const int32_t *__restrict__ pool_count, int P,
-                                                 float *__restrict__ pscore) {
-  const int m = blockIdx.y;
+                                                 float *__restrict__ pscore, SelBatch sb) {
+  const int m = blockIdx.y, set = blockIdx.z;
+  const uint16_t *q_idx = sb.s[set].q_idx;
+  const float *w_idx = sb.s[set].w_idx;
   int s;
   const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
   const int cnt = min(pool_count[m], P);
   const int e0 = blockIdx.x * E;
   if (e0 >= cnt) return;
-  float *ps = pscore + (int64_t)m * 8 * P;
+  float *ps = pscore + ((int64_t)set * gridDim.y + m) * 8 * P;
   const int l = lane_id(), n = l & 15, qq = l >> 4, wv = threadIdx.x >> 6;
   if (vis == 0) {
     for (int i = threadIdx.x; i < 8 * E; i += blockDim.x)
@@ -781,13 +787,17 @@ CSA2_DEV void load_slot_scores(const float *__restrict__ ps, int n, float (&sv)[
 // position 8*pool[e] + r; slot order equals position order because the pool
 // is ascending, so ties on the score resolve to the lower position and the
 // output comes out in ascending position order.
+// grid (queries, query sets).
 template <int NT, int PER>
 __global__ __launch_bounds__(NT) void k_topk_select(const float *__restrict__ pscore,
                                                     const int32_t *__restrict__ pool,
                                                     const int32_t *__restrict__ pool_count, int P, int K,
-                                                    int32_t *__restrict__ topk_out, float *__restrict__ topk_score) {
+                                                    SelBatch sb) {
   __shared__ __attribute__((aligned(16))) SelectLds<NT> sm;
-  const int m = blockIdx.x;
+  const int m = blockIdx.x, set = blockIdx.y;
+  int32_t *__restrict__ topk_out = sb.s[set].topk;
+  float *__restrict__ topk_score = sb.s[set].score;
+  pscore += (int64_t)set * gridDim.x * 8 * P;
   const int cnt = min(pool_count[m], P);
   int32_t blk[PER / kBlock];     // pool blocks of this thread's slots, loaded up front
   const int32_t *pl = pool + (int64_t)m * P;
@@ -854,7 +864,7 @@ static int hist_replicas(int64_t max_len, int m) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(kHistMaxReplicas, wgs / 8));
 }
 
-IndexWs index_ws_layout(int64_t max_len, int m, int pool_blocks, int top_k) {
+IndexWs index_ws_layout(int64_t max_len, int m, int pool_blocks, int top_k, int n_sets) {
   (void)top_k;
   IndexWs w{};
   w.hist_rep = hist_replicas(max_len, m);
@@ -868,44 +878,46 @@ IndexWs index_ws_layout(int64_t max_len, int m, int pool_blocks, int top_k) {
   w.counters = off; off = align256(off + sizeof(uint32_t) * (size_t)m * 4);
   w.sure = off;     off = align256(off + sizeof(int32_t) * (size_t)m * pool_blocks);
   w.tie = off;      off = align256(off + sizeof(int32_t) * (size_t)m * w.nb_max);
-  w.pscore = off;   off = align256(off + sizeof(float) * (size_t)m * w.slots);
+  w.pscore = off;   off = align256(off + sizeof(float) * (size_t)std::max(1, n_sets) * m * w.slots);
   w.total = off;
   return w;
 }
 
 template <int DI>
-static int rescore_and_select(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
-                              const float *w_idx, int heads, const int32_t *pool, const int32_t *pool_count,
-                              int P, int K, int32_t *topk_out, float *topk_score, float *pscore,
-                              hipStream_t stream) {
-  // 64 blocks per workgroup, or 16 when that would leave most CUs idle (few queries)
-  if ((int64_t)((P + kRescoreEntries - 1) / kRescoreEntries) * qs.m >= 512) {
-    const dim3 g5((P + kRescoreEntries - 1) / kRescoreEntries, qs.m);
-    hipLaunchKernelGGL((k_rescore<DI, kRescoreEntries>), g5, dim3(256), 0, stream, idx.codes, idx.scales,
-                       idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, q_idx, w_idx, heads, pool, pool_count,
-                       P, pscore);
-  } else {
-    const dim3 g5((P + 15) / 16, qs.m);
-    hipLaunchKernelGGL((k_rescore<DI, 16>), g5, dim3(256), 0, stream, idx.codes, idx.scales, idx.seq_start,
-                       idx.seq_len, idx.ratio, qs.seq, qs.pos, q_idx, w_idx, heads, pool, pool_count, P, pscore);
+static int rescore_and_select(const csa2_fp4_cache &idx, const csa2_queries &qs, int heads, const int32_t *pool,
+                              const int32_t *pool_count, int P, int K, const SelSet *sets, int n_sets,
+                              float *pscore, hipStream_t stream) {
+  for (int b0 = 0; b0 < n_sets; b0 += kSelSets) {
+    const int ns = std::min(kSelSets, n_sets - b0);
+    SelBatch sb{};
+    for (int i = 0; i < ns; ++i) sb.s[i] = sets[b0 + i];
+    float *ps = pscore + (size_t)b0 * qs.m * 8 * P;
+    // 64 blocks per workgroup, or 16 when that would leave most CUs idle (few queries)
+    if ((int64_t)((P + kRescoreEntries - 1) / kRescoreEntries) * qs.m * ns >= 512) {
+      const dim3 g5((P + kRescoreEntries - 1) / kRescoreEntries, qs.m, ns);
+      hipLaunchKernelGGL((k_rescore<DI, kRescoreEntries>), g5, dim3(256), 0, stream, idx.codes, idx.scales,
+                         idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, heads, pool, pool_count, P, ps, sb);
+    } else {
+      const dim3 g5((P + 15) / 16, qs.m, ns);
+      hipLaunchKernelGGL((k_rescore<DI, 16>), g5, dim3(256), 0, stream, idx.codes, idx.scales, idx.seq_start,
+                         idx.seq_len, idx.ratio, qs.seq, qs.pos, heads, pool, pool_count, P, ps, sb);
+    }
+    // 8P <= 32768 slots (P <= 4096)
+    const dim3 g6(qs.m, ns);
+    if (8 * P <= 256 * 16)
+      hipLaunchKernelGGL((k_topk_select<256, 16>), g6, dim3(256), 0, stream, ps, pool, pool_count, P, K, sb);
+    else if (8 * P <= 1024 * 16)
+      hipLaunchKernelGGL((k_topk_select<1024, 16>), g6, dim3(1024), 0, stream, ps, pool, pool_count, P, K, sb);
+    else
+      hipLaunchKernelGGL((k_topk_select<1024, 32>), g6, dim3(1024), 0, stream, ps, pool, pool_count, P, K, sb);
   }
-  // 8P <= 32768 slots (P <= 4096)
-  if (8 * P <= 256 * 16)
-    hipLaunchKernelGGL((k_topk_select<256, 16>), dim3(qs.m), dim3(256), 0, stream, pscore, pool, pool_count, P, K,
-                       topk_out, topk_score);
-  else if (8 * P <= 1024 * 16)
-    hipLaunchKernelGGL((k_topk_select<1024, 16>), dim3(qs.m), dim3(1024), 0, stream, pscore, pool, pool_count, P,
-                       K, topk_out, topk_score);
-  else
-    hipLaunchKernelGGL((k_topk_select<1024, 32>), dim3(qs.m), dim3(1024), 0, stream, pscore, pool, pool_count, P,
-                       K, topk_out, topk_score);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 
 template <int DI>
-static int index_full_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
+static int index_pool_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
                            const float *w_idx, int heads, int P, int K, int32_t *pool_out, int32_t *pool_count,
-                           int32_t *topk_out, float *topk_score, void *ws, hipStream_t stream) {
+                           void *ws, hipStream_t stream) {
   const IndexWs L = index_ws_layout(idx.max_len, qs.m, P, K);
   char *base = static_cast<char *>(ws);
   float *bmax = reinterpret_cast<float *>(base + L.bmax);
@@ -913,7 +925,6 @@ static int index_full_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
   uint32_t *counters = reinterpret_cast<uint32_t *>(base + L.counters);
   int32_t *sure = reinterpret_cast<int32_t *>(base + L.sure);
   int32_t *tie = reinterpret_cast<int32_t *>(base + L.tie);
-  float *pscore = reinterpret_cast<float *>(base + L.pscore);
 
   // hist and counters are adjacent: clear both with one fill kernel
   const int64_t nz = (int64_t)((L.sure - L.hist) / sizeof(uint32_t));
@@ -939,9 +950,7 @@ static int index_full_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
       hipLaunchKernelGGL(k_pool_finalize, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, counters, sure, tie,
                          idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
     }
-    if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
-    return rescore_and_select<DI>(idx, qs, q_idx, w_idx, heads, pool_out, pool_count, P, K, topk_out, topk_score,
-                                  pscore, stream);
+    return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
   }
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
   if (idx.max_len > 0) {
@@ -964,37 +973,40 @@ static int index_full_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
                      idx.ratio, P, counters, sure, tie);
   hipLaunchKernelGGL(k_pool_finalize, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, counters, sure, tie,
                      idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
-  if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
-  return rescore_and_select<DI>(idx, qs, q_idx, w_idx, heads, pool_out, pool_count, P, K, topk_out, topk_score,
-                                pscore, stream);
+  return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+}
+
+int launch_index_pool(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx, const float *w_idx,
+                      int heads, int P, int K, int32_t *pool_out, int32_t *pool_count, void *ws,
+                      hipStream_t stream) {
+  switch (idx.dim) {
+    case 64: return index_pool_impl<64>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, ws, stream);
+    case 128: return index_pool_impl<128>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, ws, stream);
+    case 256: return index_pool_impl<256>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, ws, stream);
+    default: return CSA2_ERR_UNSUPPORTED;
+  }
+}
+
+int launch_rescore_select(const csa2_fp4_cache &idx, const csa2_queries &qs, int heads, const int32_t *pool,
+                          const int32_t *pool_count, int P, int K, const SelSet *sets, int n_sets, float *pscore,
+                          hipStream_t stream) {
+  switch (idx.dim) {
+    case 64: return rescore_and_select<64>(idx, qs, heads, pool, pool_count, P, K, sets, n_sets, pscore, stream);
+    case 128: return rescore_and_select<128>(idx, qs, heads, pool, pool_count, P, K, sets, n_sets, pscore, stream);
+    case 256: return rescore_and_select<256>(idx, qs, heads, pool, pool_count, P, K, sets, n_sets, pscore, stream);
+    default: return CSA2_ERR_UNSUPPORTED;
+  }
 }
 
 int launch_index_full(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
                       const float *w_idx, int heads, int P, int K, int32_t *pool_out, int32_t *pool_count,
                       int32_t *topk_out, float *topk_score, void *ws, hipStream_t stream) {
-  switch (idx.dim) {
-    case 64: return index_full_impl<64>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, topk_out,
-                                        topk_score, ws, stream);
-    case 128: return index_full_impl<128>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, topk_out,
-                                          topk_score, ws, stream);
-    case 256: return index_full_impl<256>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, topk_out,
-                                          topk_score, ws, stream);
-    default: return CSA2_ERR_UNSUPPORTED;
-  }
-}
-
-int launch_rescore_select(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
-                          const float *w_idx, int heads, const int32_t *pool, const int32_t *pool_count, int P, int K,
-                          int32_t *topk_out, float *topk_score, float *pscore, hipStream_t stream) {
-  switch (idx.dim) {
-    case 64: return rescore_and_select<64>(idx, qs, q_idx, w_idx, heads, pool, pool_count, P, K, topk_out,
-                                           topk_score, pscore, stream);
-    case 128: return rescore_and_select<128>(idx, qs, q_idx, w_idx, heads, pool, pool_count, P, K, topk_out,
-                                             topk_score, pscore, stream);
-    case 256: return rescore_and_select<256>(idx, qs, q_idx, w_idx, heads, pool, pool_count, P, K, topk_out,
-                                             topk_score, pscore, stream);
-    default: return CSA2_ERR_UNSUPPORTED;
-  }
+  int st = launch_index_pool(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, ws, stream);
+  if (st) return st;
+  const IndexWs L = index_ws_layout(idx.max_len, qs.m, P, K);
+  const SelSet set{q_idx, w_idx, topk_out, topk_score};
+  return launch_rescore_select(idx, qs, heads, pool_out, pool_count, P, K, &set, 1,
+                               reinterpret_cast<float *>(static_cast<char *>(ws) + L.pscore), stream);
 }
 
 int launch_block_select(const float *bmax, int64_t nb_stride, int64_t nb_max, const csa2_fp4_cache &idx,
@@ -1018,8 +1030,8 @@ int launch_reindex(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint
                    float *topk_score, void *ws, hipStream_t stream) {
   const IndexWs L = index_ws_layout(idx.max_len, qs.m, P, K);
   float *pscore = reinterpret_cast<float *>(static_cast<char *>(ws) + L.pscore);
-  return launch_rescore_select(idx, qs, q_idx, w_idx, heads, pool_in, pool_count, P, K, topk_out, topk_score,
-                               pscore, stream);
+  const SelSet set{q_idx, w_idx, topk_out, topk_score};
+  return launch_rescore_select(idx, qs, heads, pool_in, pool_count, P, K, &set, 1, pscore, stream);
 }
 
 }  // namespace csa2

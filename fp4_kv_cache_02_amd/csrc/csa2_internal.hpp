@@ -30,11 +30,16 @@ struct IndexWs {
   int32_t slots;        // 8 * pool_blocks
   int32_t hist_rep;     // first-scan histogram replicas per query
 };
-IndexWs index_ws_layout(int64_t max_len, int m, int pool_blocks, int top_k);
+// n_sets: query sets (groups) re-scored and selected together over one pool.
+IndexWs index_ws_layout(int64_t max_len, int m, int pool_blocks, int top_k, int n_sets = 1);
 
 int launch_index_full(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
                       const float *w_idx, int heads, int pool_blocks, int top_k, int32_t *pool_out,
                       int32_t *pool_count, int32_t *topk_out, float *topk_score, void *ws, hipStream_t stream);
+// The first part of launch_index_full alone: the scan and the pool (no Top-K).
+int launch_index_pool(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx, const float *w_idx,
+                      int heads, int pool_blocks, int top_k, int32_t *pool_out, int32_t *pool_count, void *ws,
+                      hipStream_t stream);
 int launch_reindex(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx, const float *w_idx,
                    int heads, const int32_t *pool_in, const int32_t *pool_count, int pool_blocks, int top_k,
                    int32_t *topk_out, float *topk_score, void *ws, hipStream_t stream);
@@ -47,9 +52,20 @@ int launch_reindex(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint
 constexpr int64_t kBlockSelectMax = 1024 * 64;
 int launch_block_select(const float *bmax, int64_t nb_stride, int64_t nb_max, const csa2_fp4_cache &idx,
                         const csa2_queries &qs, int P, int32_t *pool_out, int32_t *pool_count, hipStream_t stream);
-int launch_rescore_select(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
-                          const float *w_idx, int heads, const int32_t *pool, const int32_t *pool_count, int P, int K,
-                          int32_t *topk_out, float *topk_score, float *pscore, hipStream_t stream);
+// One query set of a batched re-score and select: its indexer queries and
+// head weights, and its outputs.
+struct SelSet {
+  const uint16_t *q_idx;
+  const float *w_idx;
+  int32_t *topk;
+  float *score;
+};
+constexpr int kSelSets = 8;   // query sets per launch
+// Re-score and select for n_sets query sets over the same pools (pscore:
+// n_sets * m * 8P floats).
+int launch_rescore_select(const csa2_fp4_cache &idx, const csa2_queries &qs, int heads, const int32_t *pool,
+                          const int32_t *pool_count, int P, int K, const SelSet *sets, int n_sets, float *pscore,
+                          hipStream_t stream);
 
 // ---- multi-query scoring (csa2_prefill.hip) ----
 // Block maxima bmax[m * nb_stride + b] of every query's visible entries from

@@ -439,8 +439,8 @@ int launch_index_flat(const csa2_fp4_cache &idx, const csa2_queries &qs, const u
   st = launch_block_select(bmax, L.nb_stride, nb_max > 0 ? nb_max : 1, idx, qs, top_k, pool, pool_count,
                                stream);
   if (st != CSA2_OK) return st;
-  return launch_rescore_select(idx, qs, q_idx, w_idx, heads, pool, pool_count, top_k, top_k, topk_out, topk_score,
-                               pscore, stream);
+  const SelSet set{q_idx, w_idx, topk_out, topk_score};
+  return launch_rescore_select(idx, qs, heads, pool, pool_count, top_k, top_k, &set, 1, pscore, stream);
 }
 
 }  // namespace csa2

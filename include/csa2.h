@@ -355,7 +355,10 @@ int32_t csa2_group_step(const csa2_group_desc *g, void *workspace, size_t ws_byt
  * layers), with the same results as csa2_group_step on each group in order.
  *
  * Every group's write path and first-layer indexer are enqueued in group
- * order; the attention of all their layers follows in batches of up to 24
+ * order; a FULL group with a pool and the REINDEX groups after it that read
+ * that pool (same indexer cache, queries, pool_blocks, top_k and idx_heads;
+ * up to 8 groups) re-score and select their Top-K lists together (one launch
+ * pair).  The attention of all their layers follows in batches of up to 24
  * layers across groups (one logits and one P V launch per batch; a layer
  * reads its own group's Top-K list).  Consecutive groups share a batch when
  * they have the same main cache, queries, query format, heads, top_k and
