@@ -24,7 +24,7 @@ constexpr int kScanWaves = 8;                    // waves per scan workgroup
 constexpr int kScanTiles = 1024;                 // 16-position tiles per scan workgroup (largest chunk)
 constexpr int kScanChunk = kScanTiles * 16;      // 16384 positions
 constexpr int kScanBlocks = kScanChunk / kBlock; // 2048 block maxima
-constexpr int kFilterBlocks = 4096;              // blocks per pool-filter workgroup (fewer workgroups share each list counter)
+constexpr int kFilterBlocks = 2048;              // blocks per pool-filter workgroup (one list reservation each)
 constexpr int kRescoreEntries = 64;              // pool blocks per re-score workgroup (at most)
 
 
@@ -188,65 +188,6 @@ CSA2_DEV void wave_append(bool pred, int32_t value, int *counter, int32_t *list)
   if (pred) list[base + __popcll(mask & ((1ull << l) - 1ull))] = value;
 }
 
-// Threshold bin of each query (one workgroup per query): merge the scan's
-// histogram replicas and find the bin that holds the need-th largest block
-// maximum, need = min(P, visible blocks); -1 when every block is taken.
-// Written to counters[4m + 2] for the filter and the finalisation.
-__global__ __launch_bounds__(256) void k_hist_threshold(const uint32_t *__restrict__ hist, int hist_rep,
-                                                        const int32_t *__restrict__ seq_len,
-                                                        const int32_t *__restrict__ q_seq,
-                                                        const int32_t *__restrict__ q_pos, int ratio, int P,
-                                                        uint32_t *__restrict__ counters) {
-  __shared__ int s_scan[8];
-  __shared__ int s_T;
-  const int m = blockIdx.x;
-  int s;
-  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
-  const int64_t nb = (vis + kBlock - 1) / kBlock;
-  if (threadIdx.x == 0) s_T = -1;
-  __syncthreads();
-  if (nb > P) {
-    const int64_t need = P;
-    // thread t owns bins [4096-16(t+1), 4096-16t) (thread 0 = highest bins)
-    const int hi = kHistBins - 16 * threadIdx.x;
-    int hv[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) hv[k] = 0;
-    // every replica's loads in flight at once (a fixed trip count, replicas
-    // past hist_rep read replica 0 and count nothing)
-    uint4 x[kHistMaxReplicas][4];
-#pragma unroll
-    for (int r = 0; r < kHistMaxReplicas; ++r) {
-      const int rr = r < hist_rep ? r : 0;
-      const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + ((int64_t)m * hist_rep + rr) * kHistBins + hi - 16);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) x[r][k] = h4[k];
-    }
-#pragma unroll
-    for (int r = 0; r < kHistMaxReplicas; ++r) {
-      if (r >= hist_rep) continue;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        hv[4 * k] += (int)x[r][k].x; hv[4 * k + 1] += (int)x[r][k].y;
-        hv[4 * k + 2] += (int)x[r][k].z; hv[4 * k + 3] += (int)x[r][k].w;
-      }
-    }
-    int c = 0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) c += hv[k];
-    int tot;
-    const int before = block_exclusive_scan<256>(c, s_scan, &tot);
-    if (before < need && before + c >= need) {
-      int cum = before;
-      for (int k = 15; k >= 0; --k) {
-        cum += hv[k];
-        if (cum >= need) { s_T = hi - 16 + k; break; }
-      }
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) counters[m * 4 + 2] = (uint32_t)s_T;
-}
 
 // Histogram of block-maximum keys (top kHistBits bits) when the block
 // maxima come from the multi-query scoring kernel: grid (chunks of
@@ -278,34 +219,99 @@ __global__ __launch_bounds__(256) void k_bmax_hist(const float *__restrict__ bma
     if (s_hist[i]) atomicAdd(&hq[i], s_hist[i]);
 }
 
-// Pool filter: blocks above the threshold bin are in the pool for sure,
-// blocks in it go to the tie list.  Appends are gathered in
-// LDS and reserved in the global lists with one atomic per list per workgroup.
+// Pool filter.  Every workgroup first finds the query's threshold bin T -
+// the bin of the need-th largest block maximum, need = min(P, visible
+// blocks), -1 when every block is taken - from the scan's histogram
+// replicas (workgroup 0 records it in counters[4m + 2] for the
+// finalisation).  Blocks above T are in the pool for sure, blocks in it go
+// to the tie list and are counted by their next 12 key bits into the
+// query's fine histogram (fine[m][4096], zeroed with the coarse one).
+// Appends are gathered in LDS and reserved in the global lists with one
+// atomic per list per workgroup; a workgroup's block maxima are all loaded
+// before any is looked at.
 __global__ __launch_bounds__(256) void k_pool_filter(const float *__restrict__ bmax, int64_t nb_stride,
+                                                     const uint32_t *__restrict__ hist, int hist_rep,
                                                      const int32_t *__restrict__ seq_len, const int32_t *__restrict__ q_seq,
                                                      const int32_t *__restrict__ q_pos, int ratio, int P,
-                                                     uint32_t *__restrict__ counters, int32_t *__restrict__ sure,
-                                                     int32_t *__restrict__ tie) {
-  __shared__ int s_ns, s_nt, s_bs, s_bt;
+                                                     uint32_t *__restrict__ counters, uint32_t *__restrict__ fine,
+                                                     int32_t *__restrict__ sure, int32_t *__restrict__ tie) {
+  constexpr int PT = kFilterBlocks / 256;
+  __shared__ int s_ns, s_nt, s_bs, s_bt, s_T;
+  __shared__ int s_scan[5];
   __shared__ int32_t s_sure[kFilterBlocks], s_tie[kFilterBlocks];
+  __shared__ uint32_t s_fine[kHistBins];
   const int m = blockIdx.y;
   int s;
   const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
   const int64_t nb = (vis + kBlock - 1) / kBlock;
   const int64_t b0 = (int64_t)blockIdx.x * kFilterBlocks;
   if (b0 >= nb) return;
-  if (threadIdx.x == 0) { s_ns = 0; s_nt = 0; }
-  __syncthreads();
-  const int T = (int)counters[m * 4 + 2];
-  const float *bm = bmax + (int64_t)m * nb_stride;
-  for (int j = 0; j < kFilterBlocks / 256; ++j) {
-    const int64_t b = b0 + j * 256 + threadIdx.x;
-    const bool ok = b < nb;
-    const int bin = ok ? (int)(f2key(bm[b]) >> (32 - kHistBits)) : -2;
-    wave_append(ok && bin > T, (int32_t)b, &s_ns, s_sure);
-    wave_append(ok && bin == T, (int32_t)b, &s_nt, s_tie);
+  // unconditional loads (past the visible blocks they read 0), so that
+  // all PT are in flight before the first is used
+  const rsrc_t r_bm = make_rsrc(bmax + (int64_t)m * nb_stride + b0, (uint32_t)(min<int64_t>(nb - b0, kFilterBlocks) * 4));
+  float v[PT];
+#pragma unroll
+  for (int j = 0; j < PT; ++j)
+    v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_bm, (uint32_t)(j * 256 + threadIdx.x) * 4u, 0, 0));
+  for (int i = threadIdx.x; i < kHistBins; i += 256) s_fine[i] = 0u;
+  if (threadIdx.x == 0) { s_ns = 0; s_nt = 0; s_T = -1; }
+  if (nb > P) {
+    // thread t owns bins [4096-16(t+1), 4096-16t) (thread 0 = highest bins);
+    // every replica's loads in flight at once (a fixed trip count, replicas
+    // past hist_rep read replica 0 and count nothing)
+    const int hi = kHistBins - 16 * threadIdx.x;
+    int hv[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) hv[k] = 0;
+    uint4 x[kHistMaxReplicas][4];
+#pragma unroll
+    for (int r = 0; r < kHistMaxReplicas; ++r) {
+      const int rr = r < hist_rep ? r : 0;
+      const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + ((int64_t)m * hist_rep + rr) * kHistBins + hi - 16);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[r][k] = h4[k];
+    }
+#pragma unroll
+    for (int r = 0; r < kHistMaxReplicas; ++r) {
+      if (r >= hist_rep) continue;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        hv[4 * k] += (int)x[r][k].x; hv[4 * k + 1] += (int)x[r][k].y;
+        hv[4 * k + 2] += (int)x[r][k].z; hv[4 * k + 3] += (int)x[r][k].w;
+      }
+    }
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) c += hv[k];
+    int tot;
+    const int before = block_exclusive_scan<256>(c, s_scan, &tot);
+    if (before < P && before + c >= P) {
+      int cum = before;
+      for (int k = 15; k >= 0; --k) {
+        cum += hv[k];
+        if (cum >= P) { s_T = hi - 16 + k; break; }
+      }
+    }
   }
   __syncthreads();
+  const int T = s_T;
+  if (blockIdx.x == 0 && threadIdx.x == 0) counters[m * 4 + 2] = (uint32_t)T;
+#pragma unroll
+  for (int j = 0; j < PT; ++j) {
+    const int64_t b = b0 + j * 256 + threadIdx.x;
+    const bool ok = b < nb;
+    const uint32_t key = f2key(v[j]);
+    const int bin = ok ? (int)(key >> (32 - kHistBits)) : -2;
+    wave_append(ok && bin > T, (int32_t)b, &s_ns, s_sure);
+    wave_append(ok && bin == T, (int32_t)b, &s_nt, s_tie);
+    if (ok && bin == T) atomicAdd(&s_fine[(key >> 8) & (kHistBins - 1)], 1u);
+  }
+  __syncthreads();
+  if (s_nt > 0) {
+    uint32_t *fq = fine + (int64_t)m * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += 256)
+      if (s_fine[i]) atomicAdd(&fq[i], s_fine[i]);
+  }
   if (threadIdx.x == 0) {
     s_bs = s_ns ? (int)atomicAdd(&counters[m * 4 + 0], (uint32_t)s_ns) : 0;
     s_bt = s_nt ? (int)atomicAdd(&counters[m * 4 + 1], (uint32_t)s_nt) : 0;
@@ -327,30 +333,33 @@ __global__ __launch_bounds__(256) void k_pool_filter(const float *__restrict__ b
 // order by compacting a bitmap of the chosen blocks.
 constexpr int kMaxPool = 4096;
 constexpr int kBitmapWords = 16384;  // blocks up to 2^19 go through the bitmap
+constexpr int kFineCand = 2048;      // fine-threshold-bin ties resolved in LDS
 
-__global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict__ bmax, int64_t nb_stride,
-                                                        const uint32_t *__restrict__ counters,
-                                                        const int32_t *__restrict__ sure,
-                                                        const int32_t *__restrict__ tie,
-                                                        const int32_t *__restrict__ seq_len,
-                                                        const int32_t *__restrict__ q_seq,
-                                                        const int32_t *__restrict__ q_pos, int ratio, int P,
-                                                        int32_t *__restrict__ pool_out,
-                                                        int32_t *__restrict__ pool_count) {
-  __shared__ uint32_t s_bits[kBitmapWords];
-  __shared__ int32_t s_pool[kMaxPool];
-  __shared__ uint32_t s_h[256];
-  __shared__ int s_scan[17];
-  __shared__ int s_digit, s_rem, s_cnt, s_n;
-  const int m = blockIdx.x;
-  int s;
-  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
-  const int64_t nb = (vis + kBlock - 1) / kBlock;
+CSA2_DEV void wave_refine(const uint64_t *cand, int n, int rem, uint32_t *h, int *s_digit, int *s_rem,
+                          int *s_cnt, uint64_t &prefix, uint64_t &mask);
+CSA2_DEV uint32_t wave_incl_max(uint32_t v);
+
+struct FinLds {
+  uint32_t bits[kBitmapWords];
+  int32_t pool[kMaxPool];
+  uint64_t cand[kFineCand];
+  uint32_t h[256];
+  int scan[17];
+  int digit, rem, cnt, n, nc, Tf, af, nf;
+  uint64_t cut;
+};
+
+// The finalisation of query m by a workgroup of 1024 threads; s_T is the
+// threshold bin (-1 when every visible block is taken).
+CSA2_DEV void pool_finalize_body(FinLds &F, const float *__restrict__ bmax, int64_t nb_stride,
+                                 const uint32_t *__restrict__ counters, const uint32_t *__restrict__ fine,
+                                 const int32_t *__restrict__ sure, const int32_t *__restrict__ tie, int m,
+                                 int64_t nb, uint32_t s_T, int P, int32_t *__restrict__ pool_out,
+                                 int32_t *__restrict__ pool_count) {
   // counts as far as the lists reach (they never exceed them when the
   // histogram agrees with the block maxima)
   const int n_sure = (int)min<uint32_t>(counters[m * 4 + 0], (uint32_t)P);
   const int n_tie = (int)min<int64_t>((int64_t)counters[m * 4 + 1], nb_stride);
-  const uint32_t s_T = counters[m * 4 + 2];  // threshold bin (meaningful when there are ties)
   const int need = (int)min<int64_t>(min<int64_t>(P, nb), (int64_t)n_sure + n_tie);
   const int need_t = need - n_sure;
   const int32_t *su = sure + (int64_t)m * P;
@@ -359,19 +368,104 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
   const bool use_bits = nb <= 32 * (int64_t)kBitmapWords;
   const int words = (int)((nb + 31) / 32);
   if (use_bits)
-    for (int i = threadIdx.x; i < words; i += blockDim.x) s_bits[i] = 0u;
-  if (threadIdx.x == 0) s_n = 0;
+    for (int i = threadIdx.x; i < words; i += blockDim.x) F.bits[i] = 0u;
+  if (threadIdx.x == 0) F.n = 0;
   __syncthreads();
   auto take = [&](int32_t b) {
-    if (use_bits) atomicOr(&s_bits[b >> 5], 1u << (b & 31));
+    if (use_bits) atomicOr(&F.bits[b >> 5], 1u << (b & 31));
     else {
-      const int slot = atomicAdd(&s_n, 1);
-      if (slot < kMaxPool) s_pool[slot] = b;
+      const int slot = atomicAdd(&F.n, 1);
+      if (slot < kMaxPool) F.pool[slot] = b;
     }
   };
   for (int i = threadIdx.x; i < n_sure; i += blockDim.x)
     if ((uint64_t)su[i] < (uint64_t)nb) take(su[i]);
-  if (need_t > 0) {
+  // the fine threshold bin of the ties (thread 0 = highest fine bins)
+  if (threadIdx.x == 0) { F.Tf = 0; F.af = 0; F.nf = 0; F.nc = 0; }
+  bool fine_ok = false;
+  if (need_t > 0 && need_t < n_tie) {
+    const int hi = kHistBins - 4 * (int)threadIdx.x;
+    const uint4 x = *reinterpret_cast<const uint4 *>(fine + (int64_t)m * kHistBins + hi - 4);
+    const int hv[4] = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+    const int c = hv[0] + hv[1] + hv[2] + hv[3];
+    int tot;
+    const int before = block_exclusive_scan<1024>(c, F.scan, &tot);
+    if (before < need_t && before + c >= need_t) {
+      int cum = before;
+      for (int k = 3; k >= 0; --k) {
+        if (cum + hv[k] >= need_t) { F.Tf = hi - 4 + k; F.af = cum; F.nf = hv[k]; break; }
+        cum += hv[k];
+      }
+    }
+    __syncthreads();
+    // the fine histogram counts every tie (it agrees with the tie list unless
+    // the lists overflowed); its threshold bin must fit the LDS candidates
+    fine_ok = tot == n_tie && F.nf <= kFineCand;
+  }
+  if (need_t > 0 && need_t < n_tie && fine_ok) {
+    const uint32_t Tf = (uint32_t)F.Tf;
+    const int rem_f = need_t - F.af, nf = F.nf;
+    const bool whole = rem_f == nf;
+    // ties above Tf (and all of Tf when it is taken whole) in one gather
+    // pass; Tf's composites to LDS.  Batches of 8 ties per thread: the ids,
+    // then their block maxima, all in flight before any is used (loads past
+    // the list or the visible blocks read 0 and are skipped)
+    const rsrc_t r_ti = make_rsrc(ti, (uint32_t)(n_tie * 4));
+    const rsrc_t r_bm = make_rsrc(bm, (uint32_t)(nb * 4));
+    for (int i0 = 0; i0 < n_tie; i0 += 8 * (int)blockDim.x) {
+      int32_t ids[8];
+      float bv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        ids[u] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_ti, (uint32_t)(i0 + u * blockDim.x + threadIdx.x) * 4u,
+                                                                 0, 0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        bv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            r_bm, ((uint64_t)ids[u] < (uint64_t)nb) ? (uint32_t)ids[u] * 4u : kOutOfRange, 0, 0));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * blockDim.x + threadIdx.x;
+        const int32_t b = ids[u];
+        if (i >= n_tie || (uint64_t)b >= (uint64_t)nb) continue;
+        const uint32_t key = f2key(bv[u]);
+        const uint32_t f = (key >> 8) & (kHistBins - 1);
+        if (f > Tf || (f == Tf && whole)) take(b);
+        else if (f == Tf) {
+          const int slot = atomicAdd(&F.nc, 1);
+          if (slot < kFineCand) F.cand[slot] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)b);
+        }
+      }
+    }
+    __syncthreads();
+    if (!whole) {
+      const int n2 = min(F.nc, kFineCand);
+      const int lane = threadIdx.x & 63;
+      if (n2 <= 64) {
+        if (threadIdx.x < 64) {
+          const uint64_t c = (lane < n2) ? F.cand[lane] : 0ull;
+          const uint32_t clo = (uint32_t)c, chi = (uint32_t)(c >> 32);
+          int r = 0;
+          for (int j = 0; j < n2; ++j) {
+            const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)chi, j) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)clo, j);
+            r += o > c;
+          }
+          if (lane < n2 && r < rem_f) take((int32_t)(~(uint32_t)c));
+        }
+      } else {
+        if (threadIdx.x < 64) {
+          uint64_t pf = 0ull, mk = 0ull;
+          wave_refine(F.cand, n2, rem_f, F.h, &F.digit, &F.rem, &F.cnt, pf, mk);
+          if (threadIdx.x == 0) F.cut = pf;
+        }
+        __syncthreads();
+        const uint64_t cut = F.cut;
+        for (int i = threadIdx.x; i < n2; i += blockDim.x)
+          if (F.cand[i] >= cut) take((int32_t)(~(uint32_t)F.cand[i]));
+      }
+    }
+  } else if (need_t > 0) {
     if (need_t >= n_tie) {
       for (int i = threadIdx.x; i < n_tie; i += blockDim.x)
         if ((uint64_t)ti[i] < (uint64_t)nb) take(ti[i]);
@@ -388,21 +482,21 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
         const int width = hi < 8 ? hi : 8;
         const int shift = hi - width;
         const uint64_t dmask = (1ull << width) - 1ull;
-        for (int i = threadIdx.x; i < 256; i += blockDim.x) s_h[i] = 0u;
+        for (int i = threadIdx.x; i < 256; i += blockDim.x) F.h[i] = 0u;
         __syncthreads();
         for (int i = threadIdx.x; i < n_tie; i += blockDim.x) {
           const int32_t b = ti[i];
           if ((uint64_t)b >= (uint64_t)nb) continue;
           const uint64_t c = ((uint64_t)f2key(bm[b]) << 32) | (uint64_t)(~(uint32_t)b);
-          if ((c & mask) == prefix) atomicAdd(&s_h[(c >> shift) & dmask], 1u);
+          if ((c & mask) == prefix) atomicAdd(&F.h[(c >> shift) & dmask], 1u);
         }
         __syncthreads();
-        find_digit(s_h, rem, &s_digit, &s_rem, &s_cnt);
+        find_digit(F.h, rem, &F.digit, &F.rem, &F.cnt);
         __syncthreads();
-        prefix |= (uint64_t)s_digit << shift;
+        prefix |= (uint64_t)F.digit << shift;
         mask |= dmask << shift;
-        rem = s_rem;
-        if (s_cnt == rem) break;
+        rem = F.rem;
+        if (F.cnt == rem) break;
       }
       for (int i = threadIdx.x; i < n_tie; i += blockDim.x) {
         const int32_t b = ti[i];
@@ -420,14 +514,14 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
     int cnt = 0;
     for (int k = 0; k < wpt; ++k) {
       const int w = threadIdx.x * wpt + k;
-      if (w < words) cnt += __popc(s_bits[w]);
+      if (w < words) cnt += __popc(F.bits[w]);
     }
     int tot;
-    int pos = block_exclusive_scan<1024>(cnt, s_scan, &tot);
+    int pos = block_exclusive_scan<1024>(cnt, F.scan, &tot);
     for (int k = 0; k < wpt; ++k) {
       const int w = threadIdx.x * wpt + k;
       if (w >= words) break;
-      uint32_t bits = s_bits[w];
+      uint32_t bits = F.bits[w];
       while (bits) {
         const int bit = __ffs(bits) - 1;
         bits &= bits - 1;
@@ -440,26 +534,46 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
     int n2 = 64;
     while (n2 < need) n2 <<= 1;
     // slots past what was taken sort last (rescoring treats them as not visible)
-    for (int i = min(s_n, need) + threadIdx.x; i < n2; i += blockDim.x) s_pool[i] = 0x7FFFFFFF;
+    for (int i = min(F.n, need) + threadIdx.x; i < n2; i += blockDim.x) F.pool[i] = 0x7FFFFFFF;
     __syncthreads();
     for (int k = 2; k <= n2; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
         for (int i = threadIdx.x; i < n2; i += blockDim.x) {
           const int ixj = i ^ j;
           if (ixj > i) {
-            const int32_t a = s_pool[i], b = s_pool[ixj];
+            const int32_t a = F.pool[i], b = F.pool[ixj];
             const bool up = (i & k) == 0;
-            if ((a > b) == up) { s_pool[i] = b; s_pool[ixj] = a; }
+            if ((a > b) == up) { F.pool[i] = b; F.pool[ixj] = a; }
           }
         }
         __syncthreads();
       }
     }
-    for (int i = threadIdx.x; i < need; i += blockDim.x) out[i] = s_pool[i];
+    for (int i = threadIdx.x; i < need; i += blockDim.x) out[i] = F.pool[i];
   }
   for (int i = need + threadIdx.x; i < P; i += blockDim.x) out[i] = -1;
   if (threadIdx.x == 0) pool_count[m] = need;
 }
+
+__global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict__ bmax, int64_t nb_stride,
+                                                        const uint32_t *__restrict__ counters,
+                                                        const uint32_t *__restrict__ fine,
+                                                        const int32_t *__restrict__ sure,
+                                                        const int32_t *__restrict__ tie,
+                                                        const int32_t *__restrict__ seq_len,
+                                                        const int32_t *__restrict__ q_seq,
+                                                        const int32_t *__restrict__ q_pos, int ratio, int P,
+                                                        int32_t *__restrict__ pool_out,
+                                                        int32_t *__restrict__ pool_count) {
+  __shared__ FinLds F;
+  const int m = blockIdx.x;
+  int s;
+  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
+  const int64_t nb = (vis + kBlock - 1) / kBlock;
+  pool_finalize_body(F, bmax, nb_stride, counters, fine, sure, tie, m, nb, counters[m * 4 + 2], P, pool_out,
+                     pool_count);
+}
+
 
 // Re-score the positions of E pool blocks per workgroup (E = 64, or fewer
 // when that leaves most of the chip idle).  Slot 8*e + r of a query holds
@@ -876,6 +990,7 @@ IndexWs index_ws_layout(int64_t max_len, int m, int pool_blocks, int top_k, int 
   w.bmax = off;     off = align256(off + sizeof(float) * (size_t)m * w.nb_max);
   w.hist = off;     off = align256(off + sizeof(uint32_t) * (size_t)m * w.hist_rep * kHistBins);
   w.counters = off; off = align256(off + sizeof(uint32_t) * (size_t)m * 4);
+  w.fine = off;     off = align256(off + sizeof(uint32_t) * (size_t)m * kHistBins);
   w.sure = off;     off = align256(off + sizeof(int32_t) * (size_t)m * pool_blocks);
   w.tie = off;      off = align256(off + sizeof(int32_t) * (size_t)m * w.nb_max);
   w.pscore = off;   off = align256(off + sizeof(float) * (size_t)std::max(1, n_sets) * m * w.slots);
@@ -914,6 +1029,20 @@ static int rescore_and_select(const csa2_fp4_cache &idx, const csa2_queries &qs,
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 
+// The pool from the block maxima and their histogram: the filter (which
+// finds the threshold bin itself), then the finalisation.
+static void pool_from_hist(const csa2_fp4_cache &idx, const csa2_queries &qs, int P, int64_t nbq, const IndexWs &L,
+                           const float *bmax, const uint32_t *hist, uint32_t *counters, int32_t *sure, int32_t *tie,
+                           int32_t *pool_out, int32_t *pool_count, hipStream_t stream) {
+  (void)nbq;
+  const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);
+  uint32_t *fine = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(counters) + (L.fine - L.counters));
+  hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, hist, L.hist_rep, idx.seq_len, qs.seq,
+                     qs.pos, idx.ratio, P, counters, fine, sure, tie);
+  hipLaunchKernelGGL(k_pool_finalize, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, counters, fine, sure, tie,
+                     idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
+}
+
 template <int DI>
 static int index_pool_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
                            const float *w_idx, int heads, int P, int K, int32_t *pool_out, int32_t *pool_count,
@@ -926,7 +1055,7 @@ static int index_pool_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
   int32_t *sure = reinterpret_cast<int32_t *>(base + L.sure);
   int32_t *tie = reinterpret_cast<int32_t *>(base + L.tie);
 
-  // hist and counters are adjacent: clear both with one fill kernel
+  // hist, counters and fine are adjacent: clear them with one fill kernel
   const int64_t nz = (int64_t)((L.sure - L.hist) / sizeof(uint32_t));
   const int64_t nbq = (idx.max_len + kBlock - 1) / kBlock;   // blocks of the longest sequence
   if (qs.run >= 2) {
@@ -942,13 +1071,7 @@ static int index_pool_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
       hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
       hipLaunchKernelGGL(k_bmax_hist, dim3((unsigned)((nbq + kFilterBlocks - 1) / kFilterBlocks), qs.m), dim3(256),
                          0, stream, bmax, L.nb_max, idx.seq_len, qs.seq, qs.pos, idx.ratio, hist, L.hist_rep);
-      hipLaunchKernelGGL(k_hist_threshold, dim3(qs.m), dim3(256), 0, stream, hist, L.hist_rep, idx.seq_len, qs.seq,
-                         qs.pos, idx.ratio, P, counters);
-      const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);
-      hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, idx.seq_len, qs.seq, qs.pos,
-                         idx.ratio, P, counters, sure, tie);
-      hipLaunchKernelGGL(k_pool_finalize, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, counters, sure, tie,
-                         idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
+      pool_from_hist(idx, qs, P, nbq, L, bmax, hist, counters, sure, tie, pool_out, pool_count, stream);
     }
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
   }
@@ -966,13 +1089,7 @@ static int index_pool_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
     }
 #undef CSA2_SCAN
   }
-  hipLaunchKernelGGL(k_hist_threshold, dim3(qs.m), dim3(256), 0, stream, hist, L.hist_rep, idx.seq_len, qs.seq,
-                     qs.pos, idx.ratio, P, counters);
-  const dim3 g3((unsigned)((L.nb_max + kFilterBlocks - 1) / kFilterBlocks), qs.m);
-  hipLaunchKernelGGL(k_pool_filter, g3, dim3(256), 0, stream, bmax, L.nb_max, idx.seq_len, qs.seq, qs.pos,
-                     idx.ratio, P, counters, sure, tie);
-  hipLaunchKernelGGL(k_pool_finalize, dim3(qs.m), dim3(1024), 0, stream, bmax, L.nb_max, counters, sure, tie,
-                     idx.seq_len, qs.seq, qs.pos, idx.ratio, P, pool_out, pool_count);
+  pool_from_hist(idx, qs, P, nbq, L, bmax, hist, counters, sure, tie, pool_out, pool_count, stream);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 

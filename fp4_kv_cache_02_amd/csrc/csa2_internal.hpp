@@ -25,7 +25,7 @@ int launch_dequant_fp4(const uint8_t *codes, const uint8_t *scales, int64_t rows
 // ---- indexer (csa2_index.hip) ----
 // Workspace layout of the indexer calls, all offsets 256-byte aligned.
 struct IndexWs {
-  size_t bmax, hist, counters, sure, tie, pscore, total;
+  size_t bmax, hist, counters, fine, sure, tie, pscore, total;
   int64_t nb_max;       // block slots per query
   int32_t slots;        // 8 * pool_blocks
   int32_t hist_rep;     // first-scan histogram replicas per query
