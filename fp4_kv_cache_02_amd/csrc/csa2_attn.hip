@@ -194,6 +194,7 @@ CSA2_DEV void qk_tile(const _Float16 *kt, int KT, const half8_t *qa, const half8
 // weighting in fp32.  No partial outputs, no merge, no atomics.
 
 constexpr int kChunk = 32;                        // key slots per logit chunk = one P V k-step
+constexpr int kLogitChunks = 2;   // key chunks per logits workgroup (its queries loaded once)
 constexpr int kPvKeys = 256;                      // key slots per P V block (one per thread)
 constexpr int kPvHeads = 64;                      // heads per P V workgroup
 constexpr int kMaxChunks = (2048 + 1024) / kChunk;
@@ -376,7 +377,9 @@ struct QRaw {
 // two 16-key tiles (queries in registers, keys from LDS), logits, chunk
 // statistics and the f16 p values.  The next tile's queries load while the
 // current one computes; the first tile's load is issued with the key loads.
-template <int D, bool QF32>
+// ONE_TILE: at most 64 heads, one head tile per wave (its queries stay in
+// registers across the workgroup's chunks, with no second tile's registers).
+template <int D, bool QF32, bool ONE_TILE>
 __global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int nwc, const int32_t *__restrict__ q_seq,
                                                      const int32_t *__restrict__ q_pos,
                                                      const int64_t *__restrict__ seq_start,
@@ -394,38 +397,56 @@ __global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int 
   constexpr int DP = D / 8;
   constexpr int QE = QF32 ? 4 : 2;
   const int nch = nmc + nwc, nkp = kChunk * nch, Kp = kChunk * nmc;
-  int m, c;   // query and chunk
-  xcd_group(blockIdx.x, M, m, c);
+  int m, cp;   // query and chunk pair
+  xcd_group(blockIdx.x, M, m, cp);
   const int li = blockIdx.y;
   const int tid = threadIdx.x, l = lane_id(), wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = l & 15, quad = l >> 4;
-  const bool main_chunk = c < nmc;
   const AttnLayer &ly = lb.l[li];
   const int32_t *topk = ly.topk;
-  if (!main_chunk && kChunk * (c - nmc) >= ly.window) return;   // past this layer's window
   const int key = tid >> 3, d0 = (tid & 7) * DP;
+  const rsrc_t r_topk = make_rsrc(K ? topk + (int64_t)m * K : nullptr, (uint32_t)(K * 4));
+  // the chunk's key index (Top-K chunks; out of range otherwise)
+  auto index_of = [&](int c) {
+    const int slot = kChunk * c + key;
+    return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_topk, (c < nmc && slot < K) ? slot * 4u : kOutOfRange, 0,
+                                                         0);
+  };
   // a Top-K chunk's index load goes out first, beside the sequence lookup
   // of query_rows (the row loads need both)
-  const int slot = kChunk * c + key;
-  const rsrc_t r_topk = make_rsrc(K ? topk + (int64_t)m * K : nullptr, (uint32_t)(K * 4));
-  const int32_t j = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
-      r_topk, (main_chunk && slot < K) ? slot * 4u : kOutOfRange, 0, 0);
+  int32_t j_next = index_of(kLogitChunks * cp);
   const QueryRows qr = query_rows(seq_start, seq_len, ratio, q_seq, q_pos, m);
   const rsrc_t rq = make_rsrc(static_cast<const char *>(ly.q) + (int64_t)m * H * D * QE, (uint32_t)(H * D * QE));
   // the wave's head tiles: wv + 4 it for it < ntw
   const int nht = (H + 15) / 16;
   const int ntw = (wv < nht) ? (nht - 1 - wv) / 4 + 1 : 0;
   auto q_load = [&](int it, QR &r) { r.load(rq, 16 * (wv + 4 * it) + row, H, quad, it < ntw); };
+  QR qA;
+  QR qB_store[ONE_TILE ? 1 : 2];
+  QR &qB = qB_store[ONE_TILE ? 0 : 1];
+  q_load(0, qA);
+  // ---- the workgroup's chunks, one after another: the queries of a wave
+  // with one head tile stay in registers ----
+  for (int cc = 0; cc < kLogitChunks; ++cc) {
+  const int c = kLogitChunks * cp + cc;
+  if (c >= nch) break;
+  const bool main_chunk = c < nmc;
+  if (!main_chunk && kChunk * (c - nmc) >= ly.window) break;   // past this layer's window (as are later chunks)
+  const int slot = kChunk * c + key;
+  const int32_t j = j_next;
+  if (cc > 0) {
+    __syncthreads();                 // the previous chunk's reads of the key tile are done
+    if (!ONE_TILE && ntw > 1) q_load(0, qA);
+  }
+  if (cc + 1 < kLogitChunks && c + 1 < nch) j_next = index_of(c + 1);
 
-  // ---- issue the key index, the first tile's queries, then the key row;
-  // decode the chunk's 32 keys into LDS ----
-  QR qA, qB;
+  // ---- the key row (its index issued earlier); decode the chunk's 32 keys
+  // into LDS ----
   float ksv = 0.0f;
   auto put = [&](int u, const u32x4_t &v) {
     *reinterpret_cast<u32x4_t *>(&L.kt[key * Lds::KT + d0 + 8 * u]) = v;
   };
   if (main_chunk) {
-    q_load(0, qA);
     const bool ok = slot < K && j >= 0 && j < qr.vis;
     ksv = ok ? 1.0f : 0.0f;
     Fp4Piece<D, DP> pc;
@@ -444,7 +465,6 @@ __global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int 
     const int wcount = max(0, min(ly.swa_count[m], W));
     const int64_t wstart = ly.swa_start[m];
     const bool ok = wr < wcount;
-    q_load(0, qA);
     // every row scale of the query's window (W <= 1024): the lift is shared
     // by all window chunks of the query
     const rsrc_t r_ws = make_rsrc(ly.swa_scale + wstart, (uint32_t)(wcount * 4));
@@ -482,7 +502,7 @@ __global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int 
   const rsrc_t r_sw = make_rsrc(stats + lrow * nch, (uint32_t)(H * nch * 8));
 
   auto tile = [&](int it, const QR &cur, QR &nxt) {
-    q_load(it + 1, nxt);
+    if constexpr (!ONE_TILE) q_load(it + 1, nxt);
     const int ht = wv + 4 * it;
     float4_t sacc[2];
 #pragma unroll
@@ -527,9 +547,14 @@ __global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int 
                                             row == 0 ? (uint32_t)((h * nch + c) * 8) : kOutOfRange, 0, 0);
     }
   };
-  for (int it = 0; it < ntw; it += 2) {
-    tile(it, qA, qB);
-    if (it + 1 < ntw) tile(it + 1, qB, qA);
+  if constexpr (ONE_TILE) {
+    if (ntw > 0) tile(0, qA, qA);
+  } else {
+    for (int it = 0; it < ntw; it += 2) {
+      tile(it, qA, qB);
+      if (it + 1 < ntw) tile(it + 1, qB, qA);
+    }
+  }
   }
 }
 
@@ -936,7 +961,7 @@ static int attn_layers_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, in
                             const AttnLayer *layers, int n, float scale, void *ws, hipStream_t stream) {
   const float tau2 = scale * 1.4426950408889634f;  // log2-domain softmax: p = 2^(z - max)
   if (use_decode_kernel(qs.m, heads, D, kv.max_len)) {
-    constexpr int DS = D < 32 ? D : 32;
+    constexpr int DS = D < 64 ? D : 64;
     for (int b0 = 0; b0 < n; b0 += kAttnBatch) {
       const int nl = std::min(kAttnBatch, n - b0);
       AttnBatch lb{};
@@ -958,10 +983,15 @@ static int attn_layers_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, in
       uint8_t *gc = reinterpret_cast<uint8_t *>(base + L.gcodes);
       uint8_t *gs = reinterpret_cast<uint8_t *>(base + L.gscales);
       uint8_t *gw = reinterpret_cast<uint8_t *>(base + L.gwin);
-      const dim3 g1(xcd_grid(L.nmc + L.nwc, qs.m), (unsigned)nl);
-      CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_logits<D, QF32>), g1, dim3(256), stream, qs.m, K, L.nmc, L.nwc, qs.seq,
-                        qs.pos, kv.seq_start, kv.seq_len, kv.codes, kv.scales, kv.ratio, heads, tau2, P, st, lf,
-                        gc, gs, gw, lb);
+      const dim3 g1(xcd_grid((L.nmc + L.nwc + kLogitChunks - 1) / kLogitChunks, qs.m), (unsigned)nl);
+      if (heads <= 64)
+        CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_logits<D, QF32, true>), g1, dim3(256), stream, qs.m, K, L.nmc, L.nwc,
+                          qs.seq, qs.pos, kv.seq_start, kv.seq_len, kv.codes, kv.scales, kv.ratio, heads, tau2, P, st,
+                          lf, gc, gs, gw, lb);
+      else
+        CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_logits<D, QF32, false>), g1, dim3(256), stream, qs.m, K, L.nmc, L.nwc,
+                          qs.seq, qs.pos, kv.seq_start, kv.seq_len, kv.codes, kv.scales, kv.ratio, heads, tau2, P, st,
+                          lf, gc, gs, gw, lb);
       const int nhg = (heads + kPvHeads - 1) / kPvHeads;
       const dim3 g2(xcd_grid((D / DS) * nhg, qs.m), (unsigned)nl);
       CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_pv<D, DS>), g2, dim3(256), stream, qs.m, heads, L.nmc, L.nwc, P, st, lf, gc,
