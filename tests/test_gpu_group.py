@@ -317,7 +317,8 @@ def _stack(cfg, lens, modes, write_groups, P=2048, K=512, D=512, H=64, DI=128, H
     return build
 
 
-@pytest.mark.parametrize("case", ["decoder_64k", "decoder_ragged_32", "writes_between", "own_caches"])
+@pytest.mark.parametrize("case", ["decoder_64k", "decoder_ragged_32", "writes_between", "own_caches",
+                                  "ten_sets_one_pool", "flat_groups"])
 def test_group_steps_equal_group_by_group(case):
     """csa2_group_steps (every group's index first, then the attention of all
     layers batched across groups) gives bit-identical results to
@@ -331,8 +332,15 @@ def test_group_steps_equal_group_by_group(case):
         build = _stack(32, synth.workload(3).seq_lens, ["full"] + ["reindex"] * 4, {0})
     elif case == "writes_between":
         build = _stack(33, [40000, 9000, 70001], ["full", "reindex", "full", "reindex"], {0, 2})
-    else:
+    elif case == "own_caches":
         build = _stack(34, [30000, 50000], ["full", "full", "full"], {0, 1, 2}, P=512, K=256, shared_cache=False)
+    elif case == "ten_sets_one_pool":
+        # more query sets on one pool than one re-score launch takes: a second
+        # family headed by a Reindex group
+        build = _stack(35, [20000, 44444], ["full"] + ["reindex"] * 9, {0}, P=256, K=128)
+    else:
+        # pool_blocks = 0: flat Top-K groups (the encoder's), one with a write
+        build = _stack(36, [9000, 15001], ["full", "full"], {0}, P=0, K=128, shared_cache=False)
     announce("group steps", case)
     ref_groups, ref_out = build()
     for g in ref_groups:
