@@ -241,36 +241,38 @@ __global__ __launch_bounds__(256) void k_pool_filter(const float *__restrict__ b
   __shared__ int32_t s_sure[kFilterBlocks], s_tie[kFilterBlocks];
   __shared__ uint32_t s_fine[kHistBins];
   const int m = blockIdx.y;
-  int s;
-  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
-  const int64_t nb = (vis + kBlock - 1) / kBlock;
   const int64_t b0 = (int64_t)blockIdx.x * kFilterBlocks;
-  if (b0 >= nb) return;
-  // unconditional loads (past the visible blocks they read 0), so that
-  // all PT are in flight before the first is used
-  const rsrc_t r_bm = make_rsrc(bmax + (int64_t)m * nb_stride + b0, (uint32_t)(min<int64_t>(nb - b0, kFilterBlocks) * 4));
+  // the workgroup's block maxima and every replica's histogram bins are
+  // loaded before the query's visible count is known (both are in range of
+  // the workspace whatever it is; entries past the visible blocks are
+  // ignored below), so their latency overlaps the sequence lookup.  Thread t
+  // owns bins [4096-16(t+1), 4096-16t) (thread 0 = highest bins); replicas
+  // past hist_rep read replica 0 and count nothing
+  const rsrc_t r_bm = make_rsrc(bmax + (int64_t)m * nb_stride + b0,
+                                (uint32_t)(max<int64_t>(0, min<int64_t>(nb_stride - b0, kFilterBlocks)) * 4));
   float v[PT];
 #pragma unroll
   for (int j = 0; j < PT; ++j)
     v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_bm, (uint32_t)(j * 256 + threadIdx.x) * 4u, 0, 0));
+  const int hi = kHistBins - 16 * threadIdx.x;
+  uint4 x[kHistMaxReplicas][4];
+#pragma unroll
+  for (int r = 0; r < kHistMaxReplicas; ++r) {
+    const int rr = r < hist_rep ? r : 0;
+    const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + ((int64_t)m * hist_rep + rr) * kHistBins + hi - 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[r][k] = h4[k];
+  }
+  int s;
+  const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
+  const int64_t nb = (vis + kBlock - 1) / kBlock;
+  if (b0 >= nb) return;
   for (int i = threadIdx.x; i < kHistBins; i += 256) s_fine[i] = 0u;
   if (threadIdx.x == 0) { s_ns = 0; s_nt = 0; s_T = -1; }
   if (nb > P) {
-    // thread t owns bins [4096-16(t+1), 4096-16t) (thread 0 = highest bins);
-    // every replica's loads in flight at once (a fixed trip count, replicas
-    // past hist_rep read replica 0 and count nothing)
-    const int hi = kHistBins - 16 * threadIdx.x;
     int hv[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) hv[k] = 0;
-    uint4 x[kHistMaxReplicas][4];
-#pragma unroll
-    for (int r = 0; r < kHistMaxReplicas; ++r) {
-      const int rr = r < hist_rep ? r : 0;
-      const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + ((int64_t)m * hist_rep + rr) * kHistBins + hi - 16);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) x[r][k] = h4[k];
-    }
 #pragma unroll
     for (int r = 0; r < kHistMaxReplicas; ++r) {
       if (r >= hist_rep) continue;
@@ -351,18 +353,19 @@ struct FinLds {
 
 // The finalisation of query m by a workgroup of 1024 threads; s_T is the
 // threshold bin (-1 when every visible block is taken).
-CSA2_DEV void pool_finalize_body(FinLds &F, const float *__restrict__ bmax, int64_t nb_stride,
-                                 const uint32_t *__restrict__ counters, const uint32_t *__restrict__ fine,
-                                 const int32_t *__restrict__ sure, const int32_t *__restrict__ tie, int m,
-                                 int64_t nb, uint32_t s_T, int P, int32_t *__restrict__ pool_out,
-                                 int32_t *__restrict__ pool_count) {
+// cnt4: the query's counters (sure count, tie count, threshold bin); fine4:
+// this thread's four fine-histogram bins; su_pre: sure-list entries
+// threadIdx.x + 1024 u (all loaded before the visible count was known).
+CSA2_DEV void pool_finalize_body(FinLds &F, const float *__restrict__ bmax, int64_t nb_stride, const uint4 &cnt4,
+                                 const uint4 &fine4, const int32_t (&su_pre)[4],
+                                 const int32_t *__restrict__ tie, int m, int64_t nb, uint32_t s_T, int P,
+                                 int32_t *__restrict__ pool_out, int32_t *__restrict__ pool_count) {
   // counts as far as the lists reach (they never exceed them when the
   // histogram agrees with the block maxima)
-  const int n_sure = (int)min<uint32_t>(counters[m * 4 + 0], (uint32_t)P);
-  const int n_tie = (int)min<int64_t>((int64_t)counters[m * 4 + 1], nb_stride);
+  const int n_sure = (int)min<uint32_t>(cnt4.x, (uint32_t)P);
+  const int n_tie = (int)min<int64_t>((int64_t)cnt4.y, nb_stride);
   const int need = (int)min<int64_t>(min<int64_t>(P, nb), (int64_t)n_sure + n_tie);
   const int need_t = need - n_sure;
-  const int32_t *su = sure + (int64_t)m * P;
   const int32_t *ti = tie + (int64_t)m * nb_stride;
   const float *bm = bmax + (int64_t)m * nb_stride;
   const bool use_bits = nb <= 32 * (int64_t)kBitmapWords;
@@ -378,15 +381,15 @@ CSA2_DEV void pool_finalize_body(FinLds &F, const float *__restrict__ bmax, int6
       if (slot < kMaxPool) F.pool[slot] = b;
     }
   };
-  for (int i = threadIdx.x; i < n_sure; i += blockDim.x)
-    if ((uint64_t)su[i] < (uint64_t)nb) take(su[i]);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if ((int)threadIdx.x + 1024 * u < n_sure && (uint64_t)su_pre[u] < (uint64_t)nb) take(su_pre[u]);
   // the fine threshold bin of the ties (thread 0 = highest fine bins)
   if (threadIdx.x == 0) { F.Tf = 0; F.af = 0; F.nf = 0; F.nc = 0; }
   bool fine_ok = false;
   if (need_t > 0 && need_t < n_tie) {
     const int hi = kHistBins - 4 * (int)threadIdx.x;
-    const uint4 x = *reinterpret_cast<const uint4 *>(fine + (int64_t)m * kHistBins + hi - 4);
-    const int hv[4] = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+    const int hv[4] = {(int)fine4.x, (int)fine4.y, (int)fine4.z, (int)fine4.w};
     const int c = hv[0] + hv[1] + hv[2] + hv[3];
     int tot;
     const int before = block_exclusive_scan<1024>(c, F.scan, &tot);
@@ -566,12 +569,20 @@ __global__ __launch_bounds__(1024) void k_pool_finalize(const float *__restrict_
                                                         int32_t *__restrict__ pool_out,
                                                         int32_t *__restrict__ pool_count) {
   __shared__ FinLds F;
+  static_assert(kMaxPool <= 4 * 1024, "sure-list loads per thread");
   const int m = blockIdx.x;
+  // everything that does not depend on the visible count first
+  const uint4 cnt4 = *reinterpret_cast<const uint4 *>(counters + m * 4);
+  const uint4 fine4 = *reinterpret_cast<const uint4 *>(fine + (int64_t)m * kHistBins + kHistBins - 4 * (threadIdx.x + 1));
+  const rsrc_t r_su = make_rsrc(sure + (int64_t)m * P, (uint32_t)(P * 4));
+  int32_t su_pre[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    su_pre[u] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_su, (uint32_t)(threadIdx.x + 1024 * u) * 4u, 0, 0);
   int s;
   const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
   const int64_t nb = (vis + kBlock - 1) / kBlock;
-  pool_finalize_body(F, bmax, nb_stride, counters, fine, sure, tie, m, nb, counters[m * 4 + 2], P, pool_out,
-                     pool_count);
+  pool_finalize_body(F, bmax, nb_stride, cnt4, fine4, su_pre, tie, m, nb, cnt4.z, P, pool_out, pool_count);
 }
 
 
