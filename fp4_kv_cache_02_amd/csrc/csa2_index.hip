@@ -606,35 +606,43 @@ __global__ __launch_bounds__(256) void k_rescore(const uint8_t *__restrict__ cod
   const int m = blockIdx.y, set = blockIdx.z;
   const uint16_t *q_idx = sb.s[set].q_idx;
   const float *w_idx = sb.s[set].w_idx;
+  const int e0 = blockIdx.x * E;
+  const int l = lane_id(), n = l & 15, qq = l >> 4, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int TPW = E / 2 / 4;  // tiles per wave
+  // the pool entries and the query first: neither depends on the visible
+  // count or the pool's length, so their latency overlaps those lookups
+  const rsrc_t r_pl = make_rsrc(pool + (int64_t)m * P, (uint32_t)(P * 4));
+  int32_t blk_raw[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int e = e0 + 2 * (wv + 4 * k) + (n >> 3);
+    blk_raw[k] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_pl, (uint32_t)e * 4u, 0, 0);
+  }
+  IdxQuery<DI> Q;
+  load_idx_query<DI>(q_idx + (int64_t)m * H * DI, w_idx + (int64_t)m * H, H, Q);
   int s;
   const int64_t vis = visible_entries(seq_len, q_seq, q_pos, ratio, m, &s);
   const int cnt = min(pool_count[m], P);
-  const int e0 = blockIdx.x * E;
   if (e0 >= cnt) return;
   float *ps = pscore + ((int64_t)set * gridDim.y + m) * 8 * P;
-  const int l = lane_id(), n = l & 15, qq = l >> 4, wv = threadIdx.x >> 6;
   if (vis == 0) {
     for (int i = threadIdx.x; i < 8 * E; i += blockDim.x)
       if (e0 * 8 + i < 8 * cnt) ps[e0 * 8 + i] = -INFINITY;
     return;
   }
   const int64_t row0 = seq_start[s];
-  const int32_t *pl = pool + (int64_t)m * P;
-  constexpr int TPW = E / 2 / 4;  // tiles per wave
   int64_t pos[TPW];
   bool valid[TPW];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
     const int e = e0 + 2 * (wv + 4 * k) + (n >> 3);
-    const int32_t blk = (e < cnt) ? pl[e] : -1;
+    const int32_t blk = (e < cnt) ? blk_raw[k] : -1;
     pos[k] = (int64_t)blk * kBlock + (n & 7);
     valid[k] = blk >= 0 && pos[k] < vis;
   }
   LaneCodes<DI> c[TPW];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) load_lane_codes<DI>(codes, scales, row0 + (valid[k] ? pos[k] : 0), qq, c[k]);
-  IdxQuery<DI> Q;
-  load_idx_query<DI>(q_idx + (int64_t)m * H * DI, w_idx + (int64_t)m * H, H, Q);
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
     const int e = e0 + 2 * (wv + 4 * k) + (n >> 3);
@@ -923,13 +931,26 @@ __global__ __launch_bounds__(NT) void k_topk_select(const float *__restrict__ ps
   int32_t *__restrict__ topk_out = sb.s[set].topk;
   float *__restrict__ topk_score = sb.s[set].score;
   pscore += (int64_t)set * gridDim.x * 8 * P;
-  const int cnt = min(pool_count[m], P);
-  int32_t blk[PER / kBlock];     // pool blocks of this thread's slots, loaded up front
-  const int32_t *pl = pool + (int64_t)m * P;
+  // the pool blocks and scores of this thread's slots are loaded before the
+  // pool's length is known (slots past it are masked once it is)
+  const rsrc_t r_pl = make_rsrc(pool + (int64_t)m * P, (uint32_t)(P * 4));
+  int32_t blk[PER / kBlock];
 #pragma unroll
-  for (int b = 0; b < PER / kBlock; ++b) blk[b] = pl[min((int)threadIdx.x * (PER / kBlock) + b, max(cnt, 1) - 1)];
+  for (int b = 0; b < PER / kBlock; ++b)
+    blk[b] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+        r_pl, (uint32_t)((int)threadIdx.x * (PER / kBlock) + b) * 4u, 0, 0);
+  const rsrc_t r_ps = make_rsrc(pscore + (int64_t)m * 8 * P, (uint32_t)(8 * P * 4));
   float sv[PER];
-  load_slot_scores<PER>(pscore + (int64_t)m * 8 * P, 8 * cnt, sv);
+#pragma unroll
+  for (int k = 0; k < PER / 4; ++k) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r_ps, (uint32_t)(threadIdx.x * PER + 4 * k) * 4u, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[4 * k + e] = __uint_as_float(x[e]);
+  }
+  const int cnt = min(pool_count[m], P);
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if ((int)threadIdx.x * PER + i >= 8 * cnt) sv[i] = -INFINITY;
   int32_t *out = topk_out + (int64_t)m * K;
   float *osc = topk_score ? topk_score + (int64_t)m * K : nullptr;
   const int Kp = select_topk<NT, PER>(sv, K, sm, [&](int rank, int i, float v) {
