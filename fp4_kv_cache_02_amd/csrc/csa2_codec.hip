@@ -285,6 +285,144 @@ __global__ __launch_bounds__(64 * CT * KS) void k_quantize_fp4_derive_mfma(
   }
 }
 
+// Indexer keys of many rows already in the cache, dim = 64 GQ (64, 128, 256
+// or 512): the same fp64 product as k_quantize_fp4_derive_mfma with the work
+// laid out for throughput.  A workgroup computes key columns 16 ct .. 16 ct
+// + 15 (one FP4 group of the key) of 64 rows, wave w the 16-row tile w; its
+// 16 W_ik columns are staged once in LDS and read by all four waves.  In a
+// wave, k-slot q = l / 16 of the MFMA walks channels q dim/4 .. (q+1) dim/4
+// - 1 in ascending order: lane l holds row l % 16's codes for those channels
+// (GQ whole FP4 groups) and decodes them in registers, and reads column
+// l % 16's weight at the same channel from LDS.  Four accumulators take the
+// channels in turn and are added at the end (fp64 throughout, rounded once
+// to fp32).
+//
+// 1-D grid of idx_dim / 16 * nq workgroups (nq = row quads rounded up to a
+// multiple of 8), mapped so that the workgroups of one row quad run on one
+// XCD (consecutive workgroups go to consecutive XCDs): they read the same
+// rows, which then come from that XCD's L2.  Row quads past the last row exit.
+// The two E2M1 codes of byte `sel` of `w` -> fp32 pair (low nibble first),
+// exact (hardware convert with unit scale; sel is a constant after unrolling).
+CSA2_DEV float2_t e2m1x2_to_f32(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  }
+}
+
+template <int GQ>
+__global__ __launch_bounds__(256) void k_derive_tiles(int64_t rows, int dim, const int64_t *__restrict__ dst_row,
+                                                      const uint8_t *__restrict__ codes,
+                                                      const uint8_t *__restrict__ scales,
+                                                      const float *__restrict__ w_ik, int idx_dim,
+                                                      uint8_t *__restrict__ ik_codes,
+                                                      uint8_t *__restrict__ ik_scales) {
+  constexpr int kq = GQ * kGroup;              // channels per k-slot
+  __shared__ __attribute__((aligned(16))) float ws[kDeriveMaxDim * 16];   // [kk / 4][q][n][kk % 4]
+  __shared__ float yk[4 * 256];
+  const int cgs = idx_dim / kGroup;
+  const uint32_t b = blockIdx.x;
+  const int slot = (int)(b >> 3);
+  const int ct = slot % cgs;
+  const int64_t quad = (int64_t)(slot / cgs) * 8 + (b & 7);
+  const int64_t r0 = quad * 64;
+  if (r0 >= rows) return;
+  const int tid = threadIdx.x, l = lane_id(), wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col0 = ct * kGroup;
+  // ---- this workgroup's W_ik columns: 16 dim floats, 4 per load ----
+  const rsrc_t r_w = make_rsrc(w_ik, (uint32_t)(dim * idx_dim * 4));
+  u32x4_t wl[GQ];
+#pragma unroll
+  for (int i = 0; i < GQ; ++i) {
+    const int c = tid + 256 * i, k = c >> 2, j = c & 3;
+    wl[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                            r_w, (uint32_t)((k * idx_dim + col0 + 4 * j) * 4), 0, 0));
+  }
+  // ---- this lane's row: codes and scale values of its k-slot's groups ----
+  const int64_t r = r0 + 16 * wv + (l % 16);
+  const bool valid = r < rows;
+  const int q = l / 16;
+  const int64_t rc = valid ? r : rows - 1;     // a row in range (its codes are masked)
+  const int64_t d = dst_row ? dst_row[rc] : rc;
+  uint32_t cw[2 * GQ];
+  float sf[GQ];
+  const uint8_t *crow = codes + d * (dim / 2) + q * (kq / 2);
+  const uint8_t *srow = scales + d * (dim / kGroup) + q * GQ;
+#pragma unroll
+  for (int g = 0; g < GQ; ++g) {
+    const uint2 p = *reinterpret_cast<const uint2 *>(crow + 8 * g);
+    cw[2 * g] = valid ? p.x : 0u;
+    cw[2 * g + 1] = valid ? p.y : 0u;
+    sf[g] = e4m3_pos_value(srow[g]);
+  }
+  // ---- W_ik columns to LDS as [kk / 4][q][n][kk % 4]: a lane reads 4 channels at once ----
+#pragma unroll
+  for (int i = 0; i < GQ; ++i) {
+    const int c = tid + 256 * i, k = c >> 2, j = c & 3;
+    const int qq = k / kq, kk = k - qq * kq;
+    float *dst = &ws[(((kk >> 2) * 4 + qq) * 16 + 4 * j) * 4 + (kk & 3)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[4 * e] = __uint_as_float(wl[i][e]);
+  }
+  __syncthreads();
+  if (r0 + 16 * wv >= rows) return;
+  // ---- Y tile = DQ4 (16 rows x dim) x W (dim x 16 columns), fp64 ----
+  // the next group's weights are read from LDS while the current group's
+  // products run
+  double4_t acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = (double4_t){0.0, 0.0, 0.0, 0.0};
+  const float *wcol = ws + (q * 16 + (l % 16)) * 4;
+  u32x4_t wn[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) wn[h] = *reinterpret_cast<const u32x4_t *>(wcol + h * 256);
+#pragma unroll
+  for (int g = 0; g < GQ; ++g) {
+    u32x4_t w4[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) w4[h] = wn[h];
+    if (g + 1 < GQ) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) wn[h] = *reinterpret_cast<const u32x4_t *>(wcol + (4 * (g + 1) + h) * 256);
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {              // channels 16 g + 4 h .. + 3
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        // E2M1 pair (exact, unit scale) times the group's scale: exact in fp32
+        const float2_t e = e2m1x2_to_f32(cw[2 * g + h / 2], 2 * (h % 2) + p);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const double a = (double)(e[u] * sf[g]);
+          const double bw = (double)__uint_as_float(w4[h][2 * p + u]);
+          acc[2 * p + u] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bw, acc[2 * p + u], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // lane l holds rows l / 16 + 4 i of column l % 16
+  float *yw = yk + wv * 256;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    yw[(l / 16 + 4 * i) * 16 + l % 16] = (float)(((acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i])) + 0.0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // ---- encode each row's 16 key columns (one FP4 group) ----
+  if (l < 16 && valid) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = yw[l * 16 + i];
+    uint2 packed;
+    uint8_t sb;
+    encode_group(v, &packed, &sb);
+    *reinterpret_cast<uint2 *>(ik_codes + d * (idx_dim / 2) + ct * 8) = packed;
+    ik_scales[d * cgs + ct] = sb;
+  }
+}
+
 // Compressor (ratio r) fused with the FP4 write.  Entry j is fp32(W_c^T
 // [x_rj; ...; x_rj+r-1]) (P4 section 二; P5 section "CSA2注意力": adjacent
 // entries do not overlap and no position term is added).  The r token rows
@@ -452,6 +590,26 @@ void derive_mfma(const void *x, int64_t rows, int dim, const int64_t *dst_row, u
   // columns per workgroup: the largest tile count (up to 8) dividing the key's 16-column groups
   const int cgs = idx_dim / kGroup;
   const int ct = (cgs % 8 == 0) ? 8 : (cgs % 4 == 0) ? 4 : (cgs % 2 == 0) ? 2 : 1;
+  // many rows (dim 64, 128, 256 or 512): the rows are encoded (T = float or
+  // bf16) and their keys derived from the cache, 64 rows and one key group
+  // per workgroup
+  if (rows > 64 && (dim == 64 || dim == 128 || dim == 256 || dim == 512)) {
+    if constexpr (!__is_same(T, uint8_t)) {
+      const dim3 eg((unsigned)((rows * (dim / kGroup) + 255) / 256));
+      CSA2_TIMED_LAUNCH(kTimedWrite, k_quantize_fp4<T>, eg, dim3(256), stream, (const T *)x, rows, dim, dst_row,
+                        codes, scales);
+    }
+    const int64_t nq = ((rows + 63) / 64 + 7) / 8 * 8;
+#define CSA2_TILES_LAUNCH(GQ)                                                                                  \
+  CSA2_TIMED_LAUNCH(kTimedWrite, (k_derive_tiles<GQ>), dim3((unsigned)(nq * cgs)), dim3(256), stream, rows, dim, \
+                    dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales)
+    if (dim == 64) CSA2_TILES_LAUNCH(1);
+    else if (dim == 128) CSA2_TILES_LAUNCH(2);
+    else if (dim == 256) CSA2_TILES_LAUNCH(4);
+    else CSA2_TILES_LAUNCH(8);
+#undef CSA2_TILES_LAUNCH
+    return;
+  }
   // few rows: split the channels over 8 waves per tile instead (dim % 32 == 0)
   const bool few = rows <= 64 && dim % 32 == 0;
   const dim3 grid((unsigned)((rows + kDeriveRows - 1) / kDeriveRows), (unsigned)(few ? cgs : cgs / ct));

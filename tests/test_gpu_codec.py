@@ -92,12 +92,14 @@ def test_quantize_bf16_input_and_scattered_rows():
 @pytest.mark.parametrize("dim,di,rows", [(128, 64, 2000), (512, 128, 2000), (256, 256, 2000), (512, 128, 5),
                                          (512, 128, 1024), (128, 64, 3),
                                          (512, 32, 1500), (512, 64, 1500), (96, 32, 1100),
-                                         (256, 256, 7), (512, 32, 9)])
+                                         (256, 256, 7), (512, 32, 9), (64, 32, 200), (192, 64, 333),
+                                         (512, 128, 65), (512, 128, 4096)])
 def test_derive_indexer_key_bit_exact(dim, di, rows):
-    # dim <= 512 runs the fp64 matrix-core kernel: up to 64 rows with the
-    # channels split over 4 waves per 16-column tile, more with 1, 2, 4 or 8
-    # tiles per workgroup (32 .. 256 key columns); 16-row workgroups leave a
-    # ragged last one for every row count here, 96 channels a ragged slice.
+    # dim <= 512 runs the fp64 matrix-core kernels: up to 64 rows with the
+    # channels split over 8 waves per 16-column tile; more rows (dim a
+    # multiple of 64) with 64 rows and one key group per workgroup, else
+    # 16 rows and 1, 2, 4 or 8 key groups per workgroup (96 channels).
+    # Every row count here leaves a ragged last tile or row quad.
     announce("derive indexer key", dim, di, rows)
     x = synth.main_kv_rows(0, 0, 0, rows, dim)
     w = synth.w_ik(0, dim, di)
@@ -133,3 +135,31 @@ def test_quantize_full_cache_shape_sample():
     rc, rs = codec.fp4_encode(x)
     assert np.array_equal(h(scales), rs)
     assert np.array_equal(h(codes), rc)
+
+
+def test_derive_bf16_scattered_and_adversarial_rows():
+    # the 64-row tiles with bf16 input, scattered destination rows and the
+    # adversarial groups (saturating, subnormal-scale, exact-midpoint values)
+    announce("derive bf16 + dst_row + adversarial")
+    rng = np.random.default_rng(34)
+    dim, di = 512, 128
+    xf = np.concatenate([rng.standard_normal((300, dim)).astype(np.float32), _adversarial_rows(dim)])
+    xf = np.clip(xf, -3.0e38, 3.0e38)          # finite in bf16
+    bits = synth.f32_to_bf16_bits(xf).reshape(xf.shape)
+    xb = synth.bf16_bits_to_f32(bits)
+    n = xb.shape[0]
+    dst = rng.permutation(2 * n)[:n].astype(np.int64)
+    w = synth.w_ik(1, dim, di)
+    codes, scales = empty_u8(2 * n, dim // 2), empty_u8(2 * n, dim // 16)
+    ikc, iks = empty_u8(2 * n, di // 2), empty_u8(2 * n, di // 16)
+    for z in (codes, scales, ikc, iks):
+        z.fill_(0x5A)
+    csa2.csa2_quantize_fp4(t(bits).view(torch.bfloat16), codes, scales, dst_row=t(dst),
+                           w_ik=t(w.astype(np.float32)), ik_codes=ikc, ik_scales=iks)
+    rc, rs = codec.fp4_encode(xb)
+    kc, ks = codec.indexer_key(rc, rs, w)
+    untouched = np.setdiff1d(np.arange(2 * n), dst)
+    for got, want in ((codes, rc), (scales, rs), (ikc, kc), (iks, ks)):
+        g = h(got)
+        assert np.array_equal(g[dst], want)
+        assert np.all(g[untouched] == 0x5A)
