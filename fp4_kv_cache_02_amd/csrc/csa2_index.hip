@@ -32,9 +32,10 @@ constexpr int kRescoreEntries = 64;              // pool blocks per re-score wor
 // kernels
 // ---------------------------------------------------------------------------
 
+// Zero n words from p, 16 bytes per thread (p 16-byte aligned, n % 4 == 0).
 __global__ void k_zero_u32(uint32_t *__restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+  if (4 * i < n) reinterpret_cast<uint4 *>(p)[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Radix digit search shared by the selection kernels: s_hist[256] holds the
@@ -1088,7 +1089,7 @@ static int index_pool_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
   int32_t *tie = reinterpret_cast<int32_t *>(base + L.tie);
 
   // hist, counters and fine are adjacent: clear them with one fill kernel
-  const int64_t nz = (int64_t)((L.sure - L.hist) / sizeof(uint32_t));
+  const int64_t nz = (int64_t)((L.sure - L.hist) / sizeof(uint32_t));   // a multiple of 64 (256-byte offsets)
   const int64_t nbq = (idx.max_len + kBlock - 1) / kBlock;   // blocks of the longest sequence
   if (qs.run >= 2) {
     // queries in runs of one sequence: every streamed indexer entry is scored
@@ -1100,14 +1101,14 @@ static int index_pool_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
       st = launch_block_select(bmax, L.nb_max, nbq > 0 ? nbq : 1, idx, qs, P, pool_out, pool_count, stream);
       if (st != CSA2_OK) return st;
     } else {
-      hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
+      hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz / 4 + 255) / 256)), dim3(256), 0, stream, hist, nz);
       hipLaunchKernelGGL(k_bmax_hist, dim3((unsigned)((nbq + kFilterBlocks - 1) / kFilterBlocks), qs.m), dim3(256),
                          0, stream, bmax, L.nb_max, idx.seq_len, qs.seq, qs.pos, idx.ratio, hist, L.hist_rep);
       pool_from_hist(idx, qs, P, nbq, L, bmax, hist, counters, sure, tie, pool_out, pool_count, stream);
     }
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
   }
-  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
+  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz / 4 + 255) / 256)), dim3(256), 0, stream, hist, nz);
   if (idx.max_len > 0) {
     auto chunks_of = [&](int chunk) { return (idx.max_len + chunk - 1) / chunk; };
 #define CSA2_SCAN(T)                                                                                        \
