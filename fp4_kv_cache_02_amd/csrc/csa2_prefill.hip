@@ -71,9 +71,13 @@ CSA2_DEV void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int DI, int RPQ>
+// RT_: row tiles held by every wave (0: the default, 8, or 4 for 256 channels);
+// fewer when the queries come in short runs of one sequence, so that a
+// workgroup's queries belong to one run (no pass scores rows of other
+// sequences' queries)
+template <int DI, int RPQ, int RT_ = 0>
 struct MqShape {
-  static constexpr int RT = (DI == 256) ? 4 : 8;  // row tiles held by every wave
+  static constexpr int RT = RT_ ? RT_ : (DI == 256) ? 4 : 8;
   static constexpr int QB = RT * 16 / RPQ;        // queries per workgroup
   static constexpr int NG = QB / 4;               // groups of four queries
   static constexpr int TPG = RPQ / 4;             // row tiles per group
@@ -120,7 +124,7 @@ CSA2_DEV bool lane_stores(int i) { return NG == 4 ? (i & 2) == 0 : NG == 2 ? (i 
 // Workgroup y of a query block takes the column tiles [y*ct, (y+1)*ct) of
 // every pass (ct = 0: all of them), so a few query blocks - the tokens of a
 // multi-token decode - still spread over the chip.
-template <int DI, int RPQ>
+template <int DI, int RPQ, int RT>
 __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__restrict__ codes,
                                                            const uint8_t *__restrict__ scales,
                                                            const int64_t *__restrict__ seq_start,
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void k_score_mq(const uint8_t *__res
                                                            const uint16_t *__restrict__ q_idx,
                                                            const float *__restrict__ w_idx, int H,
                                                            float *__restrict__ bmax, int64_t nb_stride, int ct) {
-  using S = MqShape<DI, RPQ>;
+  using S = MqShape<DI, RPQ, RT>;
   constexpr int kNone = 0x7FFFFFFF;
   __shared__ int s_seq[S::QB], s_vis[S::QB];
   __shared__ MqTile<DI> ring[kMqWaves][kMqRing];
@@ -381,20 +385,46 @@ static FlatWs flat_ws_layout(int64_t max_len, int m, int top_k) {
 size_t flat_ws_bytes(int64_t max_len, int m, int top_k) { return flat_ws_layout(max_len, m, top_k).total; }
 
 // Column chunks: enough workgroups to fill the chip when the query blocks
-// alone do not (a multi-token decode), chunks of at least 64 tiles.
-template <int DI, int RPQ>
+// alone do not (a multi-token decode), chunks of at least 64 tiles; with
+// fewer row tiles a workgroup needs fewer registers and more of them fit a
+// CU (up to 4 per CU at 2 row tiles).
+template <int DI, int RPQ, int RT>
 static void launch_score_mq(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
                             const float *w_idx, int heads, float *bmax, int64_t nb_stride, hipStream_t stream) {
-  using S = MqShape<DI, RPQ>;
+  using S = MqShape<DI, RPQ, RT>;
   const int qb = (qs.m + S::QB - 1) / S::QB;
   const int64_t tiles = (idx.max_len + 15) / 16;
+  const int64_t target = 256 * (8 / S::RT);   // 256 workgroups, 512 at 4 row tiles, 1,024 at 2
   int chunks = 1;
-  while ((int64_t)qb * chunks < 256 && tiles / (2 * chunks) >= 64) chunks *= 2;
+  while ((int64_t)qb * chunks < target && tiles / (2 * chunks) >= 64) chunks *= 2;
   const int ct = chunks > 1 ? (int)((tiles + chunks - 1) / chunks) : 0;
   const dim3 grid((unsigned)qb, (unsigned)chunks);
-  CSA2_TIMED_LAUNCH(kTimedScan, (k_score_mq<DI, RPQ>), grid, dim3(64 * kMqWaves), stream, idx.codes, idx.scales,
-                    idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, qs.m, q_idx, w_idx, heads, bmax,
-                    nb_stride, ct);
+  CSA2_TIMED_LAUNCH(kTimedScan, (k_score_mq<DI, RPQ, RT>), grid, dim3(64 * kMqWaves), stream, idx.codes,
+                    idx.scales, idx.seq_start, idx.seq_len, idx.ratio, qs.seq, qs.pos, qs.m, q_idx, w_idx, heads,
+                    bmax, nb_stride, ct);
+}
+
+// Row tiles per wave from the run hint: a workgroup holds QB = 16 RT / RPQ
+// queries, so runs of up to 4 (8) tokens of 8 heads take 2 (4) row tiles and
+// one run per workgroup; 16 heads take 4 row tiles for runs of up to 4.
+template <int DI, int RPQ>
+static void launch_score_run(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
+                             const float *w_idx, int heads, float *bmax, int64_t nb_stride, hipStream_t stream) {
+  constexpr int RTD = MqShape<DI, RPQ>::RT;
+  const int run = qs.run;
+  if constexpr (RPQ == 8) {
+    if (run >= 2 && run <= 4) {
+      launch_score_mq<DI, RPQ, 2>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      return;
+    }
+  }
+  if constexpr (RTD > 4) {
+    if (run >= 2 && run <= 4 * 16 / RPQ) {
+      launch_score_mq<DI, RPQ, 4>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      return;
+    }
+  }
+  launch_score_mq<DI, RPQ, RTD>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
 }
 
 int launch_score_blocks(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
@@ -403,16 +433,16 @@ int launch_score_blocks(const csa2_fp4_cache &idx, const csa2_queries &qs, const
   const bool wide = heads > 8;
   switch (idx.dim) {
     case 64:
-      if (wide) launch_score_mq<64, 16>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
-      else launch_score_mq<64, 8>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      if (wide) launch_score_run<64, 16>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      else launch_score_run<64, 8>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
       break;
     case 128:
-      if (wide) launch_score_mq<128, 16>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
-      else launch_score_mq<128, 8>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      if (wide) launch_score_run<128, 16>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      else launch_score_run<128, 8>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
       break;
     case 256:
-      if (wide) launch_score_mq<256, 16>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
-      else launch_score_mq<256, 8>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      if (wide) launch_score_run<256, 16>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
+      else launch_score_run<256, 8>(idx, qs, q_idx, w_idx, heads, bmax, nb_stride, stream);
       break;
     default:
       return CSA2_ERR_UNSUPPORTED;

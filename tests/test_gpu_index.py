@@ -127,25 +127,44 @@ def test_index_c4_full_oracle_pass(shape):
         _check_query(rc, rs, starts[sq], vis, qf[i], wi[i], P, K, gpool[i], gcnt[i], gtopk[i], gsc[i])
 
 
-@pytest.mark.parametrize("shape", ["decode_4tok_64k", "replay_128tok_256k", "decode_4tok_1m"])
+@pytest.mark.parametrize("shape", ["decode_4tok_64k", "replay_128tok_256k", "decode_4tok_1m", "decode_2tok_64k",
+                                   "decode_8tok_64k", "decode_4tok_16heads_64k", "interleaved_run_hint_64k",
+                                   "decode_3tok_dim256_64k"])
 def test_index_full_runs_of_tokens(shape):
     """Queries in runs of consecutive tokens of one sequence (run hint >= 2):
     several decode tokens per sequence (drafted positions verified together)
     and a replayed window of 128 tokens with a pool per query.  Every streamed
-    indexer entry is scored against all the queries of its sequence at once;
-    the pool comes from the block maxima directly (up to 65,536 blocks) or
-    through the block-maximum histogram (1M entries).  Each query's pool and
-    Top-K are compared element by element with a full fp64 oracle pass,
-    modulo the near-tie band.  Caches are raw FP4 bytes."""
+    indexer entry is scored against all the queries of its sequence at once
+    (a workgroup holds one run of up to 4 or 8 tokens: 2 or 4 row tiles, or
+    16 queries for longer runs); the pool comes from the block maxima
+    directly (up to 65,536 blocks) or through the block-maximum histogram (1M
+    entries).  A hint that the queries do not keep (sequences interleaved)
+    changes nothing but speed.  Each query's pool and Top-K are compared
+    element by element with a full fp64 oracle pass, modulo the near-tie
+    band.  Caches are raw FP4 bytes."""
+    di, H, P, K = 128, 8, 2048, 512
     if shape == "decode_4tok_64k":
         lens, cfg, run = [65536, 40000], 120, 4
     elif shape == "replay_128tok_256k":
         lens, cfg, run = [262144], 121, 128
-    else:
+    elif shape == "decode_4tok_1m":
         lens, cfg, run = [1 << 20, 700001], 122, 4
+    elif shape == "decode_2tok_64k":
+        lens, cfg, run = [65536, 30001, 50000], 123, 2
+    elif shape == "decode_8tok_64k":
+        lens, cfg, run = [65536, 47000], 124, 8
+    elif shape == "decode_4tok_16heads_64k":
+        lens, cfg, run, H = [65536, 33333], 125, 4, 16
+    elif shape == "interleaved_run_hint_64k":
+        lens, cfg, run = [65536, 52000], 126, 4
+    else:
+        lens, cfg, run, di, K = [65536, 20000, 41111], 127, 3, 256, 256
     q_seq = [s for s in range(len(lens)) for _ in range(run)]
     q_pos = [lens[s] - run + k for s in range(len(lens)) for k in range(run)]
-    di, H, P, K = 128, 8, 2048, 512
+    if shape == "interleaved_run_hint_64k":    # the hint says runs of 4; the sequences alternate
+        order = sorted(range(len(q_seq)), key=lambda i: (i % run, i // run))
+        q_seq = [q_seq[i] for i in order]
+        q_pos = [q_pos[i] for i in order]
     announce("index runs of tokens", shape)
     rc, rs = synth.fp4_bytes(cfg, 0, sum(lens), di)
     starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
