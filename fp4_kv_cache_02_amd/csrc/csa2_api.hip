@@ -322,21 +322,43 @@ static int check_group(const csa2_group_desc *g) {
   return CSA2_OK;
 }
 
+// A Full group's write path.  When the group's pool comes from the first
+// scan, the write launch also clears the index workspace's histograms and
+// counters (which the scan needs zeroed), so the index path skips its own
+// fill launch; returns whether it did.
+static int enqueue_group_write(const csa2_group_desc *g, void *iws, hipStream_t s, bool *cleared) {
+  *cleared = false;
+  if (g->first_mode != CSA2_MODE_FULL || g->new_rows <= 0) return CSA2_OK;
+  uint32_t *zero = nullptr;
+  int64_t words = 0;
+  if (g->pool_blocks > 0 && g->qs.m > 0) {
+    const IndexWs L = index_ws_layout(g->idx.max_len, g->qs.m, g->pool_blocks, g->top_k);
+    zero = reinterpret_cast<uint32_t *>(static_cast<char *>(iws) + L.hist);
+    words = (int64_t)((L.sure - L.hist) / sizeof(uint32_t));
+  }
+  const int st = launch_quantize_fp4(g->new_kv, g->new_kv_dtype, g->new_rows, g->kv.dim, g->new_dst_row,
+                                     g->kv.codes, g->kv.scales, g->w_ik, g->idx.dim, g->idx.codes, g->idx.scales, s,
+                                     zero, words);
+  *cleared = st == CSA2_OK && zero != nullptr;
+  return st;
+}
+
 // The group's write path and its first layer's indexer (m > 0).
 static int enqueue_group_index(const csa2_group_desc *g, void *iws, hipStream_t s) {
-  int st = CSA2_OK;
-  if (g->first_mode == CSA2_MODE_FULL && g->new_rows > 0) {
-    st = launch_quantize_fp4(g->new_kv, g->new_kv_dtype, g->new_rows, g->kv.dim, g->new_dst_row, g->kv.codes,
-                             g->kv.scales, g->w_ik, g->idx.dim, g->idx.codes, g->idx.scales, s);
-    if (st) return st;
-  }
+  bool cleared = false;
+  int st = enqueue_group_write(g, iws, s, &cleared);
+  if (st) return st;
   if (g->first_mode == CSA2_MODE_FULL) {
     if (g->pool_blocks == 0)
       st = launch_index_flat(g->idx, g->qs, g->q_idx, g->w_idx, g->idx_heads, g->top_k, g->topk, g->topk_score,
                              iws, s);
-    else
-      st = launch_index_full(g->idx, g->qs, g->q_idx, g->w_idx, g->idx_heads, g->pool_blocks, g->top_k, g->pool,
-                             g->pool_count, g->topk, g->topk_score, iws, s);
+    else if ((st = launch_index_pool(g->idx, g->qs, g->q_idx, g->w_idx, g->idx_heads, g->pool_blocks, g->top_k,
+                                     g->pool, g->pool_count, iws, s, cleared)) == CSA2_OK) {
+      const IndexWs L = index_ws_layout(g->idx.max_len, g->qs.m, g->pool_blocks, g->top_k);
+      const SelSet set{g->q_idx, g->w_idx, g->topk, g->topk_score};
+      st = launch_rescore_select(g->idx, g->qs, g->idx_heads, g->pool, g->pool_count, g->pool_blocks, g->top_k,
+                                 &set, 1, reinterpret_cast<float *>(static_cast<char *>(iws) + L.pscore), s);
+    }
   } else {
     st = launch_reindex(g->idx, g->qs, g->q_idx, g->w_idx, g->idx_heads, g->pool, g->pool_count, g->pool_blocks,
                         g->top_k, g->topk, g->topk_score, iws, s);
@@ -506,17 +528,14 @@ int32_t csa2_group_steps(const csa2_group_desc *groups, int32_t n_groups, void *
         }
     }
     if (g->qs.m > 0) {
-      if (g->first_mode == CSA2_MODE_FULL && g->new_rows > 0) {
-        st = launch_quantize_fp4(g->new_kv, g->new_kv_dtype, g->new_rows, g->kv.dim, g->new_dst_row, g->kv.codes,
-                                 g->kv.scales, g->w_ik, g->idx.dim, g->idx.codes, g->idx.scales, s);
-        if (st) return st;
-      }
+      bool cleared = false;
+      if ((st = enqueue_group_write(g, iws, s, &cleared))) return st;
       if (g->first_mode == CSA2_MODE_FULL && g->pool_blocks == 0) {
         st = launch_index_flat(g->idx, g->qs, g->q_idx, g->w_idx, g->idx_heads, g->top_k, g->topk, g->topk_score,
                                iws, s);
       } else if (g->first_mode == CSA2_MODE_FULL) {
         st = launch_index_pool(g->idx, g->qs, g->q_idx, g->w_idx, g->idx_heads, g->pool_blocks, g->top_k, g->pool,
-                               g->pool_count, iws, s);
+                               g->pool_count, iws, s, cleared);
       }
       if (st) return st;
     }

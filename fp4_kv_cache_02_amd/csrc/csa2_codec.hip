@@ -7,6 +7,8 @@
 // projected from the main-KV entry (P4 section 二; P5 section "CSA2注意力").
 #include "csa2_internal.hpp"
 
+#include <algorithm>
+
 namespace csa2 {
 
 template <typename T>
@@ -177,12 +179,23 @@ constexpr int kDeriveMaxDim = 512;
 // T = uint8_t derives the keys of rows already in the cache instead: their
 // codes and scales are read from the destination rows (nothing is encoded or
 // written to the main planes, x is unused).
+//
+// Workgroups with blockIdx.x past the row tiles clear zero[0 .. zero_n)
+// (16-byte words) instead: a range the caller needs zeroed before its next
+// launch, cleared here rather than by a launch of its own.
 template <typename T, int CT, int KS>
 __global__ __launch_bounds__(64 * CT * KS) void k_quantize_fp4_derive_mfma(
     const T *__restrict__ x, int64_t rows, int dim, const int64_t *__restrict__ dst_row, uint8_t *__restrict__ codes,
     uint8_t *__restrict__ scales, const float *__restrict__ w_ik, int idx_dim, uint8_t *__restrict__ ik_codes,
-    uint8_t *__restrict__ ik_scales) {
+    uint8_t *__restrict__ ik_scales, uint4 *__restrict__ zero, int64_t zero_n) {
   constexpr int NT = 64 * CT * KS;
+  const int64_t row_tiles = (rows + kDeriveRows - 1) / kDeriveRows;
+  if ((int64_t)blockIdx.x >= row_tiles) {
+    const int64_t zb = ((int64_t)blockIdx.x - row_tiles) * gridDim.y + blockIdx.y;
+    const int64_t zstride = ((int64_t)gridDim.x - row_tiles) * gridDim.y * NT;
+    for (int64_t i = zb * NT + threadIdx.x; i < zero_n; i += zstride) zero[i] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
   constexpr int DS = kDeriveMaxDim + 1;                 // fp64 row stride: rows fall in different banks
   constexpr int WPL = kDeriveMaxDim / 4 / KS;           // W_ik values per lane (one per k-step)
   __shared__ double dq[kDeriveRows * DS];
@@ -584,9 +597,23 @@ __global__ __launch_bounds__(256) void k_dequant_fp4(const uint8_t *__restrict__
 // ---------------------------------------------------------------------------
 
 // The fp64-MFMA derive (dim <= kDeriveMaxDim); T = uint8_t: keys of rows already in the cache.
+// Clear n16 16-byte words (one per thread).
+__global__ __launch_bounds__(256) void k_zero16(uint4 *__restrict__ p, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n16) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+static void launch_zero16(uint32_t *zero, int64_t zero_words, hipStream_t stream) {
+  const int64_t n16 = zero_words / 4;
+  if (n16 > 0)
+    hipLaunchKernelGGL(k_zero16, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<uint4 *>(zero), n16);
+}
+
 template <typename T>
 void derive_mfma(const void *x, int64_t rows, int dim, const int64_t *dst_row, uint8_t *codes, uint8_t *scales,
-                 const float *w_ik, int idx_dim, uint8_t *ik_codes, uint8_t *ik_scales, hipStream_t stream) {
+                 const float *w_ik, int idx_dim, uint8_t *ik_codes, uint8_t *ik_scales, hipStream_t stream,
+                 uint32_t *zero = nullptr, int64_t zero_words = 0) {
   // columns per workgroup: the largest tile count (up to 8) dividing the key's 16-column groups
   const int cgs = idx_dim / kGroup;
   const int ct = (cgs % 8 == 0) ? 8 : (cgs % 4 == 0) ? 4 : (cgs % 2 == 0) ? 2 : 1;
@@ -608,14 +635,20 @@ void derive_mfma(const void *x, int64_t rows, int dim, const int64_t *dst_row, u
     else if (dim == 256) CSA2_TILES_LAUNCH(4);
     else CSA2_TILES_LAUNCH(8);
 #undef CSA2_TILES_LAUNCH
+    launch_zero16(zero, zero_words, stream);
     return;
   }
   // few rows: split the channels over 8 waves per tile instead (dim % 32 == 0)
   const bool few = rows <= 64 && dim % 32 == 0;
-  const dim3 grid((unsigned)((rows + kDeriveRows - 1) / kDeriveRows), (unsigned)(few ? cgs : cgs / ct));
+  // spare workgroups past the row tiles clear the zero range: about 32 KB each
+  const unsigned gy = (unsigned)(few ? cgs : cgs / ct);
+  const int64_t zero_n = zero ? zero_words / 4 : 0;
+  const int64_t zx = zero_n > 0 ? std::max<int64_t>(1, zero_n / (2048 * (int64_t)gy)) : 0;
+  const dim3 grid((unsigned)((rows + kDeriveRows - 1) / kDeriveRows + zx), gy);
+  uint4 *zp = reinterpret_cast<uint4 *>(zero);
 #define CSA2_MFMA_LAUNCH(CT, KS)                                                                              \
   CSA2_TIMED_LAUNCH(kTimedWrite, (k_quantize_fp4_derive_mfma<T, CT, KS>), grid, dim3(64 * CT * KS), stream, \
-                    (const T *)x, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales)
+                    (const T *)x, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales, zp, zero_n)
   if (few) CSA2_MFMA_LAUNCH(1, 8);
   else if (ct == 8) CSA2_MFMA_LAUNCH(8, 1);
   else if (ct == 4) CSA2_MFMA_LAUNCH(4, 1);
@@ -626,8 +659,9 @@ void derive_mfma(const void *x, int64_t rows, int dim, const int64_t *dst_row, u
 
 int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const int64_t *dst_row,
                         uint8_t *codes, uint8_t *scales, const float *w_ik, int idx_dim, uint8_t *ik_codes,
-                        uint8_t *ik_scales, hipStream_t stream) {
-  if (rows == 0) return CSA2_OK;
+                        uint8_t *ik_scales, hipStream_t stream, uint32_t *zero, int64_t zero_words) {
+  if (rows == 0 || !w_ik || dim > kDeriveMaxDim) launch_zero16(zero, zero_words, stream);
+  if (rows == 0) return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
   if (!w_ik) {
     const int64_t groups = rows * (dim / kGroup);
     const dim3 grid((unsigned)((groups + 255) / 256));
@@ -639,9 +673,11 @@ int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const
                          dst_row, codes, scales);
   } else if (dim <= kDeriveMaxDim) {
     if (x_dtype == CSA2_F32)
-      derive_mfma<float>(x, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales, stream);
+      derive_mfma<float>(x, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales, stream, zero,
+                         zero_words);
     else
-      derive_mfma<uint16_t>(x, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales, stream);
+      derive_mfma<uint16_t>(x, rows, dim, dst_row, codes, scales, w_ik, idx_dim, ik_codes, ik_scales, stream, zero,
+                            zero_words);
   } else {
     const int rb = kDeriveLdsFloats / dim;
     const dim3 grid((unsigned)((rows + rb - 1) / rb));

@@ -1079,7 +1079,7 @@ static void pool_from_hist(const csa2_fp4_cache &idx, const csa2_queries &qs, in
 template <int DI>
 static int index_pool_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx,
                            const float *w_idx, int heads, int P, int K, int32_t *pool_out, int32_t *pool_count,
-                           void *ws, hipStream_t stream) {
+                           void *ws, hipStream_t stream, bool cleared) {
   const IndexWs L = index_ws_layout(idx.max_len, qs.m, P, K);
   char *base = static_cast<char *>(ws);
   float *bmax = reinterpret_cast<float *>(base + L.bmax);
@@ -1101,14 +1101,16 @@ static int index_pool_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
       st = launch_block_select(bmax, L.nb_max, nbq > 0 ? nbq : 1, idx, qs, P, pool_out, pool_count, stream);
       if (st != CSA2_OK) return st;
     } else {
-      hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz / 4 + 255) / 256)), dim3(256), 0, stream, hist, nz);
+      if (!cleared)
+        hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz / 4 + 255) / 256)), dim3(256), 0, stream, hist, nz);
       hipLaunchKernelGGL(k_bmax_hist, dim3((unsigned)((nbq + kFilterBlocks - 1) / kFilterBlocks), qs.m), dim3(256),
                          0, stream, bmax, L.nb_max, idx.seq_len, qs.seq, qs.pos, idx.ratio, hist, L.hist_rep);
       pool_from_hist(idx, qs, P, nbq, L, bmax, hist, counters, sure, tie, pool_out, pool_count, stream);
     }
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
   }
-  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz / 4 + 255) / 256)), dim3(256), 0, stream, hist, nz);
+  if (!cleared)
+    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz / 4 + 255) / 256)), dim3(256), 0, stream, hist, nz);
   if (idx.max_len > 0) {
     auto chunks_of = [&](int chunk) { return (idx.max_len + chunk - 1) / chunk; };
 #define CSA2_SCAN(T)                                                                                        \
@@ -1128,11 +1130,14 @@ static int index_pool_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
 
 int launch_index_pool(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx, const float *w_idx,
                       int heads, int P, int K, int32_t *pool_out, int32_t *pool_count, void *ws,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool ws_cleared) {
   switch (idx.dim) {
-    case 64: return index_pool_impl<64>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, ws, stream);
-    case 128: return index_pool_impl<128>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, ws, stream);
-    case 256: return index_pool_impl<256>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, ws, stream);
+    case 64:
+      return index_pool_impl<64>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, ws, stream, ws_cleared);
+    case 128:
+      return index_pool_impl<128>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, ws, stream, ws_cleared);
+    case 256:
+      return index_pool_impl<256>(idx, qs, q_idx, w_idx, heads, P, K, pool_out, pool_count, ws, stream, ws_cleared);
     default: return CSA2_ERR_UNSUPPORTED;
   }
 }

@@ -9,9 +9,13 @@
 namespace csa2 {
 
 // ---- write path (csa2_codec.hip) ----
+// zero / zero_words: a 16-byte aligned range (zero_words % 4 == 0) that the
+// launch also clears - in spare workgroups of the write kernel when the rows
+// take the few-row kernel (the decode write), else with a fill kernel - so a
+// decode step's index workspace needs no fill launch of its own.
 int launch_quantize_fp4(const void *x, int x_dtype, int64_t rows, int dim, const int64_t *dst_row,
                         uint8_t *codes, uint8_t *scales, const float *w_ik, int idx_dim, uint8_t *ik_codes,
-                        uint8_t *ik_scales, hipStream_t stream);
+                        uint8_t *ik_scales, hipStream_t stream, uint32_t *zero = nullptr, int64_t zero_words = 0);
 // Compressor fused with the FP4 write (and the indexer keys of the written
 // rows when w_ik is given); dim <= 512, (ratio * d_in) % 32 == 0.
 int launch_compress_fp4(const uint16_t *tokens, int64_t entries, int ratio, int d_in, const uint16_t *w_c, int dim,
@@ -37,9 +41,11 @@ int launch_index_full(const csa2_fp4_cache &idx, const csa2_queries &qs, const u
                       const float *w_idx, int heads, int pool_blocks, int top_k, int32_t *pool_out,
                       int32_t *pool_count, int32_t *topk_out, float *topk_score, void *ws, hipStream_t stream);
 // The first part of launch_index_full alone: the scan and the pool (no Top-K).
+// ws_cleared: the workspace's [hist, sure) range (histograms, counters) is
+// already zero in stream order (cleared by the step's write launch).
 int launch_index_pool(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx, const float *w_idx,
                       int heads, int pool_blocks, int top_k, int32_t *pool_out, int32_t *pool_count, void *ws,
-                      hipStream_t stream);
+                      hipStream_t stream, bool ws_cleared = false);
 int launch_reindex(const csa2_fp4_cache &idx, const csa2_queries &qs, const uint16_t *q_idx, const float *w_idx,
                    int heads, const int32_t *pool_in, const int32_t *pool_count, int pool_blocks, int top_k,
                    int32_t *topk_out, float *topk_score, void *ws, hipStream_t stream);
