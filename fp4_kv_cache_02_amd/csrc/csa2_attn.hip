@@ -577,10 +577,12 @@ struct PvLds {
 // p values (f16) are rescaled by 2^(m_c - M) - exact, a power of two - and
 // accumulated on MFMA: Top-K chunks in one accumulator, window chunks (whose
 // p carry the lift 2^e) in another; O = (acc_main + 2^-e acc_win) / L.  The
-// loads of block b + 2 are issued while block b is multiplied (a ring of
-// three register buffers); blocks 0 and 1 are issued with the statistics.
+// loads of block b + 2 go into block b's registers once b is multiplied (a
+// ring of two register buffers, so that three waves fit a SIMD and every
+// workgroup of a 4-query, 20-layer batch is resident at once); blocks 0
+// and 1 are issued with the statistics.
 template <int D, int DS>
-__global__ __launch_bounds__(256) void k_attn_pv(int M, int H, int nmc, int nwc, const _Float16 *__restrict__ P,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_attn_pv(int M, int H, int nmc, int nwc, const _Float16 *__restrict__ P,
                                                  const float2 *__restrict__ stats, const int32_t *__restrict__ lift,
                                                  const uint8_t *__restrict__ g_codes,
                                                  const uint8_t *__restrict__ g_scales,
@@ -589,7 +591,6 @@ __global__ __launch_bounds__(256) void k_attn_pv(int M, int H, int nmc, int nwc,
   using Lds = PvLds<DS>;
   constexpr int NDT = DS / 16;
   constexpr int NT = kPvKeys / kChunk;                       // k-steps per block
-  constexpr int GPT = (kMaxChunks / 4 + 3) / 4;              // 4-chunk statistics groups per thread
   constexpr int NS = D / DS;                                  // dim slices
   const int nhg = (H + kPvHeads - 1) / kPvHeads;
   int m, k;   // query and (head group, slice) member
@@ -636,55 +637,79 @@ __global__ __launch_bounds__(256) void k_attn_pv(int M, int H, int nmc, int nwc,
   };
 
   // ---- issue: this thread's chunk statistics (head tid / 4; chunk groups
-  // 4 g .. 4 g + 3 for g = tid % 4 + 4 k), the window's lift, blocks 0, 1 ----
+  // 4 g .. 4 g + 3 for g = tid % 4 + 4 k, two groups at a time), the
+  // window's lift, blocks 0, 1 ----
   const int nblk = (nslots + kPvKeys - 1) / kPvKeys;
   const int hh = tid >> 2, q4 = tid & 3;
   const int kmax = (nchs + 15) / 16;                          // statistics groups per thread in use
-  float2 stv[GPT][4];
+  float2 sv[2][4];
+  auto load_stats = [&](int k0) {
 #pragma unroll
-  for (int k = 0; k < GPT; ++k) {
-    stv[k][0] = stv[k][1] = stv[k][2] = stv[k][3] = make_float2(-INFINITY, 0.0f);
-    if (k >= kmax) continue;   // uniform: only the groups that exist are loaded
-    const int g = q4 + 4 * k;
-    const uint32_t off = (hh < hn && 4 * g < nchs) ? (uint32_t)(hh * nchs + 4 * g) * 8u : kOutOfRange;
-    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r_st, off, 0, 0);
-    const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r_st, off == kOutOfRange ? off : off + 16u, 0, 0);
-    stv[k][0] = make_float2(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    stv[k][1] = make_float2(__uint_as_float(a[2]), __uint_as_float(a[3]));
-    stv[k][2] = make_float2(__uint_as_float(b[0]), __uint_as_float(b[1]));
-    stv[k][3] = make_float2(__uint_as_float(b[2]), __uint_as_float(b[3]));
-  }
+    for (int u = 0; u < 2; ++u) {
+      const int g = q4 + 4 * (k0 + u);
+      const uint32_t off = (k0 + u < kmax && hh < hn && 4 * g < nchs) ? (uint32_t)(hh * nchs + 4 * g) * 8u : kOutOfRange;
+      const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r_st, off, 0, 0);
+      const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r_st, off == kOutOfRange ? off : off + 16u, 0, 0);
+      sv[u][0] = make_float2(__uint_as_float(a[0]), __uint_as_float(a[1]));
+      sv[u][1] = make_float2(__uint_as_float(a[2]), __uint_as_float(a[3]));
+      sv[u][2] = make_float2(__uint_as_float(b[0]), __uint_as_float(b[1]));
+      sv[u][3] = make_float2(__uint_as_float(b[2]), __uint_as_float(b[3]));
+    }
+  };
+  load_stats(0);
   const int32_t ew_raw = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
       make_rsrc(lift + ((int64_t)li * M + m) * nchs, (uint32_t)(nchs * 4)), nmc * 4u, 0, 0);
-  Blk ba, bb, bc;
+  Blk ba, bb;
   load_block(0, ba);
   load_block(1, bb);
   // ---- per head: the largest reference M, the sum L, and each chunk's
-  // rescale 2^(m_c - M) (0 below the f16 range) ----
+  // rescale 2^(m_c - M) (0 below the f16 range).  The chunk maxima m_c are
+  // integers; the thread keeps a running maximum and a sum rescaled by exact
+  // powers of two, and parks its m_c in the V tile (free until the first
+  // block is decoded) for the rescales ----
+  float *const mpark = reinterpret_cast<float *>(L.vt);       // [chunk][head]
+  static_assert(kMaxChunks * kPvHeads * 4 <= (int)sizeof(L.vt), "chunk maxima fit the V tile");
   float lse2;
   {
-    auto valid = [&](int k, int i) { return hh < hn && 4 * (q4 + 4 * k) + i < nch; };
-    float mx = -INFINITY;
+    float mx = -INFINITY, sum = 0.0f;
+    auto fold = [&](int k0) {
 #pragma unroll
-    for (int k = 0; k < GPT; ++k)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (valid(k, i)) mx = fmaxf(mx, stv[k][i].x);
+        for (int i = 0; i < 4; ++i) {
+          const int cc = 4 * (q4 + 4 * (k0 + u)) + i;
+          const bool ok = hh < hn && cc < nch && sv[u][i].x != -INFINITY;
+          if (cc < nch) mpark[cc * kPvHeads + hh] = ok ? sv[u][i].x : -INFINITY;
+          if (ok) {
+            const float mc = sv[u][i].x;
+            if (mc > mx) {
+              sum = (mx == -INFINITY) ? 0.0f : ldexpf(sum, (int)(mx - mc));
+              mx = mc;
+            }
+            sum += ldexpf(sv[u][i].y, (int)(mc - mx));
+          }
+        }
+    };
+    fold(0);
+    for (int k0 = 2; k0 < kmax; k0 += 2) {   // more than 32 chunks per layer
+      load_stats(k0);
+      fold(k0);
+    }
+    const float mx_own = mx;
     mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-    float sum = 0.0f;
-#pragma unroll
-    for (int k = 0; k < GPT; ++k)
+    sum = (mx_own == -INFINITY) ? 0.0f : ldexpf(sum, (int)(mx_own - mx));
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    for (int k = 0; k < kmax; ++k)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int cc = 4 * (q4 + 4 * k) + i;
-        const bool ok = valid(k, i) && stv[k][i].x != -INFINITY;
-        const int sh = ok ? (int)(stv[k][i].x - mx) : -1000;    // an integer <= 0
-        sum += ok ? ldexpf(stv[k][i].y, sh) : 0.0f;
-        if (4 * (q4 + 4 * k) + i < nch) L.f[cc * kPvHeads + hh] = (sh >= -24) ? (_Float16)ldexpf(1.0f, sh) : (_Float16)0.0f;
+        if (cc >= nch) continue;
+        const float mc = mpark[cc * kPvHeads + hh];
+        const int sh = (mc != -INFINITY) ? (int)(mc - mx) : -1000;   // an integer <= 0
+        L.f[cc * kPvHeads + hh] = (sh >= -24) ? (_Float16)ldexpf(1.0f, sh) : (_Float16)0.0f;
       }
-    sum += __shfl_xor(sum, 1, 64);
-    sum += __shfl_xor(sum, 2, 64);
     if (q4 == 0) L.inv_l[hh] = (sum > 0.0f) ? 1.0f / sum : 0.0f;
     lse2 = (sum > 0.0f) ? mx + log2f(sum) : -INFINITY;
   }
@@ -697,9 +722,9 @@ __global__ __launch_bounds__(256) void k_attn_pv(int M, int H, int nmc, int nwc,
     aw[t] = am[t];
   }
   const bool active = 16 * wv < hn;
-  // block b: issue block b + 2 into `fut`, then decode `cur` and multiply
-  auto step = [&](int b, const Blk &cur, Blk &fut) {
-    load_block(b + 2, fut);
+  // block b: decode `cur` and multiply, then issue block b + 2 into the
+  // same registers (block b + 1's loads stay in flight meanwhile)
+  auto step = [&](int b, Blk &cur) {
     if (b >= nblk) return;
     __syncthreads();      // the rescales (first block) or the previous block's V reads are done
     {
@@ -736,11 +761,11 @@ __global__ __launch_bounds__(256) void k_attn_pv(int M, int H, int nmc, int nwc,
         }
       }
     }
+    load_block(b + 2, cur);
   };
-  for (int b = 0; b < nblk; b += 3) {
-    step(b, ba, bc);
-    step(b + 1, bb, ba);
-    step(b + 2, bc, bb);
+  for (int b = 0; b < nblk; b += 2) {
+    step(b, ba);
+    step(b + 1, bb);
   }
   // ---- output: lane (dim row, quad) holds heads 16 w + 4 quad + j ----
   if (active) {
