@@ -34,6 +34,8 @@
 // error <= 2^-11); everything else accumulates in fp32.
 #include "csa2_internal.hpp"
 
+#include <type_traits>
+
 namespace csa2 {
 
 constexpr int kKC = 64;    // keys per decoded tile (flash kernel)
@@ -380,7 +382,7 @@ struct QRaw {
 // ONE_TILE: at most 64 heads, one head tile per wave (its queries stay in
 // registers across the workgroup's chunks, with no second tile's registers).
 template <int D, bool QF32, bool ONE_TILE>
-__global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int nwc, const int32_t *__restrict__ q_seq,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONE_TILE ? 4 : 1))) void k_attn_logits(int M, int K, int nmc, int nwc, const int32_t *__restrict__ q_seq,
                                                      const int32_t *__restrict__ q_pos,
                                                      const int64_t *__restrict__ seq_start,
                                                      const int32_t *__restrict__ seq_len,
@@ -412,9 +414,11 @@ __global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int 
     return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_topk, (c < nmc && slot < K) ? slot * 4u : kOutOfRange, 0,
                                                          0);
   };
-  // a Top-K chunk's index load goes out first, beside the sequence lookup
-  // of query_rows (the row loads need both)
-  int32_t j_next = index_of(kLogitChunks * cp);
+  // the index loads of the workgroup's Top-K chunks go out first, beside the
+  // sequence lookup of query_rows (the row loads need both)
+  int32_t jc[kLogitChunks];
+#pragma unroll
+  for (int cc = 0; cc < kLogitChunks; ++cc) jc[cc] = index_of(kLogitChunks * cp + cc);
   const QueryRows qr = query_rows(seq_start, seq_len, ratio, q_seq, q_pos, m);
   const rsrc_t rq = make_rsrc(static_cast<const char *>(ly.q) + (int64_t)m * H * D * QE, (uint32_t)(H * D * QE));
   // the wave's head tiles: wv + 4 it for it < ntw
@@ -425,20 +429,41 @@ __global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int 
   QR qB_store[ONE_TILE ? 1 : 2];
   QR &qB = qB_store[ONE_TILE ? 0 : 1];
   q_load(0, qA);
-  // ---- the workgroup's chunks, one after another: the queries of a wave
-  // with one head tile stay in registers ----
+  // every Top-K chunk's key rows in flight at once (window chunks and slots
+  // past the list or the visible entries read out of range): one round trip
+  // to memory after the indices, not one per chunk
+  const rsrc_t r_kc = make_rsrc(kv_codes + qr.row0 * (D / 2), (uint32_t)(qr.vis * (D / 2)));
+  const rsrc_t r_ks = make_rsrc(kv_scales + qr.row0 * (D / 16), (uint32_t)(qr.vis * (D / 16)));
+  Fp4Piece<D, DP> pcm[kLogitChunks];
+  bool okm[kLogitChunks];
+#pragma unroll
   for (int cc = 0; cc < kLogitChunks; ++cc) {
+    const int c = kLogitChunks * cp + cc;
+    okm[cc] = c < nmc && kChunk * c + key < K && jc[cc] >= 0 && jc[cc] < qr.vis;
+    pcm[cc].load(r_kc, r_ks, okm[cc], (uint32_t)jc[cc], d0);
+  }
+  // the gathered copy of the Top-K rows: stores through a descriptor that
+  // drops them unless this layer makes the copy (no branch around a store,
+  // whose unknown count would make later waits wait for every store)
+  const int64_t gr = ((int64_t)ly.list * M + m) * Kp;
+  const rsrc_t r_gcw = make_rsrc(ly.gather ? g_codes + gr * (D / 2) : nullptr, ly.gather ? (uint32_t)(Kp * (D / 2)) : 0u);
+  const rsrc_t r_gsw = make_rsrc(ly.gather ? g_scales + gr * (D / 16) : nullptr, ly.gather ? (uint32_t)(Kp * (D / 16)) : 0u);
+  // ---- the workgroup's chunks, one after another: the queries of a wave
+  // with one head tile stay in registers.  MODE 1: every chunk of the pair
+  // is a Top-K chunk (one straight path, so the waits for the second
+  // chunk's rows need not wait for the first chunk's stores); MODE 2: Top-K
+  // or window chunks.  Returns false past the workgroup's last chunk ----
+  auto run_chunk = [&](int cc, auto mode_tag) -> bool {
+  constexpr int MODE = decltype(mode_tag)::value;
   const int c = kLogitChunks * cp + cc;
-  if (c >= nch) break;
-  const bool main_chunk = c < nmc;
-  if (!main_chunk && kChunk * (c - nmc) >= ly.window) break;   // past this layer's window (as are later chunks)
+  if (c >= nch) return false;
+  const bool main_chunk = MODE == 1 || c < nmc;
+  if (!main_chunk && kChunk * (c - nmc) >= ly.window) return false;   // past this layer's window (as are later chunks)
   const int slot = kChunk * c + key;
-  const int32_t j = j_next;
   if (cc > 0) {
     __syncthreads();                 // the previous chunk's reads of the key tile are done
     if (!ONE_TILE && ntw > 1) q_load(0, qA);
   }
-  if (cc + 1 < kLogitChunks && c + 1 < nch) j_next = index_of(c + 1);
 
   // ---- the key row (its index issued earlier); decode the chunk's 32 keys
   // into LDS ----
@@ -447,16 +472,9 @@ __global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int 
     *reinterpret_cast<u32x4_t *>(&L.kt[key * Lds::KT + d0 + 8 * u]) = v;
   };
   if (main_chunk) {
-    const bool ok = slot < K && j >= 0 && j < qr.vis;
-    ksv = ok ? 1.0f : 0.0f;
-    Fp4Piece<D, DP> pc;
-    pc.load(make_rsrc(kv_codes + qr.row0 * (D / 2), (uint32_t)(qr.vis * (D / 2))),
-            make_rsrc(kv_scales + qr.row0 * (D / 16), (uint32_t)(qr.vis * (D / 16))), ok, (uint32_t)j, d0);
-    if (ly.gather) {   // the gathered copy of the chunk's rows (zeros for empty slots)
-      const int64_t gr = ((int64_t)ly.list * M + m) * Kp;
-      pc.store(make_rsrc(g_codes + gr * (D / 2), (uint32_t)(Kp * (D / 2))),
-               make_rsrc(g_scales + gr * (D / 16), (uint32_t)(Kp * (D / 16))), (uint32_t)slot, d0);
-    }
+    ksv = okm[cc] ? 1.0f : 0.0f;
+    const Fp4Piece<D, DP> &pc = pcm[cc];
+    pc.store(r_gcw, r_gsw, (uint32_t)slot, d0);   // zeros for empty slots
 #pragma unroll
     for (int u = 0; u < DP / 8; ++u) put(u, QF32 ? __builtin_bit_cast(u32x4_t, pc.get(u)) : pc.get_bf16(u));
   } else {
@@ -548,13 +566,26 @@ __global__ __launch_bounds__(256) void k_attn_logits(int M, int K, int nmc, int 
     }
   };
   if constexpr (ONE_TILE) {
-    if (ntw > 0) tile(0, qA, qA);
+    // unconditional: a wave past the heads multiplies zeros and its stores
+    // fall outside the descriptors (a branch here would leave the store count
+    // unknown to the waits of the next chunk)
+    tile(0, qA, qA);
   } else {
     for (int it = 0; it < ntw; it += 2) {
       tile(it, qA, qB);
       if (it + 1 < ntw) tile(it + 1, qB, qA);
     }
   }
+  return true;
+  };
+  if (kLogitChunks * (cp + 1) <= nmc) {
+#pragma unroll
+    for (int cc = 0; cc < kLogitChunks; ++cc)
+      if (!run_chunk(cc, std::integral_constant<int, 1>{})) break;
+  } else {
+#pragma unroll
+    for (int cc = 0; cc < kLogitChunks; ++cc)
+      if (!run_chunk(cc, std::integral_constant<int, 2>{})) break;
   }
 }
 
