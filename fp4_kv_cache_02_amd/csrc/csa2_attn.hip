@@ -243,28 +243,21 @@ CSA2_DEV void buffer_load_words(uint32_t *dst, rsrc_t r, uint32_t off) {
     dst[0] = __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
   }
 }
-// Cache policy of the stores whose data the next kernel reads (the logits
-// kernel's p values, chunk statistics and gathered rows): device scope
-// (sc1), so the lines go on to memory as they are written instead of
-// staying dirty in this XCD's L2 until the kernel ends, where writing them
-// back delays the next launch.
-constexpr int kStoreDevice = 16;
-
-template <int BYTES, int CPOL = 0>
+template <int BYTES>
 CSA2_DEV void buffer_store_words(const uint32_t *src, rsrc_t r, uint32_t off) {
   if constexpr (BYTES >= 16) {
 #pragma unroll
     for (int i = 0; i < BYTES / 16; ++i)
       __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){src[4 * i], src[4 * i + 1], src[4 * i + 2], src[4 * i + 3]}, r,
-                                             off + 16 * i, 0, CPOL);
+                                             off + 16 * i, 0, 0);
   } else if constexpr (BYTES == 8) {
-    __builtin_amdgcn_raw_buffer_store_b64((u32x2_t){src[0], src[1]}, r, off, 0, CPOL);
+    __builtin_amdgcn_raw_buffer_store_b64((u32x2_t){src[0], src[1]}, r, off, 0, 0);
   } else if constexpr (BYTES == 4) {
-    __builtin_amdgcn_raw_buffer_store_b32(src[0], r, off, 0, CPOL);
+    __builtin_amdgcn_raw_buffer_store_b32(src[0], r, off, 0, 0);
   } else if constexpr (BYTES == 2) {
-    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)src[0], r, off, 0, CPOL);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)src[0], r, off, 0, 0);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)src[0], r, off, 0, CPOL);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)src[0], r, off, 0, 0);
   }
 }
 
@@ -288,8 +281,8 @@ struct Fp4Piece {
     buffer_load_words<SB>(s, scales, ok ? j * (D / 16) + d0 / 16 : kOutOfRange);
   }
   CSA2_DEV void store(rsrc_t codes, rsrc_t scales, uint32_t j, int d0) const {
-    buffer_store_words<N / 2, kStoreDevice>(w, codes, j * (D / 2) + d0 / 2);
-    buffer_store_words<SB, kStoreDevice>(s, scales, j * (D / 16) + d0 / 16);
+    buffer_store_words<N / 2>(w, codes, j * (D / 2) + d0 / 2);
+    buffer_store_words<SB>(s, scales, j * (D / 16) + d0 / 16);
   }
   // scale byte of dims d0 + 8u .. +7 (d0 % 16 == 0 when N >= 16)
   CSA2_DEV uint32_t scale_byte(int u) const {
@@ -318,7 +311,7 @@ struct Fp8Piece {
     buffer_load_words<N>(w, codes, ok ? row * (uint32_t)D + d0 : kOutOfRange);
   }
   CSA2_DEV void store(rsrc_t codes, uint32_t row, int d0, int D) const {
-    buffer_store_words<N, kStoreDevice>(w, codes, row * (uint32_t)D + d0);
+    buffer_store_words<N>(w, codes, row * (uint32_t)D + d0);
   }
   CSA2_DEV half8_t get(int u) const { return e4m3x8_to_f16(w[2 * u], w[2 * u + 1]); }
   CSA2_DEV u32x4_t get_bf16(int u) const {
@@ -567,9 +560,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONE_TILE ? 
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)ldexpf(p[i] * ksr[i], e)), r_pw,
-                                              (uint32_t)((h * nkp + kChunk * c + 16 * i + row) * 2), 0, kStoreDevice);
+                                              (uint32_t)((h * nkp + kChunk * c + 16 * i + row) * 2), 0, 0);
       __builtin_amdgcn_raw_buffer_store_b64((u32x2_t){__float_as_uint(mc), __float_as_uint(lc)}, r_sw,
-                                            row == 0 ? (uint32_t)((h * nch + c) * 8) : kOutOfRange, 0, kStoreDevice);
+                                            row == 0 ? (uint32_t)((h * nch + c) * 8) : kOutOfRange, 0, 0);
     }
   };
   if constexpr (ONE_TILE) {

@@ -114,6 +114,15 @@ def test_attn_window_only_and_small_dim():
     _run(205, 100, 64, 3, "bf16", 0, 128, 2, [99, 99], [0, 0], [0, 0], [0, 0], [128, 3])
 
 
+def test_attn_decode_odd_topk_chunks():
+    # K = 80: three 32-slot Top-K chunks, so one logits workgroup holds the
+    # last Top-K chunk and the first window chunk (the mixed path), another
+    # two Top-K chunks (the straight path); padding, invalid entries and a
+    # one-row window on the other queries
+    _run(207, 4000, 512, 64, "bf16", 80, 128, 3, [3999, 3999, 2000], [80, 50, 60], [0, 30, 10], [0, 0, 10],
+         [128, 40, 1])
+
+
 def test_attn_no_window_padded_slots():
     # K = 100 is not a multiple of the 64-slot chunk and there is no window:
     # the padding slots past K must contribute nothing
