@@ -607,13 +607,14 @@ struct PvLds {
 // come from the gathered rows of phase 1.  A chunk's
 // p values (f16) are rescaled by 2^(m_c - M) - exact, a power of two - and
 // accumulated on MFMA: Top-K chunks in one accumulator, window chunks (whose
-// p carry the lift 2^e) in another; O = (acc_main + 2^-e acc_win) / L.  The
-// loads of block b + 2 go into block b's registers once b is multiplied (a
-// ring of two register buffers, so that three waves fit a SIMD and every
-// workgroup of a 4-query, 20-layer batch is resident at once); blocks 0
-// and 1 are issued with the statistics.
-template <int D, int DS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_attn_pv(int M, int H, int nmc, int nwc, const _Float16 *__restrict__ P,
+// p carry the lift 2^e) in another; O = (acc_main + 2^-e acc_win) / L.
+// Blocks 0 and 1 are issued with the statistics.  NB = 3: block b + 2 is
+// issued into a third register buffer before block b is multiplied (two
+// waves per SIMD); NB = 2: block b + 2 goes into block b's registers once b
+// is multiplied, so that three waves fit a SIMD (for grids of more than the
+// 512 workgroups that are resident at once with NB = 3).
+template <int D, int DS, int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 3 : 2))) void k_attn_pv(int M, int H, int nmc, int nwc, const _Float16 *__restrict__ P,
                                                  const float2 *__restrict__ stats, const int32_t *__restrict__ lift,
                                                  const uint8_t *__restrict__ g_codes,
                                                  const uint8_t *__restrict__ g_scales,
@@ -690,7 +691,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   load_stats(0);
   const int32_t ew_raw = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
       make_rsrc(lift + ((int64_t)li * M + m) * nchs, (uint32_t)(nchs * 4)), nmc * 4u, 0, 0);
-  Blk ba, bb;
+  Blk ba, bb, bc;   // bc: the third buffer of the NB = 3 ring
   load_block(0, ba);
   load_block(1, bb);
   // ---- per head: the largest reference M, the sum L, and each chunk's
@@ -753,10 +754,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     aw[t] = am[t];
   }
   const bool active = 16 * wv < hn;
-  // block b: decode `cur` and multiply, then issue block b + 2 into the
-  // same registers (block b + 1's loads stay in flight meanwhile)
-  auto step = [&](int b, Blk &cur) {
-    if (b >= nblk) return;
+  // block b: decode `cur` and multiply
+  auto compute = [&](int b, const Blk &cur) {
     __syncthreads();      // the rescales (first block) or the previous block's V reads are done
     {
       // a wave's 64 slots are all Top-K or all window unless the list's end
@@ -792,11 +791,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         }
       }
     }
-    load_block(b + 2, cur);
   };
-  for (int b = 0; b < nblk; b += 2) {
-    step(b, ba);
-    step(b + 1, bb);
+  if constexpr (NB == 3) {
+    // three buffers: block b + 2 is issued before block b is multiplied
+    auto step = [&](int b, const Blk &cur, Blk &fut) {
+      load_block(b + 2, fut);
+      if (b < nblk) compute(b, cur);
+    };
+    for (int b = 0; b < nblk; b += 3) {
+      step(b, ba, bc);
+      step(b + 1, bb, ba);
+      step(b + 2, bc, bb);
+    }
+  } else {
+    // two buffers: block b + 2 goes into block b's registers once b is
+    // multiplied (block b + 1's loads stay in flight meanwhile)
+    auto step = [&](int b, Blk &cur) {
+      if (b >= nblk) return;
+      compute(b, cur);
+      load_block(b + 2, cur);
+    };
+    for (int b = 0; b < nblk; b += 2) {
+      step(b, ba);
+      step(b + 1, bb);
+    }
   }
   // ---- output: lane (dim row, quad) holds heads 16 w + 4 quad + j ----
   if (active) {
@@ -1050,8 +1068,15 @@ static int attn_layers_impl(const csa2_fp4_cache &kv, const csa2_queries &qs, in
                           lf, gc, gs, gw, lb);
       const int nhg = (heads + kPvHeads - 1) / kPvHeads;
       const dim3 g2(xcd_grid((D / DS) * nhg, qs.m), (unsigned)nl);
-      CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_pv<D, DS>), g2, dim3(256), stream, qs.m, heads, L.nmc, L.nwc, P, st, lf, gc,
-                        gs, gw, lb);
+      // up to 512 workgroups are resident at once with the three-buffer ring
+      // (two waves per SIMD); beyond that the two-buffer ring lets three
+      // fit a SIMD, so more of them run in the first round
+      if ((int64_t)g2.x * g2.y <= 512)
+        CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_pv<D, DS, 3>), g2, dim3(256), stream, qs.m, heads, L.nmc, L.nwc, P, st,
+                          lf, gc, gs, gw, lb);
+      else
+        CSA2_TIMED_LAUNCH(kTimedAttn, (k_attn_pv<D, DS, 2>), g2, dim3(256), stream, qs.m, heads, L.nmc, L.nwc, P, st,
+                          lf, gc, gs, gw, lb);
     }
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
   }
