@@ -970,7 +970,9 @@ def main():
             r = decode_record(wx, Wx, msx, ktx, "graph")
             r["tokens_per_sequence"] = Wx.T
             r["scan_bytes_per_token"] = Wx.scan_bytes_per_launch() / Wx.M
-            r["roofline"]["kernel"] = "first scan (k_score_mq: every row scored against the run's tokens)"
+            r["roofline"]["kernel"] = ("first scan (k_scan_run: the run's tokens share each streamed tile)"
+                                       if Wx.T in (2, 4) else
+                                       "first scan (k_score_mq: every row scored against the run's tokens)")
             extras[f"{wx.name}/graph"] = r
             del Wx
             torch.cuda.empty_cache()

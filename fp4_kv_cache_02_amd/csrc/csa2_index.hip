@@ -177,6 +177,168 @@ __global__ __launch_bounds__(64 * WAVES) void k_scan(const uint8_t *__restrict__
   }
 }
 
+// First scan for runs of R tokens of one sequence (R = 2 or 4 queries of at
+// most 8 indexer heads; the run hint): one pass over the sequence's entries
+// scores every streamed entry against the whole run.  Row tile g of the MFMA
+// holds query 2g in rows 0-7 and query 2g+1 in rows 8-15 (missing heads are
+// zero rows), so each decoded key tile feeds R/2 row tiles, and the bytes
+// streamed are those of one query.  tile_scores_x2 adds each query's two
+// quarters; the one-query scan adds the same two plus two quarters of zero
+// rows, so the scores, block maxima and pools are the same bit for bit.
+// Block maxima and histograms are kept per query exactly as k_scan keeps
+// them.  A run whose queries belong to more than one sequence (a hint not
+// kept) takes one pass per sequence, each leaving the run's other queries
+// out.  grid (chunks, runs).
+template <int DI, int R, int WAVES = kScanWaves, int TILES = kScanTiles, int U = kScanU>
+__global__ __launch_bounds__(64 * WAVES) void k_scan_run(const uint8_t *__restrict__ codes,
+                                                         const uint8_t *__restrict__ scales,
+                                                         const int64_t *__restrict__ seq_start,
+                                                         const int32_t *__restrict__ seq_len, int ratio,
+                                                         const int32_t *__restrict__ q_seq,
+                                                         const int32_t *__restrict__ q_pos,
+                                                         const uint16_t *__restrict__ q_idx,
+                                                         const float *__restrict__ w_idx, int H,
+                                                         float *__restrict__ bmax, int64_t nb_stride,
+                                                         uint32_t *__restrict__ hist, int hist_rep) {
+  constexpr int CHUNK = TILES * 16;
+  constexpr int BLOCKS = CHUNK / kBlock;
+  constexpr int RT = R / 2;
+  static_assert(R == 2 || R == 4, "run length");
+  static_assert(TILES % (WAVES * U) == 0 && U % 2 == 0, "scan tiling");
+  __shared__ float s_bmax[R][BLOCKS];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[R][kHistBins];
+  __shared__ int s_next;  // next unclaimed batch
+  const int m0 = blockIdx.y * R;
+  const int64_t p_begin = (int64_t)blockIdx.x * CHUNK;
+  // the run's queries: sequence and entries visible in this chunk (uniform)
+  int sq[R], vrel[R];
+  bool any = false;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int s;
+    const int64_t v = visible_entries(seq_len, q_seq, q_pos, ratio, m0 + r, &s);
+    sq[r] = __builtin_amdgcn_readfirstlane(s);
+    vrel[r] = __builtin_amdgcn_readfirstlane((int)max<int64_t>(0, min<int64_t>(CHUNK, v - p_begin)));
+    any |= vrel[r] > 0;
+  }
+  if (!any) return;
+  for (int i = threadIdx.x; i < R * kHistBins / 4; i += blockDim.x)
+    reinterpret_cast<uint4 *>(&s_hist[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+
+  const int l = lane_id(), n = l & 15, qq = l >> 4, row = l >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t done = 0;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if ((done >> k) & 1u) continue;
+    // this pass: the sequence of query k and every query of the run in it
+    const int S = sq[k];
+    uint32_t inc = 0;
+    int n_here = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (!((done >> r) & 1u) && sq[r] == S) {
+        inc |= 1u << r;
+        n_here = max(n_here, vrel[r]);
+      }
+    done |= inc;
+    if (n_here == 0) continue;
+    IdxQuery<DI> Q[RT];
+#pragma unroll
+    for (int g = 0; g < RT; ++g) {
+      const int qr = 2 * g + (n >> 3), h = n & 7;
+      const bool valid = ((inc >> qr) & 1u) && h < H;
+      const int64_t qm = m0 + qr;
+      load_query_rows<DI>(q_idx + (qm * H + (valid ? h : 0)) * DI, valid, valid ? w_idx[qm * H + h] : 0.0f, Q[g].a,
+                          Q[g].w);
+    }
+    const int64_t row0 = seq_start[S] + p_begin;
+    const uint8_t *cbase = codes + row0 * (DI / 2);
+    const uint8_t *sbase = scales + row0 * (DI / 16);
+    if (threadIdx.x == 0) s_next = WAVES;
+    __syncthreads();  // s_next is set; the previous pass's flush is done
+    // batch b: tiles b*U .. b*U + U-1 (positions past n_here are clamped to
+    // its last entry and score -inf)
+    const int n_batches = (n_here + U * 16 - 1) / (U * 16);
+    auto load_batch = [&](int b, LaneCodes<DI> *c) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = min((b * U + u) * 16 + n, n_here - 1);
+        load_lane_codes_rel<DI>(cbase, sbase, (uint32_t)p, (uint32_t)qq, c[u]);
+      }
+    };
+    // a lane's share of row tile g's scores for decoded keys kb (each key
+    // tile is decoded once for all the row tiles)
+    auto partial = [&](int g, const half8_t *kb) {
+      float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < DI / 32; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Q[g].a[t], kb[t], acc, 0, 0, 0);
+      return weighted_relu4(Q[g].w, acc);
+    };
+    auto score_batch = [&](int b, const LaneCodes<DI> *c) {
+#pragma unroll
+      for (int pr = 0; pr < U / 2; ++pr) {
+        half8_t ka[DI / 32], kb[DI / 32];
+        decode_keys<DI>(c[2 * pr], ka);
+        decode_keys<DI>(c[2 * pr + 1], kb);
+#pragma unroll
+        for (int g = 0; g < RT; ++g) {
+          // lane row r: tile 2 pr + (r & 1) of the batch, query 2 g + (r >> 1)
+          float v = tile_scores_x2(partial(g, ka), partial(g, kb));
+          const int tile = b * U + 2 * pr + (row & 1);
+          const int qr = 2 * g + (row >> 1);
+          const int vq = (row >> 1) ? vrel[2 * g + 1] : vrel[2 * g];
+          if (tile * 16 + n >= vq) v = -INFINITY;
+          v = max8_scores(v);
+          if ((n & 7) == 0 && ((inc >> qr) & 1u)) s_bmax[qr][tile * 2 + (n >> 3)] = v;
+        }
+      }
+    };
+    auto claim = [&]() {
+      int v = 0;
+      if (l == 0) v = atomicAdd(&s_next, 1);
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    int b = wv;
+    while (b < n_batches) {
+      LaneCodes<DI> c[U];
+      load_batch(b, c);
+      const int next = claim();
+      __builtin_amdgcn_sched_barrier(0);
+      score_batch(b, c);
+      b = next;
+    }
+    __syncthreads();
+    // this pass's queries: block maxima out, counted into their histograms
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (!((inc >> r) & 1u)) continue;
+      const int nb_r = (vrel[r] + kBlock - 1) / kBlock;
+      float *dst = bmax + (int64_t)(m0 + r) * nb_stride + (int64_t)blockIdx.x * BLOCKS;
+      for (int i = threadIdx.x; i < nb_r; i += blockDim.x) {
+        const float v = s_bmax[r][i];
+        dst[i] = v;
+        atomicAdd(&s_hist[r][f2key(v) >> (32 - kHistBits)], 1u);
+      }
+    }
+    __syncthreads();
+    // flush: the first block of each bin to arrive moves the bin's count out
+    // (which leaves the LDS histograms cleared for the next pass)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (!((inc >> r) & 1u)) continue;
+      const int nb_r = (vrel[r] + kBlock - 1) / kBlock;
+      uint32_t *gh = hist + ((int64_t)(m0 + r) * hist_rep + blockIdx.x % hist_rep) * kHistBins;
+      for (int i = threadIdx.x; i < nb_r; i += blockDim.x) {
+        const uint32_t bin = f2key(s_bmax[r][i]) >> (32 - kHistBits);
+        const uint32_t cnt = atomicExch(&s_hist[r][bin], 0u);
+        if (cnt) atomicAdd(&gh[bin], cnt);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Wave-aggregated append of the `pred` lanes to list[*counter ...].
 CSA2_DEV void wave_append(bool pred, int32_t value, int *counter, int32_t *list) {
   const uint64_t mask = __ballot(pred);
@@ -1091,6 +1253,29 @@ static int index_pool_impl(const csa2_fp4_cache &idx, const csa2_queries &qs, co
   // hist, counters and fine are adjacent: clear them with one fill kernel
   const int64_t nz = (int64_t)((L.sure - L.hist) / sizeof(uint32_t));   // a multiple of 64 (256-byte offsets)
   const int64_t nbq = (idx.max_len + kBlock - 1) / kBlock;   // blocks of the longest sequence
+  if ((qs.run == 2 || qs.run == 4) && heads <= 8 && qs.m % qs.run == 0 && nbq > kBlockSelectMax) {
+    // long contexts, runs of 2 or 4 tokens: the first scan with the run's
+    // queries sharing each MFMA tile, then the pool from the histograms
+    if (!cleared)
+      hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((nz / 4 + 255) / 256)), dim3(256), 0, stream, hist, nz);
+    const int runs = qs.m / qs.run;
+    auto chunks_of = [&](int chunk) { return (idx.max_len + chunk - 1) / chunk; };
+#define CSA2_SCAN_RUN(RR, T)                                                                                  \
+  CSA2_TIMED_LAUNCH(kTimedScan, (k_scan_run<DI, RR, kScanWaves, T>), dim3((unsigned)chunks_of(T * 16), runs),   \
+                    dim3(64 * kScanWaves), stream, idx.codes, idx.scales, idx.seq_start, idx.seq_len, idx.ratio, \
+                    qs.seq, qs.pos, q_idx, w_idx, heads, bmax, L.nb_max, hist, L.hist_rep)
+#define CSA2_SCAN_RUN_T(RR)                                                        \
+    switch (scan_tiles(idx.max_len, runs)) {                                       \
+      case kScanTiles: CSA2_SCAN_RUN(RR, kScanTiles); break;                       \
+      case kScanTiles / 4: CSA2_SCAN_RUN(RR, kScanTiles / 4); break;               \
+      default: CSA2_SCAN_RUN(RR, kScanTiles / 16); break;                          \
+    }
+    if (qs.run == 2) { CSA2_SCAN_RUN_T(2); } else { CSA2_SCAN_RUN_T(4); }
+#undef CSA2_SCAN_RUN_T
+#undef CSA2_SCAN_RUN
+    pool_from_hist(idx, qs, P, nbq, L, bmax, hist, counters, sure, tie, pool_out, pool_count, stream);
+    return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+  }
   if (qs.run >= 2) {
     // queries in runs of one sequence: every streamed indexer entry is scored
     // against all the queries of its sequence at once (multi-query MFMA

@@ -129,7 +129,7 @@ def test_index_c4_full_oracle_pass(shape):
 
 @pytest.mark.parametrize("shape", ["decode_4tok_64k", "replay_128tok_256k", "decode_4tok_1m", "decode_2tok_64k",
                                    "decode_8tok_64k", "decode_4tok_16heads_64k", "interleaved_run_hint_64k",
-                                   "decode_3tok_dim256_64k"])
+                                   "decode_3tok_dim256_64k", "decode_2tok_1m", "interleaved_run_hint_1m"])
 def test_index_full_runs_of_tokens(shape):
     """Queries in runs of consecutive tokens of one sequence (run hint >= 2):
     several decode tokens per sequence (drafted positions verified together)
@@ -138,8 +138,10 @@ def test_index_full_runs_of_tokens(shape):
     (a workgroup holds one run of up to 4 or 8 tokens: 2 or 4 row tiles, or
     16 queries for longer runs); the pool comes from the block maxima
     directly (up to 65,536 blocks) or through the block-maximum histogram (1M
-    entries).  A hint that the queries do not keep (sequences interleaved)
-    changes nothing but speed.  Each query's pool and Top-K are compared
+    entries, where runs of 2 or 4 tokens take the first scan with the run's
+    queries sharing each MFMA tile).  A hint that the queries do not keep
+    (sequences interleaved: at 1M the scan then takes one pass per sequence
+    of a run) changes nothing but speed.  Each query's pool and Top-K are compared
     element by element with a full fp64 oracle pass, modulo the near-tie
     band.  Caches are raw FP4 bytes."""
     di, H, P, K = 128, 8, 2048, 512
@@ -157,11 +159,15 @@ def test_index_full_runs_of_tokens(shape):
         lens, cfg, run, H = [65536, 33333], 125, 4, 16
     elif shape == "interleaved_run_hint_64k":
         lens, cfg, run = [65536, 52000], 126, 4
+    elif shape == "decode_2tok_1m":
+        lens, cfg, run = [1 << 20, 600001], 128, 2
+    elif shape == "interleaved_run_hint_1m":
+        lens, cfg, run = [1 << 20, 500001], 129, 4
     else:
         lens, cfg, run, di, K = [65536, 20000, 41111], 127, 3, 256, 256
     q_seq = [s for s in range(len(lens)) for _ in range(run)]
     q_pos = [lens[s] - run + k for s in range(len(lens)) for k in range(run)]
-    if shape == "interleaved_run_hint_64k":    # the hint says runs of 4; the sequences alternate
+    if shape.startswith("interleaved_run_hint"):    # the hint says runs of 4; the sequences alternate
         order = sorted(range(len(q_seq)), key=lambda i: (i % run, i // run))
         q_seq = [q_seq[i] for i in order]
         q_pos = [q_pos[i] for i in order]
